@@ -1,0 +1,256 @@
+"""CPU oracle for the MoK forward MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does.
+
+The arithmetic lives in ``mok_oracle.c`` (plain C, fp64, OpenMP over rows);
+this module compiles it with gcc and wraps it with numpy-array helpers.
+Every array here is plain numpy on the host.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mok_oracle.c")
+_LIB = os.path.join(_HERE, "libmok_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i32, i64 = C.c_int32, C.c_int64
+        L.orc_route_topk.argtypes = [P, i64, i32, i32, P, P]
+        L.orc_route_topk.restype = C.c_int
+        L.orc_build_schedule.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
+        L.orc_build_schedule.restype = C.c_int
+        L.orc_windows.argtypes = [P, i32, i32, i32, P]
+        L.orc_windows.restype = None
+        L.orc_choose_minibatch.argtypes = [i32, i32, i32, i32, i64]
+        L.orc_choose_minibatch.restype = i32
+        L.orc_e4m3_encode_n.argtypes = [P, i64, P]
+        L.orc_e4m3_decode_n.argtypes = [P, i64, P]
+        L.orc_bf16_round_n.argtypes = [P, i64, P]
+        L.orc_mx_quantize.argtypes = [P, i64, P, P]
+        L.orc_mx_dequantize.argtypes = [P, P, i64, P]
+        L.orc_gather_rows.argtypes = [P, i32, i32, P, P, i64, i32, P, P, P]
+        L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P]
+        L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i32, P, P]
+        for f in ("orc_e4m3_encode_n", "orc_e4m3_decode_n", "orc_bf16_round_n",
+                  "orc_mx_quantize", "orc_mx_dequantize", "orc_gather_rows",
+                  "orc_ffn_rows", "orc_combine_tokens"):
+            getattr(L, f).restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------- formats
+def bf16_round(v) -> np.ndarray:
+    v = _c(v, np.float64).reshape(-1)
+    out = np.empty(v.size, np.uint16)
+    lib().orc_bf16_round_n(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_encode(v) -> np.ndarray:
+    v = _c(v, np.float64).reshape(-1)
+    out = np.empty(v.size, np.uint8)
+    lib().orc_e4m3_encode_n(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = _c(c, np.uint8).reshape(-1)
+    out = np.empty(c.size, np.float64)
+    lib().orc_e4m3_decode_n(_p(c), c.size, _p(out))
+    return out
+
+
+def mx_quantize(v):
+    """MXFP8 (E4M3, blocks of 32) of a 1-D array whose length is a multiple of 32."""
+    v = _c(v, np.float64).reshape(-1)
+    assert v.size % 32 == 0
+    codes = np.empty(v.size, np.uint8)
+    scales = np.empty(v.size // 32, np.uint8)
+    lib().orc_mx_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    codes = _c(codes, np.uint8).reshape(-1)
+    scales = _c(scales, np.uint8).reshape(-1)
+    out = np.empty(codes.size, np.float64)
+    lib().orc_mx_dequantize(_p(codes), _p(scales), codes.size, _p(out))
+    return out
+
+
+def bf16_value(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------- steps
+def route_topk(logits: np.ndarray, k: int):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    gate = np.empty((T, k), np.float32)
+    rc = lib().orc_route_topk(_p(logits), T, E, k, _p(idx), _p(gate))
+    if rc:
+        raise ValueError(f"orc_route_topk rc={rc}")
+    return idx, gate
+
+
+def build_schedule(topk_idx: np.ndarray, expert_base: int, n_local: int):
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(n_local, np.int32)
+    offsets = np.empty(n_local + 1, np.int32)
+    soa = np.empty(T * k, np.int32)
+    aos = np.full(T * k, -1, np.int32)
+    rc = lib().orc_build_schedule(_p(idx), T, k, expert_base, n_local, _p(counts),
+                                  _p(offsets), _p(soa), _p(aos))
+    if rc:
+        raise ValueError(f"orc_build_schedule rc={rc}")
+    R = int(offsets[-1])
+    return dict(counts=counts, offsets=offsets, slot_of_assign=soa,
+                assign_of_slot=aos[:R].copy(), R=R)
+
+
+def windows(offsets: np.ndarray, M: int, nwin: int) -> np.ndarray:
+    offsets = _c(offsets, np.int32)
+    n_local = offsets.size - 1
+    out = np.empty((nwin, n_local + 1), np.int32)
+    lib().orc_windows(_p(offsets), n_local, M, nwin, _p(out))
+    return out
+
+
+def choose_minibatch(n_cus: int, tile_m: int, tile_n: int, n_out: int, rows: int = 0) -> int:
+    return int(lib().orc_choose_minibatch(n_cus, tile_m, tile_n, n_out, rows))
+
+
+def gather_rows(x: np.ndarray, k: int, assign_of_slot: np.ndarray, slots, mxfp8: bool):
+    """Dispatched rows for the given slots: bf16 bits [n,H] or (codes [n,H], scales [n,H/32])."""
+    x = _c(x, np.uint16)
+    H = x.shape[1]
+    aos = _c(assign_of_slot, np.int32)
+    slots = _c(slots, np.int64).reshape(-1)
+    n = slots.size
+    if mxfp8:
+        codes = np.empty((n, H), np.uint8)
+        scales = np.empty((n, H // 32), np.uint8)
+        lib().orc_gather_rows(_p(x), H, k, _p(aos), _p(slots), n, 1, None, _p(codes), _p(scales))
+        return codes, scales
+    out = np.empty((n, H), np.uint16)
+    lib().orc_gather_rows(_p(x), H, k, _p(aos), _p(slots), n, 0, _p(out), None, None)
+    return out
+
+
+def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: bool) -> np.ndarray:
+    """Expert SwiGLU FFN of dispatched rows -> y bf16 bits [n, H]."""
+    w_gu = _c(w_gu, np.uint16)
+    w_d = _c(w_d, np.uint16)
+    I2, H = w_gu.shape[1], w_gu.shape[2]
+    I = I2 // 2
+    eor = _c(expert_of_row, np.int32).reshape(-1)
+    n = eor.size
+    y = np.empty((n, H), np.uint16)
+    if mxfp8:
+        codes, scales = xrows
+        codes = _c(codes, np.uint8)
+        scales = _c(scales, np.uint8)
+        lib().orc_ffn_rows(None, _p(codes), _p(scales), _p(eor), n, H, I, _p(w_gu), _p(w_d), 1, _p(y))
+    else:
+        xb = _c(xrows, np.uint16)
+        lib().orc_ffn_rows(_p(xb), None, None, _p(eor), n, H, I, _p(w_gu), _p(w_d), 0, _p(y))
+    return y
+
+
+def combine_tokens(y: np.ndarray, y_row_of_slot: np.ndarray, slot_of_assign: np.ndarray,
+                   topk_gate: np.ndarray, tokens, k: int):
+    """Weighted merge for the listed tokens -> (out bf16 [n,H], written bool [n])."""
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    yr = _c(y_row_of_slot, np.int64)
+    soa = _c(slot_of_assign, np.int32)
+    gate = _c(topk_gate, np.float32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    n = tokens.size
+    out = np.zeros((n, H), np.uint16)
+    written = np.zeros(n, np.uint8)
+    lib().orc_combine_tokens(_p(y), _p(yr), _p(soa), _p(gate), _p(tokens), n, k, H,
+                             _p(out), _p(written))
+    return out, written.astype(bool)
+
+
+def expert_of_slots(offsets: np.ndarray, slots) -> np.ndarray:
+    """Local expert owning each schedule slot (segment lookup in the offsets)."""
+    offsets = np.asarray(offsets, np.int64)
+    slots = np.asarray(slots, np.int64)
+    return (np.searchsorted(offsets, slots, side="right") - 1).astype(np.int32)
+
+
+# ---------------------------------------------------------------- chain
+def forward(wl, tokens=None, slots_extra=None) -> Dict[str, np.ndarray]:
+    """The whole layer for a workload (``workloads.Workload``).
+
+    Route (when the workload routes from logits), schedule, then gather, FFN
+    and combine for the listed pool tokens (all tokens when ``tokens`` is
+    None).  Only the slots those tokens need are computed, plus
+    ``slots_extra`` if given.  Returns routing, schedule, the y rows of the
+    computed slots and the merged output rows.
+    """
+    res: Dict[str, np.ndarray] = {}
+    if wl.routing_from_logits:
+        idx, gate = route_topk(wl.logits, wl.k)
+    else:
+        idx, gate = wl.topk_idx, wl.topk_gate
+        res["route_idx"], res["route_gate"] = route_topk(wl.logits, wl.k)
+    res["topk_idx"], res["topk_gate"] = idx, gate
+    sch = build_schedule(idx, wl.expert_base, wl.n_local)
+    res.update(sch)
+    soa = sch["slot_of_assign"]
+    T, k = wl.T, wl.k
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int64)
+    tokens = np.asarray(tokens, np.int64)
+    s = soa.reshape(T, k)[tokens].reshape(-1)
+    slots = np.unique(s[s >= 0])
+    if slots_extra is not None:
+        slots = np.unique(np.concatenate([slots, np.asarray(slots_extra, np.int64)]))
+    mx = wl.act_format == 1
+    xr = gather_rows(wl.x, k, sch["assign_of_slot"], slots, mx)
+    eor = expert_of_slots(sch["offsets"], slots)
+    y = ffn_rows(xr, eor, wl.w_gu, wl.w_d, mx)
+    y_row_of_slot = np.full(max(sch["R"], 1), -1, np.int64)
+    y_row_of_slot[slots] = np.arange(slots.size)
+    out, written = combine_tokens(y, y_row_of_slot, soa, gate, tokens, k)
+    res.update(slots=slots, x_rows=xr, y=y, tokens=tokens, out=out, written=written)
+    return res
