@@ -1,0 +1,223 @@
+/*
+ * mok.h -- libmok: one GPU's share of the Mixture-of-Kittens (MoK) forward
+ * MoE layer on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the pages' statement of the layer:
+ *   route (tahou.com MoK article, routing paragraph)
+ *   -> count per expert, plan expert-contiguous positions, build the pull
+ *      table (article, layout-planning paragraph; PyTorchKR wiki summary,
+ *      key point on the {src_rank, src_index} schedule built on the device
+ *      without a sort)
+ *   -> pull dispatch into a fixed ring token buffer (article, pull-dispatch
+ *      and ring-buffer paragraphs)
+ *   -> expert SwiGLU FFN as a grouped GEMM, optional MXFP8 activations
+ *      (article, megakernel and state-machine paragraphs)
+ *   -> push combine and final weighted merge (article, push-combine and
+ *      benchmark-scope paragraphs)
+ *   -> the fused layer (article, megakernel paragraph; wiki key points on
+ *      the megakernel and on the SM split with local counters).
+ * Cross-GPU traffic is not part of this library: the token "sources" are
+ * partitions in this GPU's own HBM, addressed by (partition, row).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  Row-major.
+ *   - bf16 tensors are passed as raw 16-bit patterns (void*).
+ *   - The caller owns every buffer.  The library allocates nothing; scratch
+ *     comes from a caller workspace sized by the matching *_workspace_size
+ *     query.
+ *   - Every call is asynchronous and stream-ordered on `stream`; none
+ *     synchronises the host or copies device data to the host, except
+ *     mok_device_status.
+ *   - Synchronous argument errors return a mok_status and launch nothing.
+ *     Conditions only the device can see (more routed rows than the
+ *     capacity given) are reported through a device status word, read with
+ *     mok_device_status (fused calls) or the optional `dev_status` int32
+ *     (standalone calls; NULL = not reported).  Kernels never access memory
+ *     outside the buffers described here, whatever the routing data holds.
+ *   - Calls are stateless and may run concurrently on different streams
+ *     with disjoint buffers.
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOK_OK = 0,
+    MOK_ERR_INVALID_ARG = 1,  /* null pointer, bad size, k > E, ...            */
+    MOK_ERR_UNSUPPORTED = 2,  /* shape outside what the kernels handle         */
+    MOK_ERR_WORKSPACE = 3,    /* workspace smaller than the query returned     */
+    MOK_ERR_HIP = 4,          /* a HIP runtime call or launch failed           */
+    MOK_ERR_DEVICE = 5,       /* device-side wait gave up (persistent kernel)  */
+    MOK_ERR_CAPACITY = 6      /* more routed rows than the capacity passed in  */
+} mok_status;
+
+typedef enum { MOK_ACT_BF16 = 0, MOK_ACT_MXFP8_E4M3 = 1 } mok_act_format;
+
+typedef enum {
+    MOK_MODE_STREAM = 0,      /* one launch per step and per window           */
+    MOK_MODE_PERSISTENT = 1   /* one cooperative kernel for all windows       */
+} mok_mode;
+
+/* One GPU's share of one MoE layer. */
+typedef struct {
+    int32_t hidden;       /* H; multiple of 64                                 */
+    int32_t inter;        /* I (expert intermediate); multiple of 128          */
+    int32_t n_experts;    /* E, experts routed over                            */
+    int32_t top_k;        /* k                                                 */
+    int32_t expert_base;  /* local experts are [expert_base, expert_base+n_local) */
+    int32_t n_local;      /* 1..256                                            */
+    int32_t act_format;   /* mok_act_format                                    */
+    int32_t minibatch;    /* M rows per window; 0 = two-wave rule              */
+    int32_t ring_slots;   /* S ring rows; 0 = 2*M; must be >= M                */
+    int32_t max_rows;     /* capacity for routed rows R; 0 = T*k               */
+    int32_t n_move_cus;   /* data-movement workgroups (persistent); 0 = auto   */
+    int32_t mode;         /* mok_mode                                          */
+} mok_layer_desc;
+
+/* Tokens held in partitions: token t lives in partition t / part_rows at row
+ * t % part_rows.  part_ptr is a DEVICE array of n_partitions DEVICE pointers,
+ * each to bf16 [part_rows][H].  A plain x[T][H] is n_partitions = 1. */
+typedef struct {
+    void* const* part_ptr;
+    int32_t n_partitions;
+    int32_t part_rows;
+} mok_tokens;
+
+/* Top-k route (article, routing paragraph).  For each token t the k largest
+ * logits[t][*] (fp32 [T][E]), equal values resolved to the lower expert id,
+ * written in descending order to topk_idx (int32 [T][k]); topk_gate (fp32
+ * [T][k]) = softmax over those k logits.  1 <= k <= min(E, 32), E <= 4096.
+ * Logits must be finite. */
+mok_status mok_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                          int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+/* Bytes of scratch mok_build_schedule needs. */
+size_t mok_schedule_workspace_size(int64_t T, int32_t k, int32_t n_local);
+
+/* Schedule (article, layout-planning paragraph; wiki key point on the pull
+ * schedule).  Over the T*k assignments a = t*k + j of topk_idx (int32
+ * [T][k]), local expert e = topk_idx - expert_base in [0, n_local):
+ *   counts[e]  (int32 [n_local])    assignments to e
+ *   offsets    (int32 [n_local+1])  exclusive prefix sum; R = offsets[n_local]
+ *   slot_of_assign[a] (int32 [T*k]) offsets[e] + rank of a among e's
+ *                                   assignments in increasing a; -1 if not local
+ *   assign_of_slot[s] (int32 [T*k] capacity) inverse for s < R; entries >= R
+ *                                   are left untouched.
+ * The pull table entry of slot s is token assign_of_slot[s] / k, i.e.
+ * (partition, row) = (token / part_rows, token % part_rows).
+ * No sort and no host round trip.  T*k < 2^31. */
+mok_status mok_build_schedule(const int32_t* topk_idx, int32_t T, int32_t k,
+                              int32_t expert_base, int32_t n_local,
+                              int32_t* counts, int32_t* offsets,
+                              int32_t* slot_of_assign, int32_t* assign_of_slot,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Two-wave minibatch rule (article, minibatch paragraph; wiki key point on
+ * minibatch size): M = 2 * n_cus * tile_m * tile_n / n_out rounded up to a
+ * multiple of 64, clipped to `rows` when rows > 0.  Host only. */
+int32_t mok_choose_minibatch(int32_t n_cus, int32_t tile_m, int32_t tile_n,
+                             int32_t n_out, int64_t rows);
+
+/* Minibatch windows.  win_seg (int32 [nwin][n_local+1]): for window b,
+ * lo = min(b*M, R), hi = min((b+1)*M, R), win_seg[b][e] = clamp(offsets[e],
+ * lo, hi); expert e's rows in window b are [win_seg[b][e], win_seg[b][e+1]). */
+mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M,
+                             int32_t nwin, int32_t* win_seg, hipStream_t stream);
+
+/* Pull dispatch (article, pull-dispatch paragraph).  For each slot s in
+ * [slot_begin, min(slot_end, R)) with R = offsets[n_local]: ring row
+ * s % ring_slots receives the row of token assign_of_slot[s] / k of src
+ * (bf16, H values).  MOK_ACT_BF16: ring is bf16 [ring_slots][H], a bit copy.
+ * MOK_ACT_MXFP8_E4M3: ring is E4M3 codes u8 [ring_slots][H] and ring_scales
+ * E8M0 u8 [ring_slots][H/32] (OCP MX v1.0 blocks of 32 along H).
+ * A token index outside src sets *dev_status = MOK_ERR_CAPACITY and the row
+ * is skipped. */
+mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
+                               const int32_t* assign_of_slot, const int32_t* offsets,
+                               int32_t n_local, int32_t slot_begin, int32_t slot_end,
+                               void* ring, uint8_t* ring_scales, int32_t ring_slots,
+                               int32_t act_format, int32_t* dev_status,
+                               hipStream_t stream);
+
+/* Expert SwiGLU FFN as a grouped GEMM (article, layout-planning and
+ * megakernel paragraphs; SwiGLU and MXFP8 in the state-machine paragraph).
+ * For each slot s in [slot_begin, min(slot_end, R)) owned by local expert e
+ * (offsets[e] <= s < offsets[e+1]), with x = ring row s % ring_slots:
+ *   g = W_gu[e][0:I] . x,  u = W_gu[e][I:2I] . x      (fp32 accumulation)
+ *   a = SiLU(g) * u  -> act row s % act_rows (bf16, or MXFP8 blocks of 32
+ *                       along I into act/act_scales [act_rows][I/32])
+ *   y = W_d[e] . a   -> y row s % y_rows (bf16 [y_rows][H])
+ * w_gate_up: bf16 [n_local][2I][H], rows 0..I-1 gate, I..2I-1 up; w_down:
+ * bf16 [n_local][H][I]; no biases.  desc supplies H, I, n_local, act_format.
+ * The ring and act formats follow desc->act_format. */
+mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring,
+                          const uint8_t* ring_scales, int32_t ring_slots,
+                          const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                          const void* w_gate_up, const void* w_down,
+                          void* act, uint8_t* act_scales, int32_t act_rows,
+                          void* y, int32_t y_rows, hipStream_t stream);
+
+/* Push combine + final weighted merge (article, push-combine and benchmark
+ * scope paragraphs).  For each token t with at least one local assignment
+ * (slot_of_assign[t*k+j] >= 0):
+ *   out[t] = bf16( sum over j ascending, local, of gate[t][j] * y[slot] )
+ * accumulated in fp32 fma from 0.  y is bf16 [y_rows][H] indexed by slot.
+ * Rows of tokens with no local assignment are not written.  A slot >= y_rows
+ * sets *dev_status = MOK_ERR_CAPACITY and contributes nothing. */
+mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_assign,
+                       const float* topk_gate, int32_t T, int32_t k, int32_t H,
+                       const mok_tokens* out, int32_t* dev_status, hipStream_t stream);
+
+/* Bytes of workspace mok_moe_forward / mok_moe_forward_batches need for T
+ * source tokens per macrobatch and n_macro macrobatches. */
+size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro);
+
+/* The fused layer (article, megakernel, minibatch and ring-buffer
+ * paragraphs): schedule, windows, pull dispatch into the fixed ring, grouped
+ * SwiGLU FFN, push of y into a return area indexed by slot, weighted merge
+ * into out.  Routing (topk_idx / topk_gate, [T][k]) comes from the sources'
+ * route step.  MOK_MODE_STREAM issues stream-ordered launches per window;
+ * MOK_MODE_PERSISTENT runs the windows in one cooperative kernel whose
+ * workgroups split into data movers and MFMA workers that signal through
+ * device counters.  If R exceeds desc->max_rows the status word becomes
+ * MOK_ERR_CAPACITY and out is left untouched. */
+mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
+                           const float* topk_gate, int32_t T, const mok_tokens* x,
+                           const void* w_gate_up, const void* w_down,
+                           const mok_tokens* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* n_macro macrobatches through one ring (article, ring-buffer paragraph:
+ * the next macrobatch's dispatch overlaps the previous one's combine).
+ * topk_idx / topk_gate / out are HOST arrays of n_macro entries (device
+ * pointers / host mok_tokens); all macrobatches share x, the weights and T. */
+mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
+                                   const int32_t* const* topk_idx,
+                                   const float* const* topk_gate, int32_t T,
+                                   const mok_tokens* x, const void* w_gate_up,
+                                   const void* w_down, const mok_tokens* out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, then copies the workspace status word to
+ * *status_host (MOK_OK, MOK_ERR_CAPACITY or MOK_ERR_DEVICE). */
+mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream);
+
+/* Minibatch the fused call uses for desc (after the two-wave rule) and the
+ * number of windows it plans for T tokens.  Host only. */
+int32_t mok_forward_minibatch(const mok_layer_desc* desc, int32_t T);
+
+const char* mok_status_str(mok_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_H */

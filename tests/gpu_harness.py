@@ -1,0 +1,134 @@
+"""Helpers for the GPU parity tests and the benchmark: move a workload to the
+device and drive the libmok C-ABI through its Python binding.  No arithmetic
+of the layer happens here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import token_dispatch_grouped_top_amd as mok
+
+SENTINEL = 0x7FC1   # a bf16 NaN pattern: rows the layer must not write keep it
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    return a
+
+
+def empty_u16(*shape) -> torch.Tensor:
+    return torch.empty(shape, dtype=torch.int16, device="cuda")
+
+
+def gpu_schedule(idx, T: int, k: int, expert_base: int, n_local: int) -> dict:
+    """mok_build_schedule on device buffers; assign_of_slot pre-filled with -7."""
+    A = T * k
+    counts = torch.empty(n_local, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(n_local + 1, dtype=torch.int32, device="cuda")
+    soa = torch.empty(max(A, 1), dtype=torch.int32, device="cuda")
+    aos = torch.full((max(A, 1),), -7, dtype=torch.int32, device="cuda")
+    wsb = mok.mok_schedule_workspace_size(T, k, n_local)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    mok.mok_build_schedule(idx, T, k, expert_base, n_local, counts, offsets, soa, aos, ws)
+    return dict(counts=counts, offsets=offsets, soa=soa, aos=aos)
+
+
+class DeviceWorkload:
+    """A ``workloads.Workload`` on the GPU: each source partition and each
+    output partition in its own allocation."""
+
+    def __init__(self, wl, n_out: int = 1):
+        self.wl = wl
+        P, rows, H = wl.n_partitions, wl.part_rows, wl.H
+        self.x_parts = [to_dev(wl.x[p * rows:(p + 1) * rows]) for p in range(P)]
+        self.x = mok.Tokens(self.x_parts, rows)
+        self.w_gu = to_dev(wl.w_gu)
+        self.w_d = to_dev(wl.w_d)
+        self.logits = to_dev(wl.logits)
+        if wl.topk_idx is not None:
+            self.topk_idx = to_dev(wl.topk_idx)
+            self.topk_gate = to_dev(wl.topk_gate)
+        else:
+            self.topk_idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+            self.topk_gate = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        self.outs = [self.new_out() for _ in range(n_out)]
+
+    def new_out(self) -> mok.Tokens:
+        wl = self.wl
+        parts = [torch.full((wl.part_rows, wl.H), SENTINEL, dtype=torch.int16, device="cuda")
+                 for _ in range(wl.n_partitions)]
+        return mok.Tokens(parts, wl.part_rows)
+
+    def out_rows(self, out: mok.Tokens, tokens=None) -> np.ndarray:
+        full = torch.cat(out.parts, 0)
+        if tokens is not None:
+            full = full[torch.as_tensor(np.asarray(tokens), device="cuda")]
+        return to_host(full)
+
+    def reset_out(self, out: mok.Tokens) -> None:
+        for p in out.parts:
+            p.fill_(SENTINEL)
+
+    def desc(self, **kw) -> mok.mok_layer_desc:
+        wl = self.wl
+        d = mok.mok_layer_desc(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.k,
+                               expert_base=wl.expert_base, n_local=wl.n_local,
+                               act_format=wl.act_format)
+        for key, v in kw.items():
+            setattr(d, key, v)
+        return d
+
+    # ---- steps through the C-ABI
+    def route(self, logits=None, idx=None, gate=None):
+        wl = self.wl
+        logits = self.logits if logits is None else logits
+        T, E = logits.shape
+        idx = torch.empty((T, wl.k), dtype=torch.int32, device="cuda") if idx is None else idx
+        gate = torch.empty((T, wl.k), dtype=torch.float32, device="cuda") if gate is None else gate
+        mok.mok_route_topk(logits, T, E, wl.k, idx, gate)
+        return idx, gate
+
+    def routing(self):
+        """Routing the layer consumes: routed from logits, or the given pool routing."""
+        if self.wl.routing_from_logits:
+            self.route(idx=self.topk_idx, gate=self.topk_gate)
+        return self.topk_idx, self.topk_gate
+
+    def schedule(self, idx):
+        wl = self.wl
+        return gpu_schedule(idx, wl.T, wl.k, wl.expert_base, wl.n_local)
+
+    def forward(self, out=None, **desc_kw):
+        wl = self.wl
+        out = self.outs[0] if out is None else out
+        idx, gate = self.routing()
+        d = self.desc(**desc_kw)
+        wsb = mok.mok_forward_workspace_size(d, wl.T, 1)
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        mok.mok_moe_forward(d, idx, gate, wl.T, self.x, self.w_gu, self.w_d, out, ws)
+        return ws, d
+
+
+def bf16_vals(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
+        .astype(np.float64)
+
+
+def assert_close_rms(got_bits: np.ndarray, ref_bits: np.ndarray, tol_rms: float, what: str):
+    """max|got - ref| <= tol_rms * RMS(ref): the output bar for the layer."""
+    g, r = bf16_vals(got_bits), bf16_vals(ref_bits)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(r * r)))
+    err = float(np.max(np.abs(g - r))) if g.size else 0.0
+    assert err <= tol_rms * rms, f"{what}: max|d| = {err:.4g} > {tol_rms} * RMS {rms:.4g}"
+    return err / rms if rms > 0 else 0.0

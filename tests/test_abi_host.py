@@ -1,0 +1,96 @@
+"""Host-side checks of the libmok C-ABI (no GPU needed): the library loads,
+exports every function include/mok.h declares, rejects bad arguments with
+synchronous status codes before any launch, and its host-only minibatch rule
+agrees with the oracle's independent one."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+import oracle
+import token_dispatch_grouped_top_amd as mok
+
+
+def test_exports_every_declared_symbol():
+    names = mok.header_functions()
+    assert len(names) >= 14
+    missing = [n for n in names if not hasattr(mok._lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for s in range(7):
+        assert mok.mok_status_str(s)
+    assert "capacity" in mok.mok_status_str(mok.MOK_ERR_CAPACITY)
+
+
+def test_minibatch_rule_matches_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        n, tm, tn = int(rng.integers(1, 400)), int(rng.choice([16, 32, 64, 128, 256])), \
+            int(rng.choice([16, 32, 64, 128, 256]))
+        nout, rows = int(rng.integers(1, 40000)), int(rng.integers(0, 20000))
+        assert mok.mok_choose_minibatch(n, tm, tn, nout, rows) == \
+            oracle.choose_minibatch(n, tm, tn, nout, rows)
+    assert mok.mok_choose_minibatch(148, 128, 256, 4096) == 2368
+
+
+L = mok._lib
+
+
+def test_invalid_arguments_rejected_without_launch():
+    E = mok.MOK_ERR_INVALID_ARG
+    assert L.mok_route_topk(1, 4, 8, 9, 1, 1, None) == E          # k > E
+    assert L.mok_route_topk(1, 4, 8, 0, 1, 1, None) == E          # k = 0
+    assert L.mok_route_topk(1, 4, 5000, 2, 1, 1, None) == E       # E too large
+    assert L.mok_route_topk(0, 4, 8, 2, 1, 1, None) == E          # null logits
+    ws = 1
+    assert L.mok_build_schedule(1, 4, 2, 0, 0, 1, 1, 1, 1, ws, 1 << 20, None) == E  # n_local 0
+    assert L.mok_build_schedule(1, 4, 2, 0, 300, 1, 1, 1, 1, ws, 1 << 20, None) == E
+    assert L.mok_build_schedule(1, 4, 2, 0, 8, 1, 1, 1, 1, ws, 1, None) == mok.MOK_ERR_WORKSPACE
+    assert L.mok_build_schedule(1, 1 << 28, 16, 0, 8, 1, 1, 1, 1, ws, 1 << 40, None) == \
+        mok.MOK_ERR_UNSUPPORTED
+    assert L.mok_build_windows(0, 8, 64, 4, 1, None) == E
+    assert L.mok_build_windows(1, 8, 0, 4, 1, None) == E
+    tok = mok.mok_tokens(1, 1, 16)
+    assert L.mok_dispatch_gather(C.byref(tok), 60, 2, 1, 1, 8, 0, 10, 1, 1, 4, 1, None, None) == E
+    assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 5, 4, 1, None, 4, 0, None, None) == E
+    assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 0, 4, 1, None, 4, 1, None, None) == E
+    assert L.mok_combine(1, 4, 1, 1, 17, 2, 64, C.byref(tok), None, None) == E  # T > rows
+    assert L.mok_combine(1, 4, 1, 1, 16, 2, 60, C.byref(tok), None, None) == E  # H % 8
+
+
+def _desc(**kw):
+    d = mok.mok_layer_desc(hidden=256, inter=512, n_experts=8, top_k=2, expert_base=0, n_local=8)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("bad", [dict(hidden=100), dict(inter=96), dict(n_local=0),
+                                 dict(n_local=300), dict(top_k=9), dict(top_k=0),
+                                 dict(expert_base=4), dict(act_format=3), dict(mode=7),
+                                 dict(minibatch=-1), dict(ring_slots=64, minibatch=128)])
+def test_bad_descriptors(bad):
+    d = _desc(**bad)
+    assert mok.mok_forward_workspace_size(d, 256, 1) == 0
+    tok = mok.mok_tokens(1, 1, 256)
+    st = L.mok_moe_forward(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, 1 << 40, None)
+    assert st in (mok.MOK_ERR_INVALID_ARG, mok.MOK_ERR_UNSUPPORTED)
+
+
+def test_workspace_query_and_small_workspace():
+    d = _desc(max_rows=512)
+    n = mok.mok_forward_workspace_size(d, 256, 1)
+    assert n > 0
+    assert mok.mok_forward_workspace_size(d, 256, 2) > n
+    tok = mok.mok_tokens(1, 1, 256)
+    st = L.mok_moe_forward(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, n - 1, None)
+    assert st == mok.MOK_ERR_WORKSPACE
+
+
+def test_forward_minibatch_plan():
+    # explicit minibatch is clipped to the row capacity; S defaults to 2M
+    assert mok.mok_forward_minibatch(_desc(minibatch=100), 256) == 100
+    assert mok.mok_forward_minibatch(_desc(minibatch=5000), 256) == 512
+    assert mok.mok_forward_minibatch(_desc(minibatch=100, max_rows=64), 256) == 64

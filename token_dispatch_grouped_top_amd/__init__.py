@@ -1,0 +1,216 @@
+"""libmok: one GPU's share of the Mixture-of-Kittens forward MoE layer on MI355X.
+
+A thin ctypes binding over ``libmok.so`` (built from ``csrc/`` with hipcc
+for gfx950).  Every function here has the name of the C entry point it
+marshals and does nothing but convert arguments: torch tensors become device
+pointers, ``stream=None`` becomes torch's current HIP stream, a non-zero
+status becomes a :class:`MokError`.  All arithmetic runs in the HIP kernels.
+
+There is no fallback: importing this package without a built ``libmok.so``
+raises ``ImportError``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmok.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "mok.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m token_dispatch_grouped_top_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE = 0, 1, 2, 3
+MOK_ERR_HIP, MOK_ERR_DEVICE, MOK_ERR_CAPACITY = 4, 5, 6
+MOK_ACT_BF16, MOK_ACT_MXFP8_E4M3 = 0, 1
+MOK_MODE_STREAM, MOK_MODE_PERSISTENT = 0, 1
+
+
+class MokError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {mok_status_str(status)} ({status})")
+
+
+class mok_layer_desc(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "hidden", "inter", "n_experts", "top_k", "expert_base", "n_local", "act_format",
+        "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode")]
+
+
+class mok_tokens(C.Structure):
+    _fields_ = [("part_ptr", C.c_void_p), ("n_partitions", C.c_int32), ("part_rows", C.c_int32)]
+
+
+_P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_DESC, _TOK = C.POINTER(mok_layer_desc), C.POINTER(mok_tokens)
+_SIGS = {
+    "mok_route_topk": (C.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "mok_schedule_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "mok_build_schedule": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mok_choose_minibatch": (_I32, [_I32, _I32, _I32, _I32, _I64]),
+    "mok_build_windows": (C.c_int, [_P, _I32, _I32, _I32, _P, _P]),
+    "mok_dispatch_gather": (C.c_int, [_TOK, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32,
+                                      _I32, _P, _P]),
+    "mok_expert_ffn": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P,
+                                 _I32, _P]),
+    "mok_combine": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _I32, _TOK, _P, _P]),
+    "mok_forward_workspace_size": (_SZ, [_DESC, _I32, _I32]),
+    "mok_moe_forward": (C.c_int, [_DESC, _P, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
+    "mok_moe_forward_batches": (C.c_int, [_DESC, _I32, _P, _P, _I32, _TOK, _P, _P, _TOK, _P,
+                                          _SZ, _P]),
+    "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
+    "mok_forward_minibatch": (_I32, [_DESC, _I32]),
+    "mok_status_str": (C.c_char_p, [C.c_int]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+def header_functions() -> List[str]:
+    """Names of the functions include/mok.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mok_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> int:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, call: str) -> None:
+    if status != MOK_OK:
+        raise MokError(status, call)
+
+
+class Tokens:
+    """Token partitions on the device (a ``mok_tokens`` plus what keeps it alive).
+
+    ``parts`` are bf16-bit tensors (torch.int16/uint16/bfloat16) of shape
+    [part_rows, H] on the GPU; the pointer array is itself a device tensor.
+    """
+
+    def __init__(self, parts: Sequence, part_rows: Optional[int] = None):
+        import torch
+        self.parts = list(parts)
+        rows = part_rows if part_rows is not None else self.parts[0].shape[0]
+        dev = self.parts[0].device
+        self.ptrs = torch.tensor([p.data_ptr() for p in self.parts], dtype=torch.int64, device=dev)
+        self.c = mok_tokens(self.ptrs.data_ptr(), len(self.parts), rows)
+
+    @classmethod
+    def from_tensor(cls, x):
+        return cls([x], x.shape[0])
+
+
+# ------------------------------------------------------------------ calls
+def mok_status_str(status: int) -> str:
+    return _lib.mok_status_str(status).decode()
+
+
+def mok_route_topk(logits, T: int, E: int, k: int, topk_idx, topk_gate, stream=None) -> None:
+    _check(_lib.mok_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_gate),
+                               _stream(stream)), "mok_route_topk")
+
+
+def mok_schedule_workspace_size(T: int, k: int, n_local: int) -> int:
+    return int(_lib.mok_schedule_workspace_size(T, k, n_local))
+
+
+def mok_build_schedule(topk_idx, T: int, k: int, expert_base: int, n_local: int, counts, offsets,
+                       slot_of_assign, assign_of_slot, ws, ws_bytes: Optional[int] = None,
+                       stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.mok_build_schedule(_ptr(topk_idx), T, k, expert_base, n_local, _ptr(counts),
+                                   _ptr(offsets), _ptr(slot_of_assign), _ptr(assign_of_slot),
+                                   _ptr(ws), ws_bytes, _stream(stream)), "mok_build_schedule")
+
+
+def mok_choose_minibatch(n_cus: int, tile_m: int, tile_n: int, n_out: int, rows: int = 0) -> int:
+    return int(_lib.mok_choose_minibatch(n_cus, tile_m, tile_n, n_out, rows))
+
+
+def mok_build_windows(offsets, n_local: int, M: int, nwin: int, win_seg, stream=None) -> None:
+    _check(_lib.mok_build_windows(_ptr(offsets), n_local, M, nwin, _ptr(win_seg),
+                                  _stream(stream)), "mok_build_windows")
+
+
+def mok_dispatch_gather(src: Tokens, H: int, k: int, assign_of_slot, offsets, n_local: int,
+                        slot_begin: int, slot_end: int, ring, ring_scales, ring_slots: int,
+                        act_format: int, dev_status=None, stream=None) -> None:
+    _check(_lib.mok_dispatch_gather(C.byref(src.c), H, k, _ptr(assign_of_slot), _ptr(offsets),
+                                    n_local, slot_begin, slot_end, _ptr(ring), _ptr(ring_scales),
+                                    ring_slots, act_format, _ptr(dev_status), _stream(stream)),
+           "mok_dispatch_gather")
+
+
+def mok_expert_ffn(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, offsets,
+                   slot_begin: int, slot_end: int, w_gate_up, w_down, act, act_scales,
+                   act_rows: int, y, y_rows: int, stream=None) -> None:
+    _check(_lib.mok_expert_ffn(C.byref(desc), _ptr(ring), _ptr(ring_scales), ring_slots,
+                               _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up), _ptr(w_down),
+                               _ptr(act), _ptr(act_scales), act_rows, _ptr(y), y_rows,
+                               _stream(stream)), "mok_expert_ffn")
+
+
+def mok_combine(y, y_rows: int, slot_of_assign, topk_gate, T: int, k: int, H: int, out: Tokens,
+                dev_status=None, stream=None) -> None:
+    _check(_lib.mok_combine(_ptr(y), y_rows, _ptr(slot_of_assign), _ptr(topk_gate), T, k, H,
+                            C.byref(out.c), _ptr(dev_status), _stream(stream)), "mok_combine")
+
+
+def mok_forward_workspace_size(desc: mok_layer_desc, T: int, n_macro: int = 1) -> int:
+    return int(_lib.mok_forward_workspace_size(C.byref(desc), T, n_macro))
+
+
+def mok_forward_minibatch(desc: mok_layer_desc, T: int) -> int:
+    return int(_lib.mok_forward_minibatch(C.byref(desc), T))
+
+
+def mok_moe_forward(desc: mok_layer_desc, topk_idx, topk_gate, T: int, x: Tokens, w_gate_up,
+                    w_down, out: Tokens, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.mok_moe_forward(C.byref(desc), _ptr(topk_idx), _ptr(topk_gate), T, C.byref(x.c),
+                                _ptr(w_gate_up), _ptr(w_down), C.byref(out.c), _ptr(ws), ws_bytes,
+                                _stream(stream)), "mok_moe_forward")
+
+
+def mok_moe_forward_batches(desc: mok_layer_desc, n_macro: int, topk_idx: Sequence,
+                            topk_gate: Sequence, T: int, x: Tokens, w_gate_up, w_down,
+                            out: Sequence[Tokens], ws, ws_bytes: Optional[int] = None,
+                            stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    idx_arr = (C.c_void_p * n_macro)(*[_ptr(t) for t in topk_idx])
+    gate_arr = (C.c_void_p * n_macro)(*[_ptr(t) for t in topk_gate])
+    out_arr = (mok_tokens * n_macro)(*[o.c for o in out])
+    _check(_lib.mok_moe_forward_batches(C.byref(desc), n_macro, C.cast(idx_arr, C.c_void_p),
+                                        C.cast(gate_arr, C.c_void_p), T, C.byref(x.c),
+                                        _ptr(w_gate_up), _ptr(w_down), out_arr, _ptr(ws),
+                                        ws_bytes, _stream(stream)), "mok_moe_forward_batches")
+
+
+def mok_device_status(ws, stream=None) -> int:
+    v = C.c_int32(-1)
+    _check(_lib.mok_device_status(_ptr(ws), C.byref(v), _stream(stream)), "mok_device_status")
+    return int(v.value)

@@ -1,0 +1,359 @@
+// abi.hip -- the extern "C" entry points of libmok: argument checks,
+// workspace carving and the stream-ordered orchestration of the fused layer.
+// The kernels live in route.hip, schedule.hip, movers.hip and gemm.hip; the
+// persistent pipeline in persistent.hip.
+#include <algorithm>
+#include <cstring>
+
+#include "mok_internal.h"
+#include "persistent.h"
+
+namespace mok {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kGemmTileM = 256, kGemmTileN = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+__global__ void k_fill_i32(int32_t* p, int32_t n, int32_t v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Sets the status word when more rows were routed here than the capacity.
+__global__ void k_capacity_check(const int32_t* offsets, int32_t n_local, int32_t cap,
+                                 int32_t* status) {
+  if (threadIdx.x == 0 && offsets[n_local] > cap) set_status(status, MOK_ERR_CAPACITY);
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+bool tokens_ok(const mok_tokens* t, int64_t T) {
+  return t && t->part_ptr && t->n_partitions >= 1 && t->part_rows >= 1 &&
+         static_cast<int64_t>(t->n_partitions) * t->part_rows >= T;
+}
+
+bool desc_ok(const mok_layer_desc* d) {
+  if (!d) return false;
+  if (d->hidden <= 0 || d->hidden % 64 != 0) return false;
+  if (d->inter <= 0 || d->inter % 64 != 0) return false;
+  if (d->n_local < 1 || d->n_local > 256) return false;
+  if (d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts) return false;
+  if (d->expert_base < 0 || d->expert_base + d->n_local > d->n_experts) return false;
+  if (d->act_format != MOK_ACT_BF16 && d->act_format != MOK_ACT_MXFP8_E4M3) return false;
+  if (d->minibatch < 0 || d->ring_slots < 0 || d->max_rows < 0 || d->n_move_cus < 0) return false;
+  if (d->mode != MOK_MODE_STREAM && d->mode != MOK_MODE_PERSISTENT) return false;
+  return true;
+}
+
+// Sizes of the fused call, derived from shapes only.
+struct Plan {
+  int64_t A;          // T*k assignments per macrobatch
+  int32_t cap;        // row capacity (>= R expected)
+  int32_t M, S;       // minibatch, ring rows
+  int32_t nwin;       // windows planned per macrobatch
+  int32_t act_rows;
+  int32_t n_ybuf;     // return areas (2 when macrobatches overlap)
+  size_t off_status, off_sched, off_counts, off_offsets, off_soa, off_aos, off_win, off_ring,
+      off_ring_sc, off_act, off_act_sc, off_y, off_pers, total;
+  size_t per_macro_counts, per_macro_offsets, per_macro_soa, per_macro_aos, per_macro_win;
+};
+
+int32_t plan_minibatch(const mok_layer_desc* d, int64_t cap) {
+  if (d->minibatch > 0) return static_cast<int32_t>(std::min<int64_t>(d->minibatch, std::max<int64_t>(cap, 1)));
+  int32_t m = mok_choose_minibatch(device_cus(), kGemmTileM, kGemmTileN, 2 * d->inter, cap);
+  return std::max<int32_t>(m, 1);
+}
+
+bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
+  p.A = static_cast<int64_t>(T) * d->top_k;
+  if (p.A >= (1ll << 31)) return false;
+  int64_t cap = d->max_rows > 0 ? d->max_rows : p.A;
+  if (cap < 1) cap = 1;
+  p.cap = static_cast<int32_t>(cap);
+  p.M = plan_minibatch(d, cap);
+  p.S = d->ring_slots > 0 ? d->ring_slots : 2 * p.M;
+  if (p.S < p.M) return false;
+  p.nwin = static_cast<int32_t>((cap + p.M - 1) / p.M);
+  p.act_rows = p.S;
+  p.n_ybuf = n_macro > 1 ? 2 : 1;
+  const bool mx = d->act_format == MOK_ACT_MXFP8_E4M3;
+  const int64_t H = d->hidden, I = d->inter, nl = d->n_local;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  p.off_status = take(kAlign);
+  p.off_sched = take(sched_ws_bytes(p.A, d->n_local));
+  p.per_macro_counts = align_up(nl * 4);
+  p.per_macro_offsets = align_up((nl + 1) * 4);
+  p.per_macro_soa = align_up(std::max<int64_t>(p.A, 1) * 4);
+  p.per_macro_aos = align_up(std::max<int64_t>(p.A, 1) * 4);
+  p.per_macro_win = align_up(static_cast<size_t>(p.nwin) * (nl + 1) * 4);
+  p.off_counts = take(p.per_macro_counts * n_macro);
+  p.off_offsets = take(p.per_macro_offsets * n_macro);
+  p.off_soa = take(p.per_macro_soa * n_macro);
+  p.off_aos = take(p.per_macro_aos * n_macro);
+  p.off_win = take(p.per_macro_win * n_macro);
+  p.off_ring = take(static_cast<size_t>(p.S) * H * (mx ? 1 : 2));
+  p.off_ring_sc = take(mx ? static_cast<size_t>(p.S) * (H / 32) : 0);
+  p.off_act = take(static_cast<size_t>(p.act_rows) * I * (mx ? 1 : 2));
+  p.off_act_sc = take(mx ? static_cast<size_t>(p.act_rows) * (I / 32) : 0);
+  p.off_y = take(static_cast<size_t>(p.n_ybuf) * p.cap * H * 2);
+  p.off_pers = take(persistent_ws_bytes(p.nwin * static_cast<int64_t>(n_macro)));
+  p.total = o;
+  return true;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+mok_status hip_status(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_HIP; }
+
+}  // namespace
+}  // namespace mok
+
+using namespace mok;
+
+extern "C" {
+
+const char* mok_status_str(mok_status s) {
+  switch (s) {
+    case MOK_OK: return "ok";
+    case MOK_ERR_INVALID_ARG: return "invalid argument";
+    case MOK_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOK_ERR_WORKSPACE: return "workspace too small";
+    case MOK_ERR_HIP: return "HIP runtime or launch error";
+    case MOK_ERR_DEVICE: return "device-side wait gave up";
+    case MOK_ERR_CAPACITY: return "more routed rows than the capacity";
+  }
+  return "unknown status";
+}
+
+mok_status mok_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                          float* topk_gate, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 4096 || k < 1 || k > 32 || k > E) return MOK_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_idx || !topk_gate)) return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, stream));
+}
+
+size_t mok_schedule_workspace_size(int64_t T, int32_t k, int32_t n_local) {
+  if (T < 0 || k < 1 || n_local < 1) return 0;
+  return sched_ws_bytes(T * k, n_local);
+}
+
+mok_status mok_build_schedule(const int32_t* topk_idx, int32_t T, int32_t k, int32_t expert_base,
+                              int32_t n_local, int32_t* counts, int32_t* offsets,
+                              int32_t* slot_of_assign, int32_t* assign_of_slot, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || k < 1 || n_local < 1 || n_local > 256) return MOK_ERR_INVALID_ARG;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A >= (1ll << 31)) return MOK_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !ws) return MOK_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !slot_of_assign || !assign_of_slot)) return MOK_ERR_INVALID_ARG;
+  if (ws_bytes < sched_ws_bytes(A, n_local)) return MOK_ERR_WORKSPACE;
+  SchedWs w = sched_ws_carve(ws, A, n_local);
+  return hip_status(launch_schedule(topk_idx, A, expert_base, n_local, counts, offsets,
+                                    slot_of_assign, assign_of_slot, w, stream));
+}
+
+int32_t mok_choose_minibatch(int32_t n_cus, int32_t tile_m, int32_t tile_n, int32_t n_out,
+                             int64_t rows) {
+  if (n_cus < 1 || tile_m < 1 || tile_n < 1 || n_out < 1) return 0;
+  int64_t need = 2ll * n_cus * tile_m * tile_n;
+  int64_t m = (need + n_out - 1) / n_out;
+  m = (m + 63) / 64 * 64;
+  if (rows > 0 && m > rows) m = rows;
+  return static_cast<int32_t>(m);
+}
+
+mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M, int32_t nwin,
+                             int32_t* win_seg, hipStream_t stream) {
+  if (!offsets || n_local < 1 || M < 1 || nwin < 0) return MOK_ERR_INVALID_ARG;
+  if (nwin > 0 && !win_seg) return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_windows(offsets, n_local, M, nwin, win_seg, stream));
+}
+
+mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
+                               const int32_t* assign_of_slot, const int32_t* offsets,
+                               int32_t n_local, int32_t slot_begin, int32_t slot_end, void* ring,
+                               uint8_t* ring_scales, int32_t ring_slots, int32_t act_format,
+                               int32_t* dev_status, hipStream_t stream) {
+  if (!tokens_ok(src, 0) || H <= 0 || H % 8 != 0 || k < 1 || !assign_of_slot || !offsets ||
+      n_local < 1 || slot_begin < 0 || slot_end < slot_begin || !ring || ring_slots < 1)
+    return MOK_ERR_INVALID_ARG;
+  if (act_format == MOK_ACT_MXFP8_E4M3) {
+    if (H % 32 != 0 || !ring_scales) return MOK_ERR_INVALID_ARG;
+  } else if (act_format != MOK_ACT_BF16) {
+    return MOK_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_gather(src->part_ptr, src->n_partitions, src->part_rows, H, k,
+                                  assign_of_slot, offsets, n_local, slot_begin, slot_end, ring,
+                                  ring_scales, ring_slots, act_format, dev_status, stream));
+}
+
+mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const uint8_t* ring_scales,
+                          int32_t ring_slots, const int32_t* offsets, int32_t slot_begin,
+                          int32_t slot_end, const void* w_gate_up, const void* w_down, void* act,
+                          uint8_t* act_scales, int32_t act_rows, void* y, int32_t y_rows,
+                          hipStream_t stream) {
+  if (!desc_ok(desc) || !ring || ring_slots < 1 || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_gate_up || !w_down || !act || act_rows < 1 || !y || y_rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  const bool mx = desc->act_format == MOK_ACT_MXFP8_E4M3;
+  if (mx && (!ring_scales || !act_scales)) return MOK_ERR_INVALID_ARG;
+  FfnArgs a{};
+  a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up); a.w_d = static_cast<const uint16_t*>(w_down);
+  a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
+  a.y = y; a.y_rows = y_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  return hip_status(launch_ffn(a, stream));
+}
+
+mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_assign,
+                       const float* topk_gate, int32_t T, int32_t k, int32_t H,
+                       const mok_tokens* out, int32_t* dev_status, hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 32 || H <= 0 || H % 8 != 0 || !tokens_ok(out, T)) return MOK_ERR_INVALID_ARG;
+  if (T > 0 && (!y || y_rows < 1 || !slot_of_assign || !topk_gate)) return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y, y_rows, slot_of_assign, topk_gate, T, k, H, out->part_ptr,
+                                   out->n_partitions, out->part_rows, dev_status, false, stream));
+}
+
+size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro) {
+  Plan p;
+  if (!desc_ok(desc) || T < 0 || n_macro < 1 || !make_plan(desc, T, n_macro, p)) return 0;
+  return p.total;
+}
+
+int32_t mok_forward_minibatch(const mok_layer_desc* desc, int32_t T) {
+  Plan p;
+  if (!desc_ok(desc) || T < 0 || !make_plan(desc, T, 1, p)) return 0;
+  return p.M;
+}
+
+mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
+                                   const int32_t* const* topk_idx, const float* const* topk_gate,
+                                   int32_t T, const mok_tokens* x, const void* w_gate_up,
+                                   const void* w_down, const mok_tokens* out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (!desc_ok(desc) || n_macro < 1 || T < 0 || !topk_idx || !topk_gate || !tokens_ok(x, T) ||
+      !w_gate_up || !w_down || !out || !ws)
+    return MOK_ERR_INVALID_ARG;
+  for (int m = 0; m < n_macro; ++m) {
+    if (T > 0 && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
+    if (!tokens_ok(&out[m], T)) return MOK_ERR_INVALID_ARG;
+  }
+  Plan p;
+  if (!make_plan(desc, T, n_macro, p)) return MOK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return MOK_ERR_WORKSPACE;
+
+  const mok_layer_desc& d = *desc;
+  const bool mx = d.act_format == MOK_ACT_MXFP8_E4M3;
+  int32_t* status = at<int32_t>(ws, p.off_status);
+  hipError_t err = hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, status, 64, 0);
+  if ((err = hipGetLastError()) != hipSuccess) return MOK_ERR_HIP;
+
+  SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
+  MacroBuffers mb[64];
+  const int nm_buf = n_macro < 64 ? n_macro : 64;
+  if (n_macro > 64) return MOK_ERR_UNSUPPORTED;
+  for (int m = 0; m < nm_buf; ++m) {
+    mb[m].counts = at<int32_t>(ws, p.off_counts + m * p.per_macro_counts);
+    mb[m].offsets = at<int32_t>(ws, p.off_offsets + m * p.per_macro_offsets);
+    mb[m].soa = at<int32_t>(ws, p.off_soa + m * p.per_macro_soa);
+    mb[m].aos = at<int32_t>(ws, p.off_aos + m * p.per_macro_aos);
+    mb[m].win = at<int32_t>(ws, p.off_win + m * p.per_macro_win);
+    mb[m].gate = topk_gate[m];
+    mb[m].y = at<uint16_t>(ws, p.off_y + static_cast<size_t>(m % p.n_ybuf) * p.cap * d.hidden * 2);
+    mb[m].out = out[m];
+  }
+  // Schedules and windows for every macrobatch first: they only read routing.
+  for (int m = 0; m < n_macro; ++m) {
+    if (T > 0) {
+      err = launch_schedule(topk_idx[m], p.A, d.expert_base, d.n_local, mb[m].counts,
+                            mb[m].offsets, mb[m].soa, mb[m].aos, sw, stream);
+    } else {
+      hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, stream, mb[m].offsets, d.n_local + 1, 0);
+      err = hipGetLastError();
+    }
+    if (err != hipSuccess) return MOK_ERR_HIP;
+    if ((err = launch_windows(mb[m].offsets, d.n_local, p.M, p.nwin, mb[m].win, stream)) != hipSuccess)
+      return MOK_ERR_HIP;
+    hipLaunchKernelGGL(k_capacity_check, dim3(1), dim3(64), 0, stream, mb[m].offsets, d.n_local,
+                       p.cap, status);
+    if ((err = hipGetLastError()) != hipSuccess) return MOK_ERR_HIP;
+  }
+
+  void* ring = at<void>(ws, p.off_ring);
+  uint8_t* ring_sc = mx ? at<uint8_t>(ws, p.off_ring_sc) : nullptr;
+  void* act = at<void>(ws, p.off_act);
+  uint8_t* act_sc = mx ? at<uint8_t>(ws, p.off_act_sc) : nullptr;
+
+  if (d.mode == MOK_MODE_PERSISTENT) {
+    PersistentArgs pa{};
+    pa.n_macro = n_macro; pa.mb = mb; pa.T = T; pa.k = d.top_k;
+    pa.H = d.hidden; pa.I = d.inter; pa.n_local = d.n_local; pa.act_format = d.act_format;
+    pa.M = p.M; pa.S = p.S; pa.nwin = p.nwin; pa.cap = p.cap;
+    pa.x = *x; pa.w_gu = static_cast<const uint16_t*>(w_gate_up);
+    pa.w_d = static_cast<const uint16_t*>(w_down);
+    pa.ring = ring; pa.ring_sc = ring_sc; pa.act = act; pa.act_sc = act_sc; pa.act_rows = p.act_rows;
+    pa.status = status; pa.pers_ws = at<void>(ws, p.off_pers);
+    pa.n_move = d.n_move_cus; pa.n_cus = device_cus();
+    mok_status st = launch_persistent(pa, stream);
+    return st;
+  }
+
+  for (int m = 0; m < n_macro; ++m) {
+    for (int b = 0; b < p.nwin; ++b) {
+      const int32_t s0 = b * p.M;
+      const int32_t s1 = static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(s0) + p.M, p.cap));
+      err = launch_gather(x->part_ptr, x->n_partitions, x->part_rows, d.hidden, d.top_k,
+                          mb[m].aos, mb[m].offsets, d.n_local, s0, s1, ring, ring_sc, p.S,
+                          d.act_format, status, stream);
+      if (err != hipSuccess) return MOK_ERR_HIP;
+      FfnArgs a{};
+      a.ring = ring; a.ring_scales = ring_sc; a.ring_slots = p.S;
+      a.offsets = mb[m].offsets; a.n_local = d.n_local; a.s_begin = s0; a.s_end = s1;
+      a.w_gu = static_cast<const uint16_t*>(w_gate_up); a.w_d = static_cast<const uint16_t*>(w_down);
+      a.act = act; a.act_scales = act_sc; a.act_rows = p.act_rows;
+      a.y = mb[m].y; a.y_rows = p.cap;
+      a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
+      if ((err = launch_ffn(a, stream)) != hipSuccess) return MOK_ERR_HIP;
+    }
+    err = launch_combine(mb[m].y, p.cap, mb[m].soa, mb[m].gate, T, d.top_k, d.hidden,
+                         mb[m].out.part_ptr, mb[m].out.n_partitions, mb[m].out.part_rows, status,
+                         true, stream);
+    if (err != hipSuccess) return MOK_ERR_HIP;
+  }
+  return MOK_OK;
+}
+
+mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
+                           const float* topk_gate, int32_t T, const mok_tokens* x,
+                           const void* w_gate_up, const void* w_down, const mok_tokens* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mok_moe_forward_batches(desc, 1, &topk_idx, &topk_gate, T, x, w_gate_up, w_down, out, ws,
+                                 ws_bytes, stream);
+}
+
+mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream) {
+  if (!ws || !status_host) return MOK_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOK_ERR_HIP;
+  if (hipMemcpy(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return MOK_ERR_HIP;
+  return MOK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,343 @@
+// gemm.hip -- the expert SwiGLU FFN as two grouped bf16 MFMA GEMMs.
+//
+// tahou.com MoK article: same-expert tokens are laid out contiguously so a
+// grouped GEMM can run over them (layout-planning paragraph); the expert FFN
+// is SwiGLU and MXFP8 activation quantisation is fused into the grouped GEMM
+// and SwiGLU instead of separate kernels (state-machine paragraph).
+//
+//   gate/up:  h = x . W_gu[e]^T  (K = H),  a = SiLU(h_gate) * h_up -> act
+//   down:     y = a . W_d[e]^T   (K = I)                          -> y
+//
+// Both operands are K-contiguous (token rows, nn.Linear weight rows), which is
+// what v_mfma_f32_32x32x16_bf16 wants: lane l feeds row (l % 32), k-run
+// 8*(l / 32) .. +7 of both A and B as one 16-byte LDS read.
+//
+// Tiling (gfx950: 160 KiB LDS, wave64, 4 SIMDs per CU):
+//   workgroup tile 256 x 256 x 64, 256 threads = 4 waves in 2 x 2, each wave
+//   128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane);
+//   A and B tiles double-buffered in LDS (4 x 32 KiB), rows of 128 bytes with
+//   the 16-byte chunk index XOR-ed by (row % 8) so the fragment reads of 8
+//   consecutive rows hit distinct banks; global loads of the next k-step are
+//   issued before the MFMAs of the current one.
+// Grouped M: the window's rows [s_begin, min(s_end, R)) are cut per expert
+// segment (offsets) into 256-row tiles; the grid is sized from the window
+// length (never from counts), and blocks past the last tile exit at once.
+// Ragged tails load a clamped valid row and mask the stores.
+// SwiGLU fusion: a gate/up tile takes 128 gate rows and the 128 up rows of the
+// same intermediate columns (64 + 64 per wave column), so each lane holds g and
+// u of the same (row, i) in accumulators (mi, ni) and (mi, ni + 2).
+#include "mok_internal.h"
+
+namespace mok {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kTileBytes = BM * BK * 2;        // 32 KiB per operand tile
+constexpr int kLoopLds = 4 * kTileBytes;       // A0 A1 B0 B1 in the main loop
+constexpr int kEpiLds = BM * (BN / 2 + 4) * 4;  // fp32 staging of a 256 x 128 tile (+pad)
+constexpr int kLdsBytes = kLoopLds > kEpiLds ? kLoopLds : kEpiLds;
+
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
+
+struct GemmParams {
+  const void* A;              // bf16 [a_rows][K] or E4M3 codes [a_rows][K]
+  const uint8_t* A_scales;    // [a_rows][K/32] when A is MXFP8
+  int32_t a_rows;
+  const uint16_t* W;          // [n_local][w_rows][K]
+  int64_t w_expert_stride;    // elements
+  int32_t K;
+  int32_t N;                  // output columns (I for gate/up, H for down)
+  int32_t I;                  // up-row offset for gate/up
+  void* C;                    // bf16 [c_rows][N] or E4M3 codes [c_rows][N]
+  uint8_t* C_scales;          // [c_rows][N/32]
+  int32_t c_rows;
+  const int32_t* offsets;
+  int32_t n_local;
+  int32_t s_begin, s_end;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a 128-byte-row tile
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// Finds the (expert, first row, row count) of linear m-tile `mt` of the window.
+__device__ __forceinline__ bool decode_mtile(const int32_t* __restrict__ offsets, int32_t n_local,
+                                             int32_t s_begin, int32_t s_end, int mt, int& e_out,
+                                             int& row0, int& nrows) {
+  const int32_t R = offsets[n_local];
+  const int32_t w0 = s_begin, w1 = s_end < R ? s_end : R;
+  if (w1 <= w0) return false;
+  for (int e = 0; e < n_local; ++e) {
+    int32_t lo = offsets[e], hi = offsets[e + 1];
+    lo = lo < w0 ? w0 : lo;
+    hi = hi > w1 ? w1 : hi;
+    if (hi <= lo) continue;
+    int nt = (hi - lo + BM - 1) / BM;
+    if (mt < nt) {
+      e_out = e;
+      row0 = lo + mt * BM;
+      nrows = (hi - row0) < BM ? (hi - row0) : BM;
+      return true;
+    }
+    mt -= nt;
+  }
+  return false;
+}
+
+template <bool A_MX, int EPI>
+__global__ __launch_bounds__(kThreads)
+void k_ffn_gemm(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+
+  int e, row0, nrows;
+  if (!decode_mtile(p.offsets, p.n_local, p.s_begin, p.s_end, blockIdx.y, e, row0, nrows)) return;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool swiglu = EPI != EPI_STORE_BF16;
+  // output columns of this tile: gate/up tiles cover 128 intermediate columns
+  const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);
+  const int K = p.K;
+  const int nk = K / BK;
+
+  // ---- global -> register load descriptors
+  // B: 256 weight rows x 8 chunks; thread: chunk tid % 8, rows tid / 8 + 32 i.
+  const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
+  const int bc = tid & 7;
+  const uint4* bsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int nb = (tid >> 3) + 32 * i;
+    int wrow;
+    if (swiglu) {
+      int wc = nb >> 7, q = nb & 127;
+      int icol = n0 + 64 * wc + (q & 63);
+      if (icol >= p.I) icol = p.I - 1;                 // clamp; masked at the store
+      wrow = (q < 64) ? icol : p.I + icol;
+    } else {
+      wrow = n0 + nb;
+      if (wrow >= p.N) wrow = p.N - 1;
+    }
+    bsrc[i] = reinterpret_cast<const uint4*>(Wexp + static_cast<int64_t>(wrow) * K) + bc;
+  }
+  const int b_lds = swz(tid >> 3, bc);                 // + 32*i*128 per i (row & 7 unchanged)
+
+  // A: bf16 rows -> 8 chunks per k-step; MX rows -> 4 chunks of 16 codes.
+  constexpr int A_LOADS = A_MX ? 4 : 8;
+  const void* asrc[A_LOADS];
+  int a_scale_row[A_LOADS];
+  int a_row_local[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    int r = A_MX ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
+    a_row_local[i] = r;
+    int rr = r < nrows ? r : nrows - 1;
+    int64_t ring_row = static_cast<int64_t>(row0 + rr) % p.a_rows;
+    a_scale_row[i] = static_cast<int>(ring_row);
+    if (A_MX) {
+      asrc[i] = static_cast<const uint8_t*>(p.A) + ring_row * K + (tid & 3) * 16;
+    } else {
+      asrc[i] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.A) + ring_row * K) + bc;
+    }
+  }
+
+  uint4 areg[A_LOADS], breg[8];
+  uint8_t asc[A_LOADS];
+  auto load_k = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) breg[i] = bsrc[i][kt * (BK / 8)];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      if (A_MX) {
+        areg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(asrc[i]) + kt * BK);
+        asc[i] = p.A_scales[static_cast<int64_t>(a_scale_row[i]) * (K / 32) + kt * 2 + ((tid & 3) >> 1)];
+      } else {
+        areg[i] = static_cast<const uint4*>(asrc[i])[kt * (BK / 8)];
+      }
+    }
+  };
+  auto store_k = [&](int buf) {
+    uint8_t* As = lds + buf * kTileBytes;
+    uint8_t* Bs = lds + (2 + buf) * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(Bs + b_lds + i * 32 * 128) = breg[i];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      if (A_MX) {
+        const int r = a_row_local[i], c16 = tid & 3;
+        const int E = static_cast<int>(asc[i]) - 127;
+        const uint32_t w[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t b0 = w[q] & 0xff, b1 = (w[q] >> 8) & 0xff, b2 = (w[q] >> 16) & 0xff, b3 = w[q] >> 24;
+          o[2 * q] = pack_bf16x2(e4m3_value(b0, E), e4m3_value(b1, E));
+          o[2 * q + 1] = pack_bf16x2(e4m3_value(b2, E), e4m3_value(b3, E));
+        }
+        *reinterpret_cast<uint4*>(As + swz(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(As + swz(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+      } else {
+        *reinterpret_cast<uint4*>(As + b_lds + i * 32 * 128) = areg[i];
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  load_k(0);
+  store_k(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int khalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_k(kt + 1);
+    const uint8_t* As = lds + buf * kTileBytes;
+    const uint8_t* Bs = lds + (2 + buf) * kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kc = 2 * ks + khalf;
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, kc));
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, kc));
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_k(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue, staged through LDS for 16-byte global stores.
+  // Accumulator element q of tile (mi, ni): row 32mi + 8(q/4) + 4(lane/32) + q%4,
+  // column 32ni + lane%32, within the wave's 128 x 128 block.
+  if (EPI == EPI_STORE_BF16) {
+    constexpr int LD = BN + 8;                         // bf16 elements per staged row
+    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          int r = 128 * wm + 32 * mi + 8 * (q >> 2) + 4 * khalf + (q & 3);
+          int c = 128 * wn + 32 * ni + frag_row;
+          st[r * LD + c] = f32_to_bf16(acc[mi][ni][q]);
+        }
+    __syncthreads();
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+    for (int idx = tid; idx < BM * (BN / 8); idx += kThreads) {
+      int r = idx / (BN / 8), c8 = idx % (BN / 8);
+      int col = n0 + c8 * 8;
+      if (r >= nrows || col >= p.N) continue;
+      int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+      *reinterpret_cast<uint4*>(C + crow * p.N + col) = *reinterpret_cast<const uint4*>(st + r * LD + c8 * 8);
+    }
+  } else {
+    constexpr int LD = BN / 2 + 4;                     // fp32 per staged row (128 i-columns)
+    float* st = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          float g = acc[mi][ni][q], u = acc[mi][ni + 2][q];
+          float a = g / (1.0f + expf(-g)) * u;
+          int r = 128 * wm + 32 * mi + 8 * (q >> 2) + 4 * khalf + (q & 3);
+          int c = 64 * wn + 32 * ni + frag_row;
+          st[r * LD + c] = a;
+        }
+    __syncthreads();
+    if (EPI == EPI_SWIGLU_BF16) {
+      uint16_t* C = static_cast<uint16_t*>(p.C);
+      for (int idx = tid; idx < BM * 16; idx += kThreads) {
+        int r = idx >> 4, c8 = idx & 15;
+        int col = n0 + c8 * 8;
+        if (r >= nrows || col >= p.N) continue;
+        const float* s = st + r * LD + c8 * 8;
+        uint4 o = make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
+                             pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
+        int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) = o;
+      }
+    } else {
+      uint8_t* C = static_cast<uint8_t*>(p.C);
+      for (int idx = tid; idx < BM * 4; idx += kThreads) {
+        int r = idx >> 2, b = idx & 3;
+        int col = n0 + b * 32;
+        if (r >= nrows || col >= p.N) continue;
+        const float* s = st + r * LD + b * 32;
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(s[q]));
+        const int E = mx_scale_exp(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3_code_scaled(s[4 * q], E) | (e4m3_code_scaled(s[4 * q + 1], E) << 8) |
+                 (e4m3_code_scaled(s[4 * q + 2], E) << 16) | (e4m3_code_scaled(s[4 * q + 3], E) << 24);
+        int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+        uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        p.C_scales[crow * (p.N / 32) + col / 32] = static_cast<uint8_t>(E + 127);
+      }
+    }
+  }
+}
+
+template <bool A_MX, int EPI>
+hipError_t launch_one(const GemmParams& gp, int n_tiles, int m_tiles, hipStream_t s) {
+  hipLaunchKernelGGL((k_ffn_gemm<A_MX, EPI>), dim3(n_tiles, m_tiles), dim3(kThreads), 0, s, gp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+  const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
+  if (span <= 0) return hipSuccess;
+  const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
+  const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
+
+  GemmParams g{};
+  g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
+  // gate/up: A = ring rows (K = H), B = W_gu, C = act (N = I)
+  g.A = a.ring; g.A_scales = a.ring_scales; g.a_rows = a.ring_slots;
+  g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
+  g.N = a.I; g.I = a.I;
+  g.C = a.act; g.C_scales = a.act_scales; g.c_rows = a.act_rows;
+  const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
+  hipError_t err = mx ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
+                      : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
+  if (err != hipSuccess) return err;
+  // down: A = act (K = I), B = W_d, C = y (N = H)
+  g.A = a.act; g.A_scales = a.act_scales; g.a_rows = a.act_rows;
+  g.W = a.w_d; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.I;
+  g.N = a.H; g.I = 0;
+  g.C = a.y; g.C_scales = nullptr; g.c_rows = a.y_rows;
+  const int n2 = (a.H + BN - 1) / BN;
+  return mx ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
+            : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+}
+
+}  // namespace mok

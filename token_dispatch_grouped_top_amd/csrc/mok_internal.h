@@ -1,0 +1,132 @@
+// mok_internal.h -- device helpers and launcher declarations shared by the
+// libmok HIP sources (gfx950 / CDNA4, wave64).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mok.h"
+
+namespace mok {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 on the bit pattern (finite inputs;
+// NaN is kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// --------------------------------------------------------- MXFP8 (E4M3)
+// OCP MX v1.0 block scale from the block's largest magnitude (fp32):
+// E = floor(log2 amax) - 8, clamped to [-127, 127]; zero block -> -127.
+// Read off the exponent field: amax below 2^-126 clamps to -127 anyway.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  int E = ef - 127 - 8;
+  return E < -127 ? -127 : E;
+}
+
+// E4M3 code of v * 2^-E: round to nearest even, saturate at 448, keep the
+// sign of v (also for results that round to zero).
+__device__ __forceinline__ uint32_t e4m3_code_scaled(float v, int E) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = __builtin_amdgcn_ldexpf(fabsf(v), -E);
+  uint32_t mag;
+  if (a >= 448.0f) {
+    mag = 0x7eu;
+  } else if (a < 0.015625f) {              // below 2^-6: subnormal quantum 2^-9
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 0..8; 8 == code of 2^-6
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7ffffu + ((u >> 20) & 1u);      // RNE to 3 mantissa bits
+    mag = (u >> 20) - ((127u - 7u) << 3);  // rebias exponent 127 -> 7
+    if (mag > 0x7eu) mag = 0x7eu;
+  }
+  return sign | mag;
+}
+
+// E4M3 code * 2^E as fp32 (exact; scale applied with v_ldexp_f32).
+__device__ __forceinline__ float e4m3_value(uint32_t c, int E) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mant = static_cast<float>(e == 0 ? m : (8u | m));
+  int ex = (e == 0 ? -9 : static_cast<int>(e) - 10) + E;
+  float v = __builtin_amdgcn_ldexpf(mant, ex);
+  return (c & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------ wave ops
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Lanes holding the same key as this lane (all 64 lanes must be active).
+__device__ __forceinline__ uint64_t match_key(uint32_t key, int nbits) {
+  uint64_t peers = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    uint64_t bal = __ballot((key >> b) & 1u);
+    peers &= ((key >> b) & 1u) ? bal : ~bal;
+  }
+  return peers;
+}
+
+// --------------------------------------------------------- device status
+__device__ __forceinline__ void set_status(int32_t* st, int32_t code) {
+  if (st) __hip_atomic_fetch_max(st, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------- launchers
+// All launchers return hipSuccess or the launch error.
+hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t* idx, float* gate, hipStream_t s);
+
+struct SchedWs {
+  int32_t* blk_counts;  // [n_local][nblk]
+  int32_t* blk_base;    // [n_local][nblk]
+  int32_t nblk;
+};
+size_t sched_ws_bytes(int64_t A, int32_t n_local);
+SchedWs sched_ws_carve(void* ws, int64_t A, int32_t n_local);
+hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, int32_t n_local,
+                           int32_t* counts, int32_t* offsets, int32_t* soa, int32_t* aos,
+                           const SchedWs& w, hipStream_t s);
+hipError_t launch_windows(const int32_t* offsets, int32_t n_local, int32_t M, int32_t nwin,
+                          int32_t* win_seg, hipStream_t s);
+
+hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_rows, int32_t H,
+                         int32_t k, const int32_t* aos, const int32_t* offsets, int32_t n_local,
+                         int32_t s_begin, int32_t s_end, void* ring, uint8_t* ring_scales,
+                         int32_t ring_slots, int32_t act_format, int32_t* status, hipStream_t s);
+
+hipError_t launch_combine(const void* y, int32_t y_rows, const int32_t* soa, const float* gate,
+                          int32_t T, int32_t k, int32_t H, void* const* out_ptr, int32_t n_part,
+                          int32_t part_rows, int32_t* status, bool abort_on_status,
+                          hipStream_t s);
+
+// Grouped GEMM pair of the expert FFN over slots [s_begin, min(s_end, R)).
+struct FfnArgs {
+  const void* ring; const uint8_t* ring_scales; int32_t ring_slots;
+  const int32_t* offsets; int32_t n_local; int32_t s_begin, s_end;
+  const uint16_t* w_gu; const uint16_t* w_d;
+  void* act; uint8_t* act_scales; int32_t act_rows;
+  void* y; int32_t y_rows;
+  int32_t H, I, act_format;
+};
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+}  // namespace mok

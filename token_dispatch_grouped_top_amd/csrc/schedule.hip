@@ -1,0 +1,214 @@
+// schedule.hip -- per-expert counts, offsets and the pull table, on device.
+//
+// tahou.com MoK article, layout-planning paragraph: count the tokens per
+// expert, then plan positions so that one expert's tokens are contiguous for
+// the grouped GEMM.  PyTorchKR wiki summary, key point on scheduling: the
+// {src_rank, src_index} pull schedule is built on the device with no sort and
+// no CPU-GPU exchange.  Reading of the slot order (not fixed by the pages):
+// stable in assignment id a = t*k + j, i.e. a counting sort.
+//
+// Three launches, no atomics on the data path, so the result is unique:
+//   count   -- each block takes a chunk of 4096 assignments; each wave takes
+//              1024 consecutive ones in 16 steps of 64 and groups equal keys
+//              with ballots on the key bits (match_key); the lowest lane of a
+//              group adds the group size to the wave's LDS histogram.
+//   scan    -- one block: per expert, exclusive scan over the blocks (one
+//              wave per expert, shuffles), then the exclusive scan over
+//              experts gives offsets; block bases = offsets + block prefix.
+//   scatter -- recount per wave, prefix over the block's waves, then each
+//              lane's slot = wave cursor + popcount(group & lanes below).
+#include "mok_internal.h"
+
+namespace mok {
+
+namespace {
+
+constexpr int kSchedThreads = 256;
+constexpr int kSchedWaves = kSchedThreads / kWave;
+constexpr int kStepsPerWave = 16;
+constexpr int kChunk = kSchedThreads * kStepsPerWave;  // 4096 assignments per block
+constexpr int kMaxLocal = 256;
+
+__device__ __forceinline__ uint32_t local_key(const int32_t* idx, int64_t a, int64_t A,
+                                              int32_t base, int32_t n_local) {
+  if (a >= A) return static_cast<uint32_t>(n_local);
+  int32_t e = idx[a] - base;
+  return (e >= 0 && e < n_local) ? static_cast<uint32_t>(e) : static_cast<uint32_t>(n_local);
+}
+
+__device__ __forceinline__ int key_bits(int32_t n_local) { return 32 - __clz(n_local); }
+
+// Per-wave histogram of the block's chunk into h[wave][e].
+__device__ void wave_histogram(const int32_t* __restrict__ idx, int64_t A, int32_t base,
+                               int32_t n_local, int32_t (*h)[kMaxLocal]) {
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int nbits = key_bits(n_local);
+  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kChunk + w * (kWave * kStepsPerWave);
+  for (int e = lane; e < n_local; e += kWave) h[w][e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int it = 0; it < kStepsPerWave; ++it) {
+    uint32_t key = local_key(idx, a0 + it * kWave + lane, A, base, n_local);
+    uint64_t peers = match_key(key, nbits);
+    bool leader = (peers & lanemask_lt()) == 0;
+    if (leader && key < static_cast<uint32_t>(n_local)) h[w][key] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(kSchedThreads)
+void k_sched_count(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
+                   int32_t nblk, int32_t* __restrict__ blk_counts) {
+  __shared__ int32_t h[kSchedWaves][kMaxLocal];
+  wave_histogram(idx, A, base, n_local, h);
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
+    int32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kSchedWaves; ++w) c += h[w][e];
+    blk_counts[static_cast<int64_t>(e) * nblk + blockIdx.x] = c;
+  }
+}
+
+// One block of 1024 threads; wave w scans experts w, w+16, ...
+__global__ __launch_bounds__(1024)
+void k_sched_scan(const int32_t* __restrict__ blk_counts, int32_t n_local, int32_t nblk,
+                  int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
+                  int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[kMaxLocal];
+  __shared__ int32_t off[kMaxLocal + 1];
+  const int w = threadIdx.x / kWave, lane = lane_id(), nw = blockDim.x / kWave;
+  for (int e = w; e < n_local; e += nw) {
+    const int32_t* c = blk_counts + static_cast<int64_t>(e) * nblk;
+    int32_t* b = blk_base + static_cast<int64_t>(e) * nblk;
+    int32_t run = 0;
+    for (int j0 = 0; j0 < nblk; j0 += kWave) {
+      int j = j0 + lane;
+      int32_t v = j < nblk ? c[j] : 0;
+      int32_t incl = v;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        int32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (j < nblk) b[j] = run + incl - v;
+      run += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) tot[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int e = 0; e < n_local; ++e) { off[e] = acc; acc += tot[e]; }
+    off[n_local] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= n_local; e += blockDim.x) {
+    offsets[e] = off[e];
+    if (e < n_local) counts[e] = tot[e];
+  }
+  for (int e = w; e < n_local; e += nw) {
+    int32_t* b = blk_base + static_cast<int64_t>(e) * nblk;
+    for (int j = lane; j < nblk; j += kWave) b[j] += off[e];
+  }
+}
+
+__global__ __launch_bounds__(kSchedThreads)
+void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
+                     int32_t nblk, const int32_t* __restrict__ blk_base,
+                     int32_t* __restrict__ soa, int32_t* __restrict__ aos) {
+  __shared__ int32_t h[kSchedWaves][kMaxLocal];
+  __shared__ int32_t cur[kSchedWaves][kMaxLocal];
+  wave_histogram(idx, A, base, n_local, h);
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
+    int32_t b = blk_base[static_cast<int64_t>(e) * nblk + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < kSchedWaves; ++w) { cur[w][e] = b; b += h[w][e]; }
+  }
+  __syncthreads();
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int nbits = key_bits(n_local);
+  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kChunk + w * (kWave * kStepsPerWave);
+  for (int it = 0; it < kStepsPerWave; ++it) {
+    const int64_t a = a0 + it * kWave + lane;
+    uint32_t key = local_key(idx, a, A, base, n_local);
+    uint64_t peers = match_key(key, nbits);
+    bool local = key < static_cast<uint32_t>(n_local);
+    int32_t c = local ? cur[w][key] : 0;
+    int32_t slot = c + __popcll(peers & lanemask_lt());
+    if (a < A) {
+      soa[a] = local ? slot : -1;
+      if (local) aos[slot] = static_cast<int32_t>(a);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (local && (peers & lanemask_lt()) == 0) cur[w][key] = c + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ void k_windows(const int32_t* __restrict__ offsets, int32_t n_local, int32_t M,
+                          int32_t nwin, int32_t* __restrict__ win_seg) {
+  const int64_t R = offsets[n_local];
+  const int64_t n = static_cast<int64_t>(nwin) * (n_local + 1);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int64_t b = i / (n_local + 1), e = i % (n_local + 1);
+    int64_t lo = b * M, hi = lo + M;
+    if (lo > R) lo = R;
+    if (hi > R) hi = R;
+    int64_t v = offsets[e];
+    v = v < lo ? lo : (v > hi ? hi : v);
+    win_seg[i] = static_cast<int32_t>(v);
+  }
+}
+
+}  // namespace
+
+size_t sched_ws_bytes(int64_t A, int32_t n_local) {
+  int64_t nblk = (A + kChunk - 1) / kChunk;
+  if (nblk < 1) nblk = 1;
+  return static_cast<size_t>(2 * nblk * n_local) * sizeof(int32_t) + 256;
+}
+
+SchedWs sched_ws_carve(void* ws, int64_t A, int32_t n_local) {
+  SchedWs w;
+  int64_t nblk = (A + kChunk - 1) / kChunk;
+  if (nblk < 1) nblk = 1;
+  w.nblk = static_cast<int32_t>(nblk);
+  w.blk_counts = static_cast<int32_t*>(ws);
+  w.blk_base = w.blk_counts + nblk * n_local;
+  return w;
+}
+
+hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, int32_t n_local,
+                           int32_t* counts, int32_t* offsets, int32_t* soa, int32_t* aos,
+                           const SchedWs& w, hipStream_t s) {
+  if (n_local > kMaxLocal) return hipErrorInvalidValue;
+  if (A > 0) {
+    hipLaunchKernelGGL(k_sched_count, dim3(w.nblk), dim3(kSchedThreads), 0, s, idx, A,
+                       expert_base, n_local, w.nblk, w.blk_counts);
+  } else {
+    hipLaunchKernelGGL(k_sched_count, dim3(1), dim3(kSchedThreads), 0, s, idx, A, expert_base,
+                       n_local, w.nblk, w.blk_counts);
+  }
+  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, s, w.blk_counts, n_local, w.nblk,
+                     w.blk_base, counts, offsets);
+  if (A > 0) {
+    hipLaunchKernelGGL(k_sched_scatter, dim3(w.nblk), dim3(kSchedThreads), 0, s, idx, A,
+                       expert_base, n_local, w.nblk, w.blk_base, soa, aos);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_windows(const int32_t* offsets, int32_t n_local, int32_t M, int32_t nwin,
+                          int32_t* win_seg, hipStream_t s) {
+  int64_t n = static_cast<int64_t>(nwin) * (n_local + 1);
+  if (n == 0) return hipSuccess;
+  int blocks = static_cast<int>((n + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_windows, dim3(blocks), dim3(256), 0, s, offsets, n_local, M, nwin,
+                     win_seg);
+  return hipGetLastError();
+}
+
+}  // namespace mok
