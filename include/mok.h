@@ -69,7 +69,7 @@ typedef enum {
 /* One GPU's share of one MoE layer. */
 typedef struct {
     int32_t hidden;       /* H; multiple of 64                                 */
-    int32_t inter;        /* I (expert intermediate); multiple of 128          */
+    int32_t inter;        /* I (expert intermediate); multiple of 64           */
     int32_t n_experts;    /* E, experts routed over                            */
     int32_t top_k;        /* k                                                 */
     int32_t expert_base;  /* local experts are [expert_base, expert_base+n_local) */
@@ -215,6 +215,10 @@ mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t s
 int32_t mok_forward_minibatch(const mok_layer_desc* desc, int32_t T);
 
 const char* mok_status_str(mok_status s);
+
+/* Text of the last HIP error a call on this host thread turned into
+ * MOK_ERR_HIP ("no error" if none). */
+const char* mok_last_hip_error(void);
 
 #ifdef __cplusplus
 }

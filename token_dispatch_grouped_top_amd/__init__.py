@@ -21,7 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libmok.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "mok.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m token_dispatch_grouped_top_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python token_dispatch_grouped_top_amd/build.py`")
+# torch ships its own HIP runtime under the same soname; importing torch first
+# makes libmok bind to that one, so torch's streams and allocations are valid
+# for the library's launches (loading libmok first would pull in a second copy).
+import torch  # noqa: E402,F401
+
 _lib = C.CDLL(LIB_PATH)
 
 MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE = 0, 1, 2, 3
@@ -66,6 +71,7 @@ _SIGS = {
     "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "mok_forward_minibatch": (_I32, [_DESC, _I32]),
     "mok_status_str": (C.c_char_p, [C.c_int]),
+    "mok_last_hip_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -98,6 +104,8 @@ def _stream(s) -> int:
 
 def _check(status: int, call: str) -> None:
     if status != MOK_OK:
+        if status == MOK_ERR_HIP:
+            call = f"{call} [{_lib.mok_last_hip_error().decode()}]"
         raise MokError(status, call)
 
 

@@ -1,9 +1,9 @@
 """Builds libmok.so (HIP, gfx950) in-tree with hipcc.
 
 Each csrc/*.hip file is compiled to an object under _build/ in parallel,
-then linked into token_dispatch_grouped_top_amd/libmok.so.  Run as a module
-(``python -m token_dispatch_grouped_top_amd.build``) or through
-``__graft_entry__.build()``.
+then linked into token_dispatch_grouped_top_amd/libmok.so.  Run it as a script
+(``python token_dispatch_grouped_top_amd/build.py``) or through
+``__graft_entry__.build()``; it does not import the package.
 """
 from __future__ import annotations
 

@@ -117,7 +117,13 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
 template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
 
-mok_status hip_status(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_HIP; }
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+mok_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOK_OK;
+  g_last_hip_error = e;
+  return MOK_ERR_HIP;
+}
 
 }  // namespace
 }  // namespace mok
@@ -263,7 +269,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
   int32_t* status = at<int32_t>(ws, p.off_status);
   hipError_t err = hipSuccess;
   hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, status, 64, 0);
-  if ((err = hipGetLastError()) != hipSuccess) return MOK_ERR_HIP;
+  if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
 
   SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
   MacroBuffers mb[64];
@@ -288,12 +294,12 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, stream, mb[m].offsets, d.n_local + 1, 0);
       err = hipGetLastError();
     }
-    if (err != hipSuccess) return MOK_ERR_HIP;
+    if (err != hipSuccess) return hip_status(err);
     if ((err = launch_windows(mb[m].offsets, d.n_local, p.M, p.nwin, mb[m].win, stream)) != hipSuccess)
-      return MOK_ERR_HIP;
+      return hip_status(err);
     hipLaunchKernelGGL(k_capacity_check, dim3(1), dim3(64), 0, stream, mb[m].offsets, d.n_local,
                        p.cap, status);
-    if ((err = hipGetLastError()) != hipSuccess) return MOK_ERR_HIP;
+    if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
   }
 
   void* ring = at<void>(ws, p.off_ring);
@@ -322,7 +328,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       err = launch_gather(x->part_ptr, x->n_partitions, x->part_rows, d.hidden, d.top_k,
                           mb[m].aos, mb[m].offsets, d.n_local, s0, s1, ring, ring_sc, p.S,
                           d.act_format, status, stream);
-      if (err != hipSuccess) return MOK_ERR_HIP;
+      if (err != hipSuccess) return hip_status(err);
       FfnArgs a{};
       a.ring = ring; a.ring_scales = ring_sc; a.ring_slots = p.S;
       a.offsets = mb[m].offsets; a.n_local = d.n_local; a.s_begin = s0; a.s_end = s1;
@@ -330,12 +336,12 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       a.act = act; a.act_scales = act_sc; a.act_rows = p.act_rows;
       a.y = mb[m].y; a.y_rows = p.cap;
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
-      if ((err = launch_ffn(a, stream)) != hipSuccess) return MOK_ERR_HIP;
+      if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
     err = launch_combine(mb[m].y, p.cap, mb[m].soa, mb[m].gate, T, d.top_k, d.hidden,
                          mb[m].out.part_ptr, mb[m].out.n_partitions, mb[m].out.part_rows, status,
                          true, stream);
-    if (err != hipSuccess) return MOK_ERR_HIP;
+    if (err != hipSuccess) return hip_status(err);
   }
   return MOK_OK;
 }
@@ -350,10 +356,11 @@ mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
 
 mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream) {
   if (!ws || !status_host) return MOK_ERR_INVALID_ARG;
-  if (hipStreamSynchronize(stream) != hipSuccess) return MOK_ERR_HIP;
-  if (hipMemcpy(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
-    return MOK_ERR_HIP;
-  return MOK_OK;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(status_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost);
+  return hip_status(e);
 }
+
+const char* mok_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
 
 }  // extern "C"
