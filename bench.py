@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the MoK forward MoE layer (libmok, MI355X).
+
+Workload: the hidden 7168 / expert intermediate 2048 expert share -- 8192
+routed rows for 8 local experts (of 384, top-8) pulled from a pool of
+72 source partitions x 1024 tokens in HBM, balanced counts, bf16, seeded
+synthetic data.  The route step runs on this GPU's own 1024 source tokens.
+
+One step = the whole hot path through the C-ABI on one stream:
+route -> schedule -> windows -> pull gather -> gate/up + SwiGLU grouped GEMM
+-> down grouped GEMM -> weighted combine.  HIP events between the calls (on
+the launch stream) give each kernel's duration; the dominant kernel (the
+gate/up grouped GEMM) is priced against the bf16 MFMA peak.  Inputs are
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  Extra reports go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "MoE fwd ms/layer + grouped-GEMM TFLOP/s, dispatch/combine GB/s (7168/2048)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows here)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_workload(name: str):
+    import workloads as W
+    if name == "kimi":
+        return W.kimi_share()
+    if name == "kimi_zipf_mxfp8":
+        return W.kimi_zipf_mxfp8()
+    if name == "mixtral":
+        return W.mixtral()
+    if name == "tiny":
+        return W.tiny()
+    raise ValueError(name)
+
+
+class Step:
+    """Buffers and the call sequence of one step of the layer."""
+
+    def __init__(self, dw, max_rows: int):
+        import torch
+        import token_dispatch_grouped_top_amd as mok
+        self.mok, self.dw, wl = mok, dw, dw.wl
+        self.cap = max_rows
+        self.desc = dw.desc(max_rows=max_rows)
+        self.M = mok.mok_forward_minibatch(self.desc, wl.T)
+        mx = wl.act_format == mok.MOK_ACT_MXFP8_E4M3
+        dev = "cuda"
+        A = wl.T * wl.k
+        self.route_T, self.route_E = dw.logits.shape
+        self.r_idx = torch.empty((self.route_T, wl.k), dtype=torch.int32, device=dev)
+        self.r_gate = torch.empty((self.route_T, wl.k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(wl.n_local, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(wl.n_local + 1, dtype=torch.int32, device=dev)
+        self.soa = torch.empty(A, dtype=torch.int32, device=dev)
+        self.aos = torch.empty(A, dtype=torch.int32, device=dev)
+        self.sched_ws = torch.empty(mok.mok_schedule_workspace_size(wl.T, wl.k, wl.n_local),
+                                    dtype=torch.uint8, device=dev)
+        self.nwin = -(-max_rows // self.M)
+        self.win = torch.empty((self.nwin, wl.n_local + 1), dtype=torch.int32, device=dev)
+        cap, H, I = max_rows, wl.H, wl.I
+        self.ring = torch.empty((cap, H), dtype=torch.uint8 if mx else torch.int16, device=dev)
+        self.ring_sc = torch.empty((cap, H // 32), dtype=torch.uint8, device=dev) if mx else None
+        self.act = torch.empty((cap, I), dtype=torch.uint8 if mx else torch.int16, device=dev)
+        self.act_sc = torch.empty((cap, I // 32), dtype=torch.uint8, device=dev) if mx else None
+        self.y = torch.empty((cap, H), dtype=torch.int16, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.names = ["route", "schedule", "gather", "gate_up", "down", "combine"]
+
+    def run(self, ev=None):
+        """The hot path; ev: list of len(names)+1 events recorded between the calls."""
+        mok, dw, wl = self.mok, self.dw, self.dw.wl
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        if wl.routing_from_logits:      # every token routed here
+            mok.mok_route_topk(dw.logits, self.route_T, self.route_E, wl.k, dw.topk_idx,
+                               dw.topk_gate)
+        else:                           # this GPU's own source tokens; the pool's routing is given
+            mok.mok_route_topk(dw.logits, self.route_T, self.route_E, wl.k, self.r_idx, self.r_gate)
+        rec(1)
+        idx, gate = dw.topk_idx, dw.topk_gate
+        mok.mok_build_schedule(idx, wl.T, wl.k, wl.expert_base, wl.n_local, self.counts,
+                               self.offsets, self.soa, self.aos, self.sched_ws)
+        mok.mok_build_windows(self.offsets, wl.n_local, self.M, self.nwin, self.win)
+        rec(2)
+        mok.mok_dispatch_gather(dw.x, wl.H, wl.k, self.aos, self.offsets, wl.n_local, 0, self.cap,
+                                self.ring, self.ring_sc, self.cap, wl.act_format, self.status)
+        rec(3)
+        mok.mok_expert_gate_up(self.desc, self.ring, self.ring_sc, self.cap, self.offsets, 0,
+                               self.cap, dw.w_gu, self.act, self.act_sc, self.cap)
+        rec(4)
+        mok.mok_expert_down(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0, self.cap,
+                            dw.w_d, self.y, self.cap)
+        rec(5)
+        mok.mok_combine(self.y, self.cap, self.soa, gate, wl.T, wl.k, wl.H, dw.outs[0],
+                        self.status)
+        rec(6)
+
+
+def cpu_baseline(wl, sample_rows: int):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Route and schedule run in full; gather, FFN and combine run for random
+    routed tokens until about `sample_rows` rows are covered, and their time
+    is scaled by R / rows.  Returns the estimated ms per layer."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    if wl.routing_from_logits:
+        idx, gate = oracle.route_topk(wl.logits, wl.k)
+    else:
+        idx, gate = wl.topk_idx, wl.topk_gate
+        oracle.route_topk(wl.logits, wl.k)
+    sch = oracle.build_schedule(idx, wl.expert_base, wl.n_local)
+    t1 = time.perf_counter()
+    soa = sch["slot_of_assign"].reshape(wl.T, wl.k)
+    routed = np.nonzero((soa >= 0).any(1))[0]
+    rng = np.random.default_rng(0)
+    toks, rows = [], 0
+    for t in rng.permutation(routed):
+        toks.append(t)
+        rows += int((soa[t] >= 0).sum())
+        if rows >= sample_rows:
+            break
+    toks = np.array(toks, np.int64)
+    s = soa[toks].reshape(-1)
+    slots = np.unique(s[s >= 0])
+    mx = wl.act_format == 1
+    t2 = time.perf_counter()
+    xr = oracle.gather_rows(wl.x, wl.k, sch["assign_of_slot"], slots, mx)
+    y = oracle.ffn_rows(xr, oracle.expert_of_slots(sch["offsets"], slots), wl.w_gu, wl.w_d, mx)
+    yr = np.full(sch["R"], -1, np.int64)
+    yr[slots] = np.arange(slots.size)
+    oracle.combine_tokens(y, yr, sch["slot_of_assign"], gate, toks, wl.k)
+    t3 = time.perf_counter()
+    est_s = (t1 - t0) + (t3 - t2) * sch["R"] / slots.size
+    return dict(value=est_s * 1e3, unit="ms/layer", cores=oracle.max_threads(), kind="oracle",
+                sample=(f"route+schedule in full ({(t1 - t0) * 1e3:.0f} ms); gather+FFN+combine "
+                        f"for {toks.size} tokens = {slots.size} of {sch['R']} rows in "
+                        f"{t3 - t2:.1f} s, scaled by R/rows"))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="kimi",
+                    choices=["kimi", "kimi_zipf_mxfp8", "mixtral", "tiny"])
+    ap.add_argument("--cpu-rows", type=int, default=1536,
+                    help="rows of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--sweep", action="store_true", help="also time the fused call per minibatch")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the layer on a single GPU; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported: run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import token_dispatch_grouped_top_amd as mok
+    from gpu_harness import DeviceWorkload, to_host
+
+    torch.cuda.set_device(0)
+    t = time.time()
+    wl = make_workload(args.workload)
+    log(f"[bench] workload {wl.name} generated in {time.time() - t:.1f} s")
+    dw = DeviceWorkload(wl)
+    max_rows = BENCH_MAX_ROWS if not wl.routing_from_logits else wl.T * wl.k
+    st = Step(dw, max_rows)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    n_ev = len(st.names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.run(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+           for j, n in enumerate(st.names)}
+    assert int(st.status.item()) == 0, "device status set during the benchmark"
+
+    R = int(to_host(st.offsets)[-1])
+    soa = to_host(st.soa).reshape(wl.T, wl.k)
+    T_out = int((soa >= 0).any(1).sum())
+    H, I = wl.H, wl.I
+    mx = wl.act_format == 1
+    flop_gu, flop_dn = 4.0 * R * H * I, 2.0 * R * H * I
+    b_out = (1 + 1 / 32) if mx else 2
+    disp_bytes = R * H * (2 + b_out) + R * 8
+    comb_bytes = R * H * 2 + T_out * H * 2 + wl.T * wl.k * 8
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    gu_tf, dn_tf = tf(flop_gu, per["gate_up"]), tf(flop_dn, per["down"])
+    gemm_tf = tf(flop_gu + flop_dn, per["gate_up"] + per["down"])
+    disp_gbs, comb_gbs = gbs(disp_bytes, per["gather"]), gbs(comb_bytes, per["combine"])
+
+    log(f"[bench] R={R} T_out={T_out} M={st.M} wall {wall_ms:.3f} ms/step; per call (ms): "
+        + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    log(f"[bench] gate/up {gu_tf:.0f} TF/s, down {dn_tf:.0f} TF/s, both {gemm_tf:.0f} TF/s; "
+        f"gather {disp_gbs:.0f} GB/s, combine {comb_gbs:.0f} GB/s")
+
+    fused = {}
+    if args.sweep and not wl.routing_from_logits:
+        for M in [0] + list(wl.minibatches):
+            d = dw.desc(max_rows=max_rows, minibatch=M)
+            ws = torch.empty(mok.mok_forward_workspace_size(d, wl.T, 1), dtype=torch.uint8,
+                             device="cuda")
+            idx, gate = dw.routing()
+            for _ in range(3):
+                mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+            e1.record()
+            torch.cuda.synchronize()
+            Mu = mok.mok_forward_minibatch(d, wl.T)
+            fused[str(Mu)] = round(e0.elapsed_time(e1) / 10, 4)
+            log(f"[bench] fused mok_moe_forward, M={Mu}: {fused[str(Mu)]:.4f} ms")
+
+    cpu = None
+    if args.cpu_rows > 0:
+        t = time.time()
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        log(f"[bench] cpu baseline: {cpu['value']:.0f} ms/layer est. ({time.time() - t:.1f} s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(wall_ms, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-act/bf16" if mx else "bf16",
+        "data": "synthetic (seeded; random-init weights, no dataset)",
+        "config": {"workload": wl.name, "pool_tokens": wl.T, "partitions": wl.n_partitions,
+                   "routed_rows": R, "tokens_out": T_out, "hidden": H, "inter": I,
+                   "experts": wl.E, "n_local": wl.n_local, "top_k": wl.k, "minibatch": st.M,
+                   "max_rows": max_rows, "path": "stream-ordered C-ABI calls"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up grouped GEMM + SwiGLU",
+                     "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
+        "gemm_tflops": {"gate_up": round(gu_tf, 1), "down": round(dn_tf, 1),
+                        "both": round(gemm_tf, 1),
+                        "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)},
+        "dispatch_GBps": round(disp_gbs, 1), "dispatch_frac_hbm": round(disp_gbs / PEAK_HBM_GBS, 4),
+        "combine_GBps": round(comb_gbs, 1), "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
+        "schedule_share": round((per["schedule"]) / wall_ms, 4),
+        "fused_forward_ms": fused or None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

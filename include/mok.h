@@ -165,6 +165,18 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring,
                           void* act, uint8_t* act_scales, int32_t act_rows,
                           void* y, int32_t y_rows, hipStream_t stream);
 
+/* The two grouped GEMMs of mok_expert_ffn as separate calls, same layouts:
+ * gate/up + SwiGLU (ring -> act) and down (act -> y). */
+mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
+                              const uint8_t* ring_scales, int32_t ring_slots,
+                              const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                              const void* w_gate_up, void* act, uint8_t* act_scales,
+                              int32_t act_rows, hipStream_t stream);
+mok_status mok_expert_down(const mok_layer_desc* desc, const void* act,
+                           const uint8_t* act_scales, int32_t act_rows,
+                           const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                           const void* w_down, void* y, int32_t y_rows, hipStream_t stream);
+
 /* Push combine + final weighted merge (article, push-combine and benchmark
  * scope paragraphs).  For each token t with at least one local assignment
  * (slot_of_assign[t*k+j] >= 0):

@@ -56,6 +56,8 @@ def lib():
         L.orc_gather_rows.argtypes = [P, i32, i32, P, P, i64, i32, P, P, P]
         L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P]
         L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i32, P, P]
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = C.c_int
         for f in ("orc_e4m3_encode_n", "orc_e4m3_decode_n", "orc_bf16_round_n",
                   "orc_mx_quantize", "orc_mx_dequantize", "orc_gather_rows",
                   "orc_ffn_rows", "orc_combine_tokens"):
@@ -70,6 +72,10 @@ def _p(a: Optional[np.ndarray]):
 
 def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- formats

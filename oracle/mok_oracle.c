@@ -410,3 +410,7 @@ ORC_API void orc_bf16_round_n(const double* v, int64_t n, uint16_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(v[i]);
 }
+
+/* Threads the OpenMP loops above run on. */
+#include <omp.h>
+ORC_API int orc_max_threads(void) { return omp_get_max_threads(); }

@@ -63,6 +63,8 @@ _SIGS = {
                                       _I32, _P, _P]),
     "mok_expert_ffn": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P,
                                  _I32, _P]),
+    "mok_expert_gate_up": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "mok_expert_down": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P]),
     "mok_combine": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _I32, _TOK, _P, _P]),
     "mok_forward_workspace_size": (_SZ, [_DESC, _I32, _I32]),
     "mok_moe_forward": (C.c_int, [_DESC, _P, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
@@ -178,6 +180,22 @@ def mok_expert_ffn(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, off
                                _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up), _ptr(w_down),
                                _ptr(act), _ptr(act_scales), act_rows, _ptr(y), y_rows,
                                _stream(stream)), "mok_expert_ffn")
+
+
+def mok_expert_gate_up(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, offsets,
+                       slot_begin: int, slot_end: int, w_gate_up, act, act_scales, act_rows: int,
+                       stream=None) -> None:
+    _check(_lib.mok_expert_gate_up(C.byref(desc), _ptr(ring), _ptr(ring_scales), ring_slots,
+                                   _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up),
+                                   _ptr(act), _ptr(act_scales), act_rows, _stream(stream)),
+           "mok_expert_gate_up")
+
+
+def mok_expert_down(desc: mok_layer_desc, act, act_scales, act_rows: int, offsets,
+                    slot_begin: int, slot_end: int, w_down, y, y_rows: int, stream=None) -> None:
+    _check(_lib.mok_expert_down(C.byref(desc), _ptr(act), _ptr(act_scales), act_rows,
+                                _ptr(offsets), slot_begin, slot_end, _ptr(w_down), _ptr(y),
+                                y_rows, _stream(stream)), "mok_expert_down")
 
 
 def mok_combine(y, y_rows: int, slot_of_assign, topk_gate, T: int, k: int, H: int, out: Tokens,

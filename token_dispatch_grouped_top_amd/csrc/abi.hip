@@ -227,6 +227,42 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
   return hip_status(launch_ffn(a, stream));
 }
 
+mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
+                              const uint8_t* ring_scales, int32_t ring_slots,
+                              const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                              const void* w_gate_up, void* act, uint8_t* act_scales,
+                              int32_t act_rows, hipStream_t stream) {
+  if (!desc_ok(desc) || !ring || ring_slots < 1 || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_gate_up || !act || act_rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  if (desc->act_format == MOK_ACT_MXFP8_E4M3 && (!ring_scales || !act_scales))
+    return MOK_ERR_INVALID_ARG;
+  FfnArgs a{};
+  a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up);
+  a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  return hip_status(launch_gate_up(a, stream));
+}
+
+mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const uint8_t* act_scales,
+                           int32_t act_rows, const int32_t* offsets, int32_t slot_begin,
+                           int32_t slot_end, const void* w_down, void* y, int32_t y_rows,
+                           hipStream_t stream) {
+  if (!desc_ok(desc) || !act || act_rows < 1 || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_down || !y || y_rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  if (desc->act_format == MOK_ACT_MXFP8_E4M3 && !act_scales) return MOK_ERR_INVALID_ARG;
+  FfnArgs a{};
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_d = static_cast<const uint16_t*>(w_down);
+  a.act = const_cast<void*>(act); a.act_scales = const_cast<uint8_t*>(act_scales);
+  a.act_rows = act_rows; a.y = y; a.y_rows = y_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  return hip_status(launch_down(a, stream));
+}
+
 mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_assign,
                        const float* topk_gate, int32_t T, int32_t k, int32_t H,
                        const mok_tokens* out, int32_t* dev_status, hipStream_t stream) {

@@ -313,31 +313,39 @@ hipError_t launch_one(const GemmParams& gp, int n_tiles, int m_tiles, hipStream_
 
 }  // namespace
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
   if (span <= 0) return hipSuccess;
   const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
-  const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
-
   GemmParams g{};
   g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
-  // gate/up: A = ring rows (K = H), B = W_gu, C = act (N = I)
   g.A = a.ring; g.A_scales = a.ring_scales; g.a_rows = a.ring_slots;
   g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
   g.N = a.I; g.I = a.I;
   g.C = a.act; g.C_scales = a.act_scales; g.c_rows = a.act_rows;
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
-  hipError_t err = mx ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
-                      : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
-  if (err != hipSuccess) return err;
-  // down: A = act (K = I), B = W_d, C = y (N = H)
+  return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
+                                             : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
+}
+
+hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
+  const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
+  if (span <= 0) return hipSuccess;
+  const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
+  GemmParams g{};
+  g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
   g.A = a.act; g.A_scales = a.act_scales; g.a_rows = a.act_rows;
   g.W = a.w_d; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.I;
   g.N = a.H; g.I = 0;
   g.C = a.y; g.C_scales = nullptr; g.c_rows = a.y_rows;
   const int n2 = (a.H + BN - 1) / BN;
-  return mx ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
-            : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+  return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
+                                             : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+}
+
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+  hipError_t err = launch_gate_up(a, s);
+  return err != hipSuccess ? err : launch_down(a, s);
 }
 
 }  // namespace mok

@@ -127,6 +127,8 @@ struct FfnArgs {
   void* y; int32_t y_rows;
   int32_t H, I, act_format;
 };
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 
 }  // namespace mok
