@@ -105,87 +105,46 @@ void k_ffn_gemm(const GemmParams p) {
   const int K = p.K;
   const int nk = K / BK;
 
-  // ---- global -> register load descriptors
-  // B: 256 weight rows x 8 chunks; thread: chunk tid % 8, rows tid / 8 + 32 i.
+  // ---- operand tiles: 256 rows x 64 k of bf16 = 32 KiB, rows of 128 bytes.
+  // Each wave instruction fills 1 KiB of LDS = 8 rows; lane l lands at
+  // physical chunk l % 8 of row 8*(l/8) within it, so it fetches the logical
+  // chunk (l % 8) ^ (row % 8): the XOR swizzle is applied on the global side.
+  // Thread rows: r_j = 32 j + tid / 8, j = 0..7 (same rows for A and B).
   const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
-  const int bc = tid & 7;
-  const uint4* bsrc[8];
+  const int lrow = tid >> 3;                                  // 0..31
+  const int lchunk = (lane & 7) ^ (lrow & 7);                 // logical 16-byte chunk
+  uint32_t boff[8];                                           // element offsets in Wexp
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int nb = (tid >> 3) + 32 * i;
+  for (int j = 0; j < 8; ++j) {
+    const int nb = lrow + 32 * j;
     int wrow;
     if (swiglu) {
-      int wc = nb >> 7, q = nb & 127;
+      // B rows 0..127 -> wave column 0, 128..255 -> 1; in each, 64 gate rows
+      // then the 64 up rows of the same intermediate columns.
+      const int wc = nb >> 7, q = nb & 127;
       int icol = n0 + 64 * wc + (q & 63);
-      if (icol >= p.I) icol = p.I - 1;                 // clamp; masked at the store
+      if (icol >= p.I) icol = p.I - 1;                        // clamp; masked at the store
       wrow = (q < 64) ? icol : p.I + icol;
     } else {
       wrow = n0 + nb;
       if (wrow >= p.N) wrow = p.N - 1;
     }
-    bsrc[i] = reinterpret_cast<const uint4*>(Wexp + static_cast<int64_t>(wrow) * K) + bc;
+    boff[j] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K) + lchunk * 8;
   }
-  const int b_lds = swz(tid >> 3, bc);                 // + 32*i*128 per i (row & 7 unchanged)
-
-  // A: bf16 rows -> 8 chunks per k-step; MX rows -> 4 chunks of 16 codes.
-  constexpr int A_LOADS = A_MX ? 4 : 8;
-  const void* asrc[A_LOADS];
-  int a_scale_row[A_LOADS];
-  int a_row_local[A_LOADS];
+  // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
+  const uint16_t* Abf = static_cast<const uint16_t*>(p.A);
+  const uint8_t* Amx = static_cast<const uint8_t*>(p.A);
+  uint32_t aoff[8];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    int r = A_MX ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
-    a_row_local[i] = r;
+  for (int j = 0; j < 8; ++j) {
+    int r = A_MX ? (tid >> 2) + 64 * (j & 3) : lrow + 32 * j;
     int rr = r < nrows ? r : nrows - 1;
-    int64_t ring_row = static_cast<int64_t>(row0 + rr) % p.a_rows;
-    a_scale_row[i] = static_cast<int>(ring_row);
-    if (A_MX) {
-      asrc[i] = static_cast<const uint8_t*>(p.A) + ring_row * K + (tid & 3) * 16;
-    } else {
-      asrc[i] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.A) + ring_row * K) + bc;
-    }
+    uint32_t ring_row = static_cast<uint32_t>((static_cast<int64_t>(row0) + rr) % p.a_rows);
+    aoff[j] = A_MX ? ring_row : ring_row * static_cast<uint32_t>(K) + lchunk * 8;
   }
 
-  uint4 areg[A_LOADS], breg[8];
-  uint8_t asc[A_LOADS];
-  auto load_k = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) breg[i] = bsrc[i][kt * (BK / 8)];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      if (A_MX) {
-        areg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(asrc[i]) + kt * BK);
-        asc[i] = p.A_scales[static_cast<int64_t>(a_scale_row[i]) * (K / 32) + kt * 2 + ((tid & 3) >> 1)];
-      } else {
-        areg[i] = static_cast<const uint4*>(asrc[i])[kt * (BK / 8)];
-      }
-    }
-  };
-  auto store_k = [&](int buf) {
-    uint8_t* As = lds + buf * kTileBytes;
-    uint8_t* Bs = lds + (2 + buf) * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(Bs + b_lds + i * 32 * 128) = breg[i];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      if (A_MX) {
-        const int r = a_row_local[i], c16 = tid & 3;
-        const int E = static_cast<int>(asc[i]) - 127;
-        const uint32_t w[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t b0 = w[q] & 0xff, b1 = (w[q] >> 8) & 0xff, b2 = (w[q] >> 16) & 0xff, b3 = w[q] >> 24;
-          o[2 * q] = pack_bf16x2(e4m3_value(b0, E), e4m3_value(b1, E));
-          o[2 * q + 1] = pack_bf16x2(e4m3_value(b2, E), e4m3_value(b3, E));
-        }
-        *reinterpret_cast<uint4*>(As + swz(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(As + swz(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
-      } else {
-        *reinterpret_cast<uint4*>(As + b_lds + i * 32 * 128) = areg[i];
-      }
-    }
-  };
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto lds_tile = [&](int which, int buf) { return lds + (which * 2 + buf) * kTileBytes; };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -195,36 +154,93 @@ void k_ffn_gemm(const GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  load_k(0);
-  store_k(0);
-  __syncthreads();
-
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
+  uint4 amx[4];
+  uint32_t amx_sc[4];
+
+  // issue the (asynchronous) loads of k-step kt into LDS buffer buf
+#define MOK_ISSUE_LOADS(kt, buf)                                                             \
+  do {                                                                                       \
+    uint8_t* Bs_ = lds_tile(1, buf);                                                         \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                            \
+      __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK,                           \
+                                       (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, 0, 0);  \
+    if (!A_MX) {                                                                             \
+      uint8_t* As_ = lds_tile(0, buf);                                                       \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
+        __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK,                          \
+                                         (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
+    } else {                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
+        amx[j] = *reinterpret_cast<const uint4*>(Amx + static_cast<int64_t>(aoff[j]) * K +   \
+                                                 (kt) * BK + (tid & 3) * 16);                \
+        amx_sc[j] = p.A_scales[static_cast<int64_t>(aoff[j]) * (K / 32) + (kt) * 2 +         \
+                               ((tid & 3) >> 1)];                                            \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+
+  // MXFP8 A: dequantise the staged codes to bf16 into LDS buffer buf
+#define MOK_STORE_AMX(buf)                                                                   \
+  do {                                                                                       \
+    uint8_t* As_ = lds_tile(0, buf);                                                         \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
+      const int r = (tid >> 2) + 64 * j, c16 = tid & 3;                                      \
+      const int E = static_cast<int>(amx_sc[j]) - 127;                                       \
+      const uint32_t w4[4] = {amx[j].x, amx[j].y, amx[j].z, amx[j].w};                       \
+      uint32_t o[8];                                                                         \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
+        o[2 * q] = pack_bf16x2(e4m3_value(w4[q] & 0xff, E), e4m3_value((w4[q] >> 8) & 0xff, E)); \
+        o[2 * q + 1] = pack_bf16x2(e4m3_value((w4[q] >> 16) & 0xff, E), e4m3_value(w4[q] >> 24, E)); \
+      }                                                                                      \
+      *reinterpret_cast<uint4*>(As_ + swz(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]); \
+      *reinterpret_cast<uint4*>(As_ + swz(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]); \
+    }                                                                                        \
+  } while (0)
+
+  MOK_ISSUE_LOADS(0, 0);
+  if (A_MX) MOK_STORE_AMX(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_k(kt + 1);
-    const uint8_t* As = lds + buf * kTileBytes;
-    const uint8_t* Bs = lds + (2 + buf) * kTileBytes;
+    const bool more = kt + 1 < nk;
+    if (more) MOK_ISSUE_LOADS(kt + 1, buf ^ 1);
+    const uint8_t* As = lds_tile(0, buf);
+    const uint8_t* Bs = lds_tile(1, buf);
+    bf16x8_t af[2][4], bfr[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      af[0][mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, khalf));
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      bfr[0][ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, khalf));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = 2 * ks + khalf;
-      bf16x8_t af[4], bfr[4];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+        const int kc = 2 * (ks + 1) + khalf;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, kc));
+        for (int mi = 0; mi < 4; ++mi)
+          af[cur ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, kc));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, kc));
+        for (int ni = 0; ni < 4; ++ni)
+          bfr[cur ^ 1][ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, kc));
+      }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_k(buf ^ 1);
+    if (more && A_MX) MOK_STORE_AMX(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+#undef MOK_ISSUE_LOADS
+#undef MOK_STORE_AMX
 
   // ---- epilogue, staged through LDS for 16-byte global stores.
   // Accumulator element q of tile (mi, ni): row 32mi + 8(q/4) + 4(lane/32) + q%4,
