@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="rows of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="also time the fused call per minibatch")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 3 times (counter scale)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -181,6 +183,15 @@ def main():
     from gpu_harness import DeviceWorkload, to_host
 
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "reps": 3}), flush=True)
+        return
     t = time.time()
     wl = make_workload(args.workload)
     log(f"[bench] workload {wl.name} generated in {time.time() - t:.1f} s")

@@ -39,7 +39,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * BK * 2;        // 32 KiB per operand tile
 constexpr int kLoopLds = 4 * kTileBytes;       // A0 A1 B0 B1 in the main loop
-constexpr int kEpiLds = BM * (BN / 2 + 4) * 4;  // fp32 staging of a 256 x 128 tile (+pad)
+constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf16 / 256 x 128 fp32
 constexpr int kLdsBytes = kLoopLds > kEpiLds ? kLoopLds : kEpiLds;
 
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
@@ -59,32 +59,58 @@ struct GemmParams {
   const int32_t* offsets;
   int32_t n_local;
   int32_t s_begin, s_end;
+  int32_t n_tiles;            // output column tiles
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {   // byte offset in a 128-byte-row tile
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+// Byte offset of 16-byte chunk `chunk` of `row` in a tile of 128-byte rows.
+// The chunk index is XOR-ed with (row % 8) ^ ((row / 8) % 2): for 16
+// consecutive rows reading the same logical chunk, the 16-byte bank groups
+// are all distinct whether the LDS serves 8 or 16 lanes of a b128 read per
+// cycle, so the MFMA fragment reads are conflict-free.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ swz_key(row)) << 4);
 }
 
-// Finds the (expert, first row, row count) of linear m-tile `mt` of the window.
-__device__ __forceinline__ bool decode_mtile(const int32_t* __restrict__ offsets, int32_t n_local,
-                                             int32_t s_begin, int32_t s_end, int mt, int& e_out,
-                                             int& row0, int& nrows) {
+// Tile order and placement.  Tiles are numbered expert by expert; inside an
+// expert, n-tile major and m-tile minor, so the workgroups running at the same
+// time share the expert's A rows and a few weight tiles.  Workgroup ids are
+// dealt to the 8 XCDs round-robin (id % 8); each XCD is given a contiguous run
+// of tile numbers, so an expert's operands are fetched into one XCD's L2
+// instead of all eight.  Returns false for workgroups past the last tile.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t n_local,
+                                            int32_t s_begin, int32_t s_end, int n_tiles, int bid,
+                                            int& e_out, int& row0, int& nrows, int& ntile) {
   const int32_t R = offsets[n_local];
   const int32_t w0 = s_begin, w1 = s_end < R ? s_end : R;
   if (w1 <= w0) return false;
+  int total = 0;
   for (int e = 0; e < n_local; ++e) {
-    int32_t lo = offsets[e], hi = offsets[e + 1];
-    lo = lo < w0 ? w0 : lo;
-    hi = hi > w1 ? w1 : hi;
+    int32_t lo = offsets[e] < w0 ? w0 : offsets[e];
+    int32_t hi = offsets[e + 1] > w1 ? w1 : offsets[e + 1];
+    if (hi > lo) total += (hi - lo + BM - 1) / BM;
+  }
+  total *= n_tiles;
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = bid % kXcds, i = bid / kXcds;
+  if (i >= q + (x < r ? 1 : 0)) return false;
+  int t = x * q + (x < r ? x : r) + i;
+  for (int e = 0; e < n_local; ++e) {
+    int32_t lo = offsets[e] < w0 ? w0 : offsets[e];
+    int32_t hi = offsets[e + 1] > w1 ? w1 : offsets[e + 1];
     if (hi <= lo) continue;
-    int nt = (hi - lo + BM - 1) / BM;
-    if (mt < nt) {
+    const int mt = (hi - lo + BM - 1) / BM;
+    if (t < mt * n_tiles) {
+      const int m = t % mt;
+      ntile = t / mt;
       e_out = e;
-      row0 = lo + mt * BM;
+      row0 = lo + m * BM;
       nrows = (hi - row0) < BM ? (hi - row0) : BM;
       return true;
     }
-    mt -= nt;
+    t -= mt * n_tiles;
   }
   return false;
 }
@@ -94,14 +120,16 @@ __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
-  int e, row0, nrows;
-  if (!decode_mtile(p.offsets, p.n_local, p.s_begin, p.s_end, blockIdx.y, e, row0, nrows)) return;
+  int e, row0, nrows, ntile;
+  if (!decode_tile(p.offsets, p.n_local, p.s_begin, p.s_end, p.n_tiles, blockIdx.x, e, row0, nrows,
+                   ntile))
+    return;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave >> 1, wn = wave & 1;
   const bool swiglu = EPI != EPI_STORE_BF16;
   // output columns of this tile: gate/up tiles cover 128 intermediate columns
-  const int n0 = blockIdx.x * (swiglu ? BN / 2 : BN);
+  const int n0 = ntile * (swiglu ? BN / 2 : BN);
   const int K = p.K;
   const int nk = K / BK;
 
@@ -112,7 +140,7 @@ void k_ffn_gemm(const GemmParams p) {
   // Thread rows: r_j = 32 j + tid / 8, j = 0..7 (same rows for A and B).
   const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
   const int lrow = tid >> 3;                                  // 0..31
-  const int lchunk = (lane & 7) ^ (lrow & 7);                 // logical 16-byte chunk
+  const int lchunk = (lane & 7) ^ swz_key(lrow);              // logical 16-byte chunk
   uint32_t boff[8];                                           // element offsets in Wexp
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -199,119 +227,157 @@ void k_ffn_gemm(const GemmParams p) {
     }                                                                                        \
   } while (0)
 
+  // Pipeline.  LDS holds two k-steps (A+B, 64 KiB each).  The barrier of
+  // k-step kt sits after every wave has its last fragments of kt in registers
+  // and before their MFMAs, so (1) the loads of kt+2 are issued into the freed
+  // buffer as early as possible -- almost two k-steps ahead -- and (2) the
+  // first fragments of kt+1 are read while the last MFMAs of kt run.
+#define MOK_FRAGS(dst, buf_ptrA, buf_ptrB, ks_)                                              \
+  do {                                                                                       \
+    const int kc_ = 2 * (ks_) + khalf;                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
+      af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((buf_ptrA) + swz(128 * wm + 32 * mi + frag_row, kc_)); \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
+      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((buf_ptrB) + swz(128 * wn + 32 * ni + frag_row, kc_)); \
+  } while (0)
+#define MOK_MMA(src)                                                                         \
+  do {                                                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
+      _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                       \
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[src][ni], af[src][mi], acc[mi][ni], 0, 0, 0); \
+  } while (0)
+
   MOK_ISSUE_LOADS(0, 0);
-  if (A_MX) MOK_STORE_AMX(0);
+  if (A_MX) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    MOK_STORE_AMX(0);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (nk > 1) MOK_ISSUE_LOADS(1, 1);
 
+  bf16x8_t af[2][4], bfr[2][4];
+  MOK_FRAGS(0, lds_tile(0, 0), lds_tile(1, 0), 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) MOK_ISSUE_LOADS(kt + 1, buf ^ 1);
     const uint8_t* As = lds_tile(0, buf);
     const uint8_t* Bs = lds_tile(1, buf);
-    bf16x8_t af[2][4], bfr[2][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      af[0][mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, khalf));
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      bfr[0][ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, khalf));
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
-        const int kc = 2 * (ks + 1) + khalf;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[cur ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(As + swz(128 * wm + 32 * mi + frag_row, kc));
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          bfr[cur ^ 1][ni] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(128 * wn + 32 * ni + frag_row, kc));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0, 0);
+    MOK_FRAGS(1, As, Bs, 1);
+    MOK_MMA(0);
+    MOK_FRAGS(0, As, Bs, 2);
+    MOK_MMA(1);
+    MOK_FRAGS(1, As, Bs, 3);
+    MOK_MMA(0);
+    if (kt + 1 < nk) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of kt+1 landed
+      if (A_MX) MOK_STORE_AMX(buf ^ 1);
+      __syncthreads();                                     // all of kt+1 landed; buf is free
+      if (kt + 2 < nk) MOK_ISSUE_LOADS(kt + 2, buf);
+      MOK_FRAGS(0, lds_tile(0, buf ^ 1), lds_tile(1, buf ^ 1), 0);
     }
-    if (more && A_MX) MOK_STORE_AMX(buf ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    MOK_MMA(1);
   }
+#undef MOK_FRAGS
+#undef MOK_MMA
+  __syncthreads();                                         // LDS is reused by the epilogue
 #undef MOK_ISSUE_LOADS
 #undef MOK_STORE_AMX
 
   // ---- epilogue, staged through LDS for 16-byte global stores.
-  // Accumulator element q of tile (mi, ni): row 32mi + 8(q/4) + 4(lane/32) + q%4,
-  // column 32ni + lane%32, within the wave's 128 x 128 block.
+  // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
+  // accumulator element q of tile (mi, ni) is token row 32mi + lane%32 and
+  // output column 32ni + 8(q/4) + 4(lane/32) + q%4 of the wave's 128 x 128
+  // block, so each lane holds 4 consecutive columns of one row and writes
+  // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
+  // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
+  // the row-wise reads back are both free of bank conflicts.
+  const int erow = 128 * wm + frag_row;                  // + 32 mi
   if (EPI == EPI_STORE_BF16) {
-    constexpr int LD = BN + 8;                         // bf16 elements per staged row
-    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
+    constexpr int RB = BN * 2;                             // bytes per staged row
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          int r = 128 * wm + 32 * mi + 8 * (q >> 2) + 4 * khalf + (q & 3);
-          int c = 128 * wn + 32 * ni + frag_row;
-          st[r * LD + c] = f32_to_bf16(acc[mi][ni][q]);
+        for (int g = 0; g < 4; ++g) {
+          const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
+          const uint2 v = make_uint2(pack_bf16x2(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1]),
+                                     pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]));
+          *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
         }
+    }
     __syncthreads();
     uint16_t* C = static_cast<uint16_t*>(p.C);
     for (int idx = tid; idx < BM * (BN / 8); idx += kThreads) {
-      int r = idx / (BN / 8), c8 = idx % (BN / 8);
-      int col = n0 + c8 * 8;
+      const int r = idx / (BN / 8), k = idx % (BN / 8);
+      const int col = n0 + k * 8;
       if (r >= nrows || col >= p.N) continue;
-      int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
-      *reinterpret_cast<uint4*>(C + crow * p.N + col) = *reinterpret_cast<const uint4*>(st + r * LD + c8 * 8);
+      const int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+      *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+          *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
     }
   } else {
-    constexpr int LD = BN / 2 + 4;                     // fp32 per staged row (128 i-columns)
-    float* st = reinterpret_cast<float*>(lds);
+    // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
+    // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
+    constexpr bool MXO = EPI == EPI_SWIGLU_MX;
+    constexpr int RB = MXO ? (BN / 2) * 4 : (BN / 2) * 2;  // staged row: 128 fp32 or bf16
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          float g = acc[mi][ni][q], u = acc[mi][ni + 2][q];
-          float a = g / (1.0f + expf(-g)) * u;
-          int r = 128 * wm + 32 * mi + 8 * (q >> 2) + 4 * khalf + (q & 3);
-          int c = 64 * wn + 32 * ni + frag_row;
-          st[r * LD + c] = a;
+        for (int g = 0; g < 4; ++g) {
+          float a[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = acc[mi][ni][4 * g + j], uv = acc[mi][ni + 2][4 * g + j];
+            a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          }
+          const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if (MXO) {
+            *reinterpret_cast<float4*>(lds + r * RB + (((i >> 2) ^ (r & 15)) << 4)) =
+                make_float4(a[0], a[1], a[2], a[3]);
+          } else {
+            *reinterpret_cast<uint2*>(lds + r * RB + (((i >> 3) ^ (r & 15)) << 4) + ((i >> 2) & 1) * 8) =
+                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+          }
         }
+    }
     __syncthreads();
-    if (EPI == EPI_SWIGLU_BF16) {
+    if (!MXO) {
       uint16_t* C = static_cast<uint16_t*>(p.C);
       for (int idx = tid; idx < BM * 16; idx += kThreads) {
-        int r = idx >> 4, c8 = idx & 15;
-        int col = n0 + c8 * 8;
+        const int r = idx >> 4, k = idx & 15;
+        const int col = n0 + k * 8;
         if (r >= nrows || col >= p.N) continue;
-        const float* s = st + r * LD + c8 * 8;
-        uint4 o = make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
-                             pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
-        int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
-        *reinterpret_cast<uint4*>(C + crow * p.N + col) = o;
+        const int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
       }
     } else {
       uint8_t* C = static_cast<uint8_t*>(p.C);
       for (int idx = tid; idx < BM * 4; idx += kThreads) {
-        int r = idx >> 2, b = idx & 3;
-        int col = n0 + b * 32;
+        const int r = idx >> 2, b = idx & 3;
+        const int col = n0 + b * 32;
         if (r >= nrows || col >= p.N) continue;
-        const float* s = st + r * LD + b * 32;
+        float v[32];
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const float4 f = *reinterpret_cast<const float4*>(lds + r * RB + (((8 * b + c4) ^ (r & 15)) << 4));
+          v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
+        }
         float amax = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(s[q]));
+        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
         const int E = mx_scale_exp(amax);
         uint32_t w[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          w[q] = e4m3_code_scaled(s[4 * q], E) | (e4m3_code_scaled(s[4 * q + 1], E) << 8) |
-                 (e4m3_code_scaled(s[4 * q + 2], E) << 16) | (e4m3_code_scaled(s[4 * q + 3], E) << 24);
-        int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
+          w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
+                 (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
+        const int64_t crow = static_cast<int64_t>(row0 + r) % p.c_rows;
         uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -322,8 +388,9 @@ void k_ffn_gemm(const GemmParams p) {
 }
 
 template <bool A_MX, int EPI>
-hipError_t launch_one(const GemmParams& gp, int n_tiles, int m_tiles, hipStream_t s) {
-  hipLaunchKernelGGL((k_ffn_gemm<A_MX, EPI>), dim3(n_tiles, m_tiles), dim3(kThreads), 0, s, gp);
+hipError_t launch_one(GemmParams gp, int n_tiles, int m_tiles, hipStream_t s) {
+  gp.n_tiles = n_tiles;
+  hipLaunchKernelGGL((k_ffn_gemm<A_MX, EPI>), dim3(n_tiles * m_tiles), dim3(kThreads), 0, s, gp);
   return hipGetLastError();
 }
 
