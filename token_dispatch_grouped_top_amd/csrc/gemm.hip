@@ -10,15 +10,20 @@
 //
 // Both operands are K-contiguous (token rows, nn.Linear weight rows), which is
 // what v_mfma_f32_32x32x16_bf16 wants: lane l feeds row (l % 32), k-run
-// 8*(l / 32) .. +7 of both A and B as one 16-byte LDS read.
+// 8*(l / 32) .. +7 of both operands as one 16-byte LDS read.
 //
 // Tiling (gfx950: 160 KiB LDS, wave64, 4 SIMDs per CU):
-//   workgroup tile 256 x 256 x 64, 256 threads = 4 waves in 2 x 2, each wave
-//   128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane);
-//   A and B tiles double-buffered in LDS (4 x 32 KiB), rows of 128 bytes with
-//   the 16-byte chunk index XOR-ed by (row % 8) so the fragment reads of 8
-//   consecutive rows hit distinct banks; global loads of the next k-step are
-//   issued before the MFMAs of the current one.
+//   workgroup tile 256 x 256, 256 threads = 4 waves in 2 x 2, each wave
+//   128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane).
+//   Operand tiles stream through an LDS ring of NS k-steps; NS-1 of them are
+//   in flight while one is consumed, because these GEMMs are bound by how
+//   much load latency the LDS can cover, not by HBM bandwidth:
+//     bf16 A:  BK = 32, NS = 5 (5 x 32 KiB = 160 KiB, 128 KiB in flight);
+//     MXFP8 A: BK = 64, NS = 2, A staged through registers and dequantised.
+//   Loads go global -> LDS directly (global_load_lds_dwordx4): no staging
+//   registers, no ds_write.  Rows keep their 16-byte chunks XOR-swizzled so the
+//   fragment reads of 16 consecutive rows hit distinct banks; the swizzle is
+//   applied on the global side of the loads.
 // Grouped M: the window's rows [s_begin, min(s_end, R)) are cut per expert
 // segment (offsets) into 256-row tiles; the grid is sized from the window
 // length (never from counts), and blocks past the last tile exit at once.
@@ -35,12 +40,33 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = BM * BK * 2;        // 32 KiB per operand tile
-constexpr int kLoopLds = 4 * kTileBytes;       // A0 A1 B0 B1 in the main loop
 constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf16 / 256 x 128 fp32
-constexpr int kLdsBytes = kLoopLds > kEpiLds ? kLoopLds : kEpiLds;
+
+// Pipeline shape per A-operand format.
+template <bool A_MX> struct Pipe;
+template <> struct Pipe<false> { static constexpr int BK = 32, NS = 5; };
+template <> struct Pipe<true> { static constexpr int BK = 64, NS = 2; };
+
+template <bool A_MX> struct Geo {
+  static constexpr int BK = Pipe<A_MX>::BK, NS = Pipe<A_MX>::NS;
+  static constexpr int ROWB = BK * 2;                 // bytes per LDS tile row
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int TILEB = BM * ROWB;             // one operand tile
+  static constexpr int STAGEB = 2 * TILEB;            // A + B
+  static constexpr int RSTEP = 2048 / BK;             // row step between a thread's loads
+  static constexpr int NLOAD = 256 / RSTEP;           // loads per thread per operand tile
+  static constexpr int LOOP_LDS = NS * STAGEB;
+  static constexpr int LDS = LOOP_LDS > kEpiLds ? LOOP_LDS : kEpiLds;
+  // chunk XOR key: conflict-free b128 reads of 16 consecutive rows at one logical chunk
+  static __device__ __forceinline__ int key(int row) {
+    return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+  }
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ key(row)) << 4);
+  }
+};
 
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
 
@@ -61,16 +87,6 @@ struct GemmParams {
   int32_t s_begin, s_end;
   int32_t n_tiles;            // output column tiles
 };
-
-// Byte offset of 16-byte chunk `chunk` of `row` in a tile of 128-byte rows.
-// The chunk index is XOR-ed with (row % 8) ^ ((row / 8) % 2): for 16
-// consecutive rows reading the same logical chunk, the 16-byte bank groups
-// are all distinct whether the LDS serves 8 or 16 lanes of a b128 read per
-// cycle, so the MFMA fragment reads are conflict-free.
-__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ swz_key(row)) << 4);
-}
 
 // Tile order and placement.  Tiles are numbered expert by expert; inside an
 // expert, n-tile major and m-tile minor, so the workgroups running at the same
@@ -115,10 +131,17 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
   return false;
 }
 
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <bool A_MX, int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  using G = Geo<A_MX>;
+  constexpr int BK = G::BK, NS = G::NS, CPR = G::CPR;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS];
 
   int e, row0, nrows, ntile;
   if (!decode_tile(p.offsets, p.n_local, p.s_begin, p.s_end, p.n_tiles, blockIdx.x, e, row0, nrows,
@@ -127,24 +150,25 @@ void k_ffn_gemm(const GemmParams p) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave >> 1, wn = wave & 1;
-  const bool swiglu = EPI != EPI_STORE_BF16;
+  constexpr bool swiglu = EPI != EPI_STORE_BF16;
   // output columns of this tile: gate/up tiles cover 128 intermediate columns
   const int n0 = ntile * (swiglu ? BN / 2 : BN);
   const int K = p.K;
   const int nk = K / BK;
 
-  // ---- operand tiles: 256 rows x 64 k of bf16 = 32 KiB, rows of 128 bytes.
-  // Each wave instruction fills 1 KiB of LDS = 8 rows; lane l lands at
-  // physical chunk l % 8 of row 8*(l/8) within it, so it fetches the logical
-  // chunk (l % 8) ^ (row % 8): the XOR swizzle is applied on the global side.
-  // Thread rows: r_j = 32 j + tid / 8, j = 0..7 (same rows for A and B).
+  // ---- operand tiles: 256 rows x BK k of bf16.  A wave load instruction
+  // fills 1 KiB of LDS: lane l lands at physical chunk l % CPR of row
+  // l / CPR of that KiB, so it fetches the logical chunk (l % CPR) ^ key(row).
+  // Thread rows: r_j = tid / CPR + RSTEP * j, j < NLOAD (same rows for A, B).
   const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
-  const int lrow = tid >> 3;                                  // 0..31
-  const int lchunk = (lane & 7) ^ swz_key(lrow);              // logical 16-byte chunk
-  uint32_t boff[8];                                           // element offsets in Wexp
+  const int lrow = tid / CPR;
+  const int lchunk = (lane % CPR) ^ G::key(lrow);             // key(r_j) == key(lrow)
+  // (fixed-size arrays: a template-dependent bound here made the host pass
+  // drop the kernel's launch stub)
+  uint32_t boff[8];                                           // element offsets in Wexp, NLOAD used
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int nb = lrow + 32 * j;
+  for (int j = 0; j < G::NLOAD; ++j) {
+    const int nb = lrow + G::RSTEP * j;
     int wrow;
     if (swiglu) {
       // B rows 0..127 -> wave column 0, 128..255 -> 1; in each, 64 gate rows
@@ -162,17 +186,19 @@ void k_ffn_gemm(const GemmParams p) {
   // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
   const uint16_t* Abf = static_cast<const uint16_t*>(p.A);
   const uint8_t* Amx = static_cast<const uint8_t*>(p.A);
+  constexpr int NA = A_MX ? 4 : G::NLOAD;
   uint32_t aoff[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int r = A_MX ? (tid >> 2) + 64 * (j & 3) : lrow + 32 * j;
-    int rr = r < nrows ? r : nrows - 1;
-    uint32_t ring_row = static_cast<uint32_t>((static_cast<int64_t>(row0) + rr) % p.a_rows);
+  for (int j = 0; j < NA; ++j) {
+    const int r = A_MX ? (tid >> 2) + 64 * j : lrow + G::RSTEP * j;
+    const int rr = r < nrows ? r : nrows - 1;
+    const uint32_t ring_row = static_cast<uint32_t>((static_cast<int64_t>(row0) + rr) % p.a_rows);
     aoff[j] = A_MX ? ring_row : ring_row * static_cast<uint32_t>(K) + lchunk * 8;
   }
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  auto lds_tile = [&](int which, int buf) { return lds + (which * 2 + buf) * kTileBytes; };
+  auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
+  auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILEB; };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -190,13 +216,13 @@ void k_ffn_gemm(const GemmParams p) {
   // issue the (asynchronous) loads of k-step kt into LDS buffer buf
 #define MOK_ISSUE_LOADS(kt, buf)                                                             \
   do {                                                                                       \
-    uint8_t* Bs_ = lds_tile(1, buf);                                                         \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                            \
+    uint8_t* Bs_ = tileB(buf);                                                               \
+    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
       __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK,                           \
                                        (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, 0, 0);  \
     if (!A_MX) {                                                                             \
-      uint8_t* As_ = lds_tile(0, buf);                                                       \
-      _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
+      uint8_t* As_ = tileA(buf);                                                             \
+      _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                   \
         __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK,                          \
                                          (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
     } else {                                                                                 \
@@ -212,7 +238,7 @@ void k_ffn_gemm(const GemmParams p) {
   // MXFP8 A: dequantise the staged codes to bf16 into LDS buffer buf
 #define MOK_STORE_AMX(buf)                                                                   \
   do {                                                                                       \
-    uint8_t* As_ = lds_tile(0, buf);                                                         \
+    uint8_t* As_ = tileA(buf);                                                               \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
       const int r = (tid >> 2) + 64 * j, c16 = tid & 3;                                      \
       const int E = static_cast<int>(amx_sc[j]) - 127;                                       \
@@ -222,23 +248,18 @@ void k_ffn_gemm(const GemmParams p) {
         o[2 * q] = pack_bf16x2(e4m3_value(w4[q] & 0xff, E), e4m3_value((w4[q] >> 8) & 0xff, E)); \
         o[2 * q + 1] = pack_bf16x2(e4m3_value((w4[q] >> 16) & 0xff, E), e4m3_value(w4[q] >> 24, E)); \
       }                                                                                      \
-      *reinterpret_cast<uint4*>(As_ + swz(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]); \
-      *reinterpret_cast<uint4*>(As_ + swz(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]); \
+      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]); \
+      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]); \
     }                                                                                        \
   } while (0)
 
-  // Pipeline.  LDS holds two k-steps (A+B, 64 KiB each).  The barrier of
-  // k-step kt sits after every wave has its last fragments of kt in registers
-  // and before their MFMAs, so (1) the loads of kt+2 are issued into the freed
-  // buffer as early as possible -- almost two k-steps ahead -- and (2) the
-  // first fragments of kt+1 are read while the last MFMAs of kt run.
-#define MOK_FRAGS(dst, buf_ptrA, buf_ptrB, ks_)                                              \
+#define MOK_FRAGS(dst, pa, pb, ks_)                                                          \
   do {                                                                                       \
     const int kc_ = 2 * (ks_) + khalf;                                                       \
     _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
-      af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((buf_ptrA) + swz(128 * wm + 32 * mi + frag_row, kc_)); \
+      af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((pa) + G::off(128 * wm + 32 * mi + frag_row, kc_)); \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
-      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((buf_ptrB) + swz(128 * wn + 32 * ni + frag_row, kc_)); \
+      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::off(128 * wn + 32 * ni + frag_row, kc_)); \
   } while (0)
 #define MOK_MMA(src)                                                                         \
   do {                                                                                       \
@@ -247,41 +268,65 @@ void k_ffn_gemm(const GemmParams p) {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[src][ni], af[src][mi], acc[mi][ni], 0, 0, 0); \
   } while (0)
 
-  MOK_ISSUE_LOADS(0, 0);
-  if (A_MX) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    MOK_STORE_AMX(0);
+  // Pipeline.  Stage s lives in LDS buffer s % NS; the prologue issues stages
+  // 0 .. NS-1.  In k-step kt the barrier sits after every wave holds its last
+  // fragments of kt and before their MFMAs: then buffer kt % NS is free and
+  // stage kt + NS is issued into it at once (a clamped re-load past the end,
+  // which keeps the per-thread load count -- and so the vmcnt bookkeeping --
+  // the same in every step), and the first fragments of kt + 1 are read while
+  // the last MFMAs of kt run.  Before that barrier a thread waits until its
+  // loads of stage kt + 1 have landed: the NS - 2 newer stages may still fly.
+  constexpr int LPS = A_MX ? 0 : 2 * G::NLOAD;               // direct loads per stage (bf16)
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0) {
+    const int ks0 = s0 < nk ? s0 : nk - 1;
+    MOK_ISSUE_LOADS(ks0, s0);
+    if (A_MX && s0 == 0) {
+      wait_vm<0>();
+      MOK_STORE_AMX(0);
+    }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (A_MX) {
+    wait_vm<0>();
+  } else {
+    wait_vm<(NS - 1) * LPS>();                               // stage 0 landed
+  }
   __syncthreads();
-  if (nk > 1) MOK_ISSUE_LOADS(1, 1);
 
   bf16x8_t af[2][4], bfr[2][4];
-  MOK_FRAGS(0, lds_tile(0, 0), lds_tile(1, 0), 0);
+  MOK_FRAGS(0, tileA(0), tileB(0), 0);
+  constexpr int KS = BK / 16;                                // k-slices per k-step
+  int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const uint8_t* As = lds_tile(0, buf);
-    const uint8_t* Bs = lds_tile(1, buf);
-    MOK_FRAGS(1, As, Bs, 1);
-    MOK_MMA(0);
-    MOK_FRAGS(0, As, Bs, 2);
-    MOK_MMA(1);
-    MOK_FRAGS(1, As, Bs, 3);
-    MOK_MMA(0);
-    if (kt + 1 < nk) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of kt+1 landed
-      if (A_MX) MOK_STORE_AMX(buf ^ 1);
-      __syncthreads();                                     // all of kt+1 landed; buf is free
-      if (kt + 2 < nk) MOK_ISSUE_LOADS(kt + 2, buf);
-      MOK_FRAGS(0, lds_tile(0, buf ^ 1), lds_tile(1, buf ^ 1), 0);
+    const uint8_t* As = tileA(buf);
+    const uint8_t* Bs = tileB(buf);
+    const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
+      MOK_MMA(ks & 1);
     }
-    MOK_MMA(1);
+    if (kt + 1 < nk) {
+      if (A_MX) {
+        wait_vm<0>();
+        MOK_STORE_AMX(nbuf);
+      } else {
+        wait_vm<(NS - 2) * LPS>();                           // stage kt+1 landed
+      }
+      __syncthreads();                                       // kt+1 visible; buffer buf free
+      const int kn = kt + NS < nk ? kt + NS : nk - 1;
+      MOK_ISSUE_LOADS(kn, buf);
+      MOK_FRAGS(0, tileA(nbuf), tileB(nbuf), 0);
+    }
+    MOK_MMA((KS - 1) & 1);
+    buf = nbuf;
   }
-#undef MOK_FRAGS
-#undef MOK_MMA
-  __syncthreads();                                         // LDS is reused by the epilogue
 #undef MOK_ISSUE_LOADS
 #undef MOK_STORE_AMX
+#undef MOK_FRAGS
+#undef MOK_MMA
+  wait_vm<0>();                                              // clamped tail loads still land in LDS
+  __syncthreads();                                           // LDS is reused by the epilogue
 
   // ---- epilogue, staged through LDS for 16-byte global stores.
   // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
