@@ -76,10 +76,13 @@ typedef struct {
     int32_t n_local;      /* 1..256                                            */
     int32_t act_format;   /* mok_act_format                                    */
     int32_t minibatch;    /* M rows per window; 0 = two-wave rule              */
-    int32_t ring_slots;   /* S ring rows; 0 = 2*M; must be >= M                */
+    int32_t ring_slots;   /* S ring rows; 0 = 2*M; >= M (stream), >= 2*M (persistent) */
     int32_t max_rows;     /* capacity for routed rows R; 0 = T*k               */
     int32_t n_move_cus;   /* data-movement workgroups (persistent); 0 = auto   */
     int32_t mode;         /* mok_mode                                          */
+    int32_t wait_timeout_us; /* bound of each device-side wait of the persistent
+                                kernel; 0 = 2 s.  On expiry the kernel stops and
+                                the status word becomes MOK_ERR_DEVICE.        */
 } mok_layer_desc;
 
 /* Tokens held in partitions: token t lives in partition t / part_rows at row

@@ -44,7 +44,7 @@ class MokError(RuntimeError):
 class mok_layer_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "expert_base", "n_local", "act_format",
-        "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode")]
+        "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode", "wait_timeout_us")]
 
 
 class mok_tokens(C.Structure):

@@ -52,7 +52,9 @@ bool desc_ok(const mok_layer_desc* d) {
   if (d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts) return false;
   if (d->expert_base < 0 || d->expert_base + d->n_local > d->n_experts) return false;
   if (d->act_format != MOK_ACT_BF16 && d->act_format != MOK_ACT_MXFP8_E4M3) return false;
-  if (d->minibatch < 0 || d->ring_slots < 0 || d->max_rows < 0 || d->n_move_cus < 0) return false;
+  if (d->minibatch < 0 || d->ring_slots < 0 || d->max_rows < 0 || d->n_move_cus < 0 ||
+      d->wait_timeout_us < 0)
+    return false;
   if (d->mode != MOK_MODE_STREAM && d->mode != MOK_MODE_PERSISTENT) return false;
   return true;
 }
@@ -85,6 +87,7 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.M = plan_minibatch(d, cap);
   p.S = d->ring_slots > 0 ? d->ring_slots : 2 * p.M;
   if (p.S < p.M) return false;
+  if (d->mode == MOK_MODE_PERSISTENT && p.S < 2 * static_cast<int64_t>(p.M)) return false;
   p.nwin = static_cast<int32_t>((cap + p.M - 1) / p.M);
   p.act_rows = p.S;
   p.n_ybuf = n_macro > 1 ? 2 : 1;
@@ -352,7 +355,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
     pa.w_d = static_cast<const uint16_t*>(w_down);
     pa.ring = ring; pa.ring_sc = ring_sc; pa.act = act; pa.act_sc = act_sc; pa.act_rows = p.act_rows;
     pa.status = status; pa.pers_ws = at<void>(ws, p.off_pers);
-    pa.n_move = d.n_move_cus; pa.n_cus = device_cus();
+    pa.n_move = d.n_move_cus; pa.n_cus = device_cus(); pa.timeout_us = d.wait_timeout_us;
     mok_status st = launch_persistent(pa, stream);
     return st;
   }

@@ -1,0 +1,424 @@
+// gemm_tile.h -- the grouped bf16 MFMA GEMM tile of the expert FFN (device
+// code shared by the standalone GEMM kernels and the persistent pipeline).
+// See gemm.hip for the design notes.
+#pragma once
+
+#include "mok_internal.h"
+
+namespace mok {
+namespace gemm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256;
+constexpr int kThreads = 256;
+constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf16 / 256 x 128 fp32
+
+// Pipeline shape per A-operand format.
+template <bool A_MX> struct Pipe;
+template <> struct Pipe<false> { static constexpr int BK = 32, NS = 4; };
+template <> struct Pipe<true> { static constexpr int BK = 64, NS = 2; };
+
+template <bool A_MX> struct Geo {
+  static constexpr int BK = Pipe<A_MX>::BK, NS = Pipe<A_MX>::NS;
+  static constexpr int ROWB = BK * 2;                 // bytes per LDS tile row
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int TILEB = BM * ROWB;             // one operand tile
+  static constexpr int STAGEB = 2 * TILEB;            // A + B
+  static constexpr int RSTEP = 2048 / BK;             // row step between a thread's loads
+  static constexpr int NLOAD = 256 / RSTEP;           // loads per thread per operand tile
+  static constexpr int LOOP_LDS = NS * STAGEB;
+  static constexpr int LDS = LOOP_LDS > kEpiLds ? LOOP_LDS : kEpiLds;
+  // chunk XOR key: conflict-free b128 reads of 16 consecutive rows at one logical chunk
+  static __device__ __forceinline__ int key(int row) {
+    return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+  }
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ key(row)) << 4);
+  }
+};
+
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
+
+struct GemmParams {
+  const void* A;              // bf16 [a_rows][K] or E4M3 codes [a_rows][K]
+  const uint8_t* A_scales;    // [a_rows][K/32] when A is MXFP8
+  int32_t a_rows;
+  const uint16_t* W;          // [n_local][w_rows][K]
+  int64_t w_expert_stride;    // elements
+  int32_t K;
+  int32_t N;                  // output columns (I for gate/up, H for down)
+  int32_t I;                  // up-row offset for gate/up
+  void* C;                    // bf16 [c_rows][N] or E4M3 codes [c_rows][N]
+  uint8_t* C_scales;          // [c_rows][N/32]
+  int32_t c_rows;
+  const int32_t* offsets;
+  int32_t n_local;
+  int32_t s_begin, s_end;
+  int32_t n_tiles;            // output column tiles
+  int32_t a_row_base;         // A row of slot s: (s + a_row_base) % a_rows
+  int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
+};
+
+// Tile order and placement.  Tiles are numbered expert by expert; inside an
+// expert, n-tile major and m-tile minor, so the workgroups running at the same
+// time share the expert's A rows and a few weight tiles.  Workgroup ids are
+// dealt to the 8 XCDs round-robin (id % 8); each XCD is given a contiguous run
+// of tile numbers, so an expert's operands are fetched into one XCD's L2
+// instead of all eight.  Returns false for workgroups past the last tile.
+constexpr int kXcds = 8;
+
+// m-tiles of the window [w0, w1) (already clipped to R), summed over experts.
+__device__ __forceinline__ int window_mtiles(const int32_t* __restrict__ offsets, int32_t n_local,
+                                             int32_t w0, int32_t w1) {
+  int total = 0;
+  for (int e = 0; e < n_local; ++e) {
+    const int32_t lo = offsets[e] < w0 ? w0 : offsets[e];
+    const int32_t hi = offsets[e + 1] > w1 ? w1 : offsets[e + 1];
+    if (hi > lo) total += (hi - lo + BM - 1) / BM;
+  }
+  return total;
+}
+
+// Tile t of the window in (expert, n-tile, m-tile) order.
+__device__ __forceinline__ bool tile_of(const int32_t* __restrict__ offsets, int32_t n_local,
+                                        int32_t w0, int32_t w1, int n_tiles, int t, int& e_out,
+                                        int& row0, int& nrows, int& ntile) {
+  for (int e = 0; e < n_local; ++e) {
+    const int32_t lo = offsets[e] < w0 ? w0 : offsets[e];
+    const int32_t hi = offsets[e + 1] > w1 ? w1 : offsets[e + 1];
+    if (hi <= lo) continue;
+    const int mt = (hi - lo + BM - 1) / BM;
+    if (t < mt * n_tiles) {
+      const int m = t % mt;
+      ntile = t / mt;
+      e_out = e;
+      row0 = lo + m * BM;
+      nrows = (hi - row0) < BM ? (hi - row0) : BM;
+      return true;
+    }
+    t -= mt * n_tiles;
+  }
+  return false;
+}
+
+// Tile of workgroup `bid` in a standalone launch: XCD x = bid % 8 takes the
+// x-th contiguous eighth of the window's tiles.
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets, int32_t n_local,
+                                            int32_t s_begin, int32_t s_end, int n_tiles, int bid,
+                                            int& e_out, int& row0, int& nrows, int& ntile) {
+  const int32_t R = offsets[n_local];
+  const int32_t w0 = s_begin, w1 = s_end < R ? s_end : R;
+  if (w1 <= w0) return false;
+  const int total = window_mtiles(offsets, n_local, w0, w1) * n_tiles;
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = bid % kXcds, i = bid / kXcds;
+  if (i >= q + (x < r ? 1 : 0)) return false;
+  return tile_of(offsets, n_local, w0, w1, n_tiles, x * q + (x < r ? x : r) + i, e_out, row0, nrows,
+                 ntile);
+}
+
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 256-row x (256 | 128 SwiGLU) output tile of expert e, rows
+// [row0, row0 + nrows) of the window, column tile `ntile`.  Called by all 256
+// threads of a workgroup; `lds` is the workgroup's LDS (Geo<A_MX>::LDS bytes).
+// Starts with a barrier, so it can be called back to back on the same LDS.
+template <bool A_MX, int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, int nrows, int ntile,
+                                          uint8_t* __restrict__ lds) {
+  using G = Geo<A_MX>;
+  constexpr int BK = G::BK, NS = G::NS, CPR = G::CPR;
+  __syncthreads();
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr bool swiglu = EPI != EPI_STORE_BF16;
+  // output columns of this tile: gate/up tiles cover 128 intermediate columns
+  const int n0 = ntile * (swiglu ? BN / 2 : BN);
+  const int K = p.K;
+  const int nk = K / BK;
+
+  // ---- operand tiles: 256 rows x BK k of bf16.  A wave load instruction
+  // fills 1 KiB of LDS: lane l lands at physical chunk l % CPR of row
+  // l / CPR of that KiB, so it fetches the logical chunk (l % CPR) ^ key(row).
+  // Thread rows: r_j = tid / CPR + RSTEP * j, j < NLOAD (same rows for A, B).
+  const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
+  const int lrow = tid / CPR;
+  const int lchunk = (lane % CPR) ^ G::key(lrow);             // key(r_j) == key(lrow)
+  // (fixed-size arrays: a template-dependent bound here made the host pass
+  // drop the kernel's launch stub)
+  uint32_t boff[8];                                           // element offsets in Wexp, NLOAD used
+#pragma unroll
+  for (int j = 0; j < G::NLOAD; ++j) {
+    const int nb = lrow + G::RSTEP * j;
+    int wrow;
+    if (swiglu) {
+      // B rows 0..127 -> wave column 0, 128..255 -> 1; in each, 64 gate rows
+      // then the 64 up rows of the same intermediate columns.
+      const int wc = nb >> 7, q = nb & 127;
+      int icol = n0 + 64 * wc + (q & 63);
+      if (icol >= p.I) icol = p.I - 1;                        // clamp; masked at the store
+      wrow = (q < 64) ? icol : p.I + icol;
+    } else {
+      wrow = n0 + nb;
+      if (wrow >= p.N) wrow = p.N - 1;
+    }
+    boff[j] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K) + lchunk * 8;
+  }
+  // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
+  const uint16_t* Abf = static_cast<const uint16_t*>(p.A);
+  const uint8_t* Amx = static_cast<const uint8_t*>(p.A);
+  constexpr int NA = A_MX ? 4 : G::NLOAD;
+  uint32_t aoff[8];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = A_MX ? (tid >> 2) + 64 * j : lrow + G::RSTEP * j;
+    const int rr = r < nrows ? r : nrows - 1;
+    const uint32_t ring_row =
+        static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
+    aoff[j] = A_MX ? ring_row : ring_row * static_cast<uint32_t>(K) + lchunk * 8;
+  }
+
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
+  auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILEB; };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  const int frag_row = lane & 31;
+  const int khalf = lane >> 5;
+  uint4 amx[4];
+  uint32_t amx_sc[4];
+
+  // issue the (asynchronous) loads of k-step kt into LDS buffer buf
+#define MOK_ISSUE_LOADS(kt, buf)                                                             \
+  do {                                                                                       \
+    uint8_t* Bs_ = tileB(buf);                                                               \
+    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
+      __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK,                           \
+                                       (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, 0, 0);  \
+    if (!A_MX) {                                                                             \
+      uint8_t* As_ = tileA(buf);                                                             \
+      _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                   \
+        __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK,                          \
+                                         (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
+    } else {                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
+        amx[j] = *reinterpret_cast<const uint4*>(Amx + static_cast<int64_t>(aoff[j]) * K +   \
+                                                 (kt) * BK + (tid & 3) * 16);                \
+        amx_sc[j] = p.A_scales[static_cast<int64_t>(aoff[j]) * (K / 32) + (kt) * 2 +         \
+                               ((tid & 3) >> 1)];                                            \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+
+  // MXFP8 A: dequantise the staged codes to bf16 into LDS buffer buf
+#define MOK_STORE_AMX(buf)                                                                   \
+  do {                                                                                       \
+    uint8_t* As_ = tileA(buf);                                                               \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
+      const int r = (tid >> 2) + 64 * j, c16 = tid & 3;                                      \
+      const int E = static_cast<int>(amx_sc[j]) - 127;                                       \
+      const uint32_t w4[4] = {amx[j].x, amx[j].y, amx[j].z, amx[j].w};                       \
+      uint32_t o[8];                                                                         \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
+        o[2 * q] = pack_bf16x2(e4m3_value(w4[q] & 0xff, E), e4m3_value((w4[q] >> 8) & 0xff, E)); \
+        o[2 * q + 1] = pack_bf16x2(e4m3_value((w4[q] >> 16) & 0xff, E), e4m3_value(w4[q] >> 24, E)); \
+      }                                                                                      \
+      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]); \
+      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]); \
+    }                                                                                        \
+  } while (0)
+
+#define MOK_FRAGS(dst, pa, pb, ks_)                                                          \
+  do {                                                                                       \
+    const int kc_ = 2 * (ks_) + khalf;                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
+      af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((pa) + G::off(128 * wm + 32 * mi + frag_row, kc_)); \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
+      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::off(128 * wn + 32 * ni + frag_row, kc_)); \
+  } while (0)
+#define MOK_MMA(src)                                                                         \
+  do {                                                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
+      _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                       \
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[src][ni], af[src][mi], acc[mi][ni], 0, 0, 0); \
+  } while (0)
+
+  // Pipeline.  Stage s lives in LDS buffer s % NS; the prologue issues stages
+  // 0 .. NS-1.  In k-step kt the barrier sits after every wave holds its last
+  // fragments of kt and before their MFMAs: then buffer kt % NS is free and
+  // stage kt + NS is issued into it at once (a clamped re-load past the end,
+  // which keeps the per-thread load count -- and so the vmcnt bookkeeping --
+  // the same in every step), and the first fragments of kt + 1 are read while
+  // the last MFMAs of kt run.  Before that barrier a thread waits until its
+  // loads of stage kt + 1 have landed: the NS - 2 newer stages may still fly.
+  constexpr int LPS = A_MX ? 0 : 2 * G::NLOAD;               // direct loads per stage (bf16)
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0) {
+    const int ks0 = s0 < nk ? s0 : nk - 1;
+    MOK_ISSUE_LOADS(ks0, s0);
+    if (A_MX && s0 == 0) {
+      wait_vm<0>();
+      MOK_STORE_AMX(0);
+    }
+  }
+  if (A_MX) {
+    wait_vm<0>();
+  } else {
+    wait_vm<(NS - 1) * LPS>();                               // stage 0 landed
+  }
+  __syncthreads();
+
+  bf16x8_t af[2][4], bfr[2][4];
+  MOK_FRAGS(0, tileA(0), tileB(0), 0);
+  constexpr int KS = BK / 16;                                // k-slices per k-step
+  int buf = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* As = tileA(buf);
+    const uint8_t* Bs = tileB(buf);
+    const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
+      MOK_MMA(ks & 1);
+    }
+    if (kt + 1 < nk) {
+      if (A_MX) {
+        wait_vm<0>();
+        MOK_STORE_AMX(nbuf);
+      } else {
+        wait_vm<(NS - 2) * LPS>();                           // stage kt+1 landed
+      }
+      __syncthreads();                                       // kt+1 visible; buffer buf free
+      const int kn = kt + NS < nk ? kt + NS : nk - 1;
+      MOK_ISSUE_LOADS(kn, buf);
+      MOK_FRAGS(0, tileA(nbuf), tileB(nbuf), 0);
+    }
+    MOK_MMA((KS - 1) & 1);
+    buf = nbuf;
+  }
+#undef MOK_ISSUE_LOADS
+#undef MOK_STORE_AMX
+#undef MOK_FRAGS
+#undef MOK_MMA
+  wait_vm<0>();                                              // clamped tail loads still land in LDS
+  __syncthreads();                                           // LDS is reused by the epilogue
+
+  // ---- epilogue, staged through LDS for 16-byte global stores.
+  // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
+  // accumulator element q of tile (mi, ni) is token row 32mi + lane%32 and
+  // output column 32ni + 8(q/4) + 4(lane/32) + q%4 of the wave's 128 x 128
+  // block, so each lane holds 4 consecutive columns of one row and writes
+  // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
+  // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
+  // the row-wise reads back are both free of bank conflicts.
+  const int erow = 128 * wm + frag_row;                  // + 32 mi
+  if (EPI == EPI_STORE_BF16) {
+    constexpr int RB = BN * 2;                             // bytes per staged row
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
+          const uint2 v = make_uint2(pack_bf16x2(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1]),
+                                     pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]));
+          *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
+        }
+    }
+    __syncthreads();
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+    for (int idx = tid; idx < BM * (BN / 8); idx += kThreads) {
+      const int r = idx / (BN / 8), k = idx % (BN / 8);
+      const int col = n0 + k * 8;
+      if (r >= nrows || col >= p.N) continue;
+      const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
+      *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+          *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+    }
+  } else {
+    // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
+    // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
+    constexpr bool MXO = EPI == EPI_SWIGLU_MX;
+    constexpr int RB = MXO ? (BN / 2) * 4 : (BN / 2) * 2;  // staged row: 128 fp32 or bf16
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float a[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = acc[mi][ni][4 * g + j], uv = acc[mi][ni + 2][4 * g + j];
+            a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          }
+          const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if (MXO) {
+            *reinterpret_cast<float4*>(lds + r * RB + (((i >> 2) ^ (r & 15)) << 4)) =
+                make_float4(a[0], a[1], a[2], a[3]);
+          } else {
+            *reinterpret_cast<uint2*>(lds + r * RB + (((i >> 3) ^ (r & 15)) << 4) + ((i >> 2) & 1) * 8) =
+                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+          }
+        }
+    }
+    __syncthreads();
+    if (!MXO) {
+      uint16_t* C = static_cast<uint16_t*>(p.C);
+      for (int idx = tid; idx < BM * 16; idx += kThreads) {
+        const int r = idx >> 4, k = idx & 15;
+        const int col = n0 + k * 8;
+        if (r >= nrows || col >= p.N) continue;
+        const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+      }
+    } else {
+      uint8_t* C = static_cast<uint8_t*>(p.C);
+      for (int idx = tid; idx < BM * 4; idx += kThreads) {
+        const int r = idx >> 2, b = idx & 3;
+        const int col = n0 + b * 32;
+        if (r >= nrows || col >= p.N) continue;
+        float v[32];
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const float4 f = *reinterpret_cast<const float4*>(lds + r * RB + (((8 * b + c4) ^ (r & 15)) << 4));
+          v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+        const int E = mx_scale_exp(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
+                 (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
+        const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
+        uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        p.C_scales[crow * (p.N / 32) + col / 32] = static_cast<uint8_t>(E + 127);
+      }
+    }
+  }
+}
+
+
+}  // namespace gemm
+}  // namespace mok

@@ -31,7 +31,11 @@ struct PersistentArgs {
   void* pers_ws;
   int32_t n_move;           // 0 = auto
   int32_t n_cus;
+  int32_t timeout_us;       // bound of every device-side wait; 0 = 2 s
 };
+
+// Macrobatches handled by one persistent launch (more are run in groups).
+constexpr int kPersistMaxMacro = 16;
 
 size_t persistent_ws_bytes(int64_t total_windows);
 mok_status launch_persistent(const PersistentArgs& a, hipStream_t s);
