@@ -108,8 +108,8 @@ class Step:
         mok.mok_expert_down(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0, self.cap,
                             dw.w_d, self.y, self.cap)
         rec(5)
-        mok.mok_combine(self.y, self.cap, self.soa, gate, wl.T, wl.k, wl.H, dw.outs[0],
-                        self.status)
+        mok.mok_combine_slots(self.y, self.cap, self.aos, self.offsets, wl.n_local, self.cap,
+                              self.soa, gate, wl.k, wl.H, dw.outs[0], self.status)
         rec(6)
 
 
@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="rows of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="also time the fused call per minibatch")
+    ap.add_argument("--fused-only", default="",
+                    help="MODE:M:N_MOVE -- only run the fused call 5 times (for profiling), "
+                         "MODE 0 stream / 1 persistent")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (counter scale)")
     args = ap.parse_args()
@@ -197,6 +200,19 @@ def main():
     log(f"[bench] workload {wl.name} generated in {time.time() - t:.1f} s")
     dw = DeviceWorkload(wl)
     max_rows = BENCH_MAX_ROWS if not wl.routing_from_logits else wl.T * wl.k
+    if args.fused_only:
+        mode, M, n_move = (int(v) for v in args.fused_only.split(":"))
+        d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move)
+        ws = torch.empty(mok.mok_forward_workspace_size(d, wl.T, 1), dtype=torch.uint8,
+                         device="cuda")
+        dw.routing()
+        for _ in range(5):
+            mok.mok_moe_forward(d, dw.topk_idx, dw.topk_gate, wl.T, dw.x, dw.w_gu, dw.w_d,
+                                dw.outs[0], ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"fused_only": args.fused_only,
+                          "status": mok.mok_device_status(ws)}), flush=True)
+        return
     st = Step(dw, max_rows)
     stream = torch.cuda.current_stream()
 
@@ -237,22 +253,28 @@ def main():
 
     fused = {}
     if args.sweep and not wl.routing_from_logits:
-        for M in [0] + list(wl.minibatches):
-            d = dw.desc(max_rows=max_rows, minibatch=M)
-            ws = torch.empty(mok.mok_forward_workspace_size(d, wl.T, 1), dtype=torch.uint8,
-                             device="cuda")
-            idx, gate = dw.routing()
-            for _ in range(3):
-                mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
-            e1.record()
-            torch.cuda.synchronize()
-            Mu = mok.mok_forward_minibatch(d, wl.T)
-            fused[str(Mu)] = round(e0.elapsed_time(e1) / 10, 4)
-            log(f"[bench] fused mok_moe_forward, M={Mu}: {fused[str(Mu)]:.4f} ms")
+        idx, gate = dw.topk_idx, dw.topk_gate
+        for mode in (mok.MOK_MODE_STREAM, mok.MOK_MODE_PERSISTENT):
+            for M in [0] + list(wl.minibatches):
+                for n_move in ((0,) if mode == mok.MOK_MODE_STREAM else (16, 32)):
+                    d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move)
+                    wsb = mok.mok_forward_workspace_size(d, wl.T, 1)
+                    if wsb == 0:
+                        continue
+                    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+                    for _ in range(3):
+                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(10):
+                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    assert mok.mok_device_status(ws) == 0
+                    Mu = mok.mok_forward_minibatch(d, wl.T)
+                    key = ("stream" if mode == 0 else f"persistent_mv{n_move}") + f"_M{Mu}"
+                    fused[key] = round(e0.elapsed_time(e1) / 10, 4)
+                    log(f"[bench] fused mok_moe_forward {key}: {fused[key]:.4f} ms")
 
     cpu = None
     if args.cpu_rows > 0:

@@ -191,6 +191,17 @@ mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_ass
                        const float* topk_gate, int32_t T, int32_t k, int32_t H,
                        const mok_tokens* out, int32_t* dev_status, hipStream_t stream);
 
+/* The same merge driven by the routed slots: slot s < min(R, n_slots) merges
+ * token assign_of_slot[s] / k when s is that token's smallest local slot, so
+ * each token with a local assignment is written once and only R slots are
+ * visited instead of all T tokens.  Output identical to mok_combine.
+ * offsets: int32 [n_local + 1] (R = offsets[n_local]). */
+mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assign_of_slot,
+                             const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                             const int32_t* slot_of_assign, const float* topk_gate, int32_t k,
+                             int32_t H, const mok_tokens* out, int32_t* dev_status,
+                             hipStream_t stream);
+
 /* Bytes of workspace mok_moe_forward / mok_moe_forward_batches need for T
  * source tokens per macrobatch and n_macro macrobatches. */
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro);

@@ -172,6 +172,12 @@ def test_combine():
     d = np.abs(got[written].astype(np.int32) - o_ref[written].astype(np.int32))
     assert d.max() <= 1
     assert int(status.item()) == 0
+    # the slot-driven merge writes the same rows, bit for bit
+    out2 = dw.new_out()
+    mok.mok_combine_slots(to_dev(y_np), R, s["aos"], s["offsets"], wl.n_local, R, s["soa"],
+                          dw.topk_gate, wl.k, wl.H, out2, status)
+    torch.cuda.synchronize()
+    assert np.array_equal(dw.out_rows(out2), got)
 
 
 @pytest.mark.parametrize("mx", [False, True])

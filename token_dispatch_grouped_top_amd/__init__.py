@@ -66,6 +66,8 @@ _SIGS = {
     "mok_expert_gate_up": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P]),
     "mok_expert_down": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P]),
     "mok_combine": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _I32, _TOK, _P, _P]),
+    "mok_combine_slots": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _TOK, _P,
+                                    _P]),
     "mok_forward_workspace_size": (_SZ, [_DESC, _I32, _I32]),
     "mok_moe_forward": (C.c_int, [_DESC, _P, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
     "mok_moe_forward_batches": (C.c_int, [_DESC, _I32, _P, _P, _I32, _TOK, _P, _P, _TOK, _P,
@@ -202,6 +204,15 @@ def mok_combine(y, y_rows: int, slot_of_assign, topk_gate, T: int, k: int, H: in
                 dev_status=None, stream=None) -> None:
     _check(_lib.mok_combine(_ptr(y), y_rows, _ptr(slot_of_assign), _ptr(topk_gate), T, k, H,
                             C.byref(out.c), _ptr(dev_status), _stream(stream)), "mok_combine")
+
+
+def mok_combine_slots(y, y_rows: int, assign_of_slot, offsets, n_local: int, n_slots: int,
+                      slot_of_assign, topk_gate, k: int, H: int, out: Tokens, dev_status=None,
+                      stream=None) -> None:
+    _check(_lib.mok_combine_slots(_ptr(y), y_rows, _ptr(assign_of_slot), _ptr(offsets), n_local,
+                                  n_slots, _ptr(slot_of_assign), _ptr(topk_gate), k, H,
+                                  C.byref(out.c), _ptr(dev_status), _stream(stream)),
+           "mok_combine_slots")
 
 
 def mok_forward_workspace_size(desc: mok_layer_desc, T: int, n_macro: int = 1) -> int:

@@ -275,6 +275,22 @@ mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_ass
                                    out->n_partitions, out->part_rows, dev_status, false, stream));
 }
 
+mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assign_of_slot,
+                             const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                             const int32_t* slot_of_assign, const float* topk_gate, int32_t k,
+                             int32_t H, const mok_tokens* out, int32_t* dev_status,
+                             hipStream_t stream) {
+  if (k < 1 || k > 32 || H <= 0 || H % 8 != 0 || n_local < 1 || n_slots < 0 || !tokens_ok(out, 0))
+    return MOK_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!y || y_rows < 1 || !assign_of_slot || !offsets || !slot_of_assign ||
+                      !topk_gate))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_combine_slots(y, y_rows, assign_of_slot, offsets, n_local, n_slots,
+                                         slot_of_assign, topk_gate, k, H, out->part_ptr,
+                                         out->n_partitions, out->part_rows, dev_status, false,
+                                         stream));
+}
+
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro) {
   Plan p;
   if (!desc_ok(desc) || T < 0 || n_macro < 1 || !make_plan(desc, T, n_macro, p)) return 0;
@@ -377,9 +393,9 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
-    err = launch_combine(mb[m].y, p.cap, mb[m].soa, mb[m].gate, T, d.top_k, d.hidden,
-                         mb[m].out.part_ptr, mb[m].out.n_partitions, mb[m].out.part_rows, status,
-                         true, stream);
+    err = launch_combine_slots(mb[m].y, p.cap, mb[m].aos, mb[m].offsets, d.n_local, p.cap,
+                               mb[m].soa, mb[m].gate, d.top_k, d.hidden, mb[m].out.part_ptr,
+                               mb[m].out.n_partitions, mb[m].out.part_rows, status, true, stream);
     if (err != hipSuccess) return hip_status(err);
   }
   return MOK_OK;

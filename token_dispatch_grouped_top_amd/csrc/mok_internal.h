@@ -118,6 +118,13 @@ hipError_t launch_combine(const void* y, int32_t y_rows, const int32_t* soa, con
                           int32_t part_rows, int32_t* status, bool abort_on_status,
                           hipStream_t s);
 
+// Merge driven by routed slots: each token merged at its smallest local slot.
+hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* aos,
+                                const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                const int32_t* soa, const float* gate, int32_t k, int32_t H,
+                                void* const* out_ptr, int32_t n_part, int32_t part_rows,
+                                int32_t* status, bool abort_on_status, hipStream_t s);
+
 // Grouped GEMM pair of the expert FFN over slots [s_begin, min(s_end, R)).
 struct FfnArgs {
   const void* ring; const uint8_t* ring_scales; int32_t ring_slots;

@@ -49,6 +49,21 @@ void k_combine(const uint16_t* __restrict__ y, int32_t y_rows, const int32_t* __
   combine_token(y, y_rows, soa, gate, t, k, H, out_parts, n_part, part_rows, status);
 }
 
+// Slot-driven variant: one wave per routed slot s < min(R, n_slots).
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void k_combine_slots(const uint16_t* __restrict__ y, int32_t y_rows,
+                     const int32_t* __restrict__ aos, const int32_t* __restrict__ offsets,
+                     int32_t n_local, int32_t n_slots, const int32_t* __restrict__ soa,
+                     const float* __restrict__ gate, int32_t k, int32_t H,
+                     void* const* __restrict__ out_parts, int32_t n_part, int32_t part_rows,
+                     int32_t* status, bool abort_on_status) {
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  const int32_t R = offsets[n_local];
+  if (s >= n_slots || s >= R) return;
+  if (abort_on_status && *status != 0) return;
+  merge_slot(y, y_rows, aos, soa, gate, s, k, H, out_parts, n_part, part_rows, status);
+}
+
 }  // namespace
 
 hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_rows, int32_t H,
@@ -79,6 +94,20 @@ hipError_t launch_combine(const void* y, int32_t y_rows, const int32_t* soa, con
   hipLaunchKernelGGL(k_combine, grid, dim3(kRowsPerBlock * kWave), 0, s,
                      static_cast<const uint16_t*>(y), y_rows, soa, gate, T, k, H, out_ptr,
                      n_part, part_rows, status, abort_on_status && status != nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* aos,
+                                const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                const int32_t* soa, const float* gate, int32_t k, int32_t H,
+                                void* const* out_ptr, int32_t n_part, int32_t part_rows,
+                                int32_t* status, bool abort_on_status, hipStream_t s) {
+  if (n_slots <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((static_cast<int64_t>(n_slots) + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL(k_combine_slots, grid, dim3(kRowsPerBlock * kWave), 0, s,
+                     static_cast<const uint16_t*>(y), y_rows, aos, offsets, n_local, n_slots, soa,
+                     gate, k, H, out_ptr, n_part, part_rows, status,
+                     abort_on_status && status != nullptr);
   return hipGetLastError();
 }
 

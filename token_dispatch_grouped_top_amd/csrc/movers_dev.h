@@ -55,6 +55,42 @@ __device__ __forceinline__ void gather_row_bf16(void* const* __restrict__ parts,
   }
 }
 
+// Pull of rows s = first, first + step, ... < end, two rows per wave at a
+// time: both rows' indices are read first, then kBatch 16-byte pieces of each
+// row are loaded before any is stored, so a wave keeps 2 x kBatch pieces per
+// lane in flight (the persistent kernel runs only 4 waves per mover CU).
+// Destination row of slot s: dst_base + s.
+__device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ parts,
+                                                    int32_t n_part, int32_t part_rows, int32_t H,
+                                                    int32_t k, const int32_t* __restrict__ aos,
+                                                    int64_t first, int64_t step, int64_t end,
+                                                    uint16_t* __restrict__ ring,
+                                                    int64_t dst_base, int32_t* status) {
+  const int lane = lane_id();
+  const int nvec = H / 8;
+  for (int64_t s = first; s < end; s += 2 * step) {
+    const int64_t s2 = s + step < end ? s + step : s;   // odd tail: copy row s twice
+    const uint4* src1 = token_row(parts, n_part, part_rows, aos[s] / k, H);
+    const uint4* src2 = token_row(parts, n_part, part_rows, aos[s2] / k, H);
+    if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); continue; }
+    uint4* d1 = reinterpret_cast<uint4*>(ring + (dst_base + s) * static_cast<int64_t>(H));
+    uint4* d2 = reinterpret_cast<uint4*>(ring + (dst_base + s2) * static_cast<int64_t>(H));
+    for (int v0 = lane; v0 - lane < nvec; v0 += kWave * kBatch) {
+      uint4 b1[kBatch], b2[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < nvec) { b1[u] = src1[v]; b2[u] = src2[v]; }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < nvec) { d1[v] = b1[u]; d2[v] = b2[u]; }
+      }
+    }
+  }
+}
+
 // Same with MXFP8 quantisation on the way: a block of 32 values is 4
 // consecutive 16-byte pieces, i.e. 4 consecutive lanes; amax by two
 // xor-shuffles.  All 64 lanes must call it (wave-uniform loop).
@@ -175,6 +211,29 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
       }
     }
   }
+}
+
+// Slot-driven merge: slot s (s < R) merges its token t = assign_of_slot[s] / k
+// when s is t's smallest local slot, so every token with a local assignment is
+// merged exactly once while only the R routed slots (not all pool tokens) are
+// visited.  All 64 lanes must call it.
+__device__ __forceinline__ void merge_slot(const uint16_t* __restrict__ y, int32_t y_rows,
+                                           const int32_t* __restrict__ aos,
+                                           const int32_t* __restrict__ soa,
+                                           const float* __restrict__ gate, int64_t s, int32_t k,
+                                           int32_t H, void* const* __restrict__ out_parts,
+                                           int32_t n_part, int32_t part_rows, int32_t* status) {
+  const int lane = lane_id();
+  const int64_t t = aos[s] / k;
+  int32_t mine = 0x7fffffff;
+  if (lane < k) {
+    const int32_t v = soa[t * k + lane];
+    if (v >= 0) mine = v;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) mine = min(mine, __shfl_xor(mine, off));
+  if (mine != s) return;
+  combine_token(y, y_rows, soa, gate, t, k, H, out_parts, n_part, part_rows, status);
 }
 
 }  // namespace movers

@@ -34,8 +34,13 @@
 //     kernel sets MOK_ERR_DEVICE, raises an abort flag seen by all waits, and
 //     every workgroup returns.
 // Counters live in the workspace and are cleared by a fill kernel before the
-// plan kernel; producers publish with an agent-scope release after a device
-// fence, consumers poll with agent-scope acquire loads.
+// plan kernel.  Each XCD has its own L2, so an agent-scope release writes the
+// XCD's dirty L2 lines back and an agent-scope acquire invalidates the XCD's
+// L2: both are paid once per signal / satisfied wait, never per poll.  A
+// producer workgroup publishes with a barrier and one release add by thread 0;
+// a consumer polls with relaxed (coherent, non-invalidating) loads, then takes
+// one acquire fence.  A worker remembers the last window whose dependencies it
+// has acquired, so consecutive tiles of one window wait (and invalidate) once.
 #include "gemm_tile.h"
 #include "movers_dev.h"
 #include "persistent.h"
@@ -167,14 +172,15 @@ __global__ void k_plan(const PKArgs a) {
   *c.n_items = ni;
 }
 
-// Bounded wait by thread 0 for *ctr >= target (agent-scope acquire), result
-// broadcast to the workgroup.  False when the kernel is aborting.
+// Bounded wait by thread 0 for *ctr >= target: relaxed polls, then one
+// agent-scope acquire fence; the result is broadcast to the workgroup.  False
+// when the kernel is aborting.
 __device__ __forceinline__ bool wait_geq(int32_t* ctr, int32_t target, const CtlView& c,
                                          const PKArgs& a, int32_t* sh_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
       if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout_ticks) {
         __hip_atomic_store(c.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -184,6 +190,7 @@ __device__ __forceinline__ bool wait_geq(int32_t* ctr, int32_t target, const Ctl
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *sh_flag = ok;
   }
   __syncthreads();
@@ -192,9 +199,11 @@ __device__ __forceinline__ bool wait_geq(int32_t* ctr, int32_t target, const Ctl
   return ok;
 }
 
-// Publishes this workgroup's writes, then bumps the counter (release).
+// Publishes this workgroup's writes, then bumps the counter: the barrier
+// waits until every wave's stores have reached the XCD's L2, and thread 0's
+// release add writes that L2 back before the increment becomes visible.
 __device__ __forceinline__ void signal_add(int32_t* ctr) {
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -213,13 +222,13 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
       const PMacro pm = c.pm[c.win_m[w]];
       const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
       const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
-      for (int64_t s = s0 + mw; s < s1; s += nmw) {
-        if (A_MX)
+      if (A_MX) {
+        for (int64_t s = s0 + mw; s < s1; s += nmw)
           gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s,
                            static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, a.status);
-        else
-          gather_row_bf16(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s,
-                          static_cast<uint16_t*>(a.ring), base + s, a.status);
+      } else {
+        gather_rows_bf16_x2(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s0 + mw, nmw,
+                            s1, static_cast<uint16_t*>(a.ring), base, a.status);
       }
       signal_add(&c.gathered[w]);
     } else {
@@ -227,9 +236,10 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
       for (int w = 0; w < W; ++w)
         if (c.win_m[w] == m && !wait_geq(&c.dn_done[w], c.win_nt2[w], c, a, sh)) return;
       const PMacro pm = c.pm[m];
-      for (int64_t t = mw; t < a.T; t += nmw)
-        combine_token(pm.y, a.cap, pm.soa, pm.gate, t, a.k, a.H, pm.out_parts, pm.out_n_part,
-                      pm.out_part_rows, a.status);
+      const int32_t R = pm.offsets[a.n_local];
+      for (int64_t s = mw; s < R; s += nmw)
+        merge_slot(pm.y, a.cap, pm.aos, pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
+                   pm.out_n_part, pm.out_part_rows, a.status);
       signal_add(&c.merged[m]);
     }
   }
@@ -242,6 +252,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
   const int32_t* xs = c.xseq + x * c.xstride;
   const int32_t total = W > 0 ? xs[ne] : 0;
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2), n2 = (a.H + BN - 1) / BN;
+  int ready_g1 = -1, ready_g2 = -1;   // last window whose G1 / G2 dependencies were acquired
   while (true) {
     if (threadIdx.x == 0)
       sh[1] = __hip_atomic_fetch_add(&c.tile_ctr[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -259,13 +270,15 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
     const int32_t q = tk / kXcds, r = tk % kXcds;
     const int te = x * q + (x < r ? x : r) + (lt - xs[lo]);
     const int m = c.win_m[w];
-    bool ok;
-    if (!down) {
+    bool ok = true;
+    if (!down && w != ready_g1) {
       ok = wait_geq(&c.gathered[w], a.n_move, c, a, sh) &&
            (w < 2 || wait_geq(&c.dn_done[w - 2], c.win_nt2[w - 2], c, a, sh));
-    } else {
+      ready_g1 = w;
+    } else if (down && w != ready_g2) {
       ok = wait_geq(&c.gu_done[w], c.win_nt1[w], c, a, sh) &&
            (m < 2 || wait_geq(&c.merged[m - 2], a.n_move, c, a, sh));
+      ready_g2 = w;
     }
     if (!ok) return;
     const PMacro pm = c.pm[m];
