@@ -32,6 +32,25 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows here)
 
+# HBM bytes moved by one gate/up launch, from two rocprofv3 --pmc runs of this bench (FETCH_SIZE
+# scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
+# workload and by a hash of the GEMM sources they were taken on; any other source gives null.
+GATE_UP_TRAFFIC = {
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("894b422c9b425528", 738640010),
+}
+GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
+                "token_dispatch_grouped_top_amd/csrc/gemm.hip")
+
+
+def gate_up_traffic(workload: str):
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), f), "rb") as fh:
+            h.update(fh.read())
+    rec = GATE_UP_TRAFFIC.get(workload)
+    return rec[1] if rec and rec[0] == h.hexdigest()[:16] else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -149,11 +168,13 @@ def cpu_baseline(wl, sample_rows: int):
     yr[slots] = np.arange(slots.size)
     oracle.combine_tokens(y, yr, sch["slot_of_assign"], gate, toks, wl.k)
     t3 = time.perf_counter()
-    est_s = (t1 - t0) + (t3 - t2) * sch["R"] / slots.size
+    est_s = (t1 - t0) + (t3 - t2) * sch["R"] / max(slots.size, 1)
+    whole = slots.size == sch["R"]
+    tail = ("the whole layer, not scaled" if whole else
+            f"{toks.size} tokens = {slots.size} of {sch['R']} rows, scaled by R/rows")
     return dict(value=est_s * 1e3, unit="ms/layer", cores=oracle.max_threads(), kind="oracle",
                 sample=(f"route+schedule in full ({(t1 - t0) * 1e3:.0f} ms); gather+FFN+combine "
-                        f"for {toks.size} tokens = {slots.size} of {sch['R']} rows in "
-                        f"{t3 - t2:.1f} s, scaled by R/rows"))
+                        f"in {t3 - t2:.1f} s for {tail}"))
 
 
 def main():
@@ -163,8 +184,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kimi",
                     choices=["kimi", "kimi_zipf_mxfp8", "mixtral", "tiny"])
-    ap.add_argument("--cpu-rows", type=int, default=1536,
-                    help="rows of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="routed rows of the oracle's CPU-baseline sample; >= R runs the whole "
+                         "layer (about 10 s on 16 host threads for the default workload); 0 = skip")
     ap.add_argument("--sweep", action="store_true", help="also time the fused call per minibatch")
     ap.add_argument("--fused-only", default="",
                     help="MODE:M:N_MOVE -- only run the fused call 5 times (for profiling), "
@@ -301,7 +323,10 @@ def main():
                    "max_rows": max_rows, "path": "stream-ordered C-ABI calls"},
         "roofline": {"bound": "mfma", "kernel": "gate_up grouped GEMM + SwiGLU",
                      "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": gate_up_traffic(wl.name),
+                     "traffic_unit": "bytes per launch (HBM read + write)",
+                     "algorithmic_flop_per_launch": flop_gu},
         "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
         "gemm_tflops": {"gate_up": round(gu_tf, 1), "down": round(dn_tf, 1),
                         "both": round(gemm_tf, 1),

@@ -10,6 +10,7 @@ positional definition on tiny inputs.
 Windows and the two-wave minibatch rule (minibatch paragraph of the article;
 wiki key point giving 2368 for the hidden 7168 / intermediate 2048 shape).
 """
+import os
 import itertools
 
 import numpy as np
@@ -92,10 +93,16 @@ def test_windows(orc, M):
     assert np.all(per_win[:-2] == M) and per_win[-1] == 0
 
 
+def _golden_rows(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    with open(path) as f:
+        return [[int(v) for v in ln.split()] for ln in f if ln.strip() and not ln.startswith("#")]
+
+
 def test_minibatch_two_wave_rule(orc):
-    # 148 compute units, 128x256 tiles, gate/up output width 2*2048: two full
-    # waves need exactly 2368 rows, the number the pages quote for this shape.
-    assert orc.choose_minibatch(148, 128, 256, 4096) == 2368
+    # the one sizing figure the pages print (fixture cites it)
+    for n_cus, tm, tn, n_out, want in _golden_rows("minibatch_two_wave.txt"):
+        assert orc.choose_minibatch(n_cus, tm, tn, n_out) == want
     # closed form, rounded up to 64 rows, clipped to what is available
     assert orc.choose_minibatch(224, 256, 256, 4096) == 7168
     assert orc.choose_minibatch(256, 256, 256, 4096, 8192) == 8192
