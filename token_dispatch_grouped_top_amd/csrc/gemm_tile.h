@@ -17,7 +17,13 @@ constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf
 
 // Pipeline shape per A-operand format.
 template <bool A_MX> struct Pipe;
-template <> struct Pipe<false> { static constexpr int BK = 32, NS = 4; };
+#ifndef MOK_BF16_BK
+#define MOK_BF16_BK 32
+#endif
+#ifndef MOK_BF16_NS
+#define MOK_BF16_NS 4
+#endif
+template <> struct Pipe<false> { static constexpr int BK = MOK_BF16_BK, NS = MOK_BF16_NS; };
 template <> struct Pipe<true> { static constexpr int BK = 64, NS = 2; };
 
 template <bool A_MX> struct Geo {
@@ -32,7 +38,11 @@ template <bool A_MX> struct Geo {
   static constexpr int LDS = LOOP_LDS > kEpiLds ? LOOP_LDS : kEpiLds;
   // chunk XOR key: conflict-free b128 reads of 16 consecutive rows at one logical chunk
   static __device__ __forceinline__ int key(int row) {
+#if defined(MOK_SWZ) && MOK_SWZ == 0
+    return 0;
+#else
     return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+#endif
   }
   static __device__ __forceinline__ int off(int row, int chunk) {
     return row * ROWB + ((chunk ^ key(row)) << 4);
@@ -184,6 +194,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   }
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
+#if defined(MOK_BUFLDS) && MOK_BUFLDS
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Wexp), 0, static_cast<int>(p.w_expert_stride * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Abf), 0, static_cast<int>(static_cast<int64_t>(p.a_rows) * K * 2), 0x00020000);
+#endif
   auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
   auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILEB; };
 
@@ -201,17 +217,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   uint32_t amx_sc[4];
 
   // issue the (asynchronous) loads of k-step kt into LDS buffer buf
+#if defined(MOK_BUFLDS) && MOK_BUFLDS
+#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(dst), 16, boff[j] * 2, (kt) * BK * 2, 0, 0)
+#define MOK_LD_A(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst), 16, aoff[j] * 2, (kt) * BK * 2, 0, 0)
+#else
+#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
+#define MOK_LD_A(j, kt, dst) __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
+#endif
 #define MOK_ISSUE_LOADS(kt, buf)                                                             \
   do {                                                                                       \
     uint8_t* Bs_ = tileB(buf);                                                               \
     _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
-      __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK,                           \
-                                       (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, 0, 0);  \
+      MOK_LD_W(j, kt, Bs_ + (4 * j + wave) * 1024);                                          \
     if (!A_MX) {                                                                             \
       uint8_t* As_ = tileA(buf);                                                             \
       _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                   \
-        __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK,                          \
-                                         (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
+        MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                        \
     } else {                                                                                 \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
         amx[j] = *reinterpret_cast<const uint4*>(Amx + static_cast<int64_t>(aoff[j]) * K +   \
@@ -220,6 +241,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
                                ((tid & 3) >> 1)];                                            \
       }                                                                                      \
     }                                                                                        \
+  } while (0)
+
+  // bf16 A: the two halves of a stage's direct loads (weights, tokens)
+#define MOK_ISSUE_W(kt, buf)                                                                 \
+  do {                                                                                       \
+    uint8_t* Bs_ = tileB(buf);                                                               \
+    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
+      MOK_LD_W(j, kt, Bs_ + (4 * j + wave) * 1024);                                          \
+  } while (0)
+#define MOK_ISSUE_A(kt, buf)                                                                 \
+  do {                                                                                       \
+    uint8_t* As_ = tileA(buf);                                                               \
+    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
+      MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                          \
   } while (0)
 
   // MXFP8 A: dequantise the staged codes to bf16 into LDS buffer buf
@@ -255,28 +290,40 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[src][ni], af[src][mi], acc[mi][ni], 0, 0, 0); \
   } while (0)
 
-  // Pipeline.  Stage s lives in LDS buffer s % NS; the prologue issues stages
-  // 0 .. NS-1.  In k-step kt the barrier sits after every wave holds its last
-  // fragments of kt and before their MFMAs: then buffer kt % NS is free and
-  // stage kt + NS is issued into it at once (a clamped re-load past the end,
-  // which keeps the per-thread load count -- and so the vmcnt bookkeeping --
-  // the same in every step), and the first fragments of kt + 1 are read while
-  // the last MFMAs of kt run.  Before that barrier a thread waits until its
-  // loads of stage kt + 1 have landed: the NS - 2 newer stages may still fly.
+  // Pipeline.  Stage s lives in LDS buffer s % NS.  In k-step kt the barrier
+  // sits after every wave holds its last fragments of kt and before their
+  // MFMAs: then buffer kt % NS is free for stage kt + NS, and the first
+  // fragments of kt + 1 are read while the last MFMAs of kt run.  Before that
+  // barrier a thread waits until its loads of stage kt + 1 have landed: the
+  // NS - 2 newer stages may still fly.
+  // bf16 A: a stage's loads are issued in two halves, so no phase of a k-step
+  // issues them in one burst (a burst from all four waves right after the
+  // barrier filled the load queues and stalled the MFMA stream behind it):
+  // the weight half of stage kt + NS after the barrier of kt, the token half
+  // before the barrier of kt + 1.  The prologue issues stages 0 .. NS-2 and
+  // the weight half of NS-1, so every k-step has the same shape.  Past the
+  // end, loads are clamped re-loads of the last stage into buffers nobody
+  // reads again, which keeps the per-thread load count -- and so the vmcnt
+  // bookkeeping -- the same in every step.
   constexpr int LPS = A_MX ? 0 : 2 * G::NLOAD;               // direct loads per stage (bf16)
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0) {
     const int ks0 = s0 < nk ? s0 : nk - 1;
-    MOK_ISSUE_LOADS(ks0, s0);
-    if (A_MX && s0 == 0) {
-      wait_vm<0>();
-      MOK_STORE_AMX(0);
+    if (A_MX) {
+      MOK_ISSUE_LOADS(ks0, s0);
+      if (s0 == 0) {
+        wait_vm<0>();
+        MOK_STORE_AMX(0);
+      }
+    } else {
+      MOK_ISSUE_W(ks0, s0);
+      if (s0 + 1 < NS) MOK_ISSUE_A(ks0, s0);
     }
   }
   if (A_MX) {
     wait_vm<0>();
   } else {
-    wait_vm<(NS - 1) * LPS>();                               // stage 0 landed
+    wait_vm<(NS - 2) * LPS + G::NLOAD>();                    // stage 0 landed
   }
   __syncthreads();
 
@@ -284,7 +331,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   MOK_FRAGS(0, tileA(0), tileB(0), 0);
   constexpr int KS = BK / 16;                                // k-slices per k-step
   int buf = 0;
-  for (int kt = 0; kt < nk; ++kt) {
+  // Steady state: every k-step but the last, with no branch in the body, so
+  // the wait counters stay exact.  Two phases per k-step, pinned with
+  // scheduling barriers (the compiler otherwise moves MFMAs, which touch no
+  // memory, across the workgroup barrier and leaves LDS latency exposed):
+  //   A: MFMAs of slices 0 .. KS-2, one fragment read of the next slice after
+  //      each of the first 8;
+  //   barrier (stage kt+1 landed everywhere; buffer kt % NS free);
+  //   B: MFMAs of the last slice, one fragment read of step kt+1 after each of
+  //      the first 8, then one stage load after each of the rest.
+  constexpr bool kPinned = !A_MX;
+  constexpr int kReadsA = 8 * (KS - 1);                     // fragment reads in phase A
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const uint8_t* As = tileA(buf);
     const uint8_t* Bs = tileB(buf);
     const int nbuf = buf + 1 == NS ? 0 : buf + 1;
@@ -293,22 +351,74 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
       MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
       MOK_MMA(ks & 1);
     }
-    if (kt + 1 < nk) {
-      if (A_MX) {
-        wait_vm<0>();
-        MOK_STORE_AMX(nbuf);
-      } else {
-        wait_vm<(NS - 2) * LPS>();                           // stage kt+1 landed
-      }
-      __syncthreads();                                       // kt+1 visible; buffer buf free
-      const int kn = kt + NS < nk ? kt + NS : nk - 1;
-      MOK_ISSUE_LOADS(kn, buf);
-      MOK_FRAGS(0, tileA(nbuf), tileB(nbuf), 0);
+    if (!A_MX) {                                             // token half of stage kt-1+NS
+      const int kp = kt - 1 + NS < nk ? kt - 1 + NS : nk - 1;
+      MOK_ISSUE_A(kp, buf == 0 ? NS - 1 : buf - 1);
     }
+    if (kPinned) {
+#pragma unroll
+      for (int i = 0; i < kReadsA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read
+      }
+#pragma unroll
+      for (int i = 0; i < G::NLOAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global -> LDS load
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 * (KS - 1) - kReadsA - G::NLOAD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (A_MX) {
+      wait_vm<0>();
+      MOK_STORE_AMX(nbuf);
+    } else {
+      wait_vm<(NS - 2) * LPS>();                             // stage kt+1 landed
+    }
+    // Barrier without a fence: a workgroup fence here would wait for every
+    // direct-to-LDS load in flight (vmcnt(0)), the newest stages included.
+    // Each wave's own loads of stage kt+1 are covered by the wait above, and
+    // its fragment reads of buffer buf by lgkmcnt(0), before buf is refilled.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kPinned) __builtin_amdgcn_sched_barrier(0);
+    const int kn = kt + NS < nk ? kt + NS : nk - 1;
+    MOK_FRAGS(0, tileA(nbuf), tileB(nbuf), 0);
+    if (A_MX)
+      MOK_ISSUE_LOADS(kn, buf);
+    else
+      MOK_ISSUE_W(kn, buf);                                  // weight half of stage kt+NS
     MOK_MMA((KS - 1) & 1);
+    if (kPinned) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read
+      }
+#pragma unroll
+      for (int i = 0; i < G::NLOAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global -> LDS load
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 - G::NLOAD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     buf = nbuf;
   }
+  {                                                          // last k-step
+    const uint8_t* As = tileA(buf);
+    const uint8_t* Bs = tileB(buf);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
+      MOK_MMA(ks & 1);
+    }
+    MOK_MMA((KS - 1) & 1);
+  }
 #undef MOK_ISSUE_LOADS
+#undef MOK_ISSUE_W
+#undef MOK_ISSUE_A
+#undef MOK_LD_W
+#undef MOK_LD_A
 #undef MOK_STORE_AMX
 #undef MOK_FRAGS
 #undef MOK_MMA

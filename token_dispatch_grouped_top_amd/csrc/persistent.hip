@@ -315,8 +315,12 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
 template <bool A_MX>
 __global__ __launch_bounds__(256)
 void k_persist(const PKArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Geo<false>::LDS];
-  __shared__ int32_t sh[4];
+  constexpr int kLds = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  // The broadcast words share the first 16 bytes of the GEMM's LDS: every
+  // use is fenced by workgroup barriers from the tile that overwrites them
+  // (gemm_tile opens with one; signal_add closes each tile with one).
+  int32_t* sh = reinterpret_cast<int32_t*>(lds);
   CtlView c(a.ctl, a.max_win);
   if (static_cast<int>(blockIdx.x) < a.n_move)
     mover<A_MX>(a, c, sh);
