@@ -10,44 +10,56 @@ namespace gemm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
 constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf16 / 256 x 128 fp32
 
 // Pipeline shape per A-operand format.
-template <bool A_MX> struct Pipe;
 #ifndef MOK_BF16_BK
 #define MOK_BF16_BK 32
 #endif
 #ifndef MOK_BF16_NS
 #define MOK_BF16_NS 4
 #endif
+template <bool A_MX> struct Pipe;
 template <> struct Pipe<false> { static constexpr int BK = MOK_BF16_BK, NS = MOK_BF16_NS; };
-template <> struct Pipe<true> { static constexpr int BK = 64, NS = 2; };
+template <> struct Pipe<true> { static constexpr int BK = 64, NS = 3; };
 
+// Chunk XOR key of an LDS row of `cpr` 16-byte chunks: the b128 fragment reads
+// of 16 consecutive rows at one logical chunk hit distinct banks.
+template <int cpr> __device__ __forceinline__ int chunk_key(int row) {
+#if defined(MOK_SWZ) && MOK_SWZ == 0
+  return 0;
+#else
+  return cpr == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+#endif
+}
+
+// LDS geometry of one pipeline stage: [A tile][B tile][A scales].
+//   B (weights, bf16): 256 rows of BK * 2 bytes.
+//   A: bf16 rows like B, or E4M3 codes (BK bytes per row) plus one 4-byte
+//      slot per row holding the row's two E8M0 block scales of the k-step.
 template <bool A_MX> struct Geo {
   static constexpr int BK = Pipe<A_MX>::BK, NS = Pipe<A_MX>::NS;
-  static constexpr int ROWB = BK * 2;                 // bytes per LDS tile row
-  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
-  static constexpr int TILEB = BM * ROWB;             // one operand tile
-  static constexpr int STAGEB = 2 * TILEB;            // A + B
-  static constexpr int RSTEP = 2048 / BK;             // row step between a thread's loads
-  static constexpr int NLOAD = 256 / RSTEP;           // loads per thread per operand tile
+  static constexpr int ROWB_B = BK * 2, CPR_B = ROWB_B / 16, TILE_B = BM * ROWB_B;
+  static constexpr int ROWB_A = A_MX ? BK : BK * 2, CPR_A = ROWB_A / 16, TILE_A = BM * ROWB_A;
+  static constexpr int SCALEB = A_MX ? BM * 4 : 0;
+  static constexpr int STAGEB = TILE_A + TILE_B + SCALEB;
+  // one wave instruction fills 1 KiB; four waves cover RSTEP rows per round
+  static constexpr int NLOAD_B = TILE_B / 4096, RSTEP_B = 4 * 1024 / ROWB_B;
+  static constexpr int NLOAD_A = TILE_A / 4096, RSTEP_A = 4 * 1024 / ROWB_A;
   static constexpr int LOOP_LDS = NS * STAGEB;
   static constexpr int LDS = LOOP_LDS > kEpiLds ? LOOP_LDS : kEpiLds;
-  // chunk XOR key: conflict-free b128 reads of 16 consecutive rows at one logical chunk
-  static __device__ __forceinline__ int key(int row) {
-#if defined(MOK_SWZ) && MOK_SWZ == 0
-    return 0;
-#else
-    return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
-#endif
+  static __device__ __forceinline__ int offA(int row, int chunk) {
+    return row * ROWB_A + ((chunk ^ chunk_key<CPR_A>(row)) << 4);
   }
-  static __device__ __forceinline__ int off(int row, int chunk) {
-    return row * ROWB + ((chunk ^ key(row)) << 4);
+  static __device__ __forceinline__ int offB(int row, int chunk) {
+    return row * ROWB_B + ((chunk ^ chunk_key<CPR_B>(row)) << 4);
   }
 };
+static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LDS budget");
 
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
 
@@ -142,7 +154,7 @@ template <bool A_MX, int EPI>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, int nrows, int ntile,
                                           uint8_t* __restrict__ lds) {
   using G = Geo<A_MX>;
-  constexpr int BK = G::BK, NS = G::NS, CPR = G::CPR;
+  constexpr int BK = G::BK, NS = G::NS;
   __syncthreads();
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave >> 1, wn = wave & 1;
@@ -152,19 +164,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   const int K = p.K;
   const int nk = K / BK;
 
-  // ---- operand tiles: 256 rows x BK k of bf16.  A wave load instruction
-  // fills 1 KiB of LDS: lane l lands at physical chunk l % CPR of row
-  // l / CPR of that KiB, so it fetches the logical chunk (l % CPR) ^ key(row).
-  // Thread rows: r_j = tid / CPR + RSTEP * j, j < NLOAD (same rows for A, B).
+  // ---- operand tiles.  A wave load instruction fills 1 KiB of LDS: lane l
+  // lands at physical chunk l % CPR of row l / CPR of that KiB, so it fetches
+  // the logical chunk (l % CPR) ^ key(row).  Thread rows: tid / CPR + RSTEP * j
+  // (the key repeats every 16 rows and RSTEP is a multiple of 16).
   const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
-  const int lrow = tid / CPR;
-  const int lchunk = (lane % CPR) ^ G::key(lrow);             // key(r_j) == key(lrow)
+  const int lrowB = tid / G::CPR_B;
+  const int lchunkB = (lane % G::CPR_B) ^ chunk_key<G::CPR_B>(lrowB);
   // (fixed-size arrays: a template-dependent bound here made the host pass
   // drop the kernel's launch stub)
-  uint32_t boff[8];                                           // element offsets in Wexp, NLOAD used
+  uint32_t boff[8];                                           // element offsets in Wexp
 #pragma unroll
-  for (int j = 0; j < G::NLOAD; ++j) {
-    const int nb = lrow + G::RSTEP * j;
+  for (int j = 0; j < G::NLOAD_B; ++j) {
+    const int nb = lrowB + G::RSTEP_B * j;
     int wrow;
     if (swiglu) {
       // B rows 0..127 -> wave column 0, 128..255 -> 1; in each, 64 gate rows
@@ -177,21 +189,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
       wrow = n0 + nb;
       if (wrow >= p.N) wrow = p.N - 1;
     }
-    boff[j] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K) + lchunk * 8;
+    boff[j] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K) + lchunkB * 8;
   }
   // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
+  auto a_ring_row = [&](int r) -> uint32_t {
+    const int rr = r < nrows ? r : nrows - 1;
+    return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
+  };
   const uint16_t* Abf = static_cast<const uint16_t*>(p.A);
   const uint8_t* Amx = static_cast<const uint8_t*>(p.A);
-  constexpr int NA = A_MX ? 4 : G::NLOAD;
-  uint32_t aoff[8];
+  const int lrowA = tid / G::CPR_A;
+  const int lchunkA = (lane % G::CPR_A) ^ chunk_key<G::CPR_A>(lrowA);
+  uint32_t aoff[8];                                           // element (bf16) / byte (E4M3) offsets
 #pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int r = A_MX ? (tid >> 2) + 64 * j : lrow + G::RSTEP * j;
-    const int rr = r < nrows ? r : nrows - 1;
-    const uint32_t ring_row =
-        static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
-    aoff[j] = A_MX ? ring_row : ring_row * static_cast<uint32_t>(K) + lchunk * 8;
-  }
+  for (int j = 0; j < G::NLOAD_A; ++j)
+    aoff[j] = a_ring_row(lrowA + G::RSTEP_A * j) * static_cast<uint32_t>(K) +
+              lchunkA * (A_MX ? 16 : 8);
+  // E4M3 A: thread tid fetches the two block scales of row tid for each k-step
+  const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) : 0;
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #if defined(MOK_BUFLDS) && MOK_BUFLDS
@@ -201,7 +216,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
       const_cast<uint16_t*>(Abf), 0, static_cast<int>(static_cast<int64_t>(p.a_rows) * K * 2), 0x00020000);
 #endif
   auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
-  auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILEB; };
+  auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A; };
+  auto tileS = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A + G::TILE_B; };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -213,10 +229,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
 
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
-  uint4 amx[4];
-  uint32_t amx_sc[4];
 
-  // issue the (asynchronous) loads of k-step kt into LDS buffer buf
 #if defined(MOK_BUFLDS) && MOK_BUFLDS
 #define MOK_LD_W(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(dst), 16, boff[j] * 2, (kt) * BK * 2, 0, 0)
 #define MOK_LD_A(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst), 16, aoff[j] * 2, (kt) * BK * 2, 0, 0)
@@ -224,64 +237,90 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
 #define MOK_LD_W(j, kt, dst) __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
 #define MOK_LD_A(j, kt, dst) __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
 #endif
-#define MOK_ISSUE_LOADS(kt, buf)                                                             \
-  do {                                                                                       \
-    uint8_t* Bs_ = tileB(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
-      MOK_LD_W(j, kt, Bs_ + (4 * j + wave) * 1024);                                          \
-    if (!A_MX) {                                                                             \
-      uint8_t* As_ = tileA(buf);                                                             \
-      _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                   \
-        MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                        \
-    } else {                                                                                 \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
-        amx[j] = *reinterpret_cast<const uint4*>(Amx + static_cast<int64_t>(aoff[j]) * K +   \
-                                                 (kt) * BK + (tid & 3) * 16);                \
-        amx_sc[j] = p.A_scales[static_cast<int64_t>(aoff[j]) * (K / 32) + (kt) * 2 +         \
-                               ((tid & 3) >> 1)];                                            \
-      }                                                                                      \
-    }                                                                                        \
-  } while (0)
-
-  // bf16 A: the two halves of a stage's direct loads (weights, tokens)
+  // The two halves of a stage's direct loads: weights; tokens (+ E4M3 scales,
+  // 2 bytes per lane, which land in 4-byte slots: lane i at slot base + 4 i).
 #define MOK_ISSUE_W(kt, buf)                                                                 \
   do {                                                                                       \
     uint8_t* Bs_ = tileB(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
+    _Pragma("unroll") for (int j = 0; j < G::NLOAD_B; ++j)                                   \
       MOK_LD_W(j, kt, Bs_ + (4 * j + wave) * 1024);                                          \
   } while (0)
 #define MOK_ISSUE_A(kt, buf)                                                                 \
   do {                                                                                       \
     uint8_t* As_ = tileA(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
-      MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                          \
-  } while (0)
-
-  // MXFP8 A: dequantise the staged codes to bf16 into LDS buffer buf
-#define MOK_STORE_AMX(buf)                                                                   \
-  do {                                                                                       \
-    uint8_t* As_ = tileA(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
-      const int r = (tid >> 2) + 64 * j, c16 = tid & 3;                                      \
-      const int E = static_cast<int>(amx_sc[j]) - 127;                                       \
-      const uint32_t w4[4] = {amx[j].x, amx[j].y, amx[j].z, amx[j].w};                       \
-      uint32_t o[8];                                                                         \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                        \
-        o[2 * q] = pack_bf16x2(e4m3_value(w4[q] & 0xff, E), e4m3_value((w4[q] >> 8) & 0xff, E)); \
-        o[2 * q + 1] = pack_bf16x2(e4m3_value((w4[q] >> 16) & 0xff, E), e4m3_value(w4[q] >> 24, E)); \
-      }                                                                                      \
-      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16)) = make_uint4(o[0], o[1], o[2], o[3]); \
-      *reinterpret_cast<uint4*>(As_ + G::off(r, 2 * c16 + 1)) = make_uint4(o[4], o[5], o[6], o[7]); \
+    if (A_MX) {                                                                              \
+      _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
+        __builtin_amdgcn_global_load_lds(Amx + aoff[j] + (kt) * BK,                          \
+                                         (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
+      __builtin_amdgcn_global_load_lds(p.A_scales + soff + 2 * (kt),                         \
+                                       (lds_ptr_t)(tileS(buf) + wave * 256), 2, 0, 0);       \
+    } else {                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
+        MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                        \
     }                                                                                        \
   } while (0)
 
+  // Fragments.  v_mfma_f32_32x32x16_bf16: lane l feeds row l % 32 with 8
+  // consecutive k.  bf16 A: slice ks of a k-step takes k-chunk 2 ks + l / 32 of
+  // both operands.  E4M3 A: the k order inside a k-step of 64 is permuted the
+  // same way for both operands -- slice ks of lane half h takes k 32 h + 8 ks
+  // .. +7 -- so one 16-byte code chunk holds a lane's k of two slices and one
+  // E8M0 block scale (block h of the step) covers all four: per k-step a lane
+  // reads two code chunks and one scale per A fragment row, and converts each
+  // slice right before it is used (v_cvt_scalef32_pk_bf16_fp8: exact
+  // bf16 rounding of code x 2^E).
+  bf16x8_t af[2][4], bfr[2][4];
+  uint4 araw[4][2];
+  float ascale[4];
+#define MOK_FRAGS_B(dst, pb, ks_)                                                            \
+  do {                                                                                       \
+    const int kc_ = A_MX ? 4 * khalf + (ks_) : 2 * (ks_) + khalf;                            \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
+      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::offB(128 * wn + 32 * ni + frag_row, kc_)); \
+  } while (0)
 #define MOK_FRAGS(dst, pa, pb, ks_)                                                          \
   do {                                                                                       \
-    const int kc_ = 2 * (ks_) + khalf;                                                       \
-    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
-      af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((pa) + G::off(128 * wm + 32 * mi + frag_row, kc_)); \
-    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
-      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::off(128 * wn + 32 * ni + frag_row, kc_)); \
+    if (A_MX) {                                                                              \
+      MOK_CVT(dst, ks_);                                                                     \
+    } else {                                                                                 \
+      const int kc_ = 2 * (ks_) + khalf;                                                     \
+      _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                       \
+        af[dst][mi] = *reinterpret_cast<const bf16x8_t*>((pa) + G::offA(128 * wm + 32 * mi + frag_row, kc_)); \
+    }                                                                                        \
+    MOK_FRAGS_B(dst, pb, ks_);                                                               \
+  } while (0)
+  // E4M3 A: the raw code chunks and scales of a whole k-step
+#define MOK_RAW_A(pa, ps)                                                                    \
+  do {                                                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                       \
+      const int r_ = 128 * wm + 32 * mi + frag_row;                                          \
+      araw[mi][0] = *reinterpret_cast<const uint4*>((pa) + G::offA(r_, 2 * khalf));          \
+      araw[mi][1] = *reinterpret_cast<const uint4*>((pa) + G::offA(r_, 2 * khalf + 1));      \
+      const uint32_t e_ = (ps)[r_ * 4 + khalf];                                              \
+      ascale[mi] = __uint_as_float(e_ ? e_ << 23 : 0x00400000u);                             \
+    }                                                                                        \
+  } while (0)
+#define MOK_CVT(dst, ks_)                                                                    \
+  do {                                                                                       \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                       \
+      const uint4 c_ = araw[mi][(ks_) >> 1];                                                 \
+      const uint32_t w0_ = ((ks_) & 1) ? c_.z : c_.x, w1_ = ((ks_) & 1) ? c_.w : c_.y;        \
+      const bf16x2_t p0_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0_, ascale[mi], false); \
+      const bf16x2_t p1_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0_, ascale[mi], true);  \
+      const bf16x2_t p2_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1_, ascale[mi], false); \
+      const bf16x2_t p3_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1_, ascale[mi], true);  \
+      af[dst][mi] = bf16x8_t{p0_[0], p0_[1], p1_[0], p1_[1], p2_[0], p2_[1], p3_[0], p3_[1]}; \
+    }                                                                                        \
+  } while (0)
+  // first fragments of a k-step (E4M3: raw codes + scales; slice 0 converted later)
+#define MOK_FRAGS0(pa, pb, ps)                                                               \
+  do {                                                                                       \
+    if (A_MX) {                                                                              \
+      MOK_RAW_A(pa, ps);                                                                     \
+      MOK_FRAGS_B(0, pb, 0);                                                                 \
+    } else {                                                                                 \
+      MOK_FRAGS(0, pa, pb, 0);                                                               \
+    }                                                                                        \
   } while (0)
 #define MOK_MMA(src)                                                                         \
   do {                                                                                       \
@@ -296,117 +335,97 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   // fragments of kt + 1 are read while the last MFMAs of kt run.  Before that
   // barrier a thread waits until its loads of stage kt + 1 have landed: the
   // NS - 2 newer stages may still fly.
-  // bf16 A: a stage's loads are issued in two halves, so no phase of a k-step
-  // issues them in one burst (a burst from all four waves right after the
-  // barrier filled the load queues and stalled the MFMA stream behind it):
-  // the weight half of stage kt + NS after the barrier of kt, the token half
-  // before the barrier of kt + 1.  The prologue issues stages 0 .. NS-2 and
-  // the weight half of NS-1, so every k-step has the same shape.  Past the
-  // end, loads are clamped re-loads of the last stage into buffers nobody
-  // reads again, which keeps the per-thread load count -- and so the vmcnt
-  // bookkeeping -- the same in every step.
-  constexpr int LPS = A_MX ? 0 : 2 * G::NLOAD;               // direct loads per stage (bf16)
+  // A stage's loads are issued in two halves, so no phase of a k-step issues
+  // them in one burst (a burst from all four waves right after the barrier
+  // filled the load queues and stalled the MFMA stream behind it): the weight
+  // half of stage kt + NS after the barrier of kt, the token half before the
+  // barrier of kt + 1.  The prologue issues stages 0 .. NS-2 and the weight
+  // half of NS-1, so every k-step has the same shape.  Past the end, loads are
+  // clamped re-loads of the last stage into buffers nobody reads again, which
+  // keeps the per-thread load count -- and so the vmcnt bookkeeping -- the
+  // same in every step.
+  constexpr int LW = G::NLOAD_B, LA = G::NLOAD_A + (A_MX ? 1 : 0), LPS = LW + LA;
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0) {
     const int ks0 = s0 < nk ? s0 : nk - 1;
-    if (A_MX) {
-      MOK_ISSUE_LOADS(ks0, s0);
-      if (s0 == 0) {
-        wait_vm<0>();
-        MOK_STORE_AMX(0);
-      }
-    } else {
-      MOK_ISSUE_W(ks0, s0);
-      if (s0 + 1 < NS) MOK_ISSUE_A(ks0, s0);
-    }
+    MOK_ISSUE_W(ks0, s0);
+    if (s0 + 1 < NS) MOK_ISSUE_A(ks0, s0);
   }
-  if (A_MX) {
-    wait_vm<0>();
-  } else {
-    wait_vm<(NS - 2) * LPS + G::NLOAD>();                    // stage 0 landed
-  }
+  wait_vm<(NS - 2) * LPS + LW>();                            // stage 0 landed
   __syncthreads();
 
-  bf16x8_t af[2][4], bfr[2][4];
-  MOK_FRAGS(0, tileA(0), tileB(0), 0);
+  MOK_FRAGS0(tileA(0), tileB(0), tileS(0));
   constexpr int KS = BK / 16;                                // k-slices per k-step
   int buf = 0;
   // Steady state: every k-step but the last, with no branch in the body, so
   // the wait counters stay exact.  Two phases per k-step, pinned with
   // scheduling barriers (the compiler otherwise moves MFMAs, which touch no
   // memory, across the workgroup barrier and leaves LDS latency exposed):
-  //   A: MFMAs of slices 0 .. KS-2, one fragment read of the next slice after
-  //      each of the first 8;
+  //   A: MFMAs of slices 0 .. KS-2, with the fragment reads of the next slices
+  //      and then the token half of a stage's loads interleaved one per MFMA;
   //   barrier (stage kt+1 landed everywhere; buffer kt % NS free);
-  //   B: MFMAs of the last slice, one fragment read of step kt+1 after each of
-  //      the first 8, then one stage load after each of the rest.
-  constexpr bool kPinned = !A_MX;
-  constexpr int kReadsA = 8 * (KS - 1);                     // fragment reads in phase A
+  //   B: MFMAs of the last slice, with the fragment reads of step kt+1 and
+  //      then the weight half of stage kt+NS interleaved the same way.
+  constexpr int kReadsA = A_MX ? 4 * (KS - 1) : 8 * (KS - 1); // fragment reads in phase A
+  constexpr int kReadsB = A_MX ? 16 : 8;                     // E4M3: 4 B + 8 codes + 4 scales
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const uint8_t* As = tileA(buf);
     const uint8_t* Bs = tileB(buf);
     const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+    if (A_MX) MOK_CVT(0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
       MOK_MMA(ks & 1);
     }
-    if (!A_MX) {                                             // token half of stage kt-1+NS
+    {                                                        // token half of stage kt-1+NS
       const int kp = kt - 1 + NS < nk ? kt - 1 + NS : nk - 1;
       MOK_ISSUE_A(kp, buf == 0 ? NS - 1 : buf - 1);
     }
-    if (kPinned) {
 #pragma unroll
-      for (int i = 0; i < kReadsA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read
-      }
+    for (int i = 0; i < kReadsA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one fragment read
+    }
 #pragma unroll
-      for (int i = 0; i < G::NLOAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global -> LDS load
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 * (KS - 1) - kReadsA - G::NLOAD, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one global -> LDS load
     }
-    if (A_MX) {
-      wait_vm<0>();
-      MOK_STORE_AMX(nbuf);
-    } else {
-      wait_vm<(NS - 2) * LPS>();                             // stage kt+1 landed
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 * (KS - 1) - kReadsA - LA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(NS - 2) * LPS>();                               // stage kt+1 landed
     // Barrier without a fence: a workgroup fence here would wait for every
     // direct-to-LDS load in flight (vmcnt(0)), the newest stages included.
     // Each wave's own loads of stage kt+1 are covered by the wait above, and
     // its fragment reads of buffer buf by lgkmcnt(0), before buf is refilled.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kPinned) __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
     const int kn = kt + NS < nk ? kt + NS : nk - 1;
-    MOK_FRAGS(0, tileA(nbuf), tileB(nbuf), 0);
-    if (A_MX)
-      MOK_ISSUE_LOADS(kn, buf);
-    else
-      MOK_ISSUE_W(kn, buf);                                  // weight half of stage kt+NS
+    MOK_FRAGS0(tileA(nbuf), tileB(nbuf), tileS(nbuf));
+    MOK_ISSUE_W(kn, buf);                                    // weight half of stage kt+NS
     MOK_MMA((KS - 1) & 1);
-    if (kPinned) {
+    constexpr int kRB1 = kReadsB < 16 ? kReadsB : 16;        // reads paired one per MFMA
+    constexpr int kVB = 16 - kRB1 < LW ? 16 - kRB1 : LW;     // loads paired after them
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read
-      }
-#pragma unroll
-      for (int i = 0; i < G::NLOAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global -> LDS load
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8 - G::NLOAD, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < kRB1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one fragment read
     }
+#pragma unroll
+    for (int i = 0; i < kVB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one global -> LDS load
+    }
+    if (16 - kRB1 - kVB > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - kRB1 - kVB, 0);
+    if (LW - kVB > 0) __builtin_amdgcn_sched_group_barrier(0x020, LW - kVB, 0);
+    __builtin_amdgcn_sched_barrier(0);
     buf = nbuf;
   }
   {                                                          // last k-step
     const uint8_t* As = tileA(buf);
     const uint8_t* Bs = tileB(buf);
+    if (A_MX) MOK_CVT(0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       MOK_FRAGS((ks + 1) & 1, As, Bs, ks + 1);
@@ -414,13 +433,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
     }
     MOK_MMA((KS - 1) & 1);
   }
-#undef MOK_ISSUE_LOADS
 #undef MOK_ISSUE_W
 #undef MOK_ISSUE_A
 #undef MOK_LD_W
 #undef MOK_LD_A
-#undef MOK_STORE_AMX
+#undef MOK_FRAGS_B
 #undef MOK_FRAGS
+#undef MOK_RAW_A
+#undef MOK_CVT
+#undef MOK_FRAGS0
 #undef MOK_MMA
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();                                           // LDS is reused by the epilogue

@@ -25,6 +25,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Streaming stores of rows that are written once and read by a later kernel.
+// Non-temporal stores: with ordinary ones, rows written by one wave in pieces
+// reach HBM as partial lines under eviction pressure (a row gather measured
+// 1.84x its bytes written and ran at 4.2 TB/s; 1.00x and 6.5 TB/s with these).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
+  const u32x4_nt w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
+}
+__device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
+  const u32x2_nt w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_nt*>(p));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }

@@ -50,7 +50,7 @@ __device__ __forceinline__ void gather_row_bf16(void* const* __restrict__ parts,
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       int v = v0 + u * kWave;
-      if (v < nvec) dst[v] = buf[u];
+      if (v < nvec) st_nt(dst + v, buf[u]);
     }
   }
 }
@@ -85,7 +85,7 @@ __device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ pa
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int v = v0 + u * kWave;
-        if (v < nvec) { d1[v] = b1[u]; d2[v] = b2[u]; }
+        if (v < nvec) { st_nt(d1 + v, b1[u]); st_nt(d2 + v, b2[u]); }
       }
     }
   }
@@ -141,7 +141,7 @@ __device__ __forceinline__ void gather_row_mxfp8(void* const* __restrict__ parts
         hi |= e4m3_code_scaled(f[q + 4], E) << (8 * q);
       }
       if (ok) {
-        dst[v] = make_uint2(lo, hi);
+        st_nt(dst + v, make_uint2(lo, hi));
         if ((v & 3) == 0) sdst[v >> 2] = static_cast<uint8_t>(E + 127);
       }
     }
@@ -207,7 +207,7 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
         o.y = pack_bf16x2(acc[u][2], acc[u][3]);
         o.z = pack_bf16x2(acc[u][4], acc[u][5]);
         o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-        dst[v] = o;
+        st_nt(dst + v, o);
       }
     }
   }
