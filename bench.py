@@ -103,9 +103,11 @@ class Step:
         self.names = ["route", "schedule", "gather", "gate_up", "down", "combine"]
 
     def run(self, ev=None):
-        """The hot path; ev: list of len(names)+1 events recorded between the calls."""
+        """The hot path.  ev: {i: event} recorded before call i (i = len(names): after the
+        last call); every event marker on the stream costs a kernel drain, so the timed
+        region records only the two around the dominant launch."""
         mok, dw, wl = self.mok, self.dw, self.dw.wl
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec = (lambda i: ev[i].record() if i in ev else None) if ev else (lambda i: None)
         rec(0)
         if wl.routing_from_logits:      # every token routed here
             mok.mok_route_topk(dw.logits, self.route_T, self.route_E, wl.k, dw.topk_idx,
@@ -241,17 +243,28 @@ def main():
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
-    n_ev = len(st.names) + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    # timed region: only the dominant launch (gate/up) is bracketed by events
+    ig = st.names.index("gate_up")
+    evg = [{ig: torch.cuda.Event(enable_timing=True), ig + 1: torch.cuda.Event(enable_timing=True)}
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        st.run(evs[i])
+        st.run(evg[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gate_up_ms = float(np.mean([e[ig].elapsed_time(e[ig + 1]) for e in evg]))
+    assert int(st.status.item()) == 0, "device status set during the benchmark"
+    # per-call breakdown from a separate instrumented pass (an event between every call)
+    n_ev = len(st.names) + 1
+    evs = [{j: torch.cuda.Event(enable_timing=True) for j in range(n_ev)} for _ in range(args.steps)]
+    for i in range(args.steps):
+        st.run(evs[i])
+    torch.cuda.synchronize()
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(st.names)}
-    assert int(st.status.item()) == 0, "device status set during the benchmark"
+    per_sum = sum(per.values())
+    per["gate_up"] = gate_up_ms                    # the timed region's own measurement
 
     R = int(to_host(st.offsets)[-1])
     soa = to_host(st.soa).reshape(wl.T, wl.k)
@@ -268,8 +281,8 @@ def main():
     gemm_tf = tf(flop_gu + flop_dn, per["gate_up"] + per["down"])
     disp_gbs, comb_gbs = gbs(disp_bytes, per["gather"]), gbs(comb_bytes, per["combine"])
 
-    log(f"[bench] R={R} T_out={T_out} M={st.M} wall {wall_ms:.3f} ms/step; per call (ms): "
-        + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    log(f"[bench] R={R} T_out={T_out} M={st.M} wall {wall_ms:.3f} ms/step (instrumented pass "
+        f"{per_sum:.3f}); per call (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
     log(f"[bench] gate/up {gu_tf:.0f} TF/s, down {dn_tf:.0f} TF/s, both {gemm_tf:.0f} TF/s; "
         f"gather {disp_gbs:.0f} GB/s, combine {comb_gbs:.0f} GB/s")
 
@@ -328,12 +341,14 @@ def main():
                      "traffic_unit": "bytes per launch (HBM read + write)",
                      "algorithmic_flop_per_launch": flop_gu},
         "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
+        "breakdown_note": "gate_up from the timed region's events; the other calls from a separate "
+                          "pass with an event between every call (each marker drains the stream)",
         "gemm_tflops": {"gate_up": round(gu_tf, 1), "down": round(dn_tf, 1),
                         "both": round(gemm_tf, 1),
                         "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)},
         "dispatch_GBps": round(disp_gbs, 1), "dispatch_frac_hbm": round(disp_gbs / PEAK_HBM_GBS, 4),
         "combine_GBps": round(comb_gbs, 1), "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
-        "schedule_share": round((per["schedule"]) / wall_ms, 4),
+        "schedule_share": round(per["schedule"] / wall_ms, 4),
         "fused_forward_ms": fused or None,
         "cpu_baseline": cpu,
     }
