@@ -14,9 +14,11 @@
 //              group adds the group size to the wave's LDS histogram.
 //   scan    -- one block: per expert, exclusive scan over the blocks (one
 //              wave per expert, shuffles), then the exclusive scan over
-//              experts gives offsets; block bases = offsets + block prefix.
-//   scatter -- recount per wave, prefix over the block's waves, then each
-//              lane's slot = wave cursor + popcount(group & lanes below).
+//              experts gives offsets.
+//   scatter -- recount per wave; wave cursor = offsets[e] + block prefix +
+//              prefix over the block's waves; each lane's slot = wave cursor
+//              + popcount(group & lanes below).
+// A wave loads the keys of all its steps before the first ballot.
 #include "mok_internal.h"
 
 namespace mok {
@@ -38,16 +40,26 @@ __device__ __forceinline__ uint32_t local_key(const int32_t* idx, int64_t a, int
 
 __device__ __forceinline__ int key_bits(int32_t n_local) { return 32 - __clz(n_local); }
 
+// The keys of a wave's 1024 assignments, all loaded before any is used (the
+// steps below are otherwise one dependent global load each).
+__device__ __forceinline__ void load_keys(const int32_t* __restrict__ idx, int64_t A, int32_t base,
+                                          int32_t n_local, int64_t a0, uint32_t (&keys)[kStepsPerWave]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int it = 0; it < kStepsPerWave; ++it)
+    keys[it] = local_key(idx, a0 + it * kWave + lane, A, base, n_local);
+}
+
 // Per-wave histogram of the block's chunk into h[wave][e].
-__device__ void wave_histogram(const int32_t* __restrict__ idx, int64_t A, int32_t base,
-                               int32_t n_local, int32_t (*h)[kMaxLocal]) {
+__device__ void wave_histogram(const uint32_t (&keys)[kStepsPerWave], int32_t n_local,
+                               int32_t (*h)[kMaxLocal]) {
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int nbits = key_bits(n_local);
-  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kChunk + w * (kWave * kStepsPerWave);
   for (int e = lane; e < n_local; e += kWave) h[w][e] = 0;
   __builtin_amdgcn_wave_barrier();
+#pragma unroll
   for (int it = 0; it < kStepsPerWave; ++it) {
-    uint32_t key = local_key(idx, a0 + it * kWave + lane, A, base, n_local);
+    uint32_t key = keys[it];
     uint64_t peers = match_key(key, nbits);
     bool leader = (peers & lanemask_lt()) == 0;
     if (leader && key < static_cast<uint32_t>(n_local)) h[w][key] += __popcll(peers);
@@ -59,7 +71,11 @@ __global__ __launch_bounds__(kSchedThreads)
 void k_sched_count(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
                    int32_t nblk, int32_t* __restrict__ blk_counts) {
   __shared__ int32_t h[kSchedWaves][kMaxLocal];
-  wave_histogram(idx, A, base, n_local, h);
+  uint32_t keys[kStepsPerWave];
+  load_keys(idx, A, base, n_local,
+            static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave),
+            keys);
+  wave_histogram(keys, n_local, h);
   __syncthreads();
   for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
     int32_t c = 0;
@@ -69,7 +85,8 @@ void k_sched_count(const int32_t* __restrict__ idx, int64_t A, int32_t base, int
   }
 }
 
-// One block of 1024 threads; wave w scans experts w, w+16, ...
+// One block of 1024 threads; wave w scans experts w, w+16, ...  blk_base gets
+// the exclusive prefix over blocks only; the scatter adds offsets[e].
 __global__ __launch_bounds__(1024)
 void k_sched_scan(const int32_t* __restrict__ blk_counts, int32_t n_local, int32_t nblk,
                   int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
@@ -106,32 +123,33 @@ void k_sched_scan(const int32_t* __restrict__ blk_counts, int32_t n_local, int32
     offsets[e] = off[e];
     if (e < n_local) counts[e] = tot[e];
   }
-  for (int e = w; e < n_local; e += nw) {
-    int32_t* b = blk_base + static_cast<int64_t>(e) * nblk;
-    for (int j = lane; j < nblk; j += kWave) b[j] += off[e];
-  }
 }
 
 __global__ __launch_bounds__(kSchedThreads)
 void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
                      int32_t nblk, const int32_t* __restrict__ blk_base,
-                     int32_t* __restrict__ soa, int32_t* __restrict__ aos) {
+                     const int32_t* __restrict__ offsets, int32_t* __restrict__ soa,
+                     int32_t* __restrict__ aos) {
   __shared__ int32_t h[kSchedWaves][kMaxLocal];
   __shared__ int32_t cur[kSchedWaves][kMaxLocal];
-  wave_histogram(idx, A, base, n_local, h);
+  const int64_t a0w =
+      static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave);
+  uint32_t keys[kStepsPerWave];
+  load_keys(idx, A, base, n_local, a0w, keys);
+  wave_histogram(keys, n_local, h);
   __syncthreads();
   for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
-    int32_t b = blk_base[static_cast<int64_t>(e) * nblk + blockIdx.x];
+    int32_t b = offsets[e] + blk_base[static_cast<int64_t>(e) * nblk + blockIdx.x];
 #pragma unroll
     for (int w = 0; w < kSchedWaves; ++w) { cur[w][e] = b; b += h[w][e]; }
   }
   __syncthreads();
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int nbits = key_bits(n_local);
-  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kChunk + w * (kWave * kStepsPerWave);
+#pragma unroll
   for (int it = 0; it < kStepsPerWave; ++it) {
-    const int64_t a = a0 + it * kWave + lane;
-    uint32_t key = local_key(idx, a, A, base, n_local);
+    const int64_t a = a0w + it * kWave + lane;
+    uint32_t key = keys[it];
     uint64_t peers = match_key(key, nbits);
     bool local = key < static_cast<uint32_t>(n_local);
     int32_t c = local ? cur[w][key] : 0;
@@ -195,7 +213,7 @@ hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, i
                      w.blk_base, counts, offsets);
   if (A > 0) {
     hipLaunchKernelGGL(k_sched_scatter, dim3(w.nblk), dim3(kSchedThreads), 0, s, idx, A,
-                       expert_base, n_local, w.nblk, w.blk_base, soa, aos);
+                       expert_base, n_local, w.nblk, w.blk_base, offsets, soa, aos);
   }
   return hipGetLastError();
 }
