@@ -36,7 +36,8 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("894b422c9b425528", 738640010),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("17b5fc8b56280d63", 738669081),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("17b5fc8b56280d63", 892751480),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip")
@@ -134,6 +135,39 @@ class Step:
         rec(6)
 
 
+def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
+    """8 Kimi-shaped macrobatches (one pool, one weight set, own routing each)
+    through one ring: ms per macrobatch of mok_moe_forward_batches per mode."""
+    import torch
+    import workloads as W
+    from gpu_harness import to_dev
+    wls = W.streaming(n_macro)
+    d0 = DeviceWorkload(wls[0])
+    idx = [d0.topk_idx] + [to_dev(w.topk_idx) for w in wls[1:]]
+    gate = [d0.topk_gate] + [to_dev(w.topk_gate) for w in wls[1:]]
+    outs = [d0.new_out() for _ in wls]
+    res = {}
+    for mode, M, n_move in ((0, 2560, 0), (0, 8192, 0), (1, 2560, 32), (1, 4096, 32), (1, 8192, 32)):
+        d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=M, mode=mode, n_move_cus=n_move)
+        ws = torch.empty(mok.mok_forward_workspace_size(d, d0.wl.T, n_macro), dtype=torch.uint8,
+                         device="cuda")
+        run = lambda: mok.mok_moe_forward_batches(d, n_macro, idx, gate, d0.wl.T, d0.x, d0.w_gu,
+                                                  d0.w_d, outs, ws)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        assert mok.mok_device_status(ws) == 0
+        key = ("stream" if mode == 0 else f"persistent_mv{n_move}") + f"_M{M}"
+        res[key] = round(e0.elapsed_time(e1) / 3 / n_macro, 4)
+        log(f"[bench] streaming {n_macro} macrobatches, {key}: {res[key]:.4f} ms per macrobatch")
+    return res
+
+
 def cpu_baseline(wl, sample_rows: int):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
@@ -193,6 +227,8 @@ def main():
     ap.add_argument("--fused-only", default="",
                     help="MODE:M:N_MOVE -- only run the fused call 5 times (for profiling), "
                          "MODE 0 stream / 1 persistent")
+    ap.add_argument("--streaming", action="store_true",
+                    help="also time 8 Kimi-shaped macrobatches through one ring, per mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (counter scale)")
     args = ap.parse_args()
@@ -311,6 +347,10 @@ def main():
                     fused[key] = round(e0.elapsed_time(e1) / 10, 4)
                     log(f"[bench] fused mok_moe_forward {key}: {fused[key]:.4f} ms")
 
+    streaming = None
+    if args.streaming and wl.name.startswith("kimi_share"):
+        streaming = time_streaming(mok, DeviceWorkload)
+
     cpu = None
     if args.cpu_rows > 0:
         t = time.time()
@@ -350,6 +390,7 @@ def main():
         "combine_GBps": round(comb_gbs, 1), "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
         "schedule_share": round(per["schedule"] / wall_ms, 4),
         "fused_forward_ms": fused or None,
+        "streaming_ms_per_macrobatch": streaming,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
