@@ -78,7 +78,9 @@ class Step:
         import token_dispatch_grouped_top_amd as mok
         self.mok, self.dw, wl = mok, dw, dw.wl
         self.cap = max_rows
-        self.desc = dw.desc(max_rows=max_rows)
+        # weights packed once into the GEMMs' tile order (set-up, like loading a checkpoint)
+        self.desc = dw.desc(max_rows=max_rows, weights_packed=1)
+        self.w_gu, self.w_d = dw.weights(self.desc)
         self.M = mok.mok_forward_minibatch(self.desc, wl.T)
         mx = wl.act_format == mok.MOK_ACT_MXFP8_E4M3
         dev = "cuda"
@@ -125,10 +127,10 @@ class Step:
                                 self.ring, self.ring_sc, self.cap, wl.act_format, self.status)
         rec(3)
         mok.mok_expert_gate_up(self.desc, self.ring, self.ring_sc, self.cap, self.offsets, 0,
-                               self.cap, dw.w_gu, self.act, self.act_sc, self.cap)
+                               self.cap, self.w_gu, self.act, self.act_sc, self.cap)
         rec(4)
         mok.mok_expert_down(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0, self.cap,
-                            dw.w_d, self.y, self.cap)
+                            self.w_d, self.y, self.cap)
         rec(5)
         mok.mok_combine_slots(self.y, self.cap, self.aos, self.offsets, wl.n_local, self.cap,
                               self.soa, gate, wl.k, wl.H, dw.outs[0], self.status)
@@ -148,11 +150,13 @@ def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
     outs = [d0.new_out() for _ in wls]
     res = {}
     for mode, M, n_move in ((0, 2560, 0), (0, 8192, 0), (1, 2560, 32), (1, 4096, 32), (1, 8192, 32)):
-        d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=M, mode=mode, n_move_cus=n_move)
+        d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=M, mode=mode, n_move_cus=n_move,
+                    weights_packed=1)
+        w_gu, w_d = d0.weights(d)
         ws = torch.empty(mok.mok_forward_workspace_size(d, d0.wl.T, n_macro), dtype=torch.uint8,
                          device="cuda")
-        run = lambda: mok.mok_moe_forward_batches(d, n_macro, idx, gate, d0.wl.T, d0.x, d0.w_gu,
-                                                  d0.w_d, outs, ws)
+        run = lambda: mok.mok_moe_forward_batches(d, n_macro, idx, gate, d0.wl.T, d0.x, w_gu,
+                                                  w_d, outs, ws)
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -262,12 +266,14 @@ def main():
     max_rows = BENCH_MAX_ROWS if not wl.routing_from_logits else wl.T * wl.k
     if args.fused_only:
         mode, M, n_move = (int(v) for v in args.fused_only.split(":"))
-        d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move)
+        d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move,
+                    weights_packed=1)
         ws = torch.empty(mok.mok_forward_workspace_size(d, wl.T, 1), dtype=torch.uint8,
                          device="cuda")
         dw.routing()
+        w_gu, w_d = dw.weights(d)
         for _ in range(5):
-            mok.mok_moe_forward(d, dw.topk_idx, dw.topk_gate, wl.T, dw.x, dw.w_gu, dw.w_d,
+            mok.mok_moe_forward(d, dw.topk_idx, dw.topk_gate, wl.T, dw.x, w_gu, w_d,
                                 dw.outs[0], ws)
         torch.cuda.synchronize()
         print(json.dumps({"fused_only": args.fused_only,
@@ -328,17 +334,19 @@ def main():
         for mode in (mok.MOK_MODE_STREAM, mok.MOK_MODE_PERSISTENT):
             for M in [0] + list(wl.minibatches):
                 for n_move in ((0,) if mode == mok.MOK_MODE_STREAM else (16, 32)):
-                    d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move)
+                    d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move,
+                                weights_packed=1)
+                    w_gu, w_d = dw.weights(d)
                     wsb = mok.mok_forward_workspace_size(d, wl.T, 1)
                     if wsb == 0:
                         continue
                     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
                     for _ in range(3):
-                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, w_gu, w_d, dw.outs[0], ws)
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
                     for _ in range(10):
-                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+                        mok.mok_moe_forward(d, idx, gate, wl.T, dw.x, w_gu, w_d, dw.outs[0], ws)
                     e1.record()
                     torch.cuda.synchronize()
                     assert mok.mok_device_status(ws) == 0

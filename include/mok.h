@@ -83,6 +83,9 @@ typedef struct {
     int32_t wait_timeout_us; /* bound of each device-side wait of the persistent
                                 kernel; 0 = 2 s.  On expiry the kernel stops and
                                 the status word becomes MOK_ERR_DEVICE.        */
+    int32_t weights_packed; /* 0: w_gate_up / w_down in the documented layout;
+                                1: both written by mok_pack_weights for this
+                                hidden, inter, n_local and act_format.         */
 } mok_layer_desc;
 
 /* Tokens held in partitions: token t lives in partition t / part_rows at row
@@ -167,6 +170,20 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring,
                           const void* w_gate_up, const void* w_down,
                           void* act, uint8_t* act_scales, int32_t act_rows,
                           void* y, int32_t y_rows, hipStream_t stream);
+
+/* Weight packing (a layout of this library, not of the pages): one-time
+ * rearrangement of w_gate_up and w_down into the tile order of the grouped
+ * GEMMs, so that each load of a weight tile reads contiguous memory.  The
+ * packed buffers (device, caller-owned, sizes from mok_packed_weights_size)
+ * are then passed in place of the documented ones with desc->weights_packed
+ * = 1; results are bit-identical.  The packed format depends on hidden,
+ * inter, n_local and act_format and is private to this library version.
+ * Either pair (source, packed) may be null to pack only the other; a pair
+ * with one null pointer is MOK_ERR_INVALID_ARG.  Asynchronous on stream. */
+mok_status mok_packed_weights_size(const mok_layer_desc* desc, size_t* gate_up_bytes,
+                                   size_t* down_bytes);
+mok_status mok_pack_weights(const mok_layer_desc* desc, const void* w_gate_up, const void* w_down,
+                            void* packed_gate_up, void* packed_down, hipStream_t stream);
 
 /* The two grouped GEMMs of mok_expert_ffn as separate calls, same layouts:
  * gate/up + SwiGLU (ring -> act) and down (act -> y). */

@@ -107,6 +107,21 @@ class DeviceWorkload:
         wl = self.wl
         return gpu_schedule(idx, wl.T, wl.k, wl.expert_base, wl.n_local)
 
+    def packed(self):
+        """(gate_up, down) weights packed by mok_pack_weights for this workload."""
+        if getattr(self, "_packed", None) is None:
+            d = self.desc()
+            gu, dn = mok.mok_packed_weights_size(d)
+            pgu = torch.empty(gu, dtype=torch.uint8, device="cuda")
+            pdn = torch.empty(dn, dtype=torch.uint8, device="cuda")
+            mok.mok_pack_weights(d, self.w_gu, self.w_d, pgu, pdn)
+            self._packed = (pgu, pdn)
+        return self._packed
+
+    def weights(self, desc):
+        """The weight buffers matching desc.weights_packed."""
+        return self.packed() if desc.weights_packed else (self.w_gu, self.w_d)
+
     def forward(self, out=None, **desc_kw):
         wl = self.wl
         out = self.outs[0] if out is None else out
@@ -115,7 +130,8 @@ class DeviceWorkload:
         wsb = mok.mok_forward_workspace_size(d, wl.T, 1)
         assert wsb > 0
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-        mok.mok_moe_forward(d, idx, gate, wl.T, self.x, self.w_gu, self.w_d, out, ws)
+        w_gu, w_d = self.weights(d)
+        mok.mok_moe_forward(d, idx, gate, wl.T, self.x, w_gu, w_d, out, ws)
         return ws, d
 
 

@@ -94,3 +94,18 @@ def test_forward_minibatch_plan():
     assert mok.mok_forward_minibatch(_desc(minibatch=100), 256) == 100
     assert mok.mok_forward_minibatch(_desc(minibatch=5000), 256) == 512
     assert mok.mok_forward_minibatch(_desc(minibatch=100, max_rows=64), 256) == 64
+
+
+def test_packed_weight_sizes_and_argument_checks():
+    d = mok.mok_layer_desc(hidden=576, inter=320, n_experts=32, top_k=4, expert_base=3,
+                           n_local=5)
+    gu, dn = mok.mok_packed_weights_size(d)
+    # column tiles of 128 intermediate columns (gate + up rows: 256) and of 256 hidden rows
+    assert gu == 5 * 3 * 256 * 576 * 2 and dn == 5 * 3 * 256 * 320 * 2
+    E = mok.MOK_ERR_INVALID_ARG
+    assert L.mok_pack_weights(C.byref(d), 1, None, None, None, None) == E     # source, no target
+    assert L.mok_pack_weights(C.byref(d), None, None, None, None, None) == E  # nothing to pack
+    assert L.mok_pack_weights(C.byref(d), None, 1, None, None, None) == E     # down half-pair
+    bad = mok.mok_layer_desc(hidden=576, inter=320, n_experts=32, top_k=4, expert_base=3,
+                             n_local=5, weights_packed=2)
+    assert L.mok_packed_weights_size(C.byref(bad), None, None) == E

@@ -44,7 +44,8 @@ class MokError(RuntimeError):
 class mok_layer_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "expert_base", "n_local", "act_format",
-        "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode", "wait_timeout_us")]
+        "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode", "wait_timeout_us",
+        "weights_packed")]
 
 
 class mok_tokens(C.Structure):
@@ -64,6 +65,8 @@ _SIGS = {
     "mok_expert_ffn": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P,
                                  _I32, _P]),
     "mok_expert_gate_up": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "mok_packed_weights_size": (C.c_int, [_DESC, C.POINTER(_SZ), C.POINTER(_SZ)]),
+    "mok_pack_weights": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
     "mok_expert_down": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P]),
     "mok_combine": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _I32, _TOK, _P, _P]),
     "mok_combine_slots": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _TOK, _P,
@@ -182,6 +185,21 @@ def mok_expert_ffn(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, off
                                _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up), _ptr(w_down),
                                _ptr(act), _ptr(act_scales), act_rows, _ptr(y), y_rows,
                                _stream(stream)), "mok_expert_ffn")
+
+
+def mok_packed_weights_size(desc: mok_layer_desc):
+    """(gate_up_bytes, down_bytes) of the packed weights for desc."""
+    gu, dn = _SZ(0), _SZ(0)
+    _check(_lib.mok_packed_weights_size(C.byref(desc), C.byref(gu), C.byref(dn)),
+           "mok_packed_weights_size")
+    return gu.value, dn.value
+
+
+def mok_pack_weights(desc: mok_layer_desc, w_gate_up, w_down, packed_gate_up, packed_down,
+                     stream=None) -> None:
+    _check(_lib.mok_pack_weights(C.byref(desc), _ptr(w_gate_up), _ptr(w_down),
+                                 _ptr(packed_gate_up), _ptr(packed_down), _stream(stream)),
+           "mok_pack_weights")
 
 
 def mok_expert_gate_up(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, offsets,

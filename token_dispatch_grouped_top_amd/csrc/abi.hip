@@ -48,6 +48,7 @@ bool desc_ok(const mok_layer_desc* d) {
   if (!d) return false;
   if (d->hidden <= 0 || d->hidden % 64 != 0) return false;
   if (d->inter <= 0 || d->inter % 64 != 0) return false;
+  if (d->weights_packed != 0 && d->weights_packed != 1) return false;
   if (d->n_local < 1 || d->n_local > 256) return false;
   if (d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts) return false;
   if (d->expert_base < 0 || d->expert_base + d->n_local > d->n_experts) return false;
@@ -210,6 +211,26 @@ mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
                                   ring_scales, ring_slots, act_format, dev_status, stream));
 }
 
+mok_status mok_packed_weights_size(const mok_layer_desc* desc, size_t* gate_up_bytes,
+                                   size_t* down_bytes) {
+  if (!desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (gate_up_bytes) *gate_up_bytes = packed_gate_up_bytes(desc->hidden, desc->inter, desc->n_local);
+  if (down_bytes) *down_bytes = packed_down_bytes(desc->hidden, desc->inter, desc->n_local);
+  return MOK_OK;
+}
+
+mok_status mok_pack_weights(const mok_layer_desc* desc, const void* w_gate_up, const void* w_down,
+                            void* packed_gate_up, void* packed_down, hipStream_t stream) {
+  if (!desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!w_gate_up != !packed_gate_up || !w_down != !packed_down) return MOK_ERR_INVALID_ARG;
+  if (!w_gate_up && !w_down) return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_pack_weights(static_cast<const uint16_t*>(w_gate_up),
+                                        static_cast<const uint16_t*>(w_down), desc->hidden,
+                                        desc->inter, desc->n_local, desc->act_format,
+                                        static_cast<uint16_t*>(packed_gate_up),
+                                        static_cast<uint16_t*>(packed_down), stream));
+}
+
 mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const uint8_t* ring_scales,
                           int32_t ring_slots, const int32_t* offsets, int32_t slot_begin,
                           int32_t slot_end, const void* w_gate_up, const void* w_down, void* act,
@@ -227,6 +248,7 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
   a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
   a.y = y; a.y_rows = y_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  a.w_packed = desc->weights_packed;
   return hip_status(launch_ffn(a, stream));
 }
 
@@ -246,6 +268,7 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
   a.w_gu = static_cast<const uint16_t*>(w_gate_up);
   a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  a.w_packed = desc->weights_packed;
   return hip_status(launch_gate_up(a, stream));
 }
 
@@ -263,6 +286,7 @@ mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const ui
   a.act = const_cast<void*>(act); a.act_scales = const_cast<uint8_t*>(act_scales);
   a.act_rows = act_rows; a.y = y; a.y_rows = y_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  a.w_packed = desc->weights_packed;
   return hip_status(launch_down(a, stream));
 }
 
@@ -369,6 +393,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
     pa.M = p.M; pa.S = p.S; pa.nwin = p.nwin; pa.cap = p.cap;
     pa.x = *x; pa.w_gu = static_cast<const uint16_t*>(w_gate_up);
     pa.w_d = static_cast<const uint16_t*>(w_down);
+    pa.w_packed = d.weights_packed;
     pa.ring = ring; pa.ring_sc = ring_sc; pa.act = act; pa.act_sc = act_sc; pa.act_rows = p.act_rows;
     pa.status = status; pa.pers_ws = at<void>(ws, p.off_pers);
     pa.n_move = d.n_move_cus; pa.n_cus = device_cus(); pa.timeout_us = d.wait_timeout_us;
@@ -391,6 +416,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       a.act = act; a.act_scales = act_sc; a.act_rows = p.act_rows;
       a.y = mb[m].y; a.y_rows = p.cap;
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
+      a.w_packed = d.weights_packed;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
     err = launch_combine_slots(mb[m].y, p.cap, mb[m].aos, mb[m].offsets, d.n_local, p.cap,

@@ -50,6 +50,45 @@ void k_ffn_gemm(const GemmParams p) {
   gemm_tile<A_MX, EPI>(p, e, row0, nrows, ntile, lds);
 }
 
+// Packing: one thread per 16-byte piece of the packed weights.  Block
+// (e, column tile, k-step) holds the tile's 256 weight rows x BK in the byte
+// order the GEMM's direct-to-LDS loads land them (chunk swizzle included).
+template <bool A_MX>
+__global__ __launch_bounds__(256)
+void k_pack_weights(const uint16_t* __restrict__ W, int64_t expert_stride, int32_t K, int32_t I,
+                    int32_t N, int32_t swiglu, int32_t n_tiles, int32_t n_local,
+                    uint16_t* __restrict__ out) {
+  using G = Geo<A_MX>;
+  constexpr int BK = G::BK;
+  constexpr int64_t kPieces = BM * BK / 8;                 // 16-byte pieces per block
+  const int nk = K / BK;
+  const int64_t total = static_cast<int64_t>(n_local) * n_tiles * nk * kPieces;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t blk = u / kPieces;
+    const int o = static_cast<int>(u % kPieces) * 16;      // byte offset in the block
+    const int kt = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;
+    const int nt = static_cast<int>(et % n_tiles), e = static_cast<int>(et / n_tiles);
+    const int row = o / G::ROWB_B;
+    const int chunk = ((o % G::ROWB_B) >> 4) ^ chunk_key<G::CPR_B>(row);
+    const int wrow = w_row_of(row, nt, swiglu != 0, I, N);
+    reinterpret_cast<uint4*>(out)[u] = *reinterpret_cast<const uint4*>(
+        W + e * expert_stride + static_cast<int64_t>(wrow) * K + kt * BK + chunk * 8);
+  }
+}
+
+template <bool A_MX>
+hipError_t pack_one(const uint16_t* W, int64_t stride, int32_t K, int32_t I, int32_t N, bool swiglu,
+                    int32_t n_tiles, int32_t n_local, uint16_t* out, hipStream_t s) {
+  const int64_t pieces = static_cast<int64_t>(n_local) * n_tiles * (K / Geo<A_MX>::BK) *
+                         (BM * Geo<A_MX>::BK / 8);
+  const int64_t blocks = (pieces + 255) / 256;
+  hipLaunchKernelGGL(k_pack_weights<A_MX>, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                     dim3(256), 0, s, W, stride, K, I, N, swiglu ? 1 : 0, n_tiles, n_local, out);
+  return hipGetLastError();
+}
+
 template <bool A_MX, int EPI>
 hipError_t launch_one(GemmParams gp, int n_tiles, int m_tiles, hipStream_t s) {
   gp.n_tiles = n_tiles;
@@ -69,6 +108,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
   g.N = a.I; g.I = a.I;
   g.C = a.act; g.C_scales = a.act_scales; g.c_rows = a.act_rows;
+  g.w_packed = a.w_packed;
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
                                              : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
@@ -84,9 +124,32 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   g.W = a.w_d; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.I;
   g.N = a.H; g.I = 0;
   g.C = a.y; g.C_scales = nullptr; g.c_rows = a.y_rows;
+  g.w_packed = a.w_packed;
   const int n2 = (a.H + BN - 1) / BN;
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
                                              : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+}
+
+size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local) {
+  return static_cast<size_t>(n_local) * ((I + BN / 2 - 1) / (BN / 2)) * BM * H * 2;
+}
+size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local) {
+  return static_cast<size_t>(n_local) * ((H + BN - 1) / BN) * BM * I * 2;
+}
+
+hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
+                               int32_t n_local, int32_t act_format, uint16_t* packed_gu,
+                               uint16_t* packed_d, hipStream_t s) {
+  const bool mx = act_format == MOK_ACT_MXFP8_E4M3;
+  const int n1 = (I + BN / 2 - 1) / (BN / 2), n2 = (H + BN - 1) / BN;
+  hipError_t err = hipSuccess;
+  if (w_gu && packed_gu)
+    err = mx ? pack_one<true>(w_gu, static_cast<int64_t>(2) * I * H, H, I, 0, true, n1, n_local, packed_gu, s)
+             : pack_one<false>(w_gu, static_cast<int64_t>(2) * I * H, H, I, 0, true, n1, n_local, packed_gu, s);
+  if (err == hipSuccess && w_d && packed_d)
+    err = mx ? pack_one<true>(w_d, static_cast<int64_t>(H) * I, I, 0, H, false, n2, n_local, packed_d, s)
+             : pack_one<false>(w_d, static_cast<int64_t>(H) * I, I, 0, H, false, n2, n_local, packed_d, s);
+  return err;
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {

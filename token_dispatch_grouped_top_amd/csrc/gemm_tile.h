@@ -30,11 +30,7 @@ template <> struct Pipe<true> { static constexpr int BK = 64, NS = 3; };
 // Chunk XOR key of an LDS row of `cpr` 16-byte chunks: the b128 fragment reads
 // of 16 consecutive rows at one logical chunk hit distinct banks.
 template <int cpr> __device__ __forceinline__ int chunk_key(int row) {
-#if defined(MOK_SWZ) && MOK_SWZ == 0
-  return 0;
-#else
   return cpr == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
-#endif
 }
 
 // LDS geometry of one pipeline stage: [A tile][B tile][A scales].
@@ -79,6 +75,7 @@ struct GemmParams {
   int32_t n_local;
   int32_t s_begin, s_end;
   int32_t n_tiles;            // output column tiles
+  int32_t w_packed;           // W in the packed tile order written by launch_pack_weights
   int32_t a_row_base;         // A row of slot s: (s + a_row_base) % a_rows
   int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
 };
@@ -141,6 +138,22 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
                  ntile);
 }
 
+// Weight row held by row nb (0..255) of the B tile of output column tile
+// `ntile`.  gate/up (swiglu): B rows 0..127 feed wave column 0, 128..255 wave
+// column 1; in each, 64 gate rows then the 64 up rows of the same
+// intermediate columns, so a lane's accumulators hold g and u of one (row, i).
+// Columns past the end are clamped to the last one (masked at the store).
+__device__ __forceinline__ int w_row_of(int nb, int ntile, bool swiglu, int32_t I, int32_t N) {
+  if (swiglu) {
+    const int wc = nb >> 7, q = nb & 127;
+    int icol = ntile * (BN / 2) + 64 * wc + (q & 63);
+    if (icol >= I) icol = I - 1;
+    return (q < 64) ? icol : I + icol;
+  }
+  const int wrow = ntile * BN + nb;
+  return wrow < N ? wrow : N - 1;
+}
+
 template <int N> __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -168,28 +181,29 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   // lands at physical chunk l % CPR of row l / CPR of that KiB, so it fetches
   // the logical chunk (l % CPR) ^ key(row).  Thread rows: tid / CPR + RSTEP * j
   // (the key repeats every 16 rows and RSTEP is a multiple of 16).
-  const uint16_t* Wexp = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
-  const int lrowB = tid / G::CPR_B;
-  const int lchunkB = (lane % G::CPR_B) ^ chunk_key<G::CPR_B>(lrowB);
+  // Weights: load j of k-step kt reads Wbase + kt * wkstride + boff[j].
+  //   documented layout: the thread's row and swizzled chunk of expert e;
+  //   packed layout: the tile's blocks are stored in LDS-image order, so a
+  //   wave instruction reads 1 KiB of contiguous memory.
+  const uint16_t* Wbase;
+  int32_t wkstride;
   // (fixed-size arrays: a template-dependent bound here made the host pass
   // drop the kernel's launch stub)
-  uint32_t boff[8];                                           // element offsets in Wexp
+  uint32_t boff[8];
+  if (p.w_packed) {
+    Wbase = p.W + (static_cast<int64_t>(e) * p.n_tiles + ntile) * nk * (BM * BK);
+    wkstride = BM * BK;
 #pragma unroll
-  for (int j = 0; j < G::NLOAD_B; ++j) {
-    const int nb = lrowB + G::RSTEP_B * j;
-    int wrow;
-    if (swiglu) {
-      // B rows 0..127 -> wave column 0, 128..255 -> 1; in each, 64 gate rows
-      // then the 64 up rows of the same intermediate columns.
-      const int wc = nb >> 7, q = nb & 127;
-      int icol = n0 + 64 * wc + (q & 63);
-      if (icol >= p.I) icol = p.I - 1;                        // clamp; masked at the store
-      wrow = (q < 64) ? icol : p.I + icol;
-    } else {
-      wrow = n0 + nb;
-      if (wrow >= p.N) wrow = p.N - 1;
-    }
-    boff[j] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K) + lchunkB * 8;
+    for (int j = 0; j < G::NLOAD_B; ++j) boff[j] = (4 * j + wave) * 512 + lane * 8;
+  } else {
+    Wbase = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
+    wkstride = BK;
+    const int lrowB = tid / G::CPR_B;
+    const int lchunkB = (lane % G::CPR_B) ^ chunk_key<G::CPR_B>(lrowB);
+#pragma unroll
+    for (int j = 0; j < G::NLOAD_B; ++j)
+      boff[j] = static_cast<uint32_t>(w_row_of(lrowB + G::RSTEP_B * j, ntile, swiglu, p.I, p.N)) *
+                    static_cast<uint32_t>(K) + lchunkB * 8;
   }
   // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
   auto a_ring_row = [&](int r) -> uint32_t {
@@ -209,12 +223,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) : 0;
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
-#if defined(MOK_BUFLDS) && MOK_BUFLDS
-  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Wexp), 0, static_cast<int>(p.w_expert_stride * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Abf), 0, static_cast<int>(static_cast<int64_t>(p.a_rows) * K * 2), 0x00020000);
-#endif
   auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
   auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A; };
   auto tileS = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A + G::TILE_B; };
@@ -230,13 +238,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
 
-#if defined(MOK_BUFLDS) && MOK_BUFLDS
-#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(dst), 16, boff[j] * 2, (kt) * BK * 2, 0, 0)
-#define MOK_LD_A(j, kt, dst) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst), 16, aoff[j] * 2, (kt) * BK * 2, 0, 0)
-#else
-#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_global_load_lds(Wexp + boff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
+#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_global_load_lds(Wbase + (kt) * wkstride + boff[j], (lds_ptr_t)(dst), 16, 0, 0)
 #define MOK_LD_A(j, kt, dst) __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
-#endif
   // The two halves of a stage's direct loads: weights; tokens (+ E4M3 scales,
   // 2 bytes per lane, which land in 4-byte slots: lane i at slot base + 4 i).
 #define MOK_ISSUE_W(kt, buf)                                                                 \

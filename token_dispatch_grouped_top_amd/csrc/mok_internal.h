@@ -148,9 +148,16 @@ struct FfnArgs {
   void* act; uint8_t* act_scales; int32_t act_rows;
   void* y; int32_t y_rows;
   int32_t H, I, act_format;
+  int32_t w_packed;           // weights in the packed tile order (launch_pack_weights)
 };
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// Packed weights: bytes, and the packing launch (either source may be null).
+size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
+size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local);
+hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
+                               int32_t n_local, int32_t act_format, uint16_t* packed_gu,
+                               uint16_t* packed_d, hipStream_t s);
 
 }  // namespace mok

@@ -25,6 +25,7 @@ struct PersistentArgs {
   mok_tokens x;
   const uint16_t* w_gu;
   const uint16_t* w_d;
+  int32_t w_packed;         // weights in the packed tile order
   void* ring; uint8_t* ring_sc;
   void* act; uint8_t* act_sc; int32_t act_rows;
   int32_t* status;

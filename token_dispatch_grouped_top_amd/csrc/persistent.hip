@@ -71,6 +71,7 @@ struct PKArgs {
   int32_t x_n_part, x_part_rows;
   const uint16_t* w_gu;
   const uint16_t* w_d;
+  int32_t w_packed;
   void* ring;
   uint8_t* ring_sc;
   void* act;
@@ -297,7 +298,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
       g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
       g.N = a.I; g.I = a.I;
       g.C = a.act; g.C_scales = a.act_sc; g.c_rows = a.act_rows; g.c_row_base = rb;
-      g.n_tiles = n1;
+      g.n_tiles = n1; g.w_packed = a.w_packed;
       gemm_tile<A_MX, A_MX ? EPI_SWIGLU_MX : EPI_SWIGLU_BF16>(g, e, row0, nrows, ntile, lds);
       signal_add(&c.gu_done[w]);
     } else {
@@ -305,7 +306,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
       g.W = a.w_d; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.I;
       g.N = a.H; g.I = 0;
       g.C = pm.y; g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
-      g.n_tiles = n2;
+      g.n_tiles = n2; g.w_packed = a.w_packed;
       gemm_tile<A_MX, EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
       signal_add(&c.dn_done[w]);
     }
@@ -357,7 +358,7 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     k.act_format = a.act_format; k.M = a.M; k.S = a.S; k.cap = a.cap; k.n_move = n_move;
     k.max_win = gn * a.nwin;
     k.x_parts = a.x.part_ptr; k.x_n_part = a.x.n_partitions; k.x_part_rows = a.x.part_rows;
-    k.w_gu = a.w_gu; k.w_d = a.w_d;
+    k.w_gu = a.w_gu; k.w_d = a.w_d; k.w_packed = a.w_packed;
     k.ring = a.ring; k.ring_sc = a.ring_sc; k.act = a.act; k.act_sc = a.act_sc;
     k.act_rows = a.act_rows; k.status = a.status; k.ctl = static_cast<int32_t*>(a.pers_ws);
     k.timeout_ticks = timeout_us * 100;           // s_memrealtime runs at 100 MHz
