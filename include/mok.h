@@ -145,7 +145,9 @@ mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M,
  * MOK_ACT_MXFP8_E4M3: ring is E4M3 codes u8 [ring_slots][H] and ring_scales
  * E8M0 u8 [ring_slots][H/32] (OCP MX v1.0 blocks of 32 along H).
  * A token index outside src sets *dev_status = MOK_ERR_CAPACITY and the row
- * is skipped. */
+ * is skipped.  assign_of_slot is read at every slot of [slot_begin,
+ * slot_end) (entries at or past R are ignored), so it holds slot_end
+ * entries. */
 mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
                                const int32_t* assign_of_slot, const int32_t* offsets,
                                int32_t n_local, int32_t slot_begin, int32_t slot_end,
@@ -212,6 +214,8 @@ mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_ass
  * token assign_of_slot[s] / k when s is that token's smallest local slot, so
  * each token with a local assignment is written once and only R slots are
  * visited instead of all T tokens.  Output identical to mok_combine.
+ * assign_of_slot is read at every slot s < n_slots, so it holds n_slots
+ * entries.
  * offsets: int32 [n_local + 1] (R = offsets[n_local]). */
 mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assign_of_slot,
                              const int32_t* offsets, int32_t n_local, int32_t n_slots,

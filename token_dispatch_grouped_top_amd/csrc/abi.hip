@@ -101,7 +101,7 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.per_macro_counts = align_up(nl * 4);
   p.per_macro_offsets = align_up((nl + 1) * 4);
   p.per_macro_soa = align_up(std::max<int64_t>(p.A, 1) * 4);
-  p.per_macro_aos = align_up(std::max<int64_t>(p.A, 1) * 4);
+  p.per_macro_aos = align_up(std::max<int64_t>(std::max<int64_t>(p.A, p.cap), 1) * 4);
   p.per_macro_win = align_up(static_cast<size_t>(p.nwin) * (nl + 1) * 4);
   p.off_counts = take(p.per_macro_counts * n_macro);
   p.off_offsets = take(p.per_macro_offsets * n_macro);

@@ -20,9 +20,11 @@ void k_gather_bf16(void* const* __restrict__ parts, int32_t n_part, int32_t part
                    int32_t* status) {
   const int64_t s = static_cast<int64_t>(s_begin) + static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
                     threadIdx.x / kWave;
+  if (s >= s_end) return;
+  const int32_t a = aos[s];                 // issued together with R (aos holds s_end entries)
   const int32_t R = offsets[n_local];
-  if (s >= s_end || s >= R) return;
-  gather_row_bf16(parts, n_part, part_rows, H, k, aos, s, ring, s % ring_slots, status);
+  if (s >= R) return;
+  gather_row_bf16(parts, n_part, part_rows, H, a / k, ring, s % ring_slots, status);
 }
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
@@ -33,9 +35,11 @@ void k_gather_mxfp8(void* const* __restrict__ parts, int32_t n_part, int32_t par
                     int32_t ring_slots, int32_t* status) {
   const int64_t s = static_cast<int64_t>(s_begin) + static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
                     threadIdx.x / kWave;
+  if (s >= s_end) return;
+  const int32_t a = aos[s];                 // issued together with R (aos holds s_end entries)
   const int32_t R = offsets[n_local];
-  if (s >= s_end || s >= R) return;
-  gather_row_mxfp8(parts, n_part, part_rows, H, k, aos, s, ring, scales, s % ring_slots, status);
+  if (s >= R) return;
+  gather_row_mxfp8(parts, n_part, part_rows, H, a / k, ring, scales, s % ring_slots, status);
 }
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
@@ -58,10 +62,12 @@ void k_combine_slots(const uint16_t* __restrict__ y, int32_t y_rows,
                      void* const* __restrict__ out_parts, int32_t n_part, int32_t part_rows,
                      int32_t* status, bool abort_on_status) {
   const int64_t s = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (s >= n_slots) return;
+  const int32_t a = aos[s];                 // issued together with R (aos holds n_slots entries)
   const int32_t R = offsets[n_local];
-  if (s >= n_slots || s >= R) return;
+  if (s >= R) return;
   if (abort_on_status && *status != 0) return;
-  merge_slot(y, y_rows, aos, soa, gate, s, k, H, out_parts, n_part, part_rows, status);
+  merge_slot(y, y_rows, a, soa, gate, s, k, H, out_parts, n_part, part_rows, status);
 }
 
 }  // namespace

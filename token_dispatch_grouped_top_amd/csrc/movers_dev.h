@@ -28,14 +28,12 @@ __device__ __forceinline__ const uint4* token_row(void* const* parts, int32_t n_
   return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(parts[p]) + r * H);
 }
 
-// Pull slot s (s < R) into ring row dst_row: bf16 bit copy.
+// Pull the row of token t into ring row dst_row: bf16 bit copy.
 __device__ __forceinline__ void gather_row_bf16(void* const* __restrict__ parts, int32_t n_part,
-                                                int32_t part_rows, int32_t H, int32_t k,
-                                                const int32_t* __restrict__ aos, int64_t s,
+                                                int32_t part_rows, int32_t H, int64_t t,
                                                 uint16_t* __restrict__ ring, int64_t dst_row,
                                                 int32_t* status) {
   const int lane = lane_id();
-  const int64_t t = aos[s] / k;
   const uint4* src = token_row(parts, n_part, part_rows, t, H);
   if (!src) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
   uint4* dst = reinterpret_cast<uint4*>(ring + dst_row * static_cast<int64_t>(H));
@@ -58,14 +56,13 @@ __device__ __forceinline__ void gather_row_bf16(void* const* __restrict__ parts,
 // Pull of rows s = first, first + step, ... < end, two rows per wave at a
 // time: both rows' indices are read first, then kBatch 16-byte pieces of each
 // row are loaded before any is stored, so a wave keeps 2 x kBatch pieces per
-// lane in flight (the persistent kernel runs only 4 waves per mover CU).
-// Destination row of slot s: dst_base + s.
+// lane in flight.  Destination row of slot s: (dst_base + s) % ring_slots.
 __device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ parts,
                                                     int32_t n_part, int32_t part_rows, int32_t H,
                                                     int32_t k, const int32_t* __restrict__ aos,
                                                     int64_t first, int64_t step, int64_t end,
-                                                    uint16_t* __restrict__ ring,
-                                                    int64_t dst_base, int32_t* status) {
+                                                    uint16_t* __restrict__ ring, int64_t dst_base,
+                                                    int32_t ring_slots, int32_t* status) {
   const int lane = lane_id();
   const int nvec = H / 8;
   for (int64_t s = first; s < end; s += 2 * step) {
@@ -73,8 +70,8 @@ __device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ pa
     const uint4* src1 = token_row(parts, n_part, part_rows, aos[s] / k, H);
     const uint4* src2 = token_row(parts, n_part, part_rows, aos[s2] / k, H);
     if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); continue; }
-    uint4* d1 = reinterpret_cast<uint4*>(ring + (dst_base + s) * static_cast<int64_t>(H));
-    uint4* d2 = reinterpret_cast<uint4*>(ring + (dst_base + s2) * static_cast<int64_t>(H));
+    uint4* d1 = reinterpret_cast<uint4*>(ring + ((dst_base + s) % ring_slots) * static_cast<int64_t>(H));
+    uint4* d2 = reinterpret_cast<uint4*>(ring + ((dst_base + s2) % ring_slots) * static_cast<int64_t>(H));
     for (int v0 = lane; v0 - lane < nvec; v0 += kWave * kBatch) {
       uint4 b1[kBatch], b2[kBatch];
 #pragma unroll
@@ -95,13 +92,11 @@ __device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ pa
 // consecutive 16-byte pieces, i.e. 4 consecutive lanes; amax by two
 // xor-shuffles.  All 64 lanes must call it (wave-uniform loop).
 __device__ __forceinline__ void gather_row_mxfp8(void* const* __restrict__ parts, int32_t n_part,
-                                                 int32_t part_rows, int32_t H, int32_t k,
-                                                 const int32_t* __restrict__ aos, int64_t s,
+                                                 int32_t part_rows, int32_t H, int64_t t,
                                                  uint8_t* __restrict__ ring,
                                                  uint8_t* __restrict__ scales, int64_t dst_row,
                                                  int32_t* status) {
   const int lane = lane_id();
-  const int64_t t = aos[s] / k;
   const uint4* src = token_row(parts, n_part, part_rows, t, H);
   if (!src) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
   const int64_t rr = dst_row;
@@ -217,14 +212,14 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
 // when s is t's smallest local slot, so every token with a local assignment is
 // merged exactly once while only the R routed slots (not all pool tokens) are
 // visited.  All 64 lanes must call it.
+// a_s = assign_of_slot[s] (the caller loads it early).
 __device__ __forceinline__ void merge_slot(const uint16_t* __restrict__ y, int32_t y_rows,
-                                           const int32_t* __restrict__ aos,
-                                           const int32_t* __restrict__ soa,
+                                           int32_t a_s, const int32_t* __restrict__ soa,
                                            const float* __restrict__ gate, int64_t s, int32_t k,
                                            int32_t H, void* const* __restrict__ out_parts,
                                            int32_t n_part, int32_t part_rows, int32_t* status) {
   const int lane = lane_id();
-  const int64_t t = aos[s] / k;
+  const int64_t t = a_s / k;
   int32_t mine = 0x7fffffff;
   if (lane < k) {
     const int32_t v = soa[t * k + lane];

@@ -225,11 +225,11 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
       const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
       if (A_MX) {
         for (int64_t s = s0 + mw; s < s1; s += nmw)
-          gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s,
+          gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, pm.aos[s] / a.k,
                            static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, a.status);
       } else {
         gather_rows_bf16_x2(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s0 + mw, nmw,
-                            s1, static_cast<uint16_t*>(a.ring), base, a.status);
+                            s1, static_cast<uint16_t*>(a.ring), base, a.S, a.status);
       }
       signal_add(&c.gathered[w]);
     } else {
@@ -239,7 +239,7 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
       const PMacro pm = c.pm[m];
       const int32_t R = pm.offsets[a.n_local];
       for (int64_t s = mw; s < R; s += nmw)
-        merge_slot(pm.y, a.cap, pm.aos, pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
+        merge_slot(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
                    pm.out_n_part, pm.out_part_rows, a.status);
       signal_add(&c.merged[m]);
     }
