@@ -31,23 +31,27 @@ constexpr int kStepsPerWave = 16;
 constexpr int kChunk = kSchedThreads * kStepsPerWave;  // 4096 assignments per block
 constexpr int kMaxLocal = 256;
 
-__device__ __forceinline__ uint32_t local_key(const int32_t* idx, int64_t a, int64_t A,
-                                              int32_t base, int32_t n_local) {
-  if (a >= A) return static_cast<uint32_t>(n_local);
-  int32_t e = idx[a] - base;
-  return (e >= 0 && e < n_local) ? static_cast<uint32_t>(e) : static_cast<uint32_t>(n_local);
-}
-
 __device__ __forceinline__ int key_bits(int32_t n_local) { return 32 - __clz(n_local); }
 
-// The keys of a wave's 1024 assignments, all loaded before any is used (the
-// steps below are otherwise one dependent global load each).
+// The keys of a wave's 1024 assignments, all loaded before any is used: the
+// loads are unconditional (index clamped into [0, A)), so they are issued
+// back to back instead of one guarded load and wait per step.  A >= 1.
 __device__ __forceinline__ void load_keys(const int32_t* __restrict__ idx, int64_t A, int32_t base,
                                           int32_t n_local, int64_t a0, uint32_t (&keys)[kStepsPerWave]) {
   const int lane = lane_id();
+  int32_t v[kStepsPerWave];
 #pragma unroll
-  for (int it = 0; it < kStepsPerWave; ++it)
-    keys[it] = local_key(idx, a0 + it * kWave + lane, A, base, n_local);
+  for (int it = 0; it < kStepsPerWave; ++it) {
+    const int64_t a = a0 + it * kWave + lane;
+    v[it] = idx[a < A ? a : A - 1];
+  }
+#pragma unroll
+  for (int it = 0; it < kStepsPerWave; ++it) {
+    const int64_t a = a0 + it * kWave + lane;
+    const int32_t e = v[it] - base;
+    keys[it] = (a < A && e >= 0 && e < n_local) ? static_cast<uint32_t>(e)
+                                                 : static_cast<uint32_t>(n_local);
+  }
 }
 
 // Per-wave histogram of the block's chunk into h[wave][e].
@@ -72,9 +76,14 @@ void k_sched_count(const int32_t* __restrict__ idx, int64_t A, int32_t base, int
                    int32_t nblk, int32_t* __restrict__ blk_counts) {
   __shared__ int32_t h[kSchedWaves][kMaxLocal];
   uint32_t keys[kStepsPerWave];
-  load_keys(idx, A, base, n_local,
-            static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave),
-            keys);
+  if (A > 0) {
+    load_keys(idx, A, base, n_local,
+              static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave),
+              keys);
+  } else {
+#pragma unroll
+    for (int it = 0; it < kStepsPerWave; ++it) keys[it] = static_cast<uint32_t>(n_local);
+  }
   wave_histogram(keys, n_local, h);
   __syncthreads();
   for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
