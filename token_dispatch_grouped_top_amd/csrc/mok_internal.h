@@ -112,7 +112,6 @@ hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t 
 
 struct SchedWs {
   int32_t* blk_counts;  // [n_local][nblk]
-  int32_t* blk_base;    // [n_local][nblk]
   int32_t nblk;
 };
 size_t sched_ws_bytes(int64_t A, int32_t n_local);

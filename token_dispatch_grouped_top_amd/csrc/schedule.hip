@@ -7,15 +7,15 @@
 // no CPU-GPU exchange.  Reading of the slot order (not fixed by the pages):
 // stable in assignment id a = t*k + j, i.e. a counting sort.
 //
-// Three launches, no atomics on the data path, so the result is unique:
+// Two launches, no atomics on the data path, so the result is unique:
 //   count   -- each block takes a chunk of 4096 assignments; each wave takes
 //              1024 consecutive ones in 16 steps of 64 and groups equal keys
 //              with ballots on the key bits (match_key); the lowest lane of a
 //              group adds the group size to the wave's LDS histogram.
-//   scan    -- one block: per expert, exclusive scan over the blocks (one
-//              wave per expert, shuffles), then the exclusive scan over
-//              experts gives offsets.
-//   scatter -- recount per wave; wave cursor = offsets[e] + block prefix +
+//   scatter -- every block sums the per-block counts into the expert totals
+//              and its own block prefix (LDS atomics on counts only), scans
+//              the totals into offsets (block 0 writes counts and offsets),
+//              recounts per wave; wave cursor = offsets[e] + block prefix +
 //              prefix over the block's waves; each lane's slot = wave cursor
 //              + popcount(group & lanes below).
 // A wave loads the keys of all its steps before the first ballot.
@@ -94,33 +94,36 @@ void k_sched_count(const int32_t* __restrict__ idx, int64_t A, int32_t base, int
   }
 }
 
-// One block of 1024 threads; wave w scans experts w, w+16, ...  blk_base gets
-// the exclusive prefix over blocks only; the scatter adds offsets[e].
-__global__ __launch_bounds__(1024)
-void k_sched_scan(const int32_t* __restrict__ blk_counts, int32_t n_local, int32_t nblk,
-                  int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
-                  int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[kMaxLocal];
-  __shared__ int32_t off[kMaxLocal + 1];
-  const int w = threadIdx.x / kWave, lane = lane_id(), nw = blockDim.x / kWave;
-  for (int e = w; e < n_local; e += nw) {
-    const int32_t* c = blk_counts + static_cast<int64_t>(e) * nblk;
-    int32_t* b = blk_base + static_cast<int64_t>(e) * nblk;
-    int32_t run = 0;
-    for (int j0 = 0; j0 < nblk; j0 += kWave) {
-      int j = j0 + lane;
-      int32_t v = j < nblk ? c[j] : 0;
-      int32_t incl = v;
+__global__ __launch_bounds__(kSchedThreads)
+void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
+                     int32_t nblk, const int32_t* __restrict__ blk_counts,
+                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                     int32_t* __restrict__ soa, int32_t* __restrict__ aos) {
+  __shared__ int32_t h[kSchedWaves][kMaxLocal];
+  __shared__ int32_t cur[kSchedWaves][kMaxLocal];
+  __shared__ int32_t tot[kMaxLocal], pre[kMaxLocal], off[kMaxLocal + 1];
+  const int64_t a0w =
+      static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave);
+  uint32_t keys[kStepsPerWave];
+  if (A > 0) {
+    load_keys(idx, A, base, n_local, a0w, keys);
+  } else {
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        int32_t t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      if (j < nblk) b[j] = run + incl - v;
-      run += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) tot[e] = run;
+    for (int it = 0; it < kStepsPerWave; ++it) keys[it] = static_cast<uint32_t>(n_local);
   }
+  for (int e = threadIdx.x; e < n_local; e += kSchedThreads) { tot[e] = 0; pre[e] = 0; }
+  __syncthreads();
+  // per expert: total over all blocks and prefix over the blocks before this one
+  const int64_t nc = static_cast<int64_t>(n_local) * nblk;
+  for (int64_t i = threadIdx.x; i < nc; i += kSchedThreads) {
+    const int e = static_cast<int>(i / nblk), j = static_cast<int>(i % nblk);
+    const int32_t v = blk_counts[i];
+    if (v) {
+      atomicAdd(&tot[e], v);
+      if (j < static_cast<int>(blockIdx.x)) atomicAdd(&pre[e], v);
+    }
+  }
+  wave_histogram(keys, n_local, h);
   __syncthreads();
   if (threadIdx.x == 0) {
     int32_t acc = 0;
@@ -128,27 +131,13 @@ void k_sched_scan(const int32_t* __restrict__ blk_counts, int32_t n_local, int32
     off[n_local] = acc;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= n_local; e += blockDim.x) {
-    offsets[e] = off[e];
-    if (e < n_local) counts[e] = tot[e];
-  }
-}
-
-__global__ __launch_bounds__(kSchedThreads)
-void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
-                     int32_t nblk, const int32_t* __restrict__ blk_base,
-                     const int32_t* __restrict__ offsets, int32_t* __restrict__ soa,
-                     int32_t* __restrict__ aos) {
-  __shared__ int32_t h[kSchedWaves][kMaxLocal];
-  __shared__ int32_t cur[kSchedWaves][kMaxLocal];
-  const int64_t a0w =
-      static_cast<int64_t>(blockIdx.x) * kChunk + (threadIdx.x / kWave) * (kWave * kStepsPerWave);
-  uint32_t keys[kStepsPerWave];
-  load_keys(idx, A, base, n_local, a0w, keys);
-  wave_histogram(keys, n_local, h);
-  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = threadIdx.x; e <= n_local; e += kSchedThreads) {
+      offsets[e] = off[e];
+      if (e < n_local) counts[e] = tot[e];
+    }
   for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
-    int32_t b = offsets[e] + blk_base[static_cast<int64_t>(e) * nblk + blockIdx.x];
+    int32_t b = off[e] + pre[e];
 #pragma unroll
     for (int w = 0; w < kSchedWaves; ++w) { cur[w][e] = b; b += h[w][e]; }
   }
@@ -203,7 +192,6 @@ SchedWs sched_ws_carve(void* ws, int64_t A, int32_t n_local) {
   if (nblk < 1) nblk = 1;
   w.nblk = static_cast<int32_t>(nblk);
   w.blk_counts = static_cast<int32_t*>(ws);
-  w.blk_base = w.blk_counts + nblk * n_local;
   return w;
 }
 
@@ -218,12 +206,8 @@ hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, i
     hipLaunchKernelGGL(k_sched_count, dim3(1), dim3(kSchedThreads), 0, s, idx, A, expert_base,
                        n_local, w.nblk, w.blk_counts);
   }
-  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, s, w.blk_counts, n_local, w.nblk,
-                     w.blk_base, counts, offsets);
-  if (A > 0) {
-    hipLaunchKernelGGL(k_sched_scatter, dim3(w.nblk), dim3(kSchedThreads), 0, s, idx, A,
-                       expert_base, n_local, w.nblk, w.blk_base, offsets, soa, aos);
-  }
+  hipLaunchKernelGGL(k_sched_scatter, dim3(A > 0 ? w.nblk : 1), dim3(kSchedThreads), 0, s, idx, A,
+                     expert_base, n_local, w.nblk, w.blk_counts, counts, offsets, soa, aos);
   return hipGetLastError();
 }
 
