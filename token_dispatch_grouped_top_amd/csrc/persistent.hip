@@ -118,59 +118,100 @@ __global__ void k_fill(int32_t* p, int64_t n) {
 
 // Builds windows, the worker tile sequence and the mover item list on the
 // device from the schedules (no host round trip).
-__global__ void k_plan(const PKArgs a) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  CtlView c(a.ctl, a.max_win);
-  for (int m = 0; m < a.n_macro; ++m) c.pm[m] = a.mb[m];
-  for (int m = 0; m < a.n_macro; ++m) {
-    if (a.mb[m].offsets[a.n_local] > a.cap) {     // more rows than the capacity: no work
+// Plan of one launch, built in LDS (a chain of dependent global reads and
+// writes by one thread took up to 120 us): the macrobatches' offsets are
+// staged by all threads, thread 0 plans windows, the G1/G2 sequence and the
+// mover items, threads 0..7 build the per-XCD prefix tables, and all threads
+// copy the plan out.  Dynamic LDS: plan_lds_bytes().
+constexpr int kPlanMaxWin = 1024;
+
+__host__ __device__ inline size_t plan_lds_words(int n_macro, int n_local, int max_win) {
+  return static_cast<size_t>(n_macro) * (n_local + 1) + 8 * static_cast<size_t>(max_win) + kMaxMacro;
+}
+
+__global__ __launch_bounds__(256) void k_plan(const PKArgs a) {
+  extern __shared__ int32_t plan_lds[];
+  __shared__ int32_t sh_w, sh_ne, sh_ni, sh_fail;
+  const int tid = threadIdx.x, nl1 = a.n_local + 1, MW = a.max_win;
+  int32_t* offs = plan_lds;                                   // [n_macro][n_local + 1]
+  int32_t* wm = offs + a.n_macro * nl1;                       // windows: macrobatch,
+  int32_t* ws0 = wm + MW;                                     //   first slot,
+  int32_t* ws1 = ws0 + MW;                                    //   end slot,
+  int32_t* wn1 = ws1 + MW;                                    //   gate/up tiles,
+  int32_t* wn2 = wn1 + MW;                                    //   down tiles
+  int32_t* ent = wn2 + MW;                                    // [2 MW] sequence
+  int32_t* items = ent + 2 * MW;                              // [MW + kMaxMacro] mover items
+  CtlView c(a.ctl, MW);
+#pragma unroll
+  for (int m = 0; m < kMaxMacro; ++m) {                       // compile-time indices into the args
+    if (m < a.n_macro) {
+      for (int e = tid; e < nl1; e += blockDim.x) offs[m * nl1 + e] = a.mb[m].offsets[e];
+      if (tid == 0) c.pm[m] = a.mb[m];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int fail = 0;
+    for (int m = 0; m < a.n_macro; ++m)
+      if (offs[m * nl1 + a.n_local] > a.cap) fail = 1;       // more rows than the capacity
+    const int n1 = (a.I + BN / 2 - 1) / (BN / 2), n2 = (a.H + BN - 1) / BN;
+    int W = 0, ne = 0, ni = 0;
+    if (!fail) {
+      for (int m = 0; m < a.n_macro; ++m) {
+        const int32_t R = offs[m * nl1 + a.n_local];
+        for (int32_t s0 = 0; s0 < R && W < MW; s0 += a.M) {
+          const int32_t s1 = s0 + a.M < R ? s0 + a.M : R;
+          const int mt = window_mtiles(offs + m * nl1, a.n_local, s0, s1);
+          wm[W] = m; ws0[W] = s0; ws1[W] = s1; wn1[W] = mt * n1; wn2[W] = mt * n2;
+          ++W;
+        }
+      }
+      for (int w = 0; w < W; ++w) {
+        ent[ne++] = 2 * w;
+        if (w >= 1) ent[ne++] = 2 * (w - 1) + 1;
+      }
+      if (W >= 1) ent[ne++] = 2 * (W - 1) + 1;
+      int next_merge = 0, w = 0;
+      for (int m = 0; m < a.n_macro; ++m) {
+        const int32_t R = offs[m * nl1 + a.n_local];
+        const int nw = (R + a.M - 1) / a.M;
+        for (int b = 0; b < nw; ++b, ++w) {
+          items[ni++] = w;
+          if (b >= 1 || nw == 1)
+            while (next_merge < m) items[ni++] = -(next_merge++) - 1;
+        }
+      }
+      while (next_merge < a.n_macro) items[ni++] = -(next_merge++) - 1;
+    }
+    sh_fail = fail; sh_w = W; sh_ne = ne; sh_ni = ni;
+  }
+  __syncthreads();
+  if (sh_fail) {
+    if (tid == 0) {
       set_status(a.status, MOK_ERR_CAPACITY);
       *c.n_windows = 0;
       *c.n_items = 0;
-      return;
     }
+    return;
   }
-  const int n1 = (a.I + BN / 2 - 1) / (BN / 2), n2 = (a.H + BN - 1) / BN;
-  int W = 0;
-  for (int m = 0; m < a.n_macro; ++m) {
-    const int32_t R = a.mb[m].offsets[a.n_local];
-    for (int32_t s0 = 0; s0 < R && W < a.max_win; s0 += a.M) {
-      const int32_t s1 = s0 + a.M < R ? s0 + a.M : R;
-      const int mt = window_mtiles(a.mb[m].offsets, a.n_local, s0, s1);
-      c.win_m[W] = m; c.win_s0[W] = s0; c.win_s1[W] = s1;
-      c.win_nt1[W] = mt * n1; c.win_nt2[W] = mt * n2;
-      ++W;
-    }
-  }
-  *c.n_windows = W;
-  int ne = 0;
-  for (int w = 0; w < W; ++w) {
-    c.ent[ne++] = 2 * w;
-    if (w >= 1) c.ent[ne++] = 2 * (w - 1) + 1;
-  }
-  if (W >= 1) c.ent[ne++] = 2 * (W - 1) + 1;
-  for (int x = 0; x < kXcds; ++x) {
+  const int W = sh_w, ne = sh_ne, ni = sh_ni;
+  if (tid < kXcds) {                                          // XCD tid's share prefix
     int32_t acc = 0;
     for (int q = 0; q < ne; ++q) {
-      const int w = c.ent[q] >> 1;
-      const int32_t tk = (c.ent[q] & 1) ? c.win_nt2[w] : c.win_nt1[w];
-      c.xseq[x * c.xstride + q] = acc;
-      acc += tk / kXcds + (x < tk % kXcds ? 1 : 0);
+      const int w = ent[q] >> 1;
+      const int32_t tk = (ent[q] & 1) ? wn2[w] : wn1[w];
+      c.xseq[tid * c.xstride + q] = acc;
+      acc += tk / kXcds + (tid < tk % kXcds ? 1 : 0);
     }
-    c.xseq[x * c.xstride + ne] = acc;
+    c.xseq[tid * c.xstride + ne] = acc;
   }
-  int ni = 0, next_merge = 0, w = 0;
-  for (int m = 0; m < a.n_macro; ++m) {
-    const int32_t R = a.mb[m].offsets[a.n_local];
-    const int nw = (R + a.M - 1) / a.M;
-    for (int b = 0; b < nw; ++b, ++w) {
-      c.items[ni++] = w;
-      if (b >= 1 || nw == 1)
-        while (next_merge < m) c.items[ni++] = -(next_merge++) - 1;
-    }
+  for (int i = tid; i < W; i += blockDim.x) {
+    c.win_m[i] = wm[i]; c.win_s0[i] = ws0[i]; c.win_s1[i] = ws1[i];
+    c.win_nt1[i] = wn1[i]; c.win_nt2[i] = wn2[i];
   }
-  while (next_merge < a.n_macro) c.items[ni++] = -(next_merge++) - 1;
-  *c.n_items = ni;
+  for (int i = tid; i < ne; i += blockDim.x) c.ent[i] = ent[i];
+  for (int i = tid; i < ni; i += blockDim.x) c.items[i] = items[i];
+  if (tid == 0) { *c.n_windows = W; *c.n_items = ni; }
 }
 
 // Bounded wait by thread 0 for *ctr >= target: relaxed polls, then one
@@ -346,8 +387,10 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
     return MOK_ERR_HIP;
   const uint64_t timeout_us = a.timeout_us > 0 ? static_cast<uint64_t>(a.timeout_us) : 2000000ull;
-  for (int g0 = 0; g0 < a.n_macro; g0 += kMaxMacro) {
-    const int gn = a.n_macro - g0 < kMaxMacro ? a.n_macro - g0 : kMaxMacro;
+  if (a.nwin > kPlanMaxWin) return MOK_ERR_UNSUPPORTED;      // minibatch tiny for the capacity
+  const int group = kPlanMaxWin / a.nwin < kMaxMacro ? kPlanMaxWin / a.nwin : kMaxMacro;
+  for (int g0 = 0; g0 < a.n_macro; g0 += group) {
+    const int gn = a.n_macro - g0 < group ? a.n_macro - g0 : group;
     PKArgs k{};
     for (int m = 0; m < gn; ++m) {
       const MacroBuffers& b = a.mb[g0 + m];
@@ -365,7 +408,8 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     const int64_t words = static_cast<int64_t>(CtlView::words(k.max_win));
     hipLaunchKernelGGL(k_fill, dim3(static_cast<unsigned>((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
                        dim3(256), 0, s, k.ctl, words);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, s, k);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(256),
+                       plan_lds_words(gn, a.n_local, k.max_win) * sizeof(int32_t), s, k);
     if (hipGetLastError() != hipSuccess) return MOK_ERR_HIP;
     void* args[] = {&k};
     if (hipLaunchCooperativeKernel(fn, dim3(a.n_cus), dim3(256), args, 0, s) != hipSuccess)
