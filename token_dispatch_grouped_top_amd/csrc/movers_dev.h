@@ -19,7 +19,9 @@ namespace mok {
 namespace movers {
 
 constexpr int kBatch = 8;          // 16-byte pieces in flight per lane (gather)
-constexpr int kCombPieces = 16;    // 16-byte pieces held per lane (combine)
+constexpr int kCombPieces = 4;     // 16-byte pieces per lane per batch (several local slots:
+                                   // fp32 accumulators; kept small for occupancy)
+constexpr int kMergeFast = 8;      // 16-byte pieces per lane per batch (single local slot)
 
 __device__ __forceinline__ const uint4* token_row(void* const* parts, int32_t n_part,
                                                   int32_t part_rows, int64_t t, int32_t H) {
@@ -147,6 +149,11 @@ __device__ __forceinline__ void gather_row_mxfp8(void* const* __restrict__ parts
 // and broadcast; accumulation per element in fp32 fma in ascending j from 0.
 // A column chunk of 64 lanes x 16 pieces x 8 values (8192 values) is held in
 // registers across the k rows.  All 64 lanes must call it.
+// kFast: single-local-slot fast path and small accumulator batches (the
+// standalone merge: high occupancy).  The persistent kernel's movers use the
+// plain path with large batches: faster movers there steal the HBM / L2
+// bandwidth of the GEMM workers running beside them (measured: slower layer).
+template <bool kFast = true>
 __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, int32_t y_rows,
                                               const int32_t* __restrict__ soa,
                                               const float* __restrict__ gate, int64_t t, int32_t k,
@@ -166,10 +173,41 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
   if (p >= n_part) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
   uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out_parts[p]) + r * H);
   const int nvec = H / 8;
-  for (int c0 = 0; c0 < nvec; c0 += kWave * kCombPieces) {
-    float acc[kCombPieces][8];
+  if (kFast && __popcll(live) == 1) {
+    // one local slot (most tokens): out = bf16(fma(g, y, 0)), as the general
+    // sum gives for a single term, with no accumulators held
+    const int j = __ffsll(static_cast<long long>(live)) - 1;
+    const int32_t s = __shfl(my_s, j);
+    const float g = __shfl(my_g, j);
+    const uint4* src = reinterpret_cast<const uint4*>(y + static_cast<int64_t>(s) * H);
+    for (int c0 = 0; c0 < nvec; c0 += kWave * kMergeFast) {
+      uint4 buf[kMergeFast];
 #pragma unroll
-    for (int u = 0; u < kCombPieces; ++u)
+      for (int u = 0; u < kMergeFast; ++u) {
+        const int v = c0 + lane + u * kWave;
+        if (v < nvec) buf[u] = src[v];
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeFast; ++u) {
+        const int v = c0 + lane + u * kWave;
+        if (v < nvec) {
+          const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(fmaf(g, __uint_as_float(w[q] << 16), 0.0f),
+                               fmaf(g, __uint_as_float(w[q] & 0xffff0000u), 0.0f));
+          st_nt(dst + v, make_uint4(o[0], o[1], o[2], o[3]));
+        }
+      }
+    }
+    return;
+  }
+  constexpr int kPieces = kFast ? kCombPieces : 16;
+  for (int c0 = 0; c0 < nvec; c0 += kWave * kPieces) {
+    float acc[kPieces][8];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
     for (int j = 0; j < k; ++j) {
@@ -177,14 +215,14 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
       const int32_t s = __shfl(my_s, j);
       const float g = __shfl(my_g, j);
       const uint4* src = reinterpret_cast<const uint4*>(y + static_cast<int64_t>(s) * H);
-      uint4 buf[kCombPieces];
+      uint4 buf[kPieces];
 #pragma unroll
-      for (int u = 0; u < kCombPieces; ++u) {
+      for (int u = 0; u < kPieces; ++u) {
         int v = c0 + lane + u * kWave;
         if (v < nvec) buf[u] = src[v];
       }
 #pragma unroll
-      for (int u = 0; u < kCombPieces; ++u) {
+      for (int u = 0; u < kPieces; ++u) {
         const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -194,7 +232,7 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
       }
     }
 #pragma unroll
-    for (int u = 0; u < kCombPieces; ++u) {
+    for (int u = 0; u < kPieces; ++u) {
       int v = c0 + lane + u * kWave;
       if (v < nvec) {
         uint4 o;
@@ -213,6 +251,7 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
 // merged exactly once while only the R routed slots (not all pool tokens) are
 // visited.  All 64 lanes must call it.
 // a_s = assign_of_slot[s] (the caller loads it early).
+template <bool kFast = true>
 __device__ __forceinline__ void merge_slot(const uint16_t* __restrict__ y, int32_t y_rows,
                                            int32_t a_s, const int32_t* __restrict__ soa,
                                            const float* __restrict__ gate, int64_t s, int32_t k,
@@ -228,7 +267,7 @@ __device__ __forceinline__ void merge_slot(const uint16_t* __restrict__ y, int32
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) mine = min(mine, __shfl_xor(mine, off));
   if (mine != s) return;
-  combine_token(y, y_rows, soa, gate, t, k, H, out_parts, n_part, part_rows, status);
+  combine_token<kFast>(y, y_rows, soa, gate, t, k, H, out_parts, n_part, part_rows, status);
 }
 
 }  // namespace movers

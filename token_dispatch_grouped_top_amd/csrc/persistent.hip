@@ -280,7 +280,7 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
       const PMacro pm = c.pm[m];
       const int32_t R = pm.offsets[a.n_local];
       for (int64_t s = mw; s < R; s += nmw)
-        merge_slot(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
+        merge_slot<false>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
                    pm.out_n_part, pm.out_part_rows, a.status);
       signal_add(&c.merged[m]);
     }
