@@ -250,45 +250,75 @@ __device__ __forceinline__ void signal_add(int32_t* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Gather of window w by the waves first, first + step, ...
+template <bool A_MX>
+__device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c, int w,
+                                              int64_t first, int64_t step) {
+  const PMacro pm = c.pm[c.win_m[w]];
+  const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
+  const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
+  if (A_MX) {
+    for (int64_t s = s0 + first; s < s1; s += step)
+      gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, pm.aos[s] / a.k,
+                       static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, a.status);
+  } else {
+    gather_rows_bf16_x2(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s0 + first, step,
+                        s1, static_cast<uint16_t*>(a.ring), base, a.S, a.status);
+  }
+}
+
+// Merge of macrobatch m by the waves first, first + step, ... after every
+// down tile of its windows is done.  kFast: see combine_token.
+template <bool kFast>
+__device__ __forceinline__ bool merge_macro(const PKArgs& a, const CtlView& c, int32_t* sh, int m,
+                                            int64_t first, int64_t step) {
+  const int W = *c.n_windows;
+  for (int w = 0; w < W; ++w)
+    if (c.win_m[w] == m && !wait_geq(&c.dn_done[w], c.win_nt2[w], c, a, sh)) return false;
+  const PMacro pm = c.pm[m];
+  const int32_t R = pm.offsets[a.n_local];
+  for (int64_t s = first; s < R; s += step)
+    merge_slot<kFast>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
+                      pm.out_n_part, pm.out_part_rows, a.status);
+  return true;
+}
+
+// Movers: the item list in order, except window 0 (gathered by every
+// workgroup at the start) and the last macrobatch's merge, which they share
+// with the workers once the GEMMs are done (nothing else runs then, so it is
+// spread over all CUs).  Between those two points the movers run beside the
+// GEMM workers and keep a moderate pace: faster movers there took HBM / L2
+// bandwidth from the workers' operand stream and slowed the layer.
 template <bool A_MX>
 __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t* sh) {
   const int wave = threadIdx.x / kWave;
   const int64_t mw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   const int64_t nmw = static_cast<int64_t>(a.n_move) * 4;
-  const int ni = *c.n_items, W = *c.n_windows;
+  const int ni = *c.n_items;
   for (int it = 0; it < ni; ++it) {
     const int item = c.items[it];
     if (item >= 0) {
       const int w = item;
+      if (w == 0) continue;
       if (w >= 2 && !wait_geq(&c.gu_done[w - 2], c.win_nt1[w - 2], c, a, sh)) return;
-      const PMacro pm = c.pm[c.win_m[w]];
-      const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
-      const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
-      if (A_MX) {
-        for (int64_t s = s0 + mw; s < s1; s += nmw)
-          gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, pm.aos[s] / a.k,
-                           static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, a.status);
-      } else {
-        gather_rows_bf16_x2(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s0 + mw, nmw,
-                            s1, static_cast<uint16_t*>(a.ring), base, a.S, a.status);
-      }
+      gather_window<A_MX>(a, c, w, mw, nmw);
       signal_add(&c.gathered[w]);
     } else {
       const int m = -item - 1;
-      for (int w = 0; w < W; ++w)
-        if (c.win_m[w] == m && !wait_geq(&c.dn_done[w], c.win_nt2[w], c, a, sh)) return;
-      const PMacro pm = c.pm[m];
-      const int32_t R = pm.offsets[a.n_local];
-      for (int64_t s = mw; s < R; s += nmw)
-        merge_slot<false>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
-                   pm.out_n_part, pm.out_part_rows, a.status);
-      signal_add(&c.merged[m]);
+      if (m == a.n_macro - 1) {
+        merge_macro<true>(a, c, sh, m, mw, static_cast<int64_t>(gridDim.x) * 4);
+      } else {
+        if (!merge_macro<false>(a, c, sh, m, mw, nmw)) return;
+        signal_add(&c.merged[m]);
+      }
     }
   }
 }
 
+// Workers: GEMM tiles from the XCD's queue; false when the kernel aborts.
 template <bool A_MX>
-__device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_t* sh, uint8_t* lds) {
+__device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, int32_t* sh,
+                                             uint8_t* lds) {
   const int x = blockIdx.x % kXcds;
   const int W = *c.n_windows, ne = 2 * W;
   const int32_t* xs = c.xseq + x * c.xstride;
@@ -301,7 +331,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
     __syncthreads();
     const int32_t lt = sh[1];
     __syncthreads();
-    if (lt >= total) return;
+    if (lt >= total) return true;
     int lo = 0, hi = ne - 1;                     // last entry whose prefix <= lt
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -314,7 +344,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
     const int m = c.win_m[w];
     bool ok = true;
     if (!down && w != ready_g1) {
-      ok = wait_geq(&c.gathered[w], a.n_move, c, a, sh) &&
+      ok = wait_geq(&c.gathered[w], w == 0 ? static_cast<int32_t>(gridDim.x) : a.n_move, c, a, sh) &&
            (w < 2 || wait_geq(&c.dn_done[w - 2], c.win_nt2[w - 2], c, a, sh));
       ready_g1 = w;
     } else if (down && w != ready_g2) {
@@ -322,7 +352,7 @@ __device__ __forceinline__ void worker(const PKArgs& a, const CtlView& c, int32_
            (m < 2 || wait_geq(&c.merged[m - 2], a.n_move, c, a, sh));
       ready_g2 = w;
     }
-    if (!ok) return;
+    if (!ok) return false;
     const PMacro pm = c.pm[m];
     const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
     int e, row0, nrows, ntile;
@@ -364,10 +394,19 @@ void k_persist(const PKArgs a) {
   // (gemm_tile opens with one; signal_add closes each tile with one).
   int32_t* sh = reinterpret_cast<int32_t*>(lds);
   CtlView c(a.ctl, a.max_win);
-  if (static_cast<int>(blockIdx.x) < a.n_move)
+  const int wave = threadIdx.x / kWave;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave, ngw = static_cast<int64_t>(gridDim.x) * 4;
+  // nothing can run before window 0 is in the ring: every workgroup gathers it
+  if (*c.n_windows > 0) {
+    gather_window<A_MX>(a, c, 0, gw, ngw);
+    signal_add(&c.gathered[0]);
+  }
+  if (static_cast<int>(blockIdx.x) < a.n_move) {
     mover<A_MX>(a, c, sh);
-  else
-    worker<A_MX>(a, c, sh, lds);
+  } else if (worker_tiles<A_MX>(a, c, sh, lds) && *c.n_items > 0) {
+    // GEMMs done: help the movers with the last macrobatch's merge
+    merge_macro<true>(a, c, sh, a.n_macro - 1, gw, ngw);
+  }
 }
 
 }  // namespace
