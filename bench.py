@@ -149,7 +149,7 @@ def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
     gate = [d0.topk_gate] + [to_dev(w.topk_gate) for w in wls[1:]]
     outs = [d0.new_out() for _ in wls]
     res = {}
-    for mode, M, n_move in ((0, 2560, 0), (0, 8192, 0), (1, 2560, 32), (1, 4096, 32), (1, 8192, 32)):
+    for mode, M, n_move in ((0, 2560, 0), (0, 8192, 0), (1, 2560, 0), (1, 4096, 0), (1, 8192, 0)):
         d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=M, mode=mode, n_move_cus=n_move,
                     weights_packed=1)
         w_gu, w_d = d0.weights(d)
@@ -166,7 +166,7 @@ def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
         e1.record()
         torch.cuda.synchronize()
         assert mok.mok_device_status(ws) == 0
-        key = ("stream" if mode == 0 else f"persistent_mv{n_move}") + f"_M{M}"
+        key = ("stream" if mode == 0 else "persistent_auto_split") + f"_M{M}"
         res[key] = round(e0.elapsed_time(e1) / 3 / n_macro, 4)
         log(f"[bench] streaming {n_macro} macrobatches, {key}: {res[key]:.4f} ms per macrobatch")
     return res
@@ -333,7 +333,7 @@ def main():
         idx, gate = dw.topk_idx, dw.topk_gate
         for mode in (mok.MOK_MODE_STREAM, mok.MOK_MODE_PERSISTENT):
             for M in [0] + list(wl.minibatches):
-                for n_move in ((0,) if mode == mok.MOK_MODE_STREAM else (16, 32)):
+                for n_move in ((0,) if mode == mok.MOK_MODE_STREAM else (32, 48)):
                     d = dw.desc(max_rows=max_rows, minibatch=M, mode=mode, n_move_cus=n_move,
                                 weights_packed=1)
                     w_gu, w_d = dw.weights(d)

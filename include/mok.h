@@ -78,7 +78,9 @@ typedef struct {
     int32_t minibatch;    /* M rows per window; 0 = two-wave rule              */
     int32_t ring_slots;   /* S ring rows; 0 = 2*M; >= M (stream), >= 2*M (persistent) */
     int32_t max_rows;     /* capacity for routed rows R; 0 = T*k               */
-    int32_t n_move_cus;   /* data-movement workgroups (persistent); 0 = auto   */
+    int32_t n_move_cus;   /* data-movement workgroups (persistent); 0 = auto:
+                             1/8 of the CUs for one macrobatch, 3/16 for
+                             several                                         */
     int32_t mode;         /* mok_mode                                          */
     int32_t wait_timeout_us; /* bound of each device-side wait of the persistent
                                 kernel; 0 = 2 s.  On expiry the kernel stops and

@@ -417,7 +417,13 @@ size_t persistent_ws_bytes(int64_t total_windows) {
 }
 
 mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
-  const int n_move = a.n_move > 0 ? a.n_move : (a.n_cus >= 128 ? 32 : 8);
+  // automatic split (measured on 256 CUs, Kimi-shaped share): 1/8 of the CUs
+  // move data for one macrobatch, 3/16 when several stream through the ring
+  // (the movers then also carry the merges that overlap the next gathers)
+  const int n_move = a.n_move > 0 ? a.n_move
+                                  : (a.n_macro > 1 ? (3 * a.n_cus) / 16 : a.n_cus / 8) > 8
+                                        ? (a.n_macro > 1 ? (3 * a.n_cus) / 16 : a.n_cus / 8)
+                                        : 8;
   if (n_move < 1 || n_move > a.n_cus - kXcds) return MOK_ERR_INVALID_ARG;
   const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
   const void* fn = mx ? reinterpret_cast<const void*>(&k_persist<true>)
