@@ -457,6 +457,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
   // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
   // the row-wise reads back are both free of bank conflicts.
+  // C row of tile row r: one modulo per tile, then a compare per row (a
+  // modulo per 16-byte store cost a third of the down GEMM's time)
+  const int64_t cbase = (static_cast<int64_t>(row0) + p.c_row_base) % p.c_rows;
+  auto c_row_of = [&](int r) -> int64_t {
+    const int64_t c = cbase + r;
+    return c < p.c_rows ? c : (p.c_rows >= BM ? c - p.c_rows : c % p.c_rows);
+  };
   const int erow = 128 * wm + frag_row;                  // + 32 mi
   if (EPI == EPI_STORE_BF16) {
     constexpr int RB = BN * 2;                             // bytes per staged row
@@ -475,13 +482,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
     }
     __syncthreads();
     uint16_t* C = static_cast<uint16_t*>(p.C);
-    for (int idx = tid; idx < BM * (BN / 8); idx += kThreads) {
-      const int r = idx / (BN / 8), k = idx % (BN / 8);
-      const int col = n0 + k * 8;
-      if (r >= nrows || col >= p.N) continue;
-      const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
-      *reinterpret_cast<uint4*>(C + crow * p.N + col) =
-          *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+    const int k = tid % (BN / 8), col = n0 + k * 8;         // fixed 16-byte column per thread
+    if (col < p.N) {
+      for (int r = tid / (BN / 8); r < nrows; r += kThreads / (BN / 8)) {
+        const int64_t crow = c_row_of(r);
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+      }
     }
   } else {
     // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
@@ -514,20 +521,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
     __syncthreads();
     if (!MXO) {
       uint16_t* C = static_cast<uint16_t*>(p.C);
-      for (int idx = tid; idx < BM * 16; idx += kThreads) {
-        const int r = idx >> 4, k = idx & 15;
-        const int col = n0 + k * 8;
-        if (r >= nrows || col >= p.N) continue;
-        const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
-        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
-            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+      const int k = tid & 15, col = n0 + k * 8;             // fixed 16-byte column per thread
+      if (col < p.N) {
+        for (int r = tid >> 4; r < nrows; r += kThreads / 16) {
+          const int64_t crow = c_row_of(r);
+          *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+              *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+        }
       }
     } else {
       uint8_t* C = static_cast<uint8_t*>(p.C);
-      for (int idx = tid; idx < BM * 4; idx += kThreads) {
-        const int r = idx >> 2, b = idx & 3;
-        const int col = n0 + b * 32;
-        if (r >= nrows || col >= p.N) continue;
+      const int b = tid & 3, col = n0 + b * 32;               // fixed 32-column block per thread
+      for (int r = tid >> 2; r < nrows && col < p.N; r += kThreads / 4) {
         float v[32];
 #pragma unroll
         for (int c4 = 0; c4 < 8; ++c4) {
@@ -543,7 +548,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
         for (int q = 0; q < 8; ++q)
           w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
                  (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
-        const int64_t crow = (static_cast<int64_t>(row0) + r + p.c_row_base) % p.c_rows;
+        const int64_t crow = c_row_of(r);
         uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
