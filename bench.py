@@ -36,11 +36,12 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("10d2be8b3a3ef409", 738675531),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("10d2be8b3a3ef409", 899340068),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("556795d009af3882", 738681918),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("556795d009af3882", 902047960),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
-                "token_dispatch_grouped_top_amd/csrc/gemm.hip")
+                "token_dispatch_grouped_top_amd/csrc/gemm.hip",
+                "token_dispatch_grouped_top_amd/csrc/mok_internal.h")
 
 
 def gate_up_traffic(workload: str):

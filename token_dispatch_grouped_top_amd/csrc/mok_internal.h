@@ -12,17 +12,14 @@ namespace mok {
 constexpr int kWave = 64;
 
 // ----------------------------------------------------------------- bf16
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-// Round-to-nearest-even fp32 -> bf16 on the bit pattern (finite inputs;
-// NaN is kept quiet).
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32, two
+// values per instruction.  (A bit-pattern rounding with a NaN test costs a
+// branch per value; in the down GEMM's epilogue that was a sixth of the
+// launch.)
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Streaming stores of rows that are written once and read by a later kernel.
@@ -41,7 +38,8 @@ __device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_cvt v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt));
 }
 
 // --------------------------------------------------------- MXFP8 (E4M3)
@@ -71,15 +69,6 @@ __device__ __forceinline__ uint32_t e4m3_code_scaled(float v, int E) {
     if (mag > 0x7eu) mag = 0x7eu;
   }
   return sign | mag;
-}
-
-// E4M3 code * 2^E as fp32 (exact; scale applied with v_ldexp_f32).
-__device__ __forceinline__ float e4m3_value(uint32_t c, int E) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mant = static_cast<float>(e == 0 ? m : (8u | m));
-  int ex = (e == 0 ? -9 : static_cast<int>(e) - 10) + E;
-  float v = __builtin_amdgcn_ldexpf(mant, ex);
-  return (c & 0x80u) ? -v : v;
 }
 
 // ------------------------------------------------------------ wave ops
