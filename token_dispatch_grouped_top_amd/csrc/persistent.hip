@@ -241,11 +241,13 @@ __device__ __forceinline__ bool wait_geq(int32_t* ctr, int32_t target, const Ctl
   return ok;
 }
 
-// Publishes this workgroup's writes, then bumps the counter: the barrier
-// waits until every wave's stores have reached the XCD's L2, and thread 0's
-// release add writes that L2 back before the increment becomes visible.
+// Publishes this workgroup's writes, then bumps the counter: every wave
+// waits until its stores have reached the XCD's L2 (vmcnt(0); a workgroup
+// fence does not wait for global stores), the barrier joins the waves, and
+// thread 0's release add writes that L2 back before the increment becomes
+// visible.
 __device__ __forceinline__ void signal_add(int32_t* ctr) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -8,12 +8,12 @@
 // stable in assignment id a = t*k + j, i.e. a counting sort.
 //
 // Two launches, no atomics on the data path, so the result is unique:
-//   count   -- each block takes a chunk of 4096 assignments; each wave takes
-//              1024 consecutive ones in 16 steps of 64 and groups equal keys
+//   count   -- each block takes a chunk of 2048 assignments; each wave takes
+//              512 consecutive ones in 8 steps of 64 and groups equal keys
 //              with ballots on the key bits (match_key); the lowest lane of a
 //              group adds the group size to the wave's LDS histogram.
 //   scatter -- every block sums the per-block counts into the expert totals
-//              and its own block prefix (LDS atomics on counts only), scans
+//              and its own block prefix (a wave per expert), scans
 //              the totals into offsets (block 0 writes counts and offsets),
 //              recounts per wave; wave cursor = offsets[e] + block prefix +
 //              prefix over the block's waves; each lane's slot = wave cursor
@@ -27,8 +27,8 @@ namespace {
 
 constexpr int kSchedThreads = 256;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kStepsPerWave = 16;
-constexpr int kChunk = kSchedThreads * kStepsPerWave;  // 4096 assignments per block
+constexpr int kStepsPerWave = 8;    // 8: 14.6 us for the two launches at 589,824 ids; 16: 19.2
+constexpr int kChunk = kSchedThreads * kStepsPerWave;  // 2048 assignments per block
 constexpr int kMaxLocal = 256;
 
 __device__ __forceinline__ int key_bits(int32_t n_local) { return 32 - __clz(n_local); }
@@ -111,17 +111,23 @@ void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, i
 #pragma unroll
     for (int it = 0; it < kStepsPerWave; ++it) keys[it] = static_cast<uint32_t>(n_local);
   }
-  for (int e = threadIdx.x; e < n_local; e += kSchedThreads) { tot[e] = 0; pre[e] = 0; }
-  __syncthreads();
-  // per expert: total over all blocks and prefix over the blocks before this one
-  const int64_t nc = static_cast<int64_t>(n_local) * nblk;
-  for (int64_t i = threadIdx.x; i < nc; i += kSchedThreads) {
-    const int e = static_cast<int>(i / nblk), j = static_cast<int>(i % nblk);
-    const int32_t v = blk_counts[i];
-    if (v) {
-      atomicAdd(&tot[e], v);
-      if (j < static_cast<int>(blockIdx.x)) atomicAdd(&pre[e], v);
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  // per expert: total over all blocks and prefix over the blocks before this
+  // one; one wave per expert, lanes striding over the blocks
+  for (int e = w; e < n_local; e += kSchedWaves) {
+    const int32_t* bc = blk_counts + static_cast<int64_t>(e) * nblk;
+    int32_t t = 0, p = 0;
+    for (int j = lane; j < nblk; j += kWave) {
+      const int32_t v = bc[j];
+      t += v;
+      p += j < static_cast<int>(blockIdx.x) ? v : 0;
     }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      t += __shfl_xor(t, o);
+      p += __shfl_xor(p, o);
+    }
+    if (lane == 0) { tot[e] = t; pre[e] = p; }
   }
   wave_histogram(keys, n_local, h);
   __syncthreads();
@@ -142,7 +148,6 @@ void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, i
     for (int w = 0; w < kSchedWaves; ++w) { cur[w][e] = b; b += h[w][e]; }
   }
   __syncthreads();
-  const int w = threadIdx.x / kWave, lane = lane_id();
   const int nbits = key_bits(n_local);
 #pragma unroll
   for (int it = 0; it < kStepsPerWave; ++it) {
