@@ -104,6 +104,8 @@ class Step:
         self.act_sc = torch.empty((cap, I // 32), dtype=torch.uint8, device=dev) if mx else None
         self.y = torch.empty((cap, H), dtype=torch.int16, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # K split of the GEMMs' last partial round: counters must start at zero
+        self.gemm_ws = torch.zeros(mok.mok_gemm_workspace_size(), dtype=torch.uint8, device=dev)
         self.names = ["route", "schedule", "gather", "gate_up", "down", "combine"]
 
     def run(self, ev=None):
@@ -128,10 +130,10 @@ class Step:
                                 self.ring, self.ring_sc, self.cap, wl.act_format, self.status)
         rec(3)
         mok.mok_expert_gate_up(self.desc, self.ring, self.ring_sc, self.cap, self.offsets, 0,
-                               self.cap, self.w_gu, self.act, self.act_sc, self.cap)
+                               self.cap, self.w_gu, self.act, self.act_sc, self.cap, self.gemm_ws)
         rec(4)
         mok.mok_expert_down(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0, self.cap,
-                            self.w_d, self.y, self.cap)
+                            self.w_d, self.y, self.cap, self.gemm_ws)
         rec(5)
         mok.mok_combine_slots(self.y, self.cap, self.aos, self.offsets, wl.n_local, self.cap,
                               self.soa, gate, wl.k, wl.H, dw.outs[0], self.status)

@@ -88,6 +88,13 @@ typedef struct {
     int32_t weights_packed; /* 0: w_gate_up / w_down in the documented layout;
                                 1: both written by mok_pack_weights for this
                                 hidden, inter, n_local and act_format.         */
+    int32_t no_split_k;   /* 0: the grouped GEMMs (stream mode, and the
+                             standalone GEMM calls given a workspace) cut the
+                             tiles of a last, partial round along K over the
+                             CUs that round would leave idle, adding fp32
+                             partial sums in a fixed order; 1: every tile is
+                             computed whole (results then bit-identical to
+                             MOK_MODE_PERSISTENT).                           */
 } mok_layer_desc;
 
 /* Tokens held in partitions: token t lives in partition t / part_rows at row
@@ -167,13 +174,26 @@ mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
  *   y = W_d[e] . a   -> y row s % y_rows (bf16 [y_rows][H])
  * w_gate_up: bf16 [n_local][2I][H], rows 0..I-1 gate, I..2I-1 up; w_down:
  * bf16 [n_local][H][I]; no biases.  desc supplies H, I, n_local, act_format.
- * The ring and act formats follow desc->act_format. */
+ * The ring and act formats follow desc->act_format.
+ * ws / ws_bytes: optional workspace of mok_gemm_workspace_size() bytes for
+ * the K split of a last, partial round of tiles (desc->no_split_k); NULL =
+ * every tile whole.  Its contents must be zero before its first use; the
+ * calls leave them zero, except after a device-side wait gave up (then the
+ * workspace status word, read with mok_device_status, is MOK_ERR_DEVICE and
+ * the workspace must be zeroed again).  One workspace serves one stream. */
 mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring,
                           const uint8_t* ring_scales, int32_t ring_slots,
                           const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
                           const void* w_gate_up, const void* w_down,
                           void* act, uint8_t* act_scales, int32_t act_rows,
-                          void* y, int32_t y_rows, hipStream_t stream);
+                          void* y, int32_t y_rows, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Bytes of the optional GEMM workspace of mok_expert_ffn, mok_expert_gate_up
+ * and mok_expert_down on the current device: a status word, one counter and
+ * one 256 x 256 fp32 partial tile per compute unit (64 MiB + 2 KiB on 256
+ * CUs). */
+size_t mok_gemm_workspace_size(void);
 
 /* Weight packing (a layout of this library, not of the pages): one-time
  * rearrangement of w_gate_up and w_down into the tile order of the grouped
@@ -189,17 +209,18 @@ mok_status mok_packed_weights_size(const mok_layer_desc* desc, size_t* gate_up_b
 mok_status mok_pack_weights(const mok_layer_desc* desc, const void* w_gate_up, const void* w_down,
                             void* packed_gate_up, void* packed_down, hipStream_t stream);
 
-/* The two grouped GEMMs of mok_expert_ffn as separate calls, same layouts:
- * gate/up + SwiGLU (ring -> act) and down (act -> y). */
+/* The two grouped GEMMs of mok_expert_ffn as separate calls, same layouts
+ * and workspace rule: gate/up + SwiGLU (ring -> act) and down (act -> y). */
 mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
                               const uint8_t* ring_scales, int32_t ring_slots,
                               const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
                               const void* w_gate_up, void* act, uint8_t* act_scales,
-                              int32_t act_rows, hipStream_t stream);
+                              int32_t act_rows, void* ws, size_t ws_bytes, hipStream_t stream);
 mok_status mok_expert_down(const mok_layer_desc* desc, const void* act,
                            const uint8_t* act_scales, int32_t act_rows,
                            const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
-                           const void* w_down, void* y, int32_t y_rows, hipStream_t stream);
+                           const void* w_down, void* y, int32_t y_rows, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* Push combine + final weighted merge (article, push-combine and benchmark
  * scope paragraphs).  For each token t with at least one local assignment

@@ -9,7 +9,8 @@ ring.  Bit-exact in full: routing ids, counts, offsets, slot_of_assign,
 assign_of_slot, windows; dispatched rows on sampled slots.  Sampled against
 the oracle row by row: expert outputs y and merged rows out (bar: see
 gpu_harness.assert_close_rms).  In full on the GPU: rows of tokens with no
-local assignment keep their sentinel; persistent == stream-ordered, bit for bit.
+local assignment keep their sentinel; persistent == stream-ordered with whole
+tiles (no_split_k = 1), bit for bit.
 """
 import os
 import sys
@@ -110,12 +111,17 @@ def _check_pool_case(wl, tol):
 
 
 def _persistent_equals(dw, st, **kw):
+    """Persistent == stream-ordered with whole tiles, bit for bit; both within the bar of
+    the bench step's output (which splits the GEMMs' last round along K)."""
     import token_dispatch_grouped_top_amd as mok
-    out = dw.new_out()
+    out, ref = dw.new_out(), dw.new_out()
     ws, _ = dw.forward(out=out, max_rows=st.cap, mode=1, **kw)
     assert mok.mok_device_status(ws) == 0
-    for a, b in zip(out.parts, dw.outs[0].parts):
+    ws, _ = dw.forward(out=ref, max_rows=st.cap, no_split_k=1, **kw)
+    assert mok.mok_device_status(ws) == 0
+    for a, b in zip(out.parts, ref.parts):
         assert torch.equal(a, b)
+    return out
 
 
 def test_kimi_share_balanced():
@@ -167,7 +173,7 @@ def test_streaming_macrobatches():
                                 d0.wl.T, d0.x, d0.w_gu, d0.w_d, outs, ws)
     assert mok.mok_device_status(ws) == 0
     for m, d in enumerate(dws):
-        d.forward(max_rows=8192, minibatch=2560)        # standalone, stream-ordered
+        d.forward(max_rows=8192, minibatch=2560, no_split_k=1)   # standalone, stream-ordered
         for a, b in zip(outs[m].parts, d.outs[0].parts):
             assert torch.equal(a, b), m
     rng = np.random.default_rng(9)

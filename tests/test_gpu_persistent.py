@@ -3,7 +3,8 @@ MFMA workers signalling through device counters; tahou.com MoK article,
 megakernel / minibatch / ring-buffer paragraphs).
 
 Bars: outputs within 2e-2 * RMS (bf16) / 6e-2 * RMS (MXFP8) of the oracle,
-and bit-identical to the stream-ordered path (same per-element arithmetic);
+and bit-identical to the stream-ordered path with whole tiles (no_split_k = 1:
+same per-element arithmetic);
 macrobatches streamed through one ring equal standalone runs bit for bit.
 Every device wait is bounded, so these tests use a short bound: a stuck
 pipeline ends with MOK_ERR_DEVICE instead of hanging.
@@ -41,7 +42,7 @@ def test_persistent_matches_oracle_and_stream(mx, M):
     dw = DeviceWorkload(wl, n_out=2)
     ws, _ = dw.forward(out=dw.outs[0], minibatch=M, mode=PERSIST, wait_timeout_us=TIMEOUT_US)
     assert mok.mok_device_status(ws) == 0
-    ws2, _ = dw.forward(out=dw.outs[1], minibatch=M)
+    ws2, _ = dw.forward(out=dw.outs[1], minibatch=M, no_split_k=1)
     assert mok.mok_device_status(ws2) == 0
     got, ref_stream = dw.out_rows(dw.outs[0]), dw.out_rows(dw.outs[1])
     assert np.array_equal(got, ref_stream)
@@ -58,7 +59,7 @@ def test_persistent_mover_counts(n_move):
     ws, _ = dw.forward(out=dw.outs[0], minibatch=128, mode=PERSIST, n_move_cus=n_move,
                        wait_timeout_us=TIMEOUT_US)
     assert mok.mok_device_status(ws) == 0
-    dw.forward(out=dw.outs[1], minibatch=128)
+    dw.forward(out=dw.outs[1], minibatch=128, no_split_k=1)
     assert np.array_equal(dw.out_rows(dw.outs[0]), dw.out_rows(dw.outs[1]))
 
 
@@ -81,7 +82,7 @@ def test_persistent_macrobatches_equal_standalone():
                                 outs, ws)
     assert mok.mok_device_status(ws) == 0
     for m, d in enumerate(dws):
-        d.forward(minibatch=128)
+        d.forward(minibatch=128, no_split_k=1)
         assert np.array_equal(d0.out_rows(outs[m]), d.out_rows(d.outs[0])), m
     r = oracle.forward(wls[3])
     got = d0.out_rows(outs[3])

@@ -45,7 +45,7 @@ class mok_layer_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "expert_base", "n_local", "act_format",
         "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode", "wait_timeout_us",
-        "weights_packed")]
+        "weights_packed", "no_split_k")]
 
 
 class mok_tokens(C.Structure):
@@ -63,11 +63,14 @@ _SIGS = {
     "mok_dispatch_gather": (C.c_int, [_TOK, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32,
                                       _I32, _P, _P]),
     "mok_expert_ffn": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P,
-                                 _I32, _P]),
-    "mok_expert_gate_up": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P]),
+                                 _I32, _P, _SZ, _P]),
+    "mok_gemm_workspace_size": (_SZ, []),
+    "mok_expert_gate_up": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P,
+                                     _SZ, _P]),
     "mok_packed_weights_size": (C.c_int, [_DESC, C.POINTER(_SZ), C.POINTER(_SZ)]),
     "mok_pack_weights": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
-    "mok_expert_down": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P]),
+    "mok_expert_down": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _SZ,
+                                  _P]),
     "mok_combine": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _I32, _TOK, _P, _P]),
     "mok_combine_slots": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _TOK, _P,
                                     _P]),
@@ -178,13 +181,24 @@ def mok_dispatch_gather(src: Tokens, H: int, k: int, assign_of_slot, offsets, n_
            "mok_dispatch_gather")
 
 
+def _ws_bytes(ws, ws_bytes):
+    if ws is None:
+        return 0
+    return ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+
+
+def mok_gemm_workspace_size() -> int:
+    return int(_lib.mok_gemm_workspace_size())
+
+
 def mok_expert_ffn(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, offsets,
                    slot_begin: int, slot_end: int, w_gate_up, w_down, act, act_scales,
-                   act_rows: int, y, y_rows: int, stream=None) -> None:
+                   act_rows: int, y, y_rows: int, ws=None, ws_bytes: Optional[int] = None,
+                   stream=None) -> None:
     _check(_lib.mok_expert_ffn(C.byref(desc), _ptr(ring), _ptr(ring_scales), ring_slots,
                                _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up), _ptr(w_down),
-                               _ptr(act), _ptr(act_scales), act_rows, _ptr(y), y_rows,
-                               _stream(stream)), "mok_expert_ffn")
+                               _ptr(act), _ptr(act_scales), act_rows, _ptr(y), y_rows, _ptr(ws),
+                               _ws_bytes(ws, ws_bytes), _stream(stream)), "mok_expert_ffn")
 
 
 def mok_packed_weights_size(desc: mok_layer_desc):
@@ -204,18 +218,21 @@ def mok_pack_weights(desc: mok_layer_desc, w_gate_up, w_down, packed_gate_up, pa
 
 def mok_expert_gate_up(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, offsets,
                        slot_begin: int, slot_end: int, w_gate_up, act, act_scales, act_rows: int,
-                       stream=None) -> None:
+                       ws=None, ws_bytes: Optional[int] = None, stream=None) -> None:
     _check(_lib.mok_expert_gate_up(C.byref(desc), _ptr(ring), _ptr(ring_scales), ring_slots,
                                    _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up),
-                                   _ptr(act), _ptr(act_scales), act_rows, _stream(stream)),
+                                   _ptr(act), _ptr(act_scales), act_rows, _ptr(ws),
+                                   _ws_bytes(ws, ws_bytes), _stream(stream)),
            "mok_expert_gate_up")
 
 
 def mok_expert_down(desc: mok_layer_desc, act, act_scales, act_rows: int, offsets,
-                    slot_begin: int, slot_end: int, w_down, y, y_rows: int, stream=None) -> None:
+                    slot_begin: int, slot_end: int, w_down, y, y_rows: int, ws=None,
+                    ws_bytes: Optional[int] = None, stream=None) -> None:
     _check(_lib.mok_expert_down(C.byref(desc), _ptr(act), _ptr(act_scales), act_rows,
                                 _ptr(offsets), slot_begin, slot_end, _ptr(w_down), _ptr(y),
-                                y_rows, _stream(stream)), "mok_expert_down")
+                                y_rows, _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)),
+           "mok_expert_down")
 
 
 def mok_combine(y, y_rows: int, slot_of_assign, topk_gate, T: int, k: int, H: int, out: Tokens,

@@ -57,7 +57,18 @@ bool desc_ok(const mok_layer_desc* d) {
       d->wait_timeout_us < 0)
     return false;
   if (d->mode != MOK_MODE_STREAM && d->mode != MOK_MODE_PERSISTENT) return false;
+  if (d->no_split_k != 0 && d->no_split_k != 1) return false;
   return true;
+}
+
+// The K-split workspace of a standalone GEMM call: ws null = no split.
+mok_status gemm_split(const mok_layer_desc* d, void* ws, size_t ws_bytes, SplitWs& out) {
+  out = SplitWs{};
+  if (!ws || d->no_split_k) return MOK_OK;
+  const int n_cus = device_cus();
+  if (ws_bytes < split_ws_bytes(n_cus)) return MOK_ERR_WORKSPACE;
+  out = split_ws_carve(ws, n_cus);
+  return MOK_OK;
 }
 
 // Sizes of the fused call, derived from shapes only.
@@ -68,7 +79,8 @@ struct Plan {
   int32_t nwin;       // windows planned per macrobatch
   int32_t act_rows;
   int32_t n_ybuf;     // return areas (2 when macrobatches overlap)
-  size_t off_status, off_sched, off_counts, off_offsets, off_soa, off_aos, off_win, off_ring,
+  bool split;         // stream mode with the GEMMs' K split (workspace at off_split)
+  size_t off_status, off_split, off_sched, off_counts, off_offsets, off_soa, off_aos, off_win, off_ring,
       off_ring_sc, off_act, off_act_sc, off_y, off_pers, total;
   size_t per_macro_counts, per_macro_offsets, per_macro_soa, per_macro_aos, per_macro_win;
 };
@@ -96,7 +108,9 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   const int64_t H = d->hidden, I = d->inter, nl = d->n_local;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  p.split = d->mode == MOK_MODE_STREAM && !d->no_split_k;
   p.off_status = take(kAlign);
+  p.off_split = take(p.split ? split_ws_bytes(device_cus()) : 0);  // right after the status word
   p.off_sched = take(sched_ws_bytes(p.A, d->n_local));
   p.per_macro_counts = align_up(nl * 4);
   p.per_macro_offsets = align_up((nl + 1) * 4);
@@ -235,13 +249,14 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
                           int32_t ring_slots, const int32_t* offsets, int32_t slot_begin,
                           int32_t slot_end, const void* w_gate_up, const void* w_down, void* act,
                           uint8_t* act_scales, int32_t act_rows, void* y, int32_t y_rows,
-                          hipStream_t stream) {
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!desc_ok(desc) || !ring || ring_slots < 1 || !offsets || slot_begin < 0 ||
       slot_end < slot_begin || !w_gate_up || !w_down || !act || act_rows < 1 || !y || y_rows < 1)
     return MOK_ERR_INVALID_ARG;
   const bool mx = desc->act_format == MOK_ACT_MXFP8_E4M3;
   if (mx && (!ring_scales || !act_scales)) return MOK_ERR_INVALID_ARG;
   FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
   a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
   a.w_gu = static_cast<const uint16_t*>(w_gate_up); a.w_d = static_cast<const uint16_t*>(w_down);
@@ -256,13 +271,14 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
                               const uint8_t* ring_scales, int32_t ring_slots,
                               const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
                               const void* w_gate_up, void* act, uint8_t* act_scales,
-                              int32_t act_rows, hipStream_t stream) {
+                              int32_t act_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!desc_ok(desc) || !ring || ring_slots < 1 || !offsets || slot_begin < 0 ||
       slot_end < slot_begin || !w_gate_up || !act || act_rows < 1)
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && (!ring_scales || !act_scales))
     return MOK_ERR_INVALID_ARG;
   FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
   a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
   a.w_gu = static_cast<const uint16_t*>(w_gate_up);
@@ -275,12 +291,13 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
 mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const uint8_t* act_scales,
                            int32_t act_rows, const int32_t* offsets, int32_t slot_begin,
                            int32_t slot_end, const void* w_down, void* y, int32_t y_rows,
-                           hipStream_t stream) {
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!desc_ok(desc) || !act || act_rows < 1 || !offsets || slot_begin < 0 ||
       slot_end < slot_begin || !w_down || !y || y_rows < 1)
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && !act_scales) return MOK_ERR_INVALID_ARG;
   FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
   a.w_d = static_cast<const uint16_t*>(w_down);
   a.act = const_cast<void*>(act); a.act_scales = const_cast<uint8_t*>(act_scales);
@@ -315,6 +332,8 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
                                          stream));
 }
 
+size_t mok_gemm_workspace_size(void) { return split_ws_bytes(device_cus()); }
+
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro) {
   Plan p;
   if (!desc_ok(desc) || T < 0 || n_macro < 1 || !make_plan(desc, T, n_macro, p)) return 0;
@@ -347,8 +366,12 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
   const bool mx = d.act_format == MOK_ACT_MXFP8_E4M3;
   int32_t* status = at<int32_t>(ws, p.off_status);
   hipError_t err = hipSuccess;
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, status, 64, 0);
+  // the status word and, with the K split, its counters (which follow it)
+  const int n_cus = device_cus();
+  const int32_t n_clear = static_cast<int32_t>(kAlign / 4) + (p.split ? n_cus : 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, stream, status, n_clear, 0);
   if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
+  const SplitWs split = p.split ? split_ws_carve(at<void>(ws, p.off_split), n_cus) : SplitWs{};
 
   SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
   MacroBuffers mb[64];
@@ -417,6 +440,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       a.y = mb[m].y; a.y_rows = p.cap;
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
       a.w_packed = d.weights_packed;
+      a.split = split;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
     err = launch_combine_slots(mb[m].y, p.cap, mb[m].aos, mb[m].offsets, d.n_local, p.cap,

@@ -43,11 +43,9 @@ template <bool A_MX, int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[Geo<A_MX>::LDS];
-  int e, row0, nrows, ntile;
-  if (!decode_tile(p.offsets, p.n_local, p.s_begin, p.s_end, p.n_tiles, blockIdx.x, e, row0, nrows,
-                   ntile))
-    return;
-  gemm_tile<A_MX, EPI>(p, e, row0, nrows, ntile, lds);
+  TileJob j;
+  if (!decode_job(p, p.K / Geo<A_MX>::BK, blockIdx.x, j)) return;
+  gemm_tile<A_MX, EPI>(p, j, lds);
 }
 
 // Packing: one thread per 16-byte piece of the packed weights.  Block
@@ -89,14 +87,40 @@ hipError_t pack_one(const uint16_t* W, int64_t stride, int32_t K, int32_t I, int
   return hipGetLastError();
 }
 
+// Grid: an upper bound of the window's tiles (its rows plus one partial tile
+// per expert), plus (tail split) n_cus / 32 more workgroups per XCD for the
+// pieces of the last round.  Workgroups without work exit at once, but each
+// still waits for a CU with the kernel's LDS free, so the spare count is kept
+// small: the pieces also use the bound's slack.
 template <bool A_MX, int EPI>
 hipError_t launch_one(GemmParams gp, int n_tiles, int m_tiles, hipStream_t s) {
   gp.n_tiles = n_tiles;
-  hipLaunchKernelGGL((k_ffn_gemm<A_MX, EPI>), dim3(n_tiles * m_tiles), dim3(kThreads), 0, s, gp);
+  int64_t grid = static_cast<int64_t>(n_tiles) * m_tiles;
+  if (gp.part) grid = ((grid + kXcds - 1) / kXcds + gp.n_cus / (4 * kXcds)) * kXcds;
+  hipLaunchKernelGGL((k_ffn_gemm<A_MX, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, gp);
   return hipGetLastError();
 }
 
+void set_split(GemmParams& g, const FfnArgs& a) {
+  if (!a.split.part || a.split.n_cus < kXcds) return;
+  g.part = a.split.part; g.part_cnt = a.split.cnt; g.n_cus = a.split.n_cus;
+}
+
 }  // namespace
+
+size_t split_ws_bytes(int32_t n_cus) {
+  return ((static_cast<size_t>(n_cus) * 4 + 255) / 256) * 256 +
+         static_cast<size_t>(n_cus) * BM * BN * sizeof(float);
+}
+
+SplitWs split_ws_carve(void* ws, int32_t n_cus) {
+  SplitWs w{};
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  w.cnt = reinterpret_cast<int32_t*>(b);
+  w.part = reinterpret_cast<float*>(b + ((static_cast<size_t>(n_cus) * 4 + 255) / 256) * 256);
+  w.n_cus = n_cus;
+  return w;
+}
 
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
@@ -109,6 +133,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   g.N = a.I; g.I = a.I;
   g.C = a.act; g.C_scales = a.act_scales; g.c_rows = a.act_rows;
   g.w_packed = a.w_packed;
+  set_split(g, a);
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
                                              : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
@@ -125,6 +150,7 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   g.N = a.H; g.I = 0;
   g.C = a.y; g.C_scales = nullptr; g.c_rows = a.y_rows;
   g.w_packed = a.w_packed;
+  set_split(g, a);
   const int n2 = (a.H + BN - 1) / BN;
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
                                              : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);

@@ -78,6 +78,21 @@ struct GemmParams {
   int32_t w_packed;           // W in the packed tile order written by launch_pack_weights
   int32_t a_row_base;         // A row of slot s: (s + a_row_base) % a_rows
   int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
+  // Split of the last, partial round of tiles along K (standalone launches):
+  float* part;                // [n_cus][BM * BN] fp32 partial tiles; null = no split
+  int32_t* part_cnt;          // [n_cus] arrival counters, zero before and after a launch
+  int32_t n_cus;
+};
+
+// What one workgroup computes: a whole tile, or the k-steps [kt0, kt0 + nkt)
+// of a tile split into npieces pieces, whose fp32 sums go to slot (piece
+// slot0 + piece number) and whose arrivals are counted in *cnt.
+enum TileRole { kWhole = 0, kPiece = 1 };
+struct TileJob {
+  int e, row0, nrows, ntile;
+  int kt0, nkt;               // nkt = 0: all k-steps
+  int role, slot, slot0, npieces;
+  int32_t* cnt;
 };
 
 // Tile order and placement.  Tiles are numbered expert by expert; inside an
@@ -138,6 +153,52 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
                  ntile);
 }
 
+// Workgroup `bid` of a standalone launch with the tail split.  Per XCD x (its
+// contiguous share of c tiles, run by P = n_cus / 8 CUs in rounds), the last
+// r = c % P tiles would make a round of their own with P - r CUs idle.  They
+// are cut into s pieces of k-steps instead, run by the workgroups that follow
+// the whole tiles in dispatch order, where
+//   s = min(P / r, nk / 8, 8, 1 + (workgroups of XCD x - c) / r)
+// and s >= 3: a round half full of whole tiles runs each tile faster than a
+// full one (more L2 and memory bandwidth per CU), and two pieces did not win
+// back the partial sums' traffic (measured: 250 -> 262 us on a down GEMM with
+// 16 of 32 CUs per XCD in its last round).  Slots and counters of XCD x are
+// [x * P, (x + 1) * P).
+constexpr int kSplitMinSteps = 8, kSplitMax = 8, kSplitMinPieces = 3;
+__device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid, TileJob& j) {
+  const int32_t R = p.offsets[p.n_local];
+  const int32_t w0 = p.s_begin, w1 = p.s_end < R ? p.s_end : R;
+  if (w1 <= w0) return false;
+  const int total = window_mtiles(p.offsets, p.n_local, w0, w1) * p.n_tiles;
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = bid % kXcds, i = bid / kXcds;
+  const int c = q + (x < r ? 1 : 0), start = x * q + (x < r ? x : r);
+  j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  int t = i;
+  if (p.part != nullptr && p.n_cus >= kXcds) {
+    const int P = p.n_cus / kXcds, rx = c % P;
+    const int gx = (static_cast<int>(gridDim.x) - x + kXcds - 1) / kXcds;  // >= c
+    int sp = rx > 0 ? P / rx : 0;
+    if (sp > nk / kSplitMinSteps) sp = nk / kSplitMinSteps;
+    if (sp > kSplitMax) sp = kSplitMax;
+    if (rx > 0 && sp > 1 + (gx - c) / rx) sp = 1 + (gx - c) / rx;
+    if (sp >= kSplitMinPieces && i >= c - rx) {
+      const int u = i - (c - rx), tt = u / sp, piece = u % sp;
+      if (tt >= rx) return false;
+      t = c - rx + tt;
+      j.kt0 = piece * nk / sp;
+      j.nkt = (piece + 1) * nk / sp - j.kt0;
+      j.role = kPiece;
+      j.slot0 = x * P + tt * sp;
+      j.slot = j.slot0 + piece;
+      j.npieces = sp;
+      j.cnt = p.part_cnt + x * P + tt;
+    }
+  }
+  if (t >= c) return false;
+  return tile_of(p.offsets, p.n_local, w0, w1, p.n_tiles, start + t, j.e, j.row0, j.nrows, j.ntile);
+}
+
 // Weight row held by row nb (0..255) of the B tile of output column tile
 // `ntile`.  gate/up (swiglu): B rows 0..127 feed wave column 0, 128..255 wave
 // column 1; in each, 64 gate rows then the 64 up rows of the same
@@ -164,18 +225,22 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 // threads of a workgroup; `lds` is the workgroup's LDS (Geo<A_MX>::LDS bytes).
 // Starts with a barrier, so it can be called back to back on the same LDS.
 template <bool A_MX, int EPI>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, int nrows, int ntile,
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& job,
                                           uint8_t* __restrict__ lds) {
   using G = Geo<A_MX>;
   constexpr int BK = G::BK, NS = G::NS;
   __syncthreads();
+  const int e = job.e, row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave >> 1, wn = wave & 1;
   constexpr bool swiglu = EPI != EPI_STORE_BF16;
   // output columns of this tile: gate/up tiles cover 128 intermediate columns
   const int n0 = ntile * (swiglu ? BN / 2 : BN);
   const int K = p.K;
-  const int nk = K / BK;
+  const int nk_all = K / BK;
+  // k-steps of this job: the operand bases below start at k-step kt0
+  const int kt0 = job.kt0;
+  const int nk = job.nkt > 0 ? job.nkt : nk_all;
 
   // ---- operand tiles.  A wave load instruction fills 1 KiB of LDS: lane l
   // lands at physical chunk l % CPR of row l / CPR of that KiB, so it fetches
@@ -191,12 +256,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   // drop the kernel's launch stub)
   uint32_t boff[8];
   if (p.w_packed) {
-    Wbase = p.W + (static_cast<int64_t>(e) * p.n_tiles + ntile) * nk * (BM * BK);
+    Wbase = p.W + ((static_cast<int64_t>(e) * p.n_tiles + ntile) * nk_all + kt0) * (BM * BK);
     wkstride = BM * BK;
 #pragma unroll
     for (int j = 0; j < G::NLOAD_B; ++j) boff[j] = (4 * j + wave) * 512 + lane * 8;
   } else {
-    Wbase = p.W + static_cast<int64_t>(e) * p.w_expert_stride;
+    Wbase = p.W + static_cast<int64_t>(e) * p.w_expert_stride + kt0 * BK;
     wkstride = BK;
     const int lrowB = tid / G::CPR_B;
     const int lchunkB = (lane % G::CPR_B) ^ chunk_key<G::CPR_B>(lrowB);
@@ -218,9 +283,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
 #pragma unroll
   for (int j = 0; j < G::NLOAD_A; ++j)
     aoff[j] = a_ring_row(lrowA + G::RSTEP_A * j) * static_cast<uint32_t>(K) +
-              lchunkA * (A_MX ? 16 : 8);
+              lchunkA * (A_MX ? 16 : 8) + kt0 * BK;
   // E4M3 A: thread tid fetches the two block scales of row tid for each k-step
-  const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) : 0;
+  const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) + 2 * kt0 : 0;
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
@@ -449,6 +514,72 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();                                           // LDS is reused by the epilogue
 
+  // ---- split tiles.  Every piece stores its fp32 sums in its slot (float4 i
+  // of thread tid at slot + i * kThreads + tid: each instruction covers 4 KiB
+  // of contiguous memory) and counts itself in; the piece that arrives last
+  // adds the slots of all pieces in piece order and runs the epilogue.  No
+  // workgroup ever waits for another.
+  if (job.role == kPiece) {
+    float4* dst = reinterpret_cast<float4*>(p.part) + static_cast<int64_t>(job.slot) * (BM * BN / 4) + tid;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dst[((mi * 4 + ni) * 4 + g) * kThreads] =
+              make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+    }
+    // publish: each wave waits until its stores have reached L2 (a workgroup
+    // fence would not wait for them), then the release half of thread 0's add
+    // writes the L2 back; the acquire half, taken by the last piece, makes
+    // the other pieces' slots visible to it
+    wait_vm<0>();
+    __syncthreads();
+    int32_t* flag = reinterpret_cast<int32_t*>(lds);
+    if (tid == 0) {
+      const int32_t before = __hip_atomic_fetch_add(job.cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int32_t last = before == job.npieces - 1;
+      if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(job.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+      }
+      *flag = last;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    __syncthreads();                                         // the epilogue overwrites the flag
+    if (!last) return;
+  }
+  // Accumulator values of fragment row group mi, as 16 float4 (u = 4 ni + g:
+  // columns 8 g .. 8 g + 3 of tile (mi, ni)): the registers of a whole tile,
+  // or for a split one the sum over its pieces' slots, in piece order, loaded
+  // right before the epilogue consumes them.
+  const float4* red = reinterpret_cast<const float4*>(p.part) +
+                      static_cast<int64_t>(job.slot0) * (BM * BN / 4) + tid;
+  const bool split = job.role == kPiece;
+  auto tile_vals = [&](const int mi, float4 (&tv)[16]) {
+    if (split) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) tv[u] = red[(mi * 16 + u) * kThreads];
+      for (int q = 1; q < job.npieces; ++q) {
+        const float4* rq = red + static_cast<int64_t>(q) * (BM * BN / 4);
+        float4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = rq[(mi * 16 + u) * kThreads];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          tv[u].x += v[u].x; tv[u].y += v[u].y; tv[u].z += v[u].z; tv[u].w += v[u].w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        tv[u] = make_float4(acc[mi][u >> 2][4 * (u & 3)], acc[mi][u >> 2][4 * (u & 3) + 1],
+                            acc[mi][u >> 2][4 * (u & 3) + 2], acc[mi][u >> 2][4 * (u & 3) + 3]);
+    }
+  };
+
   // ---- epilogue, staged through LDS for 16-byte global stores.
   // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
   // accumulator element q of tile (mi, ni) is token row 32mi + lane%32 and
@@ -470,13 +601,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
-          const uint2 v = make_uint2(pack_bf16x2(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1]),
-                                     pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]));
+          const float4 t = tv[4 * ni + g];
+          const uint2 v = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
           *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
         }
     }
@@ -498,14 +631,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const float4 g4 = tv[4 * ni + g], u4 = tv[4 * (ni + 2) + g];
+          const float gvs[4] = {g4.x, g4.y, g4.z, g4.w}, uvs[4] = {u4.x, u4.y, u4.z, u4.w};
           float a[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float gv = acc[mi][ni][4 * g + j], uv = acc[mi][ni + 2][4 * g + j];
+            const float gv = gvs[j], uv = uvs[j];
             a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
           const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
@@ -558,6 +695,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   }
 }
 
+// A whole tile (all k-steps).
+template <bool A_MX, int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, int nrows, int ntile,
+                                          uint8_t* __restrict__ lds) {
+  TileJob j;
+  j.e = e; j.row0 = row0; j.nrows = nrows; j.ntile = ntile;
+  j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  gemm_tile<A_MX, EPI>(p, j, lds);
+}
 
 }  // namespace gemm
 }  // namespace mok

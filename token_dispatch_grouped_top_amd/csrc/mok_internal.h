@@ -128,6 +128,17 @@ hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* ao
                                 void* const* out_ptr, int32_t n_part, int32_t part_rows,
                                 int32_t* status, bool abort_on_status, hipStream_t s);
 
+// Workspace of the K split of the GEMMs' last, partial round of tiles:
+// [n_cus arrival counters, padded to 256 bytes][n_cus fp32 partial tiles of
+// 256 x 256].  Counters are zero between launches.
+struct SplitWs {
+  int32_t* cnt;
+  float* part;              // null: no split
+  int32_t n_cus;
+};
+size_t split_ws_bytes(int32_t n_cus);
+SplitWs split_ws_carve(void* ws, int32_t n_cus);
+
 // Grouped GEMM pair of the expert FFN over slots [s_begin, min(s_end, R)).
 struct FfnArgs {
   const void* ring; const uint8_t* ring_scales; int32_t ring_slots;
@@ -137,6 +148,7 @@ struct FfnArgs {
   void* y; int32_t y_rows;
   int32_t H, I, act_format;
   int32_t w_packed;           // weights in the packed tile order (launch_pack_weights)
+  SplitWs split;              // split.part null: every tile whole
 };
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
