@@ -36,6 +36,10 @@
  *     outside the buffers described here, whatever the routing data holds.
  *   - Calls are stateless and may run concurrently on different streams
  *     with disjoint buffers.
+ *   - The grouped GEMMs address the ring, the activation buffer and one
+ *     expert's weights with 32-bit byte offsets: each must be smaller than
+ *     4 GiB (ring_slots * H, act_rows * I and 2 * I * H elements), else the
+ *     call returns MOK_ERR_UNSUPPORTED.
  */
 #ifndef MOK_H
 #define MOK_H

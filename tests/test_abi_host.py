@@ -109,3 +109,31 @@ def test_packed_weight_sizes_and_argument_checks():
     bad = mok.mok_layer_desc(hidden=576, inter=320, n_experts=32, top_k=4, expert_base=3,
                              n_local=5, weights_packed=2)
     assert L.mok_packed_weights_size(C.byref(bad), None, None) == E
+
+
+def test_gemm_operand_limits_and_workspace_checks():
+    """Operands the GEMMs address with 32-bit byte offsets must be under 4 GiB; a GEMM
+    workspace smaller than the query is rejected.  Both before any launch."""
+    d = mok.mok_layer_desc(hidden=7168, inter=2048, n_experts=384, top_k=8, expert_base=0,
+                           n_local=8)
+    U = mok.MOK_ERR_UNSUPPORTED
+    big_ring = (1 << 31) // 7168 + 1          # ring_slots * H * 2 bytes >= 4 GiB
+    assert L.mok_expert_gate_up(C.byref(d), 1, None, big_ring, 1, 0, 8, 1, 1, None, 8, None, 0,
+                                None) == U
+    big_act = (1 << 31) // 2048 + 1
+    assert L.mok_expert_down(C.byref(d), 1, None, big_act, 1, 0, 8, 1, 1, 8, None, 0, None) == U
+    assert L.mok_expert_ffn(C.byref(d), 1, None, 8, 1, 0, 8, 1, 1, 1, None, big_act, 1, 8, None,
+                            0, None) == U
+    # the same ring is fine as E4M3 codes (1 byte per element) -- fails later on the scales
+    mx = mok.mok_layer_desc(hidden=7168, inter=2048, n_experts=384, top_k=8, expert_base=0,
+                            n_local=8, act_format=mok.MOK_ACT_MXFP8_E4M3)
+    assert L.mok_expert_gate_up(C.byref(mx), 1, None, big_ring, 1, 0, 8, 1, 1, None, 8, None, 0,
+                                None) == mok.MOK_ERR_INVALID_ARG
+    # fused plan: a ring of 2 x minibatch rows past the limit
+    big = mok.mok_layer_desc(hidden=7168, inter=2048, n_experts=384, top_k=8, expert_base=0,
+                             n_local=8, minibatch=(1 << 30) // 7168 + 1,
+                             max_rows=(1 << 30) // 7168 + 1)
+    assert mok.mok_forward_workspace_size(big, 1 << 20, 1) == 0
+    assert mok.mok_gemm_workspace_size() > 0
+    assert L.mok_expert_down(C.byref(d), 1, None, 8, 1, 0, 8, 1, 1, 8, 1, 1024, None) == \
+        mok.MOK_ERR_WORKSPACE

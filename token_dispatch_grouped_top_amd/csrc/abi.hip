@@ -61,6 +61,16 @@ bool desc_ok(const mok_layer_desc* d) {
   return true;
 }
 
+// The GEMMs address their operands through raw buffer descriptors with
+// 32-bit byte offsets: the ring, the activations and one expert's weights must
+// each stay below 4 GiB (rows = 0: that operand is not used).
+bool gemm_operands_fit(const mok_layer_desc* d, int64_t ring_rows, int64_t act_rows) {
+  const int64_t eb = d->act_format == MOK_ACT_MXFP8_E4M3 ? 1 : 2;
+  const int64_t lim = 1ll << 32;
+  return ring_rows * d->hidden * eb < lim && act_rows * d->inter * eb < lim &&
+         4ll * d->inter * d->hidden < lim;
+}
+
 // The K-split workspace of a standalone GEMM call: ws null = no split.
 mok_status gemm_split(const mok_layer_desc* d, void* ws, size_t ws_bytes, SplitWs& out) {
   out = SplitWs{};
@@ -103,6 +113,7 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   if (d->mode == MOK_MODE_PERSISTENT && p.S < 2 * static_cast<int64_t>(p.M)) return false;
   p.nwin = static_cast<int32_t>((cap + p.M - 1) / p.M);
   p.act_rows = p.S;
+  if (!gemm_operands_fit(d, p.S, p.act_rows)) return false;
   p.n_ybuf = n_macro > 1 ? 2 : 1;
   const bool mx = d->act_format == MOK_ACT_MXFP8_E4M3;
   const int64_t H = d->hidden, I = d->inter, nl = d->n_local;
@@ -255,6 +266,7 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
     return MOK_ERR_INVALID_ARG;
   const bool mx = desc->act_format == MOK_ACT_MXFP8_E4M3;
   if (mx && (!ring_scales || !act_scales)) return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, ring_slots, act_rows)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
@@ -277,6 +289,7 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && (!ring_scales || !act_scales))
     return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, ring_slots, 0)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
@@ -296,6 +309,7 @@ mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const ui
       slot_end < slot_begin || !w_down || !y || y_rows < 1)
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && !act_scales) return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, 0, act_rows)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
   a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;

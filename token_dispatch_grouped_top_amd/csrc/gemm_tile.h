@@ -215,6 +215,9 @@ __device__ __forceinline__ int w_row_of(int nb, int ntile, bool swiglu, int32_t 
   return wrow < N ? wrow : N - 1;
 }
 
+// Fourth word of a raw buffer descriptor on gfx9 (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
 template <int N> __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -231,7 +234,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   constexpr int BK = G::BK, NS = G::NS;
   __syncthreads();
   const int e = job.e, row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  // the wave index is uniform: in an SGPR the LDS destinations of the direct
+  // loads (M0) are scalar arithmetic, with no v_readfirstlane per load
+  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
   constexpr bool swiglu = EPI != EPI_STORE_BF16;
   // output columns of this tile: gate/up tiles cover 128 intermediate columns
@@ -275,8 +280,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
     const int rr = r < nrows ? r : nrows - 1;
     return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
   };
-  const uint16_t* Abf = static_cast<const uint16_t*>(p.A);
-  const uint8_t* Amx = static_cast<const uint8_t*>(p.A);
   const int lrowA = tid / G::CPR_A;
   const int lchunkA = (lane % G::CPR_A) ^ chunk_key<G::CPR_A>(lrowA);
   uint32_t aoff[8];                                           // element (bf16) / byte (E4M3) offsets
@@ -286,6 +289,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
               lchunkA * (A_MX ? 16 : 8) + kt0 * BK;
   // E4M3 A: thread tid fetches the two block scales of row tid for each k-step
   const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) + 2 * kt0 : 0;
+  // Raw buffer descriptors over the operands (byte extents below 4 GiB, which
+  // the launchers check); a load past an extent reads zero.
+  auto extent = [](int64_t bytes) -> int32_t {
+    return static_cast<int32_t>(bytes < 0xffffffffll ? bytes : 0xffffffffll);
+  };
+  const int64_t w_left = p.w_packed
+      ? static_cast<int64_t>(nk_all - kt0) * (BM * BK) * 2
+      : (p.w_expert_stride - static_cast<int64_t>(kt0) * BK) * 2;
+  const __amdgpu_buffer_rsrc_t rW =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wbase), 0, extent(w_left), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.A), 0, extent(static_cast<int64_t>(p.a_rows) * K * (A_MX ? 1 : 2)), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.A_scales), 0, extent(A_MX ? static_cast<int64_t>(p.a_rows) * (K / 32) : 0),
+      kRsrcWord3);
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   auto tileA = [&](int buf) { return lds + buf * G::STAGEB; };
@@ -303,8 +321,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
 
-#define MOK_LD_W(j, kt, dst) __builtin_amdgcn_global_load_lds(Wbase + (kt) * wkstride + boff[j], (lds_ptr_t)(dst), 16, 0, 0)
-#define MOK_LD_A(j, kt, dst) __builtin_amdgcn_global_load_lds(Abf + aoff[j] + (kt) * BK, (lds_ptr_t)(dst), 16, 0, 0)
+  // Buffer loads: a per-lane byte offset that is fixed for the tile (VGPR)
+  // plus a per-k-step offset (SGPR), so no address arithmetic per load.
+#define MOK_LD_W(j, kt, dst)                                                                 \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(dst), 16, boff[j] * 2u,            \
+                                           static_cast<uint32_t>(kt) * wkstride * 2u, 0, 0)
+#define MOK_LD_A(j, kt, dst)                                                                 \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(dst), 16, aoff[j] * 2u,            \
+                                           static_cast<uint32_t>(kt) * (BK * 2u), 0, 0)
   // The two halves of a stage's direct loads: weights; tokens (+ E4M3 scales,
   // 2 bytes per lane, which land in 4-byte slots: lane i at slot base + 4 i).
 #define MOK_ISSUE_W(kt, buf)                                                                 \
@@ -318,10 +342,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
     uint8_t* As_ = tileA(buf);                                                               \
     if (A_MX) {                                                                              \
       _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
-        __builtin_amdgcn_global_load_lds(Amx + aoff[j] + (kt) * BK,                          \
-                                         (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, 0, 0);\
-      __builtin_amdgcn_global_load_lds(p.A_scales + soff + 2 * (kt),                         \
-                                       (lds_ptr_t)(tileS(buf) + wave * 256), 2, 0, 0);       \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(As_ + (4 * j + wave) * 1024), \
+                                                 16, aoff[j], static_cast<uint32_t>(kt) * BK, 0, 0); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(tileS(buf) + wave * 256), 2, soff, \
+                                               static_cast<uint32_t>(kt) * 2u, 0, 0);        \
     } else {                                                                                 \
       _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
         MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                        \
