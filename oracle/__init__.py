@@ -54,13 +54,14 @@ def lib():
         L.orc_mx_quantize.argtypes = [P, i64, P, P]
         L.orc_mx_dequantize.argtypes = [P, P, i64, P]
         L.orc_gather_rows.argtypes = [P, i32, i32, P, P, i64, i32, P, P, P]
-        L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P]
+        L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P, P, P, P, P]
+        L.orc_mx_quantize_rows_bf16.argtypes = [P, i64, i32, P, P]
         L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i32, P, P]
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = C.c_int
         for f in ("orc_e4m3_encode_n", "orc_e4m3_decode_n", "orc_bf16_round_n",
                   "orc_mx_quantize", "orc_mx_dequantize", "orc_gather_rows",
-                  "orc_ffn_rows", "orc_combine_tokens"):
+                  "orc_ffn_rows", "orc_combine_tokens", "orc_mx_quantize_rows_bf16"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -179,8 +180,24 @@ def gather_rows(x: np.ndarray, k: int, assign_of_slot: np.ndarray, slots, mxfp8:
     return out
 
 
-def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: bool) -> np.ndarray:
-    """Expert SwiGLU FFN of dispatched rows -> y bf16 bits [n, H]."""
+def mx_quantize_rows(w_bits: np.ndarray):
+    """MXFP8 of bf16 rows [..., K] in blocks of 32 along K -> (codes [..., K], scales [..., K/32])."""
+    w = _c(w_bits, np.uint16)
+    K = w.shape[-1]
+    assert K % 32 == 0
+    rows = w.size // K
+    codes = np.empty(w.shape, np.uint8)
+    scales = np.empty(w.shape[:-1] + (K // 32,), np.uint8)
+    lib().orc_mx_quantize_rows_bf16(_p(w), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: bool,
+             mx_weights=None) -> np.ndarray:
+    """Expert SwiGLU FFN of dispatched rows -> y bf16 bits [n, H].
+
+    mx_weights: None (bf16 weights) or ((gu_codes, gu_scales), (d_codes, d_scales)) from
+    mx_quantize_rows of w_gu and w_d, used in place of them."""
     w_gu = _c(w_gu, np.uint16)
     w_d = _c(w_d, np.uint16)
     I2, H = w_gu.shape[1], w_gu.shape[2]
@@ -188,14 +205,22 @@ def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: boo
     eor = _c(expert_of_row, np.int32).reshape(-1)
     n = eor.size
     y = np.empty((n, H), np.uint16)
+    if mx_weights is None:
+        wq = (None, None, None, None)
+    else:
+        (gc, gs), (dc, ds) = mx_weights
+        wq = tuple(_c(a, np.uint8) for a in (gc, gs, dc, ds))
+    wp = [_p(a) for a in wq]
     if mxfp8:
         codes, scales = xrows
         codes = _c(codes, np.uint8)
         scales = _c(scales, np.uint8)
-        lib().orc_ffn_rows(None, _p(codes), _p(scales), _p(eor), n, H, I, _p(w_gu), _p(w_d), 1, _p(y))
+        lib().orc_ffn_rows(None, _p(codes), _p(scales), _p(eor), n, H, I, _p(w_gu), _p(w_d), 1,
+                           *wp, _p(y))
     else:
         xb = _c(xrows, np.uint16)
-        lib().orc_ffn_rows(_p(xb), None, None, _p(eor), n, H, I, _p(w_gu), _p(w_d), 0, _p(y))
+        lib().orc_ffn_rows(_p(xb), None, None, _p(eor), n, H, I, _p(w_gu), _p(w_d), 0, *wp,
+                           _p(y))
     return y
 
 
@@ -254,7 +279,10 @@ def forward(wl, tokens=None, slots_extra=None) -> Dict[str, np.ndarray]:
     mx = wl.act_format == 1
     xr = gather_rows(wl.x, k, sch["assign_of_slot"], slots, mx)
     eor = expert_of_slots(sch["offsets"], slots)
-    y = ffn_rows(xr, eor, wl.w_gu, wl.w_d, mx)
+    mxw = None
+    if getattr(wl, "weight_format", 0) == 1:
+        mxw = (mx_quantize_rows(wl.w_gu), mx_quantize_rows(wl.w_d))
+    y = ffn_rows(xr, eor, wl.w_gu, wl.w_d, mx, mx_weights=mxw)
     y_row_of_slot = np.full(max(sch["R"], 1), -1, np.int64)
     y_row_of_slot[slots] = np.arange(slots.size)
     out, written = combine_tokens(y, y_row_of_slot, soa, gate, tokens, k)

@@ -303,6 +303,33 @@ ORC_API void orc_gather_rows(const uint16_t* x, int32_t H, int32_t k,
     free(v);
 }
 
+/* MXFP8 weights (a wider reading of the article's MXFP8 datapath: the    */
+/* weights in the same OCP MX format as the activations, quantised per    */
+/* row in blocks of 32 along the contraction dimension K).  w: bf16 bits  */
+/* [rows][K]; codes [rows][K], scales [rows][K/32].                        */
+ORC_API void orc_mx_quantize_rows_bf16(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes,
+                                       uint8_t* scales)
+{
+    #pragma omp parallel
+    {
+        double* v = (double*)malloc(sizeof(double) * (size_t)K);
+        #pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            for (int32_t k = 0; k < K; ++k) v[k] = bf16_value(w[r * (int64_t)K + k]);
+            orc_mx_quantize(v, K, codes + r * (int64_t)K, scales + r * (int64_t)(K / 32));
+        }
+        free(v);
+    }
+}
+
+/* Weight element k of row r: bf16 value, or the MXFP8 code times 2^E of its block. */
+static double w_value(const uint16_t* wb, const uint8_t* wc, const uint8_t* ws, int64_t r, int32_t K,
+                      int32_t k)
+{
+    if (!wc) return bf16_value(wb[r * (int64_t)K + k]);
+    return ldexp(orc_e4m3_decode(wc[r * (int64_t)K + k]), (int)ws[r * (int64_t)(K / 32) + k / 32] - 127);
+}
+
 /* ------------------------------------------------------------------ */
 /* Expert SwiGLU FFN for a list of dispatched rows (tahou.com article:    */
 /* grouped GEMM over the expert-contiguous layout; SwiGLU named in the    */
@@ -311,12 +338,15 @@ ORC_API void orc_gather_rows(const uint16_t* x, int32_t H, int32_t k,
 /*   a_i = SiLU(h_i) * h_{I+i},  SiLU(z) = z / (1 + exp(-z))              */
 /*   a -> fp32 -> bf16 (or MXFP8 blocks of 32 along I, then dequantised)  */
 /*   y = W_d[e] . a  -> fp32 -> bf16                                       */
-/* x rows are bf16 bits (xb) or MXFP8 codes + scales (xc, xs).            */
+/* x rows are bf16 bits (xb) or MXFP8 codes + scales (xc, xs).  Weights   */
+/* are bf16 (w_gu, w_d) or, when gu_c is not null, MXFP8 codes + scales   */
+/* of the same matrices (gu_c/gu_s [n_local*2I][H], d_c/d_s [n_local*H][I]).*/
 /* ------------------------------------------------------------------ */
 ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* xs,
                           const int32_t* expert_of_row, int64_t n, int32_t H, int32_t I,
                           const uint16_t* w_gu, const uint16_t* w_d, int32_t mxfp8,
-                          uint16_t* y)
+                          const uint8_t* gu_c, const uint8_t* gu_s, const uint8_t* d_c,
+                          const uint8_t* d_s, uint16_t* y)
 {
     #pragma omp parallel
     {
@@ -332,14 +362,12 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
             } else {
                 orc_mx_dequantize(xc + r * (int64_t)H, xs + r * (int64_t)(H / 32), H, xv);
             }
-            const uint16_t* wg = w_gu + e * 2 * (int64_t)I * H;
+            const int64_t gbase = e * 2 * (int64_t)I;     /* first W_gu row of expert e */
             for (int i = 0; i < I; ++i) {
-                const uint16_t* gr = wg + (int64_t)i * H;
-                const uint16_t* ur = wg + (int64_t)(I + i) * H;
                 double g = 0.0, u = 0.0;
                 for (int h = 0; h < H; ++h) {
-                    g += bf16_value(gr[h]) * xv[h];
-                    u += bf16_value(ur[h]) * xv[h];
+                    g += w_value(w_gu, gu_c, gu_s, gbase + i, H, h) * xv[h];
+                    u += w_value(w_gu, gu_c, gu_s, gbase + I + i, H, h) * xv[h];
                 }
                 double silu = g / (1.0 + exp(-g));
                 a[i] = (double)(float)(silu * u);
@@ -350,11 +378,10 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
                 orc_mx_quantize(a, I, ac, as);
                 orc_mx_dequantize(ac, as, I, a);
             }
-            const uint16_t* wd = w_d + e * (int64_t)H * I;
+            const int64_t dbase = e * (int64_t)H;         /* first W_d row of expert e */
             for (int h = 0; h < H; ++h) {
-                const uint16_t* dr = wd + (int64_t)h * I;
                 double acc = 0.0;
-                for (int i = 0; i < I; ++i) acc += bf16_value(dr[i]) * a[i];
+                for (int i = 0; i < I; ++i) acc += w_value(w_d, d_c, d_s, dbase + h, I, i) * a[i];
                 y[r * (int64_t)H + h] = bf16_bits(round_bf16((double)(float)acc));
             }
         }

@@ -167,3 +167,59 @@ def test_combine_scaling_and_permutation(orc):
     out3, w3 = orc.combine_tokens(y, np.arange(s["R"]), s["slot_of_assign"],
                                   wl.topk_gate, perm, wl.k)
     assert np.array_equal(out3, out[perm]) and np.array_equal(w3, written[perm])
+
+
+def _mx_exact_rows(rng, rows, K):
+    """bf16 rows that MXFP8 represents exactly: each block of 32 is E4M3 codes times 2^E, with
+    one element of magnitude in [256, 448] * 2^E, so the block's scale is exactly 2^E."""
+    codes = rng.integers(0, 0x7F, (rows, K)).astype(np.uint8)           # finite magnitudes
+    codes |= (rng.integers(0, 2, (rows, K)) << 7).astype(np.uint8)      # signs
+    codes[:, ::32] = (0x78 + rng.integers(0, 7, (rows, K // 32))).astype(np.uint8) | \
+        (codes[:, ::32] & 0x80)                                          # 256 .. 448
+    E = rng.integers(-24, -4, (rows, K // 32))
+    mag = np.where((codes & 0x78) == 0, (codes & 7) * 2.0 ** -9,
+                   (8 + (codes & 7)) * 2.0 ** (((codes >> 3) & 15).astype(np.int64) - 10))
+    v = np.where(codes & 0x80, -mag, mag) * 2.0 ** np.repeat(E, 32, axis=1)
+    return _bits(v), codes, (E + 127).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mxfp8", [False, True])
+def test_mx_weights_exact_reduce_to_bf16_path(orc, mxfp8):
+    """MXFP8 weights (blocks of 32 along K, per row).  Weights that the format holds exactly
+    quantise to the codes and scales they were built from, and the FFN with them is the bf16
+    weight FFN bit for bit (a wrong block or row index in the dequantisation breaks both)."""
+    H, I, n_local = 96, 64, 3
+    rng = np.random.default_rng(21)
+    wg, cg, sg = _mx_exact_rows(rng, n_local * 2 * I, H)
+    wd, cd, sd = _mx_exact_rows(rng, n_local * H, I)
+    w_gu, w_d = wg.reshape(n_local, 2 * I, H), wd.reshape(n_local, H, I)
+    qg, qd = orc.mx_quantize_rows(w_gu), orc.mx_quantize_rows(w_d)
+    assert np.array_equal(qg[0].reshape(-1, H), cg) and np.array_equal(qg[1].reshape(-1, H // 32), sg)
+    assert np.array_equal(qd[0].reshape(-1, I), cd) and np.array_equal(qd[1].reshape(-1, I // 32), sd)
+    x = _bits(rng.standard_normal((30, H)))
+    xr = orc.mx_quantize(_val(x).reshape(-1)) if mxfp8 else x
+    if mxfp8:
+        xr = (xr[0].reshape(30, H), xr[1].reshape(30, H // 32))
+    e = rng.integers(0, n_local, 30).astype(np.int32)
+    y_bf16w = orc.ffn_rows(xr, e, w_gu, w_d, mxfp8)
+    y_mxw = orc.ffn_rows(xr, e, w_gu, w_d, mxfp8, mx_weights=(qg, qd))
+    assert np.array_equal(y_bf16w, y_mxw)
+
+
+def test_mx_weights_saturating_scale_closed_form(orc):
+    """Hand-derived MXFP8 weights: a block of 0.9 takes E = floor(log2 0.9) - 8 = -9 and
+    0.9 * 2^9 = 460.8 saturates to 448, i.e. 0.875; a block of 0.3 takes E = -10 and
+    307.2 rounds to the E4M3 value 320, i.e. 0.3125.  With x = 1 and H = 32:
+    g = 32 * 0.875, u = 32 * 0.3125, a = bf16(SiLU(g) u), y = bf16(0.3125 * I * a)."""
+    H, I = 32, 32
+    w_gu = np.concatenate([np.full((I, H), 0.9), np.full((I, H), 0.3)])[None]
+    w_d = np.full((1, H, I), 0.3)
+    w_gu, w_d = _bits(w_gu), _bits(w_d)
+    q = (orc.mx_quantize_rows(w_gu), orc.mx_quantize_rows(w_d))
+    assert set(np.unique(q[0][1])) == {127 - 9, 127 - 10}
+    x = _bits(np.ones((2, H)))
+    y = _val(orc.ffn_rows(x, np.zeros(2, np.int32), w_gu, w_d, False, mx_weights=q))
+    g, u = 32 * 0.875, 32 * 0.3125
+    a = _val(_bits(np.float32(g / (1 + np.exp(-g)) * u)))
+    expect = _val(_bits(np.float32(0.3125 * I * a)))
+    assert np.all(y == expect)

@@ -104,6 +104,7 @@ class Workload:
     topk_gate: Optional[np.ndarray] = None  # float32 [T, k]
     minibatches: List[int] = dataclasses.field(default_factory=list)
     macrobatch: int = 0
+    weight_format: int = 0  # 0: bf16 weights; 1: weights quantised to MXFP8 (act_format 1)
 
     @property
     def routing_from_logits(self) -> bool:
