@@ -29,6 +29,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "MoE fwd ms/layer + grouped-GEMM TFLOP/s, dispatch/combine GB/s (7168/2048)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (the block-scaled MXFP8 GEMMs)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows here)
 
@@ -64,6 +65,10 @@ def make_workload(name: str):
         return W.kimi_share()
     if name == "kimi_zipf_mxfp8":
         return W.kimi_zipf_mxfp8()
+    if name == "kimi_full_mxfp8":
+        return W.kimi_full_mxfp8()
+    if name == "kimi_zipf_full_mxfp8":
+        return W.kimi_zipf_full_mxfp8()
     if name == "mixtral":
         return W.mixtral()
     if name == "tiny":
@@ -206,7 +211,11 @@ def cpu_baseline(wl, sample_rows: int):
     mx = wl.act_format == 1
     t2 = time.perf_counter()
     xr = oracle.gather_rows(wl.x, wl.k, sch["assign_of_slot"], slots, mx)
-    y = oracle.ffn_rows(xr, oracle.expert_of_slots(sch["offsets"], slots), wl.w_gu, wl.w_d, mx)
+    mxw = None
+    if getattr(wl, "weight_format", 0) == 1:   # the oracle quantises the weights itself
+        mxw = (oracle.mx_quantize_rows(wl.w_gu), oracle.mx_quantize_rows(wl.w_d))
+    y = oracle.ffn_rows(xr, oracle.expert_of_slots(sch["offsets"], slots), wl.w_gu, wl.w_d, mx,
+                        mx_weights=mxw)
     yr = np.full(sch["R"], -1, np.int64)
     yr[slots] = np.arange(slots.size)
     oracle.combine_tokens(y, yr, sch["slot_of_assign"], gate, toks, wl.k)
@@ -226,7 +235,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kimi",
-                    choices=["kimi", "kimi_zipf_mxfp8", "mixtral", "tiny"])
+                    choices=["kimi", "kimi_zipf_mxfp8", "kimi_full_mxfp8", "kimi_zipf_full_mxfp8",
+                             "mixtral", "tiny"])
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="routed rows of the oracle's CPU-baseline sample; >= R runs the whole "
                          "layer (about 10 s on 16 host threads for the default workload); 0 = skip")
@@ -316,6 +326,8 @@ def main():
     T_out = int((soa >= 0).any(1).sum())
     H, I = wl.H, wl.I
     mx = wl.act_format == 1
+    wfmt = getattr(wl, "weight_format", 0)
+    peak = PEAK_FP8_TFLOPS if wfmt else PEAK_BF16_TFLOPS
     flop_gu, flop_dn = 4.0 * R * H * I, 2.0 * R * H * I
     b_out = (1 + 1 / 32) if mx else 2
     disp_bytes = R * H * (2 + b_out) + R * 8
@@ -379,15 +391,15 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-act/bf16" if mx else "bf16",
+        "dtype": ("mxfp8" if wfmt else "mxfp8-act/bf16") if mx else "bf16",
         "data": "synthetic (seeded; random-init weights, no dataset)",
         "config": {"workload": wl.name, "pool_tokens": wl.T, "partitions": wl.n_partitions,
                    "routed_rows": R, "tokens_out": T_out, "hidden": H, "inter": I,
                    "experts": wl.E, "n_local": wl.n_local, "top_k": wl.k, "minibatch": st.M,
                    "max_rows": max_rows, "path": "stream-ordered C-ABI calls"},
         "roofline": {"bound": "mfma", "kernel": "gate_up grouped GEMM + SwiGLU",
-                     "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4),
+                     "achieved": round(gu_tf, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / peak, 4),
                      "traffic": gate_up_traffic(wl.name),
                      "traffic_unit": "bytes per launch (HBM read + write)",
                      "algorithmic_flop_per_launch": flop_gu},
@@ -396,7 +408,7 @@ def main():
                           "pass with an event between every call (each marker drains the stream)",
         "gemm_tflops": {"gate_up": round(gu_tf, 1), "down": round(dn_tf, 1),
                         "both": round(gemm_tf, 1),
-                        "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)},
+                        "frac_of_peak": round(gemm_tf / peak, 4)},
         "dispatch_GBps": round(disp_gbs, 1), "dispatch_frac_hbm": round(disp_gbs / PEAK_HBM_GBS, 4),
         "combine_GBps": round(comb_gbs, 1), "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
         "schedule_share": round(per["schedule"] / wall_ms, 4),

@@ -65,6 +65,14 @@ typedef enum {
 
 typedef enum { MOK_ACT_BF16 = 0, MOK_ACT_MXFP8_E4M3 = 1 } mok_act_format;
 
+/* Weight format of the grouped GEMMs.  MOK_W_MXFP8_E4M3: both weight matrices
+ * quantised to OCP MX E4M3 with one E8M0 scale per 32 along the contraction
+ * dimension (per row of W_gu and of W_d), by mok_pack_weights from the bf16
+ * weights; needs act_format MOK_ACT_MXFP8_E4M3 and weights_packed = 1, and
+ * runs both GEMMs on gfx950's block-scaled FP8 MFMA (stream mode and the
+ * standalone calls; the persistent mode returns MOK_ERR_UNSUPPORTED). */
+typedef enum { MOK_W_BF16 = 0, MOK_W_MXFP8_E4M3 = 1 } mok_weight_format;
+
 typedef enum {
     MOK_MODE_STREAM = 0,      /* one launch per step and per window           */
     MOK_MODE_PERSISTENT = 1   /* one cooperative kernel for all windows       */
@@ -99,6 +107,7 @@ typedef struct {
                              partial sums in a fixed order; 1: every tile is
                              computed whole (results then bit-identical to
                              MOK_MODE_PERSISTENT).                           */
+    int32_t weight_format; /* mok_weight_format                               */
 } mok_layer_desc;
 
 /* Tokens held in partitions: token t lives in partition t / part_rows at row
@@ -205,7 +214,11 @@ size_t mok_gemm_workspace_size(void);
  * packed buffers (device, caller-owned, sizes from mok_packed_weights_size)
  * are then passed in place of the documented ones with desc->weights_packed
  * = 1; results are bit-identical.  The packed format depends on hidden,
- * inter, n_local and act_format and is private to this library version.
+ * inter, n_local, act_format and weight_format and is private to this
+ * library version.  With desc->weight_format = MOK_W_MXFP8_E4M3 the packing
+ * also quantises (OCP MX E4M3, blocks of 32 along the contraction dimension
+ * of each weight row, the scale rule and rounding of the MXFP8 activations):
+ * the results are then those of the quantised weights.
  * Either pair (source, packed) may be null to pack only the other; a pair
  * with one null pointer is MOK_ERR_INVALID_ARG.  Asynchronous on stream. */
 mok_status mok_packed_weights_size(const mok_layer_desc* desc, size_t* gate_up_bytes,

@@ -82,7 +82,10 @@ class DeviceWorkload:
         wl = self.wl
         d = mok.mok_layer_desc(hidden=wl.H, inter=wl.I, n_experts=wl.E, top_k=wl.k,
                                expert_base=wl.expert_base, n_local=wl.n_local,
-                               act_format=wl.act_format)
+                               act_format=wl.act_format,
+                               weight_format=getattr(wl, "weight_format", 0))
+        if d.weight_format:                 # MXFP8 weights exist only packed
+            d.weights_packed = 1
         for key, v in kw.items():
             setattr(d, key, v)
         return d

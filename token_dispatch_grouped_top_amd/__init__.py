@@ -33,6 +33,7 @@ MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE = 0, 1, 2, 3
 MOK_ERR_HIP, MOK_ERR_DEVICE, MOK_ERR_CAPACITY = 4, 5, 6
 MOK_ACT_BF16, MOK_ACT_MXFP8_E4M3 = 0, 1
 MOK_MODE_STREAM, MOK_MODE_PERSISTENT = 0, 1
+MOK_W_BF16, MOK_W_MXFP8_E4M3 = 0, 1
 
 
 class MokError(RuntimeError):
@@ -45,7 +46,7 @@ class mok_layer_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "expert_base", "n_local", "act_format",
         "minibatch", "ring_slots", "max_rows", "n_move_cus", "mode", "wait_timeout_us",
-        "weights_packed", "no_split_k")]
+        "weights_packed", "no_split_k", "weight_format")]
 
 
 class mok_tokens(C.Structure):

@@ -58,7 +58,14 @@ bool desc_ok(const mok_layer_desc* d) {
     return false;
   if (d->mode != MOK_MODE_STREAM && d->mode != MOK_MODE_PERSISTENT) return false;
   if (d->no_split_k != 0 && d->no_split_k != 1) return false;
+  if (d->weight_format != MOK_W_BF16 && d->weight_format != MOK_W_MXFP8_E4M3) return false;
+  if (d->weight_format == MOK_W_MXFP8_E4M3 && d->act_format != MOK_ACT_MXFP8_E4M3) return false;
   return true;
+}
+
+// MXFP8 weights exist only in the packed form (mok_pack_weights quantises them).
+bool weights_ok(const mok_layer_desc* d) {
+  return d->weight_format == MOK_W_BF16 || d->weights_packed == 1;
 }
 
 // The GEMMs address their operands through raw buffer descriptors with
@@ -111,6 +118,8 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.S = d->ring_slots > 0 ? d->ring_slots : 2 * p.M;
   if (p.S < p.M) return false;
   if (d->mode == MOK_MODE_PERSISTENT && p.S < 2 * static_cast<int64_t>(p.M)) return false;
+  // the persistent kernel runs the bf16-weight tiles only
+  if (d->mode == MOK_MODE_PERSISTENT && d->weight_format != MOK_W_BF16) return false;
   p.nwin = static_cast<int32_t>((cap + p.M - 1) / p.M);
   p.act_rows = p.S;
   if (!gemm_operands_fit(d, p.S, p.act_rows)) return false;
@@ -239,8 +248,10 @@ mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
 mok_status mok_packed_weights_size(const mok_layer_desc* desc, size_t* gate_up_bytes,
                                    size_t* down_bytes) {
   if (!desc_ok(desc)) return MOK_ERR_INVALID_ARG;
-  if (gate_up_bytes) *gate_up_bytes = packed_gate_up_bytes(desc->hidden, desc->inter, desc->n_local);
-  if (down_bytes) *down_bytes = packed_down_bytes(desc->hidden, desc->inter, desc->n_local);
+  if (gate_up_bytes)
+    *gate_up_bytes = packed_gate_up_bytes(desc->hidden, desc->inter, desc->n_local, desc->weight_format);
+  if (down_bytes)
+    *down_bytes = packed_down_bytes(desc->hidden, desc->inter, desc->n_local, desc->weight_format);
   return MOK_OK;
 }
 
@@ -252,7 +263,7 @@ mok_status mok_pack_weights(const mok_layer_desc* desc, const void* w_gate_up, c
   return hip_status(launch_pack_weights(static_cast<const uint16_t*>(w_gate_up),
                                         static_cast<const uint16_t*>(w_down), desc->hidden,
                                         desc->inter, desc->n_local, desc->act_format,
-                                        static_cast<uint16_t*>(packed_gate_up),
+                                        desc->weight_format, static_cast<uint16_t*>(packed_gate_up),
                                         static_cast<uint16_t*>(packed_down), stream));
 }
 
@@ -266,6 +277,7 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
     return MOK_ERR_INVALID_ARG;
   const bool mx = desc->act_format == MOK_ACT_MXFP8_E4M3;
   if (mx && (!ring_scales || !act_scales)) return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
   if (!gemm_operands_fit(desc, ring_slots, act_rows)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
@@ -275,7 +287,7 @@ mok_status mok_expert_ffn(const mok_layer_desc* desc, const void* ring, const ui
   a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
   a.y = y; a.y_rows = y_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
-  a.w_packed = desc->weights_packed;
+  a.w_packed = desc->weights_packed; a.weight_format = desc->weight_format;
   return hip_status(launch_ffn(a, stream));
 }
 
@@ -289,6 +301,7 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && (!ring_scales || !act_scales))
     return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
   if (!gemm_operands_fit(desc, ring_slots, 0)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
@@ -297,7 +310,7 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
   a.w_gu = static_cast<const uint16_t*>(w_gate_up);
   a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
-  a.w_packed = desc->weights_packed;
+  a.w_packed = desc->weights_packed; a.weight_format = desc->weight_format;
   return hip_status(launch_gate_up(a, stream));
 }
 
@@ -309,6 +322,7 @@ mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const ui
       slot_end < slot_begin || !w_down || !y || y_rows < 1)
     return MOK_ERR_INVALID_ARG;
   if (desc->act_format == MOK_ACT_MXFP8_E4M3 && !act_scales) return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
   if (!gemm_operands_fit(desc, 0, act_rows)) return MOK_ERR_UNSUPPORTED;
   FfnArgs a{};
   if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
@@ -317,7 +331,7 @@ mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const ui
   a.act = const_cast<void*>(act); a.act_scales = const_cast<uint8_t*>(act_scales);
   a.act_rows = act_rows; a.y = y; a.y_rows = y_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
-  a.w_packed = desc->weights_packed;
+  a.w_packed = desc->weights_packed; a.weight_format = desc->weight_format;
   return hip_status(launch_down(a, stream));
 }
 
@@ -366,7 +380,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
                                    const void* w_down, const mok_tokens* out, void* ws,
                                    size_t ws_bytes, hipStream_t stream) {
   if (!desc_ok(desc) || n_macro < 1 || T < 0 || !topk_idx || !topk_gate || !tokens_ok(x, T) ||
-      !w_gate_up || !w_down || !out || !ws)
+      !w_gate_up || !w_down || !out || !ws || !weights_ok(desc))
     return MOK_ERR_INVALID_ARG;
   for (int m = 0; m < n_macro; ++m) {
     if (T > 0 && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
@@ -453,7 +467,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
       a.act = act; a.act_scales = act_sc; a.act_rows = p.act_rows;
       a.y = mb[m].y; a.y_rows = p.cap;
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
-      a.w_packed = d.weights_packed;
+      a.w_packed = d.weights_packed; a.weight_format = d.weight_format;
       a.split = split;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }

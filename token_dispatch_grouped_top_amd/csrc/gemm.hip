@@ -32,6 +32,7 @@
 // same intermediate columns (64 + 64 per wave column), so each lane holds g and
 // u of the same (row, i) in accumulators (mi, ni) and (mi, ni + 2).
 #include "gemm_tile.h"
+#include "gemm_tile_mx8.h"
 
 namespace mok {
 
@@ -46,6 +47,71 @@ void k_ffn_gemm(const GemmParams p) {
   TileJob j;
   if (!decode_job(p, p.K / Geo<A_MX>::BK, blockIdx.x, j)) return;
   gemm_tile<A_MX, EPI>(p, j, lds);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads)
+void k_ffn_gemm_mx8(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GeoMX8::LDS];
+  TileJob j;
+  if (!decode_job(p, p.K / GeoMX8::BK, blockIdx.x, j)) return;
+  gemm_tile_mx8<EPI>(p, j, lds);
+}
+
+// MXFP8 packing: one thread per (expert, column tile, k-step, weight row).  The
+// row's 64 weights of the k-step are quantised as two OCP MX blocks of 32
+// (the quantiser of the MXFP8 activations) and written where the MXFP8 tile's
+// loads land them: codes in the LDS image of the block (chunk swizzle
+// included), then the 2 scale bytes of row r at TILE + 2 r.
+__global__ __launch_bounds__(256)
+void k_pack_weights_mx8(const uint16_t* __restrict__ W, int64_t expert_stride, int32_t K, int32_t I,
+                        int32_t N, int32_t swiglu, int32_t n_tiles, int32_t n_local,
+                        uint8_t* __restrict__ out) {
+  using G = GeoMX8;
+  const int nk = K / G::BK;
+  const int64_t total = static_cast<int64_t>(n_local) * n_tiles * nk * BM;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int row = static_cast<int>(u % BM);
+    const int64_t blk = u / BM;                            // (e * n_tiles + nt) * nk + kt
+    const int kt = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;
+    const int nt = static_cast<int>(et % n_tiles), e = static_cast<int>(et / n_tiles);
+    const int wrow = w_row_of(row, nt, swiglu != 0, I, N);
+    const uint4* src = reinterpret_cast<const uint4*>(W + e * expert_stride + static_cast<int64_t>(wrow) * K +
+                                                      kt * G::BK);
+    uint8_t* dst = out + blk * G::WBLOCK;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {                          // two blocks of 32
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 w = src[4 * b + c];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[8 * c + 2 * q] = __uint_as_float(ws[q] << 16);
+          v[8 * c + 2 * q + 1] = __uint_as_float(ws[q] & 0xffff0000u);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      const int E = mx_scale_exp(amax);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                        // 16-byte chunks 2 b + h of the row
+        uint32_t c4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float* t = v + 16 * h + 4 * q;
+          c4[q] = e4m3_code_scaled(t[0], E) | (e4m3_code_scaled(t[1], E) << 8) |
+                  (e4m3_code_scaled(t[2], E) << 16) | (e4m3_code_scaled(t[3], E) << 24);
+        }
+        *reinterpret_cast<uint4*>(dst + G::off(row, 2 * b + h)) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
+      }
+      dst[G::TILE + 2 * row + b] = static_cast<uint8_t>(E + 127);
+    }
+  }
 }
 
 // Packing: one thread per 16-byte piece of the packed weights.  Block
@@ -101,6 +167,24 @@ hipError_t launch_one(GemmParams gp, int n_tiles, int m_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int EPI>
+hipError_t launch_one_mx8(GemmParams gp, int n_tiles, int m_tiles, hipStream_t s) {
+  gp.n_tiles = n_tiles;
+  int64_t grid = static_cast<int64_t>(n_tiles) * m_tiles;
+  if (gp.part) grid = ((grid + kXcds - 1) / kXcds + gp.n_cus / (4 * kXcds)) * kXcds;
+  hipLaunchKernelGGL((k_ffn_gemm_mx8<EPI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, gp);
+  return hipGetLastError();
+}
+
+hipError_t pack_one_mx8(const uint16_t* W, int64_t stride, int32_t K, int32_t I, int32_t N, bool swiglu,
+                        int32_t n_tiles, int32_t n_local, uint8_t* out, hipStream_t s) {
+  const int64_t threads = static_cast<int64_t>(n_local) * n_tiles * (K / GeoMX8::BK) * BM;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_pack_weights_mx8, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                     dim3(256), 0, s, W, stride, K, I, N, swiglu ? 1 : 0, n_tiles, n_local, out);
+  return hipGetLastError();
+}
+
 void set_split(GemmParams& g, const FfnArgs& a) {
   if (!a.split.part || a.split.n_cus < kXcds) return;
   g.part = a.split.part; g.part_cnt = a.split.cnt; g.n_cus = a.split.n_cus;
@@ -135,6 +219,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   g.w_packed = a.w_packed;
   set_split(g, a);
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
+  if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_SWIGLU_MX>(g, n1, m_tiles, s);
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
                                              : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
 }
@@ -152,23 +237,37 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   g.w_packed = a.w_packed;
   set_split(g, a);
   const int n2 = (a.H + BN - 1) / BN;
+  if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_STORE_BF16>(g, n2, m_tiles, s);
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
                                              : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
 }
 
-size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local) {
-  return static_cast<size_t>(n_local) * ((I + BN / 2 - 1) / (BN / 2)) * BM * H * 2;
+size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format) {
+  const size_t tiles = static_cast<size_t>(n_local) * ((I + BN / 2 - 1) / (BN / 2));
+  if (weight_format == MOK_W_MXFP8_E4M3) return tiles * (H / GeoMX8::BK) * GeoMX8::WBLOCK;
+  return tiles * BM * H * 2;
 }
-size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local) {
-  return static_cast<size_t>(n_local) * ((H + BN - 1) / BN) * BM * I * 2;
+size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format) {
+  const size_t tiles = static_cast<size_t>(n_local) * ((H + BN - 1) / BN);
+  if (weight_format == MOK_W_MXFP8_E4M3) return tiles * (I / GeoMX8::BK) * GeoMX8::WBLOCK;
+  return tiles * BM * I * 2;
 }
 
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                               int32_t n_local, int32_t act_format, uint16_t* packed_gu,
-                               uint16_t* packed_d, hipStream_t s) {
+                               int32_t n_local, int32_t act_format, int32_t weight_format,
+                               uint16_t* packed_gu, uint16_t* packed_d, hipStream_t s) {
   const bool mx = act_format == MOK_ACT_MXFP8_E4M3;
   const int n1 = (I + BN / 2 - 1) / (BN / 2), n2 = (H + BN - 1) / BN;
   hipError_t err = hipSuccess;
+  if (weight_format == MOK_W_MXFP8_E4M3) {
+    if (w_gu && packed_gu)
+      err = pack_one_mx8(w_gu, static_cast<int64_t>(2) * I * H, H, I, 0, true, n1, n_local,
+                         reinterpret_cast<uint8_t*>(packed_gu), s);
+    if (err == hipSuccess && w_d && packed_d)
+      err = pack_one_mx8(w_d, static_cast<int64_t>(H) * I, I, 0, H, false, n2, n_local,
+                         reinterpret_cast<uint8_t*>(packed_d), s);
+    return err;
+  }
   if (w_gu && packed_gu)
     err = mx ? pack_one<true>(w_gu, static_cast<int64_t>(2) * I * H, H, I, 0, true, n1, n_local, packed_gu, s)
              : pack_one<false>(w_gu, static_cast<int64_t>(2) * I * H, H, I, 0, true, n1, n_local, packed_gu, s);

@@ -223,6 +223,201 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// After the main loop (LDS free, every load landed): the K-split exchange of
+// a piece and the epilogue.  acc holds the wave's 128 x 128 block: element q of
+// tile (mi, ni) is token row 32 mi + lane % 32, output column 32 ni + 8 (q / 4)
+// + 4 (lane / 32) + q % 4.  Shared by every operand format.
+template <int EPI>
+__device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& job,
+                                            f32x16_t (&acc)[4][4], uint8_t* __restrict__ lds) {
+  const int row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
+  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr bool swiglu = EPI != EPI_STORE_BF16;
+  const int n0 = ntile * (swiglu ? BN / 2 : BN);
+  const int frag_row = lane & 31;
+  const int khalf = lane >> 5;
+  // ---- split tiles.  Every piece stores its fp32 sums in its slot (float4 i
+  // of thread tid at slot + i * kThreads + tid: each instruction covers 4 KiB
+  // of contiguous memory) and counts itself in; the piece that arrives last
+  // adds the slots of all pieces in piece order and runs the epilogue.  No
+  // workgroup ever waits for another.
+  if (job.role == kPiece) {
+    float4* dst = reinterpret_cast<float4*>(p.part) + static_cast<int64_t>(job.slot) * (BM * BN / 4) + tid;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dst[((mi * 4 + ni) * 4 + g) * kThreads] =
+              make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+    }
+    // publish: each wave waits until its stores have reached L2 (a workgroup
+    // fence would not wait for them), then the release half of thread 0's add
+    // writes the L2 back; the acquire half, taken by the last piece, makes
+    // the other pieces' slots visible to it
+    wait_vm<0>();
+    __syncthreads();
+    int32_t* flag = reinterpret_cast<int32_t*>(lds);
+    if (tid == 0) {
+      const int32_t before = __hip_atomic_fetch_add(job.cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int32_t last = before == job.npieces - 1;
+      if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(job.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+      }
+      *flag = last;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    __syncthreads();                                         // the epilogue overwrites the flag
+    if (!last) return;
+  }
+  // Accumulator values of fragment row group mi, as 16 float4 (u = 4 ni + g:
+  // columns 8 g .. 8 g + 3 of tile (mi, ni)): the registers of a whole tile,
+  // or for a split one the sum over its pieces' slots, in piece order, loaded
+  // right before the epilogue consumes them.
+  const float4* red = reinterpret_cast<const float4*>(p.part) +
+                      static_cast<int64_t>(job.slot0) * (BM * BN / 4) + tid;
+  const bool split = job.role == kPiece;
+  auto tile_vals = [&](const int mi, float4 (&tv)[16]) {
+    if (split) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) tv[u] = red[(mi * 16 + u) * kThreads];
+      for (int q = 1; q < job.npieces; ++q) {
+        const float4* rq = red + static_cast<int64_t>(q) * (BM * BN / 4);
+        float4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = rq[(mi * 16 + u) * kThreads];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          tv[u].x += v[u].x; tv[u].y += v[u].y; tv[u].z += v[u].z; tv[u].w += v[u].w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        tv[u] = make_float4(acc[mi][u >> 2][4 * (u & 3)], acc[mi][u >> 2][4 * (u & 3) + 1],
+                            acc[mi][u >> 2][4 * (u & 3) + 2], acc[mi][u >> 2][4 * (u & 3) + 3]);
+    }
+  };
+
+  // ---- epilogue, staged through LDS for 16-byte global stores.
+  // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
+  // accumulator element q of tile (mi, ni) is token row 32mi + lane%32 and
+  // output column 32ni + 8(q/4) + 4(lane/32) + q%4 of the wave's 128 x 128
+  // block, so each lane holds 4 consecutive columns of one row and writes
+  // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
+  // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
+  // the row-wise reads back are both free of bank conflicts.
+  // C row of tile row r: one modulo per tile, then a compare per row (a
+  // modulo per 16-byte store cost a third of the down GEMM's time)
+  const int64_t cbase = (static_cast<int64_t>(row0) + p.c_row_base) % p.c_rows;
+  auto c_row_of = [&](int r) -> int64_t {
+    const int64_t c = cbase + r;
+    return c < p.c_rows ? c : (p.c_rows >= BM ? c - p.c_rows : c % p.c_rows);
+  };
+  const int erow = 128 * wm + frag_row;                  // + 32 mi
+  if (EPI == EPI_STORE_BF16) {
+    constexpr int RB = BN * 2;                             // bytes per staged row
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
+          const float4 t = tv[4 * ni + g];
+          const uint2 v = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
+          *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
+        }
+    }
+    __syncthreads();
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+    const int k = tid % (BN / 8), col = n0 + k * 8;         // fixed 16-byte column per thread
+    if (col < p.N) {
+      for (int r = tid / (BN / 8); r < nrows; r += kThreads / (BN / 8)) {
+        const int64_t crow = c_row_of(r);
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+      }
+    }
+  } else {
+    // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
+    // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
+    constexpr bool MXO = EPI == EPI_SWIGLU_MX;
+    constexpr int RB = MXO ? (BN / 2) * 4 : (BN / 2) * 2;  // staged row: 128 fp32 or bf16
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 g4 = tv[4 * ni + g], u4 = tv[4 * (ni + 2) + g];
+          const float gvs[4] = {g4.x, g4.y, g4.z, g4.w}, uvs[4] = {u4.x, u4.y, u4.z, u4.w};
+          float a[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = gvs[j], uv = uvs[j];
+            a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          }
+          const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if (MXO) {
+            *reinterpret_cast<float4*>(lds + r * RB + (((i >> 2) ^ (r & 15)) << 4)) =
+                make_float4(a[0], a[1], a[2], a[3]);
+          } else {
+            *reinterpret_cast<uint2*>(lds + r * RB + (((i >> 3) ^ (r & 15)) << 4) + ((i >> 2) & 1) * 8) =
+                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+          }
+        }
+    }
+    __syncthreads();
+    if (!MXO) {
+      uint16_t* C = static_cast<uint16_t*>(p.C);
+      const int k = tid & 15, col = n0 + k * 8;             // fixed 16-byte column per thread
+      if (col < p.N) {
+        for (int r = tid >> 4; r < nrows; r += kThreads / 16) {
+          const int64_t crow = c_row_of(r);
+          *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+              *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+        }
+      }
+    } else {
+      uint8_t* C = static_cast<uint8_t*>(p.C);
+      const int b = tid & 3, col = n0 + b * 32;               // fixed 32-column block per thread
+      for (int r = tid >> 2; r < nrows && col < p.N; r += kThreads / 4) {
+        float v[32];
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const float4 f = *reinterpret_cast<const float4*>(lds + r * RB + (((8 * b + c4) ^ (r & 15)) << 4));
+          v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+        const int E = mx_scale_exp(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
+                 (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
+        const int64_t crow = c_row_of(r);
+        uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        p.C_scales[crow * (p.N / 32) + col / 32] = static_cast<uint8_t>(E + 127);
+      }
+    }
+  }
+}
+
 // One 256-row x (256 | 128 SwiGLU) output tile of expert e, rows
 // [row0, row0 + nrows) of the window, column tile `ntile`.  Called by all 256
 // threads of a workgroup; `lds` is the workgroup's LDS (Geo<A_MX>::LDS bytes).
@@ -239,8 +434,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
   constexpr bool swiglu = EPI != EPI_STORE_BF16;
-  // output columns of this tile: gate/up tiles cover 128 intermediate columns
-  const int n0 = ntile * (swiglu ? BN / 2 : BN);
   const int K = p.K;
   const int nk_all = K / BK;
   // k-steps of this job: the operand bases below start at k-step kt0
@@ -538,185 +731,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();                                           // LDS is reused by the epilogue
 
-  // ---- split tiles.  Every piece stores its fp32 sums in its slot (float4 i
-  // of thread tid at slot + i * kThreads + tid: each instruction covers 4 KiB
-  // of contiguous memory) and counts itself in; the piece that arrives last
-  // adds the slots of all pieces in piece order and runs the epilogue.  No
-  // workgroup ever waits for another.
-  if (job.role == kPiece) {
-    float4* dst = reinterpret_cast<float4*>(p.part) + static_cast<int64_t>(job.slot) * (BM * BN / 4) + tid;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          dst[((mi * 4 + ni) * 4 + g) * kThreads] =
-              make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
-    }
-    // publish: each wave waits until its stores have reached L2 (a workgroup
-    // fence would not wait for them), then the release half of thread 0's add
-    // writes the L2 back; the acquire half, taken by the last piece, makes
-    // the other pieces' slots visible to it
-    wait_vm<0>();
-    __syncthreads();
-    int32_t* flag = reinterpret_cast<int32_t*>(lds);
-    if (tid == 0) {
-      const int32_t before = __hip_atomic_fetch_add(job.cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const int32_t last = before == job.npieces - 1;
-      if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(job.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
-      }
-      *flag = last;
-    }
-    __syncthreads();
-    const bool last = *flag != 0;
-    __syncthreads();                                         // the epilogue overwrites the flag
-    if (!last) return;
-  }
-  // Accumulator values of fragment row group mi, as 16 float4 (u = 4 ni + g:
-  // columns 8 g .. 8 g + 3 of tile (mi, ni)): the registers of a whole tile,
-  // or for a split one the sum over its pieces' slots, in piece order, loaded
-  // right before the epilogue consumes them.
-  const float4* red = reinterpret_cast<const float4*>(p.part) +
-                      static_cast<int64_t>(job.slot0) * (BM * BN / 4) + tid;
-  const bool split = job.role == kPiece;
-  auto tile_vals = [&](const int mi, float4 (&tv)[16]) {
-    if (split) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) tv[u] = red[(mi * 16 + u) * kThreads];
-      for (int q = 1; q < job.npieces; ++q) {
-        const float4* rq = red + static_cast<int64_t>(q) * (BM * BN / 4);
-        float4 v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = rq[(mi * 16 + u) * kThreads];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          tv[u].x += v[u].x; tv[u].y += v[u].y; tv[u].z += v[u].z; tv[u].w += v[u].w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        tv[u] = make_float4(acc[mi][u >> 2][4 * (u & 3)], acc[mi][u >> 2][4 * (u & 3) + 1],
-                            acc[mi][u >> 2][4 * (u & 3) + 2], acc[mi][u >> 2][4 * (u & 3) + 3]);
-    }
-  };
-
-  // ---- epilogue, staged through LDS for 16-byte global stores.
-  // The MFMA is fed (weights, tokens), i.e. it computes the tile transposed:
-  // accumulator element q of tile (mi, ni) is token row 32mi + lane%32 and
-  // output column 32ni + 8(q/4) + 4(lane/32) + q%4 of the wave's 128 x 128
-  // block, so each lane holds 4 consecutive columns of one row and writes
-  // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
-  // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
-  // the row-wise reads back are both free of bank conflicts.
-  // C row of tile row r: one modulo per tile, then a compare per row (a
-  // modulo per 16-byte store cost a third of the down GEMM's time)
-  const int64_t cbase = (static_cast<int64_t>(row0) + p.c_row_base) % p.c_rows;
-  auto c_row_of = [&](int r) -> int64_t {
-    const int64_t c = cbase + r;
-    return c < p.c_rows ? c : (p.c_rows >= BM ? c - p.c_rows : c % p.c_rows);
-  };
-  const int erow = 128 * wm + frag_row;                  // + 32 mi
-  if (EPI == EPI_STORE_BF16) {
-    constexpr int RB = BN * 2;                             // bytes per staged row
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = erow + 32 * mi;
-      float4 tv[16];
-      tile_vals(mi, tv);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
-          const float4 t = tv[4 * ni + g];
-          const uint2 v = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
-          *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
-        }
-    }
-    __syncthreads();
-    uint16_t* C = static_cast<uint16_t*>(p.C);
-    const int k = tid % (BN / 8), col = n0 + k * 8;         // fixed 16-byte column per thread
-    if (col < p.N) {
-      for (int r = tid / (BN / 8); r < nrows; r += kThreads / (BN / 8)) {
-        const int64_t crow = c_row_of(r);
-        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
-            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
-      }
-    }
-  } else {
-    // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
-    // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
-    constexpr bool MXO = EPI == EPI_SWIGLU_MX;
-    constexpr int RB = MXO ? (BN / 2) * 4 : (BN / 2) * 2;  // staged row: 128 fp32 or bf16
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = erow + 32 * mi;
-      float4 tv[16];
-      tile_vals(mi, tv);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 g4 = tv[4 * ni + g], u4 = tv[4 * (ni + 2) + g];
-          const float gvs[4] = {g4.x, g4.y, g4.z, g4.w}, uvs[4] = {u4.x, u4.y, u4.z, u4.w};
-          float a[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float gv = gvs[j], uv = uvs[j];
-            a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          }
-          const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
-          if (MXO) {
-            *reinterpret_cast<float4*>(lds + r * RB + (((i >> 2) ^ (r & 15)) << 4)) =
-                make_float4(a[0], a[1], a[2], a[3]);
-          } else {
-            *reinterpret_cast<uint2*>(lds + r * RB + (((i >> 3) ^ (r & 15)) << 4) + ((i >> 2) & 1) * 8) =
-                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-          }
-        }
-    }
-    __syncthreads();
-    if (!MXO) {
-      uint16_t* C = static_cast<uint16_t*>(p.C);
-      const int k = tid & 15, col = n0 + k * 8;             // fixed 16-byte column per thread
-      if (col < p.N) {
-        for (int r = tid >> 4; r < nrows; r += kThreads / 16) {
-          const int64_t crow = c_row_of(r);
-          *reinterpret_cast<uint4*>(C + crow * p.N + col) =
-              *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
-        }
-      }
-    } else {
-      uint8_t* C = static_cast<uint8_t*>(p.C);
-      const int b = tid & 3, col = n0 + b * 32;               // fixed 32-column block per thread
-      for (int r = tid >> 2; r < nrows && col < p.N; r += kThreads / 4) {
-        float v[32];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          const float4 f = *reinterpret_cast<const float4*>(lds + r * RB + (((8 * b + c4) ^ (r & 15)) << 4));
-          v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
-        const int E = mx_scale_exp(amax);
-        uint32_t w[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
-                 (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
-        const int64_t crow = c_row_of(r);
-        uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
-        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        p.C_scales[crow * (p.N / 32) + col / 32] = static_cast<uint8_t>(E + 127);
-      }
-    }
-  }
+  tile_finish<EPI>(p, job, acc, lds);
 }
 
 // A whole tile (all k-steps).

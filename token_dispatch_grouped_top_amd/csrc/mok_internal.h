@@ -148,16 +148,17 @@ struct FfnArgs {
   void* y; int32_t y_rows;
   int32_t H, I, act_format;
   int32_t w_packed;           // weights in the packed tile order (launch_pack_weights)
+  int32_t weight_format;      // MOK_W_MXFP8_E4M3: packed MXFP8 weights, both GEMMs in MXFP8
   SplitWs split;              // split.part null: every tile whole
 };
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // Packed weights: bytes, and the packing launch (either source may be null).
-size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
-size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local);
+size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);
+size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                               int32_t n_local, int32_t act_format, uint16_t* packed_gu,
-                               uint16_t* packed_d, hipStream_t s);
+                               int32_t n_local, int32_t act_format, int32_t weight_format,
+                               uint16_t* packed_gu, uint16_t* packed_d, hipStream_t s);
 
 }  // namespace mok

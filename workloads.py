@@ -260,6 +260,21 @@ def kimi_zipf_mxfp8(seed: int = 1004) -> Workload:
                       name="kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8")
 
 
+def kimi_full_mxfp8(seed: int = 1003, counts=None, name: str = "") -> Workload:
+    """The Kimi-shaped share with MXFP8 activations and MXFP8 weights (both GEMMs on the
+    block-scaled FP8 MFMA); balanced counts unless given."""
+    counts = BALANCED_COUNTS if counts is None else counts
+    wl = kimi_share(seed, counts=counts, act_format=ACT_MXFP8,
+                    name=name or "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8")
+    wl.weight_format = 1
+    return wl
+
+
+def kimi_zipf_full_mxfp8(seed: int = 1004) -> Workload:
+    return kimi_full_mxfp8(seed, counts=ZIPF_COUNTS,
+                           name="kimi_zipf_full_mxfp8_R8192_H7168_I2048_E384_k8_local8")
+
+
 def streaming(n_macro: int = 8, seed: int = 1005) -> List[Workload]:
     """n_macro macrobatches sharing one pool and one set of weights."""
     first = kimi_share(seed, name="stream_m0")
