@@ -37,12 +37,14 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("97753c840e537fad", 738610698),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("97753c840e537fad", 996484441),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 738607771),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 996603477),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 381907936),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
-                "token_dispatch_grouped_top_amd/csrc/mok_internal.h")
+                "token_dispatch_grouped_top_amd/csrc/mok_internal.h",
+                "token_dispatch_grouped_top_amd/csrc/gemm_tile_mx8.h")
 
 
 def gate_up_traffic(workload: str):
