@@ -11,6 +11,16 @@ namespace gemm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of LDS through a vector-typed load.  A struct copy (uint4) carries
+// no type-based alias information, and without it the compiler makes the read
+// wait for every direct-to-LDS load in flight (vmcnt(0), the newest stages
+// included); the pipelines' own vmcnt waits and barriers order the reads.
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
@@ -579,8 +589,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   do {                                                                                       \
     _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                       \
       const int r_ = 128 * wm + 32 * mi + frag_row;                                          \
-      araw[mi][0] = *reinterpret_cast<const uint4*>((pa) + G::offA(r_, 2 * khalf));          \
-      araw[mi][1] = *reinterpret_cast<const uint4*>((pa) + G::offA(r_, 2 * khalf + 1));      \
+      araw[mi][0] = lds_read16((pa) + G::offA(r_, 2 * khalf));                               \
+      araw[mi][1] = lds_read16((pa) + G::offA(r_, 2 * khalf + 1));                           \
       const uint32_t e_ = (ps)[r_ * 4 + khalf];                                              \
       ascale[mi] = __uint_as_float(e_ ? e_ << 23 : 0x00400000u);                             \
     }                                                                                        \

@@ -132,11 +132,9 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   i32x8_t tf[2][4], wf[2][4];
   int ts[2][4], wsc[2][4];
   auto frag = [&](const uint8_t* base, int r) -> i32x8_t {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + G::off(r, khalf));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + G::off(r, 2 + khalf));
-    return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
-                   static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
-                   static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + G::off(r, khalf));  // vector-typed:
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + G::off(r, 2 + khalf));  // see lds_read16
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 #define MX8_FRAGS(set, buf)                                                                  \
   do {                                                                                       \
