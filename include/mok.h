@@ -40,6 +40,14 @@
  *     expert's weights with 32-bit byte offsets: each must be smaller than
  *     4 GiB (ring_slots * H, act_rows * I and 2 * I * H elements), else the
  *     call returns MOK_ERR_UNSUPPORTED.
+ *   - The ring and the activation buffer (the grouped GEMMs' token
+ *     operands) are column-blocked: a buffer of `rows` rows of W values
+ *     holds each row in 64-byte blocks (32 bf16 or 64 E4M3 values), block
+ *     b of row r at byte (b * rows + r) * 64; its E8M0 scales (one per 32
+ *     values) go in pairs, scale j of row r at byte
+ *     (j / 2 * rows + r) * 2 + j % 2.  Sizes are those of the row-major
+ *     [rows][W] arrays (rows * W values, rows * W / 32 scales).  A GEMM
+ *     k-step of 256 rows is then 16 KiB of contiguous memory.
  */
 #ifndef MOK_H
 #define MOK_H
@@ -163,9 +171,11 @@ mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M,
 /* Pull dispatch (article, pull-dispatch paragraph).  For each slot s in
  * [slot_begin, min(slot_end, R)) with R = offsets[n_local]: ring row
  * s % ring_slots receives the row of token assign_of_slot[s] / k of src
- * (bf16, H values).  MOK_ACT_BF16: ring is bf16 [ring_slots][H], a bit copy.
- * MOK_ACT_MXFP8_E4M3: ring is E4M3 codes u8 [ring_slots][H] and ring_scales
- * E8M0 u8 [ring_slots][H/32] (OCP MX v1.0 blocks of 32 along H).
+ * (bf16, H values; H a multiple of 64).  MOK_ACT_BF16: ring holds
+ * ring_slots x H bf16, a bit copy.  MOK_ACT_MXFP8_E4M3: ring holds
+ * ring_slots x H E4M3 codes (u8) and ring_scales ring_slots x H/32 E8M0
+ * scales (OCP MX v1.0 blocks of 32 along H).  Both column-blocked (see the
+ * conventions above).
  * A token index outside src sets *dev_status = MOK_ERR_CAPACITY and the row
  * is skipped.  assign_of_slot is read at every slot of [slot_begin,
  * slot_end) (entries at or past R are ignored), so it holds slot_end
@@ -183,7 +193,8 @@ mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
  * (offsets[e] <= s < offsets[e+1]), with x = ring row s % ring_slots:
  *   g = W_gu[e][0:I] . x,  u = W_gu[e][I:2I] . x      (fp32 accumulation)
  *   a = SiLU(g) * u  -> act row s % act_rows (bf16, or MXFP8 blocks of 32
- *                       along I into act/act_scales [act_rows][I/32])
+ *                       along I into act and act_scales; both
+ *                       column-blocked like the ring)
  *   y = W_d[e] . a   -> y row s % y_rows (bf16 [y_rows][H])
  * w_gate_up: bf16 [n_local][2I][H], rows 0..I-1 gate, I..2I-1 up; w_down:
  * bf16 [n_local][H][I]; no biases.  desc supplies H, I, n_local, act_format.

@@ -25,6 +25,23 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return a
 
 
+def colblk_rows(t: torch.Tensor, rows: int) -> np.ndarray:
+    """Row-major host copy of a column-blocked row buffer (the ring, act):
+    64-byte block b of row r sits at byte (b * rows + r) * 64."""
+    a = t.detach().contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+    nb = a.size // (rows * 64)
+    out = a[:nb * rows * 64].reshape(nb, rows, 64).transpose(1, 0, 2).reshape(rows, nb * 64)
+    return out.view(np.uint16) if t.element_size() == 2 else out
+
+
+def colblk_scales(t: torch.Tensor, rows: int) -> np.ndarray:
+    """Row-major host copy of column-blocked E8M0 scales: scale j of row r
+    sits at byte (j // 2 * rows + r) * 2 + j % 2."""
+    a = t.detach().contiguous().reshape(-1).cpu().numpy()
+    npair = a.size // (rows * 2)
+    return a[:npair * rows * 2].reshape(npair, rows, 2).transpose(1, 0, 2).reshape(rows, 2 * npair)
+
+
 def empty_u16(*shape) -> torch.Tensor:
     return torch.empty(shape, dtype=torch.int16, device="cuda")
 

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_harness import SENTINEL, DeviceWorkload, assert_close_rms, to_host
+from gpu_harness import SENTINEL, DeviceWorkload, assert_close_rms, colblk_rows, colblk_scales, to_host
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -90,10 +90,10 @@ def _check_pool_case(wl, tol):
     # dispatched rows (bit-exact) and expert outputs on sampled slots
     slots = _sample_slots(sch["offsets"], rng)
     xr = oracle.gather_rows(wl.x, wl.k, sch["assign_of_slot"], slots, mx)
-    ring = to_host(st.ring[torch.as_tensor(slots, device="cuda")])
+    ring = colblk_rows(st.ring, st.cap)[slots]
     if mx:
         assert np.array_equal(ring, xr[0])
-        assert np.array_equal(to_host(st.ring_sc[torch.as_tensor(slots, device="cuda")]), xr[1])
+        assert np.array_equal(colblk_scales(st.ring_sc, st.cap)[slots], xr[1])
     else:
         assert np.array_equal(ring, xr)
     y_ref = oracle.ffn_rows(xr, oracle.expert_of_slots(sch["offsets"], slots), wl.w_gu, wl.w_d, mx)

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_harness import DeviceWorkload, assert_close_rms, empty_u16, gpu_schedule, to_dev, to_host
+from gpu_harness import (DeviceWorkload, assert_close_rms, colblk_rows, colblk_scales, empty_u16,
+                         gpu_schedule, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,7 +89,11 @@ def test_schedule_pool_and_windows():
 
 
 @pytest.mark.parametrize("mx", [False, True])
-def test_gather_bit_exact(mx):
+@pytest.mark.parametrize("S,Wn", [(256, 256), (255, 201)])
+def test_gather_bit_exact(mx, S, Wn):
+    """Windows of Wn slots through a ring of S rows.  (255, 201): windows
+    start at odd slots and wrap around the ring, also between the two slots
+    a wave gathers together."""
     import token_dispatch_grouped_top_amd as mok
     wl = W.small_pool(22, n_partitions=5, part_rows=300, H=448, I=64, E=64, k=4, expert_base=8,
                       counts=[200, 1, 0, 333, 90])
@@ -97,21 +102,21 @@ def test_gather_bit_exact(mx):
     dw = DeviceWorkload(wl)
     s = dw.schedule(dw.topk_idx)
     ref = oracle.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)
-    R, H, S = ref["R"], wl.H, 256
+    R, H = ref["R"], wl.H
     fmt = mok.MOK_ACT_MXFP8_E4M3 if mx else mok.MOK_ACT_BF16
     ring = torch.zeros((S, H), dtype=torch.uint8 if mx else torch.int16, device="cuda")
     ring_sc = torch.zeros((S, H // 32), dtype=torch.uint8, device="cuda") if mx else None
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for s0 in range(0, R, S):     # window by window through the ring
-        mok.mok_dispatch_gather(dw.x, H, wl.k, s["aos"], s["offsets"], wl.n_local, s0, s0 + S,
+    for s0 in range(0, R, Wn):    # window by window through the ring
+        mok.mok_dispatch_gather(dw.x, H, wl.k, s["aos"], s["offsets"], wl.n_local, s0, s0 + Wn,
                                 ring, ring_sc, S, fmt, status)
         torch.cuda.synchronize()
-        slots = np.arange(s0, min(s0 + S, R))
-        got = to_host(ring)[slots % S]
+        slots = np.arange(s0, min(s0 + Wn, R))
+        got = colblk_rows(ring, S)[slots % S]
         exp = oracle.gather_rows(wl.x, wl.k, ref["assign_of_slot"], slots, mx)
         if mx:
             assert np.array_equal(got, exp[0])
-            assert np.array_equal(to_host(ring_sc)[slots % S], exp[1])
+            assert np.array_equal(colblk_scales(ring_sc, S)[slots % S], exp[1])
         else:
             assert np.array_equal(got, exp)
     assert int(status.item()) == 0

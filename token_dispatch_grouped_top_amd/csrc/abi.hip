@@ -232,11 +232,11 @@ mok_status mok_dispatch_gather(const mok_tokens* src, int32_t H, int32_t k,
                                int32_t n_local, int32_t slot_begin, int32_t slot_end, void* ring,
                                uint8_t* ring_scales, int32_t ring_slots, int32_t act_format,
                                int32_t* dev_status, hipStream_t stream) {
-  if (!tokens_ok(src, 0) || H <= 0 || H % 8 != 0 || k < 1 || !assign_of_slot || !offsets ||
+  if (!tokens_ok(src, 0) || H <= 0 || H % 64 != 0 || k < 1 || !assign_of_slot || !offsets ||
       n_local < 1 || slot_begin < 0 || slot_end < slot_begin || !ring || ring_slots < 1)
     return MOK_ERR_INVALID_ARG;
   if (act_format == MOK_ACT_MXFP8_E4M3) {
-    if (H % 32 != 0 || !ring_scales) return MOK_ERR_INVALID_ARG;
+    if (!ring_scales) return MOK_ERR_INVALID_ARG;
   } else if (act_format != MOK_ACT_BF16) {
     return MOK_ERR_INVALID_ARG;
   }

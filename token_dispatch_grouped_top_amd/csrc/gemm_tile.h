@@ -70,16 +70,16 @@ static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LD
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
 
 struct GemmParams {
-  const void* A;              // bf16 [a_rows][K] or E4M3 codes [a_rows][K]
-  const uint8_t* A_scales;    // [a_rows][K/32] when A is MXFP8
+  const void* A;              // bf16 or E4M3 codes, a_rows x K, column-blocked
+  const uint8_t* A_scales;    // a_rows x K/32 scale pairs (column-blocked) when A is MXFP8
   int32_t a_rows;
   const uint16_t* W;          // [n_local][w_rows][K]
   int64_t w_expert_stride;    // elements
   int32_t K;
   int32_t N;                  // output columns (I for gate/up, H for down)
   int32_t I;                  // up-row offset for gate/up
-  void* C;                    // bf16 [c_rows][N] or E4M3 codes [c_rows][N]
-  uint8_t* C_scales;          // [c_rows][N/32]
+  void* C;                    // y: bf16 [c_rows][N]; act: bf16 or E4M3 codes, column-blocked
+  uint8_t* C_scales;          // act scale pairs, c_rows x N/32 (column-blocked)
   int32_t c_rows;
   const int32_t* offsets;
   int32_t n_local;
@@ -389,13 +389,15 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
         }
     }
     __syncthreads();
+    // act is column-blocked (the down GEMM's token operand): 64-byte block
+    // b of act row c at byte (b * c_rows + c) * 64
     if (!MXO) {
-      uint16_t* C = static_cast<uint16_t*>(p.C);
+      uint8_t* C = static_cast<uint8_t*>(p.C);
       const int k = tid & 15, col = n0 + k * 8;             // fixed 16-byte column per thread
       if (col < p.N) {
         for (int r = tid >> 4; r < nrows; r += kThreads / 16) {
           const int64_t crow = c_row_of(r);
-          *reinterpret_cast<uint4*>(C + crow * p.N + col) =
+          *reinterpret_cast<uint4*>(C + colblk_byte(crow, p.c_rows, 2 * col)) =
               *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
         }
       }
@@ -419,10 +421,10 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
           w[q] = e4m3_code_scaled(v[4 * q], E) | (e4m3_code_scaled(v[4 * q + 1], E) << 8) |
                  (e4m3_code_scaled(v[4 * q + 2], E) << 16) | (e4m3_code_scaled(v[4 * q + 3], E) << 24);
         const int64_t crow = c_row_of(r);
-        uint4* d = reinterpret_cast<uint4*>(C + crow * p.N + col);
+        uint4* d = reinterpret_cast<uint4*>(C + colblk_byte(crow, p.c_rows, col));
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        p.C_scales[crow * (p.N / 32) + col / 32] = static_cast<uint8_t>(E + 127);
+        p.C_scales[scale_byte(crow, p.c_rows, col / 32)] = static_cast<uint8_t>(E + 127);
       }
     }
   }
@@ -479,19 +481,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
                     static_cast<uint32_t>(K) + lchunkB * 8;
   }
   // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
+  // The A buffer is column-blocked (a k-step of either format is one 64-byte
+  // block per row, block-major): load j of k-step kt reads byte aoff[j] +
+  // kt * a_kstep, and the tile's rows of a k-step are contiguous memory.
   auto a_ring_row = [&](int r) -> uint32_t {
     const int rr = r < nrows ? r : nrows - 1;
     return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
   };
+  const uint32_t a_kstep = static_cast<uint32_t>(p.a_rows) * kColBlock;
   const int lrowA = tid / G::CPR_A;
   const int lchunkA = (lane % G::CPR_A) ^ chunk_key<G::CPR_A>(lrowA);
-  uint32_t aoff[8];                                           // element (bf16) / byte (E4M3) offsets
+  uint32_t aoff[8];                                           // byte offsets
 #pragma unroll
   for (int j = 0; j < G::NLOAD_A; ++j)
-    aoff[j] = a_ring_row(lrowA + G::RSTEP_A * j) * static_cast<uint32_t>(K) +
-              lchunkA * (A_MX ? 16 : 8) + kt0 * BK;
-  // E4M3 A: thread tid fetches the two block scales of row tid for each k-step
-  const uint32_t soff = A_MX ? a_ring_row(tid) * static_cast<uint32_t>(K / 32) + 2 * kt0 : 0;
+    aoff[j] = a_ring_row(lrowA + G::RSTEP_A * j) * kColBlock + lchunkA * 16 +
+              static_cast<uint32_t>(kt0) * a_kstep;
+  // E4M3 A: thread tid fetches the scale pair of row tid for each k-step
+  // (pairs are block-major too: k-step kt's pairs are a_rows * 2 bytes apart)
+  const uint32_t soff = A_MX ? a_ring_row(tid) * 2u + static_cast<uint32_t>(kt0) * p.a_rows * 2u : 0;
   // Raw buffer descriptors over the operands (byte extents below 4 GiB, which
   // the launchers check); a load past an extent reads zero.
   auto extent = [](int64_t bytes) -> int32_t {
@@ -530,8 +537,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(dst), 16, boff[j] * 2u,            \
                                            static_cast<uint32_t>(kt) * wkstride * 2u, 0, 0)
 #define MOK_LD_A(j, kt, dst)                                                                 \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(dst), 16, aoff[j] * 2u,            \
-                                           static_cast<uint32_t>(kt) * (BK * 2u), 0, 0)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(dst), 16, aoff[j],                 \
+                                           static_cast<uint32_t>(kt) * a_kstep, 0, 0)
   // The two halves of a stage's direct loads: weights; tokens (+ E4M3 scales,
   // 2 bytes per lane, which land in 4-byte slots: lane i at slot base + 4 i).
 #define MOK_ISSUE_W(kt, buf)                                                                 \
@@ -546,9 +553,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
     if (A_MX) {                                                                              \
       _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(As_ + (4 * j + wave) * 1024), \
-                                                 16, aoff[j], static_cast<uint32_t>(kt) * BK, 0, 0); \
+                                                 16, aoff[j], static_cast<uint32_t>(kt) * a_kstep, 0, 0); \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(tileS(buf) + wave * 256), 2, soff, \
-                                               static_cast<uint32_t>(kt) * 2u, 0, 0);        \
+                                               static_cast<uint32_t>(kt) * p.a_rows * 2u, 0, 0); \
     } else {                                                                                 \
       _Pragma("unroll") for (int j = 0; j < G::NLOAD_A; ++j)                                 \
         MOK_LD_A(j, kt, As_ + (4 * j + wave) * 1024);                                        \

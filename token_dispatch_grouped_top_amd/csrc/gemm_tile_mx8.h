@@ -66,18 +66,21 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #pragma unroll
   for (int j = 0; j < G::NLOAD; ++j) boff[j] = (4 * j + wave) * 1024 + lane * 16;
   // tokens: ring rows, tail rows clamped to the last valid one; lane l of load
-  // j lands at physical chunk l % 4 of row tid / 4 + RSTEP j
+  // j lands at physical chunk l % 4 of row tid / 4 + RSTEP j.  The ring is
+  // column-blocked: a k-step is one 64-byte block per row, a_kstep bytes
+  // apart, and scale pairs a_rows * 2 bytes apart.
   auto a_ring_row = [&](int r) -> uint32_t {
     const int rr = r < nrows ? r : nrows - 1;
     return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
   };
+  const uint32_t a_kstep = static_cast<uint32_t>(p.a_rows) * kColBlock;
   const int lrow = tid / G::CPR;
   const int lchunk = (lane % G::CPR) ^ chunk_key<G::CPR>(lrow);
   uint32_t aoff[G::NLOAD];
 #pragma unroll
   for (int j = 0; j < G::NLOAD; ++j)
-    aoff[j] = a_ring_row(lrow + G::RSTEP * j) * static_cast<uint32_t>(K) + lchunk * 16 + kt0 * BK;
-  const uint32_t soff = a_ring_row(tid) * static_cast<uint32_t>(K / 32) + 2 * kt0;
+    aoff[j] = a_ring_row(lrow + G::RSTEP * j) * kColBlock + lchunk * 16 + static_cast<uint32_t>(kt0) * a_kstep;
+  const uint32_t soff = a_ring_row(tid) * 2u + static_cast<uint32_t>(kt0) * p.a_rows * 2u;
   auto extent = [](int64_t bytes) -> int32_t {
     return static_cast<int32_t>(bytes < 0xffffffffll ? bytes : 0xffffffffll);
   };
@@ -122,9 +125,9 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
     uint8_t* As_ = tileA(buf);                                                               \
     _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(As_ + (4 * j + wave) * 1024), 16, \
-                                               aoff[j], static_cast<uint32_t>(kt) * BK, 0, 0); \
+                                               aoff[j], static_cast<uint32_t>(kt) * a_kstep, 0, 0); \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(tileSA(buf) + wave * 256), 2,   \
-                                             soff, static_cast<uint32_t>(kt) * 2u, 0, 0);    \
+                                             soff, static_cast<uint32_t>(kt) * p.a_rows * 2u, 0, 0); \
   } while (0)
 
   // Fragments of one k-step into register set `set`: rows of the wave's token

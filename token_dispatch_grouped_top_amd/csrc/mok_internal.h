@@ -37,6 +37,22 @@ __device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_nt*>(p));
 }
 
+// ------------------------------------------------ column-blocked row buffers
+// The buffers the grouped GEMMs read as their token operand (the ring and
+// the activation buffer) hold each row in 64-byte column blocks, block-major:
+// block b (32 bf16 or 64 E4M3 values) of row r sits at byte (b * rows + r) *
+// 64.  A GEMM k-step of a 256-row tile is then 16 KiB of contiguous memory,
+// fetched in whole 128-byte lines.  E8M0 scales go in pairs (the two blocks
+// of 32 of a 64-value block): scale j of row r at byte (j / 2 * rows + r) *
+// 2 + j % 2.
+constexpr int kColBlock = 64;
+__device__ __forceinline__ int64_t colblk_byte(int64_t r, int64_t rows, int64_t byte_in_row) {
+  return ((byte_in_row >> 6) * rows + r) * kColBlock + (byte_in_row & 63);
+}
+__device__ __forceinline__ int64_t scale_byte(int64_t r, int64_t rows, int64_t j) {
+  return ((j >> 1) * rows + r) * 2 + (j & 1);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_cvt v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt));

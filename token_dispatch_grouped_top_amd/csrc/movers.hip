@@ -1,7 +1,8 @@
 // movers.hip -- standalone pull dispatch (gather into the ring) and push
 // combine with the final weighted merge; the row routines are in
-// movers_dev.h.  Both kernels are HBM-bound row copies / reductions: one wave
-// per row, 4 rows per 256-thread workgroup.
+// movers_dev.h.  Both kernels are HBM-bound row copies / reductions: the
+// gather takes two consecutive slots per wave, the merge one token per wave,
+// 4 waves per 256-thread workgroup.
 #include "movers_dev.h"
 
 namespace mok {
@@ -10,36 +11,49 @@ namespace {
 
 using namespace movers;
 
-constexpr int kRowsPerBlock = 4;   // waves per block, one row each
+constexpr int kRowsPerBlock = 4;   // waves per block (merge: one token each)
+constexpr int kPairsPerBlock = 4;  // waves per block (gather: two consecutive slots each)
 
-__global__ __launch_bounds__(kRowsPerBlock * kWave)
+// The wave's slots s and s + 1 and their tokens t1, t2 (t2 = -1 when s + 1
+// is past the end); false: nothing to do.
+__device__ __forceinline__ bool gather_slots(const int32_t* __restrict__ aos,
+                                             const int32_t* __restrict__ offsets, int32_t n_local,
+                                             int32_t k, int32_t s_begin, int32_t s_end,
+                                             int64_t& s, int64_t& t1, int64_t& t2) {
+  s = static_cast<int64_t>(s_begin) +
+      2 * (static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + threadIdx.x / kWave);
+  if (s >= s_end) return false;
+  const int32_t a1 = aos[s];                             // aos holds s_end entries: both are
+  const int32_t a2 = s + 1 < s_end ? aos[s + 1] : 0;     // issued together with R
+  const int32_t R = offsets[n_local];
+  if (s >= R) return false;
+  t1 = a1 / k;
+  t2 = s + 1 < s_end && s + 1 < R ? a2 / k : -1;
+  return true;
+}
+
+__global__ __launch_bounds__(kPairsPerBlock * kWave)
 void k_gather_bf16(void* const* __restrict__ parts, int32_t n_part, int32_t part_rows,
                    int32_t H, int32_t k, const int32_t* __restrict__ aos,
                    const int32_t* __restrict__ offsets, int32_t n_local, int32_t s_begin,
                    int32_t s_end, uint16_t* __restrict__ ring, int32_t ring_slots,
                    int32_t* status) {
-  const int64_t s = static_cast<int64_t>(s_begin) + static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
-                    threadIdx.x / kWave;
-  if (s >= s_end) return;
-  const int32_t a = aos[s];                 // issued together with R (aos holds s_end entries)
-  const int32_t R = offsets[n_local];
-  if (s >= R) return;
-  gather_row_bf16(parts, n_part, part_rows, H, a / k, ring, s % ring_slots, status);
+  int64_t s, t1, t2;
+  if (!gather_slots(aos, offsets, n_local, k, s_begin, s_end, s, t1, t2)) return;
+  gather_pair_bf16(parts, n_part, part_rows, H, t1, t2, ring, s % ring_slots, (s + 1) % ring_slots,
+                   ring_slots, status);
 }
 
-__global__ __launch_bounds__(kRowsPerBlock * kWave)
+__global__ __launch_bounds__(kPairsPerBlock * kWave)
 void k_gather_mxfp8(void* const* __restrict__ parts, int32_t n_part, int32_t part_rows,
                     int32_t H, int32_t k, const int32_t* __restrict__ aos,
                     const int32_t* __restrict__ offsets, int32_t n_local, int32_t s_begin,
                     int32_t s_end, uint8_t* __restrict__ ring, uint8_t* __restrict__ scales,
                     int32_t ring_slots, int32_t* status) {
-  const int64_t s = static_cast<int64_t>(s_begin) + static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
-                    threadIdx.x / kWave;
-  if (s >= s_end) return;
-  const int32_t a = aos[s];                 // issued together with R (aos holds s_end entries)
-  const int32_t R = offsets[n_local];
-  if (s >= R) return;
-  gather_row_mxfp8(parts, n_part, part_rows, H, a / k, ring, scales, s % ring_slots, status);
+  int64_t s, t1, t2;
+  if (!gather_slots(aos, offsets, n_local, k, s_begin, s_end, s, t1, t2)) return;
+  gather_pair_mxfp8(parts, n_part, part_rows, H, t1, t2, ring, scales, s % ring_slots,
+                    (s + 1) % ring_slots, ring_slots, status);
 }
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
@@ -78,13 +92,14 @@ hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_row
                          int32_t ring_slots, int32_t act_format, int32_t* status, hipStream_t s) {
   int64_t rows = static_cast<int64_t>(s_end) - s_begin;
   if (rows <= 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int64_t pairs = (rows + 1) / 2;
+  dim3 grid(static_cast<unsigned>((pairs + kPairsPerBlock - 1) / kPairsPerBlock));
   if (act_format == MOK_ACT_MXFP8_E4M3) {
-    hipLaunchKernelGGL(k_gather_mxfp8, grid, dim3(kRowsPerBlock * kWave), 0, s, part_ptr, n_part,
+    hipLaunchKernelGGL(k_gather_mxfp8, grid, dim3(kPairsPerBlock * kWave), 0, s, part_ptr, n_part,
                        part_rows, H, k, aos, offsets, n_local, s_begin, s_end,
                        static_cast<uint8_t*>(ring), ring_scales, ring_slots, status);
   } else {
-    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(kRowsPerBlock * kWave), 0, s, part_ptr, n_part,
+    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(kPairsPerBlock * kWave), 0, s, part_ptr, n_part,
                        part_rows, H, k, aos, offsets, n_local, s_begin, s_end,
                        static_cast<uint16_t*>(ring), ring_slots, status);
   }

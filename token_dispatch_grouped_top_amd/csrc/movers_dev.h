@@ -8,9 +8,8 @@
 // fused into dispatch (state-machine paragraph).  With the sources being
 // HBM partitions of this GPU, the pull is a gather of whole rows.
 //
-// One wave per row.  Lane l moves the 16-byte pieces l, l+64, ... of the row,
-// so every wave instruction touches 1 KiB of contiguous memory; loads of a row
-// are issued in batches before any store to keep many requests in flight.
+// The gather moves two rows per wave, the merge one token per wave; loads are
+// issued in batches before any store to keep many requests in flight.
 #pragma once
 
 #include "mok_internal.h"
@@ -18,7 +17,6 @@
 namespace mok {
 namespace movers {
 
-constexpr int kBatch = 8;          // 16-byte pieces in flight per lane (gather)
 constexpr int kCombPieces = 4;     // 16-byte pieces per lane per batch (several local slots:
                                    // fp32 accumulators; kept small for occupancy)
 constexpr int kMergeFast = 8;      // 16-byte pieces per lane per batch (single local slot)
@@ -30,93 +28,85 @@ __device__ __forceinline__ const uint4* token_row(void* const* parts, int32_t n_
   return reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(parts[p]) + r * H);
 }
 
-// Pull the row of token t into ring row dst_row: bf16 bit copy.
-__device__ __forceinline__ void gather_row_bf16(void* const* __restrict__ parts, int32_t n_part,
-                                                int32_t part_rows, int32_t H, int64_t t,
-                                                uint16_t* __restrict__ ring, int64_t dst_row,
-                                                int32_t* status) {
-  const int lane = lane_id();
-  const uint4* src = token_row(parts, n_part, part_rows, t, H);
-  if (!src) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
-  uint4* dst = reinterpret_cast<uint4*>(ring + dst_row * static_cast<int64_t>(H));
-  const int nvec = H / 8;
-  for (int v0 = lane; v0 < nvec; v0 += kWave * kBatch) {
-    uint4 buf[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int v = v0 + u * kWave;
-      if (v < nvec) buf[u] = src[v];
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int v = v0 + u * kWave;
-      if (v < nvec) st_nt(dst + v, buf[u]);
-    }
-  }
+// Pull of two ring rows per wave: the rows of tokens t1 and t2 into ring rows
+// rr1 and rr2 (t2 < 0: t1 alone).  The ring is column-blocked (block b of
+// row r at byte (b * rows + r) * 64), so block b of two consecutive ring rows
+// is one 128-byte line.  Lane l of wave instruction u takes piece p = 64 u + l
+// of the pair, 16 source bytes (8 bf16): G consecutive lanes fill one 64-byte
+// destination block and the two rows alternate every G lanes, so an
+// instruction reads 512 contiguous source bytes of each row and writes
+// 64-byte blocks that pair up into whole lines.  kPairBatch pieces per lane
+// are loaded before any is stored.
+constexpr int kPairBatch = 16;
+template <int G>
+__device__ __forceinline__ void pair_piece(int p, int& sel, int& v) {
+  sel = (p / G) & 1;                      // which row of the pair
+  v = (p / (2 * G)) * G + p % G;          // 16-byte source piece of that row
 }
 
-// Pull of rows s = first, first + step, ... < end, two rows per wave at a
-// time: both rows' indices are read first, then kBatch 16-byte pieces of each
-// row are loaded before any is stored, so a wave keeps 2 x kBatch pieces per
-// lane in flight.  Destination row of slot s: (dst_base + s) % ring_slots.
-__device__ __forceinline__ void gather_rows_bf16_x2(void* const* __restrict__ parts,
-                                                    int32_t n_part, int32_t part_rows, int32_t H,
-                                                    int32_t k, const int32_t* __restrict__ aos,
-                                                    int64_t first, int64_t step, int64_t end,
-                                                    uint16_t* __restrict__ ring, int64_t dst_base,
-                                                    int32_t ring_slots, int32_t* status) {
-  const int lane = lane_id();
-  const int nvec = H / 8;
-  for (int64_t s = first; s < end; s += 2 * step) {
-    const int64_t s2 = s + step < end ? s + step : s;   // odd tail: copy row s twice
-    const uint4* src1 = token_row(parts, n_part, part_rows, aos[s] / k, H);
-    const uint4* src2 = token_row(parts, n_part, part_rows, aos[s2] / k, H);
-    if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); continue; }
-    uint4* d1 = reinterpret_cast<uint4*>(ring + ((dst_base + s) % ring_slots) * static_cast<int64_t>(H));
-    uint4* d2 = reinterpret_cast<uint4*>(ring + ((dst_base + s2) % ring_slots) * static_cast<int64_t>(H));
-    for (int v0 = lane; v0 - lane < nvec; v0 += kWave * kBatch) {
-      uint4 b1[kBatch], b2[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int v = v0 + u * kWave;
-        if (v < nvec) { b1[u] = src1[v]; b2[u] = src2[v]; }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int v = v0 + u * kWave;
-        if (v < nvec) { st_nt(d1 + v, b1[u]); st_nt(d2 + v, b2[u]); }
-      }
-    }
-  }
-}
-
-// Same with MXFP8 quantisation on the way: a block of 32 values is 4
-// consecutive 16-byte pieces, i.e. 4 consecutive lanes; amax by two
-// xor-shuffles.  All 64 lanes must call it (wave-uniform loop).
-__device__ __forceinline__ void gather_row_mxfp8(void* const* __restrict__ parts, int32_t n_part,
-                                                 int32_t part_rows, int32_t H, int64_t t,
-                                                 uint8_t* __restrict__ ring,
-                                                 uint8_t* __restrict__ scales, int64_t dst_row,
+// bf16: a bit copy, G = 4 (a 64-byte block is 4 source pieces).
+__device__ __forceinline__ void gather_pair_bf16(void* const* __restrict__ parts, int32_t n_part,
+                                                 int32_t part_rows, int32_t H, int64_t t1,
+                                                 int64_t t2, uint16_t* __restrict__ ring,
+                                                 int64_t rr1, int64_t rr2, int32_t rows,
                                                  int32_t* status) {
   const int lane = lane_id();
-  const uint4* src = token_row(parts, n_part, part_rows, t, H);
-  if (!src) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
-  const int64_t rr = dst_row;
-  uint2* dst = reinterpret_cast<uint2*>(ring + rr * static_cast<int64_t>(H));
-  uint8_t* sdst = scales + rr * static_cast<int64_t>(H / 32);
-  const int nvec = H / 8;   // H % 32 == 0, so nvec % 4 == 0: blocks never straddle lane groups
-  for (int v0 = lane; v0 - lane < nvec; v0 += kWave * kBatch) {
-    uint4 buf[kBatch];
+  const uint4* src1 = token_row(parts, n_part, part_rows, t1, H);
+  const uint4* src2 = t2 >= 0 ? token_row(parts, n_part, part_rows, t2, H) : src1;
+  if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
+  if (t2 < 0) rr2 = rr1;                  // the second half repeats row 1's copy
+  uint8_t* ringb = reinterpret_cast<uint8_t*>(ring);
+  const int npc = 2 * (H / 8);            // pieces of the pair
+  for (int p0 = 0; p0 < npc; p0 += kWave * kPairBatch) {
+    uint4 buf[kPairBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int v = v0 + u * kWave;
-      if (v < nvec) buf[u] = src[v];
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int p = p0 + u * kWave + lane;
+      int sel, v;
+      pair_piece<4>(p, sel, v);
+      if (p < npc) buf[u] = (sel ? src2 : src1)[v];
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int v = v0 + u * kWave;
-      if (v0 - lane + u * kWave >= nvec) break;      // wave-uniform
-      const bool ok = v < nvec;
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int p = p0 + u * kWave + lane;
+      int sel, v;
+      pair_piece<4>(p, sel, v);
+      if (p < npc) st_nt(reinterpret_cast<uint4*>(ringb + colblk_byte(sel ? rr2 : rr1, rows, 16 * v)), buf[u]);
+    }
+  }
+}
+
+// MXFP8 quantisation on the way, G = 8 (64 codes are 8 source pieces).  A
+// block of 32 values is 4 consecutive pieces, i.e. 4 consecutive lanes of one
+// row; its amax by two xor-shuffles.  Lane v % 4 == 0 of a block writes its
+// E8M0 scale.  All 64 lanes must call it (wave-uniform loop).
+__device__ __forceinline__ void gather_pair_mxfp8(void* const* __restrict__ parts, int32_t n_part,
+                                                  int32_t part_rows, int32_t H, int64_t t1,
+                                                  int64_t t2, uint8_t* __restrict__ ring,
+                                                  uint8_t* __restrict__ scales, int64_t rr1,
+                                                  int64_t rr2, int32_t rows, int32_t* status) {
+  const int lane = lane_id();
+  const uint4* src1 = token_row(parts, n_part, part_rows, t1, H);
+  const uint4* src2 = t2 >= 0 ? token_row(parts, n_part, part_rows, t2, H) : src1;
+  if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
+  if (t2 < 0) rr2 = rr1;
+  const int npc = 2 * (H / 8);            // H % 64 == 0: groups of 8 lanes are whole
+  for (int p0 = 0; p0 < npc; p0 += kWave * kPairBatch) {
+    uint4 buf[kPairBatch];
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int p = p0 + u * kWave + lane;
+      int sel, v;
+      pair_piece<8>(p, sel, v);
+      if (p < npc) buf[u] = (sel ? src2 : src1)[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      if (p0 + u * kWave >= npc) break;   // wave-uniform
+      const int p = p0 + u * kWave + lane;
+      const bool ok = p < npc;
+      int sel, v;
+      pair_piece<8>(p, sel, v);
       float f[8];
       const uint32_t w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
 #pragma unroll
@@ -138,8 +128,9 @@ __device__ __forceinline__ void gather_row_mxfp8(void* const* __restrict__ parts
         hi |= e4m3_code_scaled(f[q + 4], E) << (8 * q);
       }
       if (ok) {
-        st_nt(dst + v, make_uint2(lo, hi));
-        if ((v & 3) == 0) sdst[v >> 2] = static_cast<uint8_t>(E + 127);
+        const int64_t rr = sel ? rr2 : rr1;
+        st_nt(reinterpret_cast<uint2*>(ring + colblk_byte(rr, rows, 8 * v)), make_uint2(lo, hi));
+        if ((v & 3) == 0) scales[scale_byte(rr, rows, v >> 2)] = static_cast<uint8_t>(E + 127);
       }
     }
   }

@@ -252,20 +252,24 @@ __device__ __forceinline__ void signal_add(int32_t* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Gather of window w by the waves first, first + step, ...
+// Gather of window w by the waves first, first + step, ...: wave i takes
+// the slot pairs (s0 + 2 q, s0 + 2 q + 1), q = i, i + step, ...
 template <bool A_MX>
 __device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c, int w,
                                               int64_t first, int64_t step) {
   const PMacro pm = c.pm[c.win_m[w]];
   const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
   const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
-  if (A_MX) {
-    for (int64_t s = s0 + first; s < s1; s += step)
-      gather_row_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, pm.aos[s] / a.k,
-                       static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, a.status);
-  } else {
-    gather_rows_bf16_x2(a.x_parts, a.x_n_part, a.x_part_rows, a.H, a.k, pm.aos, s0 + first, step,
-                        s1, static_cast<uint16_t*>(a.ring), base, a.S, a.status);
+  for (int64_t s = s0 + 2 * first; s < s1; s += 2 * step) {
+    const int64_t t1 = pm.aos[s] / a.k;
+    const int64_t t2 = s + 1 < s1 ? pm.aos[s + 1] / a.k : -1;
+    if (A_MX)
+      gather_pair_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, t1, t2,
+                        static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, base + s + 1, a.S,
+                        a.status);
+    else
+      gather_pair_bf16(a.x_parts, a.x_n_part, a.x_part_rows, a.H, t1, t2,
+                       static_cast<uint16_t*>(a.ring), base + s, base + s + 1, a.S, a.status);
   }
 }
 
