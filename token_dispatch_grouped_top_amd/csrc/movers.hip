@@ -12,16 +12,31 @@ namespace {
 using namespace movers;
 
 constexpr int kRowsPerBlock = 4;   // waves per block (merge: one token each)
-constexpr int kPairsPerBlock = 4;  // waves per block (gather: two consecutive slots each)
+constexpr int kGatherWaves = 4;    // waves per block (gather)
+// Waves per slot pair, each moving a contiguous share of the pair's pieces:
+// 2 for the bf16 copy, 4 for the MXFP8 gather, whose quantisation keeps each
+// wave longer between its loads and stores (measured inside the bench step
+// on the Kimi-shaped share: bf16 53.5 -> 50 us with 2, MXFP8 62 -> 51 us
+// with 4, against one wave per pair).
+template <bool MX> struct GatherShape { static constexpr int kWavesPerPair = MX ? 4 : 2; };
 
-// The wave's slots s and s + 1 and their tokens t1, t2 (t2 = -1 when s + 1
-// is past the end); false: nothing to do.
+// The wave's slots s and s + 1, their tokens t1, t2 (t2 = -1 when s + 1 is
+// past the end) and its share [p_lo, p_hi) of the pair's 16-byte pieces
+// (whole 2 G-piece groups, G = 4 bf16 / 8 E4M3); false: nothing to do.
+template <bool MX>
 __device__ __forceinline__ bool gather_slots(const int32_t* __restrict__ aos,
                                              const int32_t* __restrict__ offsets, int32_t n_local,
-                                             int32_t k, int32_t s_begin, int32_t s_end,
-                                             int64_t& s, int64_t& t1, int64_t& t2) {
-  s = static_cast<int64_t>(s_begin) +
-      2 * (static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + threadIdx.x / kWave);
+                                             int32_t k, int32_t H, int32_t s_begin, int32_t s_end,
+                                             int64_t& s, int64_t& t1, int64_t& t2, int& p_lo,
+                                             int& p_hi) {
+  constexpr int G = MX ? 8 : 4, kWavesPerPair = GatherShape<MX>::kWavesPerPair;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kGatherWaves + threadIdx.x / kWave;
+  s = static_cast<int64_t>(s_begin) + 2 * (wid / kWavesPerPair);
+  const int npc = 2 * (H / 8);
+  const int share = (npc / (2 * G) + kWavesPerPair - 1) / kWavesPerPair * (2 * G);
+  p_lo = static_cast<int>(wid % kWavesPerPair) * share;
+  p_hi = p_lo + share < npc ? p_lo + share : npc;
+  if (p_lo >= p_hi) return false;
   if (s >= s_end) return false;
   const int32_t a1 = aos[s];                             // aos holds s_end entries: both are
   const int32_t a2 = s + 1 < s_end ? aos[s + 1] : 0;     // issued together with R
@@ -32,28 +47,30 @@ __device__ __forceinline__ bool gather_slots(const int32_t* __restrict__ aos,
   return true;
 }
 
-__global__ __launch_bounds__(kPairsPerBlock * kWave)
+__global__ __launch_bounds__(kGatherWaves * kWave)
 void k_gather_bf16(void* const* __restrict__ parts, int32_t n_part, int32_t part_rows,
                    int32_t H, int32_t k, const int32_t* __restrict__ aos,
                    const int32_t* __restrict__ offsets, int32_t n_local, int32_t s_begin,
                    int32_t s_end, uint16_t* __restrict__ ring, int32_t ring_slots,
                    int32_t* status) {
   int64_t s, t1, t2;
-  if (!gather_slots(aos, offsets, n_local, k, s_begin, s_end, s, t1, t2)) return;
+  int p_lo, p_hi;
+  if (!gather_slots<false>(aos, offsets, n_local, k, H, s_begin, s_end, s, t1, t2, p_lo, p_hi)) return;
   gather_pair_bf16(parts, n_part, part_rows, H, t1, t2, ring, s % ring_slots, (s + 1) % ring_slots,
-                   ring_slots, status);
+                   ring_slots, p_lo, p_hi, status);
 }
 
-__global__ __launch_bounds__(kPairsPerBlock * kWave)
+__global__ __launch_bounds__(kGatherWaves * kWave)
 void k_gather_mxfp8(void* const* __restrict__ parts, int32_t n_part, int32_t part_rows,
                     int32_t H, int32_t k, const int32_t* __restrict__ aos,
                     const int32_t* __restrict__ offsets, int32_t n_local, int32_t s_begin,
                     int32_t s_end, uint8_t* __restrict__ ring, uint8_t* __restrict__ scales,
                     int32_t ring_slots, int32_t* status) {
   int64_t s, t1, t2;
-  if (!gather_slots(aos, offsets, n_local, k, s_begin, s_end, s, t1, t2)) return;
+  int p_lo, p_hi;
+  if (!gather_slots<true>(aos, offsets, n_local, k, H, s_begin, s_end, s, t1, t2, p_lo, p_hi)) return;
   gather_pair_mxfp8(parts, n_part, part_rows, H, t1, t2, ring, scales, s % ring_slots,
-                    (s + 1) % ring_slots, ring_slots, status);
+                    (s + 1) % ring_slots, ring_slots, p_lo, p_hi, status);
 }
 
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
@@ -92,14 +109,16 @@ hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_row
                          int32_t ring_slots, int32_t act_format, int32_t* status, hipStream_t s) {
   int64_t rows = static_cast<int64_t>(s_end) - s_begin;
   if (rows <= 0) return hipSuccess;
-  const int64_t pairs = (rows + 1) / 2;
-  dim3 grid(static_cast<unsigned>((pairs + kPairsPerBlock - 1) / kPairsPerBlock));
-  if (act_format == MOK_ACT_MXFP8_E4M3) {
-    hipLaunchKernelGGL(k_gather_mxfp8, grid, dim3(kPairsPerBlock * kWave), 0, s, part_ptr, n_part,
+  const bool mx = act_format == MOK_ACT_MXFP8_E4M3;
+  const int64_t waves = (rows + 1) / 2 * (mx ? GatherShape<true>::kWavesPerPair
+                                              : GatherShape<false>::kWavesPerPair);
+  dim3 grid(static_cast<unsigned>((waves + kGatherWaves - 1) / kGatherWaves));
+  if (mx) {
+    hipLaunchKernelGGL(k_gather_mxfp8, grid, dim3(kGatherWaves * kWave), 0, s, part_ptr, n_part,
                        part_rows, H, k, aos, offsets, n_local, s_begin, s_end,
                        static_cast<uint8_t*>(ring), ring_scales, ring_slots, status);
   } else {
-    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(kPairsPerBlock * kWave), 0, s, part_ptr, n_part,
+    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(kGatherWaves * kWave), 0, s, part_ptr, n_part,
                        part_rows, H, k, aos, offsets, n_local, s_begin, s_end,
                        static_cast<uint16_t*>(ring), ring_slots, status);
   }

@@ -35,9 +35,10 @@ __device__ __forceinline__ const uint4* token_row(void* const* parts, int32_t n_
 // of the pair, 16 source bytes (8 bf16): G consecutive lanes fill one 64-byte
 // destination block and the two rows alternate every G lanes, so an
 // instruction reads 512 contiguous source bytes of each row and writes
-// 64-byte blocks that pair up into whole lines.  kPairBatch pieces per lane
-// are loaded before any is stored.
-constexpr int kPairBatch = 16;
+// 64-byte blocks that pair up into whole lines.  A call moves the pieces
+// [p_lo, p_hi) of the pair (both multiples of 2 G, or p_hi = 2 H / 8);
+// kPairBatch pieces per lane (16 bf16, 8 MXFP8) are loaded before any is
+// stored.
 template <int G>
 __device__ __forceinline__ void pair_piece(int p, int& sel, int& v) {
   sel = (p / G) & 1;                      // which row of the pair
@@ -49,15 +50,16 @@ __device__ __forceinline__ void gather_pair_bf16(void* const* __restrict__ parts
                                                  int32_t part_rows, int32_t H, int64_t t1,
                                                  int64_t t2, uint16_t* __restrict__ ring,
                                                  int64_t rr1, int64_t rr2, int32_t rows,
-                                                 int32_t* status) {
+                                                 int p_lo, int p_hi, int32_t* status) {
+  constexpr int kPairBatch = 16;
   const int lane = lane_id();
   const uint4* src1 = token_row(parts, n_part, part_rows, t1, H);
   const uint4* src2 = t2 >= 0 ? token_row(parts, n_part, part_rows, t2, H) : src1;
   if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
   if (t2 < 0) rr2 = rr1;                  // the second half repeats row 1's copy
   uint8_t* ringb = reinterpret_cast<uint8_t*>(ring);
-  const int npc = 2 * (H / 8);            // pieces of the pair
-  for (int p0 = 0; p0 < npc; p0 += kWave * kPairBatch) {
+  const int npc = p_hi;
+  for (int p0 = p_lo; p0 < npc; p0 += kWave * kPairBatch) {
     uint4 buf[kPairBatch];
 #pragma unroll
     for (int u = 0; u < kPairBatch; ++u) {
@@ -84,14 +86,16 @@ __device__ __forceinline__ void gather_pair_mxfp8(void* const* __restrict__ part
                                                   int32_t part_rows, int32_t H, int64_t t1,
                                                   int64_t t2, uint8_t* __restrict__ ring,
                                                   uint8_t* __restrict__ scales, int64_t rr1,
-                                                  int64_t rr2, int32_t rows, int32_t* status) {
+                                                  int64_t rr2, int32_t rows, int p_lo, int p_hi,
+                                                  int32_t* status) {
+  constexpr int kPairBatch = 8;
   const int lane = lane_id();
   const uint4* src1 = token_row(parts, n_part, part_rows, t1, H);
   const uint4* src2 = t2 >= 0 ? token_row(parts, n_part, part_rows, t2, H) : src1;
   if (!src1 || !src2) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
   if (t2 < 0) rr2 = rr1;
-  const int npc = 2 * (H / 8);            // H % 64 == 0: groups of 8 lanes are whole
-  for (int p0 = 0; p0 < npc; p0 += kWave * kPairBatch) {
+  const int npc = p_hi;                   // H % 64 == 0: groups of 8 lanes are whole
+  for (int p0 = p_lo; p0 < npc; p0 += kWave * kPairBatch) {
     uint4 buf[kPairBatch];
 #pragma unroll
     for (int u = 0; u < kPairBatch; ++u) {

@@ -265,11 +265,12 @@ __device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c,
     const int64_t t2 = s + 1 < s1 ? pm.aos[s + 1] / a.k : -1;
     if (A_MX)
       gather_pair_mxfp8(a.x_parts, a.x_n_part, a.x_part_rows, a.H, t1, t2,
-                        static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, base + s + 1, a.S,
-                        a.status);
+                        static_cast<uint8_t*>(a.ring), a.ring_sc, base + s, base + s + 1, a.S, 0,
+                        a.H / 4, a.status);
     else
       gather_pair_bf16(a.x_parts, a.x_n_part, a.x_part_rows, a.H, t1, t2,
-                       static_cast<uint16_t*>(a.ring), base + s, base + s + 1, a.S, a.status);
+                       static_cast<uint16_t*>(a.ring), base + s, base + s + 1, a.S, 0, a.H / 4,
+                       a.status);
   }
 }
 
