@@ -37,9 +37,9 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 738607771),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 996603477),
-    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("b133fb5bc53ec356", 381907936),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 738612862),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 990450616),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 381115952),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
