@@ -77,8 +77,8 @@ typedef enum { MOK_ACT_BF16 = 0, MOK_ACT_MXFP8_E4M3 = 1 } mok_act_format;
  * quantised to OCP MX E4M3 with one E8M0 scale per 32 along the contraction
  * dimension (per row of W_gu and of W_d), by mok_pack_weights from the bf16
  * weights; needs act_format MOK_ACT_MXFP8_E4M3 and weights_packed = 1, and
- * runs both GEMMs on gfx950's block-scaled FP8 MFMA (stream mode and the
- * standalone calls; the persistent mode returns MOK_ERR_UNSUPPORTED). */
+ * runs both GEMMs on gfx950's block-scaled FP8 MFMA (both modes of the fused
+ * calls and the standalone GEMM calls). */
 typedef enum { MOK_W_BF16 = 0, MOK_W_MXFP8_E4M3 = 1 } mok_weight_format;
 
 typedef enum {

@@ -7,9 +7,12 @@ path carries the same format into the weights.  Parity:
     weight row (codes and scales, read back through the packed tile order);
   - the expert outputs y and merged rows: within 6e-2 * RMS of the oracle run
     with the same quantised weights (gpu_harness.assert_close_rms), for
-    standalone calls (whole tiles and the K split) and the stream-mode fused
-    call over several windows of a ring;
-  - the persistent mode and unpacked MXFP8 weights are refused.
+    standalone calls (whole tiles and the K split), the stream-mode fused
+    call over several windows of a ring, and the persistent mode;
+  - the persistent mode is bit-identical to the stream mode with whole tiles
+    (no_split_k = 1: the same tile code);
+  - unpacked MXFP8 weights and bf16 activations with MXFP8 weights are
+    refused.
 """
 import numpy as np
 import pytest
@@ -157,12 +160,26 @@ def test_mxfp8_weight_forward_stream(M):
     assert_close_rms(got[r["written"]], r["out"][r["written"]], 6e-2, "out")
 
 
+@pytest.mark.parametrize("M", [64, 256, 1000])
+def test_mxfp8_weight_forward_persistent(M):
+    import token_dispatch_grouped_top_amd as mok
+    wl = _case(seed=75)
+    dw = DeviceWorkload(wl, n_out=2)
+    ws, _ = dw.forward(out=dw.outs[0], minibatch=M, mode=1, wait_timeout_us=500_000)
+    assert mok.mok_device_status(ws) == 0
+    ws2, _ = dw.forward(out=dw.outs[1], minibatch=M, no_split_k=1)
+    assert mok.mok_device_status(ws2) == 0
+    got, ref_stream = dw.out_rows(dw.outs[0]), dw.out_rows(dw.outs[1])
+    assert np.array_equal(got, ref_stream)
+    r = oracle.forward(wl)
+    assert np.all(got[~r["written"]] == 0x7FC1)
+    assert_close_rms(got[r["written"]], r["out"][r["written"]], 6e-2, "out")
+
+
 def test_mxfp8_weight_refusals():
     import token_dispatch_grouped_top_amd as mok
     wl = _case(seed=74)
     dw = DeviceWorkload(wl)
-    d = dw.desc(mode=1)
-    assert mok.mok_forward_workspace_size(d, wl.T, 1) == 0          # persistent: unsupported
     d = dw.desc()
     d.weights_packed = 0                                             # MXFP8 weights are packed
     ring = torch.zeros((64, wl.H), dtype=torch.uint8, device="cuda")

@@ -118,8 +118,6 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.S = d->ring_slots > 0 ? d->ring_slots : 2 * p.M;
   if (p.S < p.M) return false;
   if (d->mode == MOK_MODE_PERSISTENT && p.S < 2 * static_cast<int64_t>(p.M)) return false;
-  // the persistent kernel runs the bf16-weight tiles only
-  if (d->mode == MOK_MODE_PERSISTENT && d->weight_format != MOK_W_BF16) return false;
   p.nwin = static_cast<int32_t>((cap + p.M - 1) / p.M);
   p.act_rows = p.S;
   if (!gemm_operands_fit(d, p.S, p.act_rows)) return false;
@@ -444,7 +442,7 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
     pa.M = p.M; pa.S = p.S; pa.nwin = p.nwin; pa.cap = p.cap;
     pa.x = *x; pa.w_gu = static_cast<const uint16_t*>(w_gate_up);
     pa.w_d = static_cast<const uint16_t*>(w_down);
-    pa.w_packed = d.weights_packed;
+    pa.w_packed = d.weights_packed; pa.weight_format = d.weight_format;
     pa.ring = ring; pa.ring_sc = ring_sc; pa.act = act; pa.act_sc = act_sc; pa.act_rows = p.act_rows;
     pa.status = status; pa.pers_ws = at<void>(ws, p.off_pers);
     pa.n_move = d.n_move_cus; pa.n_cus = device_cus(); pa.timeout_us = d.wait_timeout_us;

@@ -234,5 +234,15 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   tile_finish<EPI>(p, job, acc, lds);
 }
 
+// A whole tile (all k-steps).
+template <int EPI>
+__device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, int e, int row0, int nrows,
+                                              int ntile, uint8_t* __restrict__ lds) {
+  TileJob j;
+  j.e = e; j.row0 = row0; j.nrows = nrows; j.ntile = ntile;
+  j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  gemm_tile_mx8<EPI>(p, j, lds);
+}
+
 }  // namespace gemm
 }  // namespace mok

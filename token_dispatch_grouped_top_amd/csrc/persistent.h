@@ -26,6 +26,7 @@ struct PersistentArgs {
   const uint16_t* w_gu;
   const uint16_t* w_d;
   int32_t w_packed;         // weights in the packed tile order
+  int32_t weight_format;    // mok_weight_format (MXFP8 weights: packed, MXFP8 activations)
   void* ring; uint8_t* ring_sc;
   void* act; uint8_t* act_sc; int32_t act_rows;
   int32_t* status;

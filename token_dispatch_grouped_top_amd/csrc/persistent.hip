@@ -42,6 +42,7 @@
 // one acquire fence.  A worker remembers the last window whose dependencies it
 // has acquired, so consecutive tiles of one window wait (and invalidate) once.
 #include "gemm_tile.h"
+#include "gemm_tile_mx8.h"
 #include "movers_dev.h"
 #include "persistent.h"
 
@@ -322,8 +323,12 @@ __device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t
   }
 }
 
+// Operand formats of a persistent launch: bf16 activations and weights;
+// MXFP8 activations with bf16 weights; MXFP8 activations and weights.
+enum PFormat { kPBf16 = 0, kPMxAct = 1, kPMx8 = 2 };
+
 // Workers: GEMM tiles from the XCD's queue; false when the kernel aborts.
-template <bool A_MX>
+template <int F>
 __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, int32_t* sh,
                                              uint8_t* lds) {
   const int x = blockIdx.x % kXcds;
@@ -377,7 +382,10 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
       g.N = a.I; g.I = a.I;
       g.C = a.act; g.C_scales = a.act_sc; g.c_rows = a.act_rows; g.c_row_base = rb;
       g.n_tiles = n1; g.w_packed = a.w_packed;
-      gemm_tile<A_MX, A_MX ? EPI_SWIGLU_MX : EPI_SWIGLU_BF16>(g, e, row0, nrows, ntile, lds);
+      if constexpr (F == kPMx8)
+        gemm_tile_mx8<EPI_SWIGLU_MX>(g, e, row0, nrows, ntile, lds);
+      else
+        gemm_tile<F == kPMxAct, F == kPMxAct ? EPI_SWIGLU_MX : EPI_SWIGLU_BF16>(g, e, row0, nrows, ntile, lds);
       signal_add(&c.gu_done[w]);
     } else {
       g.A = a.act; g.A_scales = a.act_sc; g.a_rows = a.act_rows; g.a_row_base = rb;
@@ -385,16 +393,21 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
       g.N = a.H; g.I = 0;
       g.C = pm.y; g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
       g.n_tiles = n2; g.w_packed = a.w_packed;
-      gemm_tile<A_MX, EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
+      if constexpr (F == kPMx8)
+        gemm_tile_mx8<EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
+      else
+        gemm_tile<F == kPMxAct, EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
       signal_add(&c.dn_done[w]);
     }
   }
 }
 
-template <bool A_MX>
+template <int F>
 __global__ __launch_bounds__(256)
 void k_persist(const PKArgs a) {
-  constexpr int kLds = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
+  constexpr bool A_MX = F != kPBf16;
+  constexpr int kLds0 = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
+  constexpr int kLds = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   // The broadcast words share the first 16 bytes of the GEMM's LDS: every
   // use is fenced by workgroup barriers from the tile that overwrites them
@@ -410,7 +423,7 @@ void k_persist(const PKArgs a) {
   }
   if (static_cast<int>(blockIdx.x) < a.n_move) {
     mover<A_MX>(a, c, sh);
-  } else if (worker_tiles<A_MX>(a, c, sh, lds) && *c.n_items > 0) {
+  } else if (worker_tiles<F>(a, c, sh, lds) && *c.n_items > 0) {
     // GEMMs done: help the movers with the last macrobatch's merge
     merge_macro<true>(a, c, sh, a.n_macro - 1, gw, ngw);
   }
@@ -433,8 +446,9 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
                                         : 8;
   if (n_move < 1 || n_move > a.n_cus - kXcds) return MOK_ERR_INVALID_ARG;
   const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
-  const void* fn = mx ? reinterpret_cast<const void*>(&k_persist<true>)
-                      : reinterpret_cast<const void*>(&k_persist<false>);
+  const void* fn = !mx ? reinterpret_cast<const void*>(&k_persist<kPBf16>)
+                   : a.weight_format == MOK_W_MXFP8_E4M3 ? reinterpret_cast<const void*>(&k_persist<kPMx8>)
+                                                         : reinterpret_cast<const void*>(&k_persist<kPMxAct>);
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
     return MOK_ERR_HIP;
