@@ -182,6 +182,36 @@ def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
     return res
 
 
+def time_router_gemm(mok, wl, reps: int = 20):
+    """mok_route_topk_gemm on this workload's routed tokens' shape (T_route x H
+    against E router rows, seeded N(0, 1) tokens and N(0, 1/H) router
+    weights): not part of the timed step, whose routing comes from the
+    workload's logits."""
+    import numpy as np
+    import torch
+    import workloads as W
+    T, E, H, k = int(wl.logits.shape[0]), wl.E, wl.H, wl.k
+    x, w = W.router_inputs(77, T, H, E)
+    xd, wd = torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(w.view(np.int16)).cuda()
+    ws = torch.empty(max(mok.mok_route_gemm_workspace_size(T, E, H), 1), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        mok.mok_route_topk_gemm(xd, wd, T, H, E, k, ws, idx, gate)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mok.mok_route_topk_gemm(xd, wd, T, H, E, k, ws, idx, gate)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = 2.0 * T * E * H
+    return {"T": T, "E": E, "H": H, "k": k, "ms": round(ms, 5),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "input_GBps": round((T + E) * H * 2 / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(wl, sample_rows: int):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
@@ -372,6 +402,10 @@ def main():
                     fused[key] = round(e0.elapsed_time(e1) / 10, 4)
                     log(f"[bench] fused mok_moe_forward {key}: {fused[key]:.4f} ms")
 
+    router = time_router_gemm(mok, wl)
+    log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
+        f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
+
     streaming = None
     if args.streaming and wl.name.startswith("kimi_share"):
         streaming = time_streaming(mok, DeviceWorkload)
@@ -416,6 +450,7 @@ def main():
         "schedule_share": round(per["schedule"] / wall_ms, 4),
         "fused_forward_ms": fused or None,
         "streaming_ms_per_macrobatch": streaming,
+        "router_gemm": router,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

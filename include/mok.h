@@ -135,6 +135,21 @@ typedef struct {
 mok_status mok_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                           int32_t* topk_idx, float* topk_gate, hipStream_t stream);
 
+/* Router GEMM fused with the route (article, routing paragraph: the router
+ * scores every token against every expert, then picks).  logits[t][e] =
+ * sum_h x[t][h] * w_router[e][h] over bf16 values with fp32 sums (products
+ * exact, the sums' order the kernel's), then the picks and gates of
+ * mok_route_topk.  The logits are never stored whole: per-split partial sums
+ * go to ws and are added in split order, so results are deterministic.
+ * x: bf16 [T][H]; w_router: bf16 [E][H] (nn.Linear layout); H a multiple of
+ * 16; 1 <= k <= min(E, 32), E <= 4096.  ws: device scratch of
+ * mok_route_gemm_workspace_size(T, E, H) bytes (MOK_ERR_WORKSPACE if
+ * smaller); its contents on entry do not matter.  T = 0 does nothing. */
+size_t mok_route_gemm_workspace_size(int32_t T, int32_t E, int32_t H);
+mok_status mok_route_topk_gemm(const void* x, const void* w_router, int32_t T, int32_t H,
+                               int32_t E, int32_t k, void* ws, size_t ws_bytes,
+                               int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
 /* Bytes of scratch mok_build_schedule needs. */
 size_t mok_schedule_workspace_size(int64_t T, int32_t k, int32_t n_local);
 

@@ -135,6 +135,18 @@ def route_topk(logits: np.ndarray, k: int):
     return idx, gate
 
 
+def router_logits(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """Router scores (tahou.com MoK article, routing paragraph: every token is
+    scored against every expert before the picks): logits[t][e] =
+    sum_h x[t][h] * w_router[e][h] over the bf16 values of x (bf16 [T][H]) and
+    w_router (bf16 [E][H], nn.Linear layout), in fp64 (a library matmul as the
+    step).  Each product of two bf16 values is exact in fp64; the fp64 sum is
+    the reference the fp32 sums of the device are held to."""
+    xv = bf16_value(x_bits).astype(np.float64)
+    wv = bf16_value(w_router_bits).astype(np.float64)
+    return xv @ wv.T
+
+
 def build_schedule(topk_idx: np.ndarray, expert_base: int, n_local: int):
     idx = _c(topk_idx, np.int32)
     T, k = idx.shape

@@ -58,6 +58,14 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 0, 4, 1, None, 4, 1, None, None) == E
     assert L.mok_combine(1, 4, 1, 1, 17, 2, 64, C.byref(tok), None, None) == E  # T > rows
     assert L.mok_combine(1, 4, 1, 1, 16, 2, 60, C.byref(tok), None, None) == E  # H % 8
+    # router GEMM + route: H % 16, k > E, null inputs, workspace below the query
+    assert L.mok_route_topk_gemm(1, 1, 4, 60, 8, 2, 1, 1 << 20, 1, 1, None) == E
+    assert L.mok_route_topk_gemm(1, 1, 4, 64, 8, 9, 1, 1 << 20, 1, 1, None) == E
+    assert L.mok_route_topk_gemm(None, 1, 4, 64, 8, 2, 1, 1 << 20, 1, 1, None) == E
+    need = L.mok_route_gemm_workspace_size(4, 8, 64)
+    assert need >= 4 * 8 * 4
+    assert L.mok_route_topk_gemm(1, 1, 4, 64, 8, 2, 1, need - 1, 1, 1, None) == mok.MOK_ERR_WORKSPACE
+    assert L.mok_route_topk_gemm(None, None, 0, 64, 8, 2, None, 0, None, None, None) == mok.MOK_OK
 
 
 def _desc(**kw):

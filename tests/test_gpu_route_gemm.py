@@ -1,0 +1,115 @@
+"""GPU tests of the router GEMM fused with the route (tahou.com MoK article,
+routing paragraph: every token is scored against every expert, then the
+router picks; mok_route_topk_gemm).
+
+The device sums the bf16 products in fp32 in its own order; the oracle sums
+them in fp64 (oracle.router_logits) and picks with oracle.route_topk.  Bars:
+  - integer-valued inputs: every fp32 sum is exact, so picks are bit-exact
+    against the oracle, ties (frequent here) included, and gates within the
+    route's own bar;
+  - Gaussian inputs: where the oracle's logits leave a margin larger than the
+    fp32 error bound around every decision (the k-th against the (k+1)-th
+    logit, and consecutive picks), the picks equal the oracle's; where only
+    the k-th against the (k+1)-th is clear, the picked set does; elsewhere
+    they are a valid top-k within that bound.  The bound for token t and
+    expert e is n * 2^-24 * sum_h |x_th w_eh| with n = H / 16 + splits + 16
+    fp32 additions on any path; the set must be clear for at least 90 % of
+    the tokens (so the test has teeth).  Gates are held to the softmax of the oracle's logits over the
+    device's picks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_harness import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _run(x, w, k):
+    import token_dispatch_grouped_top_amd as mok
+    T, H = x.shape
+    E = w.shape[0]
+    ws = torch.empty(max(mok.mok_route_gemm_workspace_size(T, E, H), 1), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.full((max(T, 1), k), -1, dtype=torch.int32, device="cuda")
+    gate = torch.zeros((max(T, 1), k), dtype=torch.float32, device="cuda")
+    mok.mok_route_topk_gemm(to_dev(x), to_dev(w), T, H, E, k, ws, idx, gate)
+    torch.cuda.synchronize()
+    return to_host(idx)[:T], to_host(gate)[:T]
+
+
+@pytest.mark.parametrize("T,E,H,k", [(100, 40, 48, 3), (1000, 384, 7168, 8), (257, 8, 4096, 2),
+                                     (33, 130, 272, 5)])
+def test_route_gemm_integer_inputs_bit_exact(T, E, H, k):
+    x = W.small_int_bf16(31 + T, (T, H), -2, 2)
+    w = W.small_int_bf16(37 + E, (E, H), -2, 2)
+    idx, gate = _run(x, w, k)
+    logits = oracle.router_logits(x, w)
+    assert np.abs(logits).max() < 2 ** 24                   # exact in fp32 too
+    idx_o, gate_o = oracle.route_topk(logits.astype(np.float32), k)
+    assert np.array_equal(idx, idx_o)
+    assert np.all(np.abs(gate.astype(np.float64) - gate_o) <= 2.0 ** -19 * gate_o + 1e-30)
+
+
+@pytest.mark.parametrize("T,E,H,k", [(1024, 384, 7168, 8), (4096, 8, 4096, 2), (256, 8, 256, 2)])
+def test_route_gemm_gaussian(T, E, H, k):
+    import token_dispatch_grouped_top_amd as mok
+    x, w = W.router_inputs(41 + T + E, T, H, E)
+    idx, gate = _run(x, w, k)
+    L = oracle.router_logits(x, w)
+    splits = mok.mok_route_gemm_workspace_size(T, E, H) // (4 * T * E)
+    n_add = H // 16 + splits + 16
+    absdot = np.abs(oracle.bf16_value(x).astype(np.float64)) @ \
+        np.abs(oracle.bf16_value(w).astype(np.float64)).T
+    delta = n_add * 2.0 ** -24 * absdot
+    decided = 0
+    for t in range(T):
+        p = idx[t]
+        assert len(set(p.tolist())) == k and p.min() >= 0 and p.max() < E
+        lt, dt = L[t], delta[t]
+        rest = np.setdiff1d(np.arange(E), p)
+        # valid: every pick beats every non-pick, and picks are in order, within the bound
+        if rest.size:
+            assert (lt[p] + dt[p]).min() >= (lt[rest] - dt[rest]).max(), t
+        assert np.all(lt[p[:-1]] + dt[p[:-1]] >= lt[p[1:]] - dt[p[1:]]), t
+        # decided tokens: the oracle's picks, exactly
+        po, _ = oracle.route_topk(lt[None, :].astype(np.float32), k)
+        po = po[0]
+        so = np.sort(lt)[::-1]
+        order = np.argsort(-lt, kind="stable")
+        margins = so[:min(k + 1, E) - 1] - so[1:min(k + 1, E)]
+        need = dt[order[:min(k + 1, E) - 1]] + dt[order[1:min(k + 1, E)]]
+        if np.all(margins > need):                      # every decision clear: same picks
+            assert np.array_equal(p, po), t
+        if k < E and margins[k - 1] > need[k - 1]:      # the set is clear: same set
+            decided += 1
+            assert set(p.tolist()) == set(po.tolist()), t
+        g_ref = np.exp(lt[p] - lt[p[0]])
+        g_ref /= g_ref.sum()
+        tol = 2.0 * dt[p].max() * 2 + 1e-6
+        assert np.all(np.abs(gate[t].astype(np.float64) - g_ref) <= tol * g_ref + 1e-7), t
+    assert decided >= 0.9 * T or E <= k + 1 and decided >= 0.8 * T, (decided, T)
+
+
+def test_route_gemm_empty_and_errors():
+    import token_dispatch_grouped_top_amd as mok
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    gate = torch.zeros((1, 2), dtype=torch.float32, device="cuda")
+    x = torch.zeros((4, 64), dtype=torch.int16, device="cuda")
+    w = torch.zeros((8, 64), dtype=torch.int16, device="cuda")
+    mok.mok_route_topk_gemm(x, w, 0, 64, 8, 2, ws, idx, gate)      # T = 0: nothing
+    with pytest.raises(mok.MokError) as e:
+        mok.mok_route_topk_gemm(x, w, 4, 64, 8, 2, ws, idx, gate)  # workspace too small
+    assert e.value.status == mok.MOK_ERR_WORKSPACE
+    with pytest.raises(mok.MokError):
+        mok.mok_route_topk_gemm(x, w, 4, 60, 8, 2, ws, idx, gate)  # H not a multiple of 16

@@ -68,3 +68,37 @@ def test_gates_are_renormalised_softmax(orc, E, k):
 def test_rejects_k_above_e(orc):
     with pytest.raises(ValueError):
         orc.route_topk(np.zeros((2, 3), np.float32), 4)
+
+
+def test_router_logits_against_exact_sums(orc):
+    """router_logits (x . w_router^T over bf16 values) against exactly rounded
+    sums of the products, term by term in pure Python, on a shape with
+    T != E != H so a transposed or swapped operand cannot pass."""
+    import math
+    rng = np.random.default_rng(11)
+    T, E, H = 3, 5, 7
+    x = orc.bf16_round(rng.standard_normal((T, H))).reshape(T, H)
+    w = orc.bf16_round(rng.standard_normal((E, H)) * 0.3).reshape(E, H)
+    got = orc.router_logits(x, w)
+    assert got.shape == (T, E)
+    xv, wv = orc.bf16_value(x).astype(float), orc.bf16_value(w).astype(float)
+    for t in range(T):
+        for e in range(E):
+            exact = math.fsum(float(xv[t, h]) * float(wv[e, h]) for h in range(H))
+            assert abs(got[t, e] - exact) <= 1e-15 * (1.0 + abs(exact)), (t, e)
+
+
+def test_router_logits_small_integers_exact(orc):
+    """Integer-valued bf16 inputs give integer logits, exactly: the case the
+    device's fp32 sums also get exactly (used by the GPU tie test)."""
+    rng = np.random.default_rng(12)
+    x = orc.bf16_round(rng.integers(-2, 3, (4, 64)).astype(np.float64)).reshape(4, 64)
+    w = orc.bf16_round(rng.integers(-2, 3, (6, 64)).astype(np.float64)).reshape(6, 64)
+    got = orc.router_logits(x, w)
+    ref = np.zeros((4, 6), np.int64)
+    xi = orc.bf16_value(x).astype(np.int64)
+    wi = orc.bf16_value(w).astype(np.int64)
+    for t in range(4):
+        for e in range(6):
+            ref[t, e] = sum(int(xi[t, h]) * int(wi[e, h]) for h in range(64))
+    assert np.array_equal(got, ref.astype(np.float64))

@@ -57,6 +57,8 @@ _P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
 _DESC, _TOK = C.POINTER(mok_layer_desc), C.POINTER(mok_tokens)
 _SIGS = {
     "mok_route_topk": (C.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "mok_route_gemm_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "mok_route_topk_gemm": (C.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mok_schedule_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "mok_build_schedule": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "mok_choose_minibatch": (_I32, [_I32, _I32, _I32, _I32, _I64]),
@@ -148,6 +150,17 @@ def mok_status_str(status: int) -> str:
 def mok_route_topk(logits, T: int, E: int, k: int, topk_idx, topk_gate, stream=None) -> None:
     _check(_lib.mok_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_gate),
                                _stream(stream)), "mok_route_topk")
+
+
+def mok_route_gemm_workspace_size(T: int, E: int, H: int) -> int:
+    return int(_lib.mok_route_gemm_workspace_size(T, E, H))
+
+
+def mok_route_topk_gemm(x, w_router, T: int, H: int, E: int, k: int, ws, topk_idx, topk_gate,
+                        ws_bytes: Optional[int] = None, stream=None) -> None:
+    _check(_lib.mok_route_topk_gemm(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(ws),
+                                    _ws_bytes(ws, ws_bytes), _ptr(topk_idx), _ptr(topk_gate),
+                                    _stream(stream)), "mok_route_topk_gemm")
 
 
 def mok_schedule_workspace_size(T: int, k: int, n_local: int) -> int:

@@ -188,6 +188,24 @@ mok_status mok_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
   return hip_status(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, stream));
 }
 
+size_t mok_route_gemm_workspace_size(int32_t T, int32_t E, int32_t H) {
+  if (T < 0 || E < 1 || H < 16) return 0;
+  return static_cast<size_t>(route_gemm_splits(T, E, H)) * static_cast<size_t>(T) * E * sizeof(float);
+}
+
+mok_status mok_route_topk_gemm(const void* x, const void* w_router, int32_t T, int32_t H, int32_t E,
+                               int32_t k, void* ws, size_t ws_bytes, int32_t* topk_idx,
+                               float* topk_gate, hipStream_t stream) {
+  if (T < 0 || H < 16 || H % 16 != 0 || E < 1 || E > 4096 || k < 1 || k > 32 || k > E)
+    return MOK_ERR_INVALID_ARG;
+  if (T == 0) return MOK_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate || !ws) return MOK_ERR_INVALID_ARG;
+  if (ws_bytes < mok_route_gemm_workspace_size(T, E, H)) return MOK_ERR_WORKSPACE;
+  return hip_status(launch_route_topk_gemm(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(w_router), T, H, E, k,
+                                           static_cast<float*>(ws), topk_idx, topk_gate, stream));
+}
+
 size_t mok_schedule_workspace_size(int64_t T, int32_t k, int32_t n_local) {
   if (T < 0 || k < 1 || n_local < 1) return 0;
   return sched_ws_bytes(T * k, n_local);

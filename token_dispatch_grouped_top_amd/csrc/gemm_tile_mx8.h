@@ -132,25 +132,33 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 
   // Fragments of one k-step into register set `set`: rows of the wave's token
   // and weight blocks, chunks khalf and 2 + khalf, and the block scale khalf.
+  // Row 128 w + 32 i + frag_row of a block has the swizzle key of frag_row
+  // (the key is bits 2..3 of the row), so a fragment sits at a wave-uniform
+  // base + 2048 i + a per-lane offset: one address per chunk serves all four
+  // row groups, i goes into the instruction's offset field, and the loop
+  // needs no address arithmetic per read.
   i32x8_t tf[2][4], wf[2][4];
   int ts[2][4], wsc[2][4];
-  auto frag = [&](const uint8_t* base, int r) -> i32x8_t {
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + G::off(r, khalf));  // vector-typed:
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + G::off(r, 2 + khalf));  // see lds_read16
+  const int key = chunk_key<G::CPR>(frag_row);
+  const int lane_lo = frag_row * G::ROWB + ((khalf ^ key) << 4);
+  const int lane_hi = frag_row * G::ROWB + (((2 + khalf) ^ key) << 4);
+  const int lane_sc = 4 * frag_row + khalf;
+  auto frag = [&](const uint8_t* lo_p, const uint8_t* hi_p, int i) -> i32x8_t {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(lo_p + 32 * G::ROWB * i);  // vector-typed:
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(hi_p + 32 * G::ROWB * i);  // see lds_read16
     return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 #define MX8_FRAGS(set, buf)                                                                  \
   do {                                                                                       \
-    const uint8_t* At_ = tileA(buf);                                                         \
-    const uint8_t* Bt_ = tileB(buf);                                                         \
-    const uint8_t* Sa_ = tileSA(buf);                                                        \
-    const uint8_t* Sb_ = tileSB(buf);                                                        \
+    const uint8_t* At_ = tileA(buf) + 128 * G::ROWB * wm;                                    \
+    const uint8_t* Bt_ = tileB(buf) + 128 * G::ROWB * wn;                                    \
+    const uint8_t* Sa_ = tileSA(buf) + 512 * wm + lane_sc;                                   \
+    const uint8_t* Sb_ = tileSB(buf) + 512 * wn + lane_sc;                                   \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                       \
-      const int rt_ = 128 * wm + 32 * i_ + frag_row, rw_ = 128 * wn + 32 * i_ + frag_row;    \
-      wf[set][i_] = frag(Bt_, rw_);                                                          \
-      tf[set][i_] = frag(At_, rt_);                                                          \
-      wsc[set][i_] = Sb_[4 * rw_ + khalf];                                                   \
-      ts[set][i_] = Sa_[4 * rt_ + khalf];                                                    \
+      wf[set][i_] = frag(Bt_ + lane_lo, Bt_ + lane_hi, i_);                                  \
+      tf[set][i_] = frag(At_ + lane_lo, At_ + lane_hi, i_);                                  \
+      wsc[set][i_] = Sb_[128 * i_];                                                          \
+      ts[set][i_] = Sa_[128 * i_];                                                           \
     }                                                                                        \
   } while (0)
   // The MFMAs of token row groups mi0, mi0 + 1 (fed weights, tokens, as in

@@ -112,6 +112,10 @@ __device__ __forceinline__ void set_status(int32_t* st, int32_t code) {
 
 // --------------------------------------------------------- launchers
 // All launchers return hipSuccess or the launch error.
+int32_t route_gemm_splits(int32_t T, int32_t E, int32_t H);
+hipError_t launch_route_topk_gemm(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
+                                  int32_t E, int32_t k, float* partial, int32_t* idx, float* gate,
+                                  hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                              int32_t* idx, float* gate, hipStream_t s);
 

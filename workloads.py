@@ -71,6 +71,21 @@ def normal_bf16(seed_seq: np.random.SeedSequence, n: int, std: float) -> np.ndar
     return out
 
 
+def small_int_bf16(seed: int, shape, lo: int, hi: int) -> np.ndarray:
+    """Integers drawn uniformly from [lo, hi] as bf16 bits (exact for |v| <= 256)."""
+    g = np.random.default_rng(seed)
+    return _bf16_bits(g.integers(lo, hi + 1, size=shape).astype(np.float32))
+
+
+def router_inputs(seed: int, T: int, H: int, E: int):
+    """Tokens x ~ N(0, 1) bf16 [T][H] and router weights W_r ~ N(0, 1/H) bf16
+    [E][H] (nn.Linear layout) for the router GEMM."""
+    ss = np.random.SeedSequence(seed).spawn(2)
+    x = normal_bf16(ss[0], T * H, 1.0).reshape(T, H)
+    w = normal_bf16(ss[1], E * H, float(1.0 / np.sqrt(H))).reshape(E, H)
+    return x, w
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """bf16 bits -> fp32 values (exact widening)."""
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
