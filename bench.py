@@ -278,6 +278,8 @@ def main():
                          "MODE 0 stream / 1 persistent")
     ap.add_argument("--streaming", action="store_true",
                     help="also time 8 Kimi-shaped macrobatches through one ring, per mode")
+    ap.add_argument("--tune", action="store_true",
+                    help="also run mok_tune_forward over minibatches (and mover counts) per mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 3 times (counter scale)")
     args = ap.parse_args()
@@ -402,6 +404,24 @@ def main():
                     fused[key] = round(e0.elapsed_time(e1) / 10, 4)
                     log(f"[bench] fused mok_moe_forward {key}: {fused[key]:.4f} ms")
 
+    tuned = None
+    if args.tune and not wl.routing_from_logits:
+        tuned = {}
+        for mode, moves in ((mok.MOK_MODE_STREAM, []), (mok.MOK_MODE_PERSISTENT, [32, 48])):
+            Ms = [m for m in wl.minibatches if m >= 2048] + [0]
+            d = dw.desc(max_rows=max_rows, mode=mode, weights_packed=1)
+            need = max(mok.mok_forward_workspace_size(dw.desc(max_rows=max_rows, mode=mode, minibatch=M,
+                                                              weights_packed=1), wl.T, 1) for M in Ms)
+            ws_t = torch.empty(need, dtype=torch.uint8, device="cuda")
+            w_gu, w_d = dw.weights(d)
+            best, ms = mok.mok_tune_forward(d, Ms, moves, 5, [dw.topk_idx], [dw.topk_gate], wl.T,
+                                            dw.x, w_gu, w_d, [dw.outs[0]], ws_t)
+            key = "stream" if mode == mok.MOK_MODE_STREAM else "persistent"
+            tuned[key] = {"minibatch": mok.mok_forward_minibatch(best, wl.T),
+                          "n_move_cus": best.n_move_cus if moves else None, "ms": round(ms, 4)}
+            log(f"[bench] tuner ({key}): {tuned[key]}")
+            del ws_t
+
     router = time_router_gemm(mok, wl)
     log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
         f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
@@ -451,6 +471,7 @@ def main():
         "fused_forward_ms": fused or None,
         "streaming_ms_per_macrobatch": streaming,
         "router_gemm": router,
+        "tuned_forward": tuned,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -319,6 +319,26 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
                                    const void* w_down, const mok_tokens* out,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Tuner of the fused call (article, minibatch paragraph: the minibatch, and
+ * the share of CUs that move data, have to be retuned for every hidden size,
+ * top-k and expert size).  For every candidate pair (minibatch[i],
+ * n_move[j]) -- the other fields from desc; n_move applies in
+ * MOK_MODE_PERSISTENT only, and n_n_move = 0 keeps desc->n_move_cus -- runs
+ * mok_moe_forward_batches on the caller's inputs once untimed and `reps`
+ * times between two HIP events, and writes the fastest candidate's
+ * descriptor to *best and its mean time per call (ms) to *best_ms.
+ * Candidates whose workspace exceeds ws_bytes, or whose calls fail or end
+ * with a device status other than MOK_OK, are skipped; MOK_ERR_UNSUPPORTED
+ * if none is left.  Synchronises `stream` (host-side timing); out is
+ * written by every run.  Meant for set-up, not for the serving loop. */
+mok_status mok_tune_forward(const mok_layer_desc* desc, const int32_t* minibatch,
+                            int32_t n_minibatch, const int32_t* n_move, int32_t n_n_move,
+                            int32_t reps, int32_t n_macro, const int32_t* const* topk_idx,
+                            const float* const* topk_gate, int32_t T, const mok_tokens* x,
+                            const void* w_gate_up, const void* w_down, const mok_tokens* out,
+                            void* ws, size_t ws_bytes, mok_layer_desc* best, float* best_ms,
+                            hipStream_t stream);
+
 /* Synchronises `stream`, then copies the workspace status word to
  * *status_host (MOK_OK, MOK_ERR_CAPACITY or MOK_ERR_DEVICE). */
 mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream);

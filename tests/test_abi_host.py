@@ -58,6 +58,17 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 0, 4, 1, None, 4, 1, None, None) == E
     assert L.mok_combine(1, 4, 1, 1, 17, 2, 64, C.byref(tok), None, None) == E  # T > rows
     assert L.mok_combine(1, 4, 1, 1, 16, 2, 60, C.byref(tok), None, None) == E  # H % 8
+    # tuner: no candidates, reps < 1, null result pointers
+    d = _desc()
+    one = (C.c_int32 * 1)(64)
+    f = C.c_float(0.0)
+    best = mok.mok_layer_desc()
+    assert L.mok_tune_forward(C.byref(d), one, 0, None, 0, 1, 1, 1, 1, 4, C.byref(tok), 1, 1,
+                              C.byref(tok), 1, 1 << 20, C.byref(best), C.byref(f), None) == E
+    assert L.mok_tune_forward(C.byref(d), one, 1, None, 0, 0, 1, 1, 1, 4, C.byref(tok), 1, 1,
+                              C.byref(tok), 1, 1 << 20, C.byref(best), C.byref(f), None) == E
+    assert L.mok_tune_forward(C.byref(d), one, 1, None, 0, 1, 1, 1, 1, 4, C.byref(tok), 1, 1,
+                              C.byref(tok), 1, 1 << 20, None, C.byref(f), None) == E
     # router GEMM + route: H % 16, k > E, null inputs, workspace below the query
     assert L.mok_route_topk_gemm(1, 1, 4, 60, 8, 2, 1, 1 << 20, 1, 1, None) == E
     assert L.mok_route_topk_gemm(1, 1, 4, 64, 8, 9, 1, 1 << 20, 1, 1, None) == E

@@ -81,6 +81,8 @@ _SIGS = {
     "mok_moe_forward": (C.c_int, [_DESC, _P, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
     "mok_moe_forward_batches": (C.c_int, [_DESC, _I32, _P, _P, _I32, _TOK, _P, _P, _TOK, _P,
                                           _SZ, _P]),
+    "mok_tune_forward": (C.c_int, [_DESC, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _I32, _TOK,
+                                   _P, _P, _TOK, _P, _SZ, _DESC, C.POINTER(C.c_float), _P]),
     "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "mok_forward_minibatch": (_I32, [_DESC, _I32]),
     "mok_status_str": (C.c_char_p, [C.c_int]),
@@ -294,6 +296,29 @@ def mok_moe_forward_batches(desc: mok_layer_desc, n_macro: int, topk_idx: Sequen
                                         C.cast(gate_arr, C.c_void_p), T, C.byref(x.c),
                                         _ptr(w_gate_up), _ptr(w_down), out_arr, _ptr(ws),
                                         ws_bytes, _stream(stream)), "mok_moe_forward_batches")
+
+
+def mok_tune_forward(desc: mok_layer_desc, minibatches: Sequence[int], n_moves: Sequence[int],
+                     reps: int, topk_idx: Sequence, topk_gate: Sequence, T: int, x: Tokens,
+                     w_gate_up, w_down, out: Sequence[Tokens], ws, ws_bytes: Optional[int] = None,
+                     stream=None):
+    """Returns (best descriptor, its mean ms per call)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    n_macro = len(topk_idx)
+    mb = (C.c_int32 * len(minibatches))(*minibatches)
+    mv = (C.c_int32 * max(len(n_moves), 1))(*(list(n_moves) or [0]))
+    idx_arr = (C.c_void_p * n_macro)(*[_ptr(t) for t in topk_idx])
+    gate_arr = (C.c_void_p * n_macro)(*[_ptr(t) for t in topk_gate])
+    out_arr = (mok_tokens * n_macro)(*[o.c for o in out])
+    best = mok_layer_desc()
+    ms = C.c_float(0.0)
+    _check(_lib.mok_tune_forward(C.byref(desc), mb, len(minibatches), mv, len(n_moves), reps,
+                                 n_macro, C.cast(idx_arr, C.c_void_p), C.cast(gate_arr, C.c_void_p),
+                                 T, C.byref(x.c), _ptr(w_gate_up), _ptr(w_down), out_arr, _ptr(ws),
+                                 ws_bytes, C.byref(best), C.byref(ms), _stream(stream)),
+           "mok_tune_forward")
+    return best, float(ms.value)
 
 
 def mok_device_status(ws, stream=None) -> int:

@@ -503,6 +503,59 @@ mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
                                  ws_bytes, stream);
 }
 
+mok_status mok_tune_forward(const mok_layer_desc* desc, const int32_t* minibatch,
+                            int32_t n_minibatch, const int32_t* n_move, int32_t n_n_move,
+                            int32_t reps, int32_t n_macro, const int32_t* const* topk_idx,
+                            const float* const* topk_gate, int32_t T, const mok_tokens* x,
+                            const void* w_gate_up, const void* w_down, const mok_tokens* out,
+                            void* ws, size_t ws_bytes, mok_layer_desc* best, float* best_ms,
+                            hipStream_t stream) {
+  if (!desc || !minibatch || n_minibatch < 1 || n_n_move < 0 || (n_n_move > 0 && !n_move) ||
+      reps < 1 || n_macro < 1 || !best || !best_ms || !ws)
+    return MOK_ERR_INVALID_ARG;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return MOK_ERR_HIP;
+  }
+  bool found = false;
+  float best_t = 0.0f;
+  mok_layer_desc best_d = *desc;
+  const int nm = n_n_move > 0 ? n_n_move : 1;
+  for (int i = 0; i < n_minibatch; ++i) {
+    for (int j = 0; j < nm; ++j) {
+      mok_layer_desc d = *desc;
+      d.minibatch = minibatch[i];
+      if (n_n_move > 0) d.n_move_cus = n_move[j];
+      if (d.mode != MOK_MODE_PERSISTENT && j > 0) continue;   // movers only in persistent mode
+      const size_t need = mok_forward_workspace_size(&d, T, n_macro);
+      if (need == 0 || need > ws_bytes) continue;
+      // one untimed call, then `reps` timed ones
+      if (mok_moe_forward_batches(&d, n_macro, topk_idx, topk_gate, T, x, w_gate_up, w_down, out,
+                                  ws, ws_bytes, stream) != MOK_OK)
+        continue;
+      bool ok = hipEventRecord(e0, stream) == hipSuccess;
+      for (int r = 0; ok && r < reps; ++r)
+        ok = mok_moe_forward_batches(&d, n_macro, topk_idx, topk_gate, T, x, w_gate_up, w_down,
+                                     out, ws, ws_bytes, stream) == MOK_OK;
+      ok = ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+      int32_t dev = MOK_OK;
+      ok = ok && mok_device_status(ws, &dev, stream) == MOK_OK && dev == MOK_OK;
+      float ms = 0.0f;
+      ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+      if (!ok) continue;
+      ms /= static_cast<float>(reps);
+      if (!found || ms < best_t) { found = true; best_t = ms; best_d = d; }
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (!found) return MOK_ERR_UNSUPPORTED;
+  *best = best_d;
+  *best_ms = best_t;
+  return MOK_OK;
+}
+
 mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream) {
   if (!ws || !status_host) return MOK_ERR_INVALID_ARG;
   hipError_t e = hipStreamSynchronize(stream);
