@@ -212,6 +212,58 @@ def time_router_gemm(mok, wl, reps: int = 20):
             "input_GBps": round((T + E) * H * 2 / (ms * 1e-3) / 1e9, 1)}
 
 
+def time_backward(mok, dw, st, reps: int = 10):
+    """The backward of the layer share after a forward step (bf16 only): merge
+    backward (dy, dgate), the expert FFN backward (recompute of h, down dgrad
+    with the SwiGLU backward, gate/up dgrad), dispatch backward (dx).  Seeded
+    N(0, 1) dout for every pool token; per-call means over `reps` calls."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from gpu_harness import to_dev
+    wl = dw.wl
+    H, I, k, cap = wl.H, wl.I, wl.k, st.cap
+    R = int(st.offsets[-1].item())
+    d = dw.desc(max_rows=cap, weights_packed=1)        # h recomputed with the packed gate/up
+    dout = mok.Tokens([to_dev(W.normal_bf16(np.random.SeedSequence(900 + p), wl.part_rows * H, 1.0)
+                              .reshape(wl.part_rows, H)) for p in range(wl.n_partitions)],
+                      wl.part_rows)
+    dx = dw.new_out()
+    a, b = mok.mok_packed_weights_bwd_size(d)
+    gu_t = torch.empty(a, dtype=torch.uint8, device="cuda")
+    d_t = torch.empty(b, dtype=torch.uint8, device="cuda")
+    mok.mok_pack_weights_bwd(d, dw.w_gu, dw.w_d, gu_t, d_t)
+    dy = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    dgate = torch.empty((wl.T, k), dtype=torch.float32, device="cuda")
+    h = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
+    dh = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
+    dxs = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    calls = {
+        "combine_bwd": lambda: mok.mok_combine_backward(dout, st.y, cap, st.aos, st.offsets,
+                                                        wl.n_local, cap, dw.topk_gate, k, H, dy,
+                                                        cap, dgate, st.status),
+        "ffn_bwd": lambda: mok.mok_expert_ffn_backward(d, st.ring, cap, dy, st.offsets, 0, cap,
+                                                       st.w_gu, gu_t, d_t, h, dh, dxs, cap),
+        "dispatch_bwd": lambda: mok.mok_dispatch_backward(dxs, cap, st.aos, st.offsets, wl.n_local,
+                                                          cap, st.soa, k, H, dx, st.status),
+    }
+    out = {}
+    for name, f in calls.items():
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps, 4)
+    assert int(st.status.item()) == 0
+    flop = 4.0 * R * H * I + 2.0 * R * H * I + 4.0 * R * H * I   # h, da, dx_s
+    out["ffn_bwd_tflops"] = round(flop / (out["ffn_bwd"] * 1e-3) / 1e12, 1)
+    out["total_ms"] = round(out["combine_bwd"] + out["ffn_bwd"] + out["dispatch_bwd"], 4)
+    return out
+
+
 def cpu_baseline(wl, sample_rows: int):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
@@ -278,6 +330,8 @@ def main():
                          "MODE 0 stream / 1 persistent")
     ap.add_argument("--streaming", action="store_true",
                     help="also time 8 Kimi-shaped macrobatches through one ring, per mode")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward of the layer share (bf16 workloads)")
     ap.add_argument("--tune", action="store_true",
                     help="also run mok_tune_forward over minibatches (and mover counts) per mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -422,6 +476,11 @@ def main():
             log(f"[bench] tuner ({key}): {tuned[key]}")
             del ws_t
 
+    backward = None
+    if args.backward and not mx and not wfmt:
+        backward = time_backward(mok, dw, st)
+        log(f"[bench] backward (ms): {backward}")
+
     router = time_router_gemm(mok, wl)
     log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
         f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
@@ -471,6 +530,7 @@ def main():
         "fused_forward_ms": fused or None,
         "streaming_ms_per_macrobatch": streaming,
         "router_gemm": router,
+        "backward_ms": backward,
         "tuned_forward": tuned,
         "cpu_baseline": cpu,
     }

@@ -289,6 +289,73 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
                              int32_t H, const mok_tokens* out, int32_t* dev_status,
                              hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the layer's share (the pages report the backward pass next to
+ * the forward; the reverse of pull dispatch and push combine).  bf16
+ * activations and weights.  Per routed slot s of token t, pick j, local
+ * expert e, gate w = topk_gate[t][j], with x_s the token's row,
+ * h_s = W_gu[e] x_s = [g, u], a_s = SiLU(g) u, y_s = W_d[e] a_s and
+ * out[t] = sum_j w y_s:
+ *   dy_s    = w dout[t]                           (mok_combine_backward)
+ *   dgate   = <dout[t], y_s>                      (mok_combine_backward)
+ *   da_s    = W_d[e]^T dy_s
+ *   dg = da u SiLU'(g),  du = da SiLU(g),  SiLU'(g) = s (1 + g (1 - s)),
+ *   s = 1 / (1 + e^-g)                            (mok_expert_ffn_backward)
+ *   dx_s    = W_gu[e]^T [dg, du]                  (mok_expert_ffn_backward)
+ *   dx[t]   = sum_j dx_s                          (mok_dispatch_backward)
+ * Weight gradients are not computed.  Storage is bf16, sums fp32.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the transposed packed weights the backward GEMMs read:
+ * W_gu^T (n_local x H x 2I) and W_d^T (n_local x I x H).  bf16 only. */
+mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
+                                       size_t* down_t_bytes);
+/* Packs them from the bf16 weights of mok_expert_ffn's layout (either pair of
+ * pointers may be null). */
+mok_status mok_pack_weights_bwd(const mok_layer_desc* desc, const void* w_gate_up,
+                                const void* w_down, void* packed_gate_up_t, void* packed_down_t,
+                                hipStream_t stream);
+
+/* Backward of the weighted merge: for each routed slot s < min(n_slots, R),
+ * with a = assign_of_slot[s], t = a / k: dy row s % dy_rows = bf16(w dout[t])
+ * (dy bf16, dy_rows x H, column-blocked like the ring) and dgate[a] =
+ * sum_h dout[t][h] y[s][h] in fp32 (y: the forward's return area, bf16
+ * [y_rows][H] indexed by slot).  dgate entries of non-local assignments are
+ * not written.  dout: bf16 rows of the pool's tokens (mok_tokens).  H a
+ * multiple of 64.  A token outside dout or s >= y_rows sets
+ * *dev_status = MOK_ERR_CAPACITY and the slot is skipped. */
+mok_status mok_combine_backward(const mok_tokens* dout, const void* y, int32_t y_rows,
+                                const int32_t* assign_of_slot, const int32_t* offsets,
+                                int32_t n_local, int32_t n_slots, const float* topk_gate,
+                                int32_t k, int32_t H, void* dy, int32_t dy_rows, float* dgate,
+                                int32_t* dev_status, hipStream_t stream);
+
+/* Backward of the expert FFN for slots [slot_begin, min(slot_end, R)):
+ * recomputes h (bf16, rows x 2I, row-major, row s % rows) from the ring (row
+ * s % ring_slots) and w_gate_up (packed as desc->weights_packed says, as for
+ * the forward), then da = dy W_d with the
+ * SwiGLU backward in its epilogue (dh: bf16 rows x 2I, column-blocked), then
+ * dx_s = dh W_gu (bf16 [rows][H], row-major, row s % rows).  h, dh and
+ * dx_slots are caller scratch / output; the packed weights come from
+ * mok_pack_weights_bwd.  Each buffer must stay below 4 GiB
+ * (MOK_ERR_UNSUPPORTED). */
+mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
+                                   int32_t ring_slots, const void* dy, const int32_t* offsets,
+                                   int32_t slot_begin, int32_t slot_end, const void* w_gate_up,
+                                   const void* packed_gate_up_t, const void* packed_down_t,
+                                   void* h, void* dh, void* dx_slots, int32_t rows,
+                                   hipStream_t stream);
+
+/* Backward of the pull dispatch (a push of gradients back to the tokens):
+ * dx[t] = bf16(sum over t's local slots s, ascending j, of dx_slots row s)
+ * in fp32, written at t's smallest local slot like mok_combine_slots (unit
+ * gates).  Tokens without a local slot are not written. */
+mok_status mok_dispatch_backward(const void* dx_slots, int32_t rows,
+                                 const int32_t* assign_of_slot, const int32_t* offsets,
+                                 int32_t n_local, int32_t n_slots, const int32_t* slot_of_assign,
+                                 int32_t k, int32_t H, const mok_tokens* dx, int32_t* dev_status,
+                                 hipStream_t stream);
+
 /* Bytes of workspace mok_moe_forward / mok_moe_forward_batches need for T
  * source tokens per macrobatch and n_macro macrobatches. */
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro);

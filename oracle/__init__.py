@@ -300,3 +300,71 @@ def forward(wl, tokens=None, slots_extra=None) -> Dict[str, np.ndarray]:
     out, written = combine_tokens(y, y_row_of_slot, soa, gate, tokens, k)
     res.update(slots=slots, x_rows=xr, y=y, tokens=tokens, out=out, written=written)
     return res
+
+
+# ---------------------------------------------------------------- backward
+# The backward of the layer's share, in fp64 from the stored bf16 values
+# (the pages report the backward pass beside the forward; its steps are the
+# chain rule through the forward's, in reverse order: the merge, the down
+# projection, SwiGLU, the gate/up projection, the pull dispatch).
+
+def silu_and_grad(g: np.ndarray):
+    """SiLU(g) = g s and its derivative s (1 + g (1 - s)), s = 1 / (1 + e^-g)."""
+    s = 1.0 / (1.0 + np.exp(-g))
+    return g * s, s * (1.0 + g * (1.0 - s))
+
+
+def ffn_backward_values(x: np.ndarray, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray,
+                        dy: np.ndarray):
+    """Backward of the expert SwiGLU FFN per row, all fp64 values: with
+    h = W_gu[e] x = [g, u] and a = SiLU(g) u, y = W_d[e] a, returns
+    (dh, dx): da = W_d[e]^T dy, dg = da u SiLU'(g), du = da SiLU(g),
+    dh = [dg, du], dx = W_gu[e]^T dh.  x [n, H], w_gu [n_local, 2I, H],
+    w_d [n_local, H, I], dy [n, H]."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    eor = np.asarray(expert_of_row, np.int64).reshape(-1)
+    I = w_gu.shape[1] // 2
+    dh = np.zeros((x.shape[0], 2 * I))
+    dx = np.zeros_like(x)
+    for e in np.unique(eor):
+        r = np.nonzero(eor == e)[0]
+        h = x[r] @ w_gu[e].T
+        g, u = h[:, :I], h[:, I:]
+        da = dy[r] @ w_d[e]
+        sl, dsl = silu_and_grad(g)
+        dh[r] = np.concatenate([da * u * dsl, da * sl], axis=1)
+        dx[r] = dh[r] @ w_gu[e]
+    return dh, dx
+
+
+def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
+    """Backward of the whole layer share for a workload with bf16 activations
+    and weights, given dout (bf16 bits [T, H], the gradient of out): the
+    schedule and the forward's stored rows (gathered x, y as bf16), then per
+    routed slot s of token t, pick j, gate w: dy_s = w dout[t] and
+    dgate[t, j] = <dout[t], y_s>; dx_s through ffn_backward_values; and
+    dx[t] = sum over t's local slots of dx_s.  fp64 throughout.  Returns
+    dy [R, H], dgate [T, k] (NaN where not local), dx [T, H] and written [T]."""
+    idx, gate = (route_topk(wl.logits, wl.k) if wl.routing_from_logits
+                 else (wl.topk_idx, wl.topk_gate))
+    sch = build_schedule(idx, wl.expert_base, wl.n_local)
+    R, aos, soa = sch["R"], sch["assign_of_slot"], sch["slot_of_assign"]
+    slots = np.arange(R)
+    xr = gather_rows(wl.x, wl.k, aos, slots, False)
+    eos = expert_of_slots(sch["offsets"], slots)
+    y = ffn_rows(xr, eos, wl.w_gu, wl.w_d, False)
+    t_of = aos[:R] // wl.k
+    w = np.asarray(gate, np.float64).reshape(-1)[aos[:R]]
+    dout_v = bf16_value(dout_bits).astype(np.float64)
+    dy = w[:, None] * dout_v[t_of]
+    dgate = np.full(idx.size, np.nan)
+    dgate[aos[:R]] = np.sum(dout_v[t_of] * bf16_value(y).astype(np.float64), axis=1)
+    dh, dx_s = ffn_backward_values(bf16_value(xr), eos, bf16_value(wl.w_gu).astype(np.float64),
+                                   bf16_value(wl.w_d).astype(np.float64), dy)
+    T = idx.shape[0]
+    dx = np.zeros((T, wl.H))
+    np.add.at(dx, t_of, dx_s)
+    written = (soa.reshape(T, wl.k) >= 0).any(axis=1)
+    return {"R": R, "dy": dy, "dgate": dgate.reshape(idx.shape), "dx": dx, "written": written,
+            "y": y, "dh": dh, "expert_of_slot": eos, "token_of_slot": t_of}

@@ -58,6 +58,15 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 0, 4, 1, None, 4, 1, None, None) == E
     assert L.mok_combine(1, 4, 1, 1, 17, 2, 64, C.byref(tok), None, None) == E  # T > rows
     assert L.mok_combine(1, 4, 1, 1, 16, 2, 60, C.byref(tok), None, None) == E  # H % 8
+    # backward: MXFP8 desc refused, H % 64 for the merge backward, null buffers
+    dmx = _desc(act_format=1)
+    a, b = C.c_size_t(0), C.c_size_t(0)
+    assert L.mok_packed_weights_bwd_size(C.byref(dmx), C.byref(a), C.byref(b)) == E
+    assert L.mok_combine_backward(C.byref(tok), 1, 4, 1, 1, 8, 4, 1, 2, 60, 1, 4, 1, None, None) == E
+    assert L.mok_combine_backward(C.byref(tok), None, 4, 1, 1, 8, 4, 1, 2, 64, 1, 4, 1, None, None) == E
+    db = _desc()
+    assert L.mok_expert_ffn_backward(C.byref(db), 1, 8, 1, 1, 0, 8, 1, 1, 1, None, 1, 1, 8, None) == E
+    assert L.mok_dispatch_backward(None, 8, 1, 1, 8, 4, 1, 2, 64, C.byref(tok), None, None) == E
     # tuner: no candidates, reps < 1, null result pointers
     d = _desc()
     one = (C.c_int32 * 1)(64)

@@ -1,0 +1,66 @@
+"""Pins for the oracle's backward of the expert FFN (the chain rule through
+gate/up, SwiGLU and down; the pages report the backward pass beside the
+forward).
+
+Pinned against things the oracle does not compute itself:
+  - central finite differences of the scalar <dy, y(x)> of an fp64 forward,
+    for dx and for dh (so a dropped term of SiLU', a swapped g/u or a
+    transposed weight fails);
+  - the closed form of the "square" expert (gate = [Id; -Id], up = [Id; Id],
+    down = c [Id, -Id] gives y = c x*x, so dx = 2 c x dy exactly).
+"""
+import numpy as np
+
+
+def _forward(x, eor, w_gu, w_d):
+    I = w_gu.shape[1] // 2
+    y = np.zeros((x.shape[0], w_d.shape[1]))
+    for r in range(x.shape[0]):
+        h = w_gu[eor[r]] @ x[r]
+        g, u = h[:I], h[I:]
+        y[r] = w_d[eor[r]] @ (g / (1.0 + np.exp(-g)) * u)
+    return y
+
+
+def test_ffn_backward_finite_differences(orc):
+    rng = np.random.default_rng(3)
+    n, nl, H, I = 5, 2, 8, 4
+    x = rng.standard_normal((n, H))
+    w_gu = rng.standard_normal((nl, 2 * I, H)) * 0.5
+    w_d = rng.standard_normal((nl, H, I)) * 0.5
+    dy = rng.standard_normal((n, H))
+    eor = np.array([0, 1, 1, 0, 1])
+    dh, dx = orc.ffn_backward_values(x, eor, w_gu, w_d, dy)
+    f = lambda xx: float(np.sum(dy * _forward(xx, eor, w_gu, w_d)))
+    eps = 1e-6
+    num = np.zeros_like(x)
+    for r in range(n):
+        for c in range(H):
+            xp, xm = x.copy(), x.copy()
+            xp[r, c] += eps
+            xm[r, c] -= eps
+            num[r, c] = (f(xp) - f(xm)) / (2 * eps)
+    assert np.allclose(dx, num, rtol=1e-6, atol=1e-7)
+    # dh against differences in h = [g, u] itself
+    for r in range(n):
+        h = w_gu[eor[r]] @ x[r]
+        fh = lambda hh: float(dy[r] @ (w_d[eor[r]] @ (hh[:I] / (1.0 + np.exp(-hh[:I])) * hh[I:])))
+        for c in range(2 * I):
+            hp, hm = h.copy(), h.copy()
+            hp[c] += eps
+            hm[c] -= eps
+            assert abs(dh[r, c] - (fh(hp) - fh(hm)) / (2 * eps)) <= 1e-6 * (1 + abs(dh[r, c]))
+
+
+def test_ffn_backward_square_expert_closed_form(orc):
+    rng = np.random.default_rng(4)
+    H, c = 6, 0.75
+    Id = np.eye(H)
+    w_gu = np.concatenate([Id, -Id, Id, Id], axis=0)[None]        # gate [Id; -Id], up [Id; Id]
+    w_d = (c * np.concatenate([Id, -Id], axis=1))[None]           # down c [Id, -Id]
+    x = rng.standard_normal((4, H))
+    dy = rng.standard_normal((4, H))
+    y = _forward(x, np.zeros(4, int), w_gu, w_d)
+    assert np.allclose(y, c * x * x, rtol=1e-12, atol=1e-12)      # the forward identity
+    _, dx = orc.ffn_backward_values(x, np.zeros(4, int), w_gu, w_d, dy)
+    assert np.allclose(dx, 2 * c * x * dy, rtol=1e-12, atol=1e-12)

@@ -83,6 +83,14 @@ _SIGS = {
                                           _SZ, _P]),
     "mok_tune_forward": (C.c_int, [_DESC, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _I32, _TOK,
                                    _P, _P, _TOK, _P, _SZ, _DESC, C.POINTER(C.c_float), _P]),
+    "mok_packed_weights_bwd_size": (C.c_int, [_DESC, C.POINTER(_SZ), C.POINTER(_SZ)]),
+    "mok_pack_weights_bwd": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
+    "mok_combine_backward": (C.c_int, [_TOK, _P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _P,
+                                       _I32, _P, _P, _P]),
+    "mok_expert_ffn_backward": (C.c_int, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P,
+                                          _P, _P, _I32, _P]),
+    "mok_dispatch_backward": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _TOK, _P,
+                                        _P]),
     "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "mok_forward_minibatch": (_I32, [_DESC, _I32]),
     "mok_status_str": (C.c_char_p, [C.c_int]),
@@ -319,6 +327,47 @@ def mok_tune_forward(desc: mok_layer_desc, minibatches: Sequence[int], n_moves: 
                                  ws_bytes, C.byref(best), C.byref(ms), _stream(stream)),
            "mok_tune_forward")
     return best, float(ms.value)
+
+
+def mok_packed_weights_bwd_size(desc: mok_layer_desc):
+    a, b = _SZ(0), _SZ(0)
+    _check(_lib.mok_packed_weights_bwd_size(C.byref(desc), C.byref(a), C.byref(b)),
+           "mok_packed_weights_bwd_size")
+    return int(a.value), int(b.value)
+
+
+def mok_pack_weights_bwd(desc: mok_layer_desc, w_gate_up, w_down, packed_gate_up_t, packed_down_t,
+                         stream=None) -> None:
+    _check(_lib.mok_pack_weights_bwd(C.byref(desc), _ptr(w_gate_up), _ptr(w_down),
+                                     _ptr(packed_gate_up_t), _ptr(packed_down_t), _stream(stream)),
+           "mok_pack_weights_bwd")
+
+
+def mok_combine_backward(dout: Tokens, y, y_rows: int, assign_of_slot, offsets, n_local: int,
+                         n_slots: int, topk_gate, k: int, H: int, dy, dy_rows: int, dgate,
+                         dev_status=None, stream=None) -> None:
+    _check(_lib.mok_combine_backward(C.byref(dout.c), _ptr(y), y_rows, _ptr(assign_of_slot),
+                                     _ptr(offsets), n_local, n_slots, _ptr(topk_gate), k, H,
+                                     _ptr(dy), dy_rows, _ptr(dgate), _ptr(dev_status),
+                                     _stream(stream)), "mok_combine_backward")
+
+
+def mok_expert_ffn_backward(desc: mok_layer_desc, ring, ring_slots: int, dy, offsets,
+                            slot_begin: int, slot_end: int, w_gate_up, packed_gate_up_t,
+                            packed_down_t, h, dh, dx_slots, rows: int, stream=None) -> None:
+    _check(_lib.mok_expert_ffn_backward(C.byref(desc), _ptr(ring), ring_slots, _ptr(dy),
+                                        _ptr(offsets), slot_begin, slot_end, _ptr(w_gate_up),
+                                        _ptr(packed_gate_up_t), _ptr(packed_down_t), _ptr(h),
+                                        _ptr(dh), _ptr(dx_slots), rows, _stream(stream)),
+           "mok_expert_ffn_backward")
+
+
+def mok_dispatch_backward(dx_slots, rows: int, assign_of_slot, offsets, n_local: int, n_slots: int,
+                          slot_of_assign, k: int, H: int, dx: Tokens, dev_status=None,
+                          stream=None) -> None:
+    _check(_lib.mok_dispatch_backward(_ptr(dx_slots), rows, _ptr(assign_of_slot), _ptr(offsets),
+                                      n_local, n_slots, _ptr(slot_of_assign), k, H, C.byref(dx.c),
+                                      _ptr(dev_status), _stream(stream)), "mok_dispatch_backward")
 
 
 def mok_device_status(ws, stream=None) -> int:

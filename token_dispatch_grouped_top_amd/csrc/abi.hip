@@ -376,6 +376,86 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
                                          stream));
 }
 
+// ------------------------------------------------------------ backward
+namespace {
+bool bwd_desc_ok(const mok_layer_desc* d) {
+  return desc_ok(d) && d->act_format == MOK_ACT_BF16 && d->weight_format == MOK_W_BF16;
+}
+}  // namespace
+
+mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
+                                       size_t* down_t_bytes) {
+  if (!bwd_desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (gate_up_t_bytes) *gate_up_t_bytes = packed_bwd_gate_up_bytes(desc->hidden, desc->inter, desc->n_local);
+  if (down_t_bytes) *down_t_bytes = packed_bwd_down_bytes(desc->hidden, desc->inter, desc->n_local);
+  return MOK_OK;
+}
+
+mok_status mok_pack_weights_bwd(const mok_layer_desc* desc, const void* w_gate_up, const void* w_down,
+                                void* packed_gate_up_t, void* packed_down_t, hipStream_t stream) {
+  if (!bwd_desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if ((w_gate_up == nullptr) != (packed_gate_up_t == nullptr) ||
+      (w_down == nullptr) != (packed_down_t == nullptr))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_pack_weights_bwd(static_cast<const uint16_t*>(w_gate_up),
+                                            static_cast<const uint16_t*>(w_down), desc->hidden,
+                                            desc->inter, desc->n_local,
+                                            static_cast<uint16_t*>(packed_gate_up_t),
+                                            static_cast<uint16_t*>(packed_down_t), stream));
+}
+
+mok_status mok_combine_backward(const mok_tokens* dout, const void* y, int32_t y_rows,
+                                const int32_t* assign_of_slot, const int32_t* offsets,
+                                int32_t n_local, int32_t n_slots, const float* topk_gate, int32_t k,
+                                int32_t H, void* dy, int32_t dy_rows, float* dgate,
+                                int32_t* dev_status, hipStream_t stream) {
+  if (k < 1 || k > 32 || H <= 0 || H % 64 != 0 || n_local < 1 || n_slots < 0 || !tokens_ok(dout, 0))
+    return MOK_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!y || y_rows < 1 || !assign_of_slot || !offsets || !topk_gate || !dy ||
+                      dy_rows < 1 || !dgate))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_unmerge_slots(dout->part_ptr, dout->n_partitions, dout->part_rows, y,
+                                         y_rows, assign_of_slot, offsets, n_local, n_slots,
+                                         topk_gate, k, H, dy, dy_rows, dgate, dev_status, stream));
+}
+
+mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring, int32_t ring_slots,
+                                   const void* dy, const int32_t* offsets, int32_t slot_begin,
+                                   int32_t slot_end, const void* w_gate_up,
+                                   const void* packed_gate_up_t, const void* packed_down_t, void* h,
+                                   void* dh, void* dx_slots, int32_t rows, hipStream_t stream) {
+  if (!bwd_desc_ok(desc) || !ring || ring_slots < 1 || !dy || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_gate_up || !packed_gate_up_t || !packed_down_t || !h || !dh ||
+      !dx_slots || rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  const int64_t lim = 1ll << 32, H = desc->hidden, I = desc->inter;
+  if (static_cast<int64_t>(ring_slots) * H * 2 >= lim || static_cast<int64_t>(rows) * 2 * I * 2 >= lim ||
+      static_cast<int64_t>(rows) * H * 2 >= lim || 4ll * I * H >= lim)
+    return MOK_ERR_UNSUPPORTED;
+  BwdArgs a{};
+  a.ring = ring; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up); a.w_gu_packed = desc->weights_packed;
+  a.w_gu_t = static_cast<const uint16_t*>(packed_gate_up_t);
+  a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
+  a.dy = dy; a.h = h; a.dh = dh; a.dx = dx_slots; a.rows = rows;
+  a.H = desc->hidden; a.I = desc->inter;
+  return hip_status(launch_ffn_backward(a, stream));
+}
+
+mok_status mok_dispatch_backward(const void* dx_slots, int32_t rows, const int32_t* assign_of_slot,
+                                 const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                 const int32_t* slot_of_assign, int32_t k, int32_t H,
+                                 const mok_tokens* dx, int32_t* dev_status, hipStream_t stream) {
+  if (k < 1 || k > 32 || H <= 0 || H % 8 != 0 || n_local < 1 || n_slots < 0 || !tokens_ok(dx, 0))
+    return MOK_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!dx_slots || rows < 1 || !assign_of_slot || !offsets || !slot_of_assign))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_combine_slots(dx_slots, rows, assign_of_slot, offsets, n_local, n_slots,
+                                         slot_of_assign, nullptr, k, H, dx->part_ptr,
+                                         dx->n_partitions, dx->part_rows, dev_status, false, stream));
+}
+
 size_t mok_gemm_workspace_size(void) { return split_ws_bytes(device_cus()); }
 
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro) {

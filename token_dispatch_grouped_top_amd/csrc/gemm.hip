@@ -142,6 +142,38 @@ void k_pack_weights(const uint16_t* __restrict__ W, int64_t expert_stride, int32
   }
 }
 
+// Packing of a transposed weight (the backward GEMMs' B): the GEMM's weight
+// row n, k-value k is src[e][k][n] of a source stored [K][N] row-major per
+// expert.  One thread per 16-byte piece, as k_pack_weights; the 8 values of a
+// piece are 8 source rows apart by N.  Rows past N repeat the last one.
+__global__ __launch_bounds__(256)
+void k_pack_weights_t(const uint16_t* __restrict__ W, int64_t expert_stride, int32_t K, int32_t N,
+                      int32_t n_tiles, int32_t n_local, uint16_t* __restrict__ out) {
+  using G = Geo<false>;
+  constexpr int BK = G::BK;
+  constexpr int64_t kPieces = BM * BK / 8;
+  const int nk = K / BK;
+  const int64_t total = static_cast<int64_t>(n_local) * n_tiles * nk * kPieces;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t blk = u / kPieces;
+    const int o = static_cast<int>(u % kPieces) * 16;
+    const int kt = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;
+    const int nt = static_cast<int>(et % n_tiles), e = static_cast<int>(et / n_tiles);
+    const int row = o / G::ROWB_B;
+    const int chunk = ((o % G::ROWB_B) >> 4) ^ chunk_key<G::CPR_B>(row);
+    const int n = nt * BN + row < N ? nt * BN + row : N - 1;
+    const uint16_t* src = W + e * expert_stride + static_cast<int64_t>(kt * BK + chunk * 8) * N + n;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = static_cast<uint32_t>(src[(2 * q) * static_cast<int64_t>(N)]) |
+             (static_cast<uint32_t>(src[(2 * q + 1) * static_cast<int64_t>(N)]) << 16);
+    reinterpret_cast<uint4*>(out)[u] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <bool A_MX>
 hipError_t pack_one(const uint16_t* W, int64_t stride, int32_t K, int32_t I, int32_t N, bool swiglu,
                     int32_t n_tiles, int32_t n_local, uint16_t* out, hipStream_t s) {
@@ -240,6 +272,87 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_STORE_BF16>(g, n2, m_tiles, s);
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
                                              : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+}
+
+// ------------------------------------------------------------ backward
+// h = x . W_gu^T, stored whole (bf16 [rows][2I], row-major) for the SwiGLU
+// backward: the forward's gate/up GEMM (packed or not) with g and u stored.
+hipError_t launch_recompute_h(const BwdArgs& a, hipStream_t s) {
+  const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
+  if (span <= 0) return hipSuccess;
+  const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
+  GemmParams g{};
+  g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
+  g.A = a.ring; g.a_rows = a.ring_slots;
+  g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
+  g.N = a.I; g.I = a.I;
+  g.C = a.h; g.c_rows = a.rows;
+  g.w_packed = a.w_gu_packed;
+  return launch_one<false, EPI_STORE_GU>(g, (a.I + BN / 2 - 1) / (BN / 2), m_tiles, s);
+}
+
+// da = dy . W_d (dy column-blocked, K = H), then dh = SwiGLU'(h) . da in the
+// epilogue (column-blocked, 2I wide).  B: W_d^T packed [n_local][I][H].
+hipError_t launch_down_dgrad(const BwdArgs& a, hipStream_t s) {
+  const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
+  if (span <= 0) return hipSuccess;
+  const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
+  GemmParams g{};
+  g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
+  g.A = a.dy; g.a_rows = a.rows;
+  g.W = a.w_d_t; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.H;
+  g.N = a.I; g.I = 0;
+  g.C = a.dh; g.c_rows = a.rows; g.H_src = static_cast<const uint16_t*>(a.h);
+  g.w_packed = 1;
+  return launch_one<false, EPI_SWIGLU_BWD>(g, (a.I + BN - 1) / BN, m_tiles, s);
+}
+
+// dx_s = dh . W_gu (dh column-blocked, K = 2I) -> bf16 [rows][H], row-major.
+// B: W_gu^T packed [n_local][H][2I].
+hipError_t launch_gate_up_dgrad(const BwdArgs& a, hipStream_t s) {
+  const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
+  if (span <= 0) return hipSuccess;
+  const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
+  GemmParams g{};
+  g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
+  g.A = a.dh; g.a_rows = a.rows;
+  g.W = a.w_gu_t; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = 2 * a.I;
+  g.N = a.H; g.I = 0;
+  g.C = a.dx; g.c_rows = a.rows;
+  g.w_packed = 1;
+  return launch_one<false, EPI_STORE_BF16>(g, (a.H + BN - 1) / BN, m_tiles, s);
+}
+
+hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s) {
+  hipError_t e = launch_recompute_h(a, s);
+  if (e == hipSuccess) e = launch_down_dgrad(a, s);
+  if (e == hipSuccess) e = launch_gate_up_dgrad(a, s);
+  return e;
+}
+
+size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local) {
+  return static_cast<size_t>(n_local) * ((H + BN - 1) / BN) * BM * (2 * static_cast<size_t>(I)) * 2;
+}
+size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local) {
+  return static_cast<size_t>(n_local) * ((I + BN - 1) / BN) * BM * static_cast<size_t>(H) * 2;
+}
+
+hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
+                                   int32_t n_local, uint16_t* packed_gu_t, uint16_t* packed_d_t,
+                                   hipStream_t s) {
+  auto pack_t = [&](const uint16_t* W, int64_t stride, int32_t K, int32_t N, uint16_t* out) {
+    const int n_tiles = (N + BN - 1) / BN;
+    const int64_t pieces = static_cast<int64_t>(n_local) * n_tiles * (K / Geo<false>::BK) *
+                           (BM * Geo<false>::BK / 8);
+    const int64_t blocks = (pieces + 255) / 256;
+    hipLaunchKernelGGL(k_pack_weights_t, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                       dim3(256), 0, s, W, stride, K, N, n_tiles, n_local, out);
+    return hipGetLastError();
+  };
+  hipError_t e = hipSuccess;
+  if (w_gu && packed_gu_t) e = pack_t(w_gu, static_cast<int64_t>(2) * I * H, 2 * I, H, packed_gu_t);
+  if (e == hipSuccess && w_d && packed_d_t) e = pack_t(w_d, static_cast<int64_t>(H) * I, H, I, packed_d_t);
+  return e;
 }
 
 size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format) {

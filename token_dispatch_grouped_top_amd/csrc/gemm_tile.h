@@ -67,7 +67,16 @@ template <bool A_MX> struct Geo {
 };
 static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LDS budget");
 
-enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2 };
+// EPI_SWIGLU_BWD: the backward of SwiGLU on the down GEMM's gradient (da):
+// reads g, u of the same (row, i) from H_src and writes dh = [dg, du].
+// EPI_STORE_GU: a gate/up tile stores g and u themselves (h = [g, u], bf16
+// [c_rows][2 N] row-major) for that backward.
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2, EPI_SWIGLU_BWD = 3,
+           EPI_STORE_GU = 4 };
+// Whether an epilogue pairs gate and up columns (the gate/up weight order).
+template <int EPI> constexpr bool epi_swiglu() {
+  return EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MX || EPI == EPI_STORE_GU;
+}
 
 struct GemmParams {
   const void* A;              // bf16 or E4M3 codes, a_rows x K, column-blocked
@@ -88,6 +97,7 @@ struct GemmParams {
   int32_t w_packed;           // W in the packed tile order written by launch_pack_weights
   int32_t a_row_base;         // A row of slot s: (s + a_row_base) % a_rows
   int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
+  const uint16_t* H_src;      // EPI_SWIGLU_BWD: h = [g, u] bf16 [c_rows][2 N], row-major
   // Split of the last, partial round of tiles along K (standalone launches):
   float* part;                // [n_cus][BM * BN] fp32 partial tiles; null = no split
   int32_t* part_cnt;          // [n_cus] arrival counters, zero before and after a launch
@@ -243,7 +253,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
   const int row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
-  constexpr bool swiglu = EPI != EPI_STORE_BF16;
+  constexpr bool swiglu = epi_swiglu<EPI>();
   const int n0 = ntile * (swiglu ? BN / 2 : BN);
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
@@ -329,7 +339,72 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
     return c < p.c_rows ? c : (p.c_rows >= BM ? c - p.c_rows : c % p.c_rows);
   };
   const int erow = 128 * wm + frag_row;                  // + 32 mi
-  if (EPI == EPI_STORE_BF16) {
+  if (EPI == EPI_STORE_GU) {
+    // gate column i pairs with up column i in tile (mi, ni + 2), as in the
+    // SwiGLU epilogue; both go out as bf16, 4 columns per 8-byte store
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+    const int64_t N2 = 2 * static_cast<int64_t>(p.N);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
+      if (r >= nrows) continue;
+      uint16_t* hrow = C + c_row_of(r) * N2;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + 64 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if (col >= p.N) continue;
+          const float4 g4 = tv[4 * ni + g], u4 = tv[4 * (ni + 2) + g];
+          *reinterpret_cast<uint2*>(hrow + col) = make_uint2(pack_bf16x2(g4.x, g4.y), pack_bf16x2(g4.z, g4.w));
+          *reinterpret_cast<uint2*>(hrow + p.N + col) = make_uint2(pack_bf16x2(u4.x, u4.y), pack_bf16x2(u4.z, u4.w));
+        }
+    }
+  } else if (EPI == EPI_SWIGLU_BWD) {
+    // da of 4 consecutive columns per lane and (mi, ni, g); with g, u of the
+    // same (row, i) from H_src: dg = da u SiLU'(g), du = da SiLU(g), where
+    // SiLU(g) = g s, SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g).  dh is
+    // column-blocked (the next GEMM's token operand), 2 N wide.
+    uint8_t* C = static_cast<uint8_t*>(p.C);
+    const int64_t N2 = 2 * static_cast<int64_t>(p.N);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = erow + 32 * mi;
+      float4 tv[16];
+      tile_vals(mi, tv);
+      if (r >= nrows) continue;
+      const int64_t crow = c_row_of(r);
+      const uint16_t* hrow = p.H_src + crow * N2;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + 128 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if (col >= p.N) continue;
+          const uint2 gb = *reinterpret_cast<const uint2*>(hrow + col);
+          const uint2 ub = *reinterpret_cast<const uint2*>(hrow + p.N + col);
+          const float gv[4] = {__uint_as_float(gb.x << 16), __uint_as_float(gb.x & 0xffff0000u),
+                               __uint_as_float(gb.y << 16), __uint_as_float(gb.y & 0xffff0000u)};
+          const float uv[4] = {__uint_as_float(ub.x << 16), __uint_as_float(ub.x & 0xffff0000u),
+                               __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xffff0000u)};
+          const float4 t = tv[4 * ni + g];
+          const float da[4] = {t.x, t.y, t.z, t.w};
+          float dg[4], du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[q]));
+            du[q] = da[q] * gv[q] * sg;
+            dg[q] = da[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+          }
+          *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * col)) =
+              make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * (p.N + col))) =
+              make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        }
+    }
+  } else if (EPI == EPI_STORE_BF16) {
     constexpr int RB = BN * 2;                             // bytes per staged row
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -445,7 +520,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   // loads (M0) are scalar arithmetic, with no v_readfirstlane per load
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
-  constexpr bool swiglu = EPI != EPI_STORE_BF16;
+  constexpr bool swiglu = epi_swiglu<EPI>();
   const int K = p.K;
   const int nk_all = K / BK;
   // k-steps of this job: the operand bases below start at k-step kt0

@@ -141,7 +141,16 @@ hipError_t launch_combine(const void* y, int32_t y_rows, const int32_t* soa, con
                           int32_t part_rows, int32_t* status, bool abort_on_status,
                           hipStream_t s);
 
-// Merge driven by routed slots: each token merged at its smallest local slot.
+// Backward of the merge, one wave per routed slot: dy (column-blocked) and
+// dgate.
+hipError_t launch_unmerge_slots(void* const* dout_ptr, int32_t n_part, int32_t part_rows,
+                                const void* y, int32_t y_rows, const int32_t* aos,
+                                const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                const float* gate, int32_t k, int32_t H, void* dy, int32_t dy_rows,
+                                float* dgate, int32_t* status, hipStream_t s);
+
+// Merge driven by routed slots: each token merged at its smallest local slot
+// (gate null: unit gates, i.e. the plain sum of the token's slot rows).
 hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* aos,
                                 const int32_t* offsets, int32_t n_local, int32_t n_slots,
                                 const int32_t* soa, const float* gate, int32_t k, int32_t H,
@@ -174,6 +183,29 @@ struct FfnArgs {
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// Backward of the expert FFN over slots [s_begin, min(s_end, R)): h = x W_gu^T
+// (recomputed, bf16 [rows][2I]); da = dy W_d and dh = SwiGLU backward (dh
+// column-blocked [rows][2I]); dx_s = dh W_gu (bf16 [rows][H]).  Rows of slot s:
+// s % rows in every buffer; x from the ring (row s % ring_slots).
+struct BwdArgs {
+  const void* ring; int32_t ring_slots;
+  const int32_t* offsets; int32_t n_local; int32_t s_begin, s_end;
+  const uint16_t* w_gu;       // the forward's gate/up weights (the recompute of h)
+  int32_t w_gu_packed;        // ... in the packed tile order
+  const uint16_t* w_gu_t;     // packed W_gu^T (launch_pack_weights_bwd)
+  const uint16_t* w_d_t;      // packed W_d^T
+  const void* dy;             // column-blocked [rows][H]
+  void* h; void* dh; void* dx;
+  int32_t rows;
+  int32_t H, I;
+};
+hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s);
+size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
+size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local);
+hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
+                                   int32_t n_local, uint16_t* packed_gu_t, uint16_t* packed_d_t,
+                                   hipStream_t s);
+
 // Packed weights: bytes, and the packing launch (either source may be null).
 size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);
 size_t packed_down_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);

@@ -101,7 +101,36 @@ void k_combine_slots(const uint16_t* __restrict__ y, int32_t y_rows,
   merge_slot(y, y_rows, a, soa, gate, s, k, H, out_parts, n_part, part_rows, status);
 }
 
+// One wave per routed slot s < min(R, n_slots): the backward of the merge.
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void k_unmerge_slots(void* const* __restrict__ dout_parts, int32_t n_part, int32_t part_rows,
+                     const uint16_t* __restrict__ y, int32_t y_rows,
+                     const int32_t* __restrict__ aos, const int32_t* __restrict__ offsets,
+                     int32_t n_local, int32_t n_slots, const float* __restrict__ gate, int32_t k,
+                     int32_t H, uint8_t* __restrict__ dy, int32_t dy_rows,
+                     float* __restrict__ dgate, int32_t* status) {
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (s >= n_slots) return;
+  const int32_t a = aos[s];                 // issued together with R (aos holds n_slots entries)
+  const int32_t R = offsets[n_local];
+  if (s >= R) return;
+  unmerge_slot(dout_parts, n_part, part_rows, y, y_rows, a, gate, s, k, H, dy, dy_rows, dgate, status);
+}
+
 }  // namespace
+
+hipError_t launch_unmerge_slots(void* const* dout_ptr, int32_t n_part, int32_t part_rows,
+                                const void* y, int32_t y_rows, const int32_t* aos,
+                                const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                const float* gate, int32_t k, int32_t H, void* dy, int32_t dy_rows,
+                                float* dgate, int32_t* status, hipStream_t s) {
+  if (n_slots <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((static_cast<int64_t>(n_slots) + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL(k_unmerge_slots, grid, dim3(kRowsPerBlock * kWave), 0, s, dout_ptr, n_part,
+                     part_rows, static_cast<const uint16_t*>(y), y_rows, aos, offsets, n_local,
+                     n_slots, gate, k, H, static_cast<uint8_t*>(dy), dy_rows, dgate, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_rows, int32_t H,
                          int32_t k, const int32_t* aos, const int32_t* offsets, int32_t n_local,

@@ -159,7 +159,7 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
   float my_g = 0.0f;
   if (lane < k) {
     my_s = soa[t * k + lane];
-    my_g = gate[t * k + lane];
+    my_g = gate ? gate[t * k + lane] : 1.0f;                // null: unit gates (plain sum)
     if (my_s >= y_rows) { set_status(status, MOK_ERR_CAPACITY); my_s = -1; }
   }
   const uint64_t live = __ballot(my_s >= 0);
@@ -239,6 +239,55 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ y, in
       }
     }
   }
+}
+
+// Backward of the weighted merge for slot s (token t = a_s / k, pick
+// j = a_s % k, gate w = gate[a_s]): dy[s] = bf16(w * dout[t]) into the
+// column-blocked dy (row s % dy_rows), and dgate[a_s] = sum_h dout[t][h] *
+// y[s][h] in fp32 (each lane sums its pieces in order, then a fixed
+// butterfly).  All 64 lanes must call it.
+__device__ __forceinline__ void unmerge_slot(void* const* __restrict__ dout_parts, int32_t n_part,
+                                             int32_t part_rows, const uint16_t* __restrict__ y,
+                                             int32_t y_rows, int32_t a_s,
+                                             const float* __restrict__ gate, int64_t s, int32_t k,
+                                             int32_t H, uint8_t* __restrict__ dy, int32_t dy_rows,
+                                             float* __restrict__ dgate, int32_t* status) {
+  const int lane = lane_id();
+  const uint4* src = token_row(dout_parts, n_part, part_rows, a_s / k, H);
+  if (!src || s >= y_rows) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
+  const float w = gate[a_s];
+  const uint4* yrow = reinterpret_cast<const uint4*>(y + s * static_cast<int64_t>(H));
+  const int64_t drow = s % dy_rows;
+  const int nvec = H / 8;
+  float part = 0.0f;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * kMergeFast) {
+    uint4 bd[kMergeFast], by[kMergeFast];
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < nvec) { bd[u] = src[v]; by[u] = yrow[v]; }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v >= nvec) continue;
+      const uint32_t d4[4] = {bd[u].x, bd[u].y, bd[u].z, bd[u].w};
+      const uint32_t y4[4] = {by[u].x, by[u].y, by[u].z, by[u].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float dlo = __uint_as_float(d4[q] << 16), dhi = __uint_as_float(d4[q] & 0xffff0000u);
+        part = fmaf(dlo, __uint_as_float(y4[q] << 16), part);
+        part = fmaf(dhi, __uint_as_float(y4[q] & 0xffff0000u), part);
+        o[q] = pack_bf16x2(w * dlo, w * dhi);
+      }
+      *reinterpret_cast<uint4*>(dy + colblk_byte(drow, dy_rows, 16 * static_cast<int64_t>(v))) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  if (lane == 0) dgate[a_s] = part;
 }
 
 // Slot-driven merge: slot s (s < R) merges its token t = assign_of_slot[s] / k
