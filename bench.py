@@ -215,7 +215,8 @@ def time_router_gemm(mok, wl, reps: int = 20):
 def time_backward(mok, dw, st, reps: int = 10):
     """The backward of the layer share after a forward step (bf16 only): merge
     backward (dy, dgate), the expert FFN backward (recompute of h, down dgrad
-    with the SwiGLU backward, gate/up dgrad), dispatch backward (dx).  Seeded
+    with the SwiGLU backward, gate/up dgrad), dispatch backward (dx), weight
+    gradients (transposes + two GEMMs over each expert's slots).  Seeded
     N(0, 1) dout for every pool token; per-call means over `reps` calls."""
     import numpy as np
     import torch
@@ -238,6 +239,9 @@ def time_backward(mok, dw, st, reps: int = 10):
     h = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
     dh = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
     dxs = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    dwgu = torch.empty((wl.n_local, 2 * I, H), dtype=torch.int16, device="cuda")
+    dwd = torch.empty((wl.n_local, H, I), dtype=torch.int16, device="cuda")
+    wws = torch.empty(mok.mok_wgrad_workspace_size(d, cap), dtype=torch.uint8, device="cuda")
     calls = {
         "combine_bwd": lambda: mok.mok_combine_backward(dout, st.y, cap, st.aos, st.offsets,
                                                         wl.n_local, cap, dw.topk_gate, k, H, dy,
@@ -246,6 +250,8 @@ def time_backward(mok, dw, st, reps: int = 10):
                                                        st.w_gu, gu_t, d_t, h, dh, dxs, cap),
         "dispatch_bwd": lambda: mok.mok_dispatch_backward(dxs, cap, st.aos, st.offsets, wl.n_local,
                                                           cap, st.soa, k, H, dx, st.status),
+        "wgrad": lambda: mok.mok_expert_wgrad(d, st.ring, cap, st.act, cap, dy, dh, cap, st.offsets,
+                                              dwgu, dwd, wws),
     }
     out = {}
     for name, f in calls.items():
@@ -260,7 +266,8 @@ def time_backward(mok, dw, st, reps: int = 10):
     assert int(st.status.item()) == 0
     flop = 4.0 * R * H * I + 2.0 * R * H * I + 4.0 * R * H * I   # h, da, dx_s
     out["ffn_bwd_tflops"] = round(flop / (out["ffn_bwd"] * 1e-3) / 1e12, 1)
-    out["total_ms"] = round(out["combine_bwd"] + out["ffn_bwd"] + out["dispatch_bwd"], 4)
+    out["wgrad_tflops"] = round(6.0 * R * H * I / (out["wgrad"] * 1e-3) / 1e12, 1)
+    out["total_ms"] = round(out["combine_bwd"] + out["ffn_bwd"] + out["dispatch_bwd"] + out["wgrad"], 4)
     return out
 
 

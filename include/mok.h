@@ -303,7 +303,9 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
  *   s = 1 / (1 + e^-g)                            (mok_expert_ffn_backward)
  *   dx_s    = W_gu[e]^T [dg, du]                  (mok_expert_ffn_backward)
  *   dx[t]   = sum_j dx_s                          (mok_dispatch_backward)
- * Weight gradients are not computed.  Storage is bf16, sums fp32.
+ *   dW_d[e] = sum_s dy_s a_s^T, dW_gu[e] = sum_s [dg, du]_s x_s^T
+ *                                                 (mok_expert_wgrad)
+ * Storage is bf16, sums fp32.
  * ------------------------------------------------------------------------ */
 
 /* Bytes of the transposed packed weights the backward GEMMs read:
@@ -345,6 +347,22 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
                                    const void* packed_gate_up_t, const void* packed_down_t,
                                    void* h, void* dh, void* dx_slots, int32_t rows,
                                    hipStream_t stream);
+
+/* Weight gradients over every routed slot s < R = offsets[n_local], per local
+ * expert e (slots offsets[e] .. offsets[e+1] - 1):
+ *   dW_down[e]    = sum_s dy_s a_s^T      bf16 [n_local][H][I]
+ *   dW_gate_up[e] = sum_s dh_s x_s^T      bf16 [n_local][2I][H]
+ * fp32 sums, bf16 results (either output may be null).  Inputs are the
+ * forward's ring (x, row s % ring_slots) and act (a, row s % act_rows) and
+ * the backward's dy (row s % rows, H) and dh (row s % rows, 2I), all
+ * column-blocked.  ws: mok_wgrad_workspace_size(desc, rows) bytes of device
+ * scratch (the operands transposed to slot-contiguous rows over a slot axis
+ * padded to 32 per expert).  rows must be >= R. */
+size_t mok_wgrad_workspace_size(const mok_layer_desc* desc, int32_t rows);
+mok_status mok_expert_wgrad(const mok_layer_desc* desc, const void* ring, int32_t ring_slots,
+                            const void* act, int32_t act_rows, const void* dy, const void* dh,
+                            int32_t rows, const int32_t* offsets, void* dw_gate_up,
+                            void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the pull dispatch (a push of gradients back to the tokens):
  * dx[t] = bf16(sum over t's local slots s, ascending j, of dx_slots row s)

@@ -338,6 +338,25 @@ def ffn_backward_values(x: np.ndarray, expert_of_row, w_gu: np.ndarray, w_d: np.
     return dh, dx
 
 
+def ffn_wgrad_values(x: np.ndarray, expert_of_row, w_gu: np.ndarray, dy: np.ndarray,
+                     dh: np.ndarray, n_local: int, H: int):
+    """Weight gradients of the expert FFN, fp64: per expert e over its rows,
+    dW_d[e] = sum dy a^T with a = SiLU(g) u, h = W_gu[e] x = [g, u], and
+    dW_gu[e] = sum dh x^T.  Returns (dW_gu [n_local, 2I, H], dW_d [n_local, H, I])."""
+    x = np.asarray(x, np.float64)
+    eor = np.asarray(expert_of_row, np.int64).reshape(-1)
+    I = w_gu.shape[1] // 2
+    dw_d = np.zeros((n_local, H, I))
+    dw_gu = np.zeros((n_local, 2 * I, H))
+    for e in np.unique(eor):
+        r = np.nonzero(eor == e)[0]
+        h = x[r] @ w_gu[e].T
+        a = silu_and_grad(h[:, :I])[0] * h[:, I:]
+        dw_d[e] = dy[r].T @ a
+        dw_gu[e] = dh[r].T @ x[r]
+    return dw_gu, dw_d
+
+
 def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     """Backward of the whole layer share for a workload with bf16 activations
     and weights, given dout (bf16 bits [T, H], the gradient of out): the
@@ -366,5 +385,8 @@ def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     dx = np.zeros((T, wl.H))
     np.add.at(dx, t_of, dx_s)
     written = (soa.reshape(T, wl.k) >= 0).any(axis=1)
+    dw_gu, dw_d = ffn_wgrad_values(bf16_value(xr), eos, bf16_value(wl.w_gu).astype(np.float64),
+                                   dy, dh, wl.n_local, wl.H)
     return {"R": R, "dy": dy, "dgate": dgate.reshape(idx.shape), "dx": dx, "written": written,
-            "y": y, "dh": dh, "expert_of_slot": eos, "token_of_slot": t_of}
+            "y": y, "dh": dh, "expert_of_slot": eos, "token_of_slot": t_of, "dw_d": dw_d,
+            "dw_gu": dw_gu}

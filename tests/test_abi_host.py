@@ -67,6 +67,11 @@ def test_invalid_arguments_rejected_without_launch():
     db = _desc()
     assert L.mok_expert_ffn_backward(C.byref(db), 1, 8, 1, 1, 0, 8, 1, 1, 1, None, 1, 1, 8, None) == E
     assert L.mok_dispatch_backward(None, 8, 1, 1, 8, 4, 1, 2, 64, C.byref(tok), None, None) == E
+    need = L.mok_wgrad_workspace_size(C.byref(db), 64)
+    assert need > 0 and L.mok_wgrad_workspace_size(C.byref(dmx), 64) == 0
+    assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, None, None, 1, need, None) == E
+    assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, 1, 1, 1, need - 1, None) == \
+        mok.MOK_ERR_WORKSPACE
     # tuner: no candidates, reps < 1, null result pointers
     d = _desc()
     one = (C.c_int32 * 1)(64)

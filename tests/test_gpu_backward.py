@@ -15,6 +15,9 @@ workload in fp64.  Bars:
     8 * 2^-9 * sum_j |W_gu[j][h]| |dh_j| (summed over the token's slots, from
     the oracle's fp64 dh) plus the layer's 2e-2 * RMS; tokens without a local
     slot are not written.
+  - weight gradients dW_d = sum dy a^T and dW_gu = sum dh x^T (mok_expert_wgrad):
+    per element 2e-2 * RMS + 8 * 2^-9 * sum_s |dy||a| (resp. |dh||x|), the
+    rounding bound of their bf16 operands; an empty expert's gradients are 0.
 Shapes: a ragged pool (tiles with tails, an empty expert) and a wider one.
 """
 import numpy as np
@@ -79,6 +82,11 @@ def test_backward_matches_oracle(name, packed):
     db = dw.desc(weights_packed=packed)                 # h recomputed with either gate/up layout
     mok.mok_expert_ffn_backward(db, ring, R, dy, s["offsets"], 0, R, dw.weights(db)[0], gu_t, d_t, h,
                                 dh, dxs, R)
+    wsb = mok.mok_wgrad_workspace_size(d, R)
+    wws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    dwgu = torch.full((wl.n_local, 2 * I, H), SENTINEL, dtype=torch.int16, device="cuda")
+    dwd = torch.full((wl.n_local, H, I), SENTINEL, dtype=torch.int16, device="cuda")
+    mok.mok_expert_wgrad(d, ring, R, act, R, dy, dh, R, s["offsets"], dwgu, dwd, wws)
     dx = dw.new_out()
     mok.mok_dispatch_backward(dxs, R, s["aos"], s["offsets"], wl.n_local, R, s["soa"], k, H, dx,
                               status)
@@ -116,3 +124,22 @@ def test_backward_matches_oracle(name, packed):
     rms = float(np.sqrt(np.mean(dref * dref)))
     bar = 2e-2 * rms + 8 * 2.0 ** -9 * mag[wr]
     assert np.all(np.abs(gv - dref) <= bar), float(np.max(np.abs(gv - dref) / bar))
+    # weight gradients: per element, 2e-2 RMS plus the rounding bound of the bf16
+    # operands over the expert's slots (8 * 2^-9 * sum_s |u_s| |v_s|)
+    eos, xv = ref["expert_of_slot"], oracle.bf16_value(oracle.gather_rows(
+        wl.x, k, aos, np.arange(R), False)).astype(np.float64)
+    wguv = oracle.bf16_value(wl.w_gu).astype(np.float64)
+    for name_, got_t, refw in (("dW_down", dwd, ref["dw_d"]), ("dW_gate_up", dwgu, ref["dw_gu"])):
+        gw = oracle.bf16_value(to_host(got_t)).astype(np.float64)
+        assert np.all(np.isfinite(gw)), name_
+        rmsw = float(np.sqrt(np.mean(refw * refw)))
+        for e in range(wl.n_local):
+            r = np.nonzero(eos == e)[0]
+            if name_ == "dW_down":
+                hh = xv[r] @ wguv[e].T
+                av = oracle.silu_and_grad(hh[:, :I])[0] * hh[:, I:]
+                magw = np.abs(ref["dy"][r]).T @ np.abs(av)
+            else:
+                magw = np.abs(ref["dh"][r]).T @ np.abs(xv[r])
+            barw = 2e-2 * rmsw + 8 * 2.0 ** -9 * magw
+            assert np.all(np.abs(gw[e] - refw[e]) <= barw), (name_, e, float(np.max(np.abs(gw[e] - refw[e]) / barw)))

@@ -64,3 +64,31 @@ def test_ffn_backward_square_expert_closed_form(orc):
     assert np.allclose(y, c * x * x, rtol=1e-12, atol=1e-12)      # the forward identity
     _, dx = orc.ffn_backward_values(x, np.zeros(4, int), w_gu, w_d, dy)
     assert np.allclose(dx, 2 * c * x * dy, rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_wgrad_finite_differences(orc):
+    """dW_d and dW_gu against central differences of <dy, y> in the weights."""
+    rng = np.random.default_rng(5)
+    n, nl, H, I = 6, 2, 5, 3
+    x = rng.standard_normal((n, H))
+    w_gu = rng.standard_normal((nl, 2 * I, H)) * 0.5
+    w_d = rng.standard_normal((nl, H, I)) * 0.5
+    dy = rng.standard_normal((n, H))
+    eor = np.array([0, 1, 1, 0, 1, 1])
+    dh, _ = orc.ffn_backward_values(x, eor, w_gu, w_d, dy)
+    dw_gu, dw_d = orc.ffn_wgrad_values(x, eor, w_gu, dy, dh, nl, H)
+    eps = 1e-6
+    f = lambda g, d: float(np.sum(dy * _forward(x, eor, g, d)))
+    for e in range(nl):
+        for i in range(H):
+            for j in range(I):
+                p_, m_ = w_d.copy(), w_d.copy()
+                p_[e, i, j] += eps
+                m_[e, i, j] -= eps
+                assert abs(dw_d[e, i, j] - (f(w_gu, p_) - f(w_gu, m_)) / (2 * eps)) < 1e-6
+        for i in range(2 * I):
+            for j in range(H):
+                p_, m_ = w_gu.copy(), w_gu.copy()
+                p_[e, i, j] += eps
+                m_[e, i, j] -= eps
+                assert abs(dw_gu[e, i, j] - (f(p_, w_d) - f(m_, w_d)) / (2 * eps)) < 1e-6

@@ -89,6 +89,9 @@ _SIGS = {
                                        _I32, _P, _P, _P]),
     "mok_expert_ffn_backward": (C.c_int, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P,
                                           _P, _P, _I32, _P]),
+    "mok_wgrad_workspace_size": (_SZ, [_DESC, _I32]),
+    "mok_expert_wgrad": (C.c_int, [_DESC, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ,
+                                   _P]),
     "mok_dispatch_backward": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _TOK, _P,
                                         _P]),
     "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
@@ -360,6 +363,19 @@ def mok_expert_ffn_backward(desc: mok_layer_desc, ring, ring_slots: int, dy, off
                                         _ptr(packed_gate_up_t), _ptr(packed_down_t), _ptr(h),
                                         _ptr(dh), _ptr(dx_slots), rows, _stream(stream)),
            "mok_expert_ffn_backward")
+
+
+def mok_wgrad_workspace_size(desc: mok_layer_desc, rows: int) -> int:
+    return int(_lib.mok_wgrad_workspace_size(C.byref(desc), rows))
+
+
+def mok_expert_wgrad(desc: mok_layer_desc, ring, ring_slots: int, act, act_rows: int, dy, dh,
+                     rows: int, offsets, dw_gate_up, dw_down, ws, ws_bytes: Optional[int] = None,
+                     stream=None) -> None:
+    _check(_lib.mok_expert_wgrad(C.byref(desc), _ptr(ring), ring_slots, _ptr(act), act_rows,
+                                 _ptr(dy), _ptr(dh), rows, _ptr(offsets), _ptr(dw_gate_up),
+                                 _ptr(dw_down), _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)),
+           "mok_expert_wgrad")
 
 
 def mok_dispatch_backward(dx_slots, rows: int, assign_of_slot, offsets, n_local: int, n_slots: int,

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmok.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "schedule.hip", "movers.hip", "gemm.hip", "persistent.hip", "abi.hip"]
+SOURCES = ["route.hip", "schedule.hip", "movers.hip", "gemm.hip", "wgrad.hip", "persistent.hip",
+           "abi.hip"]
 
 # Packed fp32 VALU ops are switched off for every HIP source (the compiler
 # would otherwise form v_pk_* fp32 ops from scalar or float2 code).

@@ -443,6 +443,31 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
   return hip_status(launch_ffn_backward(a, stream));
 }
 
+size_t mok_wgrad_workspace_size(const mok_layer_desc* desc, int32_t rows) {
+  if (!bwd_desc_ok(desc) || rows < 1) return 0;
+  return wgrad_ws_bytes(rows, desc->hidden, desc->inter, desc->n_local);
+}
+
+mok_status mok_expert_wgrad(const mok_layer_desc* desc, const void* ring, int32_t ring_slots,
+                            const void* act, int32_t act_rows, const void* dy, const void* dh,
+                            int32_t rows, const int32_t* offsets, void* dw_gate_up, void* dw_down,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!bwd_desc_ok(desc) || !ring || ring_slots < 1 || !act || act_rows < 1 || !dy || !dh ||
+      rows < 1 || !offsets || (!dw_gate_up && !dw_down) || !ws)
+    return MOK_ERR_INVALID_ARG;
+  if (ws_bytes < mok_wgrad_workspace_size(desc, rows)) return MOK_ERR_WORKSPACE;
+  const int64_t lim = 1ll << 32, H = desc->hidden, I = desc->inter;
+  const int64_t kp = wgrad_kpad(rows, desc->n_local);
+  if (kp * H * 2 >= lim || kp * 2 * I * 2 >= lim || static_cast<int64_t>(ring_slots) * H * 2 >= lim ||
+      static_cast<int64_t>(act_rows) * I * 2 >= lim || static_cast<int64_t>(rows) * 2 * I * 2 >= lim)
+    return MOK_ERR_UNSUPPORTED;
+  WgradArgs a{};
+  a.ring = ring; a.ring_slots = ring_slots; a.act = act; a.act_rows = act_rows;
+  a.dy = dy; a.dh = dh; a.rows = rows; a.offsets = offsets; a.n_local = desc->n_local;
+  a.dw_gu = dw_gate_up; a.dw_d = dw_down; a.ws = ws; a.H = desc->hidden; a.I = desc->inter;
+  return hip_status(launch_wgrad(a, stream));
+}
+
 mok_status mok_dispatch_backward(const void* dx_slots, int32_t rows, const int32_t* assign_of_slot,
                                  const int32_t* offsets, int32_t n_local, int32_t n_slots,
                                  const int32_t* slot_of_assign, int32_t k, int32_t H,

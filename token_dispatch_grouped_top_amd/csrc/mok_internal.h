@@ -200,6 +200,22 @@ struct BwdArgs {
   int32_t H, I;
 };
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s);
+// Weight gradients over all slots [0, R): dW_d = sum dy a^T, dW_gu = sum dh x^T
+// per expert (bf16 [n_local][H][I] and [n_local][2I][H]); slot s's rows are
+// s % rows (dy, dh), s % act_rows (act), s % ring_slots (ring); all
+// column-blocked.  ws: wgrad_ws_bytes(rows, H, I, n_local).
+struct WgradArgs {
+  const void* ring; int32_t ring_slots;
+  const void* act; int32_t act_rows;
+  const void* dy; const void* dh; int32_t rows;
+  const int32_t* offsets; int32_t n_local;
+  void* dw_gu; void* dw_d;
+  void* ws;
+  int32_t H, I;
+};
+int32_t wgrad_kpad(int32_t rows, int32_t n_local);
+size_t wgrad_ws_bytes(int32_t rows, int32_t H, int32_t I, int32_t n_local);
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
 size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local);
 hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
