@@ -37,9 +37,9 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 738612862),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 990450616),
-    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("51c76ab38975bd6f", 381115952),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 738619701),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 990408812),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 381087281),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
@@ -534,6 +534,12 @@ def main():
         "dispatch_GBps": round(disp_gbs, 1), "dispatch_frac_hbm": round(disp_gbs / PEAK_HBM_GBS, 4),
         "combine_GBps": round(comb_gbs, 1), "combine_frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
         "schedule_share": round(per["schedule"] / wall_ms, 4),
+        # the layer against its roofline: both GEMMs at the MFMA peak plus the
+        # gather and merge bytes at the HBM peak, over the timed wall
+        "layer_roofline_ms": round(((flop_gu + flop_dn) / (peak * 1e12) +
+                                    (disp_bytes + comb_bytes) / (PEAK_HBM_GBS * 1e9)) * 1e3, 4),
+        "layer_roofline_frac": round(((flop_gu + flop_dn) / (peak * 1e12) +
+                                      (disp_bytes + comb_bytes) / (PEAK_HBM_GBS * 1e9)) * 1e3 / wall_ms, 4),
         "fused_forward_ms": fused or None,
         "streaming_ms_per_macrobatch": streaming,
         "router_gemm": router,
