@@ -15,15 +15,19 @@
 // Tiling (gfx950: 160 KiB LDS, wave64, 4 SIMDs per CU):
 //   workgroup tile 256 x 256, 256 threads = 4 waves in 2 x 2, each wave
 //   128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane).
-//   Operand tiles stream through an LDS ring of NS k-steps; NS-1 of them are
-//   in flight while one is consumed, because these GEMMs are bound by how
-//   much load latency the LDS can cover, not by HBM bandwidth:
-//     bf16 A:  BK = 32, NS = 4 (4 x 32 KiB = 128 KiB, 96 KiB in flight);
-//     MXFP8 A: BK = 64, NS = 2, A staged through registers and dequantised.
-//   Loads go global -> LDS directly (global_load_lds_dwordx4): no staging
-//   registers, no ds_write.  Rows keep their 16-byte chunks XOR-swizzled so the
-//   fragment reads of 16 consecutive rows hit distinct banks; the swizzle is
-//   applied on the global side of the loads.
+//   Operand tiles stream through an LDS ring of NS k-steps, NS-1 of them in
+//   flight while one is consumed:
+//     bf16 tokens:  BK = 32, NS = 4 (4 x 32 KiB = 128 KiB);
+//     E4M3 tokens:  BK = 64, NS = 3, codes and E8M0 scales loaded into LDS
+//                   and converted to bf16 in registers per k-slice;
+//     E4M3 tokens and weights: gemm_tile_mx8.h (block-scaled FP8 MFMA).
+//   Loads go global -> LDS directly (buffer_load ... lds, a per-lane offset
+//   fixed for the tile plus a per-k-step scalar offset): no staging registers,
+//   no ds_write.  Weights come packed in the LDS image order, tokens from the
+//   column-blocked ring / act, so a k-step of either operand is one contiguous
+//   16 KiB block.  Rows keep their 16-byte chunks XOR-swizzled so the fragment
+//   reads of 16 consecutive rows hit distinct banks; the swizzle is applied on
+//   the global side of the loads.
 // Grouped M: the window's rows [s_begin, min(s_end, R)) are cut per expert
 // segment (offsets) into 256-row tiles; the grid is sized from the window
 // length (never from counts), and blocks past the last tile exit at once.
@@ -31,6 +35,8 @@
 // SwiGLU fusion: a gate/up tile takes 128 gate rows and the 128 up rows of the
 // same intermediate columns (64 + 64 per wave column), so each lane holds g and
 // u of the same (row, i) in accumulators (mi, ni) and (mi, ni + 2).
+// The backward's GEMMs reuse the tile with other epilogues: g and u stored
+// (EPI_STORE_GU), the SwiGLU backward (EPI_SWIGLU_BWD).
 #include "gemm_tile.h"
 #include "gemm_tile_mx8.h"
 
