@@ -37,9 +37,9 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 738619701),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 990408812),
-    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d4c42d9d86ca8d11", 381087281),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 738616935),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 990404317),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 381085806),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
