@@ -357,7 +357,9 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
  * the backward's dy (row s % rows, H) and dh (row s % rows, 2I), all
  * column-blocked.  ws: mok_wgrad_workspace_size(desc, rows) bytes of device
  * scratch (the operands transposed to slot-contiguous rows over a slot axis
- * padded to 32 per expert).  rows must be >= R. */
+ * padded to 32 per expert).  rows must be >= R; offsets that claim more
+ * slots than rows allow leave every access in bounds, but the gradients are
+ * then not meaningful. */
 size_t mok_wgrad_workspace_size(const mok_layer_desc* desc, int32_t rows);
 mok_status mok_expert_wgrad(const mok_layer_desc* desc, const void* ring, int32_t ring_slots,
                             const void* act, int32_t act_rows, const void* dy, const void* dh,

@@ -143,3 +143,32 @@ def test_backward_matches_oracle(name, packed):
                 magw = np.abs(ref["dh"][r]).T @ np.abs(xv[r])
             barw = 2e-2 * rmsw + 8 * 2.0 ** -9 * magw
             assert np.all(np.abs(gw[e] - refw[e]) <= barw), (name_, e, float(np.max(np.abs(gw[e] - refw[e]) / barw)))
+
+
+def test_wgrad_offsets_past_rows_stay_in_bounds():
+    """Device offsets that claim more slots than rows (a broken caller) must
+    not take the weight gradients outside their buffers: every expert then
+    gets one 32-slot segment.  The call returns, writes every gradient
+    element (finite, the sentinel gone) and leaves the guard bytes around
+    the workspace untouched."""
+    import token_dispatch_grouped_top_amd as mok
+    H, I, n_local, rows = 256, 128, 4, 64
+    d = mok.mok_layer_desc(hidden=H, inter=I, n_experts=8, top_k=2, expert_base=0,
+                           n_local=n_local, act_format=mok.MOK_ACT_BF16, weight_format=0)
+    g = torch.Generator().manual_seed(7)
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g) * 0.5).to(torch.bfloat16).view(torch.int16).cuda()
+    ring, act, dy, dh = rnd(rows, H), rnd(rows, I), rnd(rows, H), rnd(rows, 2 * I)
+    offsets = torch.tensor([0, 100, 5000, 5001, 90000], dtype=torch.int32, device="cuda")
+    wsb = mok.mok_wgrad_workspace_size(d, rows)
+    guard = 1 << 16
+    buf = torch.full((wsb + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    wws = buf[guard:guard + wsb]
+    dwgu = torch.full((n_local, 2 * I, H), SENTINEL, dtype=torch.int16, device="cuda")
+    dwd = torch.full((n_local, H, I), SENTINEL, dtype=torch.int16, device="cuda")
+    mok.mok_expert_wgrad(d, ring, rows, act, rows, dy, dh, rows, offsets, dwgu, dwd, wws)
+    torch.cuda.synchronize()
+    for t in (dwgu, dwd):
+        v = t.view(torch.bfloat16).float()
+        assert torch.isfinite(v).all()
+    assert int((buf[:guard] != 0x5A).sum()) == 0 and int((buf[guard + wsb:] != 0x5A).sum()) == 0

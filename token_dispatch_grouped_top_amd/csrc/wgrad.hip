@@ -23,15 +23,24 @@ using namespace gemm;
 constexpr int kPadK = 32;         // padded slot axis granularity (one bf16 k-step)
 
 // poff[e] = sum over e' < e of max(32, 32 * ceil(count_e' / 32)); one thread.
-__global__ void k_pad_offsets(const int32_t* __restrict__ offsets, int32_t n_local,
+__global__ void k_pad_offsets(const int32_t* __restrict__ offsets, int32_t n_local, int32_t kpad,
                               int32_t* __restrict__ poff) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int32_t acc = 0;
+  bool fits = true;
+  for (int e = 0; e < n_local && fits; ++e) {
+    const int32_t c = offsets[e + 1] - offsets[e];
+    if (c > kpad) { fits = false; break; }
+    acc += c > 0 ? (c + kPadK - 1) / kPadK * kPadK : kPadK;
+    fits = acc <= kpad;
+  }
+  // Counts past the padded axis (offsets claiming more than rows slots) give
+  // every expert one segment of kPadK slots, so no read leaves the buffers.
+  acc = 0;
   for (int e = 0; e < n_local; ++e) {
     poff[e] = acc;
     const int32_t c = offsets[e + 1] - offsets[e];
-    const int32_t p = c > 0 ? (c + kPadK - 1) / kPadK * kPadK : kPadK;
-    acc += p;
+    acc += fits && c > 0 ? (c + kPadK - 1) / kPadK * kPadK : kPadK;
   }
   poff[n_local] = acc;
 }
@@ -163,7 +172,7 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   void* xT = w; w += al(static_cast<size_t>(kp) * a.H * 2);
   void* dhT = w; w += al(static_cast<size_t>(kp) * 2 * a.I * 2);
   void* aT = w;
-  hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, a.n_local, poff);
+  hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, a.n_local, kp, poff);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = launch_transpose(a.dy, a.rows, a.H, a.offsets, poff, a.n_local, kp, true, dyT, s);
   if (e == hipSuccess) e = launch_transpose(a.act, a.act_rows, a.I, a.offsets, poff, a.n_local, kp, false, aT, s);
