@@ -22,6 +22,16 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
+// (bv, be) <- the better of its own pair and the pair of the lane that DPP
+// control CTRL names (every lane has a source under the row patterns used).
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& bv, int& be) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+}
+
 // Picks and gates of token t from its logits v (lane l holds logits l,
 // l + 64, ...; -inf past E).  All 64 lanes call it.
 template <int VPL>
@@ -40,11 +50,24 @@ __device__ __forceinline__ void pick_topk(const float (&v)[VPL], int32_t E, int3
       int e = lane + kWave * i;
       if (!((taken >> i) & 1ull) && e < E && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
     }
+    // best of the wave: within each 16-lane row by DPP (xor 1, xor 2, then
+    // lane i with 7 - i and with 15 - i), then the four rows' results read
+    // into scalars.  `better` is a total order, so the steps' order does not
+    // change the pick.
+    best_dpp<0xB1>(bv, be);                              // quad_perm [1,0,3,2]
+    best_dpp<0x4E>(bv, be);                              // quad_perm [2,3,0,1]
+    best_dpp<0x141>(bv, be);                             // row_half_mirror
+    best_dpp<0x140>(bv, be);                             // row_mirror
+    {
+      float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+      int re = __builtin_amdgcn_readlane(be, 0);
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oe = __shfl_xor(be, off);
-      if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+      for (int row = 1; row < 4; ++row) {
+        const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * row));
+        const int oe = __builtin_amdgcn_readlane(be, 16 * row);
+        if (better(ov, oe, rv, re)) { rv = ov; re = oe; }
+      }
+      bv = rv; be = re;
     }
     if ((be & (kWave - 1)) == lane) taken |= 1ull << (be / kWave);
     if (lane == j) { mine = bv; mine_e = be; }
