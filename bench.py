@@ -37,9 +37,9 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 738616935),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 990404317),
-    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("4e6c78d6035e4a55", 381085806),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("2ad9731a5b564065", 738608725),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("2ad9731a5b564065", 990437491),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("2ad9731a5b564065", 381108334),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
@@ -242,6 +242,7 @@ def time_backward(mok, dw, st, reps: int = 10):
     dwgu = torch.empty((wl.n_local, 2 * I, H), dtype=torch.int16, device="cuda")
     dwd = torch.empty((wl.n_local, H, I), dtype=torch.int16, device="cuda")
     wws = torch.empty(mok.mok_wgrad_workspace_size(d, cap), dtype=torch.uint8, device="cuda")
+    hsv = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
     calls = {
         "combine_bwd": lambda: mok.mok_combine_backward(dout, st.y, cap, st.aos, st.offsets,
                                                         wl.n_local, cap, dw.topk_gate, k, H, dy,
@@ -252,6 +253,15 @@ def time_backward(mok, dw, st, reps: int = 10):
                                                           cap, st.soa, k, H, dx, st.status),
         "wgrad": lambda: mok.mok_expert_wgrad(d, st.ring, cap, st.act, cap, dy, dh, cap, st.offsets,
                                               dwgu, dwd, wws),
+        # h kept by the forward instead of recomputed: the forward's gate/up that also
+        # stores h (timed whole, to set against the plain gate/up), then the backward from it
+        "gate_up_save_h": lambda: mok.mok_expert_gate_up_save_h(d, st.ring, cap, st.offsets, 0, cap,
+                                                                st.w_gu, st.act, cap, hsv,
+                                                                st.gemm_ws),
+        "gate_up_plain": lambda: mok.mok_expert_gate_up(d, st.ring, None, cap, st.offsets, 0, cap,
+                                                        st.w_gu, st.act, None, cap, st.gemm_ws),
+        "ffn_bwd_saved": lambda: mok.mok_expert_ffn_backward_saved(d, dy, st.offsets, 0, cap, gu_t,
+                                                                   d_t, hsv, dh, dxs, cap),
     }
     out = {}
     for name, f in calls.items():
@@ -268,6 +278,10 @@ def time_backward(mok, dw, st, reps: int = 10):
     out["ffn_bwd_tflops"] = round(flop / (out["ffn_bwd"] * 1e-3) / 1e12, 1)
     out["wgrad_tflops"] = round(6.0 * R * H * I / (out["wgrad"] * 1e-3) / 1e12, 1)
     out["total_ms"] = round(out["combine_bwd"] + out["ffn_bwd"] + out["dispatch_bwd"] + out["wgrad"], 4)
+    # with h saved: the backward drops the recompute, the forward pays the extra h stores
+    out["total_saved_ms"] = round(out["combine_bwd"] + out["ffn_bwd_saved"] + out["dispatch_bwd"] +
+                                  out["wgrad"], 4)
+    out["save_h_forward_extra_ms"] = round(out["gate_up_save_h"] - out["gate_up_plain"], 4)
     return out
 
 

@@ -348,6 +348,28 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
                                    void* h, void* dh, void* dx_slots, int32_t rows,
                                    hipStream_t stream);
 
+/* The forward's gate/up + SwiGLU (as mok_expert_gate_up, bf16 tokens and
+ * weights only) that also stores h = [g, u]: bf16 [act_rows][2I], row-major,
+ * row = the act row of the slot (s % act_rows), so the backward can take h
+ * instead of recomputing it (mok_expert_ffn_backward_saved).  act is
+ * bit-identical to mok_expert_gate_up's, h to the recompute's.  Costs 2I
+ * bf16 per row of extra writes.  Either buffer at 4 GiB or more:
+ * MOK_ERR_UNSUPPORTED. */
+mok_status mok_expert_gate_up_save_h(const mok_layer_desc* desc, const void* ring,
+                                     int32_t ring_slots, const int32_t* offsets,
+                                     int32_t slot_begin, int32_t slot_end, const void* w_gate_up,
+                                     void* act, int32_t act_rows, void* h, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* mok_expert_ffn_backward with h taken from mok_expert_gate_up_save_h
+ * (rows = the forward's act_rows) instead of recomputed: the down dgrad with
+ * the SwiGLU backward, then the gate/up dgrad; same outputs, bit for bit. */
+mok_status mok_expert_ffn_backward_saved(const mok_layer_desc* desc, const void* dy,
+                                         const int32_t* offsets, int32_t slot_begin,
+                                         int32_t slot_end, const void* packed_gate_up_t,
+                                         const void* packed_down_t, const void* h, void* dh,
+                                         void* dx_slots, int32_t rows, hipStream_t stream);
+
 /* Weight gradients over every routed slot s < R = offsets[n_local], per local
  * expert e (slots offsets[e] .. offsets[e+1] - 1):
  *   dW_down[e]    = sum_s dy_s a_s^T      bf16 [n_local][H][I]

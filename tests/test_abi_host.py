@@ -170,3 +170,25 @@ def test_gemm_operand_limits_and_workspace_checks():
     assert mok.mok_gemm_workspace_size() > 0
     assert L.mok_expert_down(C.byref(d), 1, None, 8, 1, 0, 8, 1, 1, 8, 1, 1024, None) == \
         mok.MOK_ERR_WORKSPACE
+
+
+def test_saved_h_calls_validate_before_launch():
+    E = mok.MOK_ERR_INVALID_ARG
+    d = mok.mok_layer_desc(hidden=256, inter=128, n_experts=8, top_k=2, expert_base=0, n_local=4,
+                           act_format=mok.MOK_ACT_BF16, weight_format=0)
+    dmx = mok.mok_layer_desc(hidden=256, inter=128, n_experts=8, top_k=2, expert_base=0,
+                             n_local=4, act_format=mok.MOK_ACT_MXFP8_E4M3, weight_format=0)
+    # gate/up keeping h: bf16 only, h required
+    assert L.mok_expert_gate_up_save_h(C.byref(dmx), 1, 64, 1, 0, 64, 1, 1, 64, 1, None, 0,
+                                       None) == E
+    assert L.mok_expert_gate_up_save_h(C.byref(d), 1, 64, 1, 0, 64, 1, 1, 64, None, None, 0,
+                                       None) == E
+    assert L.mok_expert_gate_up_save_h(C.byref(d), 1, 64, 1, 5, 4, 1, 1, 64, 1, None, 0,
+                                       None) == E
+    # backward from a saved h: every buffer required, bf16 only
+    assert L.mok_expert_ffn_backward_saved(C.byref(d), 1, 1, 0, 64, 1, 1, None, 1, 1, 64,
+                                           None) == E
+    assert L.mok_expert_ffn_backward_saved(C.byref(dmx), 1, 1, 0, 64, 1, 1, 1, 1, 1, 64,
+                                           None) == E
+    assert L.mok_expert_ffn_backward_saved(C.byref(d), 1, 1, 0, 64, 1, 1, 1, 1, 1, 0,
+                                           None) == E

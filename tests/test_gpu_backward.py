@@ -172,3 +172,44 @@ def test_wgrad_offsets_past_rows_stay_in_bounds():
         v = t.view(torch.bfloat16).float()
         assert torch.isfinite(v).all()
     assert int((buf[:guard] != 0x5A).sum()) == 0 and int((buf[guard + wsb:] != 0x5A).sum()) == 0
+
+
+@pytest.mark.parametrize("name,packed", [("ragged", 0), ("wide", 1)])
+def test_saved_h_matches_recompute(name, packed):
+    """mok_expert_gate_up_save_h stores act bit-identical to mok_expert_gate_up
+    and h bit-identical to the backward's recompute; the backward fed that h
+    (mok_expert_ffn_backward_saved) gives dh and dx bit-identical to the
+    recomputing one."""
+    import token_dispatch_grouped_top_amd as mok
+    wl = _case(name)
+    dw = DeviceWorkload(wl)
+    H, I, k = wl.H, wl.I, wl.k
+    s = dw.schedule(dw.topk_idx)
+    R = int(to_host(s["offsets"])[-1])
+    d = dw.desc(weights_packed=packed)
+    w_gu, _ = dw.weights(d)
+    ring = torch.zeros((R, H), dtype=torch.int16, device="cuda")
+    mok.mok_dispatch_gather(dw.x, H, k, s["aos"], s["offsets"], wl.n_local, 0, R, ring, None, R,
+                            mok.MOK_ACT_BF16)
+    act1 = torch.full((R, I), SENTINEL, dtype=torch.int16, device="cuda")
+    act2 = torch.full((R, I), SENTINEL, dtype=torch.int16, device="cuda")
+    hs = torch.full((R, 2 * I), SENTINEL, dtype=torch.int16, device="cuda")
+    mok.mok_expert_gate_up(d, ring, None, R, s["offsets"], 0, R, w_gu, act1, None, R)
+    mok.mok_expert_gate_up_save_h(d, ring, R, s["offsets"], 0, R, w_gu, act2, R, hs)
+    gu_t_b, d_t_b = mok.mok_packed_weights_bwd_size(d)
+    gu_t = torch.empty(gu_t_b, dtype=torch.uint8, device="cuda")
+    d_t = torch.empty(d_t_b, dtype=torch.uint8, device="cuda")
+    mok.mok_pack_weights_bwd(d, dw.w_gu, dw.w_d, gu_t, d_t)
+    g = torch.Generator().manual_seed(900 + R)
+    dy = (torch.randn(R, H, generator=g) * 0.5).to(torch.bfloat16).view(torch.int16).cuda()
+    h1 = torch.zeros((R, 2 * I), dtype=torch.int16, device="cuda")
+    dh1 = torch.zeros((R, 2 * I), dtype=torch.int16, device="cuda")
+    dh2 = torch.zeros((R, 2 * I), dtype=torch.int16, device="cuda")
+    dx1, dx2 = empty_u16(R, H), empty_u16(R, H)
+    mok.mok_expert_ffn_backward(d, ring, R, dy, s["offsets"], 0, R, w_gu, gu_t, d_t, h1, dh1, dx1, R)
+    mok.mok_expert_ffn_backward_saved(d, dy, s["offsets"], 0, R, gu_t, d_t, hs, dh2, dx2, R)
+    torch.cuda.synchronize()
+    assert torch.equal(act1, act2)
+    assert torch.equal(h1, hs)
+    assert torch.equal(dh1, dh2)
+    assert torch.equal(dx1, dx2)

@@ -89,6 +89,10 @@ _SIGS = {
                                        _I32, _P, _P, _P]),
     "mok_expert_ffn_backward": (C.c_int, [_DESC, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P,
                                           _P, _P, _I32, _P]),
+    "mok_expert_gate_up_save_h": (C.c_int, [_DESC, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P,
+                                            _P, _SZ, _P]),
+    "mok_expert_ffn_backward_saved": (C.c_int, [_DESC, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
+                                                _I32, _P]),
     "mok_wgrad_workspace_size": (_SZ, [_DESC, _I32]),
     "mok_expert_wgrad": (C.c_int, [_DESC, _P, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ,
                                    _P]),
@@ -363,6 +367,26 @@ def mok_expert_ffn_backward(desc: mok_layer_desc, ring, ring_slots: int, dy, off
                                         _ptr(packed_gate_up_t), _ptr(packed_down_t), _ptr(h),
                                         _ptr(dh), _ptr(dx_slots), rows, _stream(stream)),
            "mok_expert_ffn_backward")
+
+
+def mok_expert_gate_up_save_h(desc: mok_layer_desc, ring, ring_slots: int, offsets,
+                              slot_begin: int, slot_end: int, w_gate_up, act, act_rows: int, h,
+                              ws=None, ws_bytes: Optional[int] = None, stream=None) -> None:
+    _check(_lib.mok_expert_gate_up_save_h(C.byref(desc), _ptr(ring), ring_slots, _ptr(offsets),
+                                          slot_begin, slot_end, _ptr(w_gate_up), _ptr(act),
+                                          act_rows, _ptr(h), _ptr(ws), _ws_bytes(ws, ws_bytes),
+                                          _stream(stream)),
+           "mok_expert_gate_up_save_h")
+
+
+def mok_expert_ffn_backward_saved(desc: mok_layer_desc, dy, offsets, slot_begin: int,
+                                  slot_end: int, packed_gate_up_t, packed_down_t, h, dh, dx_slots,
+                                  rows: int, stream=None) -> None:
+    _check(_lib.mok_expert_ffn_backward_saved(C.byref(desc), _ptr(dy), _ptr(offsets), slot_begin,
+                                              slot_end, _ptr(packed_gate_up_t),
+                                              _ptr(packed_down_t), _ptr(h), _ptr(dh),
+                                              _ptr(dx_slots), rows, _stream(stream)),
+           "mok_expert_ffn_backward_saved")
 
 
 def mok_wgrad_workspace_size(desc: mok_layer_desc, rows: int) -> int:

@@ -330,6 +330,31 @@ mok_status mok_expert_gate_up(const mok_layer_desc* desc, const void* ring,
   return hip_status(launch_gate_up(a, stream));
 }
 
+mok_status mok_expert_gate_up_save_h(const mok_layer_desc* desc, const void* ring,
+                                     int32_t ring_slots, const int32_t* offsets,
+                                     int32_t slot_begin, int32_t slot_end, const void* w_gate_up,
+                                     void* act, int32_t act_rows, void* h, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!desc_ok(desc) || desc->act_format != MOK_ACT_BF16 || desc->weight_format != MOK_W_BF16 ||
+      !ring || ring_slots < 1 || !offsets || slot_begin < 0 || slot_end < slot_begin ||
+      !w_gate_up || !act || act_rows < 1 || !h)
+    return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, ring_slots, act_rows) ||
+      static_cast<int64_t>(act_rows) * 2 * desc->inter * 2 >= (1ll << 32))
+    return MOK_ERR_UNSUPPORTED;
+  FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
+  a.ring = ring; a.ring_scales = nullptr; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up);
+  a.act = act; a.act_scales = nullptr; a.act_rows = act_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = MOK_ACT_BF16;
+  a.w_packed = desc->weights_packed; a.weight_format = MOK_W_BF16;
+  a.h_out = h;
+  return hip_status(launch_gate_up(a, stream));
+}
+
 mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const uint8_t* act_scales,
                            int32_t act_rows, const int32_t* offsets, int32_t slot_begin,
                            int32_t slot_end, const void* w_down, void* y, int32_t y_rows,
@@ -439,6 +464,28 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
   a.w_gu_t = static_cast<const uint16_t*>(packed_gate_up_t);
   a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
   a.dy = dy; a.h = h; a.dh = dh; a.dx = dx_slots; a.rows = rows;
+  a.H = desc->hidden; a.I = desc->inter;
+  return hip_status(launch_ffn_backward(a, stream));
+}
+
+mok_status mok_expert_ffn_backward_saved(const mok_layer_desc* desc, const void* dy,
+                                         const int32_t* offsets, int32_t slot_begin,
+                                         int32_t slot_end, const void* packed_gate_up_t,
+                                         const void* packed_down_t, const void* h, void* dh,
+                                         void* dx_slots, int32_t rows, hipStream_t stream) {
+  if (!bwd_desc_ok(desc) || !dy || !offsets || slot_begin < 0 || slot_end < slot_begin ||
+      !packed_gate_up_t || !packed_down_t || !h || !dh || !dx_slots || rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  const int64_t lim = 1ll << 32, H = desc->hidden, I = desc->inter;
+  if (static_cast<int64_t>(rows) * 2 * I * 2 >= lim || static_cast<int64_t>(rows) * H * 2 >= lim ||
+      4ll * I * H >= lim)
+    return MOK_ERR_UNSUPPORTED;
+  BwdArgs a{};
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu_t = static_cast<const uint16_t*>(packed_gate_up_t);
+  a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
+  a.dy = dy; a.h = const_cast<void*>(h); a.dh = dh; a.dx = dx_slots; a.rows = rows;
+  a.h_saved = 1;
   a.H = desc->hidden; a.I = desc->inter;
   return hip_status(launch_ffn_backward(a, stream));
 }

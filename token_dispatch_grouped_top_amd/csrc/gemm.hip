@@ -258,6 +258,10 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   set_split(g, a);
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
   if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_SWIGLU_MX>(g, n1, m_tiles, s);
+  if (a.h_out) {                   // bf16 tokens and weights (checked at the boundary)
+    g.H_out = static_cast<uint16_t*>(a.h_out);
+    return launch_one<false, EPI_SWIGLU_BF16_H>(g, n1, m_tiles, s);
+  }
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
                                              : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
 }
@@ -330,7 +334,7 @@ hipError_t launch_gate_up_dgrad(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_recompute_h(a, s);
+  hipError_t e = a.h_saved ? hipSuccess : launch_recompute_h(a, s);
   if (e == hipSuccess) e = launch_down_dgrad(a, s);
   if (e == hipSuccess) e = launch_gate_up_dgrad(a, s);
   return e;

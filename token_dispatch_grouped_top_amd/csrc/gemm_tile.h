@@ -72,10 +72,12 @@ static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LD
 // EPI_STORE_GU: a gate/up tile stores g and u themselves (h = [g, u], bf16
 // [c_rows][2 N] row-major) for that backward.
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2, EPI_SWIGLU_BWD = 3,
-           EPI_STORE_GU = 4 };
+           EPI_STORE_GU = 4,
+          EPI_SWIGLU_BF16_H = 5 };
 // Whether an epilogue pairs gate and up columns (the gate/up weight order).
 template <int EPI> constexpr bool epi_swiglu() {
-  return EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MX || EPI == EPI_STORE_GU;
+  return EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MX || EPI == EPI_STORE_GU ||
+         EPI == EPI_SWIGLU_BF16_H;
 }
 
 struct GemmParams {
@@ -98,6 +100,7 @@ struct GemmParams {
   int32_t a_row_base;         // A row of slot s: (s + a_row_base) % a_rows
   int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
   const uint16_t* H_src;      // EPI_SWIGLU_BWD: h = [g, u] bf16 [c_rows][2 N], row-major
+  uint16_t* H_out;            // EPI_SWIGLU_BF16_H: h = [g, u] bf16 [c_rows][2 N], row-major
   // Split of the last, partial round of tiles along K (standalone launches):
   float* part;                // [n_cus][BM * BN] fp32 partial tiles; null = no split
   int32_t* part_cnt;          // [n_cus] arrival counters, zero before and after a launch
@@ -454,6 +457,15 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
             a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
           const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
+          if constexpr (EPI == EPI_SWIGLU_BF16_H) {     // h kept for the backward
+            if (r < nrows && n0 + i < p.N) {
+              uint16_t* hrow = p.H_out + c_row_of(r) * (2 * static_cast<int64_t>(p.N));
+              *reinterpret_cast<uint2*>(hrow + n0 + i) =
+                  make_uint2(pack_bf16x2(g4.x, g4.y), pack_bf16x2(g4.z, g4.w));
+              *reinterpret_cast<uint2*>(hrow + p.N + n0 + i) =
+                  make_uint2(pack_bf16x2(u4.x, u4.y), pack_bf16x2(u4.z, u4.w));
+            }
+          }
           if (MXO) {
             *reinterpret_cast<float4*>(lds + r * RB + (((i >> 2) ^ (r & 15)) << 4)) =
                 make_float4(a[0], a[1], a[2], a[3]);

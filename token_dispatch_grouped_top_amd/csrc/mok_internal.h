@@ -179,6 +179,7 @@ struct FfnArgs {
   int32_t w_packed;           // weights in the packed tile order (launch_pack_weights)
   int32_t weight_format;      // MOK_W_MXFP8_E4M3: packed MXFP8 weights, both GEMMs in MXFP8
   SplitWs split;              // split.part null: every tile whole
+  void* h_out;                // non-null (bf16 only): the gate/up also stores h = [g, u]
 };
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
@@ -196,6 +197,7 @@ struct BwdArgs {
   const uint16_t* w_d_t;      // packed W_d^T
   const void* dy;             // column-blocked [rows][H]
   void* h; void* dh; void* dx;
+  int32_t h_saved;            // h already holds [g, u] from the forward: no recompute
   int32_t rows;
   int32_t H, I;
 };
