@@ -352,9 +352,12 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
  * weights only) that also stores h = [g, u]: bf16 [act_rows][2I], row-major,
  * row = the act row of the slot (s % act_rows), so the backward can take h
  * instead of recomputing it (mok_expert_ffn_backward_saved).  act is
- * bit-identical to mok_expert_gate_up's, h to the recompute's.  Costs 2I
- * bf16 per row of extra writes.  Either buffer at 4 GiB or more:
- * MOK_ERR_UNSUPPORTED. */
+ * bit-identical to mok_expert_gate_up's given the same workspace argument.
+ * Without a workspace, h is bit-identical to the backward's recompute; with
+ * one, tiles of a last, partial round may be split along K, and their h is
+ * then the rounding of the pieces' fp32 partial sums added in piece order (a
+ * different summation order, same bar).  Costs 2I bf16 per row of extra
+ * writes.  Either buffer at 4 GiB or more: MOK_ERR_UNSUPPORTED. */
 mok_status mok_expert_gate_up_save_h(const mok_layer_desc* desc, const void* ring,
                                      int32_t ring_slots, const int32_t* offsets,
                                      int32_t slot_begin, int32_t slot_end, const void* w_gate_up,
@@ -363,7 +366,8 @@ mok_status mok_expert_gate_up_save_h(const mok_layer_desc* desc, const void* rin
 
 /* mok_expert_ffn_backward with h taken from mok_expert_gate_up_save_h
  * (rows = the forward's act_rows) instead of recomputed: the down dgrad with
- * the SwiGLU backward, then the gate/up dgrad; same outputs, bit for bit. */
+ * the SwiGLU backward, then the gate/up dgrad; the same outputs, bit for bit,
+ * when h was kept without a K-split workspace. */
 mok_status mok_expert_ffn_backward_saved(const mok_layer_desc* desc, const void* dy,
                                          const int32_t* offsets, int32_t slot_begin,
                                          int32_t slot_end, const void* packed_gate_up_t,

@@ -54,9 +54,9 @@ def lib():
         L.orc_mx_quantize.argtypes = [P, i64, P, P]
         L.orc_mx_dequantize.argtypes = [P, P, i64, P]
         L.orc_gather_rows.argtypes = [P, i32, i32, P, P, i64, i32, P, P, P]
-        L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P, P, P, P, P]
+        L.orc_ffn_rows.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, P, P, P, P, P, P, P]
         L.orc_mx_quantize_rows_bf16.argtypes = [P, i64, i32, P, P]
-        L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i32, P, P]
+        L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i32, P, P, P]
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = C.c_int
         for f in ("orc_e4m3_encode_n", "orc_e4m3_decode_n", "orc_bf16_round_n",
@@ -205,11 +205,12 @@ def mx_quantize_rows(w_bits: np.ndarray):
 
 
 def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: bool,
-             mx_weights=None) -> np.ndarray:
+             mx_weights=None, exact: bool = False):
     """Expert SwiGLU FFN of dispatched rows -> y bf16 bits [n, H].
 
     mx_weights: None (bf16 weights) or ((gu_codes, gu_scales), (d_codes, d_scales)) from
-    mx_quantize_rows of w_gu and w_d, used in place of them."""
+    mx_quantize_rows of w_gu and w_d, used in place of them.
+    exact: also return the fp64 values before rounding, (y, a_exact [n, I], y_exact [n, H])."""
     w_gu = _c(w_gu, np.uint16)
     w_d = _c(w_d, np.uint16)
     I2, H = w_gu.shape[1], w_gu.shape[2]
@@ -217,6 +218,8 @@ def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: boo
     eor = _c(expert_of_row, np.int32).reshape(-1)
     n = eor.size
     y = np.empty((n, H), np.uint16)
+    a_ex = np.empty((n, I), np.float64) if exact else None
+    y_ex = np.empty((n, H), np.float64) if exact else None
     if mx_weights is None:
         wq = (None, None, None, None)
     else:
@@ -228,17 +231,18 @@ def ffn_rows(xrows, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray, mxfp8: boo
         codes = _c(codes, np.uint8)
         scales = _c(scales, np.uint8)
         lib().orc_ffn_rows(None, _p(codes), _p(scales), _p(eor), n, H, I, _p(w_gu), _p(w_d), 1,
-                           *wp, _p(y))
+                           *wp, _p(y), _p(a_ex), _p(y_ex))
     else:
         xb = _c(xrows, np.uint16)
         lib().orc_ffn_rows(_p(xb), None, None, _p(eor), n, H, I, _p(w_gu), _p(w_d), 0, *wp,
-                           _p(y))
-    return y
+                           _p(y), _p(a_ex), _p(y_ex))
+    return (y, a_ex, y_ex) if exact else y
 
 
 def combine_tokens(y: np.ndarray, y_row_of_slot: np.ndarray, slot_of_assign: np.ndarray,
-                   topk_gate: np.ndarray, tokens, k: int):
-    """Weighted merge for the listed tokens -> (out bf16 [n,H], written bool [n])."""
+                   topk_gate: np.ndarray, tokens, k: int, exact: bool = False):
+    """Weighted merge for the listed tokens -> (out bf16 [n,H], written bool [n]), plus the
+    fp64 sums before rounding (out_exact [n, H]) when exact."""
     y = _c(y, np.uint16)
     H = y.shape[1]
     yr = _c(y_row_of_slot, np.int64)
@@ -248,9 +252,10 @@ def combine_tokens(y: np.ndarray, y_row_of_slot: np.ndarray, slot_of_assign: np.
     n = tokens.size
     out = np.zeros((n, H), np.uint16)
     written = np.zeros(n, np.uint8)
+    o_ex = np.zeros((n, H), np.float64) if exact else None
     lib().orc_combine_tokens(_p(y), _p(yr), _p(soa), _p(gate), _p(tokens), n, k, H,
-                             _p(out), _p(written))
-    return out, written.astype(bool)
+                             _p(out), _p(written), _p(o_ex))
+    return (out, written.astype(bool), o_ex) if exact else (out, written.astype(bool))
 
 
 def expert_of_slots(offsets: np.ndarray, slots) -> np.ndarray:
@@ -268,7 +273,8 @@ def forward(wl, tokens=None, slots_extra=None) -> Dict[str, np.ndarray]:
     and combine for the listed pool tokens (all tokens when ``tokens`` is
     None).  Only the slots those tokens need are computed, plus
     ``slots_extra`` if given.  Returns routing, schedule, the y rows of the
-    computed slots and the merged output rows.
+    computed slots and the merged output rows, and the fp64 values before their
+    rounding (a_exact, y_exact per computed slot, out_exact per listed token).
     """
     res: Dict[str, np.ndarray] = {}
     if wl.routing_from_logits:
@@ -294,11 +300,12 @@ def forward(wl, tokens=None, slots_extra=None) -> Dict[str, np.ndarray]:
     mxw = None
     if getattr(wl, "weight_format", 0) == 1:
         mxw = (mx_quantize_rows(wl.w_gu), mx_quantize_rows(wl.w_d))
-    y = ffn_rows(xr, eor, wl.w_gu, wl.w_d, mx, mx_weights=mxw)
+    y, a_ex, y_ex = ffn_rows(xr, eor, wl.w_gu, wl.w_d, mx, mx_weights=mxw, exact=True)
     y_row_of_slot = np.full(max(sch["R"], 1), -1, np.int64)
     y_row_of_slot[slots] = np.arange(slots.size)
-    out, written = combine_tokens(y, y_row_of_slot, soa, gate, tokens, k)
-    res.update(slots=slots, x_rows=xr, y=y, tokens=tokens, out=out, written=written)
+    out, written, o_ex = combine_tokens(y, y_row_of_slot, soa, gate, tokens, k, exact=True)
+    res.update(slots=slots, x_rows=xr, y=y, tokens=tokens, out=out, written=written,
+               a_exact=a_ex, y_exact=y_ex, out_exact=o_ex, expert_of_slot=eor)
     return res
 
 
@@ -364,7 +371,8 @@ def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     routed slot s of token t, pick j, gate w: dy_s = w dout[t] and
     dgate[t, j] = <dout[t], y_s>; dx_s through ffn_backward_values; and
     dx[t] = sum over t's local slots of dx_s.  fp64 throughout.  Returns
-    dy [R, H], dgate [T, k] (NaN where not local), dx [T, H] and written [T]."""
+    dy [R, H], dgate [T, k] (NaN where not local), dx [T, H] and written [T], and per
+    slot the forward's rows: x_rows (bf16 bits), h = [g, u] and a (fp64), y (bf16)."""
     idx, gate = (route_topk(wl.logits, wl.k) if wl.routing_from_logits
                  else (wl.topk_idx, wl.topk_gate))
     sch = build_schedule(idx, wl.expert_base, wl.n_local)
@@ -387,6 +395,13 @@ def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     written = (soa.reshape(T, wl.k) >= 0).any(axis=1)
     dw_gu, dw_d = ffn_wgrad_values(bf16_value(xr), eos, bf16_value(wl.w_gu).astype(np.float64),
                                    dy, dh, wl.n_local, wl.H)
+    xv = bf16_value(xr).astype(np.float64)
+    wgu = bf16_value(wl.w_gu).astype(np.float64)
+    h = np.zeros((R, 2 * wl.I))
+    for e in np.unique(eos):
+        r = np.nonzero(eos == e)[0]
+        h[r] = xv[r] @ wgu[e].T
+    a = silu_and_grad(h[:, :wl.I])[0] * h[:, wl.I:]
     return {"R": R, "dy": dy, "dgate": dgate.reshape(idx.shape), "dx": dx, "written": written,
             "y": y, "dh": dh, "expert_of_slot": eos, "token_of_slot": t_of, "dw_d": dw_d,
-            "dw_gu": dw_gu}
+            "dw_gu": dw_gu, "x_rows": xr, "h": h, "a": a}

@@ -22,10 +22,13 @@
  * assignment id a = t*k + j; SwiGLU a = SiLU(g)*u with gate rows first and no
  * biases; OCP MX v1.0 E4M3 blocks of 32 along the contraction dimension.
  *
- * Arithmetic: fp64 throughout.  Values whose rounding the kernel decides in
- * fp32 (the SwiGLU activation and the expert output) are first taken to
- * fp32 and then rounded to the storage format, so the oracle makes that
- * decision in the kernel's precision.
+ * Arithmetic: fp64 throughout.  Each stored value (the SwiGLU activation,
+ * the expert output, the merged output) is rounded once, from its fp64
+ * value, to the storage format (bf16 round-to-nearest-even, or the MX
+ * quantiser).  The fp64 values before that rounding can be returned too
+ * (a_exact, y_exact, out_exact): tests use them to tell where a rounding
+ * decision is close enough to a tie that an independently accumulated value
+ * may legitimately land on the neighbouring code.
  *
  * Parity pins: every function below is pinned by tests/test_oracle_*.py
  * against brute force, library routines (numpy/torch) or closed forms.
@@ -336,8 +339,10 @@ static double w_value(const uint16_t* wb, const uint8_t* wc, const uint8_t* ws, 
 /* MXFP8 datapath).  Row r belongs to local expert expert_of_row[r]:      */
 /*   h = W_gu[e] . x   (W_gu rows 0..I-1 = gate, I..2I-1 = up; no bias)   */
 /*   a_i = SiLU(h_i) * h_{I+i},  SiLU(z) = z / (1 + exp(-z))              */
-/*   a -> fp32 -> bf16 (or MXFP8 blocks of 32 along I, then dequantised)  */
-/*   y = W_d[e] . a  -> fp32 -> bf16                                       */
+/*   a -> bf16 (or MXFP8 blocks of 32 along I, then dequantised)          */
+/*   y = W_d[e] . a  -> bf16                                               */
+/* a_exact [n][I] / y_exact [n][H] (optional, may be NULL): the fp64      */
+/* values of a and y before their rounding.                                */
 /* x rows are bf16 bits (xb) or MXFP8 codes + scales (xc, xs).  Weights   */
 /* are bf16 (w_gu, w_d) or, when gu_c is not null, MXFP8 codes + scales   */
 /* of the same matrices (gu_c/gu_s [n_local*2I][H], d_c/d_s [n_local*H][I]).*/
@@ -346,7 +351,7 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
                           const int32_t* expert_of_row, int64_t n, int32_t H, int32_t I,
                           const uint16_t* w_gu, const uint16_t* w_d, int32_t mxfp8,
                           const uint8_t* gu_c, const uint8_t* gu_s, const uint8_t* d_c,
-                          const uint8_t* d_s, uint16_t* y)
+                          const uint8_t* d_s, uint16_t* y, double* a_exact, double* y_exact)
 {
     #pragma omp parallel
     {
@@ -370,8 +375,9 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
                     u += w_value(w_gu, gu_c, gu_s, gbase + I + i, H, h) * xv[h];
                 }
                 double silu = g / (1.0 + exp(-g));
-                a[i] = (double)(float)(silu * u);
+                a[i] = silu * u;
             }
+            if (a_exact) memcpy(a_exact + r * (int64_t)I, a, sizeof(double) * (size_t)I);
             if (!mxfp8) {
                 for (int i = 0; i < I; ++i) a[i] = round_bf16(a[i]);
             } else {
@@ -382,7 +388,8 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
             for (int h = 0; h < H; ++h) {
                 double acc = 0.0;
                 for (int i = 0; i < I; ++i) acc += w_value(w_d, d_c, d_s, dbase + h, I, i) * a[i];
-                y[r * (int64_t)H + h] = bf16_bits(round_bf16((double)(float)acc));
+                if (y_exact) y_exact[r * (int64_t)H + h] = acc;
+                y[r * (int64_t)H + h] = bf16_bits(round_bf16(acc));
             }
         }
         free(xv); free(a); free(ac); free(as);
@@ -396,12 +403,13 @@ ORC_API void orc_ffn_rows(const uint16_t* xb, const uint8_t* xc, const uint8_t* 
 /* assignment: out = bf16( sum over local j ascending of gate_tj * y[slot]*/
 /* ).  y_of_slot(s) is row y_row_of_slot[s] of y (so callers may pass     */
 /* only sampled rows).  Tokens without a local assignment are skipped     */
-/* (written[r] = 0) and their rows are left untouched.                    */
+/* (written[r] = 0) and their rows are left untouched.  out_exact         */
+/* (optional) receives the fp64 sums before rounding.                     */
 /* ------------------------------------------------------------------ */
 ORC_API void orc_combine_tokens(const uint16_t* y, const int64_t* y_row_of_slot,
                                 const int32_t* slot_of_assign, const float* topk_gate,
                                 const int64_t* tokens, int64_t n, int32_t k, int32_t H,
-                                uint16_t* out, uint8_t* written)
+                                uint16_t* out, uint8_t* written, double* out_exact)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
@@ -417,7 +425,8 @@ ORC_API void orc_combine_tokens(const uint16_t* y, const int64_t* y_row_of_slot,
                 if (s < 0) continue;
                 acc += (double)topk_gate[t * k + j] * bf16_value(y[y_row_of_slot[s] * H + h]);
             }
-            out[r * (int64_t)H + h] = bf16_bits(round_bf16((double)(float)acc));
+            if (out_exact) out_exact[r * (int64_t)H + h] = acc;
+            out[r * (int64_t)H + h] = bf16_bits(round_bf16(acc));
         }
     }
 }

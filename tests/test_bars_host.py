@@ -1,0 +1,191 @@
+"""CPU checks of the parity bars in tests/bars.py.
+
+The bars must (1) accept what a legitimate device computes -- here an
+independent fp32 evaluation of the same steps with bf16 stores, whose sums
+(numpy's fp32 matrix products) round after every product rather than once
+per 16-product MFMA step, so it is noisier than the device -- and (2) reject
+results that are wrong: a single element one bf16 step off where the oracle's
+value is not near a tie, and any result 10 % off.
+"""
+import numpy as np
+import pytest
+
+import bars
+import oracle
+import workloads as W
+
+
+def _f32(v):
+    return np.asarray(v, np.float64).astype(np.float32)
+
+
+def _bits(v64):
+    return (np.asarray(v64, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _sim_forward(wl, r):
+    """fp32 evaluation of the gate/up, SwiGLU and down of the oracle's computed
+    slots, with the stores of a (bf16, or MX quantised from the fp32 values)
+    and y (bf16); fp32 merge of the listed tokens."""
+    xv, wgu, wd = bars.layer_values(wl, r["x_rows"])
+    x = _f32(xv)
+    eor, I = r["expert_of_slot"], wl.I
+    a_all = np.empty((x.shape[0], I))
+    y = np.empty((x.shape[0], wl.H))
+    for e in np.unique(eor):
+        rr = np.nonzero(eor == e)[0]
+        gu = x[rr] @ _f32(wgu[e]).T
+        g, u = gu[:, :I], gu[:, I:]
+        a = (g * (np.float32(1) / (np.float32(1) + np.exp(-g))) * u).astype(np.float64)
+        if wl.act_format == 1:
+            a_all[rr] = bars._mx_blocks(a, bars._mx_exps(a))
+        else:
+            a_all[rr] = bars.bf16_rne(a)
+        y[rr] = bars.bf16_rne(_f32(a_all[rr]) @ _f32(wd[e]).T)
+    row = np.full(r["R"], -1)
+    row[r["slots"]] = np.arange(r["slots"].size)
+    soa = r["slot_of_assign"].reshape(-1, wl.k)[r["tokens"]]
+    gt = r["topk_gate"].reshape(-1, wl.k)[r["tokens"]]
+    acc = np.zeros((len(r["tokens"]), wl.H), np.float32)
+    for j in range(wl.k):
+        m = soa[:, j] >= 0
+        acc[m] = gt[m, j, None] * _f32(y[row[soa[m, j]]]) + acc[m]
+    return a_all, y, bars.bf16_rne(acc)
+
+
+@pytest.fixture(scope="module")
+def fwd():
+    wl = W.small_pool(23, n_partitions=4, part_rows=250, H=576, I=320, E=32, k=4,
+                      expert_base=3, counts=[300, 17, 0, 260, 1])
+    r = oracle.forward(wl)
+    y_lo, y_hi, o_lo, o_hi = bars.forward_band(wl, r)
+    a_sim, y_sim, out_sim = _sim_forward(wl, r)
+    return wl, r, (y_lo, y_hi, o_lo, o_hi), (a_sim, y_sim, out_sim)
+
+
+def test_band_accepts_fp32_evaluation(fwd):
+    wl, r, (y_lo, y_hi, o_lo, o_hi), (_, y_sim, out_sim) = fwd
+    st = bars.band_stats(_bits(y_sim), r["y"], y_lo, y_hi, 2e-2, "fp32 y")
+    assert st["differ"] > 0                     # the evaluation does land on neighbours
+    assert st["flagged"] < 0.1 * st["n"]        # and the band is far from blanket
+    wr = r["written"]
+    bars.band_stats(_bits(out_sim)[wr], r["out"][wr], o_lo[wr], o_hi[wr], 2e-2, "fp32 out")
+
+
+@pytest.mark.parametrize("wfmt", [0, 1])
+def test_band_accepts_fp32_evaluation_mxfp8(wfmt):
+    """MXFP8 activations (E4M3 codes and block scales decided on the fp32
+    values), with bf16 or MXFP8 weights."""
+    wl = W.small_pool(25, n_partitions=4, part_rows=250, H=576, I=320, E=32, k=4,
+                      expert_base=3, counts=[300, 17, 0, 260, 1], act_format=W.ACT_MXFP8)
+    wl.weight_format = wfmt
+    r = oracle.forward(wl)
+    y_lo, y_hi, o_lo, o_hi = bars.forward_band(wl, r)
+    _, y_sim, out_sim = _sim_forward(wl, r)
+    st = bars.band_stats(_bits(y_sim), r["y"], y_lo, y_hi, 6e-2, f"fp32 y, MXFP8 w{wfmt}")
+    assert st["differ"] > 0
+    wr = r["written"]
+    bars.band_stats(_bits(out_sim)[wr], r["out"][wr], o_lo[wr], o_hi[wr], 6e-2,
+                    f"fp32 out, MXFP8 w{wfmt}")
+
+
+def test_band_rejects_a_step_off_tie_and_ten_percent(fwd):
+    wl, r, (y_lo, y_hi, o_lo, o_hi), _ = fwd
+    ref = bars.bf16_values(r["y"])
+    exact = np.argwhere(y_lo == y_hi)
+    i = tuple(exact[len(exact) // 2])
+    bad = ref.copy()
+    bad[i] = np.nextafter(np.float32(ref[i]), np.float32(np.inf) * np.sign(ref[i] or 1.0))
+    bad[i] = bars.bf16_rne(bad[i] + np.sign(ref[i] or 1.0) * abs(ref[i]) * 2.0 ** -8)
+    assert bad[i] != ref[i]
+    with pytest.raises(AssertionError):
+        bars.band_stats(_bits(bad), r["y"], y_lo, y_hi, 2e-2, "one step off")
+    wr = r["written"]
+    o = bars.bf16_values(r["out"]).copy()
+    k = np.argmax(np.abs(o[wr]).reshape(-1) > 0)
+    flat = o[wr].reshape(-1)
+    flat[k] *= 1.1
+    with pytest.raises(AssertionError):
+        bars.band_stats(_bits(flat.reshape(o[wr].shape)), r["out"][wr], o_lo[wr], o_hi[wr], 2e-2,
+                        "10 % off")
+
+
+def _sim_backward(wl, ref, dout_bits, y_sim):
+    """fp32 evaluation of the backward chain with the device's bf16 stores:
+    dy, h = [g, u], dh, dx_s, dx, a; dgate from the forward's (simulated) y."""
+    I, R = wl.I, ref["R"]
+    eos, t_of = ref["expert_of_slot"], ref["token_of_slot"]
+    dout = _f32(bars.bf16_values(dout_bits))
+    sch = oracle.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)
+    wslot = _f32(wl.topk_gate).reshape(-1)[sch["assign_of_slot"]]
+    dy = bars.bf16_rne(wslot[:, None] * dout[t_of])
+    dgate = (dout[t_of] * _f32(y_sim)).sum(1, dtype=np.float32)
+    x = _f32(bars.bf16_values(ref["x_rows"]))
+    dh = np.empty((R, 2 * I))
+    dxs = np.empty((R, wl.H))
+    a = np.empty((R, I))
+    for e in np.unique(eos):
+        r = np.nonzero(eos == e)[0]
+        wgu = _f32(bars.bf16_values(wl.w_gu[e]))
+        wd = _f32(bars.bf16_values(wl.w_d[e]))
+        h = bars.bf16_rne(x[r] @ wgu.T)
+        g, u = _f32(h[:, :I]), _f32(h[:, I:])
+        s = np.float32(1) / (np.float32(1) + np.exp(-g))
+        da = _f32(dy[r]) @ wd
+        dh[r] = bars.bf16_rne(np.concatenate([da * u * s * (1 + g * (1 - s)), da * g * s], 1))
+        dxs[r] = bars.bf16_rne(_f32(dh[r]) @ wgu)
+        gu = x[r] @ wgu.T
+        a[r] = bars.bf16_rne(gu[:, :I] * (np.float32(1) / (np.float32(1) + np.exp(-gu[:, :I]))) *
+                             gu[:, I:])
+    dx = np.zeros((wl.T, wl.H), np.float32)
+    np.add.at(dx, t_of, _f32(dxs))
+    dwd = np.zeros((wl.n_local, wl.H, I))
+    dwg = np.zeros((wl.n_local, 2 * I, wl.H))
+    for e in range(wl.n_local):
+        r = np.nonzero(eos == e)[0]
+        dwd[e] = bars.bf16_rne(_f32(dy[r]).T @ _f32(a[r]))
+        dwg[e] = bars.bf16_rne(_f32(dh[r]).T @ x[r])
+    return dgate, bars.bf16_rne(dx), dwd, dwg
+
+
+def test_backward_bars_accept_fp32_and_reject_ten_percent():
+    wl = W.small_pool(81, n_partitions=4, part_rows=250, H=576, I=320, E=32, k=4,
+                      expert_base=3, counts=[300, 17, 0, 260, 1])
+    dout = W.normal_bf16(np.random.SeedSequence(577), wl.T * wl.H, 1.0).reshape(wl.T, wl.H)
+    ref = oracle.backward(wl, dout)
+    R = ref["R"]
+    eos, t_of = ref["expert_of_slot"], ref["token_of_slot"]
+    sch = oracle.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)
+    aos = sch["assign_of_slot"]
+    _, a_ex, y_ex = oracle.ffn_rows(ref["x_rows"], eos, wl.w_gu, wl.w_d, False, exact=True)
+    y_lo, y_hi, _ = bars.layer_y_band(wl, ref["x_rows"], eos, a_ex, y_ex)
+    r = dict(x_rows=ref["x_rows"], expert_of_slot=eos, R=R, slots=np.arange(R),
+             slot_of_assign=sch["slot_of_assign"], topk_gate=wl.topk_gate,
+             tokens=np.arange(wl.T))
+    _, y_sim, _ = _sim_forward(wl, r)
+    dgate, dx, dwd, dwg = _sim_backward(wl, ref, dout, y_sim)
+    # dgate
+    dv = bars.bf16_values(dout)[t_of]
+    g_lo, g_hi = bars.dgate_band(dv, y_lo, y_hi)
+    g_ref = ref["dgate"].reshape(-1)[aos]
+    assert np.all((dgate >= g_lo) & (dgate <= g_hi))
+    assert np.all((g_ref >= g_lo) & (g_ref <= g_hi))
+    off = g_ref * 1.1
+    typical = np.abs(g_ref) > 0.01 * np.abs(g_ref).max()     # not a cancellation
+    assert np.all(((off < g_lo) | (off > g_hi))[typical])
+    # dx
+    xv = bars.bf16_values(ref["x_rows"])
+    s_dh, s_dxs = bars.ffn_backward_sigma(xv, eos, bars.bf16_values(wl.w_gu),
+                                          bars.bf16_values(wl.w_d), ref["dy"], ref["h"], ref["dh"])
+    bar = bars.dx_bar(s_dxs, t_of, ref["dx"])
+    wr = ref["written"]
+    assert np.all(np.abs(dx - ref["dx"])[wr] <= bar[wr])
+    big = np.abs(ref["dx"]) > 0.1 * np.abs(ref["dx"]).max()
+    assert np.all((0.1 * np.abs(ref["dx"]) > bar)[wr & big.any(1)][big[wr & big.any(1)]])
+    # weight gradients
+    bd, bg = bars.wgrad_bars(eos, wl.n_local, xv, ref["a"], ref["dy"], ref["dh"], s_dh,
+                             ref["dw_d"], ref["dw_gu"])
+    for got, refw, b in ((dwd, ref["dw_d"], bd), (dwg, ref["dw_gu"], bg)):
+        assert np.all(np.abs(got - refw) <= b)
+        big = np.abs(refw) > 0.1 * np.abs(refw).max()
+        assert np.all(0.1 * np.abs(refw[big]) > b[big])

@@ -7,10 +7,14 @@ MXFP8 activations, the Mixtral-shaped layer (4096 tokens, hidden 4096,
 intermediate 14336, 8 experts, top-2) and 8 macrobatches streamed through one
 ring.  Bit-exact in full: routing ids, counts, offsets, slot_of_assign,
 assign_of_slot, windows; dispatched rows on sampled slots.  Sampled against
-the oracle row by row: expert outputs y and merged rows out (bar: see
-gpu_harness.assert_close_rms).  In full on the GPU: rows of tokens with no
-local assignment keep their sentinel; persistent == stream-ordered with whole
-tiles (no_split_k = 1), bit for bit.
+the oracle row by row: expert outputs y and merged rows out -- with bf16
+activations and weights bit-exact except where the oracle's exact value is
+within the derived fp32 error of a bf16 tie (tests/bars.py; the stated
+max|d| <= 2e-2 RMS statistic is printed beside it), with MXFP8 by the stated
+6e-2 RMS bar.  In full on the GPU: rows of tokens with no local assignment
+keep their sentinel; persistent == stream-ordered with whole tiles
+(no_split_k = 1), bit for bit; the minibatch sweep of the Kimi-shaped share
+(512, 1024, 2368, 2560, 4096) bit-identical to one window of 8192.
 """
 import os
 import sys
@@ -21,7 +25,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_harness import SENTINEL, DeviceWorkload, assert_close_rms, colblk_rows, colblk_scales, to_host
+from gpu_harness import (SENTINEL, DeviceWorkload, check_layer_out, check_y_rows, colblk_rows,
+                         colblk_scales, to_host)
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -96,18 +101,17 @@ def _check_pool_case(wl, tol):
         assert np.array_equal(colblk_scales(st.ring_sc, st.cap)[slots], xr[1])
     else:
         assert np.array_equal(ring, xr)
-    y_ref = oracle.ffn_rows(xr, oracle.expert_of_slots(sch["offsets"], slots), wl.w_gu, wl.w_d, mx)
     y_got = to_host(st.y[torch.as_tensor(slots, device="cuda")])
-    assert_close_rms(y_got, y_ref, tol, "y")
+    ys = check_y_rows(y_got, wl, xr, oracle.expert_of_slots(sch["offsets"], slots),
+                      f"{wl.name} y")
     # merged rows on sampled tokens; untouched rows in full
     toks = _sample_tokens(sch["slot_of_assign"], wl.k, rng)
     r = oracle.forward(wl, tokens=toks)
-    got = dw.out_rows(dw.outs[0], toks)
     assert r["written"].all()
-    rel = assert_close_rms(got, r["out"], tol, "out")
+    os_ = check_layer_out(dw.out_rows(dw.outs[0], toks), wl, r, f"{wl.name} out")
     written = np.nonzero((sch["slot_of_assign"].reshape(wl.T, wl.k) >= 0).any(1))[0]
     _unwritten_keep_sentinel(dw, dw.outs[0], written)
-    return dw, st, rel
+    return dw, st, (ys, os_)
 
 
 def _persistent_equals(dw, st, **kw):
@@ -125,14 +129,56 @@ def _persistent_equals(dw, st, **kw):
 
 
 def test_kimi_share_balanced():
-    dw, st, rel = _check_pool_case(W.kimi_share(), 2e-2)
-    print(f"kimi share: max|d|/RMS = {rel:.3e}")
+    dw, st, _ = _check_pool_case(W.kimi_share(), 2e-2)
     _persistent_equals(dw, st, minibatch=2560)
 
 
+def test_kimi_share_minibatch_sweep():
+    """The pages' minibatch sweep on the Kimi-shaped share: stream mode with
+    whole tiles at M = 512 ... 4096 and the persistent kernel at M = 4096 and
+    8192 write the same bits as one stream window of 8192 (the schedule does
+    not depend on M, and every tile sums its k-steps in the same order); that
+    output is held to the oracle on sampled tokens."""
+    import token_dispatch_grouped_top_amd as mok
+    wl = W.kimi_share()
+    dw = DeviceWorkload(wl)
+    ref = dw.new_out()
+    ws, _ = dw.forward(out=ref, max_rows=8192, minibatch=8192, no_split_k=1, weights_packed=1)
+    assert mok.mok_device_status(ws) == 0
+    del ws
+    for M in wl.minibatches:
+        print(f"[sweep] stream M={M}", flush=True)
+        out = dw.new_out()
+        ws, _ = dw.forward(out=out, max_rows=8192, minibatch=M, no_split_k=1, weights_packed=1)
+        assert mok.mok_device_status(ws) == 0
+        for a, b in zip(out.parts, ref.parts):
+            assert torch.equal(a, b), M
+        del ws, out
+    for M in (4096, 8192):
+        print(f"[sweep] persistent M={M}", flush=True)
+        out = dw.new_out()
+        ws, _ = dw.forward(out=out, max_rows=8192, minibatch=M, mode=1, weights_packed=1)
+        assert mok.mok_device_status(ws) == 0
+        for a, b in zip(out.parts, ref.parts):
+            assert torch.equal(a, b), ("persistent", M)
+        del ws, out
+    rng = np.random.default_rng(31)
+    sch = oracle.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)
+    toks = _sample_tokens(sch["slot_of_assign"], wl.k, rng, n=32)
+    r = oracle.forward(wl, tokens=toks)
+    check_layer_out(dw.out_rows(ref, toks), wl, r, "kimi share M=8192 whole tiles out")
+
+
 def test_kimi_share_zipf_mxfp8():
-    dw, st, rel = _check_pool_case(W.kimi_zipf_mxfp8(), 6e-2)
-    print(f"kimi zipf mxfp8: max|d|/RMS = {rel:.3e}")
+    dw, st, _ = _check_pool_case(W.kimi_zipf_mxfp8(), 6e-2)
+    _persistent_equals(dw, st, minibatch=2560)
+
+
+def test_kimi_share_full_mxfp8():
+    """MXFP8 activations and weights (block-scaled FP8 MFMA) at full size, in the
+    bench's launch configuration, against the oracle run with the same
+    quantised weights; persistent == stream with whole tiles."""
+    dw, st, _ = _check_pool_case(W.kimi_full_mxfp8(), 6e-2)
     _persistent_equals(dw, st, minibatch=2560)
 
 
@@ -149,8 +195,7 @@ def test_mixtral_layer():
     assert np.array_equal(to_host(st.aos)[:sch["R"]], sch["assign_of_slot"])
     toks = np.sort(rng.choice(wl.T, 24, replace=False))
     r = oracle.forward(wl, tokens=toks)
-    rel = assert_close_rms(dw.out_rows(dw.outs[0], toks), r["out"], 2e-2, "out")
-    print(f"mixtral: max|d|/RMS = {rel:.3e}")
+    check_layer_out(dw.out_rows(dw.outs[0], toks), wl, r, f"{wl.name} out")
 
 
 def test_streaming_macrobatches():
@@ -181,4 +226,4 @@ def test_streaming_macrobatches():
     sch = oracle.build_schedule(wl7.topk_idx, wl7.expert_base, wl7.n_local)
     toks = _sample_tokens(sch["slot_of_assign"], wl7.k, rng, n=24)
     r = oracle.forward(wl7, tokens=toks)
-    assert_close_rms(d0.out_rows(outs[7], toks), r["out"], 2e-2, "out m7")
+    check_layer_out(d0.out_rows(outs[7], toks), wl7, r, "streaming out m7")

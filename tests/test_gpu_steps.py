@@ -10,9 +10,11 @@ import numpy as np
 import pytest
 import torch
 
+import bars
 import oracle
 import workloads as W
-from gpu_harness import (DeviceWorkload, assert_close_rms, colblk_rows, colblk_scales, empty_u16,
+from gpu_harness import (DeviceWorkload, assert_close_rms, check_layer_out, check_y_rows, colblk_rows,
+                         colblk_scales, empty_u16,
                          gpu_schedule, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -151,8 +153,7 @@ def test_expert_ffn(mx):
     torch.cuda.synchronize()
     slots = np.arange(R)
     xr = oracle.gather_rows(wl.x, wl.k, ref["assign_of_slot"], slots, mx)
-    y_ref = oracle.ffn_rows(xr, oracle.expert_of_slots(ref["offsets"], slots), wl.w_gu, wl.w_d, mx)
-    assert_close_rms(to_host(y), y_ref, 6e-2 if mx else 2e-2, "y")
+    check_y_rows(to_host(y), wl, xr, oracle.expert_of_slots(ref["offsets"], slots), "y")
 
 
 def test_combine():
@@ -172,10 +173,12 @@ def test_combine():
     o_ref, written = oracle.combine_tokens(y_np, np.arange(R), ref["slot_of_assign"],
                                            wl.topk_gate, np.arange(wl.T), wl.k)
     assert np.all(got[~written] == 0x7FC1)
-    assert_close_rms(got[written], o_ref[written], 2e-2, "combine")
-    # the fp32 j-order sum differs from the fp64 one by at most one bf16 ulp
-    d = np.abs(got[written].astype(np.int32) - o_ref[written].astype(np.int32))
-    assert d.max() <= 1
+    # same y on both sides: the fp32 j-order sum may round apart from the fp64 one only
+    # where the exact sum is within the fp32 error of a bf16 tie
+    yv = bars.bf16_values(y_np)
+    lo, hi = bars.out_band(yv, yv, np.arange(R), ref["slot_of_assign"], wl.topk_gate,
+                           np.arange(wl.T), wl.k)
+    bars.band_stats(got[written], o_ref[written], lo[written], hi[written], 2e-2, "combine")
     assert int(status.item()) == 0
     # the slot-driven merge writes the same rows, bit for bit
     out2 = dw.new_out()
@@ -195,8 +198,7 @@ def test_forward_small_pool(mx, M):
     assert mok.mok_device_status(ws) == 0
     got = dw.out_rows(dw.outs[0])
     r = oracle.forward(wl)
-    assert np.array_equal(got[~r["written"]], np.full_like(got[~r["written"]], 0x7FC1))
-    assert_close_rms(got[r["written"]], r["out"][r["written"]], 6e-2 if mx else 2e-2, "out")
+    check_layer_out(got, wl, r, f"out M={M}")
 
 
 def test_forward_tiny():
@@ -210,7 +212,7 @@ def test_forward_tiny():
     _check_gates(to_host(dw.topk_gate), r["topk_gate"])
     got = dw.out_rows(dw.outs[0])
     assert r["written"].all()
-    assert_close_rms(got, r["out"], 2e-2, "out")
+    check_layer_out(got, wl, r, "out tiny")
 
 
 def test_forward_minibatch_invariance_and_determinism():
@@ -245,14 +247,14 @@ def test_forward_edge_cases():
     assert mok.mok_device_status(ws) == 0
     r = oracle.forward(wl)
     got = dw.out_rows(dw.outs[0])
-    assert_close_rms(got[r["written"]], r["out"][r["written"]], 2e-2, "out")
+    check_layer_out(got, wl, r, "out capacity 70")
     # one expert takes every row
     wl = W.small_pool(29, n_partitions=1, part_rows=600, H=256, I=128, E=8, k=1, expert_base=0,
                       counts=[600, 0, 0, 0])
     dw = DeviceWorkload(wl)
     ws, _ = dw.forward(minibatch=256)
     r = oracle.forward(wl)
-    assert_close_rms(dw.out_rows(dw.outs[0]), r["out"], 2e-2, "out")
+    check_layer_out(dw.out_rows(dw.outs[0]), wl, r, "out one expert")
 
 
 def test_forward_empty_input():

@@ -92,3 +92,69 @@ def test_ffn_wgrad_finite_differences(orc):
                 p_[e, i, j] += eps
                 m_[e, i, j] -= eps
                 assert abs(dw_gu[e, i, j] - (f(p_, w_d) - f(m_, w_d)) / (2 * eps)) < 1e-6
+
+
+def test_layer_backward_glue_finite_differences(orc):
+    """The whole-layer backward of oracle.backward (merge backward: dy = w dout
+    and dgate = <dout, y>; the dispatch backward: dx[t] = sum over t's local
+    slots) against central differences of L = sum_t <dout[t], out[t]> through
+    an unrounded fp64 forward written here from the layer's definition:
+    out[t] = sum over t's local picks j of w_tj W_d[e_tj] (SiLU(g) u), with
+    [g, u] = W_gu[e_tj] x[t].  A wrong pick <-> slot mapping, gate index or
+    dispatch sum moves dx or dgate far outside the bars; tokens without a
+    local pick must get no gradient."""
+    import workloads as W
+    wl = W.small_pool(91, n_partitions=2, part_rows=7, H=32, I=16, E=7, k=3, expert_base=2,
+                      counts=[5, 0, 6, 3])
+    val = lambda b: orc.bf16_value(b).astype(np.float64)
+    x, w_gu, w_d = val(wl.x), val(wl.w_gu) * 20.0, val(wl.w_d) * 20.0  # O(1) activations
+    wl.w_gu = orc.bf16_round(w_gu).reshape(w_gu.shape)
+    wl.w_d = orc.bf16_round(w_d).reshape(w_d.shape)
+    w_gu, w_d = val(wl.w_gu), val(wl.w_d)
+    gates = wl.topk_gate.astype(np.float64)
+    idx = wl.topk_idx - wl.expert_base
+    rng = np.random.default_rng(92)
+    dout = orc.bf16_round(rng.standard_normal((wl.T, wl.H))).reshape(wl.T, wl.H)
+    dv = val(dout)
+    I = wl.I
+
+    def loss(xx, gg):
+        total = 0.0
+        for t in range(wl.T):
+            for j in range(wl.k):
+                e = idx[t, j]
+                if 0 <= e < wl.n_local:
+                    h = w_gu[e] @ xx[t]
+                    y = w_d[e] @ (h[:I] / (1.0 + np.exp(-h[:I])) * h[I:])
+                    total += gg[t, j] * float(dv[t] @ y)
+        return total
+
+    ref = orc.backward(wl, dout)
+    local = (idx >= 0) & (idx < wl.n_local)
+    written = local.any(1)
+    assert np.array_equal(ref["written"], written) and 0 < written.sum() < wl.T
+    eps = 1e-6
+    # dx: every element of a few tokens with 0, 1 and several local picks
+    for t in [int(np.argmin(local.sum(1))), int(np.argmax(local.sum(1)))] + \
+            [int(v) for v in np.nonzero(local.sum(1) == 1)[0][:2]]:
+        for h in range(wl.H):
+            xp, xm = x.copy(), x.copy()
+            xp[t, h] += eps
+            xm[t, h] -= eps
+            fd = (loss(xp, gates) - loss(xm, gates)) / (2 * eps)
+            assert abs(ref["dx"][t, h] - fd) <= 1e-6 * (1.0 + abs(fd)), (t, h)
+    # dgate of every local pick; the oracle's uses the stored bf16 y, so the bar
+    # is the rounding of y: 2^-8 sum_h |dout y|
+    for t, j in zip(*np.nonzero(local)):
+        gp, gm = gates.copy(), gates.copy()
+        gp[t, j] += eps
+        gm[t, j] -= eps
+        fd = (loss(x, gp) - loss(x, gm)) / (2 * eps)
+        e = idx[t, j]
+        h = w_gu[e] @ x[t]
+        mag = float(np.abs(dv[t]) @ np.abs(w_d[e] @ (h[:I] / (1.0 + np.exp(-h[:I])) * h[I:])))
+        assert abs(ref["dgate"][t, j] - fd) <= 2.0 ** -8 * mag + 1e-9, (t, j)
+    assert np.all(np.isnan(ref["dgate"][~local]))
+    # dy = w dout of each slot's own pick
+    aos = orc.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)["assign_of_slot"]
+    assert np.array_equal(ref["dy"], gates.reshape(-1)[aos][:, None] * dv[aos // wl.k])
