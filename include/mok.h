@@ -402,24 +402,38 @@ mok_status mok_dispatch_backward(const void* dx_slots, int32_t rows,
                                  int32_t k, int32_t H, const mok_tokens* dx, int32_t* dev_status,
                                  hipStream_t stream);
 
-/* Bytes of workspace mok_moe_forward / mok_moe_forward_batches need for T
- * source tokens per macrobatch and n_macro macrobatches. */
+/* Bytes of workspace mok_moe_forward, mok_moe_forward_routed and
+ * mok_moe_forward_batches need for T source tokens per macrobatch and n_macro
+ * macrobatches. */
 size_t mok_forward_workspace_size(const mok_layer_desc* desc, int32_t T, int32_t n_macro);
 
-/* The fused layer (article, megakernel, minibatch and ring-buffer
- * paragraphs): schedule, windows, pull dispatch into the fixed ring, grouped
- * SwiGLU FFN, push of y into a return area indexed by slot, weighted merge
- * into out.  Routing (topk_idx / topk_gate, [T][k]) comes from the sources'
- * route step.  MOK_MODE_STREAM issues stream-ordered launches per window;
+/* The fused layer (article, routing, megakernel, minibatch and ring-buffer
+ * paragraphs): route, schedule, windows, pull dispatch into the fixed ring,
+ * grouped SwiGLU FFN, push of y into a return area indexed by slot, weighted
+ * merge into out.  logits: fp32 [T][desc->n_experts] router scores of the T
+ * tokens of x (finite; n_experts <= 4096); they are routed here as by
+ * mok_route_topk (k = desc->top_k), into the workspace, and the route also
+ * counts the picks of local experts for the schedule (one launch).
+ * MOK_MODE_STREAM issues stream-ordered launches per window;
  * MOK_MODE_PERSISTENT runs the windows in one cooperative kernel whose
  * workgroups split into data movers and MFMA workers that signal through
  * device counters.  If R exceeds desc->max_rows the status word becomes
- * MOK_ERR_CAPACITY and out is left untouched. */
-mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
-                           const float* topk_gate, int32_t T, const mok_tokens* x,
-                           const void* w_gate_up, const void* w_down,
-                           const mok_tokens* out, void* ws, size_t ws_bytes,
-                           hipStream_t stream);
+ * MOK_ERR_CAPACITY and out is left untouched.  T = 0 writes nothing (logits
+ * may then be null). */
+mok_status mok_moe_forward(const mok_layer_desc* desc, const float* logits, int32_t T,
+                           const mok_tokens* x, const void* w_gate_up, const void* w_down,
+                           const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The fused layer from routing decided elsewhere (one GPU's expert share:
+ * the sources route their own tokens, and this GPU schedules every source's
+ * picks of its local experts; article, routing and pull-dispatch
+ * paragraphs).  topk_idx / topk_gate: int32 / fp32 [T][k] over the pool of T
+ * tokens; otherwise as mok_moe_forward. */
+mok_status mok_moe_forward_routed(const mok_layer_desc* desc, const int32_t* topk_idx,
+                                  const float* topk_gate, int32_t T, const mok_tokens* x,
+                                  const void* w_gate_up, const void* w_down,
+                                  const mok_tokens* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* n_macro macrobatches through one ring (article, ring-buffer paragraph:
  * the next macrobatch's dispatch overlaps the previous one's combine).

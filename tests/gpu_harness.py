@@ -153,7 +153,10 @@ class DeviceWorkload:
         assert wsb > 0
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         w_gu, w_d = self.weights(d)
-        mok.mok_moe_forward(d, idx, gate, wl.T, self.x, w_gu, w_d, out, ws)
+        if wl.routing_from_logits:      # the fused call routes the logits itself
+            mok.mok_moe_forward(d, self.logits, wl.T, self.x, w_gu, w_d, out, ws)
+        else:
+            mok.mok_moe_forward_routed(d, idx, gate, wl.T, self.x, w_gu, w_d, out, ws)
         return ws, d
 
 

@@ -108,7 +108,10 @@ def test_bad_descriptors(bad):
     d = _desc(**bad)
     assert mok.mok_forward_workspace_size(d, 256, 1) == 0
     tok = mok.mok_tokens(1, 1, 256)
-    st = L.mok_moe_forward(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, 1 << 40, None)
+    st = L.mok_moe_forward_routed(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1,
+                                  1 << 40, None)
+    assert st in (mok.MOK_ERR_INVALID_ARG, mok.MOK_ERR_UNSUPPORTED)
+    st = L.mok_moe_forward(C.byref(d), 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, 1 << 40, None)
     assert st in (mok.MOK_ERR_INVALID_ARG, mok.MOK_ERR_UNSUPPORTED)
 
 
@@ -118,8 +121,14 @@ def test_workspace_query_and_small_workspace():
     assert n > 0
     assert mok.mok_forward_workspace_size(d, 256, 2) > n
     tok = mok.mok_tokens(1, 1, 256)
-    st = L.mok_moe_forward(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, n - 1, None)
+    st = L.mok_moe_forward_routed(C.byref(d), 1, 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1,
+                                  n - 1, None)
     assert st == mok.MOK_ERR_WORKSPACE
+    st = L.mok_moe_forward(C.byref(d), 1, 256, C.byref(tok), 1, 1, C.byref(tok), 1, n - 1, None)
+    assert st == mok.MOK_ERR_WORKSPACE
+    # the logits form needs logits when there are tokens
+    st = L.mok_moe_forward(C.byref(d), None, 256, C.byref(tok), 1, 1, C.byref(tok), 1, n, None)
+    assert st == mok.MOK_ERR_INVALID_ARG
 
 
 def test_forward_minibatch_plan():

@@ -198,6 +198,24 @@ def test_mixtral_layer():
     check_layer_out(dw.out_rows(dw.outs[0], toks), wl, r, f"{wl.name} out")
 
 
+def test_mixtral_fused_from_logits():
+    """The fused call on the Mixtral-shaped layer from its router logits: route
+    (with the schedule's counts), schedule, windows, gather, FFN and merge in
+    one mok_moe_forward, stream and persistent mode, against the oracle."""
+    import token_dispatch_grouped_top_amd as mok
+    wl = W.mixtral()
+    dw = DeviceWorkload(wl, n_out=2)
+    rng = np.random.default_rng(8)
+    toks = np.sort(rng.choice(wl.T, 16, replace=False))
+    r = oracle.forward(wl, tokens=toks)
+    for mode, out in ((0, dw.outs[0]), (1, dw.outs[1])):
+        print(f"[mixtral fused] mode {mode}", flush=True)
+        ws, _ = dw.forward(out=out, max_rows=wl.T * wl.k, mode=mode, weights_packed=1)
+        assert mok.mok_device_status(ws) == 0
+        del ws
+        check_layer_out(dw.out_rows(out, toks), wl, r, f"{wl.name} fused from logits, mode {mode}")
+
+
 def test_streaming_macrobatches():
     import token_dispatch_grouped_top_amd as mok
     wls = W.streaming(8)

@@ -265,6 +265,8 @@ def test_forward_empty_input():
     d = dw.desc()
     wsb = mok.mok_forward_workspace_size(d, 0, 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    mok.mok_moe_forward(d, dw.topk_idx, dw.topk_gate, 0, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+    mok.mok_moe_forward_routed(d, dw.topk_idx, dw.topk_gate, 0, dw.x, dw.w_gu, dw.w_d,
+                               dw.outs[0], ws)
+    mok.mok_moe_forward(d, None, 0, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
     assert mok.mok_device_status(ws) == 0
     assert np.all(dw.out_rows(dw.outs[0]) == 0x7FC1)

@@ -43,7 +43,7 @@ def test_tune_picks_a_candidate_that_runs(mode, Ms, moves):
         assert best.n_move_cus in moves
     assert best.mode == mode and best.hidden == wl.H
     out = dw.new_out()
-    mok.mok_moe_forward(best, idx, gate, wl.T, dw.x, w_gu, w_d, out, ws)
+    mok.mok_moe_forward_routed(best, idx, gate, wl.T, dw.x, w_gu, w_d, out, ws)
     assert mok.mok_device_status(ws) == 0
     r = oracle.forward(wl)
     check_layer_out(dw.out_rows(out), wl, r, "out of the tuned descriptor")

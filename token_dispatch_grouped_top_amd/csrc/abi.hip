@@ -3,6 +3,7 @@
 // The kernels live in route.hip, schedule.hip, movers.hip and gemm.hip; the
 // persistent pipeline in persistent.hip.
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 
 #include "mok_internal.h"
@@ -16,27 +17,28 @@ constexpr int kGemmTileM = 256, kGemmTileN = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-__global__ void k_fill_i32(int32_t* p, int32_t n, int32_t v) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+// Zeroes two ranges of int32 (the fused call's status word and counters).
+__global__ void k_zero2(int32_t* a, int32_t na, int32_t* b, int32_t nb) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += gridDim.x * blockDim.x) {
+    if (i < na) a[i] = 0;
+    else b[i - na] = 0;
+  }
 }
 
-// Sets the status word when more rows were routed here than the capacity.
-__global__ void k_capacity_check(const int32_t* offsets, int32_t n_local, int32_t cap,
-                                 int32_t* status) {
-  if (threadIdx.x == 0 && offsets[n_local] > cap) set_status(status, MOK_ERR_CAPACITY);
-}
-
+// Compute units of the current device, queried once per device.  Calls may
+// run concurrently on several host threads: the cache is atomic, and two
+// threads that both miss store the same value.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
       v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 bool tokens_ok(const mok_tokens* t, int64_t T) {
@@ -97,8 +99,8 @@ struct Plan {
   int32_t act_rows;
   int32_t n_ybuf;     // return areas (2 when macrobatches overlap)
   bool split;         // stream mode with the GEMMs' K split (workspace at off_split)
-  size_t off_status, off_split, off_sched, off_counts, off_offsets, off_soa, off_aos, off_win, off_ring,
-      off_ring_sc, off_act, off_act_sc, off_y, off_pers, total;
+  size_t off_status, off_split, off_sched, off_route_idx, off_route_gate, off_counts, off_offsets,
+      off_soa, off_aos, off_win, off_ring, off_ring_sc, off_act, off_act_sc, off_y, off_pers, total;
   size_t per_macro_counts, per_macro_offsets, per_macro_soa, per_macro_aos, per_macro_win;
 };
 
@@ -130,6 +132,9 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.off_status = take(kAlign);
   p.off_split = take(p.split ? split_ws_bytes(device_cus()) : 0);  // right after the status word
   p.off_sched = take(sched_ws_bytes(p.A, d->n_local));
+  // routing of the logits-taking call (T x k ids and gates of one macrobatch)
+  p.off_route_idx = take(static_cast<size_t>(std::max<int64_t>(p.A, 1)) * 4);
+  p.off_route_gate = take(static_cast<size_t>(std::max<int64_t>(p.A, 1)) * 4);
   p.per_macro_counts = align_up(nl * 4);
   p.per_macro_offsets = align_up((nl + 1) * 4);
   p.per_macro_soa = align_up(std::max<int64_t>(p.A, 1) * 4);
@@ -542,16 +547,26 @@ int32_t mok_forward_minibatch(const mok_layer_desc* desc, int32_t T) {
   return p.M;
 }
 
-mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
-                                   const int32_t* const* topk_idx, const float* const* topk_gate,
-                                   int32_t T, const mok_tokens* x, const void* w_gate_up,
-                                   const void* w_down, const mok_tokens* out, void* ws,
-                                   size_t ws_bytes, hipStream_t stream) {
-  if (!desc_ok(desc) || n_macro < 1 || T < 0 || !topk_idx || !topk_gate || !tokens_ok(x, T) ||
-      !w_gate_up || !w_down || !out || !ws || !weights_ok(desc))
+}  // extern "C"
+
+namespace mok {
+namespace {
+
+// The fused layer.  logits non-null (then n_macro = 1): the routing of the T
+// tokens is computed here, from fp32 logits [T][n_experts], into the
+// workspace; otherwise topk_idx / topk_gate hold each macrobatch's routing.
+mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float* logits,
+                        const int32_t* const* topk_idx, const float* const* topk_gate, int32_t T,
+                        const mok_tokens* x, const void* w_gate_up, const void* w_down,
+                        const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!desc_ok(desc) || n_macro < 1 || T < 0 || !tokens_ok(x, T) || !w_gate_up || !w_down ||
+      !out || !ws || !weights_ok(desc))
+    return MOK_ERR_INVALID_ARG;
+  if (logits ? (n_macro != 1 || desc->n_experts > 4096)
+             : (!topk_idx || !topk_gate))
     return MOK_ERR_INVALID_ARG;
   for (int m = 0; m < n_macro; ++m) {
-    if (T > 0 && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
+    if (T > 0 && !logits && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
     if (!tokens_ok(&out[m], T)) return MOK_ERR_INVALID_ARG;
   }
   Plan p;
@@ -562,14 +577,19 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
   const bool mx = d.act_format == MOK_ACT_MXFP8_E4M3;
   int32_t* status = at<int32_t>(ws, p.off_status);
   hipError_t err = hipSuccess;
-  // the status word and, with the K split, its counters (which follow it)
+  // the status word and, with the K split, its counters (which follow it);
+  // with logits also the schedule's chunk counts, which the route adds into
   const int n_cus = device_cus();
   const int32_t n_clear = static_cast<int32_t>(kAlign / 4) + (p.split ? n_cus : 0);
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, stream, status, n_clear, 0);
+  SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
+  const int32_t n_clear2 = logits ? sw.nblk * d.n_local : 0;
+  hipLaunchKernelGGL(k_zero2, dim3(n_clear2 > 4096 ? 16 : 1), dim3(256), 0, stream, status, n_clear,
+                     sw.blk_counts, n_clear2);
   if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
   const SplitWs split = p.split ? split_ws_carve(at<void>(ws, p.off_split), n_cus) : SplitWs{};
+  int32_t* route_idx = at<int32_t>(ws, p.off_route_idx);
+  float* route_gate = at<float>(ws, p.off_route_gate);
 
-  SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
   MacroBuffers mb[64];
   const int nm_buf = n_macro < 64 ? n_macro : 64;
   if (n_macro > 64) return MOK_ERR_UNSUPPORTED;
@@ -579,25 +599,18 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
     mb[m].soa = at<int32_t>(ws, p.off_soa + m * p.per_macro_soa);
     mb[m].aos = at<int32_t>(ws, p.off_aos + m * p.per_macro_aos);
     mb[m].win = at<int32_t>(ws, p.off_win + m * p.per_macro_win);
-    mb[m].gate = topk_gate[m];
+    mb[m].gate = logits ? route_gate : topk_gate[m];
     mb[m].y = at<uint16_t>(ws, p.off_y + static_cast<size_t>(m % p.n_ybuf) * p.cap * d.hidden * 2);
     mb[m].out = out[m];
   }
-  // Schedules and windows for every macrobatch first: they only read routing.
+  // Route (logits form), schedule, windows and capacity check for every
+  // macrobatch first: two launches each, reading only routing.
   for (int m = 0; m < n_macro; ++m) {
-    if (T > 0) {
-      err = launch_schedule(topk_idx[m], p.A, d.expert_base, d.n_local, mb[m].counts,
-                            mb[m].offsets, mb[m].soa, mb[m].aos, sw, stream);
-    } else {
-      hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, stream, mb[m].offsets, d.n_local + 1, 0);
-      err = hipGetLastError();
-    }
+    int32_t* idx = logits ? route_idx : const_cast<int32_t*>(T > 0 ? topk_idx[m] : nullptr);
+    err = launch_route_schedule(logits, d.n_experts, route_gate, idx, T, d.top_k, d.expert_base,
+                                d.n_local, mb[m].counts, mb[m].offsets, mb[m].soa, mb[m].aos, sw,
+                                p.M, p.nwin, mb[m].win, p.cap, status, stream);
     if (err != hipSuccess) return hip_status(err);
-    if ((err = launch_windows(mb[m].offsets, d.n_local, p.M, p.nwin, mb[m].win, stream)) != hipSuccess)
-      return hip_status(err);
-    hipLaunchKernelGGL(k_capacity_check, dim3(1), dim3(64), 0, stream, mb[m].offsets, d.n_local,
-                       p.cap, status);
-    if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
   }
 
   void* ring = at<void>(ws, p.off_ring);
@@ -647,12 +660,35 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
   return MOK_OK;
 }
 
-mok_status mok_moe_forward(const mok_layer_desc* desc, const int32_t* topk_idx,
-                           const float* topk_gate, int32_t T, const mok_tokens* x,
-                           const void* w_gate_up, const void* w_down, const mok_tokens* out,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
-  return mok_moe_forward_batches(desc, 1, &topk_idx, &topk_gate, T, x, w_gate_up, w_down, out, ws,
-                                 ws_bytes, stream);
+}  // namespace
+}  // namespace mok
+
+extern "C" {
+
+mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
+                                   const int32_t* const* topk_idx, const float* const* topk_gate,
+                                   int32_t T, const mok_tokens* x, const void* w_gate_up,
+                                   const void* w_down, const mok_tokens* out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  return mok::forward_impl(desc, n_macro, nullptr, topk_idx, topk_gate, T, x, w_gate_up, w_down,
+                           out, ws, ws_bytes, stream);
+}
+
+mok_status mok_moe_forward_routed(const mok_layer_desc* desc, const int32_t* topk_idx,
+                                  const float* topk_gate, int32_t T, const mok_tokens* x,
+                                  const void* w_gate_up, const void* w_down, const mok_tokens* out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mok::forward_impl(desc, 1, nullptr, &topk_idx, &topk_gate, T, x, w_gate_up, w_down, out,
+                           ws, ws_bytes, stream);
+}
+
+mok_status mok_moe_forward(const mok_layer_desc* desc, const float* logits, int32_t T,
+                           const mok_tokens* x, const void* w_gate_up, const void* w_down,
+                           const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T > 0 && !logits) return MOK_ERR_INVALID_ARG;
+  static const float kNoLogits = 0.0f;     // T = 0: nothing is read
+  return mok::forward_impl(desc, 1, T > 0 ? logits : &kNoLogits, nullptr, nullptr, T, x,
+                           w_gate_up, w_down, out, ws, ws_bytes, stream);
 }
 
 mok_status mok_tune_forward(const mok_layer_desc* desc, const int32_t* minibatch,

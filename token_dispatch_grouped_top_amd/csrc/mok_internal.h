@@ -119,6 +119,9 @@ hipError_t launch_route_topk_gemm(const uint16_t* x, const uint16_t* w_router, i
 hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                              int32_t* idx, float* gate, hipStream_t s);
 
+// The schedule counts assignments in chunks of kSchedChunk (a = t*k + j):
+// blk_counts[e][c] = local assignments to expert e in chunk c.
+constexpr int kSchedChunk = 2048;
 struct SchedWs {
   int32_t* blk_counts;  // [n_local][nblk]
   int32_t nblk;
@@ -130,6 +133,20 @@ hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, i
                            const SchedWs& w, hipStream_t s);
 hipError_t launch_windows(const int32_t* offsets, int32_t n_local, int32_t M, int32_t nwin,
                           int32_t* win_seg, hipStream_t s);
+// The fused layer's schedule.  route_logits non-null: the route of the T
+// tokens from fp32 logits [T][E] writes idx / gate and counts its local picks
+// into the chunk counts (zeroed by the caller beforehand) in the same launch;
+// null: idx is given and counted by the count kernel.  Then the scatter,
+// which also writes the window table (M, nwin) and raises MOK_ERR_CAPACITY in
+// *status when R > cap.  Two launches either way.
+hipError_t launch_route_schedule(const float* route_logits, int32_t E, float* gate,
+                                 int32_t* idx, int64_t T, int32_t k, int32_t expert_base,
+                                 int32_t n_local, int32_t* counts, int32_t* offsets, int32_t* soa,
+                                 int32_t* aos, const SchedWs& w, int32_t M, int32_t nwin,
+                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s);
+hipError_t launch_route_count(const float* logits, int32_t T, int32_t E, int32_t k,
+                              int32_t expert_base, int32_t n_local, int32_t* idx, float* gate,
+                              int32_t* blk_counts, int32_t nblk, hipStream_t s);
 
 hipError_t launch_gather(void* const* part_ptr, int32_t n_part, int32_t part_rows, int32_t H,
                          int32_t k, const int32_t* aos, const int32_t* offsets, int32_t n_local,

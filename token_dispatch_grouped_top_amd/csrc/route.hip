@@ -6,10 +6,18 @@
 // gates = softmax over the k picked logits.
 //
 // One wave per token.  Lane l holds logits l, l+64, l+128, ... in registers;
-// each of the k rounds is a lane-local argmax followed by a 6-step butterfly
-// over the wave with the (value desc, id asc) order, so the result does not
-// depend on the reduction order.  Gates: lanes 0..k-1 hold the picked
-// logits; e_j = exp(l_j - l_0) in fp32, summed by a butterfly, divided.
+// each of the k rounds is a lane-local argmax, then the best of each 16-lane
+// row by DPP moves (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row half-mirror,
+// row mirror), then the four rows' bests read with readlane.  Every step keeps
+// the better pair under one total order (value descending, expert id
+// ascending), so the pick does not depend on the order of the steps.  Gates:
+// lanes 0..k-1 hold the picked logits; e_j = exp(l_j - l_0) in fp32, summed
+// by a butterfly, divided.
+//
+// k_route_count (the fused layer): the same route, and each lane holding a
+// pick of a local expert adds one to that expert's count of the pick's
+// schedule chunk (integer atomics: the counts do not depend on their order),
+// so the schedule's separate count launch is not needed.
 #include "mok_internal.h"
 
 namespace mok {
@@ -35,8 +43,8 @@ __device__ __forceinline__ void best_dpp(float& bv, int& be) {
 // Picks and gates of token t from its logits v (lane l holds logits l,
 // l + 64, ...; -inf past E).  All 64 lanes call it.
 template <int VPL>
-__device__ __forceinline__ void pick_topk(const float (&v)[VPL], int32_t E, int32_t k, int64_t t,
-                                          int32_t* __restrict__ idx, float* __restrict__ gate) {
+__device__ __forceinline__ int pick_topk(const float (&v)[VPL], int32_t E, int32_t k, int64_t t,
+                                         int32_t* __restrict__ idx, float* __restrict__ gate) {
   const int lane = lane_id();
   uint64_t taken = 0;  // bit i: v[i] already picked
   float mine = 0.0f;   // lane j keeps the j-th picked logit
@@ -82,6 +90,7 @@ __device__ __forceinline__ void pick_topk(const float (&v)[VPL], int32_t E, int3
     idx[t * k + lane] = mine_e;
     gate[t * k + lane] = ex / sum;
   }
+  return mine_e;                 // lane j < k: the j-th pick
 }
 
 template <int VPL>
@@ -99,6 +108,29 @@ void k_route_topk(const float* __restrict__ logits, int32_t T, int32_t E, int32_
     v[i] = e < E ? row[e] : -__builtin_inff();
   }
   pick_topk<VPL>(v, E, k, t, idx, gate);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kRouteWaves * kWave)
+void k_route_count(const float* __restrict__ logits, int32_t T, int32_t E, int32_t k, int32_t base,
+                   int32_t n_local, int32_t* __restrict__ idx, float* __restrict__ gate,
+                   int32_t* __restrict__ blk_counts, int32_t nblk) {
+  const int lane = lane_id();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteWaves + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : -__builtin_inff();
+  }
+  const int e = pick_topk<VPL>(v, E, k, t, idx, gate) - base;
+  if (lane < k && e >= 0 && e < n_local) {
+    const int64_t chunk = (t * k + lane) / kSchedChunk;
+    __hip_atomic_fetch_add(blk_counts + static_cast<int64_t>(e) * nblk + chunk, 1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------- router GEMM + top-k
@@ -260,6 +292,16 @@ hipError_t launch_vpl(const float* logits, int32_t T, int32_t E, int32_t k, int3
 }
 
 template <int VPL>
+hipError_t launch_count_vpl(const float* logits, int32_t T, int32_t E, int32_t k, int32_t base,
+                            int32_t n_local, int32_t* idx, float* gate, int32_t* blk_counts,
+                            int32_t nblk, hipStream_t s) {
+  dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
+  hipLaunchKernelGGL(k_route_count<VPL>, grid, dim3(kRouteWaves * kWave), 0, s, logits, T, E, k,
+                     base, n_local, idx, gate, blk_counts, nblk);
+  return hipGetLastError();
+}
+
+template <int VPL>
 hipError_t launch_sum_vpl(const float* partial, int32_t n_split, int32_t T, int32_t E, int32_t k,
                           int32_t* idx, float* gate, hipStream_t s) {
   dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
@@ -312,6 +354,19 @@ hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t 
   if (E <= 1024) return launch_vpl<16>(logits, T, E, k, idx, gate, s);
   if (E <= 2048) return launch_vpl<32>(logits, T, E, k, idx, gate, s);
   return launch_vpl<64>(logits, T, E, k, idx, gate, s);
+}
+
+hipError_t launch_route_count(const float* logits, int32_t T, int32_t E, int32_t k,
+                              int32_t base, int32_t n_local, int32_t* idx, float* gate,
+                              int32_t* blk_counts, int32_t nblk, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (E <= 64) return launch_count_vpl<1>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  if (E <= 128) return launch_count_vpl<2>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  if (E <= 256) return launch_count_vpl<4>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  if (E <= 512) return launch_count_vpl<8>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  if (E <= 1024) return launch_count_vpl<16>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  if (E <= 2048) return launch_count_vpl<32>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
+  return launch_count_vpl<64>(logits, T, E, k, base, n_local, idx, gate, blk_counts, nblk, s);
 }
 
 }  // namespace mok

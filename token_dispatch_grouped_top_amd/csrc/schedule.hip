@@ -29,6 +29,7 @@ constexpr int kSchedThreads = 256;
 constexpr int kSchedWaves = kSchedThreads / kWave;
 constexpr int kStepsPerWave = 8;    // 8: 14.6 us for the two launches at 589,824 ids; 16: 19.2
 constexpr int kChunk = kSchedThreads * kStepsPerWave;  // 2048 assignments per block
+static_assert(kChunk == kSchedChunk, "chunk of the route's counts");
 constexpr int kMaxLocal = 256;
 
 __device__ __forceinline__ int key_bits(int32_t n_local) { return 32 - __clz(n_local); }
@@ -98,7 +99,9 @@ __global__ __launch_bounds__(kSchedThreads)
 void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, int32_t n_local,
                      int32_t nblk, const int32_t* __restrict__ blk_counts,
                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                     int32_t* __restrict__ soa, int32_t* __restrict__ aos) {
+                     int32_t* __restrict__ soa, int32_t* __restrict__ aos, int32_t M,
+                     int32_t nwin, int32_t* __restrict__ win_seg, int32_t cap,
+                     int32_t* __restrict__ status) {
   __shared__ int32_t h[kSchedWaves][kMaxLocal];
   __shared__ int32_t cur[kSchedWaves][kMaxLocal];
   __shared__ int32_t tot[kMaxLocal], pre[kMaxLocal], off[kMaxLocal + 1];
@@ -137,11 +140,26 @@ void k_sched_scatter(const int32_t* __restrict__ idx, int64_t A, int32_t base, i
     off[n_local] = acc;
   }
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e <= n_local; e += kSchedThreads) {
       offsets[e] = off[e];
       if (e < n_local) counts[e] = tot[e];
     }
+    // the fused layer's window table and capacity check (win_seg null: not asked)
+    if (win_seg) {
+      const int64_t R = off[n_local];
+      const int64_t n = static_cast<int64_t>(nwin) * (n_local + 1);
+      for (int64_t i = threadIdx.x; i < n; i += kSchedThreads) {
+        const int64_t b = i / (n_local + 1), e = i % (n_local + 1);
+        int64_t lo = b * M, hi = lo + M;
+        if (lo > R) lo = R;
+        if (hi > R) hi = R;
+        int64_t v = off[e];
+        win_seg[i] = static_cast<int32_t>(v < lo ? lo : (v > hi ? hi : v));
+      }
+      if (threadIdx.x == 0 && R > cap) set_status(status, MOK_ERR_CAPACITY);
+    }
+  }
   for (int e = threadIdx.x; e < n_local; e += kSchedThreads) {
     int32_t b = off[e] + pre[e];
 #pragma unroll
@@ -212,7 +230,31 @@ hipError_t launch_schedule(const int32_t* idx, int64_t A, int32_t expert_base, i
                        n_local, w.nblk, w.blk_counts);
   }
   hipLaunchKernelGGL(k_sched_scatter, dim3(A > 0 ? w.nblk : 1), dim3(kSchedThreads), 0, s, idx, A,
-                     expert_base, n_local, w.nblk, w.blk_counts, counts, offsets, soa, aos);
+                     expert_base, n_local, w.nblk, w.blk_counts, counts, offsets, soa, aos, 0, 0,
+                     nullptr, 0, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_schedule(const float* route_logits, int32_t E, float* gate,
+                                 int32_t* idx, int64_t T, int32_t k, int32_t expert_base,
+                                 int32_t n_local, int32_t* counts, int32_t* offsets, int32_t* soa,
+                                 int32_t* aos, const SchedWs& w, int32_t M, int32_t nwin,
+                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s) {
+  if (n_local > kMaxLocal) return hipErrorInvalidValue;
+  const int64_t A = T * k;
+  hipError_t e;
+  if (route_logits && T > 0) {
+    e = launch_route_count(route_logits, static_cast<int32_t>(T), E, k, expert_base, n_local, idx,
+                           gate, w.blk_counts, w.nblk, s);
+  } else {
+    hipLaunchKernelGGL(k_sched_count, dim3(A > 0 ? w.nblk : 1), dim3(kSchedThreads), 0, s, idx, A,
+                       expert_base, n_local, w.nblk, w.blk_counts);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_scatter, dim3(A > 0 ? w.nblk : 1), dim3(kSchedThreads), 0, s, idx, A,
+                     expert_base, n_local, w.nblk, w.blk_counts, counts, offsets, soa, aos, M,
+                     nwin, win_seg, cap, status);
   return hipGetLastError();
 }
 
