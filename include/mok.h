@@ -171,6 +171,24 @@ mok_status mok_build_schedule(const int32_t* topk_idx, int32_t T, int32_t k,
                               int32_t* slot_of_assign, int32_t* assign_of_slot,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* mok_build_schedule for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same schedule, bit for bit, with its scratch (the per-chunk
+ * expert counts) in a fixed device array of the library, of
+ * mok_schedule_noalloc_max_bytes() bytes (4 MiB) per GPU, held until the
+ * process ends; its address on each device is looked up on the first call on
+ * that device.  Calls nothing that allocates.  A schedule whose scratch
+ * (mok_schedule_workspace_size) exceeds that size returns MOK_ERR_UNSUPPORTED
+ * (e.g. more than 4.19 million assignments with 256 local experts).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (concurrent streams) race and must not be issued.  Nothing in the array has
+ * to start at zero; the last call's contents stay in it. */
+size_t mok_schedule_noalloc_max_bytes(void);
+mok_status mok_build_schedule_noalloc(const int32_t* topk_idx, int32_t T, int32_t k,
+                                      int32_t expert_base, int32_t n_local, int32_t* counts,
+                                      int32_t* offsets, int32_t* slot_of_assign,
+                                      int32_t* assign_of_slot, hipStream_t stream);
+
 /* Two-wave minibatch rule (article, minibatch paragraph; wiki key point on
  * minibatch size): M = 2 * n_cus * tile_m * tile_n / n_out rounded up to a
  * multiple of 64, clipped to `rows` when rows > 0.  Host only. */

@@ -201,3 +201,16 @@ def test_saved_h_calls_validate_before_launch():
                                            None) == E
     assert L.mok_expert_ffn_backward_saved(C.byref(d), 1, 1, 0, 64, 1, 1, 1, 1, 1, 0,
                                            None) == E
+
+
+def test_schedule_noalloc_refuses_beyond_its_array():
+    """The no-allocation schedule checks its fixed scratch size before any device
+    call: more assignments than its array holds is MOK_ERR_UNSUPPORTED."""
+    cap = mok.mok_schedule_noalloc_max_bytes()
+    assert cap == 4 << 20
+    T, k, nl = 600_000, 8, 256                      # 4.8 M assignments x 256 experts
+    assert mok.mok_schedule_workspace_size(T, k, nl) > cap
+    st = L.mok_build_schedule_noalloc(1, T, k, 0, nl, 1, 1, 1, 1, None)
+    assert st == mok.MOK_ERR_UNSUPPORTED
+    st = L.mok_build_schedule_noalloc(1, 16, 2, 0, 0, 1, 1, 1, 1, None)
+    assert st == mok.MOK_ERR_INVALID_ARG

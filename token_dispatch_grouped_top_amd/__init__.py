@@ -61,6 +61,8 @@ _SIGS = {
     "mok_route_topk_gemm": (C.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mok_schedule_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "mok_build_schedule": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mok_schedule_noalloc_max_bytes": (_SZ, []),
+    "mok_build_schedule_noalloc": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mok_choose_minibatch": (_I32, [_I32, _I32, _I32, _I32, _I64]),
     "mok_build_windows": (C.c_int, [_P, _I32, _I32, _I32, _P, _P]),
     "mok_dispatch_gather": (C.c_int, [_TOK, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32,
@@ -193,6 +195,18 @@ def mok_build_schedule(topk_idx, T: int, k: int, expert_base: int, n_local: int,
     _check(_lib.mok_build_schedule(_ptr(topk_idx), T, k, expert_base, n_local, _ptr(counts),
                                    _ptr(offsets), _ptr(slot_of_assign), _ptr(assign_of_slot),
                                    _ptr(ws), ws_bytes, _stream(stream)), "mok_build_schedule")
+
+
+def mok_schedule_noalloc_max_bytes() -> int:
+    return int(_lib.mok_schedule_noalloc_max_bytes())
+
+
+def mok_build_schedule_noalloc(topk_idx, T: int, k: int, expert_base: int, n_local: int, counts,
+                               offsets, slot_of_assign, assign_of_slot, stream=None) -> None:
+    _check(_lib.mok_build_schedule_noalloc(_ptr(topk_idx), T, k, expert_base, n_local,
+                                           _ptr(counts), _ptr(offsets), _ptr(slot_of_assign),
+                                           _ptr(assign_of_slot), _stream(stream)),
+           "mok_build_schedule_noalloc")
 
 
 def mok_choose_minibatch(n_cus: int, tile_m: int, tile_n: int, n_out: int, rows: int = 0) -> int:

@@ -231,6 +231,58 @@ mok_status mok_build_schedule(const int32_t* topk_idx, int32_t T, int32_t k, int
                                     slot_of_assign, assign_of_slot, w, stream));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------- schedule with no allocation
+// The schedule's per-chunk counts live in a fixed device array instead of a
+// caller workspace, for callers that cannot allocate.  In host code the
+// array's name is only a stand-in: its device address, one per GPU, comes
+// from hipGetSymbolAddress on the first call on that device and is what the
+// kernels receive.
+namespace {
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch(mok_status* st) {
+  static std::atomic<void*> ptr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { *st = hip_status(e); return nullptr; }
+  if (dev < 0 || dev >= 64) { *st = MOK_ERR_UNSUPPORTED; return nullptr; }
+  void* p = ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) { *st = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol); return nullptr; }
+    ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mok_schedule_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+mok_status mok_build_schedule_noalloc(const int32_t* topk_idx, int32_t T, int32_t k,
+                                      int32_t expert_base, int32_t n_local, int32_t* counts,
+                                      int32_t* offsets, int32_t* slot_of_assign,
+                                      int32_t* assign_of_slot, hipStream_t stream) {
+  if (T < 0 || k < 1 || n_local < 1 || n_local > 256) return MOK_ERR_INVALID_ARG;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A >= (1ll << 31)) return MOK_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOK_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !slot_of_assign || !assign_of_slot)) return MOK_ERR_INVALID_ARG;
+  if (sched_ws_bytes(A, n_local) > kNoAllocScratchBytes) return MOK_ERR_UNSUPPORTED;
+  mok_status st = MOK_OK;
+  void* ws = noalloc_scratch(&st);
+  if (!ws) return st;
+  // every chunk count the scatter reads is written by the count launch first:
+  // nothing in the array has to start at zero
+  SchedWs w = sched_ws_carve(ws, A, n_local);
+  return hip_status(launch_schedule(topk_idx, A, expert_base, n_local, counts, offsets,
+                                    slot_of_assign, assign_of_slot, w, stream));
+}
+
 int32_t mok_choose_minibatch(int32_t n_cus, int32_t tile_m, int32_t tile_n, int32_t n_out,
                              int64_t rows) {
   if (n_cus < 1 || tile_m < 1 || tile_n < 1 || n_out < 1) return 0;
