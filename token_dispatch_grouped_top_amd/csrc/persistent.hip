@@ -83,32 +83,46 @@ struct PKArgs {
   uint64_t timeout_ticks;
 };
 
-// Control block (int32 words) for at most W windows.
+// Control block (int32 words) for at most W windows.  The view holds only
+// the base and W; every member is an offset computed where it is used, so the
+// workers do not keep a dozen pointers live in scalar registers across a GEMM
+// tile (with them live, the tile's main loop ran short of SGPRs and the
+// compiler rebuilt a buffer descriptor with v_readfirstlane in every k-step).
 struct CtlView {
-  int32_t *tile_ctr, *abort, *n_windows, *n_items;
-  int32_t *win_m, *win_s0, *win_s1, *win_nt1, *win_nt2;
-  int32_t *gathered, *gu_done, *dn_done, *merged;
-  int32_t* xseq;   // [8][2W + 1] per-XCD prefix of tile shares over the sequence
-  int32_t* ent;    // [2W] sequence entries: 2 * window + (0 gate/up, 1 down)
-  int32_t* items;  // [W + kMaxMacro] mover items: window >= 0, merge m as -m - 1
-  PMacro* pm;      // [kMaxMacro] per-macrobatch buffers (copied from the kernel arguments,
-                   // so runtime indexing does not force the arguments into scratch)
-  int xstride;
+  int32_t* b;
+  int W;
   __host__ __device__ static size_t int_words(int W) {
-    return 16 + 5 * W + 3 * W + kMaxMacro + 8 * (2 * W + 1) + 2 * W + W + kMaxMacro;
+    return 16 + 5 * W + 3 * W + kMaxMacro + 8 * (2 * W + 1) + 2 * W + W + kMaxMacro + 16 * W;
   }
   __host__ __device__ static size_t words(int W) {
     return (int_words(W) + 3) / 4 * 4 + kMaxMacro * sizeof(PMacro) / sizeof(int32_t);
   }
-  __device__ CtlView(int32_t* b, int W) {
-    tile_ctr = b; abort = b + 8; n_windows = b + 9; n_items = b + 10;
-    int32_t* p = b + 16;
-    win_m = p; p += W; win_s0 = p; p += W; win_s1 = p; p += W; win_nt1 = p; p += W;
-    win_nt2 = p; p += W; gathered = p; p += W; gu_done = p; p += W; dn_done = p; p += W;
-    merged = p; p += kMaxMacro; xseq = p; p += 8 * (2 * W + 1); ent = p; p += 2 * W; items = p;
-    pm = reinterpret_cast<PMacro*>(b + (int_words(W) + 3) / 4 * 4);
-    xstride = 2 * W + 1;
-  }
+  __device__ CtlView(int32_t* base, int W_) : b(base), W(W_) {}
+  __device__ int32_t* tile_ctr() const { return b; }
+  __device__ int32_t* abort() const { return b + 8; }
+  __device__ int32_t* n_windows() const { return b + 9; }
+  __device__ int32_t* n_items() const { return b + 10; }
+  __device__ int32_t* win_m() const { return b + 16; }
+  __device__ int32_t* win_s0() const { return b + 16 + W; }
+  __device__ int32_t* win_s1() const { return b + 16 + 2 * W; }
+  __device__ int32_t* win_nt1() const { return b + 16 + 3 * W; }
+  __device__ int32_t* win_nt2() const { return b + 16 + 4 * W; }
+  __device__ int32_t* gathered() const { return b + 16 + 5 * W; }
+  __device__ int32_t* gu_done() const { return b + 16 + 6 * W; }
+  __device__ int32_t* dn_done() const { return b + 16 + 7 * W; }
+  __device__ int32_t* merged() const { return b + 16 + 8 * W; }
+  // [8][2W + 1] per-XCD prefix of tile shares over the sequence
+  __device__ int32_t* xseq() const { return b + 16 + 8 * W + kMaxMacro; }
+  __device__ int xstride() const { return 2 * W + 1; }
+  // [2W] sequence entries: 2 * window + (0 gate/up, 1 down)
+  __device__ int32_t* ent() const { return xseq() + 8 * (2 * W + 1); }
+  // [W + kMaxMacro] mover items: window >= 0, merge m as -m - 1
+  __device__ int32_t* items() const { return ent() + 2 * W; }
+  // [W][2][8] tiles done per window, phase (gate/up, down) and XCD
+  __device__ int32_t* xdone() const { return items() + W + kMaxMacro; }
+  // [kMaxMacro] per-macrobatch buffers (copied from the kernel arguments, so
+  // runtime indexing does not force the arguments into scratch)
+  __device__ PMacro* pm() const { return reinterpret_cast<PMacro*>(b + (int_words(W) + 3) / 4 * 4); }
 };
 
 __global__ void k_fill(int32_t* p, int64_t n) {
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(256) void k_plan(const PKArgs a) {
   for (int m = 0; m < kMaxMacro; ++m) {                       // compile-time indices into the args
     if (m < a.n_macro) {
       for (int e = tid; e < nl1; e += blockDim.x) offs[m * nl1 + e] = a.mb[m].offsets[e];
-      if (tid == 0) c.pm[m] = a.mb[m];
+      if (tid == 0) c.pm()[m] = a.mb[m];
     }
   }
   __syncthreads();
@@ -190,8 +204,8 @@ __global__ __launch_bounds__(256) void k_plan(const PKArgs a) {
   if (sh_fail) {
     if (tid == 0) {
       set_status(a.status, MOK_ERR_CAPACITY);
-      *c.n_windows = 0;
-      *c.n_items = 0;
+      *c.n_windows() = 0;
+      *c.n_items() = 0;
     }
     return;
   }
@@ -201,18 +215,18 @@ __global__ __launch_bounds__(256) void k_plan(const PKArgs a) {
     for (int q = 0; q < ne; ++q) {
       const int w = ent[q] >> 1;
       const int32_t tk = (ent[q] & 1) ? wn2[w] : wn1[w];
-      c.xseq[tid * c.xstride + q] = acc;
+      c.xseq()[tid * c.xstride() + q] = acc;
       acc += tk / kXcds + (tid < tk % kXcds ? 1 : 0);
     }
-    c.xseq[tid * c.xstride + ne] = acc;
+    c.xseq()[tid * c.xstride() + ne] = acc;
   }
   for (int i = tid; i < W; i += blockDim.x) {
-    c.win_m[i] = wm[i]; c.win_s0[i] = ws0[i]; c.win_s1[i] = ws1[i];
-    c.win_nt1[i] = wn1[i]; c.win_nt2[i] = wn2[i];
+    c.win_m()[i] = wm[i]; c.win_s0()[i] = ws0[i]; c.win_s1()[i] = ws1[i];
+    c.win_nt1()[i] = wn1[i]; c.win_nt2()[i] = wn2[i];
   }
-  for (int i = tid; i < ne; i += blockDim.x) c.ent[i] = ent[i];
-  for (int i = tid; i < ni; i += blockDim.x) c.items[i] = items[i];
-  if (tid == 0) { *c.n_windows = W; *c.n_items = ni; }
+  for (int i = tid; i < ne; i += blockDim.x) c.ent()[i] = ent[i];
+  for (int i = tid; i < ni; i += blockDim.x) c.items()[i] = items[i];
+  if (tid == 0) { *c.n_windows() = W; *c.n_items() = ni; }
 }
 
 // Bounded wait by thread 0 for *ctr >= target: relaxed polls, then one
@@ -224,9 +238,9 @@ __device__ __forceinline__ bool wait_geq(int32_t* ctr, int32_t target, const Ctl
     int ok = 1;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(c.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+      if (__hip_atomic_load(c.abort(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
       if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout_ticks) {
-        __hip_atomic_store(c.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(c.abort(), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         set_status(a.status, MOK_ERR_DEVICE);
         ok = 0;
         break;
@@ -253,13 +267,47 @@ __device__ __forceinline__ void signal_add(int32_t* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A pointer the whole wave holds (its two halves moved to scalar registers).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Completion of a GEMM tile of one phase (gate/up or down) of a window.
+// Each XCD has its own L2, and an agent-scope release writes back all of it:
+// paying that per tile stalled every tile for the write-back of its whole
+// XCD's dirty lines.  So a tile only counts itself in per XCD (every wave
+// first waits until its stores are in the XCD's L2), and the tile that
+// completes its XCD's share of the phase does the one release add on the
+// phase counter, whose write-back covers every tile of that XCD: their stores
+// reached the same L2 before their counts did.  Consumers wait for the number
+// of XCDs that hold tiles of the phase (xcds_of).
+__device__ __forceinline__ int32_t share_of(int32_t tiles, int x) {
+  return tiles / kXcds + (x < tiles % kXcds ? 1 : 0);
+}
+__device__ __forceinline__ int32_t xcds_of(int32_t tiles) {
+  return tiles < kXcds ? tiles : kXcds;
+}
+__device__ __forceinline__ void signal_tile(int32_t* xcnt, int32_t share, int32_t* done) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t before = __hip_atomic_fetch_add(xcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1 == share)
+      __hip_atomic_fetch_add(done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Gather of window w by the waves first, first + step, ...: wave i takes
 // the slot pairs (s0 + 2 q, s0 + 2 q + 1), q = i, i + step, ...
 template <bool A_MX>
 __device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c, int w,
                                               int64_t first, int64_t step) {
-  const PMacro pm = c.pm[c.win_m[w]];
-  const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
+  const PMacro pm = c.pm()[c.win_m()[w]];
+  const int32_t s0 = c.win_s0()[w], s1 = c.win_s1()[w];
   const int64_t base = static_cast<int64_t>(w & 1) * a.M - s0;
   for (int64_t s = s0 + 2 * first; s < s1; s += 2 * step) {
     const int64_t t1 = pm.aos[s] / a.k;
@@ -280,10 +328,10 @@ __device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c,
 template <bool kFast>
 __device__ __forceinline__ bool merge_macro(const PKArgs& a, const CtlView& c, int32_t* sh, int m,
                                             int64_t first, int64_t step) {
-  const int W = *c.n_windows;
+  const int W = *c.n_windows();
   for (int w = 0; w < W; ++w)
-    if (c.win_m[w] == m && !wait_geq(&c.dn_done[w], c.win_nt2[w], c, a, sh)) return false;
-  const PMacro pm = c.pm[m];
+    if (c.win_m()[w] == m && !wait_geq(&c.dn_done()[w], xcds_of(c.win_nt2()[w]), c, a, sh)) return false;
+  const PMacro pm = c.pm()[m];
   const int32_t R = pm.offsets[a.n_local];
   for (int64_t s = first; s < R; s += step)
     merge_slot<kFast>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
@@ -292,35 +340,36 @@ __device__ __forceinline__ bool merge_macro(const PKArgs& a, const CtlView& c, i
 }
 
 // Movers: the item list in order, except window 0 (gathered by every
-// workgroup at the start) and the last macrobatch's merge, which they share
-// with the workers once the GEMMs are done (nothing else runs then, so it is
+// workgroup at the start) and the last macrobatch's merge, which every
+// workgroup shares once the GEMMs are done (nothing else runs then, so it is
 // spread over all CUs).  Between those two points the movers run beside the
 // GEMM workers and keep a moderate pace: faster movers there took HBM / L2
-// bandwidth from the workers' operand stream and slowed the layer.
+// bandwidth from the workers' operand stream and slowed the layer.  After
+// their last item they take GEMM tiles like the workers (with a single
+// window they have no item at all, and the GEMMs get every CU).  False when
+// the kernel aborts.
 template <bool A_MX>
-__device__ __forceinline__ void mover(const PKArgs& a, const CtlView& c, int32_t* sh) {
+__device__ __forceinline__ bool mover(const PKArgs& a, const CtlView& c, int32_t* sh) {
   const int wave = threadIdx.x / kWave;
   const int64_t mw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   const int64_t nmw = static_cast<int64_t>(a.n_move) * 4;
-  const int ni = *c.n_items;
+  const int ni = *c.n_items();
   for (int it = 0; it < ni; ++it) {
-    const int item = c.items[it];
+    const int item = c.items()[it];
     if (item >= 0) {
       const int w = item;
       if (w == 0) continue;
-      if (w >= 2 && !wait_geq(&c.gu_done[w - 2], c.win_nt1[w - 2], c, a, sh)) return;
+      if (w >= 2 && !wait_geq(&c.gu_done()[w - 2], xcds_of(c.win_nt1()[w - 2]), c, a, sh)) return false;
       gather_window<A_MX>(a, c, w, mw, nmw);
-      signal_add(&c.gathered[w]);
+      signal_add(&c.gathered()[w]);
     } else {
       const int m = -item - 1;
-      if (m == a.n_macro - 1) {
-        merge_macro<true>(a, c, sh, m, mw, static_cast<int64_t>(gridDim.x) * 4);
-      } else {
-        if (!merge_macro<false>(a, c, sh, m, mw, nmw)) return;
-        signal_add(&c.merged[m]);
-      }
+      if (m == a.n_macro - 1) continue;       // shared by every workgroup at the end
+      if (!merge_macro<false>(a, c, sh, m, mw, nmw)) return false;
+      signal_add(&c.merged()[m]);
     }
   }
+  return true;
 }
 
 // Operand formats of a persistent launch: bf16 activations and weights;
@@ -332,16 +381,21 @@ template <int F>
 __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, int32_t* sh,
                                              uint8_t* lds) {
   const int x = blockIdx.x % kXcds;
-  const int W = *c.n_windows, ne = 2 * W;
-  const int32_t* xs = c.xseq + x * c.xstride;
+  const int W = *c.n_windows(), ne = 2 * W;
+  const int32_t* xs = c.xseq() + x * c.xstride();
   const int32_t total = W > 0 ? xs[ne] : 0;
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2), n2 = (a.H + BN - 1) / BN;
   int ready_g1 = -1, ready_g2 = -1;   // last window whose G1 / G2 dependencies were acquired
   while (true) {
     if (threadIdx.x == 0)
-      sh[1] = __hip_atomic_fetch_add(&c.tile_ctr[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh[1] = __hip_atomic_fetch_add(&c.tile_ctr()[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int32_t lt = sh[1];
+    // uniform by construction (one value broadcast through LDS); saying so keeps
+    // everything derived from it -- tile coordinates, operand bases and the
+    // buffer descriptors -- in scalar registers, where the GEMM's main loop
+    // wants them (with a vector value the compiler re-derived the descriptors
+    // with v_readfirstlane in every k-step)
+    const int32_t lt = __builtin_amdgcn_readfirstlane(sh[1]);
     __syncthreads();
     if (lt >= total) return true;
     int lo = 0, hi = ne - 1;                     // last entry whose prefix <= lt
@@ -349,33 +403,49 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
       const int mid = (lo + hi + 1) >> 1;
       if (xs[mid] <= lt) lo = mid; else hi = mid - 1;
     }
-    const int w = c.ent[lo] >> 1, down = c.ent[lo] & 1;
-    const int32_t tk = down ? c.win_nt2[w] : c.win_nt1[w];
+    const int w = c.ent()[lo] >> 1, down = c.ent()[lo] & 1;
+    const int32_t tk = down ? c.win_nt2()[w] : c.win_nt1()[w];
     const int32_t q = tk / kXcds, r = tk % kXcds;
     const int te = x * q + (x < r ? x : r) + (lt - xs[lo]);
-    const int m = c.win_m[w];
+    const int m = c.win_m()[w];
     bool ok = true;
     if (!down && w != ready_g1) {
-      ok = wait_geq(&c.gathered[w], w == 0 ? static_cast<int32_t>(gridDim.x) : a.n_move, c, a, sh) &&
-           (w < 2 || wait_geq(&c.dn_done[w - 2], c.win_nt2[w - 2], c, a, sh));
+      // window 0 is in the ring before the kernel starts (a gather launch of its own)
+      ok = (w == 0 || wait_geq(&c.gathered()[w], a.n_move, c, a, sh)) &&
+           (w < 2 || wait_geq(&c.dn_done()[w - 2], xcds_of(c.win_nt2()[w - 2]), c, a, sh));
       ready_g1 = w;
     } else if (down && w != ready_g2) {
-      ok = wait_geq(&c.gu_done[w], c.win_nt1[w], c, a, sh) &&
-           (m < 2 || wait_geq(&c.merged[m - 2], a.n_move, c, a, sh));
+      ok = wait_geq(&c.gu_done()[w], xcds_of(c.win_nt1()[w]), c, a, sh) &&
+           (m < 2 || wait_geq(&c.merged()[m - 2], a.n_move, c, a, sh));
       ready_g2 = w;
     }
+    int32_t* xcnt = c.xdone() + (2 * w + down) * kXcds + x;
+    const int32_t xshare = share_of(tk, x);
     if (!ok) return false;
-    const PMacro pm = c.pm[m];
-    const int32_t s0 = c.win_s0[w], s1 = c.win_s1[w];
+    // The control block is written during the kernel, so its loads are vector
+    // loads, whose results the compiler keeps in VGPRs: every value the tile
+    // derives from them (operand bases, buffer descriptors) would then be
+    // re-read with v_readfirstlane inside the GEMM's k-loop.  They are uniform;
+    // moving them to scalar registers here keeps the k-loop as in the
+    // standalone GEMM kernels.
+    const PMacro pm = c.pm()[m];
+    const int32_t* offs = uniform_ptr(pm.offsets);
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(c.win_s0()[w]);
+    const int32_t s1 = __builtin_amdgcn_readfirstlane(c.win_s1()[w]);
     int e, row0, nrows, ntile;
-    if (!tile_of(pm.offsets, a.n_local, s0, s1, down ? n2 : n1, te, e, row0, nrows, ntile)) {
-      signal_add(down ? &c.dn_done[w] : &c.gu_done[w]);   // cannot happen: counts come from the plan
-      continue;
+    const bool have = tile_of(offs, a.n_local, s0, s1, down ? n2 : n1, te, e, row0, nrows, ntile);
+    e = __builtin_amdgcn_readfirstlane(e);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
+    ntile = __builtin_amdgcn_readfirstlane(ntile);
+    if (!have) {
+      signal_tile(xcnt, xshare, down ? &c.dn_done()[w] : &c.gu_done()[w]);   // cannot happen: counts
+      continue;                                                          // come from the plan
     }
     const int32_t rb = static_cast<int32_t>(
         ((static_cast<int64_t>(w & 1) * a.M - s0) % a.S + a.S) % a.S);
     GemmParams g{};
-    g.offsets = pm.offsets; g.n_local = a.n_local; g.s_begin = s0; g.s_end = s1;
+    g.offsets = offs; g.n_local = a.n_local; g.s_begin = s0; g.s_end = s1;
     if (!down) {
       g.A = a.ring; g.A_scales = a.ring_sc; g.a_rows = a.S; g.a_row_base = rb;
       g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
@@ -386,18 +456,18 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
         gemm_tile_mx8<EPI_SWIGLU_MX>(g, e, row0, nrows, ntile, lds);
       else
         gemm_tile<F == kPMxAct, F == kPMxAct ? EPI_SWIGLU_MX : EPI_SWIGLU_BF16>(g, e, row0, nrows, ntile, lds);
-      signal_add(&c.gu_done[w]);
+      signal_tile(xcnt, xshare, &c.gu_done()[w]);
     } else {
       g.A = a.act; g.A_scales = a.act_sc; g.a_rows = a.act_rows; g.a_row_base = rb;
       g.W = a.w_d; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.I;
       g.N = a.H; g.I = 0;
-      g.C = pm.y; g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
+      g.C = uniform_ptr(pm.y); g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
       g.n_tiles = n2; g.w_packed = a.w_packed;
       if constexpr (F == kPMx8)
         gemm_tile_mx8<EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
       else
         gemm_tile<F == kPMxAct, EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
-      signal_add(&c.dn_done[w]);
+      signal_tile(xcnt, xshare, &c.dn_done()[w]);
     }
   }
 }
@@ -414,19 +484,12 @@ void k_persist(const PKArgs a) {
   // (gemm_tile opens with one; signal_add closes each tile with one).
   int32_t* sh = reinterpret_cast<int32_t*>(lds);
   CtlView c(a.ctl, a.max_win);
-  const int wave = threadIdx.x / kWave;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave, ngw = static_cast<int64_t>(gridDim.x) * 4;
-  // nothing can run before window 0 is in the ring: every workgroup gathers it
-  if (*c.n_windows > 0) {
-    gather_window<A_MX>(a, c, 0, gw, ngw);
-    signal_add(&c.gathered[0]);
-  }
-  if (static_cast<int>(blockIdx.x) < a.n_move) {
-    mover<A_MX>(a, c, sh);
-  } else if (worker_tiles<F>(a, c, sh, lds) && *c.n_items > 0) {
-    // GEMMs done: help the movers with the last macrobatch's merge
-    merge_macro<true>(a, c, sh, a.n_macro - 1, gw, ngw);
-  }
+  // Window 0 is gathered before the kernel and the last macrobatch merged
+  // after it, by launches of their own at full occupancy: nothing else could
+  // run beside them, and one workgroup per CU moved rows at half the rate.
+  if (static_cast<int>(blockIdx.x) < a.n_move && !mover<A_MX>(a, c, sh)) return;
+  // workers from the start, movers after their items
+  worker_tiles<F>(a, c, sh, lds);
 }
 
 }  // namespace
@@ -437,13 +500,11 @@ size_t persistent_ws_bytes(int64_t total_windows) {
 }
 
 mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
-  // automatic split (measured on 256 CUs, Kimi-shaped share): 1/8 of the CUs
-  // move data for one macrobatch, 3/16 when several stream through the ring
-  // (the movers then also carry the merges that overlap the next gathers)
-  const int n_move = a.n_move > 0 ? a.n_move
-                                  : (a.n_macro > 1 ? (3 * a.n_cus) / 16 : a.n_cus / 8) > 8
-                                        ? (a.n_macro > 1 ? (3 * a.n_cus) / 16 : a.n_cus / 8)
-                                        : 8;
+  // automatic split: a quarter of the CUs move data.  Movers take GEMM tiles
+  // once their gathers and merges are done, so more of them cost the GEMMs
+  // little, while fewer slow every window's gather (measured on 256 CUs, the
+  // Kimi-shaped share at M = 4096: 8 movers 1.68 ms, 16 1.13, 64 0.83).
+  const int n_move = a.n_move > 0 ? a.n_move : (a.n_cus / 4 > 8 ? a.n_cus / 4 : 8);
   if (n_move < 1 || n_move > a.n_cus - kXcds) return MOK_ERR_INVALID_ARG;
   const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
   const void* fn = !mx ? reinterpret_cast<const void*>(&k_persist<kPBf16>)
@@ -477,8 +538,20 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(256),
                        plan_lds_words(gn, a.n_local, k.max_win) * sizeof(int32_t), s, k);
     if (hipGetLastError() != hipSuccess) return MOK_ERR_HIP;
+    // window 0 of the group: the first macrobatch's slots [0, M) into ring half 0
+    const MacroBuffers& b0 = a.mb[g0];
+    if (launch_gather(a.x.part_ptr, a.x.n_partitions, a.x.part_rows, a.H, a.k, b0.aos, b0.offsets,
+                      a.n_local, 0, a.M < a.cap ? a.M : a.cap, a.ring, a.ring_sc, a.S,
+                      a.act_format, a.status, s) != hipSuccess)
+      return MOK_ERR_HIP;
     void* args[] = {&k};
     if (hipLaunchCooperativeKernel(fn, dim3(a.n_cus), dim3(256), args, 0, s) != hipSuccess)
+      return MOK_ERR_HIP;
+    // the group's last macrobatch, merged once every down tile is done
+    const MacroBuffers& bl = a.mb[g0 + gn - 1];
+    if (launch_combine_slots(bl.y, a.cap, bl.aos, bl.offsets, a.n_local, a.cap, bl.soa, bl.gate,
+                             a.k, a.H, bl.out.part_ptr, bl.out.n_partitions, bl.out.part_rows,
+                             a.status, true, s) != hipSuccess)
       return MOK_ERR_HIP;
   }
   return MOK_OK;
