@@ -442,6 +442,20 @@ mok_status mok_moe_forward(const mok_layer_desc* desc, const float* logits, int3
                            const mok_tokens* x, const void* w_gate_up, const void* w_down,
                            const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The fused layer from the router weights (article, routing paragraph: the
+ * router scores every token against every expert, then picks): the router
+ * GEMM of the tokens' rows x with w_router (bf16 [n_experts][H], nn.Linear
+ * layout; H a multiple of 16) as mok_route_topk_gemm computes it (fp32 sums,
+ * splits of H added in split order), whose pick kernel also counts the local
+ * picks for the schedule; then the steps of mok_moe_forward.  ws: at least
+ * mok_forward_router_workspace_size(desc, T) bytes (the fused call's bytes
+ * plus the router GEMM's partial sums). */
+size_t mok_forward_router_workspace_size(const mok_layer_desc* desc, int32_t T);
+mok_status mok_moe_forward_router(const mok_layer_desc* desc, const void* w_router, int32_t T,
+                                  const mok_tokens* x, const void* w_gate_up, const void* w_down,
+                                  const mok_tokens* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* The fused layer from routing decided elsewhere (one GPU's expert share:
  * the sources route their own tokens, and this GPU schedules every source's
  * picks of its local experts; article, routing and pull-dispatch

@@ -113,3 +113,73 @@ def test_route_gemm_empty_and_errors():
     assert e.value.status == mok.MOK_ERR_WORKSPACE
     with pytest.raises(mok.MokError):
         mok.mok_route_topk_gemm(x, w, 4, 60, 8, 2, ws, idx, gate)  # H not a multiple of 16
+
+
+def _router_layer(name, T, H, I, E, k, part_rows, seed, integer):
+    """A layer whose routing comes from a router GEMM: tokens x [T][H] (in
+    partitions of part_rows rows), router rows w_r [E][H]; the workload's
+    logits are the oracle's router_logits of them (exact in fp32 for integer
+    inputs)."""
+    import dataclasses
+    base = W.logits_workload(name, seed, T=T, H=H, I=I, E=E, k=k, x_std=1.0, w_std=0.02)
+    if integer:
+        x = W.small_int_bf16(seed + 1, (T, H), -2, 2)
+        w_r = W.small_int_bf16(seed + 2, (E, H), -2, 2)
+    else:
+        x, w_r = W.router_inputs(seed + 3, T, H, E)
+    logits = oracle.router_logits(x, w_r).astype(np.float32)
+    wl = dataclasses.replace(base, x=x, logits=logits, n_partitions=T // part_rows,
+                             part_rows=part_rows)
+    return wl, w_r
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fused_layer_from_router_weights_integer_inputs(mode):
+    """mok_moe_forward_router (router GEMM + pick + counts, schedule, gather, FFN,
+    merge in one call) on integer-valued tokens and router rows: the routing is
+    the oracle's exactly, so the merged rows meet the oracle's rounding bands."""
+    import token_dispatch_grouped_top_amd as mok
+    from gpu_harness import DeviceWorkload, check_layer_out
+    wl, w_r = _router_layer("router_int", 768, 256, 320, 16, 2, 256, 51, True)
+    assert np.abs(wl.logits).max() < 2 ** 24
+    dw = DeviceWorkload(wl)
+    d = dw.desc(mode=mode, minibatch=512, wait_timeout_us=500_000)
+    ws = torch.empty(mok.mok_forward_router_workspace_size(d, wl.T), dtype=torch.uint8,
+                     device="cuda")
+    mok.mok_moe_forward_router(d, to_dev(w_r), wl.T, dw.x, dw.w_gu, dw.w_d, dw.outs[0], ws)
+    assert mok.mok_device_status(ws) == 0
+    r = oracle.forward(wl)
+    check_layer_out(dw.out_rows(dw.outs[0]), wl, r, f"fused from router weights, mode {mode}")
+
+
+def test_fused_layer_from_router_weights_matches_two_calls():
+    """On Gaussian inputs with the Mixtral-shaped routing (T = 4096, E = 8,
+    H = 4096, k = 2; I = 1024 to keep the test short):
+    the fused router form writes the same bits as mok_route_topk_gemm followed
+    by mok_moe_forward_routed (the same kernels decide the picks), and a
+    smaller workspace is refused."""
+    import token_dispatch_grouped_top_amd as mok
+    from gpu_harness import DeviceWorkload
+    wl, w_r = _router_layer("router_gauss", 4096, 4096, 1024, 8, 2, 1024, 52, False)
+    dw = DeviceWorkload(wl, n_out=2)
+    d = dw.desc(max_rows=wl.T * wl.k, weights_packed=1)
+    w_gu, w_d = dw.weights(d)
+    wr = to_dev(w_r)
+    n = mok.mok_forward_router_workspace_size(d, wl.T)
+    assert n > mok.mok_forward_workspace_size(d, wl.T, 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mok.MokError) as e:
+        mok.mok_moe_forward_router(d, wr, wl.T, dw.x, w_gu, w_d, dw.outs[0], ws, n - 1)
+    assert e.value.status == mok.MOK_ERR_WORKSPACE
+    mok.mok_moe_forward_router(d, wr, wl.T, dw.x, w_gu, w_d, dw.outs[0], ws)
+    assert mok.mok_device_status(ws) == 0
+    x_flat = to_dev(wl.x)
+    rws = torch.empty(mok.mok_route_gemm_workspace_size(wl.T, wl.E, wl.H), dtype=torch.uint8,
+                      device="cuda")
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    mok.mok_route_topk_gemm(x_flat, wr, wl.T, wl.H, wl.E, wl.k, rws, idx, gate)
+    mok.mok_moe_forward_routed(d, idx, gate, wl.T, dw.x, w_gu, w_d, dw.outs[1], ws)
+    assert mok.mok_device_status(ws) == 0
+    for a, b in zip(dw.outs[0].parts, dw.outs[1].parts):
+        assert torch.equal(a, b)

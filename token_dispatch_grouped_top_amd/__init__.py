@@ -82,6 +82,8 @@ _SIGS = {
     "mok_forward_workspace_size": (_SZ, [_DESC, _I32, _I32]),
     "mok_moe_forward": (C.c_int, [_DESC, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
     "mok_moe_forward_routed": (C.c_int, [_DESC, _P, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
+    "mok_forward_router_workspace_size": (_SZ, [_DESC, _I32]),
+    "mok_moe_forward_router": (C.c_int, [_DESC, _P, _I32, _TOK, _P, _P, _TOK, _P, _SZ, _P]),
     "mok_moe_forward_batches": (C.c_int, [_DESC, _I32, _P, _P, _I32, _TOK, _P, _P, _TOK, _P,
                                           _SZ, _P]),
     "mok_tune_forward": (C.c_int, [_DESC, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _I32, _TOK,
@@ -311,6 +313,19 @@ def mok_moe_forward(desc: mok_layer_desc, logits, T: int, x: Tokens, w_gate_up, 
     _check(_lib.mok_moe_forward(C.byref(desc), _ptr(logits), T, C.byref(x.c), _ptr(w_gate_up),
                                 _ptr(w_down), C.byref(out.c), _ptr(ws), ws_bytes,
                                 _stream(stream)), "mok_moe_forward")
+
+
+def mok_forward_router_workspace_size(desc: mok_layer_desc, T: int) -> int:
+    return int(_lib.mok_forward_router_workspace_size(C.byref(desc), T))
+
+
+def mok_moe_forward_router(desc: mok_layer_desc, w_router, T: int, x: Tokens, w_gate_up, w_down,
+                           out: Tokens, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.mok_moe_forward_router(C.byref(desc), _ptr(w_router), T, C.byref(x.c),
+                                       _ptr(w_gate_up), _ptr(w_down), C.byref(out.c), _ptr(ws),
+                                       ws_bytes, _stream(stream)), "mok_moe_forward_router")
 
 
 def mok_moe_forward_routed(desc: mok_layer_desc, topk_idx, topk_gate, T: int, x: Tokens,

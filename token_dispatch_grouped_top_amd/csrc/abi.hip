@@ -206,9 +206,10 @@ mok_status mok_route_topk_gemm(const void* x, const void* w_router, int32_t T, i
   if (T == 0) return MOK_OK;
   if (!x || !w_router || !topk_idx || !topk_gate || !ws) return MOK_ERR_INVALID_ARG;
   if (ws_bytes < mok_route_gemm_workspace_size(T, E, H)) return MOK_ERR_WORKSPACE;
-  return hip_status(launch_route_topk_gemm(static_cast<const uint16_t*>(x),
+  return hip_status(launch_route_topk_gemm(static_cast<const uint16_t*>(x), nullptr, 0,
                                            static_cast<const uint16_t*>(w_router), T, H, E, k,
-                                           static_cast<float*>(ws), topk_idx, topk_gate, stream));
+                                           static_cast<float*>(ws), topk_idx, topk_gate,
+                                           RouteCount{}, stream));
 }
 
 size_t mok_schedule_workspace_size(int64_t T, int32_t k, int32_t n_local) {
@@ -606,24 +607,31 @@ namespace {
 
 // The fused layer.  logits non-null (then n_macro = 1): the routing of the T
 // tokens is computed here, from fp32 logits [T][n_experts], into the
-// workspace; otherwise topk_idx / topk_gate hold each macrobatch's routing.
+// workspace; w_router non-null (then n_macro = 1): from the router GEMM of
+// the tokens' rows x with the bf16 router rows w_router [n_experts][H], its
+// per-split partial sums in the workspace past the plan's bytes; otherwise
+// topk_idx / topk_gate hold each macrobatch's routing.
 mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float* logits,
-                        const int32_t* const* topk_idx, const float* const* topk_gate, int32_t T,
-                        const mok_tokens* x, const void* w_gate_up, const void* w_down,
-                        const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        const void* w_router, const int32_t* const* topk_idx,
+                        const float* const* topk_gate, int32_t T, const mok_tokens* x,
+                        const void* w_gate_up, const void* w_down, const mok_tokens* out,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!desc_ok(desc) || n_macro < 1 || T < 0 || !tokens_ok(x, T) || !w_gate_up || !w_down ||
       !out || !ws || !weights_ok(desc))
     return MOK_ERR_INVALID_ARG;
-  if (logits ? (n_macro != 1 || desc->n_experts > 4096)
-             : (!topk_idx || !topk_gate))
+  const bool route_here = logits || w_router;
+  if (route_here ? (n_macro != 1 || desc->n_experts > 4096)
+                 : (!topk_idx || !topk_gate))
     return MOK_ERR_INVALID_ARG;
   for (int m = 0; m < n_macro; ++m) {
-    if (T > 0 && !logits && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
+    if (T > 0 && !route_here && (!topk_idx[m] || !topk_gate[m])) return MOK_ERR_INVALID_ARG;
     if (!tokens_ok(&out[m], T)) return MOK_ERR_INVALID_ARG;
   }
   Plan p;
   if (!make_plan(desc, T, n_macro, p)) return MOK_ERR_UNSUPPORTED;
-  if (ws_bytes < p.total) return MOK_ERR_WORKSPACE;
+  const size_t router_bytes =
+      w_router && T > 0 ? mok_route_gemm_workspace_size(T, desc->n_experts, desc->hidden) : 0;
+  if (ws_bytes < p.total + router_bytes) return MOK_ERR_WORKSPACE;
 
   const mok_layer_desc& d = *desc;
   const bool mx = d.act_format == MOK_ACT_MXFP8_E4M3;
@@ -634,7 +642,7 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
   const int n_cus = device_cus();
   const int32_t n_clear = static_cast<int32_t>(kAlign / 4) + (p.split ? n_cus : 0);
   SchedWs sw = sched_ws_carve(at<void>(ws, p.off_sched), p.A, d.n_local);
-  const int32_t n_clear2 = logits ? sw.nblk * d.n_local : 0;
+  const int32_t n_clear2 = route_here ? sw.nblk * d.n_local : 0;
   hipLaunchKernelGGL(k_zero2, dim3(n_clear2 > 4096 ? 16 : 1), dim3(256), 0, stream, status, n_clear,
                      sw.blk_counts, n_clear2);
   if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
@@ -651,17 +659,25 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
     mb[m].soa = at<int32_t>(ws, p.off_soa + m * p.per_macro_soa);
     mb[m].aos = at<int32_t>(ws, p.off_aos + m * p.per_macro_aos);
     mb[m].win = at<int32_t>(ws, p.off_win + m * p.per_macro_win);
-    mb[m].gate = logits ? route_gate : topk_gate[m];
+    mb[m].gate = route_here ? route_gate : topk_gate[m];
     mb[m].y = at<uint16_t>(ws, p.off_y + static_cast<size_t>(m % p.n_ybuf) * p.cap * d.hidden * 2);
     mb[m].out = out[m];
   }
   // Route (logits form), schedule, windows and capacity check for every
   // macrobatch first: two launches each, reading only routing.
+  if (w_router && T > 0) {   // router GEMM + pick, counting the local picks as it goes
+    RouteCount rc;
+    rc.base = d.expert_base; rc.n_local = d.n_local; rc.blk_counts = sw.blk_counts; rc.nblk = sw.nblk;
+    err = launch_route_topk_gemm(nullptr, x->part_ptr, x->part_rows,
+                                 static_cast<const uint16_t*>(w_router), T, d.hidden, d.n_experts,
+                                 d.top_k, at<float>(ws, p.total), route_idx, route_gate, rc, stream);
+    if (err != hipSuccess) return hip_status(err);
+  }
   for (int m = 0; m < n_macro; ++m) {
-    int32_t* idx = logits ? route_idx : const_cast<int32_t*>(T > 0 ? topk_idx[m] : nullptr);
+    int32_t* idx = route_here ? route_idx : const_cast<int32_t*>(T > 0 ? topk_idx[m] : nullptr);
     err = launch_route_schedule(logits, d.n_experts, route_gate, idx, T, d.top_k, d.expert_base,
                                 d.n_local, mb[m].counts, mb[m].offsets, mb[m].soa, mb[m].aos, sw,
-                                p.M, p.nwin, mb[m].win, p.cap, status, stream);
+                                p.M, p.nwin, mb[m].win, p.cap, status, stream, w_router != nullptr);
     if (err != hipSuccess) return hip_status(err);
   }
 
@@ -722,16 +738,16 @@ mok_status mok_moe_forward_batches(const mok_layer_desc* desc, int32_t n_macro,
                                    int32_t T, const mok_tokens* x, const void* w_gate_up,
                                    const void* w_down, const mok_tokens* out, void* ws,
                                    size_t ws_bytes, hipStream_t stream) {
-  return mok::forward_impl(desc, n_macro, nullptr, topk_idx, topk_gate, T, x, w_gate_up, w_down,
-                           out, ws, ws_bytes, stream);
+  return mok::forward_impl(desc, n_macro, nullptr, nullptr, topk_idx, topk_gate, T, x, w_gate_up,
+                           w_down, out, ws, ws_bytes, stream);
 }
 
 mok_status mok_moe_forward_routed(const mok_layer_desc* desc, const int32_t* topk_idx,
                                   const float* topk_gate, int32_t T, const mok_tokens* x,
                                   const void* w_gate_up, const void* w_down, const mok_tokens* out,
                                   void* ws, size_t ws_bytes, hipStream_t stream) {
-  return mok::forward_impl(desc, 1, nullptr, &topk_idx, &topk_gate, T, x, w_gate_up, w_down, out,
-                           ws, ws_bytes, stream);
+  return mok::forward_impl(desc, 1, nullptr, nullptr, &topk_idx, &topk_gate, T, x, w_gate_up,
+                           w_down, out, ws, ws_bytes, stream);
 }
 
 mok_status mok_moe_forward(const mok_layer_desc* desc, const float* logits, int32_t T,
@@ -739,8 +755,25 @@ mok_status mok_moe_forward(const mok_layer_desc* desc, const float* logits, int3
                            const mok_tokens* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T > 0 && !logits) return MOK_ERR_INVALID_ARG;
   static const float kNoLogits = 0.0f;     // T = 0: nothing is read
-  return mok::forward_impl(desc, 1, T > 0 ? logits : &kNoLogits, nullptr, nullptr, T, x,
+  return mok::forward_impl(desc, 1, T > 0 ? logits : &kNoLogits, nullptr, nullptr, nullptr, T, x,
                            w_gate_up, w_down, out, ws, ws_bytes, stream);
+}
+
+size_t mok_forward_router_workspace_size(const mok_layer_desc* desc, int32_t T) {
+  const size_t base = mok_forward_workspace_size(desc, T, 1);
+  if (base == 0) return 0;
+  return base + (T > 0 ? mok_route_gemm_workspace_size(T, desc->n_experts, desc->hidden) : 0);
+}
+
+mok_status mok_moe_forward_router(const mok_layer_desc* desc, const void* w_router, int32_t T,
+                                  const mok_tokens* x, const void* w_gate_up, const void* w_down,
+                                  const mok_tokens* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!desc || (T > 0 && !w_router)) return MOK_ERR_INVALID_ARG;
+  if (desc->hidden % 16 != 0) return MOK_ERR_INVALID_ARG;
+  static const float kNoLogits = 0.0f;     // T = 0: no route at all
+  return mok::forward_impl(desc, 1, T > 0 ? nullptr : &kNoLogits, T > 0 ? w_router : nullptr,
+                           nullptr, nullptr, T, x, w_gate_up, w_down, out, ws, ws_bytes, stream);
 }
 
 mok_status mok_tune_forward(const mok_layer_desc* desc, const int32_t* minibatch,

@@ -113,9 +113,19 @@ __device__ __forceinline__ void set_status(int32_t* st, int32_t code) {
 // --------------------------------------------------------- launchers
 // All launchers return hipSuccess or the launch error.
 int32_t route_gemm_splits(int32_t T, int32_t E, int32_t H);
-hipError_t launch_route_topk_gemm(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
-                                  int32_t E, int32_t k, float* partial, int32_t* idx, float* gate,
-                                  hipStream_t s);
+// Counting of local picks into the schedule's chunk counts by a route kernel
+// (blk_counts null: no counting).
+struct RouteCount {
+  int32_t base = 0, n_local = 0;
+  int32_t* blk_counts = nullptr;
+  int32_t nblk = 0;
+};
+// Router GEMM + pick; token rows from x [T][H] or, x_parts non-null, from
+// partitions of x_part_rows rows.
+hipError_t launch_route_topk_gemm(const uint16_t* x, void* const* x_parts, int32_t x_part_rows,
+                                  const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+                                  int32_t k, float* partial, int32_t* idx, float* gate,
+                                  const RouteCount& rc, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                              int32_t* idx, float* gate, hipStream_t s);
 
@@ -136,14 +146,16 @@ hipError_t launch_windows(const int32_t* offsets, int32_t n_local, int32_t M, in
 // The fused layer's schedule.  route_logits non-null: the route of the T
 // tokens from fp32 logits [T][E] writes idx / gate and counts its local picks
 // into the chunk counts (zeroed by the caller beforehand) in the same launch;
-// null: idx is given and counted by the count kernel.  Then the scatter,
+// null: idx is given and counted by the count kernel (counted: the caller's
+// route already filled the chunk counts).  Then the scatter,
 // which also writes the window table (M, nwin) and raises MOK_ERR_CAPACITY in
 // *status when R > cap.  Two launches either way.
 hipError_t launch_route_schedule(const float* route_logits, int32_t E, float* gate,
                                  int32_t* idx, int64_t T, int32_t k, int32_t expert_base,
                                  int32_t n_local, int32_t* counts, int32_t* offsets, int32_t* soa,
                                  int32_t* aos, const SchedWs& w, int32_t M, int32_t nwin,
-                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s);
+                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s,
+                                 bool counted = false);
 hipError_t launch_route_count(const float* logits, int32_t T, int32_t E, int32_t k,
                               int32_t expert_base, int32_t n_local, int32_t* idx, float* gate,
                               int32_t* blk_counts, int32_t nblk, hipStream_t s);

@@ -155,7 +155,8 @@ constexpr int kRgRows = kRgTok + kRgExp;                   // LDS rows per buffe
 constexpr int kRgLoads = kRgRows * kRgRowB / (256 * 16);   // 16-byte loads per thread: 6
 
 __global__ __launch_bounds__(4 * kWave)
-void k_router_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+void k_router_partial(const uint16_t* __restrict__ x, void* const* __restrict__ x_parts,
+                      int32_t x_part_rows, const uint16_t* __restrict__ wr,
                       int32_t T, int32_t H, int32_t E, int32_t kchunk,
                       float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][kRgRows * kRgRowB];
@@ -176,7 +177,11 @@ void k_router_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict
     const uint16_t* base;
     if (row < kRgTok) {
       const int t = t0 + row < T ? t0 + row : T - 1;
-      base = x + static_cast<int64_t>(t) * H;
+      // token rows: one array x[T][H], or partitions (row t % part_rows of
+      // partition t / part_rows)
+      base = x_parts ? static_cast<const uint16_t*>(x_parts[t / x_part_rows]) +
+                           static_cast<int64_t>(t % x_part_rows) * H
+                     : x + static_cast<int64_t>(t) * H;
     } else {
       const int e = e0 + row - kRgTok < E ? e0 + row - kRgTok : E - 1;
       base = wr + static_cast<int64_t>(e) * H;
@@ -250,7 +255,8 @@ void k_router_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict
 template <int VPL>
 __global__ __launch_bounds__(kRouteWaves * kWave)
 void k_route_topk_sum(const float* __restrict__ partial, int32_t n_split, int32_t T, int32_t E,
-                      int32_t k, int32_t* __restrict__ idx, float* __restrict__ gate) {
+                      int32_t k, int32_t* __restrict__ idx, float* __restrict__ gate, int32_t base,
+                      int32_t n_local, int32_t* __restrict__ blk_counts, int32_t nblk) {
   const int lane = lane_id();
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteWaves + threadIdx.x / kWave;
   if (t >= T) return;
@@ -279,7 +285,13 @@ void k_route_topk_sum(const float* __restrict__ partial, int32_t n_split, int32_
 #pragma unroll
   for (int i = 0; i < VPL; ++i)
     if (lane + kWave * i >= E) v[i] = -__builtin_inff();
-  pick_topk<VPL>(v, E, k, t, idx, gate);
+  const int e = pick_topk<VPL>(v, E, k, t, idx, gate) - base;
+  // the fused layer's schedule counts (as k_route_count)
+  if (blk_counts && lane < k && e >= 0 && e < n_local) {
+    const int64_t chunk = (t * k + lane) / kSchedChunk;
+    __hip_atomic_fetch_add(blk_counts + static_cast<int64_t>(e) * nblk + chunk, 1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int VPL>
@@ -303,10 +315,10 @@ hipError_t launch_count_vpl(const float* logits, int32_t T, int32_t E, int32_t k
 
 template <int VPL>
 hipError_t launch_sum_vpl(const float* partial, int32_t n_split, int32_t T, int32_t E, int32_t k,
-                          int32_t* idx, float* gate, hipStream_t s) {
+                          int32_t* idx, float* gate, const RouteCount& rc, hipStream_t s) {
   dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
   hipLaunchKernelGGL(k_route_topk_sum<VPL>, grid, dim3(kRouteWaves * kWave), 0, s, partial, n_split,
-                     T, E, k, idx, gate);
+                     T, E, k, idx, gate, rc.base, rc.n_local, rc.blk_counts, rc.nblk);
   return hipGetLastError();
 }
 
@@ -324,24 +336,25 @@ int32_t route_gemm_splits(int32_t T, int32_t E, int32_t H) {
   return static_cast<int32_t>(ks < 1 ? 1 : ks);
 }
 
-hipError_t launch_route_topk_gemm(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
-                                  int32_t E, int32_t k, float* partial, int32_t* idx, float* gate,
-                                  hipStream_t s) {
+hipError_t launch_route_topk_gemm(const uint16_t* x, void* const* x_parts, int32_t x_part_rows,
+                                  const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+                                  int32_t k, float* partial, int32_t* idx, float* gate,
+                                  const RouteCount& rc, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int32_t ks = route_gemm_splits(T, E, H);
   const int32_t kchunk = ((H + ks - 1) / ks + kRgK - 1) / kRgK * kRgK;
   dim3 grid((T + kRgTok - 1) / kRgTok, (E + kRgExp - 1) / kRgExp, ks);
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(4 * kWave), 0, s, x, w_router, T, H, E, kchunk,
-                     partial);
+  hipLaunchKernelGGL(k_router_partial, grid, dim3(4 * kWave), 0, s, x, x_parts, x_part_rows,
+                     w_router, T, H, E, kchunk, partial);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (E <= 64) return launch_sum_vpl<1>(partial, ks, T, E, k, idx, gate, s);
-  if (E <= 128) return launch_sum_vpl<2>(partial, ks, T, E, k, idx, gate, s);
-  if (E <= 256) return launch_sum_vpl<4>(partial, ks, T, E, k, idx, gate, s);
-  if (E <= 512) return launch_sum_vpl<8>(partial, ks, T, E, k, idx, gate, s);
-  if (E <= 1024) return launch_sum_vpl<16>(partial, ks, T, E, k, idx, gate, s);
-  if (E <= 2048) return launch_sum_vpl<32>(partial, ks, T, E, k, idx, gate, s);
-  return launch_sum_vpl<64>(partial, ks, T, E, k, idx, gate, s);
+  if (E <= 64) return launch_sum_vpl<1>(partial, ks, T, E, k, idx, gate, rc, s);
+  if (E <= 128) return launch_sum_vpl<2>(partial, ks, T, E, k, idx, gate, rc, s);
+  if (E <= 256) return launch_sum_vpl<4>(partial, ks, T, E, k, idx, gate, rc, s);
+  if (E <= 512) return launch_sum_vpl<8>(partial, ks, T, E, k, idx, gate, rc, s);
+  if (E <= 1024) return launch_sum_vpl<16>(partial, ks, T, E, k, idx, gate, rc, s);
+  if (E <= 2048) return launch_sum_vpl<32>(partial, ks, T, E, k, idx, gate, rc, s);
+  return launch_sum_vpl<64>(partial, ks, T, E, k, idx, gate, rc, s);
 }
 
 hipError_t launch_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,

@@ -239,11 +239,14 @@ hipError_t launch_route_schedule(const float* route_logits, int32_t E, float* ga
                                  int32_t* idx, int64_t T, int32_t k, int32_t expert_base,
                                  int32_t n_local, int32_t* counts, int32_t* offsets, int32_t* soa,
                                  int32_t* aos, const SchedWs& w, int32_t M, int32_t nwin,
-                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s) {
+                                 int32_t* win_seg, int32_t cap, int32_t* status, hipStream_t s,
+                                 bool counted) {
   if (n_local > kMaxLocal) return hipErrorInvalidValue;
   const int64_t A = T * k;
-  hipError_t e;
-  if (route_logits && T > 0) {
+  hipError_t e = hipSuccess;
+  if (counted && T > 0) {
+    // the chunk counts come from the caller's route
+  } else if (route_logits && T > 0) {
     e = launch_route_count(route_logits, static_cast<int32_t>(T), E, k, expert_base, n_local, idx,
                            gate, w.blk_counts, w.nblk, s);
   } else {
