@@ -321,6 +321,17 @@ def silu_and_grad(g: np.ndarray):
     return g * s, s * (1.0 + g * (1.0 - s))
 
 
+def swiglu_backward_values(h: np.ndarray, da: np.ndarray) -> np.ndarray:
+    """Backward of a = SiLU(g) u per row, fp64: h = [g, u] [n, 2I], da [n, I]
+    -> dh = [dg, du] = [da u SiLU'(g), da SiLU(g)] [n, 2I]."""
+    h = np.asarray(h, np.float64)
+    da = np.asarray(da, np.float64)
+    I = da.shape[1]
+    g, u = h[:, :I], h[:, I:]
+    sl, dsl = silu_and_grad(g)
+    return np.concatenate([da * u * dsl, da * sl], axis=1)
+
+
 def ffn_backward_values(x: np.ndarray, expert_of_row, w_gu: np.ndarray, w_d: np.ndarray,
                         dy: np.ndarray):
     """Backward of the expert SwiGLU FFN per row, all fp64 values: with
@@ -336,11 +347,7 @@ def ffn_backward_values(x: np.ndarray, expert_of_row, w_gu: np.ndarray, w_d: np.
     dx = np.zeros_like(x)
     for e in np.unique(eor):
         r = np.nonzero(eor == e)[0]
-        h = x[r] @ w_gu[e].T
-        g, u = h[:, :I], h[:, I:]
-        da = dy[r] @ w_d[e]
-        sl, dsl = silu_and_grad(g)
-        dh[r] = np.concatenate([da * u * dsl, da * sl], axis=1)
+        dh[r] = swiglu_backward_values(x[r] @ w_gu[e].T, dy[r] @ w_d[e])
         dx[r] = dh[r] @ w_gu[e]
     return dh, dx
 
@@ -405,3 +412,103 @@ def backward(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     return {"R": R, "dy": dy, "dgate": dgate.reshape(idx.shape), "dx": dx, "written": written,
             "y": y, "dh": dh, "expert_of_slot": eos, "token_of_slot": t_of, "dw_d": dw_d,
             "dw_gu": dw_gu, "x_rows": xr, "h": h, "a": a}
+
+
+# ---------------------------------------------------------------- MXFP8 backward
+def mx_quantize_values(v: np.ndarray):
+    """MXFP8 of fp64 rows [n, K] in blocks of 32 along K -> (codes [n, K] u8,
+    scales [n, K / 32] u8)."""
+    v = np.asarray(v, np.float64)
+    n, K = v.shape
+    assert K % 32 == 0
+    codes, scales = mx_quantize(v.reshape(-1))
+    return codes.reshape(n, K), scales.reshape(n, K // 32)
+
+
+def mx_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of MXFP8 rows: codes [n, K], scales [n, K / 32] -> fp64 [n, K]."""
+    n, K = codes.shape
+    return mx_dequantize(codes.reshape(-1), scales.reshape(-1)).reshape(n, K)
+
+
+def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
+    """Backward of the whole layer share with MXFP8 activations and bf16
+    weights (the article reports the MXFP8 backward beside the bf16 one; the
+    MXFP8 quantisation sits in the data path, so here the backward's token
+    operands dy and dh are MXFP8 like the forward's x and a).
+
+    Each buffer the path stores is rounded once, from the fp64 value of its
+    inputs as stored, where the path stores it:
+      x_q     the forward's ring (MXFP8 of the gathered bf16 rows, along H)
+      a_q     the forward's act (MXFP8 of SiLU(g) u, along I)
+      y       the forward's y (bf16)
+      dy_q    MXFP8 along H of w * dout[t], the product taken in fp32
+      dgate   <dout[t], y_s> (fp64)
+      h       bf16 of W_gu[e] x_q                  (g = h[:I], u = h[I:])
+      dh_q    MXFP8 along 2I of swiglu_backward_values(h, W_d[e]^T dy_q)
+              (I a multiple of 32: the dg and du blocks are separate)
+      dx_s    bf16 of W_gu[e]^T dh_q
+      dx[t]   bf16 of the sum of t's local dx_s
+      dW_d[e] bf16 of sum_s dy_q a_q^T;  dW_gu[e] bf16 of sum_s dh_q x_q^T
+    Returns the stored values (bf16 bits, or MXFP8 codes and scales) and the
+    fp64 values before each rounding (keys ending in _exact)."""
+    assert wl.act_format == 1 and getattr(wl, "weight_format", 0) == 0
+    idx, gate = (route_topk(wl.logits, wl.k) if wl.routing_from_logits
+                 else (wl.topk_idx, wl.topk_gate))
+    sch = build_schedule(idx, wl.expert_base, wl.n_local)
+    R, aos, soa = sch["R"], sch["assign_of_slot"], sch["slot_of_assign"]
+    k, H, I = wl.k, wl.H, wl.I
+    slots = np.arange(R)
+    xc, xs = gather_rows(wl.x, k, aos, slots, True)
+    xq = mx_values(xc, xs)
+    eos = expert_of_slots(sch["offsets"], slots)
+    y, a_ex, y_ex = ffn_rows((xc, xs), eos, wl.w_gu, wl.w_d, True, exact=True)
+    ac, asc = mx_quantize_values(a_ex)
+    aq = mx_values(ac, asc)
+    t_of = aos[:R] // k
+    w32 = np.asarray(gate, np.float32).reshape(-1)[aos[:R]]
+    dout32 = bf16_value(dout_bits)
+    dy32 = w32[:, None] * dout32[t_of]                     # fp32 products
+    dyc, dys = mx_quantize_values(dy32.astype(np.float64))
+    dyq = mx_values(dyc, dys)
+    dout_v = dout32.astype(np.float64)
+    dgate = np.full(idx.size, np.nan)
+    dgate[aos[:R]] = np.sum(dout_v[t_of] * bf16_value(y).astype(np.float64), axis=1)
+    wgu = bf16_value(wl.w_gu).astype(np.float64)
+    wd = bf16_value(wl.w_d).astype(np.float64)
+    h_ex = np.zeros((R, 2 * I))
+    dh_ex = np.zeros((R, 2 * I))
+    for e in np.unique(eos):
+        r = np.nonzero(eos == e)[0]
+        h_ex[r] = xq[r] @ wgu[e].T
+    h_bits = bf16_round(h_ex).reshape(R, 2 * I)
+    hv = bf16_value(h_bits).astype(np.float64)
+    for e in np.unique(eos):
+        r = np.nonzero(eos == e)[0]
+        dh_ex[r] = swiglu_backward_values(hv[r], dyq[r] @ wd[e])
+    dhc, dhs = mx_quantize_values(dh_ex)
+    dhq = mx_values(dhc, dhs)
+    dxs_ex = np.zeros((R, H))
+    for e in np.unique(eos):
+        r = np.nonzero(eos == e)[0]
+        dxs_ex[r] = dhq[r] @ wgu[e]
+    dxs_bits = bf16_round(dxs_ex).reshape(R, H)
+    T = idx.shape[0]
+    dx_ex = np.zeros((T, H))
+    np.add.at(dx_ex, t_of, bf16_value(dxs_bits).astype(np.float64))
+    dx_bits = bf16_round(dx_ex).reshape(T, H)
+    written = (soa.reshape(T, k) >= 0).any(axis=1)
+    dwd_ex = np.zeros((wl.n_local, H, I))
+    dwg_ex = np.zeros((wl.n_local, 2 * I, H))
+    for e in range(wl.n_local):
+        r = np.nonzero(eos == e)[0]
+        dwd_ex[e] = dyq[r].T @ aq[r]
+        dwg_ex[e] = dhq[r].T @ xq[r]
+    return {"R": R, "expert_of_slot": eos, "token_of_slot": t_of, "written": written,
+            "x_codes": xc, "x_scales": xs, "a_exact": a_ex, "a_codes": ac, "a_scales": asc,
+            "y": y, "y_exact": y_ex, "dy_exact": dy32.astype(np.float64), "dy_codes": dyc,
+            "dy_scales": dys, "dgate": dgate.reshape(idx.shape), "h_exact": h_ex, "h": h_bits,
+            "dh_exact": dh_ex, "dh_codes": dhc, "dh_scales": dhs, "dx_slots_exact": dxs_ex,
+            "dx_slots": dxs_bits, "dx_exact": dx_ex, "dx": dx_bits, "dw_d_exact": dwd_ex,
+            "dw_d": bf16_round(dwd_ex).reshape(dwd_ex.shape), "dw_gu_exact": dwg_ex,
+            "dw_gu": bf16_round(dwg_ex).reshape(dwg_ex.shape)}

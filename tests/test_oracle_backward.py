@@ -158,3 +158,145 @@ def test_layer_backward_glue_finite_differences(orc):
     # dy = w dout of each slot's own pick
     aos = orc.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)["assign_of_slot"]
     assert np.array_equal(ref["dy"], gates.reshape(-1)[aos][:, None] * dv[aos // wl.k])
+
+
+# ---------------------------------------------------------------- MXFP8 backward
+def _e4m3_table():
+    """Non-negative finite OCP E4M3FN values by code 0..126 (0x7f is NaN),
+    from the format's fields: 4 exponent bits (bias 7), 3 mantissa bits,
+    subnormals at exponent field 0."""
+    out = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+def _mx_brute(v):
+    """MXFP8 of rows [n, K] along K by exhaustive search: per block of 32 the
+    E8M0 scale 2^E with E = floor(log2 amax) - 8 (the exponent of E4M3's
+    largest power of two, 2^8), clipped to [-127, 127] (-127 for an all-zero
+    block); each value v / 2^E saturated at 448 and rounded to the nearest
+    code value, ties to the even code; the sign kept, also for zero."""
+    tab = _e4m3_table()
+    v = np.asarray(v, np.float64)
+    n, K = v.shape
+    codes = np.zeros((n, K), np.uint8)
+    scales = np.zeros((n, K // 32), np.uint8)
+    for i in range(n):
+        for b in range(K // 32):
+            blk = v[i, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            E = -127 if amax == 0 else int(np.clip(np.frexp(amax)[1] - 1 - 8, -127, 127))
+            scales[i, b] = E + 127
+            for j, x in enumerate(blk):
+                d = np.abs(tab - min(abs(x) / 2.0 ** E, 448.0))
+                best = np.nonzero(d == d.min())[0]
+                c = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+                codes[i, 32 * b + j] = c | (0x80 if np.signbit(x) else 0)
+    return codes, scales
+
+
+def _mx_vals(codes, scales):
+    tab = _e4m3_table()
+    mag = tab[codes & 0x7f] * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+    return np.where(codes & 0x80, -mag, mag)
+
+
+def _mx_case(orc, seed=31):
+    import workloads as W
+    wl = W.small_pool(seed, n_partitions=2, part_rows=20, H=64, I=32, E=8, k=3, expert_base=1,
+                      counts=[17, 0, 9, 6], act_format=W.ACT_MXFP8)
+    val = lambda b: orc.bf16_value(b).astype(np.float64)
+    wl.w_gu = orc.bf16_round(val(wl.w_gu) * 20.0).reshape(wl.w_gu.shape)  # O(1) activations
+    wl.w_d = orc.bf16_round(val(wl.w_d) * 20.0).reshape(wl.w_d.shape)
+    rng = np.random.default_rng(seed + 1)
+    dout = orc.bf16_round(rng.standard_normal((wl.T, wl.H))).reshape(wl.T, wl.H)
+    return wl, dout
+
+
+def test_mx_backward_storage_points(orc):
+    """Every MXFP8 buffer of oracle.backward_mx against a brute-force search
+    written from the E4M3 and E8M0 definitions (the quantisation axis and
+    block alignment, the scale rule, ties, saturation), each from the inputs
+    the path stores: dy from the fp32 w dout; h bf16 of W_gu x_q with x_q the
+    ring's values; dh from the stored h and dy_q through the SwiGLU backward
+    pinned above by finite differences; dx_s, dx and the weight gradients from
+    the quantised operands."""
+    import bars
+    wl, dout = _mx_case(orc)
+    r = orc.backward_mx(wl, dout)
+    R, I, H = r["R"], wl.I, wl.H
+    eos, t_of = r["expert_of_slot"], r["token_of_slot"]
+    aos = orc.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)["assign_of_slot"][:R]
+    # the ring: MXFP8 of the gathered bf16 rows along H
+    xc, xs = _mx_brute(orc.bf16_value(wl.x).astype(np.float64)[t_of])
+    assert np.array_equal(xc, r["x_codes"]) and np.array_equal(xs, r["x_scales"])
+    xq = _mx_vals(xc, xs)
+    # dy = MXFP8 of the fp32 product w * dout along H
+    w32 = wl.topk_gate.astype(np.float32).reshape(-1)[aos]
+    prod = (w32[:, None] * orc.bf16_value(dout)[t_of]).astype(np.float64)
+    dyc, dys = _mx_brute(prod)
+    assert np.array_equal(dyc, r["dy_codes"]) and np.array_equal(dys, r["dy_scales"])
+    dyq = _mx_vals(dyc, dys)
+    wgu, wd = orc.bf16_value(wl.w_gu).astype(np.float64), orc.bf16_value(wl.w_d).astype(np.float64)
+    hv = np.zeros((R, 2 * I))
+    dh = np.zeros((R, 2 * I))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        hv[rr] = bars.bf16_rne(xq[rr] @ wgu[e].T)
+    assert np.array_equal(hv, orc.bf16_value(r["h"]).astype(np.float64))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        dh[rr] = orc.swiglu_backward_values(hv[rr], dyq[rr] @ wd[e])
+    dhc, dhs = _mx_brute(dh)
+    assert np.array_equal(dhc, r["dh_codes"]) and np.array_equal(dhs, r["dh_scales"])
+    dhq = _mx_vals(dhc, dhs)
+    dxs = np.zeros((R, H))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        dxs[rr] = bars.bf16_rne(dhq[rr] @ wgu[e])
+    assert np.array_equal(dxs, orc.bf16_value(r["dx_slots"]))
+    dx = np.zeros((wl.T, H))
+    np.add.at(dx, t_of, dxs)
+    assert np.array_equal(bars.bf16_rne(dx), orc.bf16_value(r["dx"]))
+    ac, asc = _mx_brute(r["a_exact"])
+    aq = _mx_vals(ac, asc)
+    for e in range(wl.n_local):
+        rr = np.nonzero(eos == e)[0]
+        assert np.array_equal(bars.bf16_rne(dyq[rr].T @ aq[rr]), orc.bf16_value(r["dw_d"][e]))
+        assert np.array_equal(bars.bf16_rne(dhq[rr].T @ xq[rr]), orc.bf16_value(r["dw_gu"][e]))
+    # the cases the search covers are really present: several scales, ties
+    # of neither kind missing from dh, negative zeros in dy
+    assert len(np.unique(dhs)) > 4 and len(np.unique(dys)) > 4
+
+
+def test_mx_backward_near_the_unquantised_chain(orc):
+    """The MXFP8 chain stays within the size of its quantisation errors of
+    the unquantised fp64 chain (ffn_backward_values / ffn_wgrad_values, pinned
+    by finite differences, on the same x_q and the exact dy = w dout): each
+    E4M3 rounding moves a value by at most 2^-4 of it, so the RMS difference
+    is a few per cent -- and it is not zero (the quantisation is applied),
+    while a transposed weight or a dropped SiLU' term moves dx by tens of per
+    cent."""
+    wl, dout = _mx_case(orc, seed=43)
+    r = orc.backward_mx(wl, dout)
+    R, H = r["R"], wl.H
+    eos, t_of = r["expert_of_slot"], r["token_of_slot"]
+    aos = orc.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)["assign_of_slot"][:R]
+    xq = orc.mx_values(r["x_codes"], r["x_scales"])
+    wgu, wd = orc.bf16_value(wl.w_gu).astype(np.float64), orc.bf16_value(wl.w_d).astype(np.float64)
+    dy = wl.topk_gate.astype(np.float64).reshape(-1)[aos][:, None] * \
+        orc.bf16_value(dout).astype(np.float64)[t_of]
+    dh, dxs = orc.ffn_backward_values(xq, eos, wgu, wd, dy)
+    dx = np.zeros((wl.T, H))
+    np.add.at(dx, t_of, dxs)
+    dw_gu, dw_d = orc.ffn_wgrad_values(xq, eos, wgu, dy, dh, wl.n_local, H)
+    rel = lambda got, ref: float(np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2)))
+    wr = r["written"]
+    for name, got, ref in (("dx", orc.bf16_value(r["dx"])[wr], dx[wr]),
+                           ("dw_d", orc.bf16_value(r["dw_d"]), dw_d),
+                           ("dw_gu", orc.bf16_value(r["dw_gu"]), dw_gu),
+                           ("dh", orc.mx_values(r["dh_codes"], r["dh_scales"]), dh)):
+        d = rel(got.astype(np.float64), ref)
+        assert 1e-3 < d < 0.06, (name, d)
