@@ -327,7 +327,9 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
  * ------------------------------------------------------------------------ */
 
 /* Bytes of the transposed packed weights the backward GEMMs read:
- * W_gu^T (n_local x H x 2I) and W_d^T (n_local x I x H).  bf16 only. */
+ * W_gu^T (n_local x H x 2I) and W_d^T (n_local x I x H).  bf16 weights; the
+ * packing follows desc->act_format (the backward GEMMs' k-step differs for
+ * MXFP8 tokens), the size does not. */
 mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
                                        size_t* down_t_bytes);
 /* Packs them from the bf16 weights of mok_expert_ffn's layout (either pair of
@@ -409,6 +411,68 @@ mok_status mok_expert_wgrad(const mok_layer_desc* desc, const void* ring, int32_
                             const void* act, int32_t act_rows, const void* dy, const void* dh,
                             int32_t rows, const int32_t* offsets, void* dw_gate_up,
                             void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP8 backward (the article reports the MXFP8 backward beside the bf16 one;
+ * MXFP8 quantisation sits in the data path).  desc->act_format =
+ * MOK_ACT_MXFP8_E4M3 with bf16 weights: the forward's ring and act are MXFP8,
+ * and so are the backward's token operands dy (blocks of 32 along H) and dh
+ * (blocks of 32 along 2I: the dg blocks, then the du blocks), each as E4M3
+ * codes (u8, column-blocked like the ring) and E8M0 scales (pairs, as the
+ * ring's).  h, dx_slots, dx and the weight gradients stay bf16, the sums
+ * fp32.  The steps and their order are the bf16 backward's above.
+ * ------------------------------------------------------------------------ */
+
+/* mok_combine_backward with MXFP8 dy: the fp32 products w dout[t][h] of a
+ * slot quantised per block of 32 along H (OCP MX v1.0: scale 2^E with E =
+ * floor(log2 amax) - 8, codes rounded to nearest even, saturating at 448)
+ * into dy (dy_rows x H codes) and dy_scales (dy_rows x H/32).  dgate as
+ * mok_combine_backward. */
+mok_status mok_combine_backward_mx(const mok_tokens* dout, const void* y, int32_t y_rows,
+                                   const int32_t* assign_of_slot, const int32_t* offsets,
+                                   int32_t n_local, int32_t n_slots, const float* topk_gate,
+                                   int32_t k, int32_t H, void* dy, uint8_t* dy_scales,
+                                   int32_t dy_rows, float* dgate, int32_t* dev_status,
+                                   hipStream_t stream);
+
+/* The forward's gate/up + SwiGLU with MXFP8 tokens and act (as
+ * mok_expert_gate_up) that also stores h = [g, u] in bf16 as
+ * mok_expert_gate_up_save_h does.  act and act_scales are bit-identical to
+ * mok_expert_gate_up's given the same workspace argument; without a workspace
+ * h is bit-identical to the backward's recompute. */
+mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* ring,
+                                        const uint8_t* ring_scales, int32_t ring_slots,
+                                        const int32_t* offsets, int32_t slot_begin,
+                                        int32_t slot_end, const void* w_gate_up, void* act,
+                                        uint8_t* act_scales, int32_t act_rows, void* h, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
+/* mok_expert_ffn_backward (h_kept = 0: h recomputed from the MXFP8 ring and
+ * w_gate_up) or mok_expert_ffn_backward_saved (h_kept != 0: h from
+ * mok_expert_gate_up_save_h_mx, rows = its act_rows; ring, ring_scales and
+ * w_gate_up are not read) with MXFP8 dy in and MXFP8 dh out: dh = [dg, du]
+ * of the SwiGLU backward quantised per block of 32 along 2I (as dy) into dh
+ * (rows x 2I codes) and dh_scales (rows x 2I/32); dx_s = dh W_gu in bf16.
+ * The packed weights come from mok_pack_weights_bwd with this desc. */
+mok_status mok_expert_ffn_backward_mx(const mok_layer_desc* desc, const void* ring,
+                                      const uint8_t* ring_scales, int32_t ring_slots,
+                                      const void* dy, const uint8_t* dy_scales,
+                                      const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                                      const void* w_gate_up, const void* packed_gate_up_t,
+                                      const void* packed_down_t, void* h, int32_t h_kept, void* dh,
+                                      uint8_t* dh_scales, void* dx_slots, int32_t rows,
+                                      hipStream_t stream);
+
+/* mok_expert_wgrad over MXFP8 operands (the ring, act, dy and dh with their
+ * scales): each operand's values, code x 2^E, enter the fp32 sums exactly
+ * (converted to bf16 in the slot transposes: exact for every value of at
+ * least 2^-133).  ws: mok_wgrad_workspace_size(desc, rows) bytes. */
+mok_status mok_expert_wgrad_mx(const mok_layer_desc* desc, const void* ring,
+                               const uint8_t* ring_scales, int32_t ring_slots, const void* act,
+                               const uint8_t* act_scales, int32_t act_rows, const void* dy,
+                               const uint8_t* dy_scales, const void* dh, const uint8_t* dh_scales,
+                               int32_t rows, const int32_t* offsets, void* dw_gate_up,
+                               void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the pull dispatch (a push of gradients back to the tokens):
  * dx[t] = bf16(sum over t's local slots s, ascending j, of dx_slots row s)

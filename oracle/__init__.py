@@ -505,7 +505,8 @@ def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
         dwd_ex[e] = dyq[r].T @ aq[r]
         dwg_ex[e] = dhq[r].T @ xq[r]
     return {"R": R, "expert_of_slot": eos, "token_of_slot": t_of, "written": written,
-            "x_codes": xc, "x_scales": xs, "a_exact": a_ex, "a_codes": ac, "a_scales": asc,
+            "slot_of_assign": soa, "assign_of_slot": aos, "offsets": sch["offsets"],
+            "topk_idx": idx, "topk_gate": gate, "x_codes": xc, "x_scales": xs, "a_exact": a_ex, "a_codes": ac, "a_scales": asc,
             "y": y, "y_exact": y_ex, "dy_exact": dy32.astype(np.float64), "dy_codes": dyc,
             "dy_scales": dys, "dgate": dgate.reshape(idx.shape), "h_exact": h_ex, "h": h_bits,
             "dh_exact": dh_ex, "dh_codes": dhc, "dh_scales": dhs, "dx_slots_exact": dxs_ex,

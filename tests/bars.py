@@ -125,29 +125,40 @@ def _mx_exps(a: np.ndarray) -> np.ndarray:
     return np.where(amax > 0, np.clip(e - 1 - 8, -127, 127), -127)
 
 
+def _mx_moves(center: np.ndarray, lo: np.ndarray, hi: np.ndarray):
+    """MX quantisation of rows [n, K] (blocks of 32 along K) whose values the
+    device knows only within [lo, hi] around the oracle's center: returns the
+    oracle's quantised values q0 and the largest moves up (dp >= 0) and down
+    (dm <= 0) the device's quantised values can take from them.  Inside one
+    block the codes move with the value; a block whose largest magnitude may
+    lie in the neighbouring binade may take the neighbouring scale, and then
+    every element of it moves."""
+    E = _mx_exps(center)
+    q0 = _mx_blocks(center, E)
+    moves = [_mx_blocks(hi, E) - q0, _mx_blocks(lo, E) - q0]
+    n = center.shape[0]
+    amax_hi = np.maximum(np.abs(lo), np.abs(hi)).reshape(n, -1, 32).max(2)
+    low_mag = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    amax_lo = low_mag.reshape(n, -1, 32).max(2)
+    for dE in (-1, 1):
+        E2 = np.clip(E + dE, -127, 127)
+        b_lo, b_hi = np.ldexp(1.0, E2 + 8), np.ldexp(1.0, E2 + 9)   # amax range of exponent E2
+        reach = (amax_hi >= b_lo) & (amax_lo < b_hi) & (E2 != E)
+        if reach.any():
+            m = np.repeat(reach, 32, axis=1)
+            for v in (center, lo, hi):
+                moves.append(np.where(m, _mx_blocks(v, E2) - q0, 0.0))
+    st = np.stack(moves)
+    return q0, np.maximum(st, 0.0).max(0), np.minimum(st, 0.0).min(0)
+
+
 def _candidates(ae: np.ndarray, band: np.ndarray, act_mx: bool):
     """The oracle's stored a (a0) and the largest moves up (dp >= 0) and down
     (dm <= 0) a device value within +-band of a_exact can make it take."""
     if not act_mx:
         a0 = bf16_rne(ae)
         return a0, bf16_rne(ae + band) - a0, bf16_rne(ae - band) - a0
-    E = _mx_exps(ae)
-    a0 = _mx_blocks(ae, E)
-    moves = [_mx_blocks(ae + band, E) - a0, _mx_blocks(ae - band, E) - a0]
-    # a block whose amax lies within the band of a power of two may take the
-    # neighbouring scale: every element of it may then move
-    n, I = ae.shape
-    amax = np.abs(ae).reshape(n, -1, 32).max(2)
-    bmax = band.reshape(n, -1, 32).max(2)
-    for dE in (-1, 1):
-        E2 = np.clip(E + dE, -127, 127)
-        lo, hi = np.ldexp(1.0, E2 + 8), np.ldexp(1.0, E2 + 9)   # amax range of exponent E2
-        reach = (amax + bmax >= lo) & (amax - bmax < hi) & (E2 != E)
-        if reach.any():
-            alt = np.where(np.repeat(reach, 32, axis=1), _mx_blocks(ae, E2) - a0, 0.0)
-            moves += [alt]
-    st = np.stack(moves)
-    return a0, np.maximum(st, 0.0).max(0), np.minimum(st, 0.0).min(0)
+    return _mx_moves(ae, ae - band, ae + band)
 
 
 # Sum error of one step of gfx950's block-scaled FP8 MFMA (64 products of E4M3
@@ -160,20 +171,22 @@ MX_MFMA_REL = 2.0 ** -12
 
 def ffn_y_band(x_vals: np.ndarray, expert_of_row, w_gu_vals: np.ndarray, w_d_vals: np.ndarray,
                a_exact: np.ndarray, y_exact: np.ndarray, act_mx: bool = False,
-               w_mx: bool = False):
+               w_mx: bool = False, return_a: bool = False):
     """Allowed bf16 values of y per element for dispatched rows (values
     [n, H], as the GEMM reads them) of experts expert_of_row, given the
     oracle's fp64 a and y before their rounding (or MX quantisation of a when
     act_mx).  Weights as values ([n_local, 2I, H], [n_local, H, I]); w_mx:
     MXFP8 weights, multiplied by the block-scaled FP8 MFMA.  Returns (y_lo,
     y_hi) as float64 values [n, H] and the number of activation elements whose
-    stored value may move."""
+    stored value may move; with return_a also (a0, dp, dm) [n, I]: the
+    oracle's stored a and the largest moves of the device's from it."""
     x = np.asarray(x_vals, np.float64)
     eor = np.asarray(expert_of_row, np.int64).reshape(-1)
     n, H = x.shape
     I = a_exact.shape[1]
     y_lo = np.empty((n, H))
     y_hi = np.empty((n, H))
+    a_all = np.zeros((3, n, I))
     n_aflag = 0
 
     def acc_sigma(W, X, K):
@@ -200,6 +213,7 @@ def ffn_y_band(x_vals: np.ndarray, expert_of_row, w_gu_vals: np.ndarray, w_d_val
         band_a = (C_SIGMA * np.sqrt((dsilu * u * sg) ** 2 + (silu * su) ** 2) +
                   (np.abs(g) + 8.0) * 2.0 ** -23 * np.abs(ae) + 1e-38)
         a0, dp, dm = _candidates(ae, band_a, act_mx)
+        a_all[0, r], a_all[1, r], a_all[2, r] = a0, dp, dm
         n_aflag += int(np.count_nonzero(dp) + np.count_nonzero(dm))
         wd = np.asarray(w_d_vals[e], np.float64)                      # [H, I]
         wp, wm = np.maximum(wd, 0.0), np.minimum(wd, 0.0)
@@ -210,6 +224,8 @@ def ffn_y_band(x_vals: np.ndarray, expert_of_row, w_gu_vals: np.ndarray, w_d_val
         ye = y_exact[r]
         y_lo[r] = bf16_rne(ye + lo - band_y)
         y_hi[r] = bf16_rne(ye + hi + band_y)
+    if return_a:
+        return y_lo, y_hi, n_aflag, (a_all[0], a_all[1], a_all[2])
     return y_lo, y_hi, n_aflag
 
 
@@ -389,3 +405,142 @@ def wgrad_bars(expert_of_row, n_local: int, x_vals, a_vals, dy, dh, s_dh, dw_d, 
         bd[e] = C_SIGMA * np.sqrt(v_d + (RHO16 * dw_d[e]) ** 2) + 1e-30
         bg[e] = C_SIGMA * np.sqrt(v_g + (RHO16 * dw_gu[e]) ** 2) + 1e-30
     return bd, bg
+
+
+# ------------------------------------------------------------------ MXFP8 backward
+def _acc_sigma_padded(W: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """std of the device's fp32 sum error of X [n, K] against W [N, K] (the
+    K/16-roundings model of the forward), for any K: the sums are zero-padded
+    to a multiple of 16 block boundaries."""
+    N, K = W.shape
+    n = X.shape[0]
+    if K == 0:
+        return np.zeros((n, N))
+    bs = max(1, -(-K // 16))
+    Kp = bs * 16
+    Wp = np.zeros((N, Kp), np.float32)
+    Xp = np.zeros((n, Kp), np.float32)
+    Wp[:, :K], Xp[:, :K] = W, X
+    rms, _ = _prefix_rms(Wp, Xp, bs)
+    return U32 * rms * np.sqrt(max(K / 16.0, 1.0) / 3.0)
+
+
+def swiglu_bwd_values(g, u, da):
+    """[da u SiLU'(g), da SiLU(g)] (numpy, any float type)."""
+    s = 1.0 / (1.0 + np.exp(-g))
+    return np.concatenate([da * u * s * (1.0 + g * (1.0 - s)), da * g * s], axis=1)
+
+
+def mx_backward_bands(wl, r: dict, dout_bits) -> dict:
+    """Bands of the MXFP8 backward for the oracle's result r
+    (oracle.backward_mx), built like the forward's: from where the device
+    rounds and what it decides.
+      dy      the device takes the same decisions on the same fp32 products:
+              bit-exact (no band).
+      dgate   the interval of <dout, y> over the forward's y bands.
+      h       bf16 roundings within 6 sigma of the fp32 sum over H.
+      dh      the device's value before quantisation lies within the SwiGLU
+              backward evaluated at the corners of its inputs' bands (h, and
+              da within 6 sigma of its fp32 sum over H) plus the epilogue's
+              fp32 arithmetic; the band is the quantisations of that interval
+              (neighbouring codes, and the neighbouring scale for a block whose
+              amax may cross a power of two).
+      dx_s    the oracle's sum over the dh_q moves (interval per weight sign)
+              plus 6 sigma of the fp32 sum over 2I, rounded to bf16.
+      dx      the fp32 sum of the slots' dx_s bands, rounded to bf16.
+      dW_d    sum_s dy_q a^T over the forward's a moves; dW_gu: sum_s dh x_q^T
+              over the dh moves; each plus 6 sigma of its fp32 sum over the
+              expert's slots, rounded to bf16.
+    Returns a dict of (lo, hi) pairs of values (and 'dh' as the device's
+    dequantised values' interval, 'dh_q0' the oracle's), plus 'dh_flagged'."""
+    import oracle
+    I, H = wl.I, wl.H
+    eos, t_of, R = r["expert_of_slot"], r["token_of_slot"], r["R"]
+    xq = oracle.mx_values(r["x_codes"], r["x_scales"])
+    wgu, wd = bf16_values(wl.w_gu), bf16_values(wl.w_d)
+    y_lo, y_hi, _, (a0, a_dp, a_dm) = ffn_y_band(xq, eos, wgu, wd, r["a_exact"], r["y_exact"],
+                                                 act_mx=True, return_a=True)
+    out = {"y": (y_lo, y_hi)}
+    out["dgate"] = dgate_band(bf16_values(dout_bits)[t_of], y_lo, y_hi)
+    dyq = oracle.mx_values(r["dy_codes"], r["dy_scales"])
+    h_ex = r["h_exact"]
+    h_lo, h_hi = np.empty_like(h_ex), np.empty_like(h_ex)
+    d_lo, d_hi = np.empty((R, 2 * I)), np.empty((R, 2 * I))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        sig_h = _acc_sigma_padded(np.asarray(wgu[e], np.float32), xq[rr])
+        h_lo[rr] = bf16_rne(h_ex[rr] - C_SIGMA * sig_h)
+        h_hi[rr] = bf16_rne(h_ex[rr] + C_SIGMA * sig_h)
+        da = dyq[rr] @ wd[e]
+        sig_da = _acc_sigma_padded(np.asarray(wd[e].T, np.float32), dyq[rr])
+        corners = []
+        for g in (h_lo[rr, :I], h_hi[rr, :I]):
+            for u in (h_lo[rr, I:], h_hi[rr, I:]):
+                for dd in (da - C_SIGMA * sig_da, da + C_SIGMA * sig_da):
+                    corners.append(swiglu_bwd_values(g, u, dd))
+        st = np.stack(corners)
+        g_abs = np.concatenate([np.abs(h_ex[rr, :I])] * 2, axis=1)
+        err = (g_abs + 8.0) * 2.0 ** -23 * np.abs(st).max(0) + 1e-38
+        d_lo[rr], d_hi[rr] = st.min(0) - err, st.max(0) + err
+    out["h"] = (h_lo, h_hi)
+    q0, dp, dm = _mx_moves(r["dh_exact"], d_lo, d_hi)
+    out["dh"] = (q0 + dm, q0 + dp)
+    out["dh_q0"] = q0
+    out["dh_flagged"] = int(np.count_nonzero(dp) + np.count_nonzero(dm))
+    dxs_lo, dxs_hi = np.empty((R, H)), np.empty((R, H))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        W = wgu[e]                                                    # [2I, H]
+        wp, wm = np.maximum(W, 0.0), np.minimum(W, 0.0)
+        lo = dm[rr] @ wp + dp[rr] @ wm
+        hi = dp[rr] @ wp + dm[rr] @ wm
+        band = C_SIGMA * _acc_sigma_padded(np.asarray(W.T, np.float32), q0[rr]) + 1e-38
+        ce = r["dx_slots_exact"][rr]
+        dxs_lo[rr], dxs_hi[rr] = bf16_rne(ce + lo - band), bf16_rne(ce + hi + band)
+    out["dx_slots"] = (dxs_lo, dxs_hi)
+    soa = r["slot_of_assign"]
+    out["dx"] = out_band(dxs_lo, dxs_hi, np.arange(max(R, 1)), soa,
+                         np.ones(soa.size), np.arange(wl.T), wl.k)
+    dwd_lo, dwd_hi = np.empty_like(r["dw_d_exact"]), np.empty_like(r["dw_d_exact"])
+    dwg_lo, dwg_hi = np.empty_like(r["dw_gu_exact"]), np.empty_like(r["dw_gu_exact"])
+    for e in range(wl.n_local):
+        rr = np.nonzero(eos == e)[0]
+        dy = dyq[rr]                                                   # [n_e, H]
+        yp, ym = np.maximum(dy, 0.0), np.minimum(dy, 0.0)
+        lo = yp.T @ a_dm[rr] + ym.T @ a_dp[rr]
+        hi = yp.T @ a_dp[rr] + ym.T @ a_dm[rr]
+        band = C_SIGMA * _acc_sigma_padded(np.asarray(a0[rr].T, np.float32), dy.T) + 1e-38
+        ce = r["dw_d_exact"][e]
+        dwd_lo[e], dwd_hi[e] = bf16_rne(ce + lo - band), bf16_rne(ce + hi + band)
+        x = xq[rr]
+        xp_, xm_ = np.maximum(x, 0.0), np.minimum(x, 0.0)
+        lo = dm[rr].T @ xp_ + dp[rr].T @ xm_
+        hi = dp[rr].T @ xp_ + dm[rr].T @ xm_
+        band = C_SIGMA * _acc_sigma_padded(np.asarray(x.T, np.float32), q0[rr].T) + 1e-38
+        ce = r["dw_gu_exact"][e]
+        dwg_lo[e], dwg_hi[e] = bf16_rne(ce + lo - band), bf16_rne(ce + hi + band)
+    out["dw_d"] = (dwd_lo, dwd_hi)
+    out["dw_gu"] = (dwg_lo, dwg_hi)
+    return out
+
+
+def interval_stats(got: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray,
+                   what: str) -> dict:
+    """lo <= got <= hi for values (not bf16 bits: the MXFP8 dh), the oracle's
+    own value inside too; prints how many elements differ from the oracle."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert np.all((ref >= lo) & (ref <= hi)), f"{what}: the oracle's value is outside its own band"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    bad = (got < lo) | (got > hi)
+    if bad.any():
+        i = np.unravel_index(np.argmax(bad), got.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {got.size} elements outside their band; "
+                             f"e.g. at {tuple(int(v) for v in i)} got {got[i]!r}, oracle {ref[i]!r}, "
+                             f"band [{lo[i]!r}, {hi[i]!r}]")
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    st = dict(n=int(got.size), differ=int(np.count_nonzero(got != ref)),
+              flagged=int(np.count_nonzero(lo != hi)),
+              strict=float(np.abs(got - ref).max() / rms) if rms > 0 else 0.0)
+    print(f"[parity] {what}: {st['differ']} of {st['n']} elements differ from the oracle, "
+          f"{st['flagged']} in a band, max|d|/RMS = {st['strict']:.3e}", flush=True)
+    return st

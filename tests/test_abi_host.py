@@ -58,17 +58,46 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 0, 4, 1, None, 4, 1, None, None) == E
     assert L.mok_combine(1, 4, 1, 1, 17, 2, 64, C.byref(tok), None, None) == E  # T > rows
     assert L.mok_combine(1, 4, 1, 1, 16, 2, 60, C.byref(tok), None, None) == E  # H % 8
-    # backward: MXFP8 desc refused, H % 64 for the merge backward, null buffers
+    # backward: the bf16 calls refuse an MXFP8 desc and the _mx calls a bf16
+    # one; H % 64 for the merge backward, null buffers and scales
     dmx = _desc(act_format=1)
     a, b = C.c_size_t(0), C.c_size_t(0)
-    assert L.mok_packed_weights_bwd_size(C.byref(dmx), C.byref(a), C.byref(b)) == E
+    assert L.mok_packed_weights_bwd_size(C.byref(dmx), C.byref(a), C.byref(b)) == 0
+    a2, b2 = C.c_size_t(0), C.c_size_t(0)
+    assert L.mok_packed_weights_bwd_size(C.byref(_desc()), C.byref(a2), C.byref(b2)) == 0
+    assert (a.value, b.value) == (a2.value, b2.value) and a.value > 0
+    assert L.mok_packed_weights_bwd_size(C.byref(_desc(act_format=1, weight_format=1)),
+                                         C.byref(a), C.byref(b)) == E
+    assert L.mok_combine_backward_mx(C.byref(tok), 1, 4, 1, 1, 8, 4, 1, 2, 64, 1, None, 4, 1,
+                                     None, None) == E                  # null dy scales
+    assert L.mok_combine_backward_mx(C.byref(tok), 1, 4, 1, 1, 8, 4, 1, 2, 96, 1, 1, 4, 1,
+                                     None, None) == E                  # H % 64
+    assert L.mok_expert_ffn_backward(C.byref(dmx), 1, 8, 1, 1, 0, 8, 1, 1, 1, 1, 1, 1, 8,
+                                     None) == E
+    assert L.mok_expert_ffn_backward_mx(C.byref(_desc()), 1, 1, 8, 1, 1, 1, 0, 8, 1, 1, 1, 1, 0,
+                                        1, 1, 1, 8, None) == E         # bf16 desc
+    assert L.mok_expert_ffn_backward_mx(C.byref(dmx), 1, 1, 8, 1, 1, 1, 0, 8, 1, 1, 1, 1, 0,
+                                        1, None, 1, 8, None) == E      # null dh scales
+    assert L.mok_expert_ffn_backward_mx(C.byref(dmx), None, None, 8, 1, 1, 1, 0, 8, None, 1, 1,
+                                        1, 0, 1, 1, 1, 8, None) == E   # recompute needs the ring
+    assert L.mok_expert_gate_up_save_h_mx(C.byref(_desc()), 1, 1, 64, 1, 0, 64, 1, 1, 1, 64, 1,
+                                          None, 0, None) == E          # bf16 desc
+    assert L.mok_expert_gate_up_save_h_mx(C.byref(dmx), 1, None, 64, 1, 0, 64, 1, 1, 1, 64, 1,
+                                          None, 0, None) == E          # null ring scales
     assert L.mok_combine_backward(C.byref(tok), 1, 4, 1, 1, 8, 4, 1, 2, 60, 1, 4, 1, None, None) == E
     assert L.mok_combine_backward(C.byref(tok), None, 4, 1, 1, 8, 4, 1, 2, 64, 1, 4, 1, None, None) == E
     db = _desc()
     assert L.mok_expert_ffn_backward(C.byref(db), 1, 8, 1, 1, 0, 8, 1, 1, 1, None, 1, 1, 8, None) == E
     assert L.mok_dispatch_backward(None, 8, 1, 1, 8, 4, 1, 2, 64, C.byref(tok), None, None) == E
     need = L.mok_wgrad_workspace_size(C.byref(db), 64)
-    assert need > 0 and L.mok_wgrad_workspace_size(C.byref(dmx), 64) == 0
+    assert need > 0 and L.mok_wgrad_workspace_size(C.byref(dmx), 64) == need
+    assert L.mok_expert_wgrad(C.byref(dmx), 1, 64, 1, 64, 1, 1, 64, 1, 1, 1, 1, need, None) == E
+    assert L.mok_expert_wgrad_mx(C.byref(db), 1, 1, 64, 1, 1, 64, 1, 1, 1, 1, 64, 1, 1, 1, 1,
+                                 need, None) == E                      # bf16 desc
+    assert L.mok_expert_wgrad_mx(C.byref(dmx), 1, 1, 64, 1, None, 64, 1, 1, 1, 1, 64, 1, 1, 1,
+                                 1, need, None) == E                   # null act scales
+    assert L.mok_expert_wgrad_mx(C.byref(dmx), 1, 1, 64, 1, 1, 64, 1, 1, 1, 1, 64, 1, 1, 1, 1,
+                                 need - 1, None) == mok.MOK_ERR_WORKSPACE
     assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, None, None, 1, need, None) == E
     assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, 1, 1, 1, need - 1, None) == \
         mok.MOK_ERR_WORKSPACE

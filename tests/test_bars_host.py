@@ -189,3 +189,71 @@ def test_backward_bars_accept_fp32_and_reject_ten_percent():
         assert np.all(np.abs(got - refw) <= b)
         big = np.abs(refw) > 0.1 * np.abs(refw).max()
         assert np.all(0.1 * np.abs(refw[big]) > b[big])
+
+
+def _sim_backward_mx(wl, r, dout_bits, a_sim):
+    """fp32 evaluation of the MXFP8 backward (numpy fp32 products, which round
+    after every product): the same dy_q, then h, dh (quantised from its fp32
+    values), dx_s, dx and the weight gradients, with the forward's act taken
+    from the fp32 forward evaluation a_sim."""
+    import oracle as O
+    I, H, R = wl.I, wl.H, r["R"]
+    eos, t_of = r["expert_of_slot"], r["token_of_slot"]
+    xq = _f32(O.mx_values(r["x_codes"], r["x_scales"]))
+    dyq = _f32(O.mx_values(r["dy_codes"], r["dy_scales"]))
+    wgu = _f32(bars.bf16_values(wl.w_gu))
+    wd = _f32(bars.bf16_values(wl.w_d))
+    h = np.empty((R, 2 * I))
+    dh = np.empty((R, 2 * I))
+    dxs = np.empty((R, H))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        h[rr] = bars.bf16_rne(xq[rr] @ wgu[e].T)
+        hh = _f32(h[rr])
+        dh[rr] = bars.swiglu_bwd_values(hh[:, :I], hh[:, I:], dyq[rr] @ wd[e]).astype(np.float64)
+    dhq = bars._mx_blocks(dh, bars._mx_exps(dh))
+    for e in np.unique(eos):
+        rr = np.nonzero(eos == e)[0]
+        dxs[rr] = bars.bf16_rne(_f32(dhq[rr]) @ wgu[e])
+    dx = np.zeros((wl.T, H), np.float32)
+    np.add.at(dx, t_of, _f32(dxs))
+    dwd = np.zeros((wl.n_local, H, I))
+    dwg = np.zeros((wl.n_local, 2 * I, H))
+    for e in range(wl.n_local):
+        rr = np.nonzero(eos == e)[0]
+        dwd[e] = bars.bf16_rne(dyq[rr].T @ _f32(a_sim[rr]))
+        dwg[e] = bars.bf16_rne(_f32(dhq[rr]).T @ xq[rr])
+    return h, dhq, dxs, bars.bf16_rne(dx), dwd, dwg
+
+
+def test_mx_backward_bands_accept_fp32_and_reject_ten_percent():
+    wl = W.small_pool(83, n_partitions=4, part_rows=250, H=576, I=320, E=32, k=4,
+                      expert_base=3, counts=[300, 17, 0, 260, 1], act_format=W.ACT_MXFP8)
+    dout = W.normal_bf16(np.random.SeedSequence(579), wl.T * wl.H, 1.0).reshape(wl.T, wl.H)
+    r = oracle.backward_mx(wl, dout)
+    b = bars.mx_backward_bands(wl, r, dout)
+    fwd = dict(x_rows=(r["x_codes"], r["x_scales"]), expert_of_slot=r["expert_of_slot"],
+               R=r["R"], slots=np.arange(r["R"]), slot_of_assign=r["slot_of_assign"],
+               topk_gate=r["topk_gate"], tokens=np.arange(wl.T))
+    a_sim, _, _ = _sim_forward(wl, fwd)
+    h, dhq, dxs, dx, dwd, dwg = _sim_backward_mx(wl, r, dout, a_sim)
+    ref = dict(h=bars.bf16_values(r["h"]), dx_slots=bars.bf16_values(r["dx_slots"]),
+               dx=bars.bf16_values(r["dx"]), dw_d=bars.bf16_values(r["dw_d"]),
+               dw_gu=bars.bf16_values(r["dw_gu"]),
+               dh=oracle.mx_values(r["dh_codes"], r["dh_scales"]))
+    assert np.array_equal(ref["dh"], b["dh_q0"])
+    wr = r["written"]
+    got = dict(h=h, dh=dhq, dx_slots=dxs, dx=dx, dw_d=dwd, dw_gu=dwg)
+    for name in ("h", "dh", "dx_slots", "dx", "dw_d", "dw_gu"):
+        lo, hi = b[name]
+        g, rf = got[name], ref[name]
+        if name == "dx":
+            g, rf, lo, hi = g[wr], rf[wr], lo[wr], hi[wr]
+        st = bars.interval_stats(g, rf, lo, hi, f"fp32 MXFP8 backward {name}")
+        assert st["flagged"] < 0.5 * st["n"], name          # not a blanket band
+        off = rf * 1.1
+        typical = np.abs(rf) > 0.01 * np.abs(rf).max()
+        caught = float(np.mean(((off < lo) | (off > hi))[typical]))
+        print(f"  10 % off rejected at {caught:.5f} of the typical elements")
+        assert caught > 0.999, (name, caught)
+    assert b["dh_flagged"] > 0

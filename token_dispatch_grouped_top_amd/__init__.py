@@ -103,6 +103,14 @@ _SIGS = {
                                    _P]),
     "mok_dispatch_backward": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _TOK, _P,
                                         _P]),
+    "mok_combine_backward_mx": (C.c_int, [_TOK, _P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32,
+                                          _P, _P, _I32, _P, _P, _P]),
+    "mok_expert_gate_up_save_h_mx": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P,
+                                               _I32, _P, _P, _SZ, _P]),
+    "mok_expert_ffn_backward_mx": (C.c_int, [_DESC, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
+                                             _P, _P, _I32, _P, _P, _P, _I32, _P]),
+    "mok_expert_wgrad_mx": (C.c_int, [_DESC, _P, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
+                                      _P, _P, _P, _P, _SZ, _P]),
     "mok_device_status": (C.c_int, [_P, C.POINTER(C.c_int32), _P]),
     "mok_forward_minibatch": (_I32, [_DESC, _I32]),
     "mok_status_str": (C.c_char_p, [C.c_int]),
@@ -449,6 +457,53 @@ def mok_dispatch_backward(dx_slots, rows: int, assign_of_slot, offsets, n_local:
     _check(_lib.mok_dispatch_backward(_ptr(dx_slots), rows, _ptr(assign_of_slot), _ptr(offsets),
                                       n_local, n_slots, _ptr(slot_of_assign), k, H, C.byref(dx.c),
                                       _ptr(dev_status), _stream(stream)), "mok_dispatch_backward")
+
+
+def mok_combine_backward_mx(dout: Tokens, y, y_rows: int, assign_of_slot, offsets, n_local: int,
+                            n_slots: int, topk_gate, k: int, H: int, dy, dy_scales, dy_rows: int,
+                            dgate, dev_status=None, stream=None) -> None:
+    _check(_lib.mok_combine_backward_mx(C.byref(dout.c), _ptr(y), y_rows, _ptr(assign_of_slot),
+                                        _ptr(offsets), n_local, n_slots, _ptr(topk_gate), k, H,
+                                        _ptr(dy), _ptr(dy_scales), dy_rows, _ptr(dgate),
+                                        _ptr(dev_status), _stream(stream)),
+           "mok_combine_backward_mx")
+
+
+def mok_expert_gate_up_save_h_mx(desc: mok_layer_desc, ring, ring_scales, ring_slots: int,
+                                 offsets, slot_begin: int, slot_end: int, w_gate_up, act,
+                                 act_scales, act_rows: int, h, ws=None,
+                                 ws_bytes: Optional[int] = None, stream=None) -> None:
+    _check(_lib.mok_expert_gate_up_save_h_mx(C.byref(desc), _ptr(ring), _ptr(ring_scales),
+                                             ring_slots, _ptr(offsets), slot_begin, slot_end,
+                                             _ptr(w_gate_up), _ptr(act), _ptr(act_scales),
+                                             act_rows, _ptr(h), _ptr(ws), _ws_bytes(ws, ws_bytes),
+                                             _stream(stream)),
+           "mok_expert_gate_up_save_h_mx")
+
+
+def mok_expert_ffn_backward_mx(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, dy,
+                               dy_scales, offsets, slot_begin: int, slot_end: int, w_gate_up,
+                               packed_gate_up_t, packed_down_t, h, h_kept: bool, dh, dh_scales,
+                               dx_slots, rows: int, stream=None) -> None:
+    _check(_lib.mok_expert_ffn_backward_mx(C.byref(desc), _ptr(ring), _ptr(ring_scales),
+                                           ring_slots, _ptr(dy), _ptr(dy_scales), _ptr(offsets),
+                                           slot_begin, slot_end, _ptr(w_gate_up),
+                                           _ptr(packed_gate_up_t), _ptr(packed_down_t), _ptr(h),
+                                           1 if h_kept else 0, _ptr(dh), _ptr(dh_scales),
+                                           _ptr(dx_slots), rows, _stream(stream)),
+           "mok_expert_ffn_backward_mx")
+
+
+def mok_expert_wgrad_mx(desc: mok_layer_desc, ring, ring_scales, ring_slots: int, act,
+                        act_scales, act_rows: int, dy, dy_scales, dh, dh_scales, rows: int,
+                        offsets, dw_gate_up, dw_down, ws, ws_bytes: Optional[int] = None,
+                        stream=None) -> None:
+    _check(_lib.mok_expert_wgrad_mx(C.byref(desc), _ptr(ring), _ptr(ring_scales), ring_slots,
+                                    _ptr(act), _ptr(act_scales), act_rows, _ptr(dy),
+                                    _ptr(dy_scales), _ptr(dh), _ptr(dh_scales), rows,
+                                    _ptr(offsets), _ptr(dw_gate_up), _ptr(dw_down), _ptr(ws),
+                                    _ws_bytes(ws, ws_bytes), _stream(stream)),
+           "mok_expert_wgrad_mx")
 
 
 def mok_device_status(ws, stream=None) -> int:

@@ -413,6 +413,32 @@ mok_status mok_expert_gate_up_save_h(const mok_layer_desc* desc, const void* rin
   return hip_status(launch_gate_up(a, stream));
 }
 
+mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* ring,
+                                        const uint8_t* ring_scales, int32_t ring_slots,
+                                        const int32_t* offsets, int32_t slot_begin,
+                                        int32_t slot_end, const void* w_gate_up, void* act,
+                                        uint8_t* act_scales, int32_t act_rows, void* h, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  if (!desc_ok(desc) || desc->act_format != MOK_ACT_MXFP8_E4M3 || desc->weight_format != MOK_W_BF16 ||
+      !ring || !ring_scales || ring_slots < 1 || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_gate_up || !act || !act_scales || act_rows < 1 || !h)
+    return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, ring_slots, act_rows) ||
+      static_cast<int64_t>(act_rows) * 2 * desc->inter * 2 >= (1ll << 32))
+    return MOK_ERR_UNSUPPORTED;
+  FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
+  a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up);
+  a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = MOK_ACT_MXFP8_E4M3;
+  a.w_packed = desc->weights_packed; a.weight_format = MOK_W_BF16;
+  a.h_out = h;
+  return hip_status(launch_gate_up(a, stream));
+}
+
 mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const uint8_t* act_scales,
                            int32_t act_rows, const int32_t* offsets, int32_t slot_begin,
                            int32_t slot_end, const void* w_down, void* y, int32_t y_rows,
@@ -461,14 +487,19 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
 
 // ------------------------------------------------------------ backward
 namespace {
+// bf16 tokens and weights
 bool bwd_desc_ok(const mok_layer_desc* d) {
   return desc_ok(d) && d->act_format == MOK_ACT_BF16 && d->weight_format == MOK_W_BF16;
+}
+// MXFP8 tokens, bf16 weights
+bool bwd_desc_mx_ok(const mok_layer_desc* d) {
+  return desc_ok(d) && d->act_format == MOK_ACT_MXFP8_E4M3 && d->weight_format == MOK_W_BF16;
 }
 }  // namespace
 
 mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
                                        size_t* down_t_bytes) {
-  if (!bwd_desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!bwd_desc_ok(desc) && !bwd_desc_mx_ok(desc)) return MOK_ERR_INVALID_ARG;
   if (gate_up_t_bytes) *gate_up_t_bytes = packed_bwd_gate_up_bytes(desc->hidden, desc->inter, desc->n_local);
   if (down_t_bytes) *down_t_bytes = packed_bwd_down_bytes(desc->hidden, desc->inter, desc->n_local);
   return MOK_OK;
@@ -476,13 +507,13 @@ mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_
 
 mok_status mok_pack_weights_bwd(const mok_layer_desc* desc, const void* w_gate_up, const void* w_down,
                                 void* packed_gate_up_t, void* packed_down_t, hipStream_t stream) {
-  if (!bwd_desc_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!bwd_desc_ok(desc) && !bwd_desc_mx_ok(desc)) return MOK_ERR_INVALID_ARG;
   if ((w_gate_up == nullptr) != (packed_gate_up_t == nullptr) ||
       (w_down == nullptr) != (packed_down_t == nullptr))
     return MOK_ERR_INVALID_ARG;
   return hip_status(launch_pack_weights_bwd(static_cast<const uint16_t*>(w_gate_up),
                                             static_cast<const uint16_t*>(w_down), desc->hidden,
-                                            desc->inter, desc->n_local,
+                                            desc->inter, desc->n_local, bwd_desc_mx_ok(desc),
                                             static_cast<uint16_t*>(packed_gate_up_t),
                                             static_cast<uint16_t*>(packed_down_t), stream));
 }
@@ -499,7 +530,25 @@ mok_status mok_combine_backward(const mok_tokens* dout, const void* y, int32_t y
     return MOK_ERR_INVALID_ARG;
   return hip_status(launch_unmerge_slots(dout->part_ptr, dout->n_partitions, dout->part_rows, y,
                                          y_rows, assign_of_slot, offsets, n_local, n_slots,
-                                         topk_gate, k, H, dy, dy_rows, dgate, dev_status, stream));
+                                         topk_gate, k, H, dy, nullptr, dy_rows, dgate, dev_status,
+                                         stream));
+}
+
+mok_status mok_combine_backward_mx(const mok_tokens* dout, const void* y, int32_t y_rows,
+                                   const int32_t* assign_of_slot, const int32_t* offsets,
+                                   int32_t n_local, int32_t n_slots, const float* topk_gate,
+                                   int32_t k, int32_t H, void* dy, uint8_t* dy_scales,
+                                   int32_t dy_rows, float* dgate, int32_t* dev_status,
+                                   hipStream_t stream) {
+  if (k < 1 || k > 32 || H <= 0 || H % 64 != 0 || n_local < 1 || n_slots < 0 || !tokens_ok(dout, 0))
+    return MOK_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!y || y_rows < 1 || !assign_of_slot || !offsets || !topk_gate || !dy ||
+                      !dy_scales || dy_rows < 1 || !dgate))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_unmerge_slots(dout->part_ptr, dout->n_partitions, dout->part_rows, y,
+                                         y_rows, assign_of_slot, offsets, n_local, n_slots,
+                                         topk_gate, k, H, dy, dy_scales, dy_rows, dgate,
+                                         dev_status, stream));
 }
 
 mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring, int32_t ring_slots,
@@ -548,8 +597,38 @@ mok_status mok_expert_ffn_backward_saved(const mok_layer_desc* desc, const void*
   return hip_status(launch_ffn_backward(a, stream));
 }
 
+mok_status mok_expert_ffn_backward_mx(const mok_layer_desc* desc, const void* ring,
+                                      const uint8_t* ring_scales, int32_t ring_slots,
+                                      const void* dy, const uint8_t* dy_scales,
+                                      const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                                      const void* w_gate_up, const void* packed_gate_up_t,
+                                      const void* packed_down_t, void* h, int32_t h_kept, void* dh,
+                                      uint8_t* dh_scales, void* dx_slots, int32_t rows,
+                                      hipStream_t stream) {
+  if (!bwd_desc_mx_ok(desc) || !dy || !dy_scales || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !packed_gate_up_t || !packed_down_t || !h || !dh || !dh_scales ||
+      !dx_slots || rows < 1)
+    return MOK_ERR_INVALID_ARG;
+  if (!h_kept && (!ring || !ring_scales || ring_slots < 1 || !w_gate_up)) return MOK_ERR_INVALID_ARG;
+  const int64_t lim = 1ll << 32, H = desc->hidden, I = desc->inter;
+  if ((!h_kept && static_cast<int64_t>(ring_slots) * H >= lim) ||
+      static_cast<int64_t>(rows) * 2 * I * 2 >= lim || static_cast<int64_t>(rows) * H * 2 >= lim ||
+      4ll * I * H >= lim)
+    return MOK_ERR_UNSUPPORTED;
+  BwdArgs a{};
+  a.ring = ring; a.ring_scales = ring_scales; a.ring_slots = ring_slots;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_gu = static_cast<const uint16_t*>(w_gate_up); a.w_gu_packed = desc->weights_packed;
+  a.w_gu_t = static_cast<const uint16_t*>(packed_gate_up_t);
+  a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
+  a.dy = dy; a.dy_scales = dy_scales; a.h = h; a.dh = dh; a.dh_scales = dh_scales;
+  a.dx = dx_slots; a.rows = rows; a.h_saved = h_kept ? 1 : 0; a.mx = 1;
+  a.H = desc->hidden; a.I = desc->inter;
+  return hip_status(launch_ffn_backward(a, stream));
+}
+
 size_t mok_wgrad_workspace_size(const mok_layer_desc* desc, int32_t rows) {
-  if (!bwd_desc_ok(desc) || rows < 1) return 0;
+  if ((!bwd_desc_ok(desc) && !bwd_desc_mx_ok(desc)) || rows < 1) return 0;
   return wgrad_ws_bytes(rows, desc->hidden, desc->inter, desc->n_local);
 }
 
@@ -569,6 +648,32 @@ mok_status mok_expert_wgrad(const mok_layer_desc* desc, const void* ring, int32_
   WgradArgs a{};
   a.ring = ring; a.ring_slots = ring_slots; a.act = act; a.act_rows = act_rows;
   a.dy = dy; a.dh = dh; a.rows = rows; a.offsets = offsets; a.n_local = desc->n_local;
+  a.dw_gu = dw_gate_up; a.dw_d = dw_down; a.ws = ws; a.H = desc->hidden; a.I = desc->inter;
+  return hip_status(launch_wgrad(a, stream));
+}
+
+mok_status mok_expert_wgrad_mx(const mok_layer_desc* desc, const void* ring,
+                               const uint8_t* ring_scales, int32_t ring_slots, const void* act,
+                               const uint8_t* act_scales, int32_t act_rows, const void* dy,
+                               const uint8_t* dy_scales, const void* dh, const uint8_t* dh_scales,
+                               int32_t rows, const int32_t* offsets, void* dw_gate_up,
+                               void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!bwd_desc_mx_ok(desc) || !ring || !ring_scales || ring_slots < 1 || !act || !act_scales ||
+      act_rows < 1 || !dy || !dy_scales || !dh || !dh_scales || rows < 1 || !offsets ||
+      (!dw_gate_up && !dw_down) || !ws)
+    return MOK_ERR_INVALID_ARG;
+  if (ws_bytes < mok_wgrad_workspace_size(desc, rows)) return MOK_ERR_WORKSPACE;
+  const int64_t lim = 1ll << 32, H = desc->hidden, I = desc->inter;
+  const int64_t kp = wgrad_kpad(rows, desc->n_local);
+  if (kp * H * 2 >= lim || kp * 2 * I * 2 >= lim || static_cast<int64_t>(ring_slots) * H >= lim ||
+      static_cast<int64_t>(act_rows) * I >= lim || static_cast<int64_t>(rows) * 2 * I >= lim ||
+      static_cast<int64_t>(rows) * H >= lim)
+    return MOK_ERR_UNSUPPORTED;
+  WgradArgs a{};
+  a.ring = ring; a.ring_slots = ring_slots; a.act = act; a.act_rows = act_rows;
+  a.dy = dy; a.dh = dh; a.rows = rows; a.offsets = offsets; a.n_local = desc->n_local;
+  a.ring_scales = ring_scales; a.act_scales = act_scales; a.dy_scales = dy_scales;
+  a.dh_scales = dh_scales;
   a.dw_gu = dw_gate_up; a.dw_d = dw_down; a.ws = ws; a.H = desc->hidden; a.I = desc->inter;
   return hip_status(launch_wgrad(a, stream));
 }

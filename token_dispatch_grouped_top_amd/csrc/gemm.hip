@@ -151,11 +151,13 @@ void k_pack_weights(const uint16_t* __restrict__ W, int64_t expert_stride, int32
 // Packing of a transposed weight (the backward GEMMs' B): the GEMM's weight
 // row n, k-value k is src[e][k][n] of a source stored [K][N] row-major per
 // expert.  One thread per 16-byte piece, as k_pack_weights; the 8 values of a
-// piece are 8 source rows apart by N.  Rows past N repeat the last one.
+// piece are 8 source rows apart by N.  Rows past N repeat the last one.  A_MX:
+// the k-step and LDS layout of the GEMMs whose token operand is MXFP8.
+template <bool A_MX>
 __global__ __launch_bounds__(256)
 void k_pack_weights_t(const uint16_t* __restrict__ W, int64_t expert_stride, int32_t K, int32_t N,
                       int32_t n_tiles, int32_t n_local, uint16_t* __restrict__ out) {
-  using G = Geo<false>;
+  using G = Geo<A_MX>;
   constexpr int BK = G::BK;
   constexpr int64_t kPieces = BM * BK / 8;
   const int nk = K / BK;
@@ -258,9 +260,10 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   set_split(g, a);
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
   if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_SWIGLU_MX>(g, n1, m_tiles, s);
-  if (a.h_out) {                   // bf16 tokens and weights (checked at the boundary)
+  if (a.h_out) {                   // bf16 weights (checked at the boundary)
     g.H_out = static_cast<uint16_t*>(a.h_out);
-    return launch_one<false, EPI_SWIGLU_BF16_H>(g, n1, m_tiles, s);
+    return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX_H>(g, n1, m_tiles, s)
+                                               : launch_one<false, EPI_SWIGLU_BF16_H>(g, n1, m_tiles, s);
   }
   return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX>(g, n1, m_tiles, s)
                                              : launch_one<false, EPI_SWIGLU_BF16>(g, n1, m_tiles, s);
@@ -293,28 +296,34 @@ hipError_t launch_recompute_h(const BwdArgs& a, hipStream_t s) {
   const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
   GemmParams g{};
   g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
-  g.A = a.ring; g.a_rows = a.ring_slots;
+  g.A = a.ring; g.A_scales = a.ring_scales; g.a_rows = a.ring_slots;
   g.W = a.w_gu; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = a.H;
   g.N = a.I; g.I = a.I;
   g.C = a.h; g.c_rows = a.rows;
   g.w_packed = a.w_gu_packed;
-  return launch_one<false, EPI_STORE_GU>(g, (a.I + BN / 2 - 1) / (BN / 2), m_tiles, s);
+  const int nt = (a.I + BN / 2 - 1) / (BN / 2);
+  return a.mx ? launch_one<true, EPI_STORE_GU>(g, nt, m_tiles, s)
+              : launch_one<false, EPI_STORE_GU>(g, nt, m_tiles, s);
 }
 
 // da = dy . W_d (dy column-blocked, K = H), then dh = SwiGLU'(h) . da in the
-// epilogue (column-blocked, 2I wide).  B: W_d^T packed [n_local][I][H].
+// epilogue (column-blocked, 2I wide; MXFP8 dy in, MXFP8 dh out when a.mx).
+// B: W_d^T packed [n_local][I][H].
 hipError_t launch_down_dgrad(const BwdArgs& a, hipStream_t s) {
   const int64_t span = static_cast<int64_t>(a.s_end) - a.s_begin;
   if (span <= 0) return hipSuccess;
   const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
   GemmParams g{};
   g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
-  g.A = a.dy; g.a_rows = a.rows;
+  g.A = a.dy; g.A_scales = a.dy_scales; g.a_rows = a.rows;
   g.W = a.w_d_t; g.w_expert_stride = static_cast<int64_t>(a.H) * a.I; g.K = a.H;
   g.N = a.I; g.I = 0;
-  g.C = a.dh; g.c_rows = a.rows; g.H_src = static_cast<const uint16_t*>(a.h);
+  g.C = a.dh; g.C_scales = a.dh_scales; g.c_rows = a.rows;
+  g.H_src = static_cast<const uint16_t*>(a.h);
   g.w_packed = 1;
-  return launch_one<false, EPI_SWIGLU_BWD>(g, (a.I + BN - 1) / BN, m_tiles, s);
+  const int nt = (a.I + BN - 1) / BN;
+  return a.mx ? launch_one<true, EPI_SWIGLU_BWD_MX>(g, nt, m_tiles, s)
+              : launch_one<false, EPI_SWIGLU_BWD>(g, nt, m_tiles, s);
 }
 
 // dx_s = dh . W_gu (dh column-blocked, K = 2I) -> bf16 [rows][H], row-major.
@@ -325,12 +334,14 @@ hipError_t launch_gate_up_dgrad(const BwdArgs& a, hipStream_t s) {
   const int m_tiles = static_cast<int>((span + BM - 1) / BM) + a.n_local;
   GemmParams g{};
   g.offsets = a.offsets; g.n_local = a.n_local; g.s_begin = a.s_begin; g.s_end = a.s_end;
-  g.A = a.dh; g.a_rows = a.rows;
+  g.A = a.dh; g.A_scales = a.dh_scales; g.a_rows = a.rows;
   g.W = a.w_gu_t; g.w_expert_stride = static_cast<int64_t>(2) * a.I * a.H; g.K = 2 * a.I;
   g.N = a.H; g.I = 0;
   g.C = a.dx; g.c_rows = a.rows;
   g.w_packed = 1;
-  return launch_one<false, EPI_STORE_BF16>(g, (a.H + BN - 1) / BN, m_tiles, s);
+  const int nt = (a.H + BN - 1) / BN;
+  return a.mx ? launch_one<true, EPI_STORE_BF16>(g, nt, m_tiles, s)
+              : launch_one<false, EPI_STORE_BF16>(g, nt, m_tiles, s);
 }
 
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s) {
@@ -348,15 +359,20 @@ size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local) {
 }
 
 hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                                   int32_t n_local, uint16_t* packed_gu_t, uint16_t* packed_d_t,
-                                   hipStream_t s) {
+                                   int32_t n_local, bool act_mx, uint16_t* packed_gu_t,
+                                   uint16_t* packed_d_t, hipStream_t s) {
   auto pack_t = [&](const uint16_t* W, int64_t stride, int32_t K, int32_t N, uint16_t* out) {
     const int n_tiles = (N + BN - 1) / BN;
-    const int64_t pieces = static_cast<int64_t>(n_local) * n_tiles * (K / Geo<false>::BK) *
-                           (BM * Geo<false>::BK / 8);
+    // the same number of 16-byte pieces for either k-step (K % 64 == 0)
+    const int64_t pieces = static_cast<int64_t>(n_local) * n_tiles * K * BM / 8;
     const int64_t blocks = (pieces + 255) / 256;
-    hipLaunchKernelGGL(k_pack_weights_t, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
-                       dim3(256), 0, s, W, stride, K, N, n_tiles, n_local, out);
+    const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
+    if (act_mx)
+      hipLaunchKernelGGL(k_pack_weights_t<true>, grid, dim3(256), 0, s, W, stride, K, N, n_tiles,
+                         n_local, out);
+    else
+      hipLaunchKernelGGL(k_pack_weights_t<false>, grid, dim3(256), 0, s, W, stride, K, N, n_tiles,
+                         n_local, out);
     return hipGetLastError();
   };
   hipError_t e = hipSuccess;

@@ -68,16 +68,17 @@ template <bool A_MX> struct Geo {
 static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LDS budget");
 
 // EPI_SWIGLU_BWD: the backward of SwiGLU on the down GEMM's gradient (da):
-// reads g, u of the same (row, i) from H_src and writes dh = [dg, du].
+// reads g, u of the same (row, i) from H_src and writes dh = [dg, du] (bf16;
+// EPI_SWIGLU_BWD_MX: MXFP8, blocks of 32 along 2I, into C and C_scales).
 // EPI_STORE_GU: a gate/up tile stores g and u themselves (h = [g, u], bf16
-// [c_rows][2 N] row-major) for that backward.
+// [c_rows][2 N] row-major) for that backward.  EPI_SWIGLU_BF16_H and
+// EPI_SWIGLU_MX_H: the forward's SwiGLU epilogues that also store h so.
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2, EPI_SWIGLU_BWD = 3,
-           EPI_STORE_GU = 4,
-          EPI_SWIGLU_BF16_H = 5 };
+           EPI_STORE_GU = 4, EPI_SWIGLU_BF16_H = 5, EPI_SWIGLU_BWD_MX = 6, EPI_SWIGLU_MX_H = 7 };
 // Whether an epilogue pairs gate and up columns (the gate/up weight order).
 template <int EPI> constexpr bool epi_swiglu() {
   return EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MX || EPI == EPI_STORE_GU ||
-         EPI == EPI_SWIGLU_BF16_H;
+         EPI == EPI_SWIGLU_BF16_H || EPI == EPI_SWIGLU_MX_H;
 }
 
 struct GemmParams {
@@ -365,11 +366,18 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
           *reinterpret_cast<uint2*>(hrow + p.N + col) = make_uint2(pack_bf16x2(u4.x, u4.y), pack_bf16x2(u4.z, u4.w));
         }
     }
-  } else if (EPI == EPI_SWIGLU_BWD) {
+  } else if (EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_BWD_MX) {
     // da of 4 consecutive columns per lane and (mi, ni, g); with g, u of the
     // same (row, i) from H_src: dg = da u SiLU'(g), du = da SiLU(g), where
     // SiLU(g) = g s, SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g).  dh is
     // column-blocked (the next GEMM's token operand), 2 N wide.
+    // MXFP8: the 32 columns of (mi, ni) are one block of dg and one of du (N
+    // a multiple of 32); lane l holds 16 of them (4 columns at 8 g + 4 (l /
+    // 32)) and lane l ^ 32 the other 16, so the block amax takes one
+    // shuffle; two more swap code words so that each lane stores 16
+    // consecutive codes.  Lanes l and l ^ 32 share the row and the block, so
+    // the skips below never split a pair.
+    constexpr bool MXO = EPI == EPI_SWIGLU_BWD_MX;
     uint8_t* C = static_cast<uint8_t*>(p.C);
     const int64_t N2 = 2 * static_cast<int64_t>(p.N);
 #pragma unroll
@@ -381,11 +389,13 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
       const int64_t crow = c_row_of(r);
       const uint16_t* hrow = p.H_src + crow * N2;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni) {
+        const int cb = n0 + 128 * wn + 32 * ni;              // first column of the block
+        if (cb >= p.N) continue;
+        float dg[4][4], du[4][4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + 128 * wn + 32 * ni + 8 * g + 4 * khalf;
-          if (col >= p.N) continue;
+          const int col = cb + 8 * g + 4 * khalf;
           const uint2 gb = *reinterpret_cast<const uint2*>(hrow + col);
           const uint2 ub = *reinterpret_cast<const uint2*>(hrow + p.N + col);
           const float gv[4] = {__uint_as_float(gb.x << 16), __uint_as_float(gb.x & 0xffff0000u),
@@ -394,18 +404,52 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
                                __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xffff0000u)};
           const float4 t = tv[4 * ni + g];
           const float da[4] = {t.x, t.y, t.z, t.w};
-          float dg[4], du[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[q]));
-            du[q] = da[q] * gv[q] * sg;
-            dg[q] = da[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+            du[g][q] = da[q] * gv[q] * sg;
+            dg[g][q] = da[q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
           }
-          *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * col)) =
-              make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * (p.N + col))) =
-              make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          if (!MXO) {
+            *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * col)) =
+                make_uint2(pack_bf16x2(dg[g][0], dg[g][1]), pack_bf16x2(dg[g][2], dg[g][3]));
+            *reinterpret_cast<uint2*>(C + colblk_byte(crow, p.c_rows, 2 * (p.N + col))) =
+                make_uint2(pack_bf16x2(du[g][0], du[g][1]), pack_bf16x2(du[g][2], du[g][3]));
+          }
         }
+        if (MXO) {
+          float mg = 0.0f, mu = 0.0f;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { mg = fmaxf(mg, fabsf(dg[g][q])); mu = fmaxf(mu, fabsf(du[g][q])); }
+          mg = fmaxf(mg, __shfl_xor(mg, 32));
+          mu = fmaxf(mu, __shfl_xor(mu, 32));
+          const int Eg = mx_scale_exp(mg), Eu = mx_scale_exp(mu);
+          uint32_t cg[4], cu[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            cg[g] = e4m3_code_scaled(dg[g][0], Eg) | (e4m3_code_scaled(dg[g][1], Eg) << 8) |
+                    (e4m3_code_scaled(dg[g][2], Eg) << 16) | (e4m3_code_scaled(dg[g][3], Eg) << 24);
+            cu[g] = e4m3_code_scaled(du[g][0], Eu) | (e4m3_code_scaled(du[g][1], Eu) << 8) |
+                    (e4m3_code_scaled(du[g][2], Eu) << 16) | (e4m3_code_scaled(du[g][3], Eu) << 24);
+          }
+          // half 0 keeps columns 0-3 and 8-11 and takes 4-7 and 12-15; half 1
+          // keeps 20-23 and 28-31 and takes 16-19 and 24-27
+          const uint32_t xg0 = __shfl_xor(khalf ? cg[0] : cg[2], 32);
+          const uint32_t xg1 = __shfl_xor(khalf ? cg[1] : cg[3], 32);
+          const uint32_t xu0 = __shfl_xor(khalf ? cu[0] : cu[2], 32);
+          const uint32_t xu1 = __shfl_xor(khalf ? cu[1] : cu[3], 32);
+          const uint4 og = khalf ? make_uint4(xg0, cg[2], xg1, cg[3]) : make_uint4(cg[0], xg0, cg[1], xg1);
+          const uint4 ou = khalf ? make_uint4(xu0, cu[2], xu1, cu[3]) : make_uint4(cu[0], xu0, cu[1], xu1);
+          *reinterpret_cast<uint4*>(C + colblk_byte(crow, p.c_rows, cb + 16 * khalf)) = og;
+          *reinterpret_cast<uint4*>(C + colblk_byte(crow, p.c_rows, p.N + cb + 16 * khalf)) = ou;
+          if (khalf == 0) {
+            p.C_scales[scale_byte(crow, p.c_rows, cb / 32)] = static_cast<uint8_t>(Eg + 127);
+            p.C_scales[scale_byte(crow, p.c_rows, (p.N + cb) / 32)] = static_cast<uint8_t>(Eu + 127);
+          }
+        }
+      }
     }
   } else if (EPI == EPI_STORE_BF16) {
     constexpr int RB = BN * 2;                             // bytes per staged row
@@ -437,7 +481,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
   } else {
     // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
     // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
-    constexpr bool MXO = EPI == EPI_SWIGLU_MX;
+    constexpr bool MXO = EPI == EPI_SWIGLU_MX || EPI == EPI_SWIGLU_MX_H;
     constexpr int RB = MXO ? (BN / 2) * 4 : (BN / 2) * 2;  // staged row: 128 fp32 or bf16
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -457,7 +501,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
             a[j] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
           const int i = 64 * wn + 32 * ni + 8 * g + 4 * khalf;
-          if constexpr (EPI == EPI_SWIGLU_BF16_H) {     // h kept for the backward
+          if constexpr (EPI == EPI_SWIGLU_BF16_H || EPI == EPI_SWIGLU_MX_H) {  // h kept for the backward
             if (r < nrows && n0 + i < p.N) {
               uint16_t* hrow = p.H_out + c_row_of(r) * (2 * static_cast<int64_t>(p.N));
               *reinterpret_cast<uint2*>(hrow + n0 + i) =

@@ -175,8 +175,9 @@ hipError_t launch_combine(const void* y, int32_t y_rows, const int32_t* soa, con
 hipError_t launch_unmerge_slots(void* const* dout_ptr, int32_t n_part, int32_t part_rows,
                                 const void* y, int32_t y_rows, const int32_t* aos,
                                 const int32_t* offsets, int32_t n_local, int32_t n_slots,
-                                const float* gate, int32_t k, int32_t H, void* dy, int32_t dy_rows,
-                                float* dgate, int32_t* status, hipStream_t s);
+                                const float* gate, int32_t k, int32_t H, void* dy,
+                                uint8_t* dy_scales, int32_t dy_rows, float* dgate, int32_t* status,
+                                hipStream_t s);
 
 // Merge driven by routed slots: each token merged at its smallest local slot
 // (gate null: unit gates, i.e. the plain sum of the token's slot rows).
@@ -219,6 +220,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // s % rows in every buffer; x from the ring (row s % ring_slots).
 struct BwdArgs {
   const void* ring; int32_t ring_slots;
+  const uint8_t* ring_scales;  // MXFP8 tokens (mx): the ring's, dy's and dh's E8M0 scales
+  const uint8_t* dy_scales;
+  uint8_t* dh_scales;
+  int32_t mx;
   const int32_t* offsets; int32_t n_local; int32_t s_begin, s_end;
   const uint16_t* w_gu;       // the forward's gate/up weights (the recompute of h)
   int32_t w_gu_packed;        // ... in the packed tile order
@@ -239,6 +244,9 @@ struct WgradArgs {
   const void* ring; int32_t ring_slots;
   const void* act; int32_t act_rows;
   const void* dy; const void* dh; int32_t rows;
+  // MXFP8 operands: E8M0 scales of each (all null for bf16 operands)
+  const uint8_t* ring_scales; const uint8_t* act_scales;
+  const uint8_t* dy_scales; const uint8_t* dh_scales;
   const int32_t* offsets; int32_t n_local;
   void* dw_gu; void* dw_d;
   void* ws;
@@ -250,8 +258,8 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
 size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
 size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local);
 hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                                   int32_t n_local, uint16_t* packed_gu_t, uint16_t* packed_d_t,
-                                   hipStream_t s);
+                                   int32_t n_local, bool act_mx, uint16_t* packed_gu_t,
+                                   uint16_t* packed_d_t, hipStream_t s);
 
 // Packed weights: bytes, and the packing launch (either source may be null).
 size_t packed_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);

@@ -290,6 +290,73 @@ __device__ __forceinline__ void unmerge_slot(void* const* __restrict__ dout_part
   if (lane == 0) dgate[a_s] = part;
 }
 
+// unmerge_slot with MXFP8 dy: the fp32 products w * dout[t] quantised in
+// blocks of 32 along H (E4M3 codes column-blocked like the ring, E8M0 scales
+// in pairs).  A block is 4 consecutive pieces, i.e. 4 consecutive lanes of
+// one instruction: its amax by two xor-shuffles, as in the MXFP8 gather.
+// dgate as unmerge_slot (the same fp32 sum order).  All 64 lanes must call it.
+__device__ __forceinline__ void unmerge_slot_mx(void* const* __restrict__ dout_parts, int32_t n_part,
+                                                int32_t part_rows, const uint16_t* __restrict__ y,
+                                                int32_t y_rows, int32_t a_s,
+                                                const float* __restrict__ gate, int64_t s, int32_t k,
+                                                int32_t H, uint8_t* __restrict__ dy,
+                                                uint8_t* __restrict__ dy_scales, int32_t dy_rows,
+                                                float* __restrict__ dgate, int32_t* status) {
+  const int lane = lane_id();
+  const uint4* src = token_row(dout_parts, n_part, part_rows, a_s / k, H);
+  if (!src || s >= y_rows) { if (lane == 0) set_status(status, MOK_ERR_CAPACITY); return; }
+  const float w = gate[a_s];
+  const uint4* yrow = reinterpret_cast<const uint4*>(y + s * static_cast<int64_t>(H));
+  const int64_t drow = s % dy_rows;
+  const int nvec = H / 8;                 // H % 64 == 0: groups of 4 lanes are whole
+  float part = 0.0f;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * kMergeFast) {
+    uint4 bd[kMergeFast], by[kMergeFast];
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < nvec) { bd[u] = src[v]; by[u] = yrow[v]; }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      if (v0 + u * kWave >= nvec) break;  // wave-uniform
+      const int v = v0 + u * kWave + lane;
+      const bool ok = v < nvec;
+      const uint32_t d4[4] = {ok ? bd[u].x : 0u, ok ? bd[u].y : 0u, ok ? bd[u].z : 0u, ok ? bd[u].w : 0u};
+      const uint32_t y4[4] = {ok ? by[u].x : 0u, ok ? by[u].y : 0u, ok ? by[u].z : 0u, ok ? by[u].w : 0u};
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float dlo = __uint_as_float(d4[q] << 16), dhi = __uint_as_float(d4[q] & 0xffff0000u);
+        part = fmaf(dlo, __uint_as_float(y4[q] << 16), part);
+        part = fmaf(dhi, __uint_as_float(y4[q] & 0xffff0000u), part);
+        f[2 * q] = w * dlo;
+        f[2 * q + 1] = w * dhi;
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const int E = mx_scale_exp(amax);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo |= e4m3_code_scaled(f[q], E) << (8 * q);
+        hi |= e4m3_code_scaled(f[q + 4], E) << (8 * q);
+      }
+      if (ok) {
+        *reinterpret_cast<uint2*>(dy + colblk_byte(drow, dy_rows, 8 * static_cast<int64_t>(v))) =
+            make_uint2(lo, hi);
+        if ((v & 3) == 0) dy_scales[scale_byte(drow, dy_rows, v >> 2)] = static_cast<uint8_t>(E + 127);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  if (lane == 0) dgate[a_s] = part;
+}
+
 // Slot-driven merge: slot s (s < R) merges its token t = assign_of_slot[s] / k
 // when s is t's smallest local slot, so every token with a local assignment is
 // merged exactly once while only the R routed slots (not all pool tokens) are

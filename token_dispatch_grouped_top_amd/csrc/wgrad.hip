@@ -50,9 +50,13 @@ __global__ void k_pad_offsets(const int32_t* __restrict__ offsets, int32_t n_loc
 // features per workgroup, through an LDS tile.  dst_blocked: column-blocked
 // (64-byte block kb of feature row f at (kb * F + f) * 64); else row-major
 // [F][kpad].  Positions past a segment's count, and past poff[n_local], get
-// zeros.
+// zeros.  MX: the source holds E4M3 codes (one byte per feature) and E8M0
+// scales (pairs); each value is converted to bf16 on the way, code x 2^E,
+// which bf16 holds exactly for every code whose value is at least 2^-133.
+template <bool MX>
 __global__ __launch_bounds__(256)
-void k_slot_transpose(const uint8_t* __restrict__ src, int32_t src_rows, int32_t F,
+void k_slot_transpose(const uint8_t* __restrict__ src, const uint8_t* __restrict__ src_scales,
+                      int32_t src_rows, int32_t F,
                       const int32_t* __restrict__ offsets, const int32_t* __restrict__ poff,
                       int32_t n_local, int32_t kpad, int32_t dst_blocked,
                       uint8_t* __restrict__ dst) {
@@ -76,7 +80,18 @@ void k_slot_transpose(const uint8_t* __restrict__ src, int32_t src_rows, int32_t
     uint4 v = make_uint4(0, 0, 0, 0);
     if (q < s_poff[n_local] && jj >= 0 && jj < cnt) {
       const int64_t s = s_off[e] + jj;
-      v = *reinterpret_cast<const uint4*>(src + colblk_byte(s % src_rows, src_rows, 2 * (f0 + 8 * c)));
+      if (MX) {
+        const int64_t row = s % src_rows;
+        const uint2 c8 = *reinterpret_cast<const uint2*>(src + colblk_byte(row, src_rows, f0 + 8 * c));
+        const uint32_t S = src_scales[scale_byte(row, src_rows, (f0 + 8 * c) >> 5)];
+        const float sc = __uint_as_float(S ? S << 23 : 0x00400000u);      // 2^(S - 127)
+        v = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, true)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, true)));
+      } else {
+        v = *reinterpret_cast<const uint4*>(src + colblk_byte(s % src_rows, src_rows, 2 * (f0 + 8 * c)));
+      }
     }
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -138,13 +153,18 @@ hipError_t launch_wgrad_one(const void* at, const void* bt, int32_t M, int32_t N
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, int32_t src_rows, int32_t F, const int32_t* offsets,
-                            const int32_t* poff, int32_t n_local, int32_t kpad, bool blocked,
-                            void* dst, hipStream_t s) {
+hipError_t launch_transpose(const void* src, const uint8_t* scales, int32_t src_rows, int32_t F,
+                            const int32_t* offsets, const int32_t* poff, int32_t n_local,
+                            int32_t kpad, bool blocked, void* dst, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(F / 64));
-  hipLaunchKernelGGL(k_slot_transpose, grid, dim3(256), 0, s, static_cast<const uint8_t*>(src),
-                     src_rows, F, offsets, poff, n_local, kpad, blocked ? 1 : 0,
-                     static_cast<uint8_t*>(dst));
+  if (scales)
+    hipLaunchKernelGGL(k_slot_transpose<true>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(src),
+                       scales, src_rows, F, offsets, poff, n_local, kpad, blocked ? 1 : 0,
+                       static_cast<uint8_t*>(dst));
+  else
+    hipLaunchKernelGGL(k_slot_transpose<false>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(src),
+                       scales, src_rows, F, offsets, poff, n_local, kpad, blocked ? 1 : 0,
+                       static_cast<uint8_t*>(dst));
   return hipGetLastError();
 }
 
@@ -174,10 +194,14 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s) {
   void* aT = w;
   hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, a.n_local, kp, poff);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = launch_transpose(a.dy, a.rows, a.H, a.offsets, poff, a.n_local, kp, true, dyT, s);
-  if (e == hipSuccess) e = launch_transpose(a.act, a.act_rows, a.I, a.offsets, poff, a.n_local, kp, false, aT, s);
-  if (e == hipSuccess) e = launch_transpose(a.dh, a.rows, 2 * a.I, a.offsets, poff, a.n_local, kp, true, dhT, s);
-  if (e == hipSuccess) e = launch_transpose(a.ring, a.ring_slots, a.H, a.offsets, poff, a.n_local, kp, false, xT, s);
+  if (e == hipSuccess)
+    e = launch_transpose(a.dy, a.dy_scales, a.rows, a.H, a.offsets, poff, a.n_local, kp, true, dyT, s);
+  if (e == hipSuccess)
+    e = launch_transpose(a.act, a.act_scales, a.act_rows, a.I, a.offsets, poff, a.n_local, kp, false, aT, s);
+  if (e == hipSuccess)
+    e = launch_transpose(a.dh, a.dh_scales, a.rows, 2 * a.I, a.offsets, poff, a.n_local, kp, true, dhT, s);
+  if (e == hipSuccess)
+    e = launch_transpose(a.ring, a.ring_scales, a.ring_slots, a.H, a.offsets, poff, a.n_local, kp, false, xT, s);
   if (e == hipSuccess && a.dw_d) e = launch_wgrad_one(dyT, aT, a.H, a.I, kp, a.offsets, poff, a.n_local, a.dw_d, s);
   if (e == hipSuccess && a.dw_gu)
     e = launch_wgrad_one(dhT, xT, 2 * a.I, a.H, kp, a.offsets, poff, a.n_local, a.dw_gu, s);
