@@ -18,6 +18,7 @@ Prints ONE JSON line.  Extra reports go to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -213,16 +214,18 @@ def time_router_gemm(mok, wl, reps: int = 20):
 
 
 def time_backward(mok, dw, st, reps: int = 10):
-    """The backward of the layer share after a forward step (bf16 only): merge
-    backward (dy, dgate), the expert FFN backward (recompute of h, down dgrad
-    with the SwiGLU backward, gate/up dgrad), dispatch backward (dx), weight
-    gradients (transposes + two GEMMs over each expert's slots).  Seeded
-    N(0, 1) dout for every pool token; per-call means over `reps` calls."""
+    """The backward of the layer share after a forward step (bf16 weights; bf16
+    or MXFP8 activations, the latter through the _mx calls): merge backward
+    (dy, dgate), the expert FFN backward (recompute of h, down dgrad with the
+    SwiGLU backward, gate/up dgrad), dispatch backward (dx), weight gradients
+    (transposes + two GEMMs over each expert's slots).  Seeded N(0, 1) dout for
+    every pool token; per-call means over `reps` calls."""
     import numpy as np
     import torch
     import workloads as W
     from gpu_harness import to_dev
     wl = dw.wl
+    mx = wl.act_format == mok.MOK_ACT_MXFP8_E4M3
     H, I, k, cap = wl.H, wl.I, wl.k, st.cap
     R = int(st.offsets[-1].item())
     d = dw.desc(max_rows=cap, weights_packed=1)        # h recomputed with the packed gate/up
@@ -234,35 +237,61 @@ def time_backward(mok, dw, st, reps: int = 10):
     gu_t = torch.empty(a, dtype=torch.uint8, device="cuda")
     d_t = torch.empty(b, dtype=torch.uint8, device="cuda")
     mok.mok_pack_weights_bwd(d, dw.w_gu, dw.w_d, gu_t, d_t)
-    dy = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    tok = torch.uint8 if mx else torch.int16
+    scales = (lambda n: torch.empty((cap, n // 32), dtype=torch.uint8, device="cuda")) if mx \
+        else (lambda n: None)
+    dy, dy_sc = torch.empty((cap, H), dtype=tok, device="cuda"), scales(H)
     dgate = torch.empty((wl.T, k), dtype=torch.float32, device="cuda")
     h = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
-    dh = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
+    dh, dh_sc = torch.empty((cap, 2 * I), dtype=tok, device="cuda"), scales(2 * I)
     dxs = torch.empty((cap, H), dtype=torch.int16, device="cuda")
     dwgu = torch.empty((wl.n_local, 2 * I, H), dtype=torch.int16, device="cuda")
     dwd = torch.empty((wl.n_local, H, I), dtype=torch.int16, device="cuda")
     wws = torch.empty(mok.mok_wgrad_workspace_size(d, cap), dtype=torch.uint8, device="cuda")
     hsv = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
-    calls = {
-        "combine_bwd": lambda: mok.mok_combine_backward(dout, st.y, cap, st.aos, st.offsets,
-                                                        wl.n_local, cap, dw.topk_gate, k, H, dy,
-                                                        cap, dgate, st.status),
-        "ffn_bwd": lambda: mok.mok_expert_ffn_backward(d, st.ring, cap, dy, st.offsets, 0, cap,
-                                                       st.w_gu, gu_t, d_t, h, dh, dxs, cap),
-        "dispatch_bwd": lambda: mok.mok_dispatch_backward(dxs, cap, st.aos, st.offsets, wl.n_local,
-                                                          cap, st.soa, k, H, dx, st.status),
-        "wgrad": lambda: mok.mok_expert_wgrad(d, st.ring, cap, st.act, cap, dy, dh, cap, st.offsets,
-                                              dwgu, dwd, wws),
-        # h kept by the forward instead of recomputed: the forward's gate/up that also
-        # stores h (timed whole, to set against the plain gate/up), then the backward from it
-        "gate_up_save_h": lambda: mok.mok_expert_gate_up_save_h(d, st.ring, cap, st.offsets, 0, cap,
-                                                                st.w_gu, st.act, cap, hsv,
-                                                                st.gemm_ws),
-        "gate_up_plain": lambda: mok.mok_expert_gate_up(d, st.ring, None, cap, st.offsets, 0, cap,
-                                                        st.w_gu, st.act, None, cap, st.gemm_ws),
-        "ffn_bwd_saved": lambda: mok.mok_expert_ffn_backward_saved(d, dy, st.offsets, 0, cap, gu_t,
-                                                                   d_t, hsv, dh, dxs, cap),
-    }
+    dispatch_bwd = lambda: mok.mok_dispatch_backward(dxs, cap, st.aos, st.offsets, wl.n_local, cap,
+                                                     st.soa, k, H, dx, st.status)
+    gate_up_plain = lambda: mok.mok_expert_gate_up(d, st.ring, st.ring_sc, cap, st.offsets, 0, cap,
+                                                   st.w_gu, st.act, st.act_sc, cap, st.gemm_ws)
+    if mx:
+        calls = {
+            "combine_bwd": lambda: mok.mok_combine_backward_mx(dout, st.y, cap, st.aos, st.offsets,
+                                                               wl.n_local, cap, dw.topk_gate, k, H,
+                                                               dy, dy_sc, cap, dgate, st.status),
+            "ffn_bwd": lambda: mok.mok_expert_ffn_backward_mx(d, st.ring, st.ring_sc, cap, dy, dy_sc,
+                                                              st.offsets, 0, cap, st.w_gu, gu_t, d_t,
+                                                              h, False, dh, dh_sc, dxs, cap),
+            "dispatch_bwd": dispatch_bwd,
+            "wgrad": lambda: mok.mok_expert_wgrad_mx(d, st.ring, st.ring_sc, cap, st.act, st.act_sc,
+                                                     cap, dy, dy_sc, dh, dh_sc, cap, st.offsets,
+                                                     dwgu, dwd, wws),
+            "gate_up_save_h": lambda: mok.mok_expert_gate_up_save_h_mx(
+                d, st.ring, st.ring_sc, cap, st.offsets, 0, cap, st.w_gu, st.act, st.act_sc, cap,
+                hsv, st.gemm_ws),
+            "gate_up_plain": gate_up_plain,
+            "ffn_bwd_saved": lambda: mok.mok_expert_ffn_backward_mx(
+                d, None, None, cap, dy, dy_sc, st.offsets, 0, cap, None, gu_t, d_t, hsv, True, dh,
+                dh_sc, dxs, cap),
+        }
+    else:
+        calls = {
+            "combine_bwd": lambda: mok.mok_combine_backward(dout, st.y, cap, st.aos, st.offsets,
+                                                            wl.n_local, cap, dw.topk_gate, k, H, dy,
+                                                            cap, dgate, st.status),
+            "ffn_bwd": lambda: mok.mok_expert_ffn_backward(d, st.ring, cap, dy, st.offsets, 0, cap,
+                                                           st.w_gu, gu_t, d_t, h, dh, dxs, cap),
+            "dispatch_bwd": dispatch_bwd,
+            "wgrad": lambda: mok.mok_expert_wgrad(d, st.ring, cap, st.act, cap, dy, dh, cap,
+                                                  st.offsets, dwgu, dwd, wws),
+            # h kept by the forward instead of recomputed: the forward's gate/up that also
+            # stores h (timed whole, to set against the plain gate/up), then the backward from it
+            "gate_up_save_h": lambda: mok.mok_expert_gate_up_save_h(d, st.ring, cap, st.offsets, 0,
+                                                                    cap, st.w_gu, st.act, cap, hsv,
+                                                                    st.gemm_ws),
+            "gate_up_plain": gate_up_plain,
+            "ffn_bwd_saved": lambda: mok.mok_expert_ffn_backward_saved(d, dy, st.offsets, 0, cap,
+                                                                       gu_t, d_t, hsv, dh, dxs, cap),
+        }
     out = {}
     for name, f in calls.items():
         f()
@@ -426,7 +455,7 @@ def time_fused(mok, d, run, reps: int = 10) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def measure_extras(mok, DeviceWorkload, dw, wl, args) -> dict:
+def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
     """The other configurations, each as its own step (or fused call): the Mixtral-shaped
     layer (also as one fused call from its logits), the Zipf MXFP8 and full-MXFP8 shares,
     the minibatch sweep of the fused call in stream and persistent mode on the headline's
@@ -458,6 +487,19 @@ def measure_extras(mok, DeviceWorkload, dw, wl, args) -> dict:
         del st2, dw2, wl2
         torch.cuda.empty_cache()
     res["streaming"] = time_streaming(mok, DeviceWorkload)
+    torch.cuda.empty_cache()
+    # the backward of the headline's share, bf16 and with MXFP8 activations (the same
+    # tokens, weights and routing; bf16 weights)
+    res["backward"] = time_backward(mok, dw, st)
+    log(f"[bench] backward bf16 (ms): {res['backward']}")
+    wl_mx = dataclasses.replace(wl, act_format=1, name=wl.name + "_mxfp8act")
+    dw_mx = DeviceWorkload(wl_mx)
+    st_mx = Step(dw_mx, BENCH_MAX_ROWS)
+    for _ in range(3):
+        st_mx.run()
+    res["backward_mxfp8"] = time_backward(mok, dw_mx, st_mx)
+    log(f"[bench] backward MXFP8 (ms): {res['backward_mxfp8']}")
+    del st_mx, dw_mx, wl_mx
     torch.cuda.empty_cache()
     # minibatch sweep of the fused call on the headline's share: last, so that the
     # headline's warm-up follows GPU work rather than host-side set-up
@@ -504,12 +546,15 @@ def main():
     ap.add_argument("--no-extras", dest="extras", action="store_false",
                     help="time the headline only (default: also the Mixtral-shaped layer, the "
                          "Zipf MXFP8 and full-MXFP8 shares, the minibatch sweep of the fused "
-                         "call in both modes, and 8 streamed macrobatches)")
+                         "call in both modes, 8 streamed macrobatches, and the backward of the "
+                         "headline share in bf16 and with MXFP8 activations)")
     ap.add_argument("--fused-only", default="",
                     help="MODE:M:N_MOVE -- only run the fused call 5 times (for profiling), "
                          "MODE 0 stream / 1 persistent")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the backward of the layer share (bf16 workloads)")
+                    help="also time the backward of the layer share with --no-extras or another "
+                         "workload (bf16 weights; the default run times it in bf16 and with "
+                         "MXFP8 activations)")
     ap.add_argument("--tune", action="store_true",
                     help="also run mok_tune_forward over minibatches (and mover counts) per mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -570,7 +615,7 @@ def main():
     log(f"[bench] first pass (after {args.warmup} warm-up steps): {first['wall_ms']:.4f} ms/step")
     extras = {}
     if args.extras and args.workload == "kimi":
-        extras = measure_extras(mok, DeviceWorkload, dw, wl, args)
+        extras = measure_extras(mok, DeviceWorkload, dw, wl, st, args)
     m = measure(st, args.steps, args.warmup)
     wall_ms, per, per_sum = m["wall_ms"], m["per"], m["per_sum"]
     rr = step_rates(wl, st, per, wall_ms)
@@ -604,8 +649,8 @@ def main():
             log(f"[bench] tuner ({key}): {tuned[key]}")
             del ws_t
 
-    backward = None
-    if args.backward and not mx and not wfmt:
+    backward = extras.get("backward")
+    if backward is None and args.backward and not wfmt:
         backward = time_backward(mok, dw, st)
         log(f"[bench] backward (ms): {backward}")
 
@@ -666,6 +711,7 @@ def main():
         "streaming_ms_per_macrobatch": extras.get("streaming"),
         "router_gemm": router,
         "backward_ms": backward,
+        "backward_mxfp8_ms": extras.get("backward_mxfp8"),
         "tuned_forward": tuned,
         "cpu_baseline": cpu,
     }

@@ -566,8 +566,11 @@ mok_status mok_tune_forward(const mok_layer_desc* desc, const int32_t* minibatch
  * *status_host (MOK_OK, MOK_ERR_CAPACITY or MOK_ERR_DEVICE). */
 mok_status mok_device_status(const void* ws, int32_t* status_host, hipStream_t stream);
 
-/* Minibatch the fused call uses for desc (after the two-wave rule) and the
- * number of windows it plans for T tokens.  Host only. */
+/* Minibatch the fused call uses for desc: desc->minibatch if set (clipped to
+ * the row capacity), else the two-wave rule (mok_choose_minibatch) for each
+ * of a window's GEMMs on this device's CUs with 256 x 256 tiles -- gate/up
+ * (n_out = 2I) and down (n_out = H) -- the larger of the two, so that both
+ * fill at least two waves.  Host only. */
 int32_t mok_forward_minibatch(const mok_layer_desc* desc, int32_t T);
 
 const char* mok_status_str(mok_status s);

@@ -161,6 +161,12 @@ def test_workspace_query_and_small_workspace():
 
 
 def test_forward_minibatch_plan():
+    # the rule for both GEMMs of a window, the larger; no GPU here: 256 CUs
+    for H, I, T, k in ((7168, 2048, 1024, 8), (4096, 14336, 4096, 2), (256, 512, 256, 2)):
+        d = mok.mok_layer_desc(hidden=H, inter=I, n_experts=8, top_k=k, expert_base=0, n_local=8)
+        want = max(oracle.choose_minibatch(256, 256, 256, 2 * I, T * k),
+                   oracle.choose_minibatch(256, 256, 256, H, T * k))
+        assert mok.mok_forward_minibatch(d, T) == want
     # explicit minibatch is clipped to the row capacity; S defaults to 2M
     assert mok.mok_forward_minibatch(_desc(minibatch=100), 256) == 100
     assert mok.mok_forward_minibatch(_desc(minibatch=5000), 256) == 512

@@ -104,9 +104,14 @@ struct Plan {
   size_t per_macro_counts, per_macro_offsets, per_macro_soa, per_macro_aos, per_macro_win;
 };
 
+// The two-wave rule for each of the window's GEMMs (gate/up: 2I output
+// columns; down: H), the larger of the two: every GEMM of a window then fills
+// at least two waves of the chip.
 int32_t plan_minibatch(const mok_layer_desc* d, int64_t cap) {
   if (d->minibatch > 0) return static_cast<int32_t>(std::min<int64_t>(d->minibatch, std::max<int64_t>(cap, 1)));
-  int32_t m = mok_choose_minibatch(device_cus(), kGemmTileM, kGemmTileN, 2 * d->inter, cap);
+  const int n = device_cus();
+  const int32_t m = std::max(mok_choose_minibatch(n, kGemmTileM, kGemmTileN, 2 * d->inter, cap),
+                             mok_choose_minibatch(n, kGemmTileM, kGemmTileN, d->hidden, cap));
   return std::max<int32_t>(m, 1);
 }
 
