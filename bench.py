@@ -111,6 +111,7 @@ class Step:
         self.act = torch.empty((cap, I), dtype=torch.uint8 if mx else torch.int16, device=dev)
         self.act_sc = torch.empty((cap, I // 32), dtype=torch.uint8, device=dev) if mx else None
         self.y = torch.empty((cap, H), dtype=torch.int16, device=dev)
+        self.plan = torch.empty((cap, 16), dtype=torch.uint8, device=dev)   # merge plan records
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         # K split of the GEMMs' last partial round: counters must start at zero
         self.gemm_ws = torch.zeros(mok.mok_gemm_workspace_size(), dtype=torch.uint8, device=dev)
@@ -140,11 +141,14 @@ class Step:
         mok.mok_expert_gate_up(self.desc, self.ring, self.ring_sc, self.cap, self.offsets, 0,
                                self.cap, self.w_gu, self.act, self.act_sc, self.cap, self.gemm_ws)
         rec(4)
-        mok.mok_expert_down(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0, self.cap,
-                            self.w_d, self.y, self.cap, self.gemm_ws)
+        # the down GEMM writes each single-slot token's output row itself (bf16(g y));
+        # the merge then takes the tokens with several local slots
+        mok.mok_expert_down_merge(self.desc, self.act, self.act_sc, self.cap, self.offsets, 0,
+                                  self.cap, self.w_d, self.y, self.cap, self.aos, self.soa, gate,
+                                  dw.outs[0], self.plan, self.gemm_ws)
         rec(5)
-        mok.mok_combine_slots(self.y, self.cap, self.aos, self.offsets, wl.n_local, self.cap,
-                              self.soa, gate, wl.k, wl.H, dw.outs[0], self.status)
+        mok.mok_combine_slots_multi(self.y, self.cap, self.aos, self.offsets, wl.n_local, self.cap,
+                                    self.soa, gate, wl.k, wl.H, dw.outs[0], self.status)
         rec(6)
 
 
@@ -399,21 +403,28 @@ def measure(st, steps: int, warmup: int) -> dict:
 def step_rates(wl, st, per: dict, wall_ms: float) -> dict:
     """Algorithmic work of the step's kernels over their measured times: GEMM flop
     (4 R H I gate/up, 2 R H I down) against the MFMA peak of the weights' format, gather
-    bytes R H (2 + b_out) + R 8 and merge bytes R H 2 + T_out H 2 + T k 8 against HBM."""
+    bytes R H (2 + b_out) + R 8 against HBM, and the merge's bytes: the down GEMM writes
+    the output rows of tokens with one local slot itself (in place of their y rows), so
+    the merge moves the y rows of the R_multi slots of the T_multi tokens with several
+    local slots and their output rows, R_multi H 2 + T_multi H 2, plus every slot's
+    routing words R (1 + k) 4."""
     from gpu_harness import to_host
     R = int(to_host(st.offsets)[-1])
     soa = to_host(st.soa).reshape(wl.T, wl.k)
-    T_out = int((soa >= 0).any(1).sum())
+    n_loc = (soa >= 0).sum(1)
+    T_out = int((n_loc > 0).sum())
+    T_multi, R_multi = int((n_loc >= 2).sum()), int(n_loc[n_loc >= 2].sum())
     H, I = wl.H, wl.I
     mx = wl.act_format == 1
     peak = PEAK_FP8_TFLOPS if getattr(wl, "weight_format", 0) else PEAK_BF16_TFLOPS
     flop_gu, flop_dn = 4.0 * R * H * I, 2.0 * R * H * I
     b_out = (1 + 1 / 32) if mx else 2
     disp_bytes = R * H * (2 + b_out) + R * 8
-    comb_bytes = R * H * 2 + T_out * H * 2 + wl.T * wl.k * 8
+    comb_bytes = R_multi * H * 2 + T_multi * H * 2 + R * (1 + wl.k) * 4
     tf = lambda f, ms: f / (ms * 1e-3) / 1e12
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
-    return dict(R=R, T_out=T_out, peak=peak, flop_gate_up=flop_gu,
+    return dict(R=R, T_out=T_out, T_multi=T_multi, R_multi=R_multi, peak=peak,
+                flop_gate_up=flop_gu,
                 gate_up_tflops=tf(flop_gu, per["gate_up"]), down_tflops=tf(flop_dn, per["down"]),
                 gemm_tflops=tf(flop_gu + flop_dn, per["gate_up"] + per["down"]),
                 dispatch_GBps=gbs(disp_bytes, per["gather"]),
@@ -428,7 +439,8 @@ def config_summary(wl, st, m: dict) -> dict:
     pk = rr["peak"]
     return {"ms_per_layer": round(m["wall_ms"], 4),
             "breakdown_ms": {k: round(v, 4) for k, v in m["per"].items()},
-            "routed_rows": rr["R"], "tokens_out": rr["T_out"], "minibatch": st.M,
+            "routed_rows": rr["R"], "tokens_out": rr["T_out"],
+            "tokens_merged_by_combine": rr["T_multi"], "minibatch": st.M,
             "gate_up_tflops": round(rr["gate_up_tflops"], 1),
             "gate_up_frac": round(rr["gate_up_tflops"] / pk, 4),
             "down_tflops": round(rr["down_tflops"], 1),
@@ -689,7 +701,13 @@ def main():
                      "algorithmic_flop_per_launch": flop_gu},
         "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
         "breakdown_note": "gate_up from the timed region's events; the other calls from a separate "
-                          "pass with an event between every call (each marker drains the stream)",
+                          "pass with an event between every call (each marker drains the stream); "
+                          "down = mok_expert_down_merge (also writes the output rows of tokens "
+                          "with one local slot), combine = mok_combine_slots_multi (the tokens "
+                          "with several local slots)",
+        "merge_split": {"tokens_out": T_out, "tokens_merged_in_down": T_out - rr["T_multi"],
+                        "tokens_merged_by_combine": rr["T_multi"],
+                        "slots_of_those": rr["R_multi"]},
         "first_pass_ms": round(first["wall_ms"], 4),
         "first_pass_note": "the same K steps timed right after the W warm-up steps, before the "
                            "other configurations ran (the chip below its working clock)",

@@ -307,6 +307,39 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
                              int32_t H, const mok_tokens* out, int32_t* dev_status,
                              hipStream_t stream);
 
+/* The down GEMM with the merge of single-slot tokens in its epilogue (the
+ * article's push combine: a result goes straight back to its token).  For
+ * each slot s in [slot_begin, min(slot_end, R)) with a = assign_of_slot[s],
+ * t = a / k (k = desc->top_k): if s is t's only local slot (exactly one
+ * slot_of_assign[t][j] >= 0), out row t = bf16(fma(topk_gate[a], y_s, 0))
+ * with y_s the bf16 result, which is what mok_combine_slots writes for a
+ * single term; every other slot's y_s goes to y as mok_expert_down writes it.
+ * mok_expert_down_merge over all routed slots followed by
+ * mok_combine_slots_multi writes the same out, bit for bit, as
+ * mok_expert_down followed by mok_combine_slots; y then holds only the rows
+ * of tokens with several local slots (a forward whose y the backward reads
+ * uses mok_expert_down).  Arguments as mok_expert_down and mok_combine_slots
+ * (slot_of_assign: T x k, topk_gate: T x k, out: the tokens' output rows,
+ * H = desc->hidden wide; slot_end <= y_rows).  merge_plan: caller scratch of
+ * 16 * y_rows bytes (device), where a first launch writes, per slot, the
+ * output row's address and the gate, which the GEMM's epilogue reads. */
+mok_status mok_expert_down_merge(const mok_layer_desc* desc, const void* act,
+                                 const uint8_t* act_scales, int32_t act_rows,
+                                 const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                                 const void* w_down, void* y, int32_t y_rows,
+                                 const int32_t* assign_of_slot, const int32_t* slot_of_assign,
+                                 const float* topk_gate, const mok_tokens* out, void* merge_plan,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* mok_combine_slots for the tokens with at least two local slots only (the
+ * others are written by mok_expert_down_merge).  A single-slot token outside
+ * the out partitions still sets *dev_status = MOK_ERR_CAPACITY. */
+mok_status mok_combine_slots_multi(const void* y, int32_t y_rows, const int32_t* assign_of_slot,
+                                   const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                   const int32_t* slot_of_assign, const float* topk_gate,
+                                   int32_t k, int32_t H, const mok_tokens* out,
+                                   int32_t* dev_status, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Backward of the layer's share (the pages report the backward pass next to
  * the forward; the reverse of pull dispatch and push combine).  bf16

@@ -101,6 +101,21 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, None, None, 1, need, None) == E
     assert L.mok_expert_wgrad(C.byref(db), 1, 64, 1, 64, 1, 1, 64, 1, 1, 1, 1, need - 1, None) == \
         mok.MOK_ERR_WORKSPACE
+    # down GEMM merging single-slot tokens: routing arrays and out required
+    assert L.mok_expert_down_merge(C.byref(db), 1, None, 64, 1, 0, 64, 1, 1, 64, None, 1, 1,
+                                   C.byref(tok), 1, None, 0, None) == E
+    assert L.mok_expert_down_merge(C.byref(db), 1, None, 64, 1, 0, 64, 1, 1, 64, 1, 1, 1, None,
+                                   1, None, 0, None) == E
+    assert L.mok_expert_down_merge(C.byref(db), 1, None, 64, 1, 0, 64, 1, 1, 64, 1, 1, 1,
+                                   C.byref(tok), None, None, 0, None) == E   # no plan buffer
+    assert L.mok_expert_down_merge(C.byref(db), 1, None, 64, 1, 0, 65, 1, 1, 64, 1, 1, 1,
+                                   C.byref(tok), 1, None, 0, None) == E      # slot_end > y_rows
+    assert L.mok_expert_down_merge(C.byref(dmx), 1, None, 64, 1, 0, 64, 1, 1, 64, 1, 1, 1,
+                                   C.byref(tok), 1, None, 0, None) == E   # MXFP8 act, no scales
+    assert L.mok_combine_slots_multi(1, 4, 1, 1, 8, 4, 1, 1, 2, 60, C.byref(tok), None,
+                                     None) == E                        # H % 8
+    assert L.mok_combine_slots_multi(None, 4, 1, 1, 8, 4, 1, 1, 2, 64, C.byref(tok), None,
+                                     None) == E
     # tuner: no candidates, reps < 1, null result pointers
     d = _desc()
     one = (C.c_int32 * 1)(64)

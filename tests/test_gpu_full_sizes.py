@@ -101,7 +101,18 @@ def _check_pool_case(wl, tol):
         assert np.array_equal(colblk_scales(st.ring_sc, st.cap)[slots], xr[1])
     else:
         assert np.array_equal(ring, xr)
-    y_got = to_host(st.y[torch.as_tensor(slots, device="cuda")])
+    # the step's down GEMM merges single-slot tokens into their output rows and
+    # keeps y only for tokens with several local slots: y of every slot comes
+    # from the plain down GEMM on the same act, and the step's y rows equal it
+    import token_dispatch_grouped_top_amd as mok
+    y_all = torch.empty_like(st.y)
+    mok.mok_expert_down(st.desc, st.act, st.act_sc, st.cap, st.offsets, 0, st.cap, st.w_d, y_all,
+                        st.cap, st.gemm_ws)
+    n_loc = (sch["slot_of_assign"].reshape(wl.T, wl.k) >= 0).sum(1)
+    multi = np.nonzero(n_loc[sch["assign_of_slot"][:sch["R"]] // wl.k] >= 2)[0]
+    mt = torch.as_tensor(multi, device="cuda")
+    assert torch.equal(st.y[mt], y_all[mt])
+    y_got = to_host(y_all[torch.as_tensor(slots, device="cuda")])
     ys = check_y_rows(y_got, wl, xr, oracle.expert_of_slots(sch["offsets"], slots),
                       f"{wl.name} y")
     # merged rows on sampled tokens; untouched rows in full

@@ -103,6 +103,10 @@ _SIGS = {
                                    _P]),
     "mok_dispatch_backward": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _TOK, _P,
                                         _P]),
+    "mok_expert_down_merge": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P,
+                                        _P, _P, _TOK, _P, _P, _SZ, _P]),
+    "mok_combine_slots_multi": (C.c_int, [_P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _TOK,
+                                          _P, _P]),
     "mok_combine_backward_mx": (C.c_int, [_TOK, _P, _I32, _P, _P, _I32, _I32, _P, _I32, _I32,
                                           _P, _P, _I32, _P, _P, _P]),
     "mok_expert_gate_up_save_h_mx": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P,
@@ -457,6 +461,27 @@ def mok_dispatch_backward(dx_slots, rows: int, assign_of_slot, offsets, n_local:
     _check(_lib.mok_dispatch_backward(_ptr(dx_slots), rows, _ptr(assign_of_slot), _ptr(offsets),
                                       n_local, n_slots, _ptr(slot_of_assign), k, H, C.byref(dx.c),
                                       _ptr(dev_status), _stream(stream)), "mok_dispatch_backward")
+
+
+def mok_expert_down_merge(desc: mok_layer_desc, act, act_scales, act_rows: int, offsets,
+                          slot_begin: int, slot_end: int, w_down, y, y_rows: int, assign_of_slot,
+                          slot_of_assign, topk_gate, out: Tokens, merge_plan, ws=None,
+                          ws_bytes: Optional[int] = None, stream=None) -> None:
+    _check(_lib.mok_expert_down_merge(C.byref(desc), _ptr(act), _ptr(act_scales), act_rows,
+                                      _ptr(offsets), slot_begin, slot_end, _ptr(w_down), _ptr(y),
+                                      y_rows, _ptr(assign_of_slot), _ptr(slot_of_assign),
+                                      _ptr(topk_gate), C.byref(out.c), _ptr(merge_plan), _ptr(ws),
+                                      _ws_bytes(ws, ws_bytes), _stream(stream)),
+           "mok_expert_down_merge")
+
+
+def mok_combine_slots_multi(y, y_rows: int, assign_of_slot, offsets, n_local: int, n_slots: int,
+                            slot_of_assign, topk_gate, k: int, H: int, out: Tokens,
+                            dev_status=None, stream=None) -> None:
+    _check(_lib.mok_combine_slots_multi(_ptr(y), y_rows, _ptr(assign_of_slot), _ptr(offsets),
+                                        n_local, n_slots, _ptr(slot_of_assign), _ptr(topk_gate), k,
+                                        H, C.byref(out.c), _ptr(dev_status), _stream(stream)),
+           "mok_combine_slots_multi")
 
 
 def mok_combine_backward_mx(dout: Tokens, y, y_rows: int, assign_of_slot, offsets, n_local: int,

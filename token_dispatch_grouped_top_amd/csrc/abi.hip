@@ -100,7 +100,8 @@ struct Plan {
   int32_t n_ybuf;     // return areas (2 when macrobatches overlap)
   bool split;         // stream mode with the GEMMs' K split (workspace at off_split)
   size_t off_status, off_split, off_sched, off_route_idx, off_route_gate, off_counts, off_offsets,
-      off_soa, off_aos, off_win, off_ring, off_ring_sc, off_act, off_act_sc, off_y, off_pers, total;
+      off_soa, off_aos, off_win, off_ring, off_ring_sc, off_act, off_act_sc, off_y, off_plan,
+      off_pers, total;
   size_t per_macro_counts, per_macro_offsets, per_macro_soa, per_macro_aos, per_macro_win;
 };
 
@@ -155,6 +156,8 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.off_act = take(static_cast<size_t>(p.act_rows) * I * (mx ? 1 : 2));
   p.off_act_sc = take(mx ? static_cast<size_t>(p.act_rows) * (I / 32) : 0);
   p.off_y = take(static_cast<size_t>(p.n_ybuf) * p.cap * H * 2);
+  // merge plan of the down GEMM's epilogue (stream mode): 16 bytes per slot
+  p.off_plan = take(d->mode == MOK_MODE_STREAM ? static_cast<size_t>(p.cap) * 16 : 0);
   p.off_pers = take(persistent_ws_bytes(p.nwin * static_cast<int64_t>(n_macro)));
   p.total = o;
   return true;
@@ -465,6 +468,34 @@ mok_status mok_expert_down(const mok_layer_desc* desc, const void* act, const ui
   return hip_status(launch_down(a, stream));
 }
 
+mok_status mok_expert_down_merge(const mok_layer_desc* desc, const void* act,
+                                 const uint8_t* act_scales, int32_t act_rows,
+                                 const int32_t* offsets, int32_t slot_begin, int32_t slot_end,
+                                 const void* w_down, void* y, int32_t y_rows,
+                                 const int32_t* assign_of_slot, const int32_t* slot_of_assign,
+                                 const float* topk_gate, const mok_tokens* out, void* merge_plan,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!desc_ok(desc) || !act || act_rows < 1 || !offsets || slot_begin < 0 ||
+      slot_end < slot_begin || !w_down || !y || y_rows < 1 || !assign_of_slot ||
+      !slot_of_assign || !topk_gate || !tokens_ok(out, 0) || !merge_plan || slot_end > y_rows)
+    return MOK_ERR_INVALID_ARG;
+  if (desc->act_format == MOK_ACT_MXFP8_E4M3 && !act_scales) return MOK_ERR_INVALID_ARG;
+  if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
+  if (!gemm_operands_fit(desc, 0, act_rows)) return MOK_ERR_UNSUPPORTED;
+  FfnArgs a{};
+  if (mok_status st = gemm_split(desc, ws, ws_bytes, a.split)) return st;
+  a.offsets = offsets; a.n_local = desc->n_local; a.s_begin = slot_begin; a.s_end = slot_end;
+  a.w_d = static_cast<const uint16_t*>(w_down);
+  a.act = const_cast<void*>(act); a.act_scales = const_cast<uint8_t*>(act_scales);
+  a.act_rows = act_rows; a.y = y; a.y_rows = y_rows;
+  a.H = desc->hidden; a.I = desc->inter; a.act_format = desc->act_format;
+  a.w_packed = desc->weights_packed; a.weight_format = desc->weight_format;
+  a.merge.aos = assign_of_slot; a.merge.soa = slot_of_assign; a.merge.gate = topk_gate;
+  a.merge.k = desc->top_k; a.merge.out_parts = out->part_ptr; a.merge.n_part = out->n_partitions;
+  a.merge.part_rows = out->part_rows; a.merge.plan = merge_plan; a.merge.status = nullptr;
+  return hip_status(launch_down(a, stream));
+}
+
 mok_status mok_combine(const void* y, int32_t y_rows, const int32_t* slot_of_assign,
                        const float* topk_gate, int32_t T, int32_t k, int32_t H,
                        const mok_tokens* out, int32_t* dev_status, hipStream_t stream) {
@@ -488,6 +519,22 @@ mok_status mok_combine_slots(const void* y, int32_t y_rows, const int32_t* assig
                                          slot_of_assign, topk_gate, k, H, out->part_ptr,
                                          out->n_partitions, out->part_rows, dev_status, false,
                                          stream));
+}
+
+mok_status mok_combine_slots_multi(const void* y, int32_t y_rows, const int32_t* assign_of_slot,
+                                   const int32_t* offsets, int32_t n_local, int32_t n_slots,
+                                   const int32_t* slot_of_assign, const float* topk_gate,
+                                   int32_t k, int32_t H, const mok_tokens* out,
+                                   int32_t* dev_status, hipStream_t stream) {
+  if (k < 1 || k > 32 || H <= 0 || H % 8 != 0 || n_local < 1 || n_slots < 0 || !tokens_ok(out, 0))
+    return MOK_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!y || y_rows < 1 || !assign_of_slot || !offsets || !slot_of_assign ||
+                      !topk_gate))
+    return MOK_ERR_INVALID_ARG;
+  return hip_status(launch_combine_slots(y, y_rows, assign_of_slot, offsets, n_local, n_slots,
+                                         slot_of_assign, topk_gate, k, H, out->part_ptr,
+                                         out->n_partitions, out->part_rows, dev_status, false,
+                                         stream, true));
 }
 
 // ------------------------------------------------------------ backward
@@ -828,11 +875,17 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
       a.H = d.hidden; a.I = d.inter; a.act_format = d.act_format;
       a.w_packed = d.weights_packed; a.weight_format = d.weight_format;
       a.split = split;
+      // single-slot tokens merged in the down GEMM's epilogue; the rest below
+      a.merge.aos = mb[m].aos; a.merge.soa = mb[m].soa; a.merge.gate = mb[m].gate;
+      a.merge.k = d.top_k; a.merge.out_parts = mb[m].out.part_ptr;
+      a.merge.n_part = mb[m].out.n_partitions; a.merge.part_rows = mb[m].out.part_rows;
+      a.merge.plan = at<void>(ws, p.off_plan); a.merge.status = status;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
     err = launch_combine_slots(mb[m].y, p.cap, mb[m].aos, mb[m].offsets, d.n_local, p.cap,
                                mb[m].soa, mb[m].gate, d.top_k, d.hidden, mb[m].out.part_ptr,
-                               mb[m].out.n_partitions, mb[m].out.part_rows, status, true, stream);
+                               mb[m].out.n_partitions, mb[m].out.part_rows, status, true, stream,
+                               true);
     if (err != hipSuccess) return hip_status(err);
   }
   return MOK_OK;

@@ -49,7 +49,7 @@ using namespace gemm;
 template <bool A_MX, int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Geo<A_MX>::LDS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kernel_lds<Geo<A_MX>::LDS, EPI>()];
   TileJob j;
   if (!decode_job(p, p.K / Geo<A_MX>::BK, blockIdx.x, j)) return;
   gemm_tile<A_MX, EPI>(p, j, lds);
@@ -58,7 +58,7 @@ void k_ffn_gemm(const GemmParams p) {
 template <int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm_mx8(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[GeoMX8::LDS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kernel_lds<GeoMX8::LDS, EPI>()];
   TileJob j;
   if (!decode_job(p, p.K / GeoMX8::BK, blockIdx.x, j)) return;
   gemm_tile_mx8<EPI>(p, j, lds);
@@ -282,9 +282,21 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   g.w_packed = a.w_packed;
   set_split(g, a);
   const int n2 = (a.H + BN - 1) / BN;
+  const bool mx = a.act_format == MOK_ACT_MXFP8_E4M3;
+  if (a.merge.aos) {               // single-slot tokens merged in the epilogue
+    const hipError_t e = launch_merge_plan(a.merge.aos, a.offsets, a.n_local, a.s_begin, a.s_end,
+                                           a.merge.soa, a.merge.gate, a.merge.k, a.H,
+                                           a.merge.out_parts, a.merge.n_part, a.merge.part_rows,
+                                           a.merge.plan, s);
+    if (e != hipSuccess) return e;
+    g.m_plan = static_cast<const uint4*>(a.merge.plan); g.m_status = a.merge.status;
+    if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_DOWN_MERGE>(g, n2, m_tiles, s);
+    return mx ? launch_one<true, EPI_DOWN_MERGE>(g, n2, m_tiles, s)
+              : launch_one<false, EPI_DOWN_MERGE>(g, n2, m_tiles, s);
+  }
   if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_STORE_BF16>(g, n2, m_tiles, s);
-  return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
-                                             : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
+  return mx ? launch_one<true, EPI_STORE_BF16>(g, n2, m_tiles, s)
+            : launch_one<false, EPI_STORE_BF16>(g, n2, m_tiles, s);
 }
 
 // ------------------------------------------------------------ backward

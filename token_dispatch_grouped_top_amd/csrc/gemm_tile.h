@@ -25,6 +25,7 @@ __device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
 constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
 constexpr int kEpiLds = BM * BN * 2;           // epilogue staging: 256 x 256 bf16 / 256 x 128 fp32
+constexpr int kMergeLds = kEpiLds + BM * 12;   // EPI_DOWN_MERGE: + a destination and a gate per row
 
 // Pipeline shape per A-operand format.
 #ifndef MOK_BF16_BK
@@ -73,8 +74,17 @@ static_assert(Geo<false>::LDS <= 160 * 1024 && Geo<true>::LDS <= 160 * 1024, "LD
 // EPI_STORE_GU: a gate/up tile stores g and u themselves (h = [g, u], bf16
 // [c_rows][2 N] row-major) for that backward.  EPI_SWIGLU_BF16_H and
 // EPI_SWIGLU_MX_H: the forward's SwiGLU epilogues that also store h so.
+// EPI_DOWN_MERGE: the down GEMM's store with the merge of single-slot tokens
+// (a slot that is its token's only local slot goes to the token's output row
+// as bf16(gate * y); every other slot's y to C as EPI_STORE_BF16).
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_MX = 1, EPI_STORE_BF16 = 2, EPI_SWIGLU_BWD = 3,
-           EPI_STORE_GU = 4, EPI_SWIGLU_BF16_H = 5, EPI_SWIGLU_BWD_MX = 6, EPI_SWIGLU_MX_H = 7 };
+           EPI_STORE_GU = 4, EPI_SWIGLU_BF16_H = 5, EPI_SWIGLU_BWD_MX = 6, EPI_SWIGLU_MX_H = 7,
+           EPI_DOWN_MERGE = 8 };
+// LDS of a GEMM kernel: the pipeline's (with the usual epilogue's), or the
+// merging epilogue's if larger.
+template <int LOOP, int EPI> constexpr int kernel_lds() {
+  return EPI == EPI_DOWN_MERGE && kMergeLds > LOOP ? kMergeLds : LOOP;
+}
 // Whether an epilogue pairs gate and up columns (the gate/up weight order).
 template <int EPI> constexpr bool epi_swiglu() {
   return EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MX || EPI == EPI_STORE_GU ||
@@ -102,6 +112,10 @@ struct GemmParams {
   int32_t c_row_base;         // C row of slot s: (s + c_row_base) % c_rows
   const uint16_t* H_src;      // EPI_SWIGLU_BWD: h = [g, u] bf16 [c_rows][2 N], row-major
   uint16_t* H_out;            // EPI_SWIGLU_BF16_H: h = [g, u] bf16 [c_rows][2 N], row-major
+  // EPI_DOWN_MERGE: per slot s, m_plan[s] = {output row address (lo, hi), gate
+  // bits, 0}, address 0 for a slot whose y goes to C (launch_merge_plan)
+  const uint4* m_plan;
+  const int32_t* m_status;    // non-null: a raised status word stops the output stores
   // Split of the last, partial round of tiles along K (standalone launches):
   float* part;                // [n_cus][BM * BN] fp32 partial tiles; null = no split
   int32_t* part_cnt;          // [n_cus] arrival counters, zero before and after a launch
@@ -248,12 +262,26 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 }
 
 // After the main loop (LDS free, every load landed): the K-split exchange of
+// EPI_DOWN_MERGE: row tid's plan record (slot row0 + tid), loaded at the
+// start of the tile so that it lands under the main loop.  The records are
+// contiguous by slot (a wave's 64 rows are 1 KiB); looking the token up in
+// the epilogue instead (assign_of_slot, then k slot_of_assign entries and the
+// gate, scattered by token, again in each of a row block's column tiles) added
+// about 15 % to the down GEMM's L2 requests, which bound it.
+struct MergeRow {
+  uint4 rec;
+};
+__device__ __forceinline__ void merge_row_load(const GemmParams& p, int row0, int nrows, MergeRow& m) {
+  m.rec = threadIdx.x < nrows ? p.m_plan[row0 + threadIdx.x] : make_uint4(0, 0, 0, 0);
+}
+
 // a piece and the epilogue.  acc holds the wave's 128 x 128 block: element q of
 // tile (mi, ni) is token row 32 mi + lane % 32, output column 32 ni + 8 (q / 4)
 // + 4 (lane / 32) + q % 4.  Shared by every operand format.
 template <int EPI>
 __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& job,
-                                            f32x16_t (&acc)[4][4], uint8_t* __restrict__ lds) {
+                                            f32x16_t (&acc)[4][4], uint8_t* __restrict__ lds,
+                                            const MergeRow& mr) {
   const int row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
@@ -451,7 +479,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
         }
       }
     }
-  } else if (EPI == EPI_STORE_BF16) {
+  } else if (EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE) {
     constexpr int RB = BN * 2;                             // bytes per staged row
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -468,14 +496,43 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
           *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
         }
     }
+    // EPI_DOWN_MERGE: where each row goes, one thread per row.  A slot that is
+    // its token's only local slot (its plan record holds the token's output row)
+    // goes there as bf16(fma(g, y, 0)) of the bf16 y: the slot-driven merge's
+    // value for a single term, bit for bit.  Every other slot (and every slot
+    // once m_status is raised) stores y in C.
+    uint16_t** m_dst = reinterpret_cast<uint16_t**>(lds + kEpiLds);
+    float* m_g = reinterpret_cast<float*>(lds + kEpiLds + BM * 8);
+    if constexpr (EPI == EPI_DOWN_MERGE) {
+      if (tid < nrows) {
+        const bool go = p.m_status == nullptr || *p.m_status == 0;
+        const uint64_t addr = static_cast<uint64_t>(mr.rec.x) | (static_cast<uint64_t>(mr.rec.y) << 32);
+        m_dst[tid] = go ? reinterpret_cast<uint16_t*>(addr) : nullptr;
+        m_g[tid] = __uint_as_float(mr.rec.z);
+      }
+    }
     __syncthreads();
     uint16_t* C = static_cast<uint16_t*>(p.C);
     const int k = tid % (BN / 8), col = n0 + k * 8;         // fixed 16-byte column per thread
     if (col < p.N) {
       for (int r = tid / (BN / 8); r < nrows; r += kThreads / (BN / 8)) {
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+        if constexpr (EPI == EPI_DOWN_MERGE) {
+          uint16_t* d = m_dst[r];
+          if (d != nullptr) {
+            const float g = m_g[r];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              o[q] = pack_bf16x2(fmaf(g, __uint_as_float(w[q] << 16), 0.0f),
+                                 fmaf(g, __uint_as_float(w[q] & 0xffff0000u), 0.0f));
+            *reinterpret_cast<uint4*>(d + col) = make_uint4(o[0], o[1], o[2], o[3]);
+            continue;
+          }
+        }
         const int64_t crow = c_row_of(r);
-        *reinterpret_cast<uint4*>(C + crow * p.N + col) =
-            *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+        *reinterpret_cast<uint4*>(C + crow * p.N + col) = v;
       }
     }
   } else {
@@ -778,6 +835,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   // keeps the per-thread load count -- and so the vmcnt bookkeeping -- the
   // same in every step.
   constexpr int LW = G::NLOAD_B, LA = G::NLOAD_A + (A_MX ? 1 : 0), LPS = LW + LA;
+  // EPI_DOWN_MERGE: the plan record of this thread's row is loaded before the
+  // prologue's loads (it only makes the first waits below stricter)
+  MergeRow mr;
+  if constexpr (EPI == EPI_DOWN_MERGE) merge_row_load(p, job.row0, job.nrows, mr);
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0) {
     const int ks0 = s0 < nk ? s0 : nk - 1;
@@ -879,7 +940,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();                                           // LDS is reused by the epilogue
 
-  tile_finish<EPI>(p, job, acc, lds);
+  tile_finish<EPI>(p, job, acc, lds, mr);
 }
 
 // A whole tile (all k-steps).

@@ -178,6 +178,8 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   // half of stage kt+NS and runs the MFMAs of row groups 2, 3.  The loop is
   // unrolled by two so the register sets alternate at compile time.
   constexpr int LW = G::NLOAD + 1, LA = G::NLOAD + 1, LPS = LW + LA;
+  MergeRow mr;                                               // EPI_DOWN_MERGE, as gemm_tile
+  if constexpr (EPI == EPI_DOWN_MERGE) merge_row_load(p, job.row0, job.nrows, mr);
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0) {
     const int ks0 = s0 < nk ? s0 : nk - 1;
@@ -239,7 +241,7 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #undef MX8_ISSUE_W
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();
-  tile_finish<EPI>(p, job, acc, lds);
+  tile_finish<EPI>(p, job, acc, lds, mr);
 }
 
 // A whole tile (all k-steps).

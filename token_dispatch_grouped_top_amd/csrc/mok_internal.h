@@ -185,7 +185,8 @@ hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* ao
                                 const int32_t* offsets, int32_t n_local, int32_t n_slots,
                                 const int32_t* soa, const float* gate, int32_t k, int32_t H,
                                 void* const* out_ptr, int32_t n_part, int32_t part_rows,
-                                int32_t* status, bool abort_on_status, hipStream_t s);
+                                int32_t* status, bool abort_on_status, hipStream_t s,
+                                bool multi_only = false);
 
 // Workspace of the K split of the GEMMs' last, partial round of tiles:
 // [n_cus arrival counters, padded to 256 bytes][n_cus fp32 partial tiles of
@@ -199,6 +200,19 @@ size_t split_ws_bytes(int32_t n_cus);
 SplitWs split_ws_carve(void* ws, int32_t n_cus);
 
 // Grouped GEMM pair of the expert FFN over slots [s_begin, min(s_end, R)).
+// The merge of single-slot tokens in the down GEMM's epilogue (aos null: none):
+// launch_merge_plan writes a 16-byte record per slot into plan (y_rows of them),
+// which the epilogue reads.
+struct MergeArgs {
+  const int32_t* aos; const int32_t* soa; const float* gate; int32_t k;
+  void* const* out_parts; int32_t n_part, part_rows;
+  void* plan;
+  const int32_t* status;      // non-null: no output row is written once it is raised
+};
+hipError_t launch_merge_plan(const int32_t* aos, const int32_t* offsets, int32_t n_local,
+                             int32_t s0, int32_t s1, const int32_t* soa, const float* gate,
+                             int32_t k, int32_t H, void* const* out_parts, int32_t n_part,
+                             int32_t part_rows, void* plan, hipStream_t s);
 struct FfnArgs {
   const void* ring; const uint8_t* ring_scales; int32_t ring_slots;
   const int32_t* offsets; int32_t n_local; int32_t s_begin, s_end;
@@ -209,7 +223,8 @@ struct FfnArgs {
   int32_t w_packed;           // weights in the packed tile order (launch_pack_weights)
   int32_t weight_format;      // MOK_W_MXFP8_E4M3: packed MXFP8 weights, both GEMMs in MXFP8
   SplitWs split;              // split.part null: every tile whole
-  void* h_out;                // non-null (bf16 only): the gate/up also stores h = [g, u]
+  void* h_out;                // non-null (bf16 weights): the gate/up also stores h = [g, u]
+  MergeArgs merge;            // down: single-slot tokens straight to their output rows
 };
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);

@@ -91,14 +91,14 @@ void k_combine_slots(const uint16_t* __restrict__ y, int32_t y_rows,
                      int32_t n_local, int32_t n_slots, const int32_t* __restrict__ soa,
                      const float* __restrict__ gate, int32_t k, int32_t H,
                      void* const* __restrict__ out_parts, int32_t n_part, int32_t part_rows,
-                     int32_t* status, bool abort_on_status) {
+                     int32_t* status, bool abort_on_status, bool multi_only) {
   const int64_t s = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
   if (s >= n_slots) return;
   const int32_t a = aos[s];                 // issued together with R (aos holds n_slots entries)
   const int32_t R = offsets[n_local];
   if (s >= R) return;
   if (abort_on_status && *status != 0) return;
-  merge_slot(y, y_rows, a, soa, gate, s, k, H, out_parts, n_part, part_rows, status);
+  merge_slot(y, y_rows, a, soa, gate, s, k, H, out_parts, n_part, part_rows, status, multi_only);
 }
 
 // One wave per routed slot s < min(R, n_slots): the backward of the merge.
@@ -122,7 +122,48 @@ void k_unmerge_slots(void* const* __restrict__ dout_parts, int32_t n_part, int32
                  status);
 }
 
+// Merge plan of the slots [s0, min(s1, R)): plan[s] = {address of token t's
+// output row (lo, hi), gate bits, 0} when s is the only local slot of its
+// token t (exactly one slot_of_assign[t][j] >= 0) and t lies in the output
+// partitions, else zeros.  One thread per slot; read by the down GEMM's
+// merging epilogue.
+__global__ __launch_bounds__(256)
+void k_merge_plan(const int32_t* __restrict__ aos, const int32_t* __restrict__ offsets,
+                  int32_t n_local, int32_t s0, int32_t s1, const int32_t* __restrict__ soa,
+                  const float* __restrict__ gate, int32_t k, int32_t H,
+                  void* const* __restrict__ out_parts, int32_t n_part, int32_t part_rows,
+                  uint4* __restrict__ plan) {
+  const int64_t s = s0 + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int32_t R = offsets[n_local];
+  if (s >= s1 || s >= R) return;
+  const int32_t a = aos[s];
+  const int64_t t = a / k;
+  int live = 0;
+  for (int j = 0; j < k; ++j) live += soa[t * k + j] >= 0 ? 1 : 0;
+  uint4 rec = make_uint4(0, 0, 0, 0);
+  const int64_t part = t / part_rows;
+  if (live == 1 && part < n_part) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<uint16_t*>(out_parts[part]) +
+                                                     (t % part_rows) * static_cast<int64_t>(H));
+    rec = make_uint4(static_cast<uint32_t>(addr), static_cast<uint32_t>(addr >> 32),
+                     __float_as_uint(gate[a]), 0u);
+  }
+  plan[s] = rec;
+}
+
 }  // namespace
+
+hipError_t launch_merge_plan(const int32_t* aos, const int32_t* offsets, int32_t n_local,
+                             int32_t s0, int32_t s1, const int32_t* soa, const float* gate,
+                             int32_t k, int32_t H, void* const* out_parts, int32_t n_part,
+                             int32_t part_rows, void* plan, hipStream_t s) {
+  if (s1 <= s0) return hipSuccess;
+  const int64_t n = static_cast<int64_t>(s1) - s0;
+  hipLaunchKernelGGL(k_merge_plan, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     aos, offsets, n_local, s0, s1, soa, gate, k, H, out_parts, n_part, part_rows,
+                     static_cast<uint4*>(plan));
+  return hipGetLastError();
+}
 
 hipError_t launch_unmerge_slots(void* const* dout_ptr, int32_t n_part, int32_t part_rows,
                                 const void* y, int32_t y_rows, const int32_t* aos,
@@ -177,13 +218,14 @@ hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* ao
                                 const int32_t* offsets, int32_t n_local, int32_t n_slots,
                                 const int32_t* soa, const float* gate, int32_t k, int32_t H,
                                 void* const* out_ptr, int32_t n_part, int32_t part_rows,
-                                int32_t* status, bool abort_on_status, hipStream_t s) {
+                                int32_t* status, bool abort_on_status, hipStream_t s,
+                                bool multi_only) {
   if (n_slots <= 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((static_cast<int64_t>(n_slots) + kRowsPerBlock - 1) / kRowsPerBlock));
   hipLaunchKernelGGL(k_combine_slots, grid, dim3(kRowsPerBlock * kWave), 0, s,
                      static_cast<const uint16_t*>(y), y_rows, aos, offsets, n_local, n_slots, soa,
                      gate, k, H, out_ptr, n_part, part_rows, status,
-                     abort_on_status && status != nullptr);
+                     abort_on_status && status != nullptr, multi_only);
   return hipGetLastError();
 }
 

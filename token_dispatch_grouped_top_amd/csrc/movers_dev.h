@@ -361,23 +361,31 @@ __device__ __forceinline__ void unmerge_slot_mx(void* const* __restrict__ dout_p
 // when s is t's smallest local slot, so every token with a local assignment is
 // merged exactly once while only the R routed slots (not all pool tokens) are
 // visited.  All 64 lanes must call it.
-// a_s = assign_of_slot[s] (the caller loads it early).
+// a_s = assign_of_slot[s] (the caller loads it early).  multi_only: tokens
+// with a single local slot are skipped (the down GEMM's merging epilogue has
+// written them); an index outside the partitions still raises the status.
 template <bool kFast = true>
 __device__ __forceinline__ void merge_slot(const uint16_t* __restrict__ y, int32_t y_rows,
                                            int32_t a_s, const int32_t* __restrict__ soa,
                                            const float* __restrict__ gate, int64_t s, int32_t k,
                                            int32_t H, void* const* __restrict__ out_parts,
-                                           int32_t n_part, int32_t part_rows, int32_t* status) {
+                                           int32_t n_part, int32_t part_rows, int32_t* status,
+                                           bool multi_only = false) {
   const int lane = lane_id();
   const int64_t t = a_s / k;
   int32_t mine = 0x7fffffff;
+  bool local = false;
   if (lane < k) {
     const int32_t v = soa[t * k + lane];
-    if (v >= 0) mine = v;
+    if (v >= 0) { mine = v; local = true; }
   }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) mine = min(mine, __shfl_xor(mine, off));
   if (mine != s) return;
+  if (multi_only && __popcll(__ballot(local)) == 1) {
+    if (lane == 0 && t / part_rows >= n_part) set_status(status, MOK_ERR_CAPACITY);
+    return;
+  }
   combine_token<kFast>(y, y_rows, soa, gate, t, k, H, out_parts, n_part, part_rows, status);
 }
 
