@@ -66,7 +66,7 @@ __device__ __forceinline__ void gather_pair_bf16(void* const* __restrict__ parts
       const int p = p0 + u * kWave + lane;
       int sel, v;
       pair_piece<4>(p, sel, v);
-      if (p < npc) buf[u] = (sel ? src2 : src1)[v];
+      if (p < npc) buf[u] = ld_nt((sel ? src2 : src1) + v);
     }
 #pragma unroll
     for (int u = 0; u < kPairBatch; ++u) {
@@ -102,7 +102,7 @@ __device__ __forceinline__ void gather_pair_mxfp8(void* const* __restrict__ part
       const int p = p0 + u * kWave + lane;
       int sel, v;
       pair_piece<8>(p, sel, v);
-      if (p < npc) buf[u] = (sel ? src2 : src1)[v];
+      if (p < npc) buf[u] = ld_nt((sel ? src2 : src1) + v);
     }
 #pragma unroll
     for (int u = 0; u < kPairBatch; ++u) {
