@@ -111,14 +111,15 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   // A stage's loads in two halves (as in gemm_tile.h): weights (codes +
   // scales) and tokens (codes + scales); the 2-byte scale loads land in
   // 4-byte slots, lane i at slot base + 4 i, i.e. row tid at 4 tid.
+// Weights with the non-temporal policy (aux bit 1), as the bf16 tile's.
 #define MX8_ISSUE_W(kt, buf)                                                                 \
   do {                                                                                       \
     uint8_t* Bs_ = tileB(buf);                                                               \
     _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, \
-                                               boff[j], static_cast<uint32_t>(kt) * G::WBLOCK, 0, 0); \
+                                               boff[j], static_cast<uint32_t>(kt) * G::WBLOCK, 0, 2); \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(tileSB(buf) + wave * 256), 2,   \
-                                             G::TILE + 2 * tid, static_cast<uint32_t>(kt) * G::WBLOCK, 0, 0); \
+                                             G::TILE + 2 * tid, static_cast<uint32_t>(kt) * G::WBLOCK, 0, 2); \
   } while (0)
 #define MX8_ISSUE_A(kt, buf)                                                                 \
   do {                                                                                       \
