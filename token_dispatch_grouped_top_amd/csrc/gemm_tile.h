@@ -527,7 +527,8 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
             for (int q = 0; q < 4; ++q)
               o[q] = pack_bf16x2(fmaf(g, __uint_as_float(w[q] << 16), 0.0f),
                                  fmaf(g, __uint_as_float(w[q] & 0xffff0000u), 0.0f));
-            *reinterpret_cast<uint4*>(d + col) = make_uint4(o[0], o[1], o[2], o[3]);
+            // the token's row is read by no later kernel of the layer: streaming store
+            st_nt(reinterpret_cast<uint4*>(d + col), make_uint4(o[0], o[1], o[2], o[3]));
             continue;
           }
         }
