@@ -156,8 +156,8 @@ bool make_plan(const mok_layer_desc* d, int32_t T, int32_t n_macro, Plan& p) {
   p.off_act = take(static_cast<size_t>(p.act_rows) * I * (mx ? 1 : 2));
   p.off_act_sc = take(mx ? static_cast<size_t>(p.act_rows) * (I / 32) : 0);
   p.off_y = take(static_cast<size_t>(p.n_ybuf) * p.cap * H * 2);
-  // merge plan of the down GEMM's epilogue (stream mode): 16 bytes per slot
-  p.off_plan = take(d->mode == MOK_MODE_STREAM ? static_cast<size_t>(p.cap) * 16 : 0);
+  // merge plans of the down GEMM's epilogue: 16 bytes per slot and macrobatch
+  p.off_plan = take(static_cast<size_t>(n_macro) * p.cap * 16);
   p.off_pers = take(persistent_ws_bytes(p.nwin * static_cast<int64_t>(n_macro)));
   p.total = o;
   return true;
@@ -819,6 +819,7 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
     mb[m].gate = route_here ? route_gate : topk_gate[m];
     mb[m].y = at<uint16_t>(ws, p.off_y + static_cast<size_t>(m % p.n_ybuf) * p.cap * d.hidden * 2);
     mb[m].out = out[m];
+    mb[m].plan = at<void>(ws, p.off_plan + static_cast<size_t>(m) * p.cap * 16);
   }
   // Route (logits form), schedule, windows and capacity check for every
   // macrobatch first: two launches each, reading only routing.
@@ -879,7 +880,7 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
       a.merge.aos = mb[m].aos; a.merge.soa = mb[m].soa; a.merge.gate = mb[m].gate;
       a.merge.k = d.top_k; a.merge.out_parts = mb[m].out.part_ptr;
       a.merge.n_part = mb[m].out.n_partitions; a.merge.part_rows = mb[m].out.part_rows;
-      a.merge.plan = at<void>(ws, p.off_plan); a.merge.status = status;
+      a.merge.plan = mb[m].plan; a.merge.status = status;
       if ((err = launch_ffn(a, stream)) != hipSuccess) return hip_status(err);
     }
     err = launch_combine_slots(mb[m].y, p.cap, mb[m].aos, mb[m].offsets, d.n_local, p.cap,

@@ -15,6 +15,7 @@ struct MacroBuffers {
   const float* gate;  // topk_gate [T*k]
   uint16_t* y;        // return area bf16 [cap][H], indexed by slot
   mok_tokens out;     // destination partitions
+  void* plan;         // merge plan of the down GEMM's epilogue: 16 bytes per slot [cap]
 };
 
 struct PersistentArgs {

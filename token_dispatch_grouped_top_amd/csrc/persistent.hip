@@ -63,6 +63,7 @@ struct PMacro {
   uint16_t* y;
   void* const* out_parts;
   int32_t out_n_part, out_part_rows;
+  uint4* plan;              // merge plan of the down tiles' epilogue [cap]
 };
 
 struct PKArgs {
@@ -333,9 +334,9 @@ __device__ __forceinline__ bool merge_macro(const PKArgs& a, const CtlView& c, i
     if (c.win_m()[w] == m && !wait_geq(&c.dn_done()[w], xcds_of(c.win_nt2()[w]), c, a, sh)) return false;
   const PMacro pm = c.pm()[m];
   const int32_t R = pm.offsets[a.n_local];
-  for (int64_t s = first; s < R; s += step)
+  for (int64_t s = first; s < R; s += step)             // single-slot tokens: by the down tiles
     merge_slot<kFast>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
-                      pm.out_n_part, pm.out_part_rows, a.status);
+                      pm.out_n_part, pm.out_part_rows, a.status, true);
   return true;
 }
 
@@ -463,10 +464,11 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
       g.N = a.H; g.I = 0;
       g.C = uniform_ptr(pm.y); g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
       g.n_tiles = n2; g.w_packed = a.w_packed;
+      g.m_plan = uniform_ptr(pm.plan); g.m_status = a.status;     // single-slot tokens merged here
       if constexpr (F == kPMx8)
-        gemm_tile_mx8<EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
+        gemm_tile_mx8<EPI_DOWN_MERGE>(g, e, row0, nrows, ntile, lds);
       else
-        gemm_tile<F == kPMxAct, EPI_STORE_BF16>(g, e, row0, nrows, ntile, lds);
+        gemm_tile<F == kPMxAct, EPI_DOWN_MERGE>(g, e, row0, nrows, ntile, lds);
       signal_tile(xcnt, xshare, &c.dn_done()[w]);
     }
   }
@@ -477,7 +479,8 @@ __global__ __launch_bounds__(256)
 void k_persist(const PKArgs a) {
   constexpr bool A_MX = F != kPBf16;
   constexpr int kLds0 = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
-  constexpr int kLds = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
+  constexpr int kLds1 = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
+  constexpr int kLds = kLds1 > kMergeLds ? kLds1 : kMergeLds;     // the merging down epilogue
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   // The broadcast words share the first 16 bytes of the GEMM's LDS: every
   // use is fenced by workgroup barriers from the tile that overwrites them
@@ -493,6 +496,31 @@ void k_persist(const PKArgs a) {
 }
 
 }  // namespace
+
+// Merge plans of the group's macrobatches (launch_merge_plan's records, one
+// launch for all of them): blockIdx.y = macrobatch.  Slots s < min(R, cap):
+// a plan holds cap records (with R > cap the launch computes nothing and
+// raises the capacity status; records past cap would overwrite the next
+// workspace region, the control block).
+__global__ __launch_bounds__(256)
+void k_merge_plans(const PKArgs a) {
+  const PMacro pm = a.mb[blockIdx.y];
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (s >= pm.offsets[a.n_local] || s >= a.cap) return;
+  const int32_t asg = pm.aos[s];
+  const int64_t t = asg / a.k;
+  int live = 0;
+  for (int j = 0; j < a.k; ++j) live += pm.soa[t * a.k + j] >= 0 ? 1 : 0;
+  uint4 rec = make_uint4(0, 0, 0, 0);
+  const int64_t part = t / pm.out_part_rows;
+  if (live == 1 && part < pm.out_n_part) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<uint16_t*>(pm.out_parts[part]) +
+                                                     (t % pm.out_part_rows) * static_cast<int64_t>(a.H));
+    rec = make_uint4(static_cast<uint32_t>(addr), static_cast<uint32_t>(addr >> 32),
+                     __float_as_uint(pm.gate[asg]), 0u);
+  }
+  pm.plan[s] = rec;
+}
 
 size_t persistent_ws_bytes(int64_t total_windows) {
   int W = static_cast<int>(total_windows > 0 ? total_windows : 1);
@@ -522,7 +550,7 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     for (int m = 0; m < gn; ++m) {
       const MacroBuffers& b = a.mb[g0 + m];
       k.mb[m] = PMacro{b.offsets, b.aos, b.soa, b.gate, b.y, b.out.part_ptr, b.out.n_partitions,
-                       b.out.part_rows};
+                       b.out.part_rows, static_cast<uint4*>(b.plan)};
     }
     k.n_macro = gn; k.T = a.T; k.k = a.k; k.H = a.H; k.I = a.I; k.n_local = a.n_local;
     k.act_format = a.act_format; k.M = a.M; k.S = a.S; k.cap = a.cap; k.n_move = n_move;
@@ -537,6 +565,8 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
                        dim3(256), 0, s, k.ctl, words);
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(256),
                        plan_lds_words(gn, a.n_local, k.max_win) * sizeof(int32_t), s, k);
+    hipLaunchKernelGGL(k_merge_plans, dim3(static_cast<unsigned>((a.cap + 255) / 256),
+                                           static_cast<unsigned>(gn)), dim3(256), 0, s, k);
     if (hipGetLastError() != hipSuccess) return MOK_ERR_HIP;
     // window 0 of the group: the first macrobatch's slots [0, M) into ring half 0
     const MacroBuffers& b0 = a.mb[g0];
@@ -551,7 +581,7 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     const MacroBuffers& bl = a.mb[g0 + gn - 1];
     if (launch_combine_slots(bl.y, a.cap, bl.aos, bl.offsets, a.n_local, a.cap, bl.soa, bl.gate,
                              a.k, a.H, bl.out.part_ptr, bl.out.n_partitions, bl.out.part_rows,
-                             a.status, true, s) != hipSuccess)
+                             a.status, true, s, true) != hipSuccess)
       return MOK_ERR_HIP;
   }
   return MOK_OK;
