@@ -26,7 +26,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_harness import (SENTINEL, DeviceWorkload, check_layer_out, check_y_rows, colblk_rows,
-                         colblk_scales, to_host)
+                         colblk_scales, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -256,3 +256,122 @@ def test_streaming_macrobatches():
     toks = _sample_tokens(sch["slot_of_assign"], wl7.k, rng, n=24)
     r = oracle.forward(wl7, tokens=toks)
     check_layer_out(d0.out_rows(outs[7], toks), wl7, r, "streaming out m7")
+
+
+def test_kimi_share_backward_full_size():
+    """The backward at the bench's size (Kimi-shaped share, R = 8192, H = 7168,
+    I = 2048), every step through the C ABI as bench.py times it (merge backward,
+    the FFN backward with h recomputed, the dispatch backward, the weight
+    gradients), checked with the bars of tests/bars.py against the oracle's
+    per-row backward: every slot of one local expert (dy, dgate, dh's effect
+    through dx_s, and all of that expert's dW_d and dW_gu), and dx of sampled
+    tokens (all their local slots).  dout: seeded N(0, 1) bf16 rows for every
+    token with a local pick."""
+    import token_dispatch_grouped_top_amd as mok
+    import bars
+    wl = W.kimi_share()
+    dw, st = _run_bench_step(wl)
+    H, I, k, cap = wl.H, wl.I, wl.k, st.cap
+    sch = oracle.build_schedule(wl.topk_idx, wl.expert_base, wl.n_local)
+    R, aos, soa = int(sch["R"]), sch["assign_of_slot"][:sch["R"]], sch["slot_of_assign"]
+    t_of = aos // k
+    # the forward's y of every slot (the step's down GEMM keeps y only for tokens
+    # with several local slots)
+    y_all = torch.empty_like(st.y)
+    mok.mok_expert_down(st.desc, st.act, None, cap, st.offsets, 0, cap, st.w_d, y_all, cap,
+                        st.gemm_ws)
+    # dout: rows of the tokens with a local pick
+    routed = np.unique(t_of)
+    drows = W.normal_bf16(np.random.SeedSequence(4242), routed.size * H, 1.0).reshape(-1, H)
+    dout_np = np.zeros((wl.T, H), np.uint16)
+    dout_np[routed] = drows
+    dout = mok.Tokens([to_dev(dout_np[p * wl.part_rows:(p + 1) * wl.part_rows])
+                       for p in range(wl.n_partitions)], wl.part_rows)
+    d = dw.desc(max_rows=cap, weights_packed=1)
+    gu_b, d_b = mok.mok_packed_weights_bwd_size(d)
+    gu_t = torch.empty(gu_b, dtype=torch.uint8, device="cuda")
+    d_t = torch.empty(d_b, dtype=torch.uint8, device="cuda")
+    mok.mok_pack_weights_bwd(d, dw.w_gu, dw.w_d, gu_t, d_t)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dy = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    dgate = torch.full((wl.T, k), float("nan"), dtype=torch.float32, device="cuda")
+    h = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
+    dh = torch.empty((cap, 2 * I), dtype=torch.int16, device="cuda")
+    dxs = torch.empty((cap, H), dtype=torch.int16, device="cuda")
+    mok.mok_combine_backward(dout, y_all, cap, st.aos, st.offsets, wl.n_local, cap, dw.topk_gate,
+                             k, H, dy, cap, dgate, status)
+    mok.mok_expert_ffn_backward(d, st.ring, cap, dy, st.offsets, 0, cap, st.w_gu, gu_t, d_t, h, dh,
+                                dxs, cap)
+    dx = dw.new_out()
+    mok.mok_dispatch_backward(dxs, cap, st.aos, st.offsets, wl.n_local, cap, st.soa, k, H, dx,
+                              status)
+    wws = torch.empty(mok.mok_wgrad_workspace_size(d, cap), dtype=torch.uint8, device="cuda")
+    dwgu = torch.empty((wl.n_local, 2 * I, H), dtype=torch.int16, device="cuda")
+    dwd = torch.empty((wl.n_local, H, I), dtype=torch.int16, device="cuda")
+    mok.mok_expert_wgrad(d, st.ring, cap, st.act, cap, dy, dh, cap, st.offsets, dwgu, dwd, wws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    wgu_v, wd_v = bars.bf16_values(wl.w_gu), bars.bf16_values(wl.w_d)
+    gates = wl.topk_gate.astype(np.float64).reshape(-1)
+    dv = bars.bf16_values(dout_np)
+    # ---- one expert, all its slots
+    e0 = 3
+    lo, hi = int(sch["offsets"][e0]), int(sch["offsets"][e0 + 1])
+    rows = np.arange(lo, hi)
+    xr = oracle.gather_rows(wl.x, k, sch["assign_of_slot"], rows, False)
+    xv = bars.bf16_values(xr)
+    eor = np.full(rows.size, e0, np.int32)
+    dy_ref = gates[aos[rows]][:, None] * dv[t_of[rows]]
+    dy_got = bars.bf16_values(colblk_rows(dy, cap)[rows])
+    assert np.all(np.abs(dy_got - dy_ref) <= 2.0 ** -8 * np.abs(dy_ref) + 1e-30)
+    _, a_ex, y_ex = oracle.ffn_rows(xr, eor, wl.w_gu, wl.w_d, False, exact=True)
+    y_lo, y_hi, _ = bars.ffn_y_band(xv, eor, wgu_v, wd_v, a_ex, y_ex)
+    g_lo, g_hi = bars.dgate_band(dv[t_of[rows]], y_lo, y_hi)
+    g_got = to_host(dgate).reshape(-1)[aos[rows]].astype(np.float64)
+    assert np.all((g_got >= g_lo) & (g_got <= g_hi)), int(((g_got < g_lo) | (g_got > g_hi)).sum())
+    dh_ref, dxs_ref = oracle.ffn_backward_values(xv, eor, wgu_v, wd_v, dy_ref)
+    hh = np.zeros((rows.size, 2 * I))
+    hh[:] = xv @ wgu_v[e0].T
+    s_dh, s_dxs = bars.ffn_backward_sigma(xv, eor, wgu_v, wd_v, dy_ref, hh, dh_ref)
+    dxs_got = bars.bf16_values(to_host(dxs)[rows])
+    bar = bars.C_SIGMA * np.sqrt(s_dxs ** 2 + (bars.RHO16 * dxs_ref) ** 2) + 1e-30
+    assert np.all(np.abs(dxs_got - dxs_ref) <= bar), float(np.max(np.abs(dxs_got - dxs_ref) / bar))
+    a_ref = oracle.silu_and_grad(hh[:, :I])[0] * hh[:, I:]
+    dwg_ref = dh_ref.T @ xv
+    dwd_ref = dy_ref.T @ a_ref
+    bd, bg = bars.wgrad_bars(np.zeros(rows.size, np.int64), 1, xv, a_ref, dy_ref, dh_ref, s_dh,
+                             dwd_ref[None], dwg_ref[None])
+    for name, got, ref, b in (("dW_d", to_host(dwd[e0]), dwd_ref, bd[0]),
+                              ("dW_gu", to_host(dwgu[e0]), dwg_ref, bg[0])):
+        gv = bars.bf16_values(got)
+        assert np.all(np.abs(gv - ref) <= b), (name, float(np.max(np.abs(gv - ref) / b)))
+        print(f"[parity] full-size backward {name}[{e0}]: max|d|/bar = "
+              f"{float(np.max(np.abs(gv - ref) / b)):.3f}, median bar / |ref| = "
+              f"{float(np.median(b / (np.abs(ref) + 1e-30))):.3g}", flush=True)
+    # ---- dx of sampled tokens: all their local slots
+    rng = np.random.default_rng(77)
+    n_loc = (soa.reshape(wl.T, k) >= 0).sum(1)
+    multi = np.nonzero(n_loc >= 2)[0]
+    toks = np.unique(np.concatenate([rng.choice(routed, size=16, replace=False),
+                                     rng.choice(multi, size=8, replace=False)]))
+    srows = np.nonzero(np.isin(t_of, toks))[0]
+    xs = oracle.gather_rows(wl.x, k, sch["assign_of_slot"], srows, False)
+    xsv = bars.bf16_values(xs)
+    es = oracle.expert_of_slots(sch["offsets"], srows)
+    dys = gates[aos[srows]][:, None] * dv[t_of[srows]]
+    dhs, dxss = oracle.ffn_backward_values(xsv, es, wgu_v, wd_v, dys)
+    hs = np.zeros((srows.size, 2 * I))
+    for e in np.unique(es):
+        m = es == e
+        hs[m] = xsv[m] @ wgu_v[e].T
+    _, s_dxs2 = bars.ffn_backward_sigma(xsv, es, wgu_v, wd_v, dys, hs, dhs)
+    dx_ref = np.zeros((toks.size, H))
+    var = np.zeros((toks.size, H))
+    pos = np.searchsorted(toks, t_of[srows])
+    np.add.at(dx_ref, pos, dxss)
+    np.add.at(var, pos, s_dxs2 ** 2)
+    dx_bar = bars.C_SIGMA * np.sqrt(var + (bars.RHO16 * dx_ref) ** 2) + 1e-30
+    dx_got = bars.bf16_values(dw.out_rows(dx, toks))
+    assert np.all(np.abs(dx_got - dx_ref) <= dx_bar), float(np.max(np.abs(dx_got - dx_ref) / dx_bar))
+    print(f"[parity] full-size backward: expert {e0} ({rows.size} slots) dy, dgate, dx_s, dW; dx of "
+          f"{toks.size} tokens ({srows.size} slots) within their bars", flush=True)
