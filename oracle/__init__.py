@@ -450,9 +450,15 @@ def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
       dx_s    bf16 of W_gu[e]^T dh_q
       dx[t]   bf16 of the sum of t's local dx_s
       dW_d[e] bf16 of sum_s dy_q a_q^T;  dW_gu[e] bf16 of sum_s dh_q x_q^T
+    With MXFP8 weights (weight_format 1) every GEMM takes its weights quantised
+    along its own contraction dimension, the forward's rule for each GEMM: the
+    forward and the recompute of h use W_gu along H and W_d along I, the down
+    dgrad W_d along H (its columns) and the gate/up dgrad W_gu along 2I (its
+    columns).  The weight gradients contract over the slots and take no
+    weights.
     Returns the stored values (bf16 bits, or MXFP8 codes and scales) and the
     fp64 values before each rounding (keys ending in _exact)."""
-    assert wl.act_format == 1 and getattr(wl, "weight_format", 0) == 0
+    assert wl.act_format == 1
     idx, gate = (route_topk(wl.logits, wl.k) if wl.routing_from_logits
                  else (wl.topk_idx, wl.topk_gate))
     sch = build_schedule(idx, wl.expert_base, wl.n_local)
@@ -462,7 +468,9 @@ def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     xc, xs = gather_rows(wl.x, k, aos, slots, True)
     xq = mx_values(xc, xs)
     eos = expert_of_slots(sch["offsets"], slots)
-    y, a_ex, y_ex = ffn_rows((xc, xs), eos, wl.w_gu, wl.w_d, True, exact=True)
+    w_mx = getattr(wl, "weight_format", 0) == 1
+    mxw = (mx_quantize_rows(wl.w_gu), mx_quantize_rows(wl.w_d)) if w_mx else None
+    y, a_ex, y_ex = ffn_rows((xc, xs), eos, wl.w_gu, wl.w_d, True, mx_weights=mxw, exact=True)
     ac, asc = mx_quantize_values(a_ex)
     aq = mx_values(ac, asc)
     t_of = aos[:R] // k
@@ -476,22 +484,30 @@ def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
     dgate[aos[:R]] = np.sum(dout_v[t_of] * bf16_value(y).astype(np.float64), axis=1)
     wgu = bf16_value(wl.w_gu).astype(np.float64)
     wd = bf16_value(wl.w_d).astype(np.float64)
+    wgu_h, wd_da, wgu_dx = wgu, wd, wgu                    # the weights of h, da and dx_s
+    if w_mx:
+        deq = lambda cs: mx_dequantize(cs[0].reshape(-1), cs[1].reshape(-1))
+        wgu_h = deq(mxw[0]).reshape(wgu.shape)
+        t_d = mx_quantize_rows(np.ascontiguousarray(np.swapaxes(wl.w_d, 1, 2)))   # [n_local][I][H]
+        wd_da = np.swapaxes(deq(t_d).reshape(wl.n_local, I, H), 1, 2)
+        t_gu = mx_quantize_rows(np.ascontiguousarray(np.swapaxes(wl.w_gu, 1, 2)))  # [n_local][H][2I]
+        wgu_dx = np.swapaxes(deq(t_gu).reshape(wl.n_local, H, 2 * I), 1, 2)
     h_ex = np.zeros((R, 2 * I))
     dh_ex = np.zeros((R, 2 * I))
     for e in np.unique(eos):
         r = np.nonzero(eos == e)[0]
-        h_ex[r] = xq[r] @ wgu[e].T
+        h_ex[r] = xq[r] @ wgu_h[e].T
     h_bits = bf16_round(h_ex).reshape(R, 2 * I)
     hv = bf16_value(h_bits).astype(np.float64)
     for e in np.unique(eos):
         r = np.nonzero(eos == e)[0]
-        dh_ex[r] = swiglu_backward_values(hv[r], dyq[r] @ wd[e])
+        dh_ex[r] = swiglu_backward_values(hv[r], dyq[r] @ wd_da[e])
     dhc, dhs = mx_quantize_values(dh_ex)
     dhq = mx_values(dhc, dhs)
     dxs_ex = np.zeros((R, H))
     for e in np.unique(eos):
         r = np.nonzero(eos == e)[0]
-        dxs_ex[r] = dhq[r] @ wgu[e]
+        dxs_ex[r] = dhq[r] @ wgu_dx[e]
     dxs_bits = bf16_round(dxs_ex).reshape(R, H)
     T = idx.shape[0]
     dx_ex = np.zeros((T, H))
@@ -512,4 +528,5 @@ def backward_mx(wl, dout_bits: np.ndarray) -> Dict[str, np.ndarray]:
             "dh_exact": dh_ex, "dh_codes": dhc, "dh_scales": dhs, "dx_slots_exact": dxs_ex,
             "dx_slots": dxs_bits, "dx_exact": dx_ex, "dx": dx_bits, "dw_d_exact": dwd_ex,
             "dw_d": bf16_round(dwd_ex).reshape(dwd_ex.shape), "dw_gu_exact": dwg_ex,
-            "dw_gu": bf16_round(dwg_ex).reshape(dwg_ex.shape)}
+            "dw_gu": bf16_round(dwg_ex).reshape(dwg_ex.shape),
+            "w_gu_h": wgu_h, "w_d_da": wd_da, "w_gu_dx": wgu_dx}

@@ -10,6 +10,7 @@ Pinned against things the oracle does not compute itself:
     down = c [Id, -Id] gives y = c x*x, so dx = 2 c x dy exactly).
 """
 import numpy as np
+import pytest
 
 
 def _forward(x, eor, w_gu, w_d):
@@ -203,28 +204,32 @@ def _mx_vals(codes, scales):
     return np.where(codes & 0x80, -mag, mag)
 
 
-def _mx_case(orc, seed=31):
+def _mx_case(orc, seed=31, wfmt=0):
     import workloads as W
     wl = W.small_pool(seed, n_partitions=2, part_rows=20, H=64, I=32, E=8, k=3, expert_base=1,
                       counts=[17, 0, 9, 6], act_format=W.ACT_MXFP8)
     val = lambda b: orc.bf16_value(b).astype(np.float64)
     wl.w_gu = orc.bf16_round(val(wl.w_gu) * 20.0).reshape(wl.w_gu.shape)  # O(1) activations
     wl.w_d = orc.bf16_round(val(wl.w_d) * 20.0).reshape(wl.w_d.shape)
+    wl.weight_format = wfmt
     rng = np.random.default_rng(seed + 1)
     dout = orc.bf16_round(rng.standard_normal((wl.T, wl.H))).reshape(wl.T, wl.H)
     return wl, dout
 
 
-def test_mx_backward_storage_points(orc):
+@pytest.mark.parametrize("wfmt", [0, 1])
+def test_mx_backward_storage_points(orc, wfmt):
     """Every MXFP8 buffer of oracle.backward_mx against a brute-force search
     written from the E4M3 and E8M0 definitions (the quantisation axis and
     block alignment, the scale rule, ties, saturation), each from the inputs
     the path stores: dy from the fp32 w dout; h bf16 of W_gu x_q with x_q the
     ring's values; dh from the stored h and dy_q through the SwiGLU backward
     pinned above by finite differences; dx_s, dx and the weight gradients from
-    the quantised operands."""
+    the quantised operands.  wfmt = 1: MXFP8 weights, each GEMM's along its own
+    contraction dimension (W_gu along H for h, W_d along H for da, W_gu along
+    2I for dx_s), by the same search."""
     import bars
-    wl, dout = _mx_case(orc)
+    wl, dout = _mx_case(orc, wfmt=wfmt)
     r = orc.backward_mx(wl, dout)
     R, I, H = r["R"], wl.I, wl.H
     eos, t_of = r["expert_of_slot"], r["token_of_slot"]
@@ -240,22 +245,28 @@ def test_mx_backward_storage_points(orc):
     assert np.array_equal(dyc, r["dy_codes"]) and np.array_equal(dys, r["dy_scales"])
     dyq = _mx_vals(dyc, dys)
     wgu, wd = orc.bf16_value(wl.w_gu).astype(np.float64), orc.bf16_value(wl.w_d).astype(np.float64)
+    wgu_h, wd_da, wgu_dx = wgu, wd, wgu
+    if wfmt:
+        q_rows = lambda w: _mx_vals(*_mx_brute(w.reshape(-1, w.shape[-1]))).reshape(w.shape)
+        wgu_h = q_rows(wgu)                                           # along H
+        wd_da = np.swapaxes(q_rows(np.swapaxes(wd, 1, 2)), 1, 2)      # along H (columns)
+        wgu_dx = np.swapaxes(q_rows(np.swapaxes(wgu, 1, 2)), 1, 2)    # along 2I (columns)
     hv = np.zeros((R, 2 * I))
     dh = np.zeros((R, 2 * I))
     for e in np.unique(eos):
         rr = np.nonzero(eos == e)[0]
-        hv[rr] = bars.bf16_rne(xq[rr] @ wgu[e].T)
+        hv[rr] = bars.bf16_rne(xq[rr] @ wgu_h[e].T)
     assert np.array_equal(hv, orc.bf16_value(r["h"]).astype(np.float64))
     for e in np.unique(eos):
         rr = np.nonzero(eos == e)[0]
-        dh[rr] = orc.swiglu_backward_values(hv[rr], dyq[rr] @ wd[e])
+        dh[rr] = orc.swiglu_backward_values(hv[rr], dyq[rr] @ wd_da[e])
     dhc, dhs = _mx_brute(dh)
     assert np.array_equal(dhc, r["dh_codes"]) and np.array_equal(dhs, r["dh_scales"])
     dhq = _mx_vals(dhc, dhs)
     dxs = np.zeros((R, H))
     for e in np.unique(eos):
         rr = np.nonzero(eos == e)[0]
-        dxs[rr] = bars.bf16_rne(dhq[rr] @ wgu[e])
+        dxs[rr] = bars.bf16_rne(dhq[rr] @ wgu_dx[e])
     assert np.array_equal(dxs, orc.bf16_value(r["dx_slots"]))
     dx = np.zeros((wl.T, H))
     np.add.at(dx, t_of, dxs)
