@@ -360,13 +360,17 @@ mok_status mok_combine_slots_multi(const void* y, int32_t y_rows, const int32_t*
  * ------------------------------------------------------------------------ */
 
 /* Bytes of the transposed packed weights the backward GEMMs read:
- * W_gu^T (n_local x H x 2I) and W_d^T (n_local x I x H).  bf16 weights; the
- * packing follows desc->act_format (the backward GEMMs' k-step differs for
- * MXFP8 tokens), the size does not. */
+ * W_gu^T (n_local x H x 2I) and W_d^T (n_local x I x H).  The packing follows
+ * desc->act_format (the backward GEMMs' k-step differs for MXFP8 tokens) and
+ * desc->weight_format: with MOK_W_MXFP8_E4M3 (MXFP8 tokens, packed forward
+ * weights) the transposed weights are quantised to OCP MX E4M3 along the
+ * backward GEMMs' contraction dimension (W_d along H, W_gu along 2I: blocks of
+ * 32 down each column of the forward's matrices), and the down and gate/up
+ * dgrads run on the block-scaled FP8 MFMA. */
 mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
                                        size_t* down_t_bytes);
 /* Packs them from the bf16 weights of mok_expert_ffn's layout (either pair of
- * pointers may be null). */
+ * pointers may be null; bf16 sources also for MXFP8 weights). */
 mok_status mok_pack_weights_bwd(const mok_layer_desc* desc, const void* w_gate_up,
                                 const void* w_down, void* packed_gate_up_t, void* packed_down_t,
                                 hipStream_t stream);
@@ -469,8 +473,8 @@ mok_status mok_combine_backward_mx(const mok_tokens* dout, const void* y, int32_
                                    hipStream_t stream);
 
 /* The forward's gate/up + SwiGLU with MXFP8 tokens and act (as
- * mok_expert_gate_up) that also stores h = [g, u] in bf16 as
- * mok_expert_gate_up_save_h does.  act and act_scales are bit-identical to
+ * mok_expert_gate_up; bf16 or packed MXFP8 weights) that also stores
+ * h = [g, u] in bf16 as mok_expert_gate_up_save_h does.  act and act_scales are bit-identical to
  * mok_expert_gate_up's given the same workspace argument; without a workspace
  * h is bit-identical to the backward's recompute. */
 mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* ring,
@@ -486,7 +490,10 @@ mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* 
  * w_gate_up are not read) with MXFP8 dy in and MXFP8 dh out: dh = [dg, du]
  * of the SwiGLU backward quantised per block of 32 along 2I (as dy) into dh
  * (rows x 2I codes) and dh_scales (rows x 2I/32); dx_s = dh W_gu in bf16.
- * The packed weights come from mok_pack_weights_bwd with this desc. */
+ * The packed weights come from mok_pack_weights_bwd with this desc.  With
+ * desc->weight_format = MOK_W_MXFP8_E4M3, w_gate_up is the forward's packed
+ * MXFP8 gate/up (the recompute of h) and all three GEMMs run on the
+ * block-scaled FP8 MFMA. */
 mok_status mok_expert_ffn_backward_mx(const mok_layer_desc* desc, const void* ring,
                                       const uint8_t* ring_scales, int32_t ring_slots,
                                       const void* dy, const uint8_t* dy_scales,

@@ -201,14 +201,13 @@ def _sim_backward_mx(wl, r, dout_bits, a_sim):
     eos, t_of = r["expert_of_slot"], r["token_of_slot"]
     xq = _f32(O.mx_values(r["x_codes"], r["x_scales"]))
     dyq = _f32(O.mx_values(r["dy_codes"], r["dy_scales"]))
-    wgu = _f32(bars.bf16_values(wl.w_gu))
-    wd = _f32(bars.bf16_values(wl.w_d))
+    wgu_h, wd, wgu = _f32(r["w_gu_h"]), _f32(r["w_d_da"]), _f32(r["w_gu_dx"])
     h = np.empty((R, 2 * I))
     dh = np.empty((R, 2 * I))
     dxs = np.empty((R, H))
     for e in np.unique(eos):
         rr = np.nonzero(eos == e)[0]
-        h[rr] = bars.bf16_rne(xq[rr] @ wgu[e].T)
+        h[rr] = bars.bf16_rne(xq[rr] @ wgu_h[e].T)
         hh = _f32(h[rr])
         dh[rr] = bars.swiglu_bwd_values(hh[:, :I], hh[:, I:], dyq[rr] @ wd[e]).astype(np.float64)
     dhq = bars._mx_blocks(dh, bars._mx_exps(dh))
@@ -226,9 +225,12 @@ def _sim_backward_mx(wl, r, dout_bits, a_sim):
     return h, dhq, dxs, bars.bf16_rne(dx), dwd, dwg
 
 
-def test_mx_backward_bands_accept_fp32_and_reject_ten_percent():
+@pytest.mark.parametrize("wfmt", [0, 1])
+def test_mx_backward_bands_accept_fp32_and_reject_ten_percent(wfmt):
+    """MXFP8 activations with bf16 (wfmt 0) or MXFP8 weights (wfmt 1)."""
     wl = W.small_pool(83, n_partitions=4, part_rows=250, H=576, I=320, E=32, k=4,
                       expert_base=3, counts=[300, 17, 0, 260, 1], act_format=W.ACT_MXFP8)
+    wl.weight_format = wfmt
     dout = W.normal_bf16(np.random.SeedSequence(579), wl.T * wl.H, 1.0).reshape(wl.T, wl.H)
     r = oracle.backward_mx(wl, dout)
     b = bars.mx_backward_bands(wl, r, dout)
@@ -240,20 +242,43 @@ def test_mx_backward_bands_accept_fp32_and_reject_ten_percent():
     ref = dict(h=bars.bf16_values(r["h"]), dx_slots=bars.bf16_values(r["dx_slots"]),
                dx=bars.bf16_values(r["dx"]), dw_d=bars.bf16_values(r["dw_d"]),
                dw_gu=bars.bf16_values(r["dw_gu"]),
-               dh=oracle.mx_values(r["dh_codes"], r["dh_scales"]))
+               dh=oracle.mx_values(r["dh_codes"], r["dh_scales"]), a=b["a_q0"])
     assert np.array_equal(ref["dh"], b["dh_q0"])
     wr = r["written"]
-    got = dict(h=h, dh=dhq, dx_slots=dxs, dx=dx, dw_d=dwd, dw_gu=dwg)
-    for name in ("h", "dh", "dx_slots", "dx", "dw_d", "dw_gu"):
+    assert np.array_equal(b["a_q0"], oracle.mx_values(r["a_codes"], r["a_scales"]))
+    got = dict(a=a_sim, h=h, dh=dhq, dx_slots=dxs, dx=dx, dw_d=dwd, dw_gu=dwg)
+    if wfmt:
+        # MXFP8 weights: the later stages given the evaluation's own dh and act
+        sb = bars.mx_stage_bands(wl, r, dhq, a_sim)
+        for key in ("dx_slots", "dw_d", "dw_gu"):
+            b[key], ref[key] = sb[key][:2], sb[key][2]
+        soa = r["slot_of_assign"]
+        b["dx"] = bars.out_band(dxs, dxs, np.arange(r["R"]), soa, np.ones(soa.size),
+                                np.arange(wl.T), wl.k)
+        dxc = np.zeros((wl.T, wl.H))
+        np.add.at(dxc, r["token_of_slot"], dxs)
+        ref["dx"] = bars.bf16_rne(dxc)
+    for name in ("a", "h", "dh", "dx_slots", "dx", "dw_d", "dw_gu"):
         lo, hi = b[name]
         g, rf = got[name], ref[name]
         if name == "dx":
             g, rf, lo, hi = g[wr], rf[wr], lo[wr], hi[wr]
         st = bars.interval_stats(g, rf, lo, hi, f"fp32 MXFP8 backward {name}")
-        assert st["flagged"] < 0.5 * st["n"], name          # not a blanket band
+        if wfmt == 0:
+            assert st["flagged"] < 0.5 * st["n"], name      # not a blanket band
+        else:
+            # the block-scaled MFMA's error model (2^-12 of each step's
+            # magnitudes) puts most elements in a band of a few bf16 steps
+            # (dh: of one E4M3 step, 2^-4 to 2^-3 of the value)
+            width = np.median((hi - lo) / (np.abs(rf) + 1e-30))
+            print(f"  median band width {width:.2e} of |value|")
+            assert width < (0.13 if name in ("a", "dh") else 0.03), (name, width)
         off = rf * 1.1
         typical = np.abs(rf) > 0.01 * np.abs(rf).max()
         caught = float(np.mean(((off < lo) | (off > hi))[typical]))
         print(f"  10 % off rejected at {caught:.5f} of the typical elements")
-        assert caught > 0.999, (name, caught)
+        # MXFP8 weights: the MFMA error model (2^-12 of each step's magnitudes,
+        # about 10x the error a GPU probe measured) widens some dh bands to two
+        # E4M3 steps, where a 10 % move is inside
+        assert caught > (0.9 if wfmt and name in ("a", "dh") else 0.999), (name, caught)
     assert b["dh_flagged"] > 0

@@ -427,9 +427,9 @@ mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* 
                                         int32_t slot_end, const void* w_gate_up, void* act,
                                         uint8_t* act_scales, int32_t act_rows, void* h, void* ws,
                                         size_t ws_bytes, hipStream_t stream) {
-  if (!desc_ok(desc) || desc->act_format != MOK_ACT_MXFP8_E4M3 || desc->weight_format != MOK_W_BF16 ||
-      !ring || !ring_scales || ring_slots < 1 || !offsets || slot_begin < 0 ||
-      slot_end < slot_begin || !w_gate_up || !act || !act_scales || act_rows < 1 || !h)
+  if (!desc_ok(desc) || desc->act_format != MOK_ACT_MXFP8_E4M3 || !ring || !ring_scales ||
+      ring_slots < 1 || !offsets || slot_begin < 0 || slot_end < slot_begin || !w_gate_up || !act ||
+      !act_scales || act_rows < 1 || !h)
     return MOK_ERR_INVALID_ARG;
   if (!weights_ok(desc)) return MOK_ERR_INVALID_ARG;
   if (!gemm_operands_fit(desc, ring_slots, act_rows) ||
@@ -442,7 +442,7 @@ mok_status mok_expert_gate_up_save_h_mx(const mok_layer_desc* desc, const void* 
   a.w_gu = static_cast<const uint16_t*>(w_gate_up);
   a.act = act; a.act_scales = act_scales; a.act_rows = act_rows;
   a.H = desc->hidden; a.I = desc->inter; a.act_format = MOK_ACT_MXFP8_E4M3;
-  a.w_packed = desc->weights_packed; a.weight_format = MOK_W_BF16;
+  a.w_packed = desc->weights_packed; a.weight_format = desc->weight_format;
   a.h_out = h;
   return hip_status(launch_gate_up(a, stream));
 }
@@ -543,17 +543,20 @@ namespace {
 bool bwd_desc_ok(const mok_layer_desc* d) {
   return desc_ok(d) && d->act_format == MOK_ACT_BF16 && d->weight_format == MOK_W_BF16;
 }
-// MXFP8 tokens, bf16 weights
+// MXFP8 tokens; bf16 weights, or MXFP8 weights (packed, as the forward needs them)
 bool bwd_desc_mx_ok(const mok_layer_desc* d) {
-  return desc_ok(d) && d->act_format == MOK_ACT_MXFP8_E4M3 && d->weight_format == MOK_W_BF16;
+  return desc_ok(d) && d->act_format == MOK_ACT_MXFP8_E4M3 &&
+         (d->weight_format == MOK_W_BF16 || (d->weight_format == MOK_W_MXFP8_E4M3 && d->weights_packed));
 }
 }  // namespace
 
 mok_status mok_packed_weights_bwd_size(const mok_layer_desc* desc, size_t* gate_up_t_bytes,
                                        size_t* down_t_bytes) {
   if (!bwd_desc_ok(desc) && !bwd_desc_mx_ok(desc)) return MOK_ERR_INVALID_ARG;
-  if (gate_up_t_bytes) *gate_up_t_bytes = packed_bwd_gate_up_bytes(desc->hidden, desc->inter, desc->n_local);
-  if (down_t_bytes) *down_t_bytes = packed_bwd_down_bytes(desc->hidden, desc->inter, desc->n_local);
+  if (gate_up_t_bytes)
+    *gate_up_t_bytes = packed_bwd_gate_up_bytes(desc->hidden, desc->inter, desc->n_local, desc->weight_format);
+  if (down_t_bytes)
+    *down_t_bytes = packed_bwd_down_bytes(desc->hidden, desc->inter, desc->n_local, desc->weight_format);
   return MOK_OK;
 }
 
@@ -566,6 +569,7 @@ mok_status mok_pack_weights_bwd(const mok_layer_desc* desc, const void* w_gate_u
   return hip_status(launch_pack_weights_bwd(static_cast<const uint16_t*>(w_gate_up),
                                             static_cast<const uint16_t*>(w_down), desc->hidden,
                                             desc->inter, desc->n_local, bwd_desc_mx_ok(desc),
+                                            desc->weight_format == MOK_W_MXFP8_E4M3,
                                             static_cast<uint16_t*>(packed_gate_up_t),
                                             static_cast<uint16_t*>(packed_down_t), stream));
 }
@@ -675,6 +679,7 @@ mok_status mok_expert_ffn_backward_mx(const mok_layer_desc* desc, const void* ri
   a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
   a.dy = dy; a.dy_scales = dy_scales; a.h = h; a.dh = dh; a.dh_scales = dh_scales;
   a.dx = dx_slots; a.rows = rows; a.h_saved = h_kept ? 1 : 0; a.mx = 1;
+  a.w_mx8 = desc->weight_format == MOK_W_MXFP8_E4M3 ? 1 : 0;
   a.H = desc->hidden; a.I = desc->inter;
   return hip_status(launch_ffn_backward(a, stream));
 }

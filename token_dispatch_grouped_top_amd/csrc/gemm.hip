@@ -120,6 +120,53 @@ void k_pack_weights_mx8(const uint16_t* __restrict__ W, int64_t expert_stride, i
   }
 }
 
+// MXFP8 packing of a transposed weight (a backward GEMM's B with MXFP8 weights):
+// weight row n, k-value k is src[e][k][n] of a source stored [K][N] row-major
+// per expert, quantised along k like k_pack_weights_mx8 (two blocks of 32 per
+// k-step of 64).  Adjacent threads take adjacent rows n, so each of their 2-byte
+// reads is coalesced across the wave.  Rows past N repeat the last one.
+__global__ __launch_bounds__(256)
+void k_pack_weights_mx8_t(const uint16_t* __restrict__ W, int64_t expert_stride, int32_t K,
+                          int32_t N, int32_t n_tiles, int32_t n_local, uint8_t* __restrict__ out) {
+  using G = GeoMX8;
+  const int nk = K / G::BK;
+  const int64_t total = static_cast<int64_t>(n_local) * n_tiles * nk * BM;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int row = static_cast<int>(u % BM);
+    const int64_t blk = u / BM;                            // (e * n_tiles + nt) * nk + kt
+    const int kt = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;
+    const int nt = static_cast<int>(et % n_tiles), e = static_cast<int>(et / n_tiles);
+    const int n = nt * BN + row < N ? nt * BN + row : N - 1;
+    const uint16_t* src = W + e * expert_stride + static_cast<int64_t>(kt * G::BK) * N + n;
+    uint8_t* dst = out + blk * G::WBLOCK;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {                          // two blocks of 32
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q)
+        v[q] = __uint_as_float(static_cast<uint32_t>(src[static_cast<int64_t>(32 * b + q) * N]) << 16);
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      const int E = mx_scale_exp(amax);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                        // 16-byte chunks 2 b + h of the row
+        uint32_t c4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float* t = v + 16 * h + 4 * q;
+          c4[q] = e4m3_code_scaled(t[0], E) | (e4m3_code_scaled(t[1], E) << 8) |
+                  (e4m3_code_scaled(t[2], E) << 16) | (e4m3_code_scaled(t[3], E) << 24);
+        }
+        *reinterpret_cast<uint4*>(dst + G::off(row, 2 * b + h)) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
+      }
+      dst[G::TILE + 2 * row + b] = static_cast<uint8_t>(E + 127);
+    }
+  }
+}
+
 // Packing: one thread per 16-byte piece of the packed weights.  Block
 // (e, column tile, k-step) holds the tile's 256 weight rows x BK in the byte
 // order the GEMM's direct-to-LDS loads land them (chunk swizzle included).
@@ -259,9 +306,11 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
   g.w_packed = a.w_packed;
   set_split(g, a);
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2);
-  if (a.weight_format == MOK_W_MXFP8_E4M3) return launch_one_mx8<EPI_SWIGLU_MX>(g, n1, m_tiles, s);
-  if (a.h_out) {                   // bf16 weights (checked at the boundary)
-    g.H_out = static_cast<uint16_t*>(a.h_out);
+  if (a.h_out) g.H_out = static_cast<uint16_t*>(a.h_out);
+  if (a.weight_format == MOK_W_MXFP8_E4M3)
+    return a.h_out ? launch_one_mx8<EPI_SWIGLU_MX_H>(g, n1, m_tiles, s)
+                   : launch_one_mx8<EPI_SWIGLU_MX>(g, n1, m_tiles, s);
+  if (a.h_out) {                   // the gate/up also keeps h = [g, u]
     return a.act_format == MOK_ACT_MXFP8_E4M3 ? launch_one<true, EPI_SWIGLU_MX_H>(g, n1, m_tiles, s)
                                                : launch_one<false, EPI_SWIGLU_BF16_H>(g, n1, m_tiles, s);
   }
@@ -314,6 +363,7 @@ hipError_t launch_recompute_h(const BwdArgs& a, hipStream_t s) {
   g.C = a.h; g.c_rows = a.rows;
   g.w_packed = a.w_gu_packed;
   const int nt = (a.I + BN / 2 - 1) / (BN / 2);
+  if (a.w_mx8) return launch_one_mx8<EPI_STORE_GU>(g, nt, m_tiles, s);   // forward-packed W_gu
   return a.mx ? launch_one<true, EPI_STORE_GU>(g, nt, m_tiles, s)
               : launch_one<false, EPI_STORE_GU>(g, nt, m_tiles, s);
 }
@@ -334,6 +384,7 @@ hipError_t launch_down_dgrad(const BwdArgs& a, hipStream_t s) {
   g.H_src = static_cast<const uint16_t*>(a.h);
   g.w_packed = 1;
   const int nt = (a.I + BN - 1) / BN;
+  if (a.w_mx8) return launch_one_mx8<EPI_SWIGLU_BWD_MX>(g, nt, m_tiles, s);
   return a.mx ? launch_one<true, EPI_SWIGLU_BWD_MX>(g, nt, m_tiles, s)
               : launch_one<false, EPI_SWIGLU_BWD>(g, nt, m_tiles, s);
 }
@@ -352,6 +403,7 @@ hipError_t launch_gate_up_dgrad(const BwdArgs& a, hipStream_t s) {
   g.C = a.dx; g.c_rows = a.rows;
   g.w_packed = 1;
   const int nt = (a.H + BN - 1) / BN;
+  if (a.w_mx8) return launch_one_mx8<EPI_STORE_BF16>(g, nt, m_tiles, s);
   return a.mx ? launch_one<true, EPI_STORE_BF16>(g, nt, m_tiles, s)
               : launch_one<false, EPI_STORE_BF16>(g, nt, m_tiles, s);
 }
@@ -363,18 +415,30 @@ hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s) {
   return e;
 }
 
-size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local) {
-  return static_cast<size_t>(n_local) * ((H + BN - 1) / BN) * BM * (2 * static_cast<size_t>(I)) * 2;
+size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format) {
+  const size_t tiles = static_cast<size_t>(n_local) * ((H + BN - 1) / BN);
+  if (weight_format == MOK_W_MXFP8_E4M3) return tiles * (2 * I / GeoMX8::BK) * GeoMX8::WBLOCK;
+  return tiles * BM * (2 * static_cast<size_t>(I)) * 2;
 }
-size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local) {
-  return static_cast<size_t>(n_local) * ((I + BN - 1) / BN) * BM * static_cast<size_t>(H) * 2;
+size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format) {
+  const size_t tiles = static_cast<size_t>(n_local) * ((I + BN - 1) / BN);
+  if (weight_format == MOK_W_MXFP8_E4M3) return tiles * (H / GeoMX8::BK) * GeoMX8::WBLOCK;
+  return tiles * BM * static_cast<size_t>(H) * 2;
 }
 
 hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                                   int32_t n_local, bool act_mx, uint16_t* packed_gu_t,
+                                   int32_t n_local, bool act_mx, bool w_mx8, uint16_t* packed_gu_t,
                                    uint16_t* packed_d_t, hipStream_t s) {
   auto pack_t = [&](const uint16_t* W, int64_t stride, int32_t K, int32_t N, uint16_t* out) {
     const int n_tiles = (N + BN - 1) / BN;
+    if (w_mx8) {                   // MXFP8: quantised along k, the backward GEMM's contraction
+      const int64_t threads = static_cast<int64_t>(n_local) * n_tiles * (K / GeoMX8::BK) * BM;
+      const int64_t blocks = (threads + 255) / 256;
+      hipLaunchKernelGGL(k_pack_weights_mx8_t, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                         dim3(256), 0, s, W, stride, K, N, n_tiles, n_local,
+                         reinterpret_cast<uint8_t*>(out));
+      return hipGetLastError();
+    }
     // the same number of 16-byte pieces for either k-step (K % 64 == 0)
     const int64_t pieces = static_cast<int64_t>(n_local) * n_tiles * K * BM / 8;
     const int64_t blocks = (pieces + 255) / 256;

@@ -246,6 +246,7 @@ struct BwdArgs {
   const uint8_t* dy_scales;
   uint8_t* dh_scales;
   int32_t mx;
+  int32_t w_mx8;              // MXFP8 weights: the block-scaled FP8 tile (mx too)
   const int32_t* offsets; int32_t n_local; int32_t s_begin, s_end;
   const uint16_t* w_gu;       // the forward's gate/up weights (the recompute of h)
   int32_t w_gu_packed;        // ... in the packed tile order
@@ -277,10 +278,10 @@ struct WgradArgs {
 int32_t wgrad_kpad(int32_t rows, int32_t n_local);
 size_t wgrad_ws_bytes(int32_t rows, int32_t H, int32_t I, int32_t n_local);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t s);
-size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local);
-size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local);
+size_t packed_bwd_gate_up_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);
+size_t packed_bwd_down_bytes(int32_t H, int32_t I, int32_t n_local, int32_t weight_format);
 hipError_t launch_pack_weights_bwd(const uint16_t* w_gu, const uint16_t* w_d, int32_t H, int32_t I,
-                                   int32_t n_local, bool act_mx, uint16_t* packed_gu_t,
+                                   int32_t n_local, bool act_mx, bool w_mx8, uint16_t* packed_gu_t,
                                    uint16_t* packed_d_t, hipStream_t s);
 
 // Packed weights: bytes, and the packing launch (either source may be null).
