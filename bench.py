@@ -218,8 +218,9 @@ def time_router_gemm(mok, wl, reps: int = 20):
 
 
 def time_backward(mok, dw, st, reps: int = 10):
-    """The backward of the layer share after a forward step (bf16 weights; bf16
-    or MXFP8 activations, the latter through the _mx calls): merge backward
+    """The backward of the layer share after a forward step (bf16 activations
+    and weights; MXFP8 activations through the _mx calls, with bf16 or MXFP8
+    weights, the latter packed for each GEMM's contraction): merge backward
     (dy, dgate), the expert FFN backward (recompute of h, down dgrad with the
     SwiGLU backward, gate/up dgrad), dispatch backward (dx), weight gradients
     (transposes + two GEMMs over each expert's slots).  Seeded N(0, 1) dout for
@@ -500,19 +501,21 @@ def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
         torch.cuda.empty_cache()
     res["streaming"] = time_streaming(mok, DeviceWorkload)
     torch.cuda.empty_cache()
-    # the backward of the headline's share, bf16 and with MXFP8 activations (the same
-    # tokens, weights and routing; bf16 weights)
+    # the backward of the headline's share: bf16, with MXFP8 activations, and with
+    # MXFP8 activations and weights (the same tokens, weights and routing)
     res["backward"] = time_backward(mok, dw, st)
     log(f"[bench] backward bf16 (ms): {res['backward']}")
-    wl_mx = dataclasses.replace(wl, act_format=1, name=wl.name + "_mxfp8act")
-    dw_mx = DeviceWorkload(wl_mx)
-    st_mx = Step(dw_mx, BENCH_MAX_ROWS)
-    for _ in range(3):
-        st_mx.run()
-    res["backward_mxfp8"] = time_backward(mok, dw_mx, st_mx)
-    log(f"[bench] backward MXFP8 (ms): {res['backward_mxfp8']}")
-    del st_mx, dw_mx, wl_mx
-    torch.cuda.empty_cache()
+    for key, wfmt, suffix in (("backward_mxfp8", 0, "_mxfp8act"),
+                              ("backward_full_mxfp8", 1, "_full_mxfp8")):
+        wl_mx = dataclasses.replace(wl, act_format=1, weight_format=wfmt, name=wl.name + suffix)
+        dw_mx = DeviceWorkload(wl_mx)
+        st_mx = Step(dw_mx, BENCH_MAX_ROWS)
+        for _ in range(3):
+            st_mx.run()
+        res[key] = time_backward(mok, dw_mx, st_mx)
+        log(f"[bench] {key} (ms): {res[key]}")
+        del st_mx, dw_mx, wl_mx
+        torch.cuda.empty_cache()
     # minibatch sweep of the fused call on the headline's share: last, so that the
     # headline's warm-up follows GPU work rather than host-side set-up
     sweep = {}
@@ -730,6 +733,7 @@ def main():
         "router_gemm": router,
         "backward_ms": backward,
         "backward_mxfp8_ms": extras.get("backward_mxfp8"),
+        "backward_full_mxfp8_ms": extras.get("backward_full_mxfp8"),
         "tuned_forward": tuned,
         "cpu_baseline": cpu,
     }

@@ -80,11 +80,13 @@ bool gemm_operands_fit(const mok_layer_desc* d, int64_t ring_rows, int64_t act_r
          4ll * d->inter * d->hidden < lim;
 }
 
-// The K-split workspace of a standalone GEMM call: ws null = no split.
+// The K-split workspace of a standalone GEMM call: ws null = no split.  The
+// CU count is passed either way (the down GEMM's half-width tail uses it).
 mok_status gemm_split(const mok_layer_desc* d, void* ws, size_t ws_bytes, SplitWs& out) {
   out = SplitWs{};
-  if (!ws || d->no_split_k) return MOK_OK;
   const int n_cus = device_cus();
+  out.n_cus = n_cus;
+  if (!ws || d->no_split_k) return MOK_OK;
   if (ws_bytes < split_ws_bytes(n_cus)) return MOK_ERR_WORKSPACE;
   out = split_ws_carve(ws, n_cus);
   return MOK_OK;
@@ -627,7 +629,7 @@ mok_status mok_expert_ffn_backward(const mok_layer_desc* desc, const void* ring,
   a.w_gu_t = static_cast<const uint16_t*>(packed_gate_up_t);
   a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
   a.dy = dy; a.h = h; a.dh = dh; a.dx = dx_slots; a.rows = rows;
-  a.H = desc->hidden; a.I = desc->inter;
+  a.H = desc->hidden; a.I = desc->inter; a.n_cus = device_cus();
   return hip_status(launch_ffn_backward(a, stream));
 }
 
@@ -649,7 +651,7 @@ mok_status mok_expert_ffn_backward_saved(const mok_layer_desc* desc, const void*
   a.w_d_t = static_cast<const uint16_t*>(packed_down_t);
   a.dy = dy; a.h = const_cast<void*>(h); a.dh = dh; a.dx = dx_slots; a.rows = rows;
   a.h_saved = 1;
-  a.H = desc->hidden; a.I = desc->inter;
+  a.H = desc->hidden; a.I = desc->inter; a.n_cus = device_cus();
   return hip_status(launch_ffn_backward(a, stream));
 }
 
@@ -680,7 +682,7 @@ mok_status mok_expert_ffn_backward_mx(const mok_layer_desc* desc, const void* ri
   a.dy = dy; a.dy_scales = dy_scales; a.h = h; a.dh = dh; a.dh_scales = dh_scales;
   a.dx = dx_slots; a.rows = rows; a.h_saved = h_kept ? 1 : 0; a.mx = 1;
   a.w_mx8 = desc->weight_format == MOK_W_MXFP8_E4M3 ? 1 : 0;
-  a.H = desc->hidden; a.I = desc->inter;
+  a.H = desc->hidden; a.I = desc->inter; a.n_cus = device_cus();
   return hip_status(launch_ffn_backward(a, stream));
 }
 
@@ -808,7 +810,8 @@ mok_status forward_impl(const mok_layer_desc* desc, int32_t n_macro, const float
   hipLaunchKernelGGL(k_zero2, dim3(n_clear2 > 4096 ? 16 : 1), dim3(256), 0, stream, status, n_clear,
                      sw.blk_counts, n_clear2);
   if ((err = hipGetLastError()) != hipSuccess) return hip_status(err);
-  const SplitWs split = p.split ? split_ws_carve(at<void>(ws, p.off_split), n_cus) : SplitWs{};
+  SplitWs split = p.split ? split_ws_carve(at<void>(ws, p.off_split), n_cus) : SplitWs{};
+  split.n_cus = n_cus;
   int32_t* route_idx = at<int32_t>(ws, p.off_route_idx);
   float* route_gate = at<float>(ws, p.off_route_gate);
 

@@ -50,8 +50,15 @@ template <bool A_MX, int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kernel_lds<Geo<A_MX>::LDS, EPI>()];
+  constexpr bool halves = EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE;
   TileJob j;
-  if (!decode_job(p, p.K / Geo<A_MX>::BK, blockIdx.x, j)) return;
+  if (!decode_job(p, p.K / Geo<A_MX>::BK, blockIdx.x, j, halves)) return;
+  if constexpr (halves) {
+    if (j.half != 0) {
+      gemm_tile<A_MX, EPI, BN / 2>(p, j, lds);
+      return;
+    }
+  }
   gemm_tile<A_MX, EPI>(p, j, lds);
 }
 
@@ -59,8 +66,15 @@ template <int EPI>
 __global__ __launch_bounds__(kThreads)
 void k_ffn_gemm_mx8(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kernel_lds<GeoMX8::LDS, EPI>()];
+  constexpr bool halves = EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE;
   TileJob j;
-  if (!decode_job(p, p.K / GeoMX8::BK, blockIdx.x, j)) return;
+  if (!decode_job(p, p.K / GeoMX8::BK, blockIdx.x, j, halves)) return;
+  if constexpr (halves) {
+    if (j.half != 0) {
+      gemm_tile_mx8<EPI, BN / 2>(p, j, lds);
+      return;
+    }
+  }
   gemm_tile_mx8<EPI>(p, j, lds);
 }
 
@@ -272,9 +286,11 @@ hipError_t pack_one_mx8(const uint16_t* W, int64_t stride, int32_t K, int32_t I,
   return hipGetLastError();
 }
 
+// The device's CUs (the half-width tail) and, with a workspace, the K split.
 void set_split(GemmParams& g, const FfnArgs& a) {
+  g.n_cus = a.split.n_cus;
   if (!a.split.part || a.split.n_cus < kXcds) return;
-  g.part = a.split.part; g.part_cnt = a.split.cnt; g.n_cus = a.split.n_cus;
+  g.part = a.split.part; g.part_cnt = a.split.cnt;
 }
 
 }  // namespace
@@ -402,6 +418,7 @@ hipError_t launch_gate_up_dgrad(const BwdArgs& a, hipStream_t s) {
   g.N = a.H; g.I = 0;
   g.C = a.dx; g.c_rows = a.rows;
   g.w_packed = 1;
+  g.n_cus = a.n_cus;
   const int nt = (a.H + BN - 1) / BN;
   if (a.w_mx8) return launch_one_mx8<EPI_STORE_BF16>(g, nt, m_tiles, s);
   return a.mx ? launch_one<true, EPI_STORE_BF16>(g, nt, m_tiles, s)

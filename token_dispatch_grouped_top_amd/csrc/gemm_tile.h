@@ -131,6 +131,7 @@ struct TileJob {
   int kt0, nkt;               // nkt = 0: all k-steps
   int role, slot, slot0, npieces;
   int32_t* cnt;
+  int half;                   // 0: the whole column tile; 1, 2: its first or second 128 columns
 };
 
 // Tile order and placement.  Tiles are numbered expert by expert; inside an
@@ -202,8 +203,17 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
 // back the partial sums' traffic (measured: 250 -> 262 us on a down GEMM with
 // 16 of 32 CUs per XCD in its last round).  Slots and counters of XCD x are
 // [x * P, (x + 1) * P).
+// Half-width tail (`halves`, the y-storing epilogues): where no split into
+// pieces is taken and the r tail tiles fill at most half of the XCD's CUs,
+// each is run as two tiles of 128 columns instead, by the workgroups that
+// follow the whole tiles.  A round of tiles runs as long as a full one however
+// few of them there are (measured on the Kimi-shaped down GEMM, 256 tiles per
+// round: 3.5 rounds took as long as 4); a half-width tile does half the MFMAs
+// on the same token panel and needs no partial sums.  Every output element is
+// summed by the same MFMAs in the same order either way.
 constexpr int kSplitMinSteps = 8, kSplitMax = 8, kSplitMinPieces = 3;
-__device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid, TileJob& j) {
+__device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid, TileJob& j,
+                                           bool halves = false) {
   const int32_t R = p.offsets[p.n_local];
   const int32_t w0 = p.s_begin, w1 = p.s_end < R ? p.s_end : R;
   if (w1 <= w0) return false;
@@ -212,7 +222,9 @@ __device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid,
   const int x = bid % kXcds, i = bid / kXcds;
   const int c = q + (x < r ? 1 : 0), start = x * q + (x < r ? x : r);
   j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  j.half = 0;
   int t = i;
+  bool pieces = false;
   if (p.part != nullptr && p.n_cus >= kXcds) {
     const int P = p.n_cus / kXcds, rx = c % P;
     const int gx = (static_cast<int>(gridDim.x) - x + kXcds - 1) / kXcds;  // >= c
@@ -220,6 +232,7 @@ __device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid,
     if (sp > nk / kSplitMinSteps) sp = nk / kSplitMinSteps;
     if (sp > kSplitMax) sp = kSplitMax;
     if (rx > 0 && sp > 1 + (gx - c) / rx) sp = 1 + (gx - c) / rx;
+    pieces = sp >= kSplitMinPieces;
     if (sp >= kSplitMinPieces && i >= c - rx) {
       const int u = i - (c - rx), tt = u / sp, piece = u % sp;
       if (tt >= rx) return false;
@@ -231,6 +244,16 @@ __device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid,
       j.slot = j.slot0 + piece;
       j.npieces = sp;
       j.cnt = p.part_cnt + x * P + tt;
+    }
+  }
+  if (halves && !pieces && p.n_cus >= kXcds) {
+    const int P = p.n_cus / kXcds, rx = c % P;
+    const int gx = (static_cast<int>(gridDim.x) - x + kXcds - 1) / kXcds;  // workgroups of XCD x
+    if (rx > 0 && 2 * rx <= P && gx >= c + rx && i >= c - rx) {
+      const int u = i - (c - rx);
+      if ((u >> 1) >= rx) return false;
+      t = c - rx + (u >> 1);
+      j.half = 1 + (u & 1);
     }
   }
   if (t >= c) return false;
@@ -261,7 +284,6 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// After the main loop (LDS free, every load landed): the K-split exchange of
 // EPI_DOWN_MERGE: row tid's plan record (slot row0 + tid), loaded at the
 // start of the tile so that it lands under the main loop.  The records are
 // contiguous by slot (a wave's 64 rows are 1 KiB); looking the token up in
@@ -272,9 +294,115 @@ struct MergeRow {
   uint4 rec;
 };
 __device__ __forceinline__ void merge_row_load(const GemmParams& p, int row0, int nrows, MergeRow& m) {
-  m.rec = threadIdx.x < nrows ? p.m_plan[row0 + threadIdx.x] : make_uint4(0, 0, 0, 0);
+  m.rec = static_cast<int>(threadIdx.x) < nrows ? p.m_plan[row0 + threadIdx.x] : make_uint4(0, 0, 0, 0);
 }
 
+// C row of tile row r, for tiles starting at window row row0: one modulo per
+// tile, then a compare per row (a modulo per 16-byte store cost a third of
+// the down GEMM's time).
+struct CRows {
+  int64_t base, rows;
+  __device__ __forceinline__ CRows(const GemmParams& p, int row0)
+      : base((static_cast<int64_t>(row0) + p.c_row_base) % p.c_rows), rows(p.c_rows) {}
+  __device__ __forceinline__ int64_t operator()(int r) const {
+    const int64_t c = base + r;
+    return c < rows ? c : (rows >= BM ? c - rows : c % rows);
+  }
+};
+
+// The y store of EPI_STORE_BF16 / EPI_DOWN_MERGE for a tile TN columns wide
+// (256, or a half-width tail tile of 128) starting at output column n0.
+// vals(mi, tv) gives the wave's accumulators of fragment row group mi as TN/16
+// float4 (u = 4 ni + g: columns 8 g .. 8 g + 3 of tile (mi, ni)).  Staged
+// through LDS for 16-byte global stores: accumulator element q of tile (mi, ni)
+// is token row 32 mi + lane % 32 and column 32 ni + 8 (q / 4) + 4 (lane / 32) +
+// q % 4 of the wave's 128 x TN/2 block, so each lane writes 4 consecutive
+// columns of one row with one 8-byte store; staged rows keep their 16-byte
+// chunk k at k ^ (row % 16), so the writes of 16 rows and the row-wise reads
+// back are both free of bank conflicts.
+template <int EPI, int TN, typename Vals>
+__device__ __forceinline__ void store_y(const GemmParams& p, const TileJob& job, int n0, Vals&& vals,
+                                        uint8_t* __restrict__ lds, const MergeRow& mr) {
+  constexpr int NB = TN / 64, RB = TN * 2;                 // fragments per wave row, bytes per staged row
+  const int nrows = job.nrows;
+  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int erow = 128 * wm + (lane & 31), khalf = lane >> 5;
+  const CRows c_row_of(p, job.row0);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int r = erow + 32 * mi;
+    float4 tv[4 * NB];
+    vals(mi, tv);
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = (TN / 2) * wn + 32 * ni + 8 * g + 4 * khalf;
+        const float4 t = tv[4 * ni + g];
+        const uint2 v = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
+        *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
+      }
+  }
+  // EPI_DOWN_MERGE: where each row goes, one thread per row.  A slot that is
+  // its token's only local slot (its plan record holds the token's output row)
+  // goes there as bf16(fma(g, y, 0)) of the bf16 y: the slot-driven merge's
+  // value for a single term, bit for bit.  Every other slot (and every slot
+  // once m_status is raised) stores y in C.
+  uint16_t** m_dst = reinterpret_cast<uint16_t**>(lds + kEpiLds);
+  float* m_g = reinterpret_cast<float*>(lds + kEpiLds + BM * 8);
+  if constexpr (EPI == EPI_DOWN_MERGE) {
+    if (tid < nrows) {
+      const bool go = p.m_status == nullptr || *p.m_status == 0;
+      const uint64_t addr = static_cast<uint64_t>(mr.rec.x) | (static_cast<uint64_t>(mr.rec.y) << 32);
+      m_dst[tid] = go ? reinterpret_cast<uint16_t*>(addr) : nullptr;
+      m_g[tid] = __uint_as_float(mr.rec.z);
+    }
+  }
+  __syncthreads();
+  uint16_t* C = static_cast<uint16_t*>(p.C);
+  const int k = tid % (TN / 8), col = n0 + k * 8;           // fixed 16-byte column per thread
+  if (col < p.N) {
+    for (int r = tid / (TN / 8); r < nrows; r += kThreads / (TN / 8)) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
+      if constexpr (EPI == EPI_DOWN_MERGE) {
+        uint16_t* d = m_dst[r];
+        if (d != nullptr) {
+          const float g = m_g[r];
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(fmaf(g, __uint_as_float(w[q] << 16), 0.0f),
+                               fmaf(g, __uint_as_float(w[q] & 0xffff0000u), 0.0f));
+          // the token's row is read by no later kernel of the layer: streaming store
+          st_nt(reinterpret_cast<uint4*>(d + col), make_uint4(o[0], o[1], o[2], o[3]));
+          continue;
+        }
+      }
+      *reinterpret_cast<uint4*>(C + c_row_of(r) * p.N + col) = v;
+    }
+  }
+}
+
+// A half-width tail tile (columns [n0, n0 + 128) of its column tile): the y
+// store only (such tiles are never split into pieces).
+template <int EPI>
+__device__ __forceinline__ void tile_finish_half(const GemmParams& p, const TileJob& job,
+                                                 f32x16_t (&acc)[4][2], uint8_t* __restrict__ lds,
+                                                 const MergeRow& mr) {
+  static_assert(EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE, "half-width tiles store y only");
+  const int n0 = job.ntile * BN + (job.half - 1) * (BN / 2);
+  auto vals = [&](const int mi, float4 (&tv)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      tv[u] = make_float4(acc[mi][u >> 2][4 * (u & 3)], acc[mi][u >> 2][4 * (u & 3) + 1],
+                          acc[mi][u >> 2][4 * (u & 3) + 2], acc[mi][u >> 2][4 * (u & 3) + 3]);
+  };
+  store_y<EPI, BN / 2>(p, job, n0, vals, lds, mr);
+}
+
+// After the main loop (LDS free, every load landed): the K-split exchange of
 // a piece and the epilogue.  acc holds the wave's 128 x 128 block: element q of
 // tile (mi, ni) is token row 32 mi + lane % 32, output column 32 ni + 8 (q / 4)
 // + 4 (lane / 32) + q % 4.  Shared by every operand format.
@@ -363,13 +491,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
   // them to LDS with one 8-byte (bf16) or 16-byte (fp32) store.  Staged rows
   // keep their 16-byte chunk k at k ^ (row % 16): the writes of 16 rows and
   // the row-wise reads back are both free of bank conflicts.
-  // C row of tile row r: one modulo per tile, then a compare per row (a
-  // modulo per 16-byte store cost a third of the down GEMM's time)
-  const int64_t cbase = (static_cast<int64_t>(row0) + p.c_row_base) % p.c_rows;
-  auto c_row_of = [&](int r) -> int64_t {
-    const int64_t c = cbase + r;
-    return c < p.c_rows ? c : (p.c_rows >= BM ? c - p.c_rows : c % p.c_rows);
-  };
+  const CRows c_row_of(p, row0);
   const int erow = 128 * wm + frag_row;                  // + 32 mi
   if (EPI == EPI_STORE_GU) {
     // gate column i pairs with up column i in tile (mi, ni + 2), as in the
@@ -480,62 +602,7 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
       }
     }
   } else if (EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE) {
-    constexpr int RB = BN * 2;                             // bytes per staged row
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = erow + 32 * mi;
-      float4 tv[16];
-      tile_vals(mi, tv);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = 128 * wn + 32 * ni + 8 * g + 4 * khalf;
-          const float4 t = tv[4 * ni + g];
-          const uint2 v = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
-          *reinterpret_cast<uint2*>(lds + r * RB + (((n >> 3) ^ (r & 15)) << 4) + ((n >> 2) & 1) * 8) = v;
-        }
-    }
-    // EPI_DOWN_MERGE: where each row goes, one thread per row.  A slot that is
-    // its token's only local slot (its plan record holds the token's output row)
-    // goes there as bf16(fma(g, y, 0)) of the bf16 y: the slot-driven merge's
-    // value for a single term, bit for bit.  Every other slot (and every slot
-    // once m_status is raised) stores y in C.
-    uint16_t** m_dst = reinterpret_cast<uint16_t**>(lds + kEpiLds);
-    float* m_g = reinterpret_cast<float*>(lds + kEpiLds + BM * 8);
-    if constexpr (EPI == EPI_DOWN_MERGE) {
-      if (tid < nrows) {
-        const bool go = p.m_status == nullptr || *p.m_status == 0;
-        const uint64_t addr = static_cast<uint64_t>(mr.rec.x) | (static_cast<uint64_t>(mr.rec.y) << 32);
-        m_dst[tid] = go ? reinterpret_cast<uint16_t*>(addr) : nullptr;
-        m_g[tid] = __uint_as_float(mr.rec.z);
-      }
-    }
-    __syncthreads();
-    uint16_t* C = static_cast<uint16_t*>(p.C);
-    const int k = tid % (BN / 8), col = n0 + k * 8;         // fixed 16-byte column per thread
-    if (col < p.N) {
-      for (int r = tid / (BN / 8); r < nrows; r += kThreads / (BN / 8)) {
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * RB + ((k ^ (r & 15)) << 4));
-        if constexpr (EPI == EPI_DOWN_MERGE) {
-          uint16_t* d = m_dst[r];
-          if (d != nullptr) {
-            const float g = m_g[r];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              o[q] = pack_bf16x2(fmaf(g, __uint_as_float(w[q] << 16), 0.0f),
-                                 fmaf(g, __uint_as_float(w[q] & 0xffff0000u), 0.0f));
-            // the token's row is read by no later kernel of the layer: streaming store
-            st_nt(reinterpret_cast<uint4*>(d + col), make_uint4(o[0], o[1], o[2], o[3]));
-            continue;
-          }
-        }
-        const int64_t crow = c_row_of(r);
-        *reinterpret_cast<uint4*>(C + crow * p.N + col) = v;
-      }
-    }
+    store_y<EPI, BN>(p, job, n0, tile_vals, lds, mr);
   } else {
     // SwiGLU: gate column i pairs with up column i in tile (mi, ni + 2).
     // SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal.
@@ -623,11 +690,18 @@ __device__ __forceinline__ void tile_finish(const GemmParams& p, const TileJob& 
 // [row0, row0 + nrows) of the window, column tile `ntile`.  Called by all 256
 // threads of a workgroup; `lds` is the workgroup's LDS (Geo<A_MX>::LDS bytes).
 // Starts with a barrier, so it can be called back to back on the same LDS.
-template <bool A_MX, int EPI>
+// TN = 128: a half-width tail tile (job.half), the y-storing epilogues only.
+template <bool A_MX, int EPI, int TN = BN>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& job,
                                           uint8_t* __restrict__ lds) {
   using G = Geo<A_MX>;
   constexpr int BK = G::BK, NS = G::NS;
+  static_assert(TN == BN || (TN == BN / 2 && (EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE)),
+                "half-width tiles store y only");
+  constexpr int NB = TN / 64;                   // 32-column fragments per wave
+  constexpr int NLB = G::NLOAD_B * TN / BN;     // weight loads per stage and thread
+  // first weight row of a half-width tile within its column tile
+  const int hrow = TN == BN ? 0 : (job.half - 1) * TN;
   __syncthreads();
   const int e = job.e, row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
   // the wave index is uniform: in an SGPR the LDS destinations of the direct
@@ -657,16 +731,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   if (p.w_packed) {
     Wbase = p.W + ((static_cast<int64_t>(e) * p.n_tiles + ntile) * nk_all + kt0) * (BM * BK);
     wkstride = BM * BK;
+    // (the LDS image is row-major: a half's rows are one contiguous half of it)
 #pragma unroll
-    for (int j = 0; j < G::NLOAD_B; ++j) boff[j] = (4 * j + wave) * 512 + lane * 8;
+    for (int j = 0; j < NLB; ++j) boff[j] = (4 * j + wave) * 512 + lane * 8 + hrow * BK;
   } else {
     Wbase = p.W + static_cast<int64_t>(e) * p.w_expert_stride + kt0 * BK;
     wkstride = BK;
     const int lrowB = tid / G::CPR_B;
     const int lchunkB = (lane % G::CPR_B) ^ chunk_key<G::CPR_B>(lrowB);
 #pragma unroll
-    for (int j = 0; j < G::NLOAD_B; ++j)
-      boff[j] = static_cast<uint32_t>(w_row_of(lrowB + G::RSTEP_B * j, ntile, swiglu, p.I, p.N)) *
+    for (int j = 0; j < NLB; ++j)
+      boff[j] = static_cast<uint32_t>(w_row_of(hrow + lrowB + G::RSTEP_B * j, ntile, swiglu, p.I, p.N)) *
                     static_cast<uint32_t>(K) + lchunkB * 8;
   }
   // A rows (slots) -> ring rows, tail rows clamped to the last valid one.
@@ -709,11 +784,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A; };
   auto tileS = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A + G::TILE_B; };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
@@ -736,7 +811,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
 #define MOK_ISSUE_W(kt, buf)                                                                 \
   do {                                                                                       \
     uint8_t* Bs_ = tileB(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < G::NLOAD_B; ++j)                                   \
+    _Pragma("unroll") for (int j = 0; j < NLB; ++j)                                          \
       MOK_LD_W(j, kt, Bs_ + (4 * j + wave) * 1024);                                          \
   } while (0)
 #define MOK_ISSUE_A(kt, buf)                                                                 \
@@ -763,14 +838,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   // reads two code chunks and one scale per A fragment row, and converts each
   // slice right before it is used (v_cvt_scalef32_pk_bf16_fp8: exact
   // bf16 rounding of code x 2^E).
-  bf16x8_t af[2][4], bfr[2][4];
+  bf16x8_t af[2][4], bfr[2][NB];
   uint4 araw[4][2];
   float ascale[4];
 #define MOK_FRAGS_B(dst, pb, ks_)                                                            \
   do {                                                                                       \
     const int kc_ = A_MX ? 4 * khalf + (ks_) : 2 * (ks_) + khalf;                            \
-    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                         \
-      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::offB(128 * wn + 32 * ni + frag_row, kc_)); \
+    _Pragma("unroll") for (int ni = 0; ni < NB; ++ni)                                        \
+      bfr[dst][ni] = *reinterpret_cast<const bf16x8_t*>((pb) + G::offB((TN / 2) * wn + 32 * ni + frag_row, kc_)); \
   } while (0)
 #define MOK_FRAGS(dst, pa, pb, ks_)                                                          \
   do {                                                                                       \
@@ -819,7 +894,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
 #define MOK_MMA(src)                                                                         \
   do {                                                                                       \
     _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                         \
-      _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                       \
+      _Pragma("unroll") for (int ni = 0; ni < NB; ++ni)                                      \
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[src][ni], af[src][mi], acc[mi][ni], 0, 0, 0); \
   } while (0)
 
@@ -838,7 +913,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   // clamped re-loads of the last stage into buffers nobody reads again, which
   // keeps the per-thread load count -- and so the vmcnt bookkeeping -- the
   // same in every step.
-  constexpr int LW = G::NLOAD_B, LA = G::NLOAD_A + (A_MX ? 1 : 0), LPS = LW + LA;
+  constexpr int LW = NLB, LA = G::NLOAD_A + (A_MX ? 1 : 0), LPS = LW + LA;
   // EPI_DOWN_MERGE: the plan record of this thread's row is loaded before the
   // prologue's loads (it only makes the first waits below stricter)
   MergeRow mr;
@@ -864,8 +939,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   //   barrier (stage kt+1 landed everywhere; buffer kt % NS free);
   //   B: MFMAs of the last slice, with the fragment reads of step kt+1 and
   //      then the weight half of stage kt+NS interleaved the same way.
-  constexpr int kReadsA = A_MX ? 4 * (KS - 1) : 8 * (KS - 1); // fragment reads in phase A
-  constexpr int kReadsB = A_MX ? 16 : 8;                     // E4M3: 4 B + 8 codes + 4 scales
+  constexpr int MPS = 4 * NB;                                // MFMAs per k-slice
+  constexpr int kReadsA = A_MX ? NB * (KS - 1) : (4 + NB) * (KS - 1);  // fragment reads in phase A
+  constexpr int kReadsB = A_MX ? NB + 12 : 4 + NB;           // E4M3: NB B + 8 codes + 4 scales
+  constexpr int kMA = MPS * (KS - 1);                        // MFMAs in phase A
+  constexpr int kRA1 = kReadsA < kMA ? kReadsA : kMA;        // reads paired one per MFMA
+  constexpr int kVA = kMA - kRA1 < LA ? kMA - kRA1 : LA;     // loads paired after them
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const uint8_t* As = tileA(buf);
     const uint8_t* Bs = tileB(buf);
@@ -881,16 +960,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
       MOK_ISSUE_A(kp, buf == 0 ? NS - 1 : buf - 1);
     }
 #pragma unroll
-    for (int i = 0; i < kReadsA; ++i) {
+    for (int i = 0; i < kRA1; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one fragment read
     }
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
+    for (int i = 0; i < kVA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one global -> LDS load
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 * (KS - 1) - kReadsA - LA, 0);
+    if (kMA - kRA1 - kVA > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMA - kRA1 - kVA, 0);
+    if (kReadsA - kRA1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, kReadsA - kRA1, 0);
+    if (LA - kVA > 0) __builtin_amdgcn_sched_group_barrier(0x020, LA - kVA, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(NS - 2) * LPS>();                               // stage kt+1 landed
     // Barrier without a fence: a workgroup fence here would wait for every
@@ -903,8 +984,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
     MOK_FRAGS0(tileA(nbuf), tileB(nbuf), tileS(nbuf));
     MOK_ISSUE_W(kn, buf);                                    // weight half of stage kt+NS
     MOK_MMA((KS - 1) & 1);
-    constexpr int kRB1 = kReadsB < 16 ? kReadsB : 16;        // reads paired one per MFMA
-    constexpr int kVB = 16 - kRB1 < LW ? 16 - kRB1 : LW;     // loads paired after them
+    constexpr int kRB1 = kReadsB < MPS ? kReadsB : MPS;      // reads paired one per MFMA
+    constexpr int kVB = MPS - kRB1 < LW ? MPS - kRB1 : LW;   // loads paired after them
 #pragma unroll
     for (int i = 0; i < kRB1; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
@@ -915,7 +996,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one global -> LDS load
     }
-    if (16 - kRB1 - kVB > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - kRB1 - kVB, 0);
+    if (MPS - kRB1 - kVB > 0) __builtin_amdgcn_sched_group_barrier(0x008, MPS - kRB1 - kVB, 0);
+    if (kReadsB - kRB1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, kReadsB - kRB1, 0);
     if (LW - kVB > 0) __builtin_amdgcn_sched_group_barrier(0x020, LW - kVB, 0);
     __builtin_amdgcn_sched_barrier(0);
     buf = nbuf;
@@ -944,7 +1026,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();                                           // LDS is reused by the epilogue
 
-  tile_finish<EPI>(p, job, acc, lds, mr);
+  if constexpr (TN == BN) {
+    tile_finish<EPI>(p, job, acc, lds, mr);
+  } else {
+    tile_finish_half<EPI>(p, job, acc, lds, mr);
+  }
 }
 
 // A whole tile (all k-steps).
@@ -954,6 +1040,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int row0, 
   TileJob j;
   j.e = e; j.row0 = row0; j.nrows = nrows; j.ntile = ntile;
   j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  j.half = 0;
   gemm_tile<A_MX, EPI>(p, j, lds);
 }
 

@@ -44,11 +44,18 @@ struct GeoMX8 {
 };
 static_assert(GeoMX8::LDS <= 160 * 1024, "LDS budget");
 
-template <int EPI>
+// TN = 128: a half-width tail tile (job.half), the y-storing epilogues only.
+template <int EPI, int TN = BN>
 __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob& job,
                                               uint8_t* __restrict__ lds) {
   using G = GeoMX8;
   constexpr int BK = G::BK, NS = G::NS;
+  static_assert(TN == BN || (TN == BN / 2 && (EPI == EPI_STORE_BF16 || EPI == EPI_DOWN_MERGE)),
+                "half-width tiles store y only");
+  constexpr int NB = TN / 64;                   // 32-column fragments per wave
+  constexpr int NLB = G::NLOAD * TN / BN;       // weight code loads per stage and thread
+  // first weight row of a half-width tile within its column tile
+  const int hrow = TN == BN ? 0 : (job.half - 1) * TN;
   __syncthreads();
   const int e = job.e, row0 = job.row0, nrows = job.nrows, ntile = job.ntile;
   const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -59,12 +66,15 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   const int nk = job.nkt > 0 ? job.nkt : nk_all;
 
   // weights: the tile's blocks from k-step kt0 on; load j of a wave reads the
-  // contiguous KiB (4 j + wave) of a block, the scales 2 bytes per thread
+  // contiguous KiB (4 j + wave) of a block, the scales 2 bytes per thread (a
+  // half-width tile: the half's rows, one contiguous half of the codes; its
+  // threads 128..255 load the half's scales again, into slots nobody reads)
   const uint8_t* Wq = reinterpret_cast<const uint8_t*>(p.W) +
                       ((static_cast<int64_t>(e) * p.n_tiles + ntile) * nk_all + kt0) * G::WBLOCK;
   uint32_t boff[G::NLOAD];
 #pragma unroll
-  for (int j = 0; j < G::NLOAD; ++j) boff[j] = (4 * j + wave) * 1024 + lane * 16;
+  for (int j = 0; j < NLB; ++j) boff[j] = (4 * j + wave) * 1024 + lane * 16 + hrow * G::ROWB;
+  const uint32_t wsoff = G::TILE + 2 * (hrow + (TN == BN ? tid : (tid & (TN - 1))));
   // tokens: ring rows, tail rows clamped to the last valid one; lane l of load
   // j lands at physical chunk l % 4 of row tid / 4 + RSTEP j.  The ring is
   // column-blocked: a k-step is one 64-byte block per row, a_kstep bytes
@@ -97,11 +107,11 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   auto tileSA = [&](int buf) { return lds + buf * G::STAGEB + 2 * G::TILE; };
   auto tileSB = [&](int buf) { return lds + buf * G::STAGEB + 2 * G::TILE + G::SCALEB; };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
@@ -115,11 +125,11 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #define MX8_ISSUE_W(kt, buf)                                                                 \
   do {                                                                                       \
     uint8_t* Bs_ = tileB(buf);                                                               \
-    _Pragma("unroll") for (int j = 0; j < G::NLOAD; ++j)                                     \
+    _Pragma("unroll") for (int j = 0; j < NLB; ++j)                                          \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(Bs_ + (4 * j + wave) * 1024), 16, \
                                                boff[j], static_cast<uint32_t>(kt) * G::WBLOCK, 0, 2); \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(tileSB(buf) + wave * 256), 2,   \
-                                             G::TILE + 2 * tid, static_cast<uint32_t>(kt) * G::WBLOCK, 0, 2); \
+                                             wsoff, static_cast<uint32_t>(kt) * G::WBLOCK, 0, 2); \
   } while (0)
 #define MX8_ISSUE_A(kt, buf)                                                                 \
   do {                                                                                       \
@@ -138,8 +148,8 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   // base + 2048 i + a per-lane offset: one address per chunk serves all four
   // row groups, i goes into the instruction's offset field, and the loop
   // needs no address arithmetic per read.
-  i32x8_t tf[2][4], wf[2][4];
-  int ts[2][4], wsc[2][4];
+  i32x8_t tf[2][4], wf[2][NB];
+  int ts[2][4], wsc[2][NB];
   const int key = chunk_key<G::CPR>(frag_row);
   const int lane_lo = frag_row * G::ROWB + ((khalf ^ key) << 4);
   const int lane_hi = frag_row * G::ROWB + (((2 + khalf) ^ key) << 4);
@@ -152,13 +162,13 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #define MX8_FRAGS(set, buf)                                                                  \
   do {                                                                                       \
     const uint8_t* At_ = tileA(buf) + 128 * G::ROWB * wm;                                    \
-    const uint8_t* Bt_ = tileB(buf) + 128 * G::ROWB * wn;                                    \
+    const uint8_t* Bt_ = tileB(buf) + (TN / 2) * G::ROWB * wn;                               \
     const uint8_t* Sa_ = tileSA(buf) + 512 * wm + lane_sc;                                   \
-    const uint8_t* Sb_ = tileSB(buf) + 512 * wn + lane_sc;                                   \
+    const uint8_t* Sb_ = tileSB(buf) + (TN / 2) * 4 * wn + lane_sc;                          \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                       \
-      wf[set][i_] = frag(Bt_ + lane_lo, Bt_ + lane_hi, i_);                                  \
+      if (i_ < NB) wf[set][i_ < NB ? i_ : 0] = frag(Bt_ + lane_lo, Bt_ + lane_hi, i_);        \
       tf[set][i_] = frag(At_ + lane_lo, At_ + lane_hi, i_);                                  \
-      wsc[set][i_] = Sb_[128 * i_];                                                          \
+      if (i_ < NB) wsc[set][i_ < NB ? i_ : 0] = Sb_[128 * i_];                               \
       ts[set][i_] = Sa_[128 * i_];                                                           \
     }                                                                                        \
   } while (0)
@@ -167,7 +177,7 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #define MX8_MMA(set, mi0)                                                                    \
   do {                                                                                       \
     _Pragma("unroll") for (int mi = (mi0); mi < (mi0) + 2; ++mi)                              \
-      _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                       \
+      _Pragma("unroll") for (int ni = 0; ni < NB; ++ni)                                      \
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                       \
             wf[set][ni], tf[set][mi], acc[mi][ni], 0, 0, 0, wsc[set][ni], 0, ts[set][mi]);   \
   } while (0)
@@ -178,7 +188,12 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   // all fragments of step kt+1 into the other register set, issues the weight
   // half of stage kt+NS and runs the MFMAs of row groups 2, 3.  The loop is
   // unrolled by two so the register sets alternate at compile time.
-  constexpr int LW = G::NLOAD + 1, LA = G::NLOAD + 1, LPS = LW + LA;
+  constexpr int LW = NLB + 1, LA = G::NLOAD + 1, LPS = LW + LA;
+  // scheduling groups: phase A's MFMAs paired with the token loads, phase B's
+  // with the fragment reads (3 per row group: two code chunks and a scale)
+  constexpr int kMP = 2 * NB;                                // MFMAs per phase
+  constexpr int kVA = LA < kMP ? LA : kMP;
+  constexpr int kRB = 3 * (4 + NB), kRPer = kRB / kMP;
   MergeRow mr;                                               // EPI_DOWN_MERGE, as gemm_tile
   if constexpr (EPI == EPI_DOWN_MERGE) merge_row_load(p, job.row0, job.nrows, mr);
 #pragma unroll
@@ -199,11 +214,12 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
       const int kp_ = kt - 1 + NS < nk ? kt - 1 + NS : nk - 1;                               \
       MX8_ISSUE_A(kp_, buf == 0 ? NS - 1 : buf - 1);                                         \
     }                                                                                        \
-    _Pragma("unroll") for (int i_ = 0; i_ < LA; ++i_) {                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < kVA; ++i_) {                                     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
     }                                                                                        \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 - LA, 0);                                  \
+    if (kMP - kVA > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMP - kVA, 0);            \
+    if (LA - kVA > 0) __builtin_amdgcn_sched_group_barrier(0x020, LA - kVA, 0);              \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     wait_vm<(NS - 2) * LPS>();                                                               \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                          \
@@ -212,10 +228,11 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
     MX8_FRAGS(nxt, nbuf_);                                                                   \
     MX8_ISSUE_W(kn_, buf);                                                                   \
     MX8_MMA(cur, 2);                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < kMP; ++i_) {                                     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, kRPer, 0);                                 \
     }                                                                                        \
+    if (kRB - kRPer * kMP > 0) __builtin_amdgcn_sched_group_barrier(0x100, kRB - kRPer * kMP, 0); \
     __builtin_amdgcn_sched_group_barrier(0x020, LW, 0);                                      \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     buf = nbuf_;                                                                             \
@@ -229,9 +246,9 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   if ((nk - 1) & 1) {                                        // odd: one more step, set 1 -> 0
     MX8_STEP(0, 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tf[0][i] = tf[1][i]; wf[0][i] = wf[1][i]; ts[0][i] = ts[1][i]; wsc[0][i] = wsc[1][i];
-    }
+    for (int i = 0; i < 4; ++i) { tf[0][i] = tf[1][i]; ts[0][i] = ts[1][i]; }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) { wf[0][i] = wf[1][i]; wsc[0][i] = wsc[1][i]; }
   }
   MX8_MMA(0, 0);                                             // last k-step
   MX8_MMA(0, 2);
@@ -242,7 +259,11 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
 #undef MX8_ISSUE_W
   wait_vm<0>();                                              // clamped tail loads still land in LDS
   __syncthreads();
-  tile_finish<EPI>(p, job, acc, lds, mr);
+  if constexpr (TN == BN) {
+    tile_finish<EPI>(p, job, acc, lds, mr);
+  } else {
+    tile_finish_half<EPI>(p, job, acc, lds, mr);
+  }
 }
 
 // A whole tile (all k-steps).
@@ -252,6 +273,7 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, int e, int ro
   TileJob j;
   j.e = e; j.row0 = row0; j.nrows = nrows; j.ntile = ntile;
   j.kt0 = 0; j.nkt = 0; j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  j.half = 0;
   gemm_tile_mx8<EPI>(p, j, lds);
 }
 

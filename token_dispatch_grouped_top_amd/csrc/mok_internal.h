@@ -201,7 +201,7 @@ hipError_t launch_combine_slots(const void* y, int32_t y_rows, const int32_t* ao
 struct SplitWs {
   int32_t* cnt;
   float* part;              // null: no split
-  int32_t n_cus;
+  int32_t n_cus;            // the device's CUs (set with or without a split)
 };
 size_t split_ws_bytes(int32_t n_cus);
 SplitWs split_ws_carve(void* ws, int32_t n_cus);
@@ -257,6 +257,7 @@ struct BwdArgs {
   int32_t h_saved;            // h already holds [g, u] from the forward: no recompute
   int32_t rows;
   int32_t H, I;
+  int32_t n_cus;              // the device's CUs (the dx_s GEMM's half-width tail); 0: none
 };
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t s);
 // Weight gradients over all slots [0, R): dW_d = sum dy a^T, dW_gu = sum dh x^T

@@ -131,7 +131,7 @@ void k_wgrad(const GemmParams p, const int32_t* __restrict__ poff, int32_t M, in
   j.ntile = ntile;
   j.kt0 = poff[e] / kPadK;
   j.nkt = (poff[e + 1] - poff[e]) / kPadK;   // >= 1
-  j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr;
+  j.role = kWhole; j.slot = 0; j.slot0 = 0; j.npieces = 0; j.cnt = nullptr; j.half = 0;
   gemm_tile<false, EPI_STORE_BF16>(p, j, lds);
 }
 
