@@ -187,6 +187,42 @@ def time_streaming(mok, DeviceWorkload, n_macro: int = 8):
     return res
 
 
+def time_merge_all_slots(mok, st, reps: int = 20) -> dict:
+    """The weighted merge as one standalone kernel over every routed slot
+    (mok_combine_slots, the slot-driven merge of all R slots from a y that
+    holds every slot's row), timed with HIP events after the timed region: the
+    layer step itself merges the single-slot tokens in the down GEMM's epilogue
+    and only the rest in mok_combine_slots_multi.  Algorithmic bytes: every
+    slot's y row read and every written token's row stored, R H 2 + T_out H 2,
+    plus the routing words R (1 + k) 4."""
+    import numpy as np
+    import torch
+    from gpu_harness import to_host
+    dw, wl = st.dw, st.dw.wl
+    mok.mok_expert_down(st.desc, st.act, st.act_sc, st.cap, st.offsets, 0, st.cap, st.w_d, st.y,
+                        st.cap, st.gemm_ws)
+    run = lambda: mok.mok_combine_slots(st.y, st.cap, st.aos, st.offsets, wl.n_local, st.cap,
+                                        st.soa, dw.topk_gate, wl.k, wl.H, dw.outs[0], st.status)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for i in range(reps):
+        ev[2 * i].record()
+        run()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]))
+    R = int(to_host(st.offsets)[-1])
+    soa = to_host(st.soa).reshape(wl.T, wl.k)
+    T_out = int(((soa >= 0).sum(1) > 0).sum())
+    b = R * wl.H * 2 + T_out * wl.H * 2 + R * (1 + wl.k) * 4
+    gbs = b / (ms * 1e-3) / 1e9
+    return {"kernel": "mok_combine_slots over all R slots", "ms": round(ms, 4),
+            "algorithmic_bytes": b, "GBps": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def time_router_gemm(mok, wl, reps: int = 20):
     """mok_route_topk_gemm on this workload's routed tokens' shape (T_route x H
     against E router rows, seeded N(0, 1) tokens and N(0, 1/H) router
@@ -669,6 +705,11 @@ def main():
         backward = time_backward(mok, dw, st)
         log(f"[bench] backward (ms): {backward}")
 
+    merge_all = time_merge_all_slots(mok, st) if not wl.routing_from_logits else None
+    if merge_all:
+        log(f"[bench] merge of all {R} slots (mok_combine_slots): {merge_all['ms'] * 1e3:.1f} us, "
+            f"{merge_all['GBps']:.0f} GB/s, {merge_all['frac_hbm']:.3f} of HBM")
+
     router = time_router_gemm(mok, wl)
     log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
         f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
@@ -722,6 +763,7 @@ def main():
         "dispatch_frac_hbm": round(rr["dispatch_GBps"] / PEAK_HBM_GBS, 4),
         "combine_GBps": round(rr["combine_GBps"], 1),
         "combine_frac_hbm": round(rr["combine_GBps"] / PEAK_HBM_GBS, 4),
+        "merge_all_slots": merge_all,
         "schedule_share": round(per["schedule"] / wall_ms, 4),
         # the layer against its roofline: both GEMMs at the MFMA peak plus the
         # gather and merge bytes at the HBM peak, over the timed wall
