@@ -310,6 +310,26 @@ struct CRows {
   }
 };
 
+// A (token) row of tile row r, tail rows clamped to the last valid one: one
+// 32-bit modulo per tile, then a compare per row (a 64-bit modulo per row
+// kept every tile's first loads waiting behind a few hundred instructions).
+// Row numbers and the base are non-negative int32, so their sum fits in 32
+// bits; a tile row beyond the ring's size takes the modulo again.
+struct ARows {
+  uint32_t base, rows;
+  int nrows;
+  __device__ __forceinline__ ARows(const GemmParams& p, int row0, int nrows_)
+      : base((static_cast<uint32_t>(row0) + static_cast<uint32_t>(p.a_row_base)) %
+             static_cast<uint32_t>(p.a_rows)),
+        rows(static_cast<uint32_t>(p.a_rows)), nrows(nrows_) {}
+  __device__ __forceinline__ uint32_t operator()(int r) const {
+    uint32_t c = base + static_cast<uint32_t>(r < nrows ? r : nrows - 1);
+    if (c >= rows) c -= rows;
+    if (c >= rows) c %= rows;
+    return c;
+  }
+};
+
 // The y store of EPI_STORE_BF16 / EPI_DOWN_MERGE for a tile TN columns wide
 // (256, or a half-width tail tile of 128) starting at output column n0.
 // vals(mi, tv) gives the wave's accumulators of fragment row group mi as TN/16
@@ -748,10 +768,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   // The A buffer is column-blocked (a k-step of either format is one 64-byte
   // block per row, block-major): load j of k-step kt reads byte aoff[j] +
   // kt * a_kstep, and the tile's rows of a k-step are contiguous memory.
-  auto a_ring_row = [&](int r) -> uint32_t {
-    const int rr = r < nrows ? r : nrows - 1;
-    return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
-  };
+  const ARows a_ring_row(p, row0, nrows);
   const uint32_t a_kstep = static_cast<uint32_t>(p.a_rows) * kColBlock;
   const int lrowA = tid / G::CPR_A;
   const int lchunkA = (lane % G::CPR_A) ^ chunk_key<G::CPR_A>(lrowA);
@@ -784,13 +801,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
   auto tileB = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A; };
   auto tileS = [&](int buf) { return lds + buf * G::STAGEB + G::TILE_A + G::TILE_B; };
 
+  // (zeroed after the prologue's loads are issued: 256 accumulator writes
+  // per lane would otherwise sit in front of them)
   f32x16_t acc[4][NB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
@@ -924,6 +937,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileJob& jo
     MOK_ISSUE_W(ks0, s0);
     if (s0 + 1 < NS) MOK_ISSUE_A(ks0, s0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   wait_vm<(NS - 2) * LPS + LW>();                            // stage 0 landed
   __syncthreads();
 

@@ -79,10 +79,7 @@ __device__ __forceinline__ void gemm_tile_mx8(const GemmParams& p, const TileJob
   // j lands at physical chunk l % 4 of row tid / 4 + RSTEP j.  The ring is
   // column-blocked: a k-step is one 64-byte block per row, a_kstep bytes
   // apart, and scale pairs a_rows * 2 bytes apart.
-  auto a_ring_row = [&](int r) -> uint32_t {
-    const int rr = r < nrows ? r : nrows - 1;
-    return static_cast<uint32_t>((static_cast<int64_t>(row0) + rr + p.a_row_base) % p.a_rows);
-  };
+  const ARows a_ring_row(p, row0, nrows);
   const uint32_t a_kstep = static_cast<uint32_t>(p.a_rows) * kColBlock;
   const int lrow = tid / G::CPR;
   const int lchunk = (lane % G::CPR) ^ chunk_key<G::CPR>(lrow);
