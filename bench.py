@@ -223,6 +223,55 @@ def time_merge_all_slots(mok, st, reps: int = 20) -> dict:
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def mover_sweep(mok, DeviceWorkload) -> dict:
+    """The persistent kernel's mover count against the stream path: ms per macrobatch of
+    mok_moe_forward_batches on the streaming workload, one macrobatch at M = 1024, 2560 and
+    4096 and 8 macrobatches at M = 2560, 4096 and 8192, for n_move_cus in 40 .. 128."""
+    import torch
+    import workloads as W
+    from gpu_harness import to_dev
+    n_macro = 8
+    wls = W.streaming(n_macro)
+    d0 = DeviceWorkload(wls[0])
+    idx = [d0.topk_idx] + [to_dev(w.topk_idx) for w in wls[1:]]
+    gate = [d0.topk_gate] + [to_dev(w.topk_gate) for w in wls[1:]]
+    outs = [d0.new_out() for _ in wls]
+    d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=BENCH_MAX_ROWS, mode=0, weights_packed=1)
+    w_gu, w_d = d0.weights(d)
+    ws = torch.empty(mok.mok_forward_workspace_size(d, d0.wl.T, n_macro), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(30):            # the chip's clock falls within milliseconds of idling
+        mok.mok_moe_forward_batches(d, n_macro, idx, gate, d0.wl.T, d0.x, w_gu, w_d, outs, ws)
+    torch.cuda.synchronize()
+    del ws
+    res = {}
+    for nm, M in ((1, 1024), (1, 2560), (1, 4096), (n_macro, 2560), (n_macro, 4096), (n_macro, 8192)):
+        row = {}
+        for mode, n_move in [(0, 0)] + [(1, n) for n in (40, 48, 56, 64, 80, 96, 128)]:
+            d = d0.desc(max_rows=BENCH_MAX_ROWS, minibatch=M, mode=mode, n_move_cus=n_move,
+                        weights_packed=1)
+            ws = torch.empty(mok.mok_forward_workspace_size(d, d0.wl.T, nm), dtype=torch.uint8,
+                             device="cuda")
+            run = lambda: mok.mok_moe_forward_batches(d, nm, idx[:nm], gate[:nm], d0.wl.T, d0.x,
+                                                      w_gu, w_d, outs[:nm], ws)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 6 if nm == 1 else 3
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            assert mok.mok_device_status(ws) == 0
+            row["stream" if mode == 0 else str(n_move)] = round(e0.elapsed_time(e1) / reps / nm, 4)
+            del ws
+        res[f"macrobatches{nm}_M{M}"] = row
+        log(f"[bench] mover sweep, {nm} macrobatch(es), M={M}: {row}")
+    return res
+
+
 def time_router_gemm(mok, wl, reps: int = 20):
     """mok_route_topk_gemm on this workload's routed tokens' shape (T_route x H
     against E router rows, seeded N(0, 1) tokens and N(0, 1/H) router
@@ -606,6 +655,9 @@ def main():
                     help="also time the backward of the layer share with --no-extras or another "
                          "workload (bf16 weights; the default run times it in bf16 and with "
                          "MXFP8 activations)")
+    ap.add_argument("--mover-sweep", action="store_true",
+                    help="only time the persistent kernel's mover counts against the stream path "
+                         "on the streaming workload, and print them as one JSON line")
     ap.add_argument("--tune", action="store_true",
                     help="also run mok_tune_forward over minibatches (and mover counts) per mode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -633,6 +685,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "reps": 3}), flush=True)
+        return
+    if args.mover_sweep:
+        print(json.dumps({"mover_sweep_ms_per_macrobatch": mover_sweep(mok, DeviceWorkload)}),
+              flush=True)
         return
     t = time.time()
     wl = make_workload(args.workload)

@@ -205,8 +205,9 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
 // [x * P, (x + 1) * P).
 // Half-width tail (`halves`, the y-storing epilogues): where no split into
 // pieces is taken and the r tail tiles fill at most half of the XCD's CUs,
-// each is run as two tiles of 128 columns instead, by the workgroups that
-// follow the whole tiles.  A round of tiles runs as long as a full one however
+// each is run as two tiles of 128 columns instead (the first half of these
+// jobs before the whole tiles, the rest after them).  A round of tiles runs as
+// long as a full one however
 // few of them there are (measured on the Kimi-shaped down GEMM, 256 tiles per
 // round: 3.5 rounds took as long as 4); a half-width tile does half the MFMAs
 // on the same token panel and needs no partial sums.  Every output element is
@@ -249,11 +250,22 @@ __device__ __forceinline__ bool decode_job(const GemmParams& p, int nk, int bid,
   if (halves && !pieces && p.n_cus >= kXcds) {
     const int P = p.n_cus / kXcds, rx = c % P;
     const int gx = (static_cast<int>(gridDim.x) - x + kXcds - 1) / kXcds;  // workgroups of XCD x
-    if (rx > 0 && 2 * rx <= P && gx >= c + rx && i >= c - rx) {
-      const int u = i - (c - rx);
-      if ((u >> 1) >= rx) return false;
-      t = c - rx + (u >> 1);
-      j.half = 1 + (u & 1);
+    if (rx > 0 && 2 * rx <= P && gx >= c + rx) {
+      // Dispatch order of XCD x: the first rx half-width jobs, the c - rx
+      // whole tiles, then the other rx half-width jobs (u = 0 .. 2 rx - 1
+      // numbers the halves of the tail tiles).  The CUs that start with a
+      // half-width job stay half a tile ahead of the others until the end,
+      // so the rounds' epilogue stores and first loads are spread over two
+      // half-size bursts instead of one that all CUs of the XCD wait on.
+      int u = -1;
+      if (i < rx) u = i;
+      else if (i >= c) u = i - c + rx;
+      else t = i - rx;
+      if (u >= 2 * rx) return false;
+      if (u >= 0) {
+        t = c - rx + (u >> 1);
+        j.half = 1 + (u & 1);
+      }
     }
   }
   if (t >= c) return false;
