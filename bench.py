@@ -38,9 +38,9 @@ BENCH_MAX_ROWS = 8192         # row capacity handed to the layer (= routed rows 
 # scaled by 2.0 and WRITE_SIZE by 1.0: what the counters read for a plain 1 GiB copy), keyed by
 # workload and by a hash of the GEMM sources they were taken on; any other source gives null.
 GATE_UP_TRAFFIC = {
-    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("d48e4fc5058446b6", 740615881),
-    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d48e4fc5058446b6", 1017784581),
-    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("d48e4fc5058446b6", 382117120),
+    "kimi_share_R8192_H7168_I2048_E384_k8_local8": ("136c9b7ea24adaa0", 740556123),
+    "kimi_zipf_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("136c9b7ea24adaa0", 1016708215),
+    "kimi_full_mxfp8_R8192_H7168_I2048_E384_k8_local8": ("136c9b7ea24adaa0", 382201381),
 }
 GEMM_SOURCES = ("token_dispatch_grouped_top_amd/csrc/gemm_tile.h",
                 "token_dispatch_grouped_top_amd/csrc/gemm.hip",
