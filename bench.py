@@ -569,6 +569,8 @@ def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
         st2 = Step(dw2, cap)
         cs = config_summary(wl2, st2, measure(st2, steps, warm))
         cs["workload"] = wl2.name
+        if not wl2.routing_from_logits:   # the merge of every routed slot as one kernel
+            cs["merge_all_slots"] = time_merge_all_slots(mok, st2)
         if wl2.routing_from_logits:       # the whole layer as one call from the logits
             d = dw2.desc(max_rows=cap, weights_packed=1)
             w_gu, w_d = dw2.weights(d)
