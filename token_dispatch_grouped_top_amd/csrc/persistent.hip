@@ -126,11 +126,6 @@ struct CtlView {
   __device__ PMacro* pm() const { return reinterpret_cast<PMacro*>(b + (int_words(W) + 3) / 4 * 4); }
 };
 
-__global__ void k_fill(int32_t* p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = 0;
-}
 
 // Builds windows, the worker tile sequence and the mover item list on the
 // device from the schedules (no host round trip).
@@ -145,10 +140,16 @@ __host__ __device__ inline size_t plan_lds_words(int n_macro, int n_local, int m
   return static_cast<size_t>(n_macro) * (n_local + 1) + 8 * static_cast<size_t>(max_win) + kMaxMacro;
 }
 
-__global__ __launch_bounds__(256) void k_plan(const PKArgs a) {
-  extern __shared__ int32_t plan_lds[];
+// Block 0 of k_setup: clears the control block (every counter at zero), then
+// plans into it.
+__device__ __forceinline__ void plan_block(const PKArgs& a, int32_t* plan_lds) {
   __shared__ int32_t sh_w, sh_ne, sh_ni, sh_fail;
   const int tid = threadIdx.x, nl1 = a.n_local + 1, MW = a.max_win;
+  {
+    const int64_t words = static_cast<int64_t>(CtlView::words(MW));
+    for (int64_t i = tid; i < words; i += blockDim.x) a.ctl[i] = 0;
+    __syncthreads();                 // the plan below writes into the cleared block
+  }
   int32_t* offs = plan_lds;                                   // [n_macro][n_local + 1]
   int32_t* wm = offs + a.n_macro * nl1;                       // windows: macrobatch,
   int32_t* ws0 = wm + MW;                                     //   first slot,
@@ -497,15 +498,12 @@ void k_persist(const PKArgs a) {
 
 }  // namespace
 
-// Merge plans of the group's macrobatches (launch_merge_plan's records, one
-// launch for all of them): blockIdx.y = macrobatch.  Slots s < min(R, cap):
-// a plan holds cap records (with R > cap the launch computes nothing and
+// Merge plan record of slot s of one macrobatch (launch_merge_plan's records;
+// k_setup writes those of all the group's macrobatches).  Slots s < min(R,
+// cap): a plan holds cap records (with R > cap the set-up plans nothing and
 // raises the capacity status; records past cap would overwrite the next
 // workspace region, the control block).
-__global__ __launch_bounds__(256)
-void k_merge_plans(const PKArgs a) {
-  const PMacro pm = a.mb[blockIdx.y];
-  const int64_t s = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void merge_plan_slot(const PKArgs& a, const PMacro& pm, int64_t s) {
   if (s >= pm.offsets[a.n_local] || s >= a.cap) return;
   const int32_t asg = pm.aos[s];
   const int64_t t = asg / a.k;
@@ -520,6 +518,24 @@ void k_merge_plans(const PKArgs a) {
                      __float_as_uint(pm.gate[asg]), 0u);
   }
   pm.plan[s] = rec;
+}
+
+// The set-up of a group of macrobatches in one launch: block 0 clears the
+// control block and plans the windows, the worker tile sequence and the mover
+// items (plan_block); blocks 1 .. gn * mb_blocks write the merge plans,
+// mb_blocks blocks of 256 slots per macrobatch.  (Three launches before:
+// a fill, the plan, the merge plans.)
+__global__ __launch_bounds__(256)
+void k_setup(const PKArgs a, int32_t mb_blocks) {
+  extern __shared__ int32_t plan_lds[];
+  if (blockIdx.x == 0) {
+    plan_block(a, plan_lds);
+    return;
+  }
+  const int b = static_cast<int>(blockIdx.x) - 1, m = b / mb_blocks;
+  if (m >= a.n_macro) return;
+  const PMacro pm = a.mb[m];
+  merge_plan_slot(a, pm, static_cast<int64_t>(b % mb_blocks) * blockDim.x + threadIdx.x);
 }
 
 size_t persistent_ws_bytes(int64_t total_windows) {
@@ -560,13 +576,10 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     k.ring = a.ring; k.ring_sc = a.ring_sc; k.act = a.act; k.act_sc = a.act_sc;
     k.act_rows = a.act_rows; k.status = a.status; k.ctl = static_cast<int32_t*>(a.pers_ws);
     k.timeout_ticks = timeout_us * 100;           // s_memrealtime runs at 100 MHz
-    const int64_t words = static_cast<int64_t>(CtlView::words(k.max_win));
-    hipLaunchKernelGGL(k_fill, dim3(static_cast<unsigned>((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
-                       dim3(256), 0, s, k.ctl, words);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(256),
-                       plan_lds_words(gn, a.n_local, k.max_win) * sizeof(int32_t), s, k);
-    hipLaunchKernelGGL(k_merge_plans, dim3(static_cast<unsigned>((a.cap + 255) / 256),
-                                           static_cast<unsigned>(gn)), dim3(256), 0, s, k);
+    const int32_t mb_blocks = static_cast<int32_t>((a.cap + 255) / 256);
+    hipLaunchKernelGGL(k_setup, dim3(static_cast<unsigned>(1 + static_cast<int64_t>(gn) * mb_blocks)),
+                       dim3(256), plan_lds_words(gn, a.n_local, k.max_win) * sizeof(int32_t), s, k,
+                       mb_blocks);
     if (hipGetLastError() != hipSuccess) return MOK_ERR_HIP;
     // window 0 of the group: the first macrobatch's slots [0, M) into ring half 0
     const MacroBuffers& b0 = a.mb[g0];
