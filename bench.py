@@ -131,9 +131,11 @@ class Step:
             mok.mok_route_topk(dw.logits, self.route_T, self.route_E, wl.k, self.r_idx, self.r_gate)
         rec(1)
         idx, gate = dw.topk_idx, dw.topk_gate
-        mok.mok_build_schedule(idx, wl.T, wl.k, wl.expert_base, wl.n_local, self.counts,
-                               self.offsets, self.soa, self.aos, self.sched_ws)
-        mok.mok_build_windows(self.offsets, wl.n_local, self.M, self.nwin, self.win)
+        # the schedule and its window table (two launches: count, then the
+        # scatter whose first block also writes the windows)
+        mok.mok_build_schedule_windows(idx, wl.T, wl.k, wl.expert_base, wl.n_local, self.counts,
+                                       self.offsets, self.soa, self.aos, self.M, self.nwin,
+                                       self.win, self.sched_ws)
         rec(2)
         mok.mok_dispatch_gather(dw.x, wl.H, wl.k, self.aos, self.offsets, wl.n_local, 0, self.cap,
                                 self.ring, self.ring_sc, self.cap, wl.act_format, self.status)

@@ -201,6 +201,19 @@ int32_t mok_choose_minibatch(int32_t n_cus, int32_t tile_m, int32_t tile_n,
 mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M,
                              int32_t nwin, int32_t* win_seg, hipStream_t stream);
 
+/* mok_build_schedule and mok_build_windows in one call, as the fused layer
+ * runs them (article, layout-planning and minibatch paragraphs): the same
+ * counts, offsets, slot_of_assign, assign_of_slot and win_seg, bit for bit,
+ * in two launches instead of three (the scatter's first block also writes
+ * the window table once the offsets are known).  Arguments as in the two
+ * calls; ws as for mok_build_schedule; nwin may be 0 (win_seg unused). */
+mok_status mok_build_schedule_windows(const int32_t* topk_idx, int32_t T, int32_t k,
+                                      int32_t expert_base, int32_t n_local, int32_t* counts,
+                                      int32_t* offsets, int32_t* slot_of_assign,
+                                      int32_t* assign_of_slot, int32_t M, int32_t nwin,
+                                      int32_t* win_seg, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* Pull dispatch (article, pull-dispatch paragraph).  For each slot s in
  * [slot_begin, min(slot_end, R)) with R = offsets[n_local]: ring row
  * s % ring_slots receives the row of token assign_of_slot[s] / k of src

@@ -52,6 +52,11 @@ def test_invalid_arguments_rejected_without_launch():
         mok.MOK_ERR_UNSUPPORTED
     assert L.mok_build_windows(0, 8, 64, 4, 1, None) == E
     assert L.mok_build_windows(1, 8, 0, 4, 1, None) == E
+    sw = L.mok_build_schedule_windows
+    assert sw(1, 4, 2, 0, 8, 1, 1, 1, 1, 0, 4, 1, ws, 1 << 20, None) == E          # M = 0
+    assert sw(1, 4, 2, 0, 8, 1, 1, 1, 1, 64, 4, None, ws, 1 << 20, None) == E      # no win_seg
+    assert sw(1, 4, 2, 0, 0, 1, 1, 1, 1, 64, 4, 1, ws, 1 << 20, None) == E         # n_local 0
+    assert sw(1, 4, 2, 0, 8, 1, 1, 1, 1, 64, 4, 1, ws, 1, None) == mok.MOK_ERR_WORKSPACE
     tok = mok.mok_tokens(1, 1, 16)
     assert L.mok_dispatch_gather(C.byref(tok), 60, 2, 1, 1, 8, 0, 10, 1, 1, 4, 1, None, None) == E
     assert L.mok_dispatch_gather(C.byref(tok), 64, 2, 1, 1, 8, 5, 4, 1, None, 4, 0, None, None) == E

@@ -88,6 +88,26 @@ def test_schedule_pool_and_windows():
         assert np.array_equal(to_host(win), oracle.windows(ref["offsets"], M, nwin)), M
     assert np.array_equal(to_host(s["soa"]), ref["slot_of_assign"])
     assert np.array_equal(to_host(s["aos"])[:ref["R"]], ref["assign_of_slot"])
+    # schedule and windows in one call: the same arrays, bit for bit
+    A = wl.T * wl.k
+    ws = torch.empty(mok.mok_schedule_workspace_size(wl.T, wl.k, wl.n_local), dtype=torch.uint8,
+                     device="cuda")
+    for M in (64, 2243):
+        nwin = min(-(-A // M), 200)
+        counts = torch.full((wl.n_local,), -7, dtype=torch.int32, device="cuda")
+        offs = torch.full((wl.n_local + 1,), -7, dtype=torch.int32, device="cuda")
+        soa = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+        aos = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+        win = torch.full((nwin, wl.n_local + 1), -7, dtype=torch.int32, device="cuda")
+        mok.mok_build_schedule_windows(dw.topk_idx, wl.T, wl.k, wl.expert_base, wl.n_local, counts,
+                                       offs, soa, aos, M, nwin, win, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(counts), np.diff(ref["offsets"]))
+        assert np.array_equal(to_host(offs), ref["offsets"])
+        assert np.array_equal(to_host(soa), ref["slot_of_assign"])
+        assert np.array_equal(to_host(aos)[:ref["R"]], ref["assign_of_slot"])
+        assert np.all(to_host(aos)[ref["R"]:] == -7)
+        assert np.array_equal(to_host(win), oracle.windows(ref["offsets"], M, nwin)), M
 
 
 @pytest.mark.parametrize("mx", [False, True])

@@ -65,6 +65,8 @@ _SIGS = {
     "mok_build_schedule_noalloc": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "mok_choose_minibatch": (_I32, [_I32, _I32, _I32, _I32, _I64]),
     "mok_build_windows": (C.c_int, [_P, _I32, _I32, _I32, _P, _P]),
+    "mok_build_schedule_windows": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32,
+                                             _I32, _P, _P, _SZ, _P]),
     "mok_dispatch_gather": (C.c_int, [_TOK, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32,
                                       _I32, _P, _P]),
     "mok_expert_ffn": (C.c_int, [_DESC, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P,
@@ -225,6 +227,17 @@ def mok_build_schedule_noalloc(topk_idx, T: int, k: int, expert_base: int, n_loc
 
 def mok_choose_minibatch(n_cus: int, tile_m: int, tile_n: int, n_out: int, rows: int = 0) -> int:
     return int(_lib.mok_choose_minibatch(n_cus, tile_m, tile_n, n_out, rows))
+
+
+def mok_build_schedule_windows(topk_idx, T: int, k: int, expert_base: int, n_local: int, counts,
+                               offsets, slot_of_assign, assign_of_slot, M: int, nwin: int,
+                               win_seg, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.mok_build_schedule_windows(_ptr(topk_idx), T, k, expert_base, n_local,
+                                           _ptr(counts), _ptr(offsets), _ptr(slot_of_assign),
+                                           _ptr(assign_of_slot), M, nwin, _ptr(win_seg), _ptr(ws),
+                                           ws_bytes, _stream(stream)), "mok_build_schedule_windows")
 
 
 def mok_build_windows(offsets, n_local: int, M: int, nwin: int, win_seg, stream=None) -> None:

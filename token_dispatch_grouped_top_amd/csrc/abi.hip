@@ -304,6 +304,28 @@ int32_t mok_choose_minibatch(int32_t n_cus, int32_t tile_m, int32_t tile_n, int3
   return static_cast<int32_t>(m);
 }
 
+mok_status mok_build_schedule_windows(const int32_t* topk_idx, int32_t T, int32_t k,
+                                      int32_t expert_base, int32_t n_local, int32_t* counts,
+                                      int32_t* offsets, int32_t* slot_of_assign,
+                                      int32_t* assign_of_slot, int32_t M, int32_t nwin,
+                                      int32_t* win_seg, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (T < 0 || k < 1 || n_local < 1 || n_local > 256 || M < 1 || nwin < 0)
+    return MOK_ERR_INVALID_ARG;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A >= (1ll << 31)) return MOK_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !ws || (nwin > 0 && !win_seg)) return MOK_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !slot_of_assign || !assign_of_slot)) return MOK_ERR_INVALID_ARG;
+  if (ws_bytes < sched_ws_bytes(A, n_local)) return MOK_ERR_WORKSPACE;
+  SchedWs w = sched_ws_carve(ws, A, n_local);
+  // the fused layer's two launches: count, then the scatter whose block 0
+  // also writes the window table (no capacity bound here)
+  return hip_status(launch_route_schedule(nullptr, 0, nullptr, const_cast<int32_t*>(topk_idx), T, k,
+                                          expert_base, n_local, counts, offsets, slot_of_assign,
+                                          assign_of_slot, w, M, nwin, win_seg, 0x7fffffff, nullptr,
+                                          stream, false));
+}
+
 mok_status mok_build_windows(const int32_t* offsets, int32_t n_local, int32_t M, int32_t nwin,
                              int32_t* win_seg, hipStream_t stream) {
   if (!offsets || n_local < 1 || M < 1 || nwin < 0) return MOK_ERR_INVALID_ARG;
