@@ -274,6 +274,38 @@ def mover_sweep(mok, DeviceWorkload) -> dict:
     return res
 
 
+def measured_peaks(reps: int = 10) -> dict:
+    """Measured references on this GPU: a plain 1 GiB device-to-device copy
+    (torch copy_, bytes read + written over its time: the HBM rate a pure
+    stream reaches here) and a dense bf16 GEMM from the vendor library
+    (torch.matmul on contiguous 8192 x 8192 x 8192 operands, hipBLASLt)."""
+    import numpy as np
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]))
+    copy_ms = timed(lambda: dst.copy_(src))
+    mm_ms = timed(lambda: torch.matmul(a, b))
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_1GiB_GBps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "hipblaslt_bf16_8192cube_tflops": round(2 * 8192 ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+
+
 def time_router_gemm(mok, wl, reps: int = 20):
     """mok_route_topk_gemm on this workload's routed tokens' shape (T_route x H
     against E router rows, seeded N(0, 1) tokens and N(0, 1/H) router
@@ -770,6 +802,9 @@ def main():
         log(f"[bench] merge of all {R} slots (mok_combine_slots): {merge_all['ms'] * 1e3:.1f} us, "
             f"{merge_all['GBps']:.0f} GB/s, {merge_all['frac_hbm']:.3f} of HBM")
 
+    peaks = measured_peaks()
+    log(f"[bench] measured references: {peaks}")
+
     router = time_router_gemm(mok, wl)
     log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
         f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
@@ -824,6 +859,12 @@ def main():
         "combine_GBps": round(rr["combine_GBps"], 1),
         "combine_frac_hbm": round(rr["combine_GBps"] / PEAK_HBM_GBS, 4),
         "merge_all_slots": merge_all,
+        # the same rates against what this GPU measures for a plain copy and a dense
+        # library GEMM (context beside the nominal peaks)
+        "measured_peaks": dict(peaks, gate_up_vs_hipblaslt=round(gu_tf / peaks[
+            "hipblaslt_bf16_8192cube_tflops"], 4), gather_vs_copy=round(rr["dispatch_GBps"] / peaks[
+            "hbm_copy_1GiB_GBps"], 4), merge_all_vs_copy=(round(merge_all["GBps"] / peaks[
+            "hbm_copy_1GiB_GBps"], 4) if merge_all else None)),
         "schedule_share": round(per["schedule"] / wall_ms, 4),
         # the layer against its roofline: both GEMMs at the MFMA peak plus the
         # gather and merge bytes at the HBM peak, over the timed wall
