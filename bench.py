@@ -604,7 +604,11 @@ def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
         cs = config_summary(wl2, st2, measure(st2, steps, warm))
         cs["workload"] = wl2.name
         if not wl2.routing_from_logits:   # the merge of every routed slot as one kernel
-            cs["merge_all_slots"] = time_merge_all_slots(mok, st2)
+            ma = time_merge_all_slots(mok, st2)
+            cs["merge_all_slots"] = ma
+            cs["step_merge_multi_GBps"] = cs["combine_GBps"]
+            cs["step_merge_multi_frac_hbm"] = cs["combine_frac_hbm"]
+            cs["combine_GBps"], cs["combine_frac_hbm"] = ma["GBps"], ma["frac_hbm"]
         if wl2.routing_from_logits:       # the whole layer as one call from the logits
             d = dw2.desc(max_rows=cap, weights_packed=1)
             w_gu, w_d = dw2.weights(d)
@@ -856,8 +860,14 @@ def main():
                         "down_frac_of_peak": round(rr["down_tflops"] / peak, 4)},
         "dispatch_GBps": round(rr["dispatch_GBps"], 1),
         "dispatch_frac_hbm": round(rr["dispatch_GBps"] / PEAK_HBM_GBS, 4),
-        "combine_GBps": round(rr["combine_GBps"], 1),
-        "combine_frac_hbm": round(rr["combine_GBps"] / PEAK_HBM_GBS, 4),
+        # combine: the weighted merge of every routed slot as one kernel (merge_all_slots);
+        # the layer step splits it between the down GEMM's epilogue (single-slot tokens)
+        # and a merge of the rest, whose own rate is step_merge_multi_*
+        "combine_GBps": merge_all["GBps"] if merge_all else round(rr["combine_GBps"], 1),
+        "combine_frac_hbm": (merge_all["frac_hbm"] if merge_all
+                             else round(rr["combine_GBps"] / PEAK_HBM_GBS, 4)),
+        "step_merge_multi_GBps": round(rr["combine_GBps"], 1),
+        "step_merge_multi_frac_hbm": round(rr["combine_GBps"] / PEAK_HBM_GBS, 4),
         "merge_all_slots": merge_all,
         # the same rates against what this GPU measures for a plain copy and a dense
         # library GEMM (context beside the nominal peaks)
