@@ -20,8 +20,9 @@
 //     (rows (w % 2) * M + s - s0) and the same half of the activation buffer;
 //   - movers walk an item list: gather window w (after the gate/up tiles of
 //     window w - 2 freed the ring half), and merge macrobatch m (after every
-//     down tile of m); merges of m are placed after the second window of m + 1
-//     so they run while the workers compute m + 1;
+//     down tile of m), in the order in which the workers free them, so each
+//     gather starts as soon as its ring half is free and each merge runs
+//     while the workers compute the next macrobatch;
 //   - workers take tiles from a per-XCD queue over the sequence
 //     G1(0), G1(1), G2(0), G1(2), G2(1), ..., G2(W-1) (G1 = gate/up + SwiGLU,
 //     G2 = down); each XCD owns a contiguous eighth of every window's tiles so
@@ -33,8 +34,8 @@
 //     waits cannot cycle; every wait is bounded by a timeout after which the
 //     kernel sets MOK_ERR_DEVICE, raises an abort flag seen by all waits, and
 //     every workgroup returns.
-// Counters live in the workspace and are cleared by a fill kernel before the
-// plan kernel.  Each XCD has its own L2, so an agent-scope release writes the
+// Counters live in the workspace and are cleared by the set-up launch
+// (k_setup) before it plans.  Each XCD has its own L2, so an agent-scope release writes the
 // XCD's dirty L2 lines back and an agent-scope acquire invalidates the XCD's
 // L2: both are paid once per signal / satisfied wait, never per poll.  A
 // producer workgroup publishes with a barrier and one release add by thread 0;
@@ -188,17 +189,22 @@ __device__ __forceinline__ void plan_block(const PKArgs& a, int32_t* plan_lds) {
         if (w >= 1) ent[ne++] = 2 * (w - 1) + 1;
       }
       if (W >= 1) ent[ne++] = 2 * (W - 1) + 1;
-      int next_merge = 0, w = 0;
-      for (int m = 0; m < a.n_macro; ++m) {
-        const int32_t R = offs[m * nl1 + a.n_local];
-        const int nw = (R + a.M - 1) / a.M;
-        for (int b = 0; b < nw; ++b, ++w) {
-          items[ni++] = w;
-          if (b >= 1 || nw == 1)
-            while (next_merge < m) items[ni++] = -(next_merge++) - 1;
-        }
+      // Mover items in the order in which the worker sequence frees them:
+      // the gather of w waits for G1(w - 2) (its ring half), the merge of m
+      // for G2 of m's last window.  A mover then never waits on an item
+      // while a later one of its list is ready, and every gather starts as
+      // soon as its ring half is free.  Positions in the sequence: G1(0) at
+      // 0, G1(v) at 2v - 1, G2(v) at 2v + 2, the last G2 at 2W - 1.
+      auto g1pos = [](int v) { return v == 0 ? 0 : 2 * v - 1; };
+      auto g2pos = [W](int v) { return v == W - 1 ? 2 * W - 1 : 2 * v + 2; };
+      int gw = 0, mm = 0, wi = 0;
+      while (gw < W || mm < a.n_macro) {
+        while (wi < W && wm[wi] <= mm) ++wi;          // windows of macrobatches <= mm
+        const int kg = gw >= W ? 0x7fffffff : gw < 2 ? -1 : g1pos(gw - 2);
+        const int km = mm >= a.n_macro ? 0x7fffffff : wi > 0 ? g2pos(wi - 1) : -1;
+        if (kg <= km) items[ni++] = gw++;
+        else items[ni++] = -(mm++) - 1;
       }
-      while (next_merge < a.n_macro) items[ni++] = -(next_merge++) - 1;
     }
     sh_fail = fail; sh_w = W; sh_ne = ne; sh_ni = ni;
   }
