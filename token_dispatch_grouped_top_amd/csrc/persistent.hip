@@ -118,7 +118,7 @@ struct CtlView {
   __device__ int xstride() const { return 2 * W + 1; }
   // [2W] sequence entries: 2 * window + (0 gate/up, 1 down)
   __device__ int32_t* ent() const { return xseq() + 8 * (2 * W + 1); }
-  // [W + kMaxMacro] mover items: window >= 0, merge m as -m - 1
+  // [W + kMaxMacro] mover items: window w >= 1, merge of m < n_macro - 1 as -m - 1
   __device__ int32_t* items() const { return ent() + 2 * W; }
   // [W][2][8] tiles done per window, phase (gate/up, down) and XCD
   __device__ int32_t* xdone() const { return items() + W + kMaxMacro; }
@@ -202,8 +202,15 @@ __device__ __forceinline__ void plan_block(const PKArgs& a, int32_t* plan_lds) {
         while (wi < W && wm[wi] <= mm) ++wi;          // windows of macrobatches <= mm
         const int kg = gw >= W ? 0x7fffffff : gw < 2 ? -1 : g1pos(gw - 2);
         const int km = mm >= a.n_macro ? 0x7fffffff : wi > 0 ? g2pos(wi - 1) : -1;
-        if (kg <= km) items[ni++] = gw++;
-        else items[ni++] = -(mm++) - 1;
+        // window 0 is gathered before the kernel, the last macrobatch merged
+        // after it (launches of their own at full occupancy)
+        if (kg <= km) {
+          if (gw > 0) items[ni++] = gw;
+          ++gw;
+        } else {
+          if (mm < a.n_macro - 1) items[ni++] = -mm - 1;
+          ++mm;
+        }
       }
     }
     sh_fail = fail; sh_w = W; sh_ne = ne; sh_ni = ni;
@@ -331,105 +338,212 @@ __device__ __forceinline__ void gather_window(const PKArgs& a, const CtlView& c,
   }
 }
 
-// Merge of macrobatch m by the waves first, first + step, ... after every
-// down tile of its windows is done.  kFast: see combine_token.
+// Merge of macrobatch m by the waves first, first + step, ... once every
+// down tile of its windows is done (item_ready).  kFast: see combine_token.
 template <bool kFast>
-__device__ __forceinline__ bool merge_macro(const PKArgs& a, const CtlView& c, int32_t* sh, int m,
+__device__ __forceinline__ void merge_macro(const PKArgs& a, const CtlView& c, int m,
                                             int64_t first, int64_t step) {
-  const int W = *c.n_windows();
-  for (int w = 0; w < W; ++w)
-    if (c.win_m()[w] == m && !wait_geq(&c.dn_done()[w], xcds_of(c.win_nt2()[w]), c, a, sh)) return false;
   const PMacro pm = c.pm()[m];
   const int32_t R = pm.offsets[a.n_local];
   for (int64_t s = first; s < R; s += step)             // single-slot tokens: by the down tiles
     merge_slot<kFast>(pm.y, a.cap, pm.aos[s], pm.soa, pm.gate, s, a.k, a.H, pm.out_parts,
                       pm.out_n_part, pm.out_part_rows, a.status, true);
+}
+
+__device__ __forceinline__ int32_t ld_relaxed(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0, no wait: whether mover item `item` can start (window >= 0: its
+// ring half was freed by G1(w - 2); merge -m - 1: every down tile of m is
+// done; the windows of m are contiguous).
+__device__ __forceinline__ bool item_ready(const PKArgs& a, const CtlView& c, int item) {
+  if (item >= 0)
+    return item < 2 || ld_relaxed(&c.gu_done()[item - 2]) >= xcds_of(c.win_nt1()[item - 2]);
+  const int m = -item - 1, W = *c.n_windows();
+  int lo = 0, hi = W;                            // first window of m
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (c.win_m()[mid] < m) lo = mid + 1; else hi = mid;
+  }
+  for (int w = lo; w < W && c.win_m()[w] == m; ++w)
+    if (ld_relaxed(&c.dn_done()[w]) < xcds_of(c.win_nt2()[w])) return false;
   return true;
 }
 
-// Movers: the item list in order, except window 0 (gathered by every
-// workgroup at the start) and the last macrobatch's merge, which every
-// workgroup shares once the GEMMs are done (nothing else runs then, so it is
-// spread over all CUs).  Between those two points the movers run beside the
-// GEMM workers and keep a moderate pace: faster movers there took HBM / L2
-// bandwidth from the workers' operand stream and slowed the layer.  After
-// their last item they take GEMM tiles like the workers (with a single
-// window they have no item at all, and the GEMMs get every CU).  False when
-// the kernel aborts.
-template <bool A_MX>
-__device__ __forceinline__ bool mover(const PKArgs& a, const CtlView& c, int32_t* sh) {
-  const int wave = threadIdx.x / kWave;
-  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t nmw = static_cast<int64_t>(a.n_move) * 4;
-  const int ni = *c.n_items();
-  for (int it = 0; it < ni; ++it) {
-    const int item = c.items()[it];
-    if (item >= 0) {
-      const int w = item;
-      if (w == 0) continue;
-      if (w >= 2 && !wait_geq(&c.gu_done()[w - 2], xcds_of(c.win_nt1()[w - 2]), c, a, sh)) return false;
-      gather_window<A_MX>(a, c, w, mw, nmw);
-      signal_add(&c.gathered()[w]);
-    } else {
-      const int m = -item - 1;
-      if (m == a.n_macro - 1) continue;       // shared by every workgroup at the end
-      if (!merge_macro<false>(a, c, sh, m, mw, nmw)) return false;
-      signal_add(&c.merged()[m]);
-    }
+// Thread 0, no wait: whether every dependency of a tile of entry (w, down) is
+// met.  G1(w): the gather of w (window 0 is in the ring before the kernel)
+// and G2(w - 2) (activation half).  G2(w): G1(w) and the merge of m - 2
+// (return area).
+__device__ __forceinline__ bool deps_met(const PKArgs& a, const CtlView& c, int w, int down) {
+  if (!down)
+    return (w == 0 || ld_relaxed(&c.gathered()[w]) >= a.n_move) &&
+           (w < 2 || ld_relaxed(&c.dn_done()[w - 2]) >= xcds_of(c.win_nt2()[w - 2]));
+  const int m = c.win_m()[w];
+  return ld_relaxed(&c.gu_done()[w]) >= xcds_of(c.win_nt1()[w]) &&
+         (m < 2 || ld_relaxed(&c.merged()[m - 2]) >= a.n_move);
+}
+
+// Last sequence entry whose prefix (in the XCD's share table xs) is <= lt.
+__device__ __forceinline__ int entry_of(const int32_t* xs, int ne, int32_t lt) {
+  int lo = 0, hi = ne - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (xs[mid] <= lt) lo = mid; else hi = mid - 1;
   }
-  return true;
+  return lo;
 }
 
 // Operand formats of a persistent launch: bf16 activations and weights;
 // MXFP8 activations with bf16 weights; MXFP8 activations and weights.
 enum PFormat { kPBf16 = 0, kPMxAct = 1, kPMx8 = 2 };
 
-// Workers: GEMM tiles from the XCD's queue; false when the kernel aborts.
+// One loop per workgroup.
+//   Movers (workgroups 0 .. n_move - 1) walk the item list, except window 0
+//   (gathered by a launch of its own before the kernel) and the last
+//   macrobatch's merge (a launch of its own after it: nothing else runs
+//   then, so it gets every CU at full occupancy).  While their next item is
+//   not ready they take the XCD's next tile if it is a down tile whose
+//   dependencies are all met (a compare-and-swap on the queue counter, so a
+//   mover never holds a tile it would have to wait for, and its item waits
+//   at most one tile), else they poll.  Down tiles only: gate/up tiles are
+//   the next step after a gather on the workers' path, and with the Kimi-
+//   shaped share (K = 7168 against the down GEMM's 2048) each is 3.5 times
+//   longer; a mover that took them delayed the gathers of later windows.
+//   Beside the GEMM workers the movers keep a moderate pace: faster movers
+//   took HBM / L2 bandwidth from the workers' operand stream and slowed the
+//   layer.  After their last item (with a single window they have none) they
+//   take tiles like the workers.
+//   Workers take the XCD's next tile and wait for its dependencies.
 template <int F>
-__device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, int32_t* sh,
-                                             uint8_t* lds) {
+__global__ __launch_bounds__(256)
+void k_persist(const PKArgs a) {
+  constexpr bool A_MX = F != kPBf16;
+  constexpr int kLds0 = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
+  constexpr int kLds1 = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
+  constexpr int kLds = kLds1 > kMergeLds ? kLds1 : kMergeLds;     // the merging down epilogue
+  // One LDS array: with a second __shared__ object the compiler could no
+  // longer tell the GEMM's LDS reads from its direct-to-LDS loads and made
+  // every k-step wait for all loads in flight (vmcnt(0)).
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds + 16];
+  // The broadcast words share the first 16 bytes of the GEMM's LDS: every
+  // use is fenced by workgroup barriers from the tile that overwrites them
+  // (gemm_tile opens with one; signal_add / signal_tile close with one).
+  int32_t* sh = reinterpret_cast<int32_t*>(lds);
+  CtlView c(a.ctl, a.max_win);
   const int x = blockIdx.x % kXcds;
-  const int W = *c.n_windows(), ne = 2 * W;
+  // loop state in scalar registers (readfirstlane): the GEMM tile inside the
+  // loop needs every vector register
+  const int W = __builtin_amdgcn_readfirstlane(*c.n_windows()), ne = 2 * W;
   const int32_t* xs = c.xseq() + x * c.xstride();
-  const int32_t total = W > 0 ? xs[ne] : 0;
+  const int32_t total = W > 0 ? __builtin_amdgcn_readfirstlane(xs[ne]) : 0;
   const int n1 = (a.I + BN / 2 - 1) / (BN / 2), n2 = (a.H + BN - 1) / BN;
   int ready_g1 = -1, ready_g2 = -1;   // last window whose G1 / G2 dependencies were acquired
+  // A mover's next item and its last progress (for the wait bound) stay in
+  // the 16 bytes past the GEMM's LDS, so no register holds them across a
+  // GEMM tile.  Thread 0 writes both.
+  int32_t& sh_it = *reinterpret_cast<int32_t*>(lds + kLds);
+  uint64_t& sh_t0 = *reinterpret_cast<uint64_t*>(lds + kLds + 8);
+  if (threadIdx.x == 0) { sh_it = 0; sh_t0 = __builtin_amdgcn_s_memrealtime(); }
+  __syncthreads();
   while (true) {
-    if (threadIdx.x == 0)
-      sh[1] = __hip_atomic_fetch_add(&c.tile_ctr()[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    // uniform by construction (one value broadcast through LDS); saying so keeps
-    // everything derived from it -- tile coordinates, operand bases and the
-    // buffer descriptors -- in scalar registers, where the GEMM's main loop
-    // wants them (with a vector value the compiler re-derived the descriptors
-    // with v_readfirstlane in every k-step)
-    const int32_t lt = __builtin_amdgcn_readfirstlane(sh[1]);
-    __syncthreads();
-    if (lt >= total) return true;
-    int lo = 0, hi = ne - 1;                     // last entry whose prefix <= lt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (xs[mid] <= lt) lo = mid; else hi = mid - 1;
+    int32_t lt;
+    bool met = false;                 // the tile's dependencies are met and acquired
+    const int ni = static_cast<int>(blockIdx.x) < a.n_move
+                       ? __builtin_amdgcn_readfirstlane(*c.n_items()) : 0;
+    const int it = ni > 0 ? __builtin_amdgcn_readfirstlane(sh_it) : 0;
+    if (it < ni) {
+      const int item = __builtin_amdgcn_readfirstlane(c.items()[it]);
+      constexpr int32_t kItem = -1, kIdle = -2, kAbort = -3;
+      if (threadIdx.x == 0) {
+        int32_t r = kIdle;
+        if (item_ready(a, c, item)) {
+          r = kItem;
+        } else {
+          const int32_t cur = ld_relaxed(&c.tile_ctr()[x]);
+          if (cur < total) {
+            const int q = entry_of(xs, ne, cur);
+            const int ent = c.ent()[q];
+            int32_t expect = cur;
+            if ((ent & 1) && deps_met(a, c, ent >> 1, 1) &&
+                __hip_atomic_compare_exchange_strong(&c.tile_ctr()[x], &expect, cur + 1,
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+              r = cur;
+          }
+        }
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
+        if (r != kIdle) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          sh_t0 = now;
+        } else if (ld_relaxed(c.abort())) {
+          r = kAbort;
+        } else if (now - sh_t0 > a.timeout_ticks) {
+          __hip_atomic_store(c.abort(), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          set_status(a.status, MOK_ERR_DEVICE);
+          r = kAbort;
+        } else {
+          __builtin_amdgcn_s_sleep(1);
+        }
+        sh[1] = r;
+      }
+      __syncthreads();
+      const int32_t r = __builtin_amdgcn_readfirstlane(sh[1]);
+      __syncthreads();
+      if (r == kAbort) return;
+      if (r == kIdle) continue;
+      if (r == kItem) {
+        // every wave read sh_it before the barriers above; the next read
+        // follows the item's closing barrier (signal_add)
+        if (threadIdx.x == 0) sh_it = it + 1;
+        const int64_t mw = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+        const int64_t nmw = static_cast<int64_t>(a.n_move) * 4;
+        if (item >= 0) {
+          gather_window<A_MX>(a, c, item, mw, nmw);
+          signal_add(&c.gathered()[item]);
+        } else {
+          // 4 pieces per lane and slot (kFast): the 16 of the plain merge held
+          // 128 accumulators per lane in this loop beside the GEMM's state and
+          // pushed registers of every tile to scratch; the sums are the same
+          merge_macro<true>(a, c, -item - 1, mw, nmw);
+          signal_add(&c.merged()[-item - 1]);
+        }
+        continue;
+      }
+      lt = r;
+      met = true;
+    } else {
+      if (threadIdx.x == 0)
+        sh[1] = __hip_atomic_fetch_add(&c.tile_ctr()[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      // uniform by construction (one value broadcast through LDS); saying so
+      // keeps everything derived from it -- tile coordinates, operand bases and
+      // the buffer descriptors -- in scalar registers, where the GEMM's main
+      // loop wants them (with a vector value the compiler re-derived the
+      // descriptors with v_readfirstlane in every k-step)
+      lt = __builtin_amdgcn_readfirstlane(sh[1]);
+      __syncthreads();
+      if (lt >= total) return;
     }
+    const int lo = entry_of(xs, ne, lt);
     const int w = c.ent()[lo] >> 1, down = c.ent()[lo] & 1;
     const int32_t tk = down ? c.win_nt2()[w] : c.win_nt1()[w];
     const int32_t q = tk / kXcds, r = tk % kXcds;
     const int te = x * q + (x < r ? x : r) + (lt - xs[lo]);
     const int m = c.win_m()[w];
     bool ok = true;
-    if (!down && w != ready_g1) {
-      // window 0 is in the ring before the kernel starts (a gather launch of its own)
+    if (!met && !down && w != ready_g1) {
       ok = (w == 0 || wait_geq(&c.gathered()[w], a.n_move, c, a, sh)) &&
            (w < 2 || wait_geq(&c.dn_done()[w - 2], xcds_of(c.win_nt2()[w - 2]), c, a, sh));
       ready_g1 = w;
-    } else if (down && w != ready_g2) {
+    } else if (!met && down && w != ready_g2) {
       ok = wait_geq(&c.gu_done()[w], xcds_of(c.win_nt1()[w]), c, a, sh) &&
            (m < 2 || wait_geq(&c.merged()[m - 2], a.n_move, c, a, sh));
       ready_g2 = w;
     }
     int32_t* xcnt = c.xdone() + (2 * w + down) * kXcds + x;
     const int32_t xshare = share_of(tk, x);
-    if (!ok) return false;
+    if (!ok) return;
     // The control block is written during the kernel, so its loads are vector
     // loads, whose results the compiler keeps in VGPRs: every value the tile
     // derives from them (operand bases, buffer descriptors) would then be
@@ -479,27 +593,6 @@ __device__ __forceinline__ bool worker_tiles(const PKArgs& a, const CtlView& c, 
       signal_tile(xcnt, xshare, &c.dn_done()[w]);
     }
   }
-}
-
-template <int F>
-__global__ __launch_bounds__(256)
-void k_persist(const PKArgs a) {
-  constexpr bool A_MX = F != kPBf16;
-  constexpr int kLds0 = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
-  constexpr int kLds1 = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
-  constexpr int kLds = kLds1 > kMergeLds ? kLds1 : kMergeLds;     // the merging down epilogue
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
-  // The broadcast words share the first 16 bytes of the GEMM's LDS: every
-  // use is fenced by workgroup barriers from the tile that overwrites them
-  // (gemm_tile opens with one; signal_add closes each tile with one).
-  int32_t* sh = reinterpret_cast<int32_t*>(lds);
-  CtlView c(a.ctl, a.max_win);
-  // Window 0 is gathered before the kernel and the last macrobatch merged
-  // after it, by launches of their own at full occupancy: nothing else could
-  // run beside them, and one workgroup per CU moved rows at half the rate.
-  if (static_cast<int>(blockIdx.x) < a.n_move && !mover<A_MX>(a, c, sh)) return;
-  // workers from the start, movers after their items
-  worker_tiles<F>(a, c, sh, lds);
 }
 
 }  // namespace
