@@ -69,7 +69,8 @@ struct PMacro {
 
 struct PKArgs {
   PMacro mb[kMaxMacro];
-  int32_t n_macro, T, k, H, I, n_local, act_format, M, S, cap, n_move, max_win;
+  int32_t n_macro, T, k, H, I, n_local, act_format, M, S, cap, n_move, max_win, n_cus;
+  int32_t halves;           // the last down phase's tail may run as half-width tiles
   void* const* x_parts;
   int32_t x_n_part, x_part_rows;
   const uint16_t* w_gu;
@@ -127,6 +128,29 @@ struct CtlView {
   __device__ PMacro* pm() const { return reinterpret_cast<PMacro*>(b + (int_words(W) + 3) / 4 * 4); }
 };
 
+
+// XCD x's share of a phase of `tiles` tiles (a contiguous run of the tile list).
+__host__ __device__ __forceinline__ int32_t share_of(int32_t tiles, int x) {
+  return tiles / kXcds + (x < tiles % kXcds ? 1 : 0);
+}
+
+// Half-width tail of a one-window launch.  Its sequence is G1(0), G2(0): the
+// down tiles start together on an XCD's P = n_cus / 8 workgroups once every
+// gate/up tile is done, and the last r = c % P of the XCD's c down tiles would
+// make a round of their own with P - r CUs idle until the kernel ends.  Where
+// that round fills at most half of the CUs, its r tiles run as 2 r tiles of
+// 128 columns, as the standalone y-storing GEMMs do: the round takes half as
+// long, and every output element is summed by the same MFMAs in the same
+// order.  With several windows the down phases interleave with gate/up tiles
+// and the rounds do not start together: the same rule there (on the last two
+// down phases) measured 1.6 % slower at two windows and no faster at eight,
+// while one window gained 2.3 % (the Kimi-shaped share at M = 4096 / 8192,
+// A/B in one box).  Returns r (the tiles split), or 0.
+__host__ __device__ __forceinline__ int32_t tail_halves(int W, int32_t nt_down, int x, int P) {
+  if (W != 1 || P <= 0) return 0;
+  const int32_t c = share_of(nt_down, x), rx = c % P;
+  return (rx > 0 && 2 * rx <= P) ? rx : 0;
+}
 
 // Builds windows, the worker tile sequence and the mover item list on the
 // device from the schedules (no host round trip).
@@ -226,12 +250,14 @@ __device__ __forceinline__ void plan_block(const PKArgs& a, int32_t* plan_lds) {
   }
   const int W = sh_w, ne = sh_ne, ni = sh_ni;
   if (tid < kXcds) {                                          // XCD tid's share prefix
+    // the last entry (G2(W - 1)) holds r more jobs where its tail runs as halves
+    const int32_t hx = W > 0 && a.halves ? tail_halves(W, wn2[W - 1], tid, a.n_cus / kXcds) : 0;
     int32_t acc = 0;
     for (int q = 0; q < ne; ++q) {
       const int w = ent[q] >> 1;
       const int32_t tk = (ent[q] & 1) ? wn2[w] : wn1[w];
       c.xseq()[tid * c.xstride() + q] = acc;
-      acc += tk / kXcds + (tid < tk % kXcds ? 1 : 0);
+      acc += share_of(tk, tid) + (q == ne - 1 ? hx : 0);
     }
     c.xseq()[tid * c.xstride() + ne] = acc;
   }
@@ -300,9 +326,6 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 // phase counter, whose write-back covers every tile of that XCD: their stores
 // reached the same L2 before their counts did.  Consumers wait for the number
 // of XCDs that hold tiles of the phase (xcds_of).
-__device__ __forceinline__ int32_t share_of(int32_t tiles, int x) {
-  return tiles / kXcds + (x < tiles % kXcds ? 1 : 0);
-}
 __device__ __forceinline__ int32_t xcds_of(int32_t tiles) {
   return tiles < kXcds ? tiles : kXcds;
 }
@@ -419,6 +442,11 @@ template <int F>
 __global__ __launch_bounds__(256)
 void k_persist(const PKArgs a) {
   constexpr bool A_MX = F != kPBf16;
+  // Half-width tail tiles (tail_halves) with bf16 or full-MXFP8 operands: with
+  // MXFP8 activations and bf16 weights the second tile variant took the loop
+  // past 256 VGPRs (12 bytes of scratch per lane), so that format keeps whole
+  // tiles (the host sets PKArgs::halves to match).
+  constexpr bool kHalves = F != kPMxAct;
   constexpr int kLds0 = Geo<false>::LDS > Geo<true>::LDS ? Geo<false>::LDS : Geo<true>::LDS;
   constexpr int kLds1 = kLds0 > GeoMX8::LDS ? kLds0 : GeoMX8::LDS;
   constexpr int kLds = kLds1 > kMergeLds ? kLds1 : kMergeLds;     // the merging down epilogue
@@ -529,7 +557,27 @@ void k_persist(const PKArgs a) {
     const int w = c.ent()[lo] >> 1, down = c.ent()[lo] & 1;
     const int32_t tk = down ? c.win_nt2()[w] : c.win_nt1()[w];
     const int32_t q = tk / kXcds, r = tk % kXcds;
-    const int te = x * q + (x < r ? x : r) + (lt - xs[lo]);
+    // the last entry's tail as half-width jobs (tail_halves): dispatch order
+    // of XCD x is the first hx halves, the c - hx whole tiles, then the other
+    // hx halves, as in the standalone GEMM (the CUs that start with a half
+    // stay half a tile ahead, so the round's stores and loads come in two
+    // half-size bursts)
+    const int32_t hx = kHalves && lo == ne - 1
+        ? tail_halves(W, tk, x, static_cast<int>(gridDim.x) / kXcds) : 0;
+    int32_t u = lt - xs[lo];
+    int half = 0;
+    if (hx > 0) {
+      const int32_t cx = share_of(tk, x);
+      const int32_t v = u < hx ? u : u >= cx ? u - cx + hx : -1;
+      if (v >= 0) {
+        u = cx - hx + (v >> 1);
+        half = 1 + (v & 1);
+      } else {
+        u -= hx;
+      }
+    }
+    half = __builtin_amdgcn_readfirstlane(half);
+    const int te = x * q + (x < r ? x : r) + u;
     const int m = c.win_m()[w];
     bool ok = true;
     if (!met && !down && w != ready_g1) {
@@ -542,7 +590,7 @@ void k_persist(const PKArgs a) {
       ready_g2 = w;
     }
     int32_t* xcnt = c.xdone() + (2 * w + down) * kXcds + x;
-    const int32_t xshare = share_of(tk, x);
+    const int32_t xshare = share_of(tk, x) + hx;
     if (!ok) return;
     // The control block is written during the kernel, so its loads are vector
     // loads, whose results the compiler keeps in VGPRs: every value the tile
@@ -586,10 +634,18 @@ void k_persist(const PKArgs a) {
       g.C = uniform_ptr(pm.y); g.C_scales = nullptr; g.c_rows = a.cap; g.c_row_base = 0;
       g.n_tiles = n2; g.w_packed = a.w_packed;
       g.m_plan = uniform_ptr(pm.plan); g.m_status = a.status;     // single-slot tokens merged here
-      if constexpr (F == kPMx8)
+      if (kHalves && half != 0) {
+        TileJob j{};
+        j.e = e; j.row0 = row0; j.nrows = nrows; j.ntile = ntile; j.role = kWhole; j.half = half;
+        if constexpr (F == kPMx8)
+          gemm_tile_mx8<EPI_DOWN_MERGE, BN / 2>(g, j, lds);
+        else if constexpr (F == kPBf16)
+          gemm_tile<false, EPI_DOWN_MERGE, BN / 2>(g, j, lds);
+      } else if constexpr (F == kPMx8) {
         gemm_tile_mx8<EPI_DOWN_MERGE>(g, e, row0, nrows, ntile, lds);
-      else
+      } else {
         gemm_tile<F == kPMxAct, EPI_DOWN_MERGE>(g, e, row0, nrows, ntile, lds);
+      }
       signal_tile(xcnt, xshare, &c.dn_done()[w]);
     }
   }
@@ -669,6 +725,8 @@ mok_status launch_persistent(const PersistentArgs& a, hipStream_t s) {
     }
     k.n_macro = gn; k.T = a.T; k.k = a.k; k.H = a.H; k.I = a.I; k.n_local = a.n_local;
     k.act_format = a.act_format; k.M = a.M; k.S = a.S; k.cap = a.cap; k.n_move = n_move;
+    k.n_cus = a.n_cus;
+    k.halves = (!mx || a.weight_format == MOK_W_MXFP8_E4M3) ? 1 : 0;   // as kHalves of k_persist
     k.max_win = gn * a.nwin;
     k.x_parts = a.x.part_ptr; k.x_n_part = a.x.n_partitions; k.x_part_rows = a.x.part_rows;
     k.w_gu = a.w_gu; k.w_d = a.w_d; k.w_packed = a.w_packed;
