@@ -438,12 +438,16 @@ def time_backward(mok, dw, st, reps: int = 10):
     return out
 
 
-def cpu_baseline(wl, sample_rows: int):
+def cpu_baseline(wl, sample_rows: int, got=None):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
     Route and schedule run in full; gather, FFN and combine run for random
     routed tokens until about `sample_rows` rows are covered, and their time
-    is scaled by R / rows.  Returns the estimated ms per layer."""
+    is scaled by R / rows.  Returns the estimated ms per layer.  With `got`
+    (the GPU step's output rows of every token, bf16 bits), the oracle's rows
+    of the sampled tokens are also compared with the GPU's, after the timing:
+    the stated bar's statistic max|got - ref| / RMS(ref) over every element of
+    those rows, with no allowance (`parity`)."""
     import numpy as np
     import oracle
     t0 = time.perf_counter()
@@ -476,16 +480,28 @@ def cpu_baseline(wl, sample_rows: int):
                         mx_weights=mxw)
     yr = np.full(sch["R"], -1, np.int64)
     yr[slots] = np.arange(slots.size)
-    oracle.combine_tokens(y, yr, sch["slot_of_assign"], gate, toks, wl.k)
+    ref, written = oracle.combine_tokens(y, yr, sch["slot_of_assign"], gate, toks, wl.k)
     t3 = time.perf_counter()
     est_s = (t1 - t0) + (t3 - t2) * sch["R"] / max(slots.size, 1)
     whole = slots.size == sch["R"]
     tail = ("the whole layer, not scaled" if whole else
             f"{toks.size} tokens = {slots.size} of {sch['R']} rows, scaled by R/rows")
-    return dict(value=est_s * 1e3, unit="ms/layer", cores=oracle.max_threads(), kind="oracle",
-                cpu_model=cpu_model(),
-                sample=(f"route+schedule in full ({(t1 - t0) * 1e3:.0f} ms); gather+FFN+combine "
-                        f"in {t3 - t2:.1f} s for {tail}"))
+    res = dict(value=est_s * 1e3, unit="ms/layer", cores=oracle.max_threads(), kind="oracle",
+               cpu_model=cpu_model(),
+               sample=(f"route+schedule in full ({(t1 - t0) * 1e3:.0f} ms); gather+FFN+combine "
+                       f"in {t3 - t2:.1f} s for {tail}"))
+    if got is not None:
+        bf = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)) \
+            .view(np.float32).astype(np.float64)
+        g, r = bf(got[toks][written]), bf(ref[written])
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        stat = float(np.abs(g - r).max()) / rms if rms > 0 else 0.0
+        bar = 2e-2 if wl.act_format == 0 and getattr(wl, "weight_format", 0) == 0 else 6e-2
+        res["parity"] = {"max_abs_over_rms": round(stat, 5), "bar": bar, "pass": stat <= bar,
+                         "tokens": int(written.sum()), "elements": int(r.size),
+                         "bits_differ": int(np.count_nonzero(got[toks][written] != ref[written])),
+                         "finite": bool(np.all(np.isfinite(g)))}
+    return res
 
 
 def measure(st, steps: int, warmup: int) -> dict:
@@ -813,11 +829,13 @@ def main():
     log(f"[bench] router GEMM + route (mok_route_topk_gemm) T={router['T']} E={router['E']} "
         f"H={router['H']}: {router['ms'] * 1e3:.1f} us, {router['tflops']:.0f} TF/s")
 
-    cpu = None
+    cpu = parity = None
     if args.cpu_rows > 0:
         t = time.time()
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, args.cpu_rows, got=dw.out_rows(dw.outs[0]))
+        parity = cpu.pop("parity")
         log(f"[bench] cpu baseline: {cpu['value']:.0f} ms/layer est. ({time.time() - t:.1f} s)")
+        log(f"[bench] step output against the oracle's rows of the sampled tokens: {parity}")
 
     out = {
         "metric": METRIC,
@@ -889,6 +907,8 @@ def main():
         "backward_full_mxfp8_ms": extras.get("backward_full_mxfp8"),
         "tuned_forward": tuned,
         "cpu_baseline": cpu,
+        # the timed step's output rows against the oracle's, from the cpu_baseline leg
+        "parity_vs_oracle": parity,
     }
     print(json.dumps(out), flush=True)
 
