@@ -438,7 +438,7 @@ def time_backward(mok, dw, st, reps: int = 10):
     return out
 
 
-def cpu_baseline(wl, sample_rows: int, got=None):
+def cpu_baseline(wl, sample_rows: int, got=None, got_y=None):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
     Route and schedule run in full; gather, FFN and combine run for random
@@ -447,7 +447,12 @@ def cpu_baseline(wl, sample_rows: int, got=None):
     (the GPU step's output rows of every token, bf16 bits), the oracle's rows
     of the sampled tokens are also compared with the GPU's, after the timing:
     the stated bar's statistic max|got - ref| / RMS(ref) over every element of
-    those rows, with no allowance (`parity`)."""
+    those rows, with no allowance (`parity`).  With `got_y` (the GPU's y of every
+    slot, bf16 bits [>= R, H]) the same statistic for y against the oracle's y,
+    and the oracle's merge applied to the GPU's own y against the GPU's rows:
+    where that merge reproduces the GPU's value at every element above the bar,
+    each such element differs only through a y that differs from the oracle's
+    (by its rounding), not through the merge."""
     import numpy as np
     import oracle
     t0 = time.perf_counter()
@@ -497,10 +502,28 @@ def cpu_baseline(wl, sample_rows: int, got=None):
         rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
         stat = float(np.abs(g - r).max()) / rms if rms > 0 else 0.0
         bar = 2e-2 if wl.act_format == 0 and getattr(wl, "weight_format", 0) == 0 else 6e-2
+        gw = got[toks][written]
         res["parity"] = {"max_abs_over_rms": round(stat, 5), "bar": bar, "pass": stat <= bar,
                          "tokens": int(written.sum()), "elements": int(r.size),
-                         "bits_differ": int(np.count_nonzero(got[toks][written] != ref[written])),
+                         "bits_differ": int(np.count_nonzero(gw != ref[written])),
+                         "above_bar": int(np.count_nonzero(np.abs(g - r) > bar * rms)),
                          "finite": bool(np.all(np.isfinite(g)))}
+        if got_y is not None:
+            yg, yo = bf(got_y[slots]), bf(y)
+            yrms = float(np.sqrt(np.mean(yo * yo))) if yo.size else 0.0
+            ystat = float(np.abs(yg - yo).max()) / yrms if yrms > 0 else 0.0
+            ident = np.arange(max(int(sch["R"]), 1), dtype=np.int64)
+            m_out, _ = oracle.combine_tokens(got_y, ident, sch["slot_of_assign"], gate, toks, wl.k)
+            mw = m_out[written]
+            above = np.abs(g - r) > bar * rms
+            mv = bf(mw)
+            mstat = float(np.abs(g - mv).max()) / rms if rms > 0 else 0.0
+            res["parity"].update({
+                "y_max_abs_over_rms": round(ystat, 5), "y_pass": ystat <= bar,
+                "y_slots": int(slots.size), "y_bits_differ": int(np.count_nonzero(got_y[slots] != y)),
+                "merge_of_device_y_max_abs_over_rms": round(mstat, 5),
+                "merge_of_device_y_bits_differ": int(np.count_nonzero(gw != mw)),
+                "above_bar_from_y_only": bool(np.all(gw[above] == mw[above]))})
     return res
 
 
@@ -780,6 +803,8 @@ def main():
     if args.extras and args.workload == "kimi":
         extras = measure_extras(mok, DeviceWorkload, dw, wl, st, args)
     m = measure(st, args.steps, args.warmup)
+    # the timed step's output rows (host copy) for the parity report of the cpu_baseline leg
+    step_out = dw.out_rows(dw.outs[0]) if args.cpu_rows > 0 else None
     wall_ms, per, per_sum = m["wall_ms"], m["per"], m["per_sum"]
     rr = step_rates(wl, st, per, wall_ms)
     R, T_out, peak = rr["R"], rr["T_out"], rr["peak"]
@@ -818,6 +843,8 @@ def main():
         log(f"[bench] backward (ms): {backward}")
 
     merge_all = time_merge_all_slots(mok, st) if not wl.routing_from_logits else None
+    # y of every slot (the plain down GEMM of time_merge_all_slots), for the parity report
+    step_y = to_host(st.y) if merge_all and args.cpu_rows > 0 else None
     if merge_all:
         log(f"[bench] merge of all {R} slots (mok_combine_slots): {merge_all['ms'] * 1e3:.1f} us, "
             f"{merge_all['GBps']:.0f} GB/s, {merge_all['frac_hbm']:.3f} of HBM")
@@ -832,7 +859,7 @@ def main():
     cpu = parity = None
     if args.cpu_rows > 0:
         t = time.time()
-        cpu = cpu_baseline(wl, args.cpu_rows, got=dw.out_rows(dw.outs[0]))
+        cpu = cpu_baseline(wl, args.cpu_rows, got=step_out, got_y=step_y)
         parity = cpu.pop("parity")
         log(f"[bench] cpu baseline: {cpu['value']:.0f} ms/layer est. ({time.time() - t:.1f} s)")
         log(f"[bench] step output against the oracle's rows of the sampled tokens: {parity}")

@@ -52,3 +52,38 @@ def test_cpu_baseline_parity_statistic():
     bad[t, 3] = (np.array([vals[t, 3] + 0.1 * rms], np.float32).view(np.uint32) >> 16).astype(np.uint16)[0]
     p = bench.cpu_baseline(wl, 1 << 30, got=bad)["parity"]
     assert not p["pass"] and p["max_abs_over_rms"] > 0.05 and p["bits_differ"] == 1
+
+
+def test_cpu_baseline_parity_separates_y_from_the_merge():
+    """With the GPU's y passed in: y against the oracle's y, and the oracle's
+    merge of that y against the GPU's rows.  A y moved by a few bf16 steps,
+    merged exactly, is reported as coming from y only; an output element
+    moved by itself is not."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    wl = W.tiny()
+    r = oracle.forward(wl)
+    R = int(r["R"])
+    y_dev = np.zeros((R, wl.H), np.uint16)
+    y_dev[r["slots"]] = r["y"]
+    got = np.full((wl.T, wl.H), 0x7FC1, np.uint16)
+    got[r["tokens"][r["written"]]] = r["out"][r["written"]]
+    p = bench.cpu_baseline(wl, 1 << 30, got=got, got_y=y_dev)["parity"]
+    assert p["y_max_abs_over_rms"] == 0.0 and p["y_bits_differ"] == 0 and p["y_pass"]
+    assert p["merge_of_device_y_bits_differ"] == 0 and p["above_bar_from_y_only"]
+    # y of one slot moved by 40 bf16 steps in every column, merged by the oracle's merge
+    s = int(r["slots"][0])
+    y2 = y_dev.copy()
+    y2[s] = (y2[s].astype(np.int64) + 40 * np.where(y2[s] & 0x8000, -1, 1)).astype(np.uint16)
+    ident = np.arange(R, dtype=np.int64)
+    toks = r["tokens"]
+    m_out, wr = oracle.combine_tokens(y2, ident, r["slot_of_assign"], r["topk_gate"], toks, wl.k)
+    got2 = np.full_like(got, 0x7FC1)
+    got2[toks[wr]] = m_out[wr]
+    p = bench.cpu_baseline(wl, 1 << 30, got=got2, got_y=y2)["parity"]
+    assert not p["y_pass"] and p["above_bar"] > 0
+    assert p["merge_of_device_y_bits_differ"] == 0 and p["above_bar_from_y_only"]
+    # the same output with an exact y: the merge is what differs
+    p = bench.cpu_baseline(wl, 1 << 30, got=got2, got_y=y_dev)["parity"]
+    assert p["y_pass"] and not p["above_bar_from_y_only"]
