@@ -628,9 +628,10 @@ def time_fused(mok, d, run, reps: int = 10) -> float:
 
 def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
     """The other configurations, each as its own step (or fused call): the Mixtral-shaped
-    layer (also as one fused call from its logits), the Zipf MXFP8 and full-MXFP8 shares,
-    the minibatch sweep of the fused call in stream and persistent mode on the headline's
-    share, and 8 macrobatches streamed through one ring."""
+    layer (also as one fused call from its logits, and from its tokens and router weights),
+    the Zipf MXFP8 and full-MXFP8 shares, the minibatch sweep of the fused call in stream and
+    persistent mode on the headline's share, and 8 macrobatches streamed through one ring."""
+    import numpy as np
     import torch
     steps, warm = max(5, args.steps // 2), 10
     res = {"configs": {}}
@@ -657,10 +658,25 @@ def measure_extras(mok, DeviceWorkload, dw, wl, st, args) -> dict:
                 d, dw2.logits, wl2.T, dw2.x, w_gu, w_d, dw2.outs[0], ws)), 4)
             assert mok.mok_device_status(ws) == 0
             del ws
+            # and from the tokens and router weights (router GEMM + pick + counts in the
+            # same call; seeded N(0, 1/H) router rows, so its picks are this call's own)
+            import workloads as W
+            _, w_r = W.router_inputs(78, 1, wl2.H, wl2.E)
+            wrd = torch.from_numpy(w_r.view(np.int16)).cuda()
+            ws = torch.empty(mok.mok_forward_router_workspace_size(d, wl2.T), dtype=torch.uint8,
+                             device="cuda")
+            cs["fused_from_router_weights_ms"] = round(time_fused(
+                mok, d, lambda: mok.mok_moe_forward_router(d, wrd, wl2.T, dw2.x, w_gu, w_d,
+                                                           dw2.outs[0], ws)), 4)
+            assert mok.mok_device_status(ws) == 0
+            del ws, wrd
         res["configs"][name] = cs
         log(f"[bench] {wl2.name}: {cs['ms_per_layer']:.4f} ms/layer, gate/up {cs['gate_up_frac']:.3f}"
             f" / down {cs['down_frac']:.3f} of peak, gather {cs['dispatch_frac_hbm']:.3f} / merge "
-            f"{cs['combine_frac_hbm']:.3f} of HBM ({time.time() - t:.1f} s)")
+            f"{cs['combine_frac_hbm']:.3f} of HBM ({time.time() - t:.1f} s)"
+            + (f"; one fused call from the logits {cs['fused_from_logits_ms']:.4f} ms, from the "
+               f"router weights {cs['fused_from_router_weights_ms']:.4f} ms"
+               if "fused_from_logits_ms" in cs else ""))
         del st2, dw2, wl2
         torch.cuda.empty_cache()
     res["streaming"] = time_streaming(mok, DeviceWorkload)
