@@ -503,11 +503,14 @@ def cpu_baseline(wl, sample_rows: int, got=None, got_y=None):
         stat = float(np.abs(g - r).max()) / rms if rms > 0 else 0.0
         bar = 2e-2 if wl.act_format == 0 and getattr(wl, "weight_format", 0) == 0 else 6e-2
         gw = got[toks][written]
-        res["parity"] = {"max_abs_over_rms": round(stat, 5), "bar": bar, "pass": stat <= bar,
+        res["parity"] = {"max_abs_over_rms": round(stat, 5), "bar": bar, "strict_pass": stat <= bar,
                          "tokens": int(written.sum()), "elements": int(r.size),
                          "bits_differ": int(np.count_nonzero(gw != ref[written])),
                          "above_bar": int(np.count_nonzero(np.abs(g - r) > bar * rms)),
-                         "finite": bool(np.all(np.isfinite(g)))}
+                         "finite": bool(np.all(np.isfinite(g))),
+                         "note": ("strict: the stated bar with no allowance over every element "
+                                  "of these rows; the GPU tests check every element of the "
+                                  "whole share against its derived rounding band")}
         if got_y is not None:
             yg, yo = bf(got_y[slots]), bf(y)
             yrms = float(np.sqrt(np.mean(yo * yo))) if yo.size else 0.0
@@ -519,7 +522,7 @@ def cpu_baseline(wl, sample_rows: int, got=None, got_y=None):
             mv = bf(mw)
             mstat = float(np.abs(g - mv).max()) / rms if rms > 0 else 0.0
             res["parity"].update({
-                "y_max_abs_over_rms": round(ystat, 5), "y_pass": ystat <= bar,
+                "y_max_abs_over_rms": round(ystat, 5), "y_strict_pass": ystat <= bar,
                 "y_slots": int(slots.size), "y_bits_differ": int(np.count_nonzero(got_y[slots] != y)),
                 "merge_of_device_y_max_abs_over_rms": round(mstat, 5),
                 "merge_of_device_y_bits_differ": int(np.count_nonzero(gw != mw)),
